@@ -1,0 +1,139 @@
+/*
+ * kda.h — C ABI of the MI355X (gfx950) Kimi Delta Attention library (libkda.so).
+ *
+ * The operation.  For one sequence and one head, with a d_k x d_v state S
+ * (rows = key channels, columns = value channels), every token t applies
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t                      (read after token t's own write)
+ *
+ * with alpha_t = exp(log_alpha_t) a per-key-channel retention factor.
+ * Source: "Kimi K3" study notes (dimensionstp.github.io/study-concept/kimi_k3),
+ * section 3-2 "Module breakdown", item 2) Kimi Delta Attention — the state
+ * update and read-out equations; "Kimi K3 架构、训练与系统全景解析"
+ * (kimi-k3-analysis), section 4.2.2 — the order: decay each key channel,
+ * erase along k, write beta k v^T, then read with q.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, who keeps
+ *     them alive until the work enqueued on `stream` has completed.  The
+ *     library never allocates device memory.
+ *   - Layouts are dense row-major, token-major: q/k/v/log_alpha/o are
+ *     [T_total, H, 128]; beta is [T_total, H]; states are [N, H, 128, 128]
+ *     fp32 with S[n][h][i][j], i = key channel (row), j = value channel.
+ *   - Only d_k = d_v = 128 is supported (KDA_ERR_UNSUPPORTED otherwise).
+ *   - Work is asynchronous on `stream` (0 = the null stream); no host sync.
+ *     Argument errors are detected on the host and returned before anything
+ *     is enqueued.  A failed launch returns KDA_ERR_HIP.
+ *   - Preconditions that are documented but not checked: log_alpha in
+ *     [-5, 0] (the lower-bounded decay of "Kimi K3 架构…" section 4.2.5,
+ *     gate_lower_bound = -5 of section 2.1); beta in [0, 1]; ||q||, ||k||
+ *     about 1 per head when no prologue runs; cu_seqlens non-decreasing from
+ *     0 to total_tokens.  Outside them the results are undefined (they may
+ *     overflow) but every access stays in bounds.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = 1, /* NULL where required, bad sizes, illegal overlap */
+  KDA_ERR_UNSUPPORTED = 2, /* d_k or d_v other than 128, unknown dtype       */
+  KDA_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required        */
+  KDA_ERR_HIP = 4          /* a HIP launch or runtime call failed            */
+} kda_status;
+
+typedef enum {
+  KDA_DTYPE_F32 = 0,  /* q, k, v, gate and o are float                      */
+  KDA_DTYPE_BF16 = 1  /* q, k, v, gate and o are bfloat16 (round-to-nearest-even on output) */
+} kda_dtype;
+
+/*
+ * Optional fused prologue and epilogue ("Kimi K3 架构…" section 4.2.3:
+ * ShortConv with kernel size 4, Swish, L2Norm on q and k; section 4.2.6:
+ * head-wise RMSNorm of the recurrent output, then a full-rank sigmoid output
+ * gate).  Pass NULL for plain KDA.  Each field may be NULL independently.
+ *
+ *   conv_q_w / conv_k_w  [H*128, 4] fp32 depthwise causal conv weights.  When
+ *       given, the q (resp. k) read from memory is the raw projection and the
+ *       recurrence uses  x'_t[c] = L2( SiLU( sum_{m=0..3} w[c][m] x_{t-3+m}[c] ) )
+ *       with channel c = h*128 + j, zero history before each sequence start,
+ *       and L2(x) = x / sqrt(sum_j x_j^2 + l2_eps) over the 128 channels of a head.
+ *   gate  [T_total, H, 128] logits in the I/O dtype.  When given, the stored
+ *       output is  y_t = o_t / sqrt(mean_j o_t[j]^2 + rms_eps) * norm_w * sigmoid(gate_t).
+ *   norm_w  [128] fp32 RMSNorm weight; NULL means all ones.  Used only with gate.
+ */
+typedef struct {
+  const float* conv_q_w;
+  const float* conv_k_w;
+  const void* gate;
+  const float* norm_w;
+  float l2_eps;
+  float rms_eps;
+} kda_fused_opts;
+
+/*
+ * Bytes of device workspace kda_chunk_fwd needs for these sizes (host-only
+ * computation, no device access).  Returns 0 for invalid sizes.
+ */
+size_t kda_chunk_fwd_workspace_bytes(int num_seqs, int64_t total_tokens, int num_heads, int d_k,
+                                     int d_v, kda_dtype dtype, const kda_fused_opts* opts);
+
+/*
+ * Chunkwise-parallel prefill over a packed batch of sequences ("Kimi K3 架构…"
+ * section 4.2.4 chunkwise parallel form; section 7.1 FlashKDA and in-device
+ * sequence splitting).  Sequence n owns tokens [cu_seqlens[n], cu_seqlens[n+1]).
+ *
+ *   q, k, v        [T_total, H, 128] dtype (raw projections for q/k when the
+ *                  prologue convolution is enabled)
+ *   log_alpha      [T_total, H, 128] fp32, natural-log per-key-channel decay
+ *   beta           [T_total, H] fp32 write strength
+ *   initial_state  [N, H, 128, 128] fp32, read only, or NULL for zeros.  It may
+ *                  be exactly the same pointer as final_state (in-place
+ *                  continuation); any other overlap is KDA_ERR_INVALID_ARG.
+ *   cu_seqlens     device int32 [N+1] or NULL (then N must be 1 and the one
+ *                  sequence spans all T_total tokens).  Zero-length sequences
+ *                  are allowed; their final state equals the initial state.
+ *   opts           NULL or the fused prologue/epilogue options above.
+ *   o              [T_total, H, 128] dtype output; must not overlap any input.
+ *   final_state    [N, H, 128, 128] fp32 output or NULL (not written).
+ *   workspace      device scratch of at least kda_chunk_fwd_workspace_bytes()
+ *                  bytes (may be NULL when that is 0).  Contents on entry are
+ *                  ignored; it must not be in use by other work on the GPU.
+ */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                         const float* beta, const float* initial_state, const int32_t* cu_seqlens,
+                         int num_seqs, int64_t total_tokens, int num_heads, int d_k, int d_v,
+                         kda_dtype dtype, const kda_fused_opts* opts, void* o, float* final_state,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One decode step for N independent sequences: each (n, h) state advances by
+ * one token in place ("Kimi K3 架构…" section 4.2.7: decoding keeps one
+ * fixed-size d_k x d_v state per head and advances it in place).
+ *
+ *   state       [N, H, 128, 128] fp32, read and overwritten in place
+ *   q, k, v     [N, H, 128] dtype;  log_alpha [N, H, 128] fp32;  beta [N, H] fp32
+ *   o           [N, H, 128] dtype output (o_t read after the token's write);
+ *               must not overlap any input.
+ */
+kda_status kda_decode_step(float* state, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, int num_seqs, int num_heads,
+                           int d_k, int d_v, kda_dtype dtype, void* o, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* kda_status_string(kda_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,137 @@
+"""TEST INFRASTRUCTURE ONLY: the fp64 CPU oracle of the KDA recurrence.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The library's compute path
+(``gated_delta_rule_25_amd``) never imports it, and it never imports that
+package: the two share no code.
+
+The arithmetic lives in ``kda_oracle.c`` (plain C, fp64, one token at a
+time); this module only builds it with gcc, loads it with ctypes and
+marshals numpy arrays.  See that file's header for what is computed and the
+passages of the pages it follows.
+
+Pins (tests/test_oracle_pins.py) tie it to the pages' worked examples,
+closed forms and brute-force products.  The prologue/epilogue epsilon values
+and the convolution tap order are fixed only by our own reading of the pages
+(they print no numbers for them): parity unpinned for those constants.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile kda_oracle.c into libkda_oracle.so with gcc and OpenMP."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"],
+                       check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.kda_oracle_chunk_fwd.restype = ctypes.c_int
+        lib.kda_oracle_chunk_fwd.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.POINTER(ctypes.c_int64),
+                                             ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, dp, dp, dp, dp, ctypes.c_double,
+                                             ctypes.c_double, dp, dp, ctypes.c_int]
+        lib.kda_oracle_decode_step.restype = ctypes.c_int
+        lib.kda_oracle_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int, dp, ctypes.c_int]
+        lib.kda_oracle_max_threads.restype = ctypes.c_int
+        lib.kda_oracle_max_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def max_threads() -> int:
+    return int(_load().kda_oracle_max_threads())
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, *, conv_q_w=None,
+              conv_k_w=None, gate=None, norm_w=None, l2_eps=1e-6, rms_eps=1e-6, threads=0):
+    """Per-token fp64 recurrence over a packed batch.
+
+    q, k, log_alpha: [T, H, dk]; v (and gate): [T, H, dv]; beta: [T, H];
+    initial_state: [N, H, dk, dv] or None (zeros); cu_seqlens: [N+1] or None
+    (one sequence).  Returns (o [T, H, dv], final_state [N, H, dk, dv]).
+    """
+    lib = _load()
+    q, k, v, la, b = _f64(q), _f64(k), _f64(v), _f64(log_alpha), _f64(beta)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    assert k.shape == (T, H, dk) and la.shape == (T, H, dk) and v.shape == (T, H, dv)
+    assert b.shape == (T, H)
+    if cu_seqlens is None:
+        N, cu = 1, None
+    else:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        N = cu.shape[0] - 1
+        assert cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
+    s0 = _f64(initial_state)
+    if s0 is not None:
+        assert s0.shape == (N, H, dk, dv)
+    cq, ck, g, nw = _f64(conv_q_w), _f64(conv_k_w), _f64(gate), _f64(norm_w)
+    if cq is not None:
+        assert cq.shape == (H * dk, 4)
+    if ck is not None:
+        assert ck.shape == (H * dk, 4)
+    if g is not None:
+        assert g.shape == (T, H, dv)
+    if nw is not None:
+        assert nw.shape == (dv,)
+    o = np.zeros((T, H, dv), dtype=np.float64)
+    fs = np.zeros((N, H, dk, dv), dtype=np.float64)
+    cu_p = None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    rc = lib.kda_oracle_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(b), _ptr(s0), cu_p, N, T,
+                                  H, dk, dv, _ptr(cq), _ptr(ck), _ptr(g), _ptr(nw), float(l2_eps),
+                                  float(rms_eps), _ptr(o), _ptr(fs), int(threads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_chunk_fwd failed with code %d" % rc)
+    return o, fs
+
+
+def decode_step(state, q, k, v, log_alpha, beta, threads=0):
+    """One token per (n, h).  ``state`` [N, H, dk, dv] float64 C-contiguous is
+    updated in place; q, k, log_alpha [N, H, dk]; v [N, H, dv]; beta [N, H].
+    Returns o [N, H, dv]."""
+    lib = _load()
+    if not (isinstance(state, np.ndarray) and state.dtype == np.float64 and state.flags.c_contiguous):
+        raise TypeError("state must be a C-contiguous float64 numpy array (updated in place)")
+    N, H, dk, dv = state.shape
+    q, k, v, la, b = _f64(q), _f64(k), _f64(v), _f64(log_alpha), _f64(beta)
+    assert q.shape == (N, H, dk) and k.shape == (N, H, dk) and la.shape == (N, H, dk)
+    assert v.shape == (N, H, dv) and b.shape == (N, H)
+    o = np.zeros((N, H, dv), dtype=np.float64)
+    rc = lib.kda_oracle_decode_step(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(b), N, H, dk,
+                                    dv, _ptr(o), int(threads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_decode_step failed with code %d" % rc)
+    return o

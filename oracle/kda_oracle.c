@@ -1,0 +1,179 @@
+/*
+ * kda_oracle.c — TEST INFRASTRUCTURE ONLY.  A plain, slow, fp64 CPU reference
+ * of the Kimi Delta Attention recurrence.  Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg may load it; the library's
+ * compute path never does.  It shares no code with the HIP library.
+ *
+ * What it computes, token by token, for one (sequence, head):
+ *
+ *   a_j   = exp(log_alpha_t[j])                         per key channel j
+ *   S'    = Diag(a) S                                   row j of S scaled by a_j
+ *   vhat  = S'^T k_t                                    old prediction at key k_t
+ *   u     = beta_t (v_t - vhat)                         delta-rule correction
+ *   S     = S' + k_t u^T
+ *         = (I - beta_t k_t k_t^T) Diag(a) S + beta_t k_t v_t^T
+ *   o_t   = S^T q_t                                     read after the write
+ *
+ * Sources: "Kimi K3" study notes (dimensionstp.github.io/study-concept/kimi_k3),
+ * section 3-2 item 2) Kimi Delta Attention: the update and read-out equations.
+ * "Kimi K3 架构、训练与系统全景解析", section 4.2.2: the three sub-steps in this
+ * order (per-key-channel decay, erase along k, write beta k v^T) and the read
+ * o = S^T q.  "AI-Workshop 文献分享 #15", section 7.2 ("Delta" paragraph): the
+ * correction form  S' + beta k (v - vhat)^T ; the talk's own simplified
+ * formula reads vhat from the undecayed state and is a teaching shortcut it
+ * labels as such; here vhat is read from the decayed state, which is what the
+ * exact update above implies.
+ *
+ * Optional prologue ("Kimi K3 架构…" section 4.2.3; study notes section 3-2,
+ * "ShortConv, Swish and L2 normalization on Q and K"): for q and k,
+ *   c_t[j] = sum_{m=0..3} w[h*dk+j][m] x_{t-3+m}[j]    (zeros before the sequence start)
+ *   s      = c * sigmoid(c)                              (SiLU / Swish)
+ *   x'_t   = s / sqrt(sum_j s_j^2 + l2_eps)
+ * Optional epilogue ("Kimi K3 架构…" section 4.2.6): head-wise RMSNorm of o_t,
+ * times norm_w, times sigmoid(gate_t) channel-wise.
+ *
+ * Layouts (all double): q,k,log_alpha [T,H,dk]; v,gate,o [T,H,dv];
+ * beta [T,H]; states [N,H,dk,dv] row-major; cu_seqlens int64 [N+1].
+ * Any dk, dv >= 1.  OpenMP over (sequence, head) pairs.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* One token of the recurrence on a dk x dv state S (row-major). */
+static void kda_token(double* S, int dk, int dv, const double* q, const double* k, const double* v,
+                      const double* log_alpha, double beta, double* vhat, double* o) {
+  for (int i = 0; i < dk; ++i) {
+    const double a = exp(log_alpha[i]);
+    for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= a;
+  }
+  for (int j = 0; j < dv; ++j) vhat[j] = 0.0;
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) vhat[j] += S[(size_t)i * dv + j] * k[i];
+  for (int j = 0; j < dv; ++j) vhat[j] = beta * (v[j] - vhat[j]); /* now u */
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += k[i] * vhat[j];
+  for (int j = 0; j < dv; ++j) o[j] = 0.0;
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) o[j] += S[(size_t)i * dv + j] * q[i];
+}
+
+/* ShortConv(4) + SiLU + L2 for token t (absolute index) of a sequence starting at bos. */
+static void prologue(const double* x, const double* w, int64_t bos, int64_t t, int H, int h, int d,
+                     double eps, double* out) {
+  double ss = 0.0;
+  for (int j = 0; j < d; ++j) {
+    double c = 0.0;
+    for (int m = 0; m < 4; ++m) {
+      const int64_t src = t - 3 + m;
+      if (src < bos) continue;
+      c += w[((size_t)h * d + j) * 4 + m] * x[((size_t)src * H + h) * d + j];
+    }
+    const double s = c / (1.0 + exp(-c));
+    out[j] = s;
+    ss += s * s;
+  }
+  const double inv = 1.0 / sqrt(ss + eps);
+  for (int j = 0; j < d; ++j) out[j] *= inv;
+}
+
+static void epilogue(double* o, const double* gate, const double* norm_w, int dv, double eps) {
+  double ms = 0.0;
+  for (int j = 0; j < dv; ++j) ms += o[j] * o[j];
+  ms /= (double)dv;
+  const double inv = 1.0 / sqrt(ms + eps);
+  for (int j = 0; j < dv; ++j) {
+    const double w = norm_w ? norm_w[j] : 1.0;
+    o[j] = o[j] * inv * w * (1.0 / (1.0 + exp(-gate[j])));
+  }
+}
+
+int kda_oracle_chunk_fwd(const double* q, const double* k, const double* v, const double* log_alpha,
+                         const double* beta, const double* initial_state, const int64_t* cu_seqlens,
+                         int num_seqs, int64_t total_tokens, int H, int dk, int dv,
+                         const double* conv_q_w, const double* conv_k_w, const double* gate,
+                         const double* norm_w, double l2_eps, double rms_eps, double* o,
+                         double* final_state, int num_threads) {
+  if (num_seqs < 1 || H < 1 || dk < 1 || dv < 1 || total_tokens < 0) return 1;
+  if (!cu_seqlens && num_seqs != 1) return 1;
+  const int64_t units = (int64_t)num_seqs * H;
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#else
+  (void)num_threads;
+#endif
+  int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < units; ++u) {
+    const int n = (int)(u / H), h = (int)(u % H);
+    const int64_t bos = cu_seqlens ? cu_seqlens[n] : 0;
+    const int64_t eos = cu_seqlens ? cu_seqlens[n + 1] : total_tokens;
+    double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+    double* tmp = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* qb = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* kb = (double*)malloc(sizeof(double) * (size_t)dk);
+    if (!S || !tmp || !qb || !kb) {
+#pragma omp atomic write
+      err = 2;
+      free(S); free(tmp); free(qb); free(kb);
+      continue;
+    }
+    const size_t soff = ((size_t)n * H + h) * (size_t)dk * dv;
+    if (initial_state)
+      memcpy(S, initial_state + soff, sizeof(double) * (size_t)dk * dv);
+    else
+      memset(S, 0, sizeof(double) * (size_t)dk * dv);
+    for (int64_t t = bos; t < eos; ++t) {
+      const size_t tk = ((size_t)t * H + h) * dk, tv = ((size_t)t * H + h) * dv;
+      const double* qt = q + tk;
+      const double* kt = k + tk;
+      if (conv_q_w) { prologue(q, conv_q_w, bos, t, H, h, dk, l2_eps, qb); qt = qb; }
+      if (conv_k_w) { prologue(k, conv_k_w, bos, t, H, h, dk, l2_eps, kb); kt = kb; }
+      kda_token(S, dk, dv, qt, kt, v + tv, log_alpha + tk, beta[(size_t)t * H + h], tmp, o + tv);
+      if (gate) epilogue(o + tv, gate + tv, norm_w, dv, rms_eps);
+    }
+    if (final_state) memcpy(final_state + soff, S, sizeof(double) * (size_t)dk * dv);
+    free(S); free(tmp); free(qb); free(kb);
+  }
+  return err;
+}
+
+/* One decode token per (n, h): the same token body, state updated in place. */
+int kda_oracle_decode_step(double* state, const double* q, const double* k, const double* v,
+                           const double* log_alpha, const double* beta, int num_seqs, int H, int dk,
+                           int dv, double* o, int num_threads) {
+  if (num_seqs < 1 || H < 1 || dk < 1 || dv < 1) return 1;
+  const int64_t units = (int64_t)num_seqs * H;
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#else
+  (void)num_threads;
+#endif
+  int err = 0;
+#pragma omp parallel for schedule(static)
+  for (int64_t u = 0; u < units; ++u) {
+    double* tmp = (double*)malloc(sizeof(double) * (size_t)dv);
+    if (!tmp) {
+#pragma omp atomic write
+      err = 2;
+      continue;
+    }
+    kda_token(state + (size_t)u * dk * dv, dk, dv, q + (size_t)u * dk, k + (size_t)u * dk,
+              v + (size_t)u * dv, log_alpha + (size_t)u * dk, beta[u], tmp, o + (size_t)u * dv);
+    free(tmp);
+  }
+  return err;
+}
+
+/* Number of threads an OpenMP parallel region would use (1 without OpenMP). */
+int kda_oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
