@@ -1,0 +1,203 @@
+"""KDA hot-path benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 1]
+                    [--no-decode] [--no-cpu-baseline] [--decode-steps 64]
+
+A step is one kda_chunk_fwd over one layer of the workload (all heads, all
+tokens, inputs already resident in HBM): by default the one-layer K3 shape
+H=96, d=128, T=8192 with a carried fp32 state.  `value` is prefill tokens/s.
+The decode workload (256 sequences x 96 heads, 64 in-place kda_decode_step
+calls) is timed after it and reported under "decode".  Kernel durations come
+from HIP events on the stream the kernels run on.
+
+Prints one JSON line.  Only the optional CPU-baseline leg touches the oracle.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+
+
+def prefill_algorithmic_bytes(T: int, H: int, N: int, es: int, fused: bool, with_state_in: bool,
+                              with_state_out: bool) -> int:
+    """Compulsory HBM bytes of one kda_chunk_fwd: read q, k, v (I/O dtype),
+    log_alpha (fp32), beta (fp32), [gate]; write o; state in/out fp32."""
+    d = 128
+    per_tok_head = 3 * d * es + d * 4 + 4 + d * es + (d * es if fused else 0)
+    b = T * H * per_tok_head
+    if with_state_in:
+        b += N * H * d * d * 4
+    if with_state_out:
+        b += N * H * d * d * 4
+    return b
+
+
+def decode_algorithmic_bytes(N: int, H: int, es: int) -> int:
+    """One kda_decode_step: state read + write, q, k, v, log_alpha, beta, o."""
+    d = 128
+    return N * H * (2 * d * d * 4 + 3 * d * es + d * 4 + 4 + d * es)
+
+
+def time_events(fn, steps, stream):
+    import torch
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
+def cpu_baseline(inp, max_seconds_hint=20.0):
+    """Time the fp64 oracle on a bounded sample of the same workload: the first
+    `nh` heads over all tokens, OpenMP over heads on the host cores."""
+    import numpy as np
+    import oracle
+
+    threads = oracle.max_threads()
+    H, T = inp["H"], inp["T"]
+    nh = max(1, min(H, 2 * threads))
+
+    def f64(t):
+        return t.detach().float().cpu().double().numpy()
+
+    hs = slice(0, nh)
+    q, k, v = f64(inp["q"][:, hs]), f64(inp["k"][:, hs]), f64(inp["v"][:, hs])
+    la, b = f64(inp["log_alpha"][:, hs]), f64(inp["beta"][:, hs])
+    s0 = None if inp["initial_state"] is None else f64(inp["initial_state"][:, hs])
+    t0 = time.perf_counter()
+    oracle.chunk_fwd(q, k, v, la, b, initial_state=s0, threads=threads)
+    dt = time.perf_counter() - t0
+    # whole-layer rate: the sample covers nh of H heads for all T tokens
+    rate = T * nh / H / dt
+    used = min(threads, nh)
+    return {"value": rate, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": "fp64 oracle on %d of %d heads x %d tokens (%.1f s), scaled to the full %d-head layer"
+                      % (nh, H, T, dt, H)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 4])
+    ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-decode", action="store_true", help="time only the decode workload (profiling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the KDA path here is built and timed on a single MI355X; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_25_amd as kda
+    import kda_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    w = kda_inputs.WORKLOADS[args.workload]
+    result = {}
+
+    if not args.only_decode:
+        inp = kda_inputs.make_workload(args.workload, device=dev)
+        T, H, N = inp["T"], inp["H"], inp["N"]
+        es = 2 if w["dtype"] == "bf16" else 4
+        kw = dict(initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"])
+        for key in ("conv_q_w", "conv_k_w", "gate", "norm_w"):
+            if inp.get(key) is not None:
+                kw[key] = inp[key]
+        o = torch.empty_like(inp["v"])
+        fs = torch.empty((N, H, 128, 128), dtype=torch.float32, device=dev)
+        ws_bytes = kda.chunk_fwd_workspace_bytes(N, T, H, inp["q"].dtype)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+        def step():
+            kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], out=o, final_state=fs,
+                          workspace=ws, **kw)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        per = time_events(step, args.steps, stream)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        ms_avg = sum(per) / len(per)
+        algo = prefill_algorithmic_bytes(T, H, N, es, w["fused"], inp["initial_state"] is not None, True)
+        achieved = algo / (ms_avg * 1e-3) / 1e9
+        result.update({
+            "metric": "KDA prefill tokens/s (H=96,d=128,T=8K) + decode steps/s; % of roofline",
+            "value": T / (wall / args.steps),
+            "unit": "tokens/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": wall / args.steps * 1e3,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": w["dtype"],
+            "data": "synthetic",
+            "config": {"workload": w["name"], "N": N, "H": H, "T": T, "d": 128, "chunk": 64 if es == 2 else 32,
+                       "fused_prologue_epilogue": bool(w["fused"])},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                         "kernel": "prefill_kernel", "kernel_ms_avg": ms_avg, "algorithmic_bytes": algo},
+        })
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = cpu_baseline(inp)
+        del inp, o, fs, ws
+        torch.cuda.empty_cache()
+
+    if not args.no_decode or args.only_decode:
+        wd = kda_inputs.WORKLOADS[3]
+        d = kda_inputs.make_workload(3, device=dev, steps=args.decode_steps)
+        state = d["state"]
+        outs = torch.empty_like(d["v"])
+        for s in range(min(3, args.decode_steps)):  # warm-up on a scratch copy of the state
+            scratch = state[:1].clone()
+            kda.decode_step(scratch, d["q"][s][:1].contiguous(), d["k"][s][:1].contiguous(),
+                            d["v"][s][:1].contiguous(), d["log_alpha"][s][:1].contiguous(),
+                            d["beta"][s][:1].contiguous())
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.decode_steps + 1)]
+        ev[0].record(stream)
+        for s in range(args.decode_steps):
+            kda.decode_step(state, d["q"][s], d["k"][s], d["v"][s], d["log_alpha"][s], d["beta"][s], out=outs[s])
+            ev[s + 1].record(stream)
+        torch.cuda.synchronize()
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.decode_steps)]
+        total_ms = ev[0].elapsed_time(ev[-1])
+        ms_avg = total_ms / args.decode_steps
+        dbytes = decode_algorithmic_bytes(wd["N"], wd["H"], 2)
+        ach = dbytes / (ms_avg * 1e-3) / 1e9
+        result["decode"] = {"workload": wd["name"], "steps_per_s": 1e3 / ms_avg, "ms_per_step": ms_avg,
+                            "tokens_per_s": wd["N"] * 1e3 / ms_avg, "steps": args.decode_steps,
+                            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                         "frac": ach / HBM_PEAK_GBPS, "algorithmic_bytes": dbytes,
+                                         "kernel": "decode_kernel", "kernel_ms_min": min(per)}}
+        if args.only_decode:
+            result.update({"metric": "KDA decode steps/s", "value": 1e3 / ms_avg, "unit": "steps/s"})
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+"""MI355X (gfx950) Kimi Delta Attention: Python binding of libkda.so.
+
+Thin ctypes marshalling over the C ABI declared in include/kda.h: checks
+dtypes, devices, shapes and contiguity of torch tensors, allocates outputs
+and workspace with torch (device memory and streams only), and passes raw
+pointers plus torch's current HIP stream.  Every step of the computation
+runs in the HIP kernels of libkda.so; there is no fallback path.  If the
+library is not built this module raises on first use.
+
+    o, final_state = chunk_fwd(q, k, v, log_alpha, beta, initial_state, cu_seqlens)
+    o = decode_step(state, q, k, v, log_alpha, beta)      # state updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["chunk_fwd", "decode_step", "chunk_fwd_workspace_bytes", "status_string", "KDAError",
+           "library_path", "D"]
+
+D = 128
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkda.so")
+_lib = None
+
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+
+class KDAError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s failed: %s (kda_status %d)" % (where, status_string(code), code))
+
+
+class _FusedOpts(ctypes.Structure):
+    _fields_ = [("conv_q_w", ctypes.c_void_p), ("conv_k_w", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+                ("norm_w", ctypes.c_void_p), ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libkda.so is not built (%s); run `python -m gated_delta_rule_25_amd.build`"
+                           % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [i32]
+    lib.kda_chunk_fwd_workspace_bytes.restype = sz
+    lib.kda_chunk_fwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32, vp]
+    lib.kda_chunk_fwd.restype = i32
+    lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, vp, vp, vp, vp,
+                                  sz, vp]
+    lib.kda_decode_step.restype = i32
+    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return _load().kda_status_string(int(code)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def chunk_fwd_workspace_bytes(num_seqs: int, total_tokens: int, num_heads: int,
+                              dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(_load().kda_chunk_fwd_workspace_bytes(num_seqs, total_tokens, num_heads, D, D,
+                                                     _DTYPES[dtype], None))
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor, beta: torch.Tensor,
+              initial_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None, *,
+              conv_q_w: Optional[torch.Tensor] = None, conv_k_w: Optional[torch.Tensor] = None,
+              gate: Optional[torch.Tensor] = None, norm_w: Optional[torch.Tensor] = None,
+              l2_eps: float = 1e-6, rms_eps: float = 1e-6, out: Optional[torch.Tensor] = None,
+              final_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
+              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """KDA prefill over a packed batch (kda_chunk_fwd).
+
+    q, k, v: [T, H, 128] float32 or bfloat16; log_alpha [T, H, 128] float32;
+    beta [T, H] float32; initial_state [N, H, 128, 128] float32 or None;
+    cu_seqlens int32 [N+1] on the device or None.  Optional fused prologue
+    (conv_q_w / conv_k_w [H*128, 4] float32) and epilogue (gate [T, H, 128],
+    norm_w [128] float32).  Returns (o, final_state); final_state may be the
+    same tensor as initial_state (in-place continuation).
+    """
+    lib = _load()
+    if q.dim() != 3 or q.shape[2] != D:
+        raise ValueError("q must be [T, H, 128]")
+    T, H, _ = q.shape
+    dev, dt = q.device, q.dtype
+    if dt not in _DTYPES:
+        raise TypeError("q/k/v must be float32 or bfloat16")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, (T, H, D), dt, dev)
+    _check(log_alpha, "log_alpha", (T, H, D), torch.float32, dev)
+    _check(beta, "beta", (T, H), torch.float32, dev)
+    if cu_seqlens is None:
+        N = 1
+    else:
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be [N+1]")
+        N = cu_seqlens.numel() - 1
+        _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (N, H, D, D), torch.float32, dev)
+    if conv_q_w is not None:
+        _check(conv_q_w, "conv_q_w", (H * D, 4), torch.float32, dev)
+    if conv_k_w is not None:
+        _check(conv_k_w, "conv_k_w", (H * D, 4), torch.float32, dev)
+    if gate is not None:
+        _check(gate, "gate", (T, H, D), dt, dev)
+    if norm_w is not None:
+        _check(norm_w, "norm_w", (D,), torch.float32, dev)
+    if out is None:
+        out = torch.empty((T, H, D), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (T, H, D), dt, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check(final_state, "final_state", (N, H, D, D), torch.float32, dev)
+    dtc = _DTYPES[dt]
+    opts = None
+    if any(x is not None for x in (conv_q_w, conv_k_w, gate, norm_w)):
+        opts = _FusedOpts(_ptr(conv_q_w), _ptr(conv_k_w), _ptr(gate), _ptr(norm_w), float(l2_eps),
+                          float(rms_eps))
+    opts_p = ctypes.byref(opts) if opts is not None else None
+    need = int(lib.kda_chunk_fwd_workspace_bytes(N, T, H, D, D, dtc, opts_p))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
+                           _ptr(cu_seqlens), N, T, H, D, D, dtc, opts_p, _ptr(out), _ptr(final_state),
+                           _ptr(workspace), ws_bytes, _stream(dev))
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_chunk_fwd")
+    return out, final_state
+
+
+def decode_step(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                log_alpha: torch.Tensor, beta: torch.Tensor,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One token for every (sequence, head); ``state`` [N, H, 128, 128] float32
+    is advanced in place (kda_decode_step).  q, k, v [N, H, 128] float32 or
+    bfloat16, log_alpha [N, H, 128] float32, beta [N, H] float32.  Returns o."""
+    lib = _load()
+    if state.dim() != 4:
+        raise ValueError("state must be [N, H, 128, 128]")
+    N, H = state.shape[0], state.shape[1]
+    dev, dt = q.device, q.dtype
+    if dt not in _DTYPES:
+        raise TypeError("q/k/v must be float32 or bfloat16")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    _check(state, "state", (N, H, D, D), torch.float32, dev)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, (N, H, D), dt, dev)
+    _check(log_alpha, "log_alpha", (N, H, D), torch.float32, dev)
+    _check(beta, "beta", (N, H), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, H, D), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (N, H, D), dt, dev)
+    rc = lib.kda_decode_step(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), N, H, D, D,
+                             _DTYPES[dt], _ptr(out), _stream(dev))
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_decode_step")
+    return out

@@ -1,0 +1,190 @@
+// kda_api.hip — the extern "C" boundary of libkda.so (declared in include/kda.h).
+//
+// Host side only: argument validation (before anything is enqueued), the
+// launch plan, and the launches on the caller's stream.  No device memory is
+// allocated and the host never waits on the device.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+constexpr int kD = 128;
+
+struct Range {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+};
+
+Range range_of(const void* p, size_t bytes) {
+  Range r;
+  if (p && bytes) {
+    r.lo = reinterpret_cast<uintptr_t>(p);
+    r.hi = r.lo + bytes;
+  }
+  return r;
+}
+
+bool overlap(const Range& a, const Range& b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+int cu_count_for_current_device() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+size_t elem_size(kda_dtype dt) { return dt == KDA_DTYPE_BF16 ? 2 : 4; }
+
+bool dtype_ok(kda_dtype dt) { return dt == KDA_DTYPE_F32 || dt == KDA_DTYPE_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "success";
+    case KDA_ERR_INVALID_ARG: return "invalid argument (null pointer, bad size or illegal buffer overlap)";
+    case KDA_ERR_UNSUPPORTED: return "unsupported configuration (d_k and d_v must be 128; dtype f32 or bf16)";
+    case KDA_ERR_WORKSPACE: return "workspace missing or smaller than kda_chunk_fwd_workspace_bytes()";
+    case KDA_ERR_HIP: return "HIP runtime or launch error";
+  }
+  return "unknown kda_status";
+}
+
+size_t kda_chunk_fwd_workspace_bytes(int num_seqs, int64_t total_tokens, int num_heads, int d_k, int d_v,
+                                     kda_dtype dtype, const kda_fused_opts* opts) {
+  (void)opts;
+  if (num_seqs < 1 || total_tokens < 0 || num_heads < 1 || d_k != kD || d_v != kD || !dtype_ok(dtype))
+    return 0;
+  if (num_seqs == 1) return 0;
+  // int32 sequence order, longest first
+  return ((size_t)num_seqs * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                         const float* initial_state, const int32_t* cu_seqlens, int num_seqs,
+                         int64_t total_tokens, int num_heads, int d_k, int d_v, kda_dtype dtype,
+                         const kda_fused_opts* opts, void* o, float* final_state, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (num_seqs < 1 || num_heads < 1 || total_tokens < 0) return KDA_ERR_INVALID_ARG;
+  if (d_k != kD || d_v != kD || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+  if (!cu_seqlens && num_seqs != 1) return KDA_ERR_INVALID_ARG;
+  if ((int64_t)num_seqs * num_heads > (int64_t)INT32_MAX / 2) return KDA_ERR_INVALID_ARG;
+  if (total_tokens > (int64_t)INT32_MAX) return KDA_ERR_INVALID_ARG;  // cu_seqlens is int32
+  if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_INVALID_ARG;
+  const kda_fused_opts none = {nullptr, nullptr, nullptr, nullptr, 1e-6f, 1e-6f};
+  const kda_fused_opts& f = opts ? *opts : none;
+  if (!(f.l2_eps >= 0.f) || !(f.rms_eps >= 0.f)) return KDA_ERR_INVALID_ARG;
+
+  const size_t need = kda_chunk_fwd_workspace_bytes(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, opts);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+
+  const size_t es = elem_size(dtype);
+  const size_t tok_elems = (size_t)total_tokens * num_heads * kD;
+  const size_t state_bytes = (size_t)num_seqs * num_heads * kD * kD * sizeof(float);
+  const Range r_q = range_of(q, tok_elems * es), r_k = range_of(k, tok_elems * es), r_v = range_of(v, tok_elems * es);
+  const Range r_la = range_of(log_alpha, tok_elems * sizeof(float));
+  const Range r_b = range_of(beta, (size_t)total_tokens * num_heads * sizeof(float));
+  const Range r_s0 = range_of(initial_state, state_bytes);
+  const Range r_cu = range_of(cu_seqlens, cu_seqlens ? (size_t)(num_seqs + 1) * sizeof(int32_t) : 0);
+  const Range r_g = range_of(f.gate, f.gate ? tok_elems * es : 0);
+  const Range r_cq = range_of(f.conv_q_w, f.conv_q_w ? (size_t)num_heads * kD * 4 * sizeof(float) : 0);
+  const Range r_ck = range_of(f.conv_k_w, f.conv_k_w ? (size_t)num_heads * kD * 4 * sizeof(float) : 0);
+  const Range r_nw = range_of(f.norm_w, f.norm_w ? kD * sizeof(float) : 0);
+  const Range r_o = range_of(o, tok_elems * es);
+  const Range r_fs = range_of(final_state, final_state ? state_bytes : 0);
+  const Range r_ws = range_of(workspace, need);
+  const Range inputs[] = {r_q, r_k, r_v, r_la, r_b, r_s0, r_cu, r_g, r_cq, r_ck, r_nw};
+  for (const Range& in : inputs) {
+    if (overlap(r_o, in) || overlap(r_ws, in)) return KDA_ERR_INVALID_ARG;
+    const bool exact_alias = (in.lo == r_s0.lo && in.hi == r_s0.hi && r_fs.lo == r_s0.lo && r_fs.hi == r_s0.hi);
+    if (overlap(r_fs, in) && !exact_alias) return KDA_ERR_INVALID_ARG;
+  }
+  if (overlap(r_o, r_fs) || overlap(r_o, r_ws) || overlap(r_fs, r_ws)) return KDA_ERR_INVALID_ARG;
+
+  kda::PrefillArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_alpha = log_alpha;
+  a.beta = beta;
+  a.init = initial_state;
+  a.cu = cu_seqlens;
+  a.order = (num_seqs > 1) ? static_cast<int32_t*>(workspace) : nullptr;
+  a.o = o;
+  a.fin = final_state;
+  a.conv_q_w = f.conv_q_w;
+  a.conv_k_w = f.conv_k_w;
+  a.gate = f.gate;
+  a.norm_w = f.norm_w;
+  a.l2_eps = f.l2_eps;
+  a.rms_eps = f.rms_eps;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.total_tokens = total_tokens;
+  a.units = num_seqs * num_heads;
+  a.bf16 = (dtype == KDA_DTYPE_BF16);
+  // Split the value columns in two when the (sequence, head) chains alone
+  // cannot occupy the GPU; the epilogue normalises whole heads, so it keeps one.
+  a.col_split = (!f.gate && a.units <= cu_count_for_current_device()) ? 2 : 1;
+
+  if (num_seqs > 1) {
+    if (kda::launch_worklist(cu_seqlens, num_seqs, a.order, stream) != hipSuccess) return KDA_ERR_HIP;
+  }
+  if (kda::launch_prefill(a, stream) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+kda_status kda_decode_step(float* state, const void* q, const void* k, const void* v, const float* log_alpha,
+                           const float* beta, int num_seqs, int num_heads, int d_k, int d_v, kda_dtype dtype,
+                           void* o, hipStream_t stream) {
+  if (num_seqs < 1 || num_heads < 1) return KDA_ERR_INVALID_ARG;
+  if (d_k != kD || d_v != kD || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+  if (!state || !q || !k || !v || !log_alpha || !beta || !o) return KDA_ERR_INVALID_ARG;
+  const int64_t units = (int64_t)num_seqs * num_heads;
+  if (units > (int64_t)INT32_MAX) return KDA_ERR_INVALID_ARG;
+  const size_t es = elem_size(dtype);
+  const Range r_s = range_of(state, (size_t)units * kD * kD * sizeof(float));
+  const Range r_q = range_of(q, (size_t)units * kD * es), r_k = range_of(k, (size_t)units * kD * es),
+              r_v = range_of(v, (size_t)units * kD * es);
+  const Range r_la = range_of(log_alpha, (size_t)units * kD * sizeof(float));
+  const Range r_b = range_of(beta, (size_t)units * sizeof(float));
+  const Range r_o = range_of(o, (size_t)units * kD * es);
+  const Range inputs[] = {r_q, r_k, r_v, r_la, r_b};
+  for (const Range& in : inputs)
+    if (overlap(r_o, in) || overlap(r_s, in)) return KDA_ERR_INVALID_ARG;
+  if (overlap(r_o, r_s)) return KDA_ERR_INVALID_ARG;
+
+  kda::DecodeArgs a;
+  a.state = state;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_alpha = log_alpha;
+  a.beta = beta;
+  a.o = o;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.bf16 = (dtype == KDA_DTYPE_BF16);
+  if (kda::launch_decode(a, stream) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,155 @@
+// kda_device.h — device-side building blocks for the gfx950 KDA kernels.
+//
+// Matrix-core fragments.  Every contraction uses the 16x16 output tile of the
+// CDNA4 MFMA unit with fp32 accumulation:
+//   bf16 operands:  v_mfma_f32_16x16x32_bf16   (one instruction per 32-deep step)
+//   fp32 operands:  v_mfma_f32_16x16x4_f32     (eight instructions per 32-deep step)
+// For both, lane l of a 64-wide wave supplies 8 operand values of row (A) or
+// column (B) l % 16 for the lane group g = l / 16, and receives the output
+// rows 4g..4g+3 of column l % 16.  Which 8 contraction indices a lane group
+// carries is free as long as the A and B operands agree; two index sets are
+// used:
+//   contiguous:  k0 + 8g + {0..7}
+//   d-permuted:  k0 + 4g + {0..3}  and  k0 + 16 + 4g + {0..3}
+// The d-permuted set is exactly what a lane holds of two vertically stacked
+// output tiles, so an fp32 result tile pair can feed the next contraction as
+// a B operand straight from registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int D = 128;  // d_k = d_v
+
+template <typename E>
+struct Frag;
+
+template <>
+struct Frag<__bf16> {
+  bf16x8 v;
+};
+
+template <>
+struct Frag<float> {
+  f32x4 lo, hi;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename E>
+__device__ __forceinline__ E from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// 8 consecutive operand values (contiguous index set); p must be 16-byte aligned.
+__device__ __forceinline__ void ld_frag(Frag<__bf16>& f, const __bf16* p) {
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void ld_frag(Frag<float>& f, const float* p) {
+  f.lo = *reinterpret_cast<const f32x4*>(p);
+  f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+}
+
+// d-permuted index set: p points at k0 + 4g; the second half is 16 further.
+__device__ __forceinline__ void ld_frag_perm(Frag<__bf16>& f, const __bf16* p) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 16);
+  f.v = (bf16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ void ld_frag_perm(Frag<float>& f, const float* p) {
+  f.lo = *reinterpret_cast<const f32x4*>(p);
+  f.hi = *reinterpret_cast<const f32x4*>(p + 16);
+}
+
+// B operand from two stacked fp32 output tiles held by this lane.
+__device__ __forceinline__ void frag_from_acc(Frag<__bf16>& f, f32x4 x0, f32x4 x1) {
+  f.v = (bf16x8){(__bf16)x0[0], (__bf16)x0[1], (__bf16)x0[2], (__bf16)x0[3],
+                 (__bf16)x1[0], (__bf16)x1[1], (__bf16)x1[2], (__bf16)x1[3]};
+}
+__device__ __forceinline__ void frag_from_acc(Frag<float>& f, f32x4 x0, f32x4 x1) {
+  f.lo = x0;
+  f.hi = x1;
+}
+
+// Operand from 8 fp32 values.
+__device__ __forceinline__ void frag_from_f32(Frag<__bf16>& f, const float* x) {
+  f.v = (bf16x8){(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3],
+                 (__bf16)x[4], (__bf16)x[5], (__bf16)x[6], (__bf16)x[7]};
+}
+__device__ __forceinline__ void frag_from_f32(Frag<float>& f, const float* x) {
+  f.lo = (f32x4){x[0], x[1], x[2], x[3]};
+  f.hi = (f32x4){x[4], x[5], x[6], x[7]};
+}
+
+__device__ __forceinline__ void frag_unpack(const Frag<__bf16>& f, float* x) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = (float)f.v[j];
+}
+__device__ __forceinline__ void frag_unpack(const Frag<float>& f, float* x) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[j] = f.lo[j];
+    x[j + 4] = f.hi[j];
+  }
+}
+
+__device__ __forceinline__ Frag<__bf16> frag_neg(Frag<__bf16> f) {
+  u32x4 bits = __builtin_bit_cast(u32x4, f.v);
+  bits ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  f.v = __builtin_bit_cast(bf16x8, bits);
+  return f;
+}
+__device__ __forceinline__ Frag<float> frag_neg(Frag<float> f) {
+  f.lo = -f.lo;
+  f.hi = -f.hi;
+  return f;
+}
+
+// acc += A * B over one 32-deep contraction step.
+__device__ __forceinline__ f32x4 mma(f32x4 acc, const Frag<__bf16>& a, const Frag<__bf16>& b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(f32x4 acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[j], b.lo[j], acc, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[j], b.hi[j], acc, 0, 0, 0);
+  return acc;
+}
+
+__device__ __forceinline__ float sigmoidf_fast(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+}  // namespace kda
+
+namespace kda {
+
+// Store 8 consecutive operand values; p must be 16-byte aligned.
+__device__ __forceinline__ void st_frag(__bf16* p, const Frag<__bf16>& f) {
+  *reinterpret_cast<bf16x8*>(p) = f.v;
+}
+__device__ __forceinline__ void st_frag(float* p, const Frag<float>& f) {
+  *reinterpret_cast<f32x4*>(p) = f.lo;
+  *reinterpret_cast<f32x4*>(p + 4) = f.hi;
+}
+
+// x ~= hi + lo with both parts in bf16 (lo carries the next 8 significant bits).
+__device__ __forceinline__ void frag_split(Frag<__bf16>& hi, Frag<__bf16>& lo, const float* x) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 h = (__bf16)x[j];
+    hi.v[j] = h;
+    lo.v[j] = (__bf16)(x[j] - (float)h);
+  }
+}
+
+}  // namespace kda

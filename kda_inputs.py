@@ -1,0 +1,156 @@
+"""Seeded synthetic inputs for the KDA hot path (shared by tests and bench).
+
+This module only draws random inputs with the shapes and distributions of
+the K3 KDA layers ("Kimi K3 架构、训练与系统全景解析", section 2.1: 96 heads,
+head_dim 128, ShortConv kernel 4, gate_lower_bound -5; contexts up to 1M
+tokens).  It contains none of the recurrence's arithmetic; the library and
+the fp64 oracle both consume what it produces, and the oracle always reads
+back the exact bytes the library was given.
+
+Recipe (every draw uses torch's counter-based generator on the target
+device, seeded per workload; slices are drawn in a fixed order so the result
+is deterministic for a given device type):
+  q, k     N(0,1) fp32, then L2-normalised over the 128 channels of each
+           (token, head) in fp32, then cast to the I/O dtype (RNE).  With
+           the fused prologue q and k are the raw N(0,1) projections instead.
+  v        N(0,1), cast to the I/O dtype.
+  beta     sigmoid(N(0,1)) fp32, [T, H].
+  log_alpha  -5 * sigmoid(N(0,1)) fp32, [T, H, 128]  (values in (-5, 0)).
+  S0       std * N(0,1) fp32 [N, H, 128, 128], or None (zeros) when std = 0.
+  prologue conv weights 0.5 * N(0,1) fp32 [H*128, 4] for each of q and k.
+  epilogue gate logits N(0,1) in the I/O dtype, norm weight = ones (None).
+  varlen   L_n = floor(1024 * 64**u_n), u_n ~ U[0,1) from numpy's Philox
+           generator (log-uniform in [1024, 65536]).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+D = 128
+SEED_BASE = 0x4B444100
+
+# The five workloads: shapes of one K3 KDA layer (and the small fp32 case).
+WORKLOADS = {
+    0: dict(name="kda_fp32_H2_T256", kind="prefill", dtype="f32", H=2, lengths=[256], s0_std=0.0,
+            fused=False),
+    1: dict(name="kda_prefill_H96_T8192", kind="prefill", dtype="bf16", H=96, lengths=[8192],
+            s0_std=0.02, fused=False),
+    2: dict(name="kda_prefill_H96_T131072", kind="prefill", dtype="bf16", H=96, lengths=[131072],
+            s0_std=0.02, fused=False),
+    3: dict(name="kda_decode_N256_H96_64steps", kind="decode", dtype="bf16", N=256, H=96, steps=64,
+            s0_std=0.02),
+    4: dict(name="kda_varlen64_fused_H96", kind="prefill", dtype="bf16", H=96, lengths="loguniform64",
+            s0_std=0.0, fused=True),
+}
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+def varlen_lengths(seed: int, n: int = 64, lo: int = 1024, hi: int = 65536) -> list:
+    rng = np.random.Generator(np.random.Philox(seed))
+    u = rng.random(n)
+    ratio = hi / lo
+    return [int(math.floor(lo * ratio ** x)) for x in u]
+
+
+def workload_lengths(wid: int) -> list:
+    w = WORKLOADS[wid]
+    if w["lengths"] == "loguniform64":
+        return varlen_lengths(SEED_BASE + wid)
+    return list(w["lengths"])
+
+
+def _gen(device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _randn(shape, g, device):
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+
+
+def _fill_unit(dst, g, device, normalise, slab):
+    """Fill dst [T, H, 128] slab by slab with N(0,1) draws (L2-normalised per row if asked)."""
+    T = dst.shape[0]
+    for a in range(0, T, slab):
+        e = min(T, a + slab)
+        x = _randn((e - a,) + tuple(dst.shape[1:]), g, device)
+        if normalise:
+            x = x / x.norm(dim=-1, keepdim=True)
+        dst[a:e].copy_(x)
+        del x
+
+
+def make_prefill(H, lengths, dtype="bf16", s0_std=0.0, fused=False, device="cpu", seed=SEED_BASE,
+                 slab_tokens=16384):
+    """Packed prefill inputs.  Returns a dict of tensors on ``device``."""
+    dt = torch_dtype(dtype)
+    g = _gen(device, seed)
+    lengths = [int(x) for x in lengths]
+    N = len(lengths)
+    T = int(sum(lengths))
+    cu = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32)
+    out = {"H": H, "N": N, "T": T, "lengths": lengths, "dtype": dtype}
+    q = torch.empty((T, H, D), dtype=dt, device=device)
+    k = torch.empty((T, H, D), dtype=dt, device=device)
+    v = torch.empty((T, H, D), dtype=dt, device=device)
+    la = torch.empty((T, H, D), dtype=torch.float32, device=device)
+    _fill_unit(q, g, device, not fused, slab_tokens)
+    _fill_unit(k, g, device, not fused, slab_tokens)
+    _fill_unit(v, g, device, False, slab_tokens)
+    for a in range(0, T, slab_tokens):
+        e = min(T, a + slab_tokens)
+        la[a:e] = -5.0 * torch.sigmoid(_randn((e - a, H, D), g, device))
+    beta = torch.sigmoid(_randn((T, H), g, device))
+    s0 = None
+    if s0_std > 0:
+        s0 = s0_std * _randn((N, H, D, D), g, device)
+    out.update(q=q, k=k, v=v, log_alpha=la, beta=beta, initial_state=s0,
+               cu_seqlens=cu.to(device) if N > 1 else None, cu_host=cu)
+    if fused:
+        out["conv_q_w"] = 0.5 * _randn((H * D, 4), g, device)
+        out["conv_k_w"] = 0.5 * _randn((H * D, 4), g, device)
+        gate = torch.empty((T, H, D), dtype=dt, device=device)
+        _fill_unit(gate, g, device, False, slab_tokens)
+        out["gate"] = gate
+        out["norm_w"] = None
+    return out
+
+
+def make_decode(N, H, steps, dtype="bf16", s0_std=0.02, device="cpu", seed=SEED_BASE):
+    """Decode inputs: state [N,H,128,128] and `steps` distinct tokens per sequence."""
+    dt = torch_dtype(dtype)
+    g = _gen(device, seed)
+    state = s0_std * _randn((N, H, D, D), g, device)
+    q = torch.empty((steps, N, H, D), dtype=dt, device=device)
+    k = torch.empty((steps, N, H, D), dtype=dt, device=device)
+    v = torch.empty((steps, N, H, D), dtype=dt, device=device)
+    la = torch.empty((steps, N, H, D), dtype=torch.float32, device=device)
+    beta = torch.empty((steps, N, H), dtype=torch.float32, device=device)
+    for s in range(steps):
+        x = _randn((N, H, D), g, device)
+        q[s] = x / x.norm(dim=-1, keepdim=True)
+        x = _randn((N, H, D), g, device)
+        k[s] = x / x.norm(dim=-1, keepdim=True)
+        v[s] = _randn((N, H, D), g, device)
+        la[s] = -5.0 * torch.sigmoid(_randn((N, H, D), g, device))
+        beta[s] = torch.sigmoid(_randn((N, H), g, device))
+    return dict(N=N, H=H, steps=steps, dtype=dtype, state=state, q=q, k=k, v=v, log_alpha=la,
+                beta=beta)
+
+
+def make_workload(wid: int, device="cpu", **overrides):
+    """Inputs of one of the five workloads (overrides: e.g. lengths or steps)."""
+    w = dict(WORKLOADS[wid])
+    w.update(overrides)
+    seed = SEED_BASE + wid
+    if w["kind"] == "decode":
+        return make_decode(w["N"], w["H"], w["steps"], w["dtype"], w["s0_std"], device, seed)
+    lengths = w["lengths"] if w["lengths"] != "loguniform64" else varlen_lengths(seed)
+    return make_prefill(w["H"], lengths, w["dtype"], w["s0_std"], w["fused"], device, seed)

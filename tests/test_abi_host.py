@@ -1,0 +1,174 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+- libkda.so loads and exports every function include/kda.h declares;
+- status strings and the workspace query;
+- argument validation returns its error before anything reaches the device
+  (every call here is built to fail validation; the pointers are never
+  dereferenced);
+- the input generator's recipe (ranges, determinism, varlen lengths).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "gated_delta_rule_25_amd", "libkda.so")
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = range(5)
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from gated_delta_rule_25_amd import build
+        build.build()
+    L = ctypes.CDLL(LIB)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    L.kda_status_string.restype = ctypes.c_char_p
+    L.kda_status_string.argtypes = [i32]
+    L.kda_chunk_fwd_workspace_bytes.restype = sz
+    L.kda_chunk_fwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32, vp]
+    L.kda_chunk_fwd.restype = i32
+    L.kda_chunk_fwd.argtypes = [vp] * 7 + [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.kda_decode_step.restype = i32
+    L.kda_decode_step.argtypes = [vp] * 6 + [i32, i32, i32, i32, i32, vp, vp]
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(lib):
+    names = declared_functions()
+    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_decode_step",
+                          "kda_status_string"}
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(kda_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        s = lib.kda_status_string(code).decode()
+        assert s and s != "unknown kda_status"
+    assert lib.kda_status_string(99).decode() == "unknown kda_status"
+
+
+def test_workspace_bytes(lib):
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, None) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(64, 10 ** 6, 96, 128, 128, BF16, None) == 256
+    assert lib.kda_chunk_fwd_workspace_bytes(65, 10 ** 6, 96, 128, 128, BF16, None) == 512
+    assert lib.kda_chunk_fwd_workspace_bytes(2, 10, 2, 64, 128, BF16, None) == 0  # invalid sizes
+    assert lib.kda_chunk_fwd_workspace_bytes(0, 10, 2, 128, 128, BF16, None) == 0
+
+
+# Fake, never-dereferenced device addresses for validation-only calls.
+BASE = 0x7F0000000000
+MB = 1 << 20
+
+
+def p(i):
+    return ctypes.c_void_p(BASE + i * 64 * MB)
+
+
+def chunk(lib, **kw):
+    a = dict(q=p(0), k=p(1), v=p(2), la=p(3), b=p(4), s0=None, cu=None, N=1, T=10, H=2, dk=128, dv=128,
+             dt=BF16, opts=None, o=p(5), fs=p(6), ws=None, wsb=0)
+    a.update(kw)
+    return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["la"], a["b"], a["s0"], a["cu"], a["N"], a["T"], a["H"],
+                             a["dk"], a["dv"], a["dt"], a["opts"], a["o"], a["fs"], a["ws"], a["wsb"], None)
+
+
+def test_chunk_validation(lib):
+    assert chunk(lib, dk=64) == UNSUPPORTED
+    assert chunk(lib, dv=256) == UNSUPPORTED
+    assert chunk(lib, dt=7) == UNSUPPORTED
+    assert chunk(lib, N=0) == INVALID
+    assert chunk(lib, H=0) == INVALID
+    assert chunk(lib, T=-1) == INVALID
+    assert chunk(lib, q=None) == INVALID
+    assert chunk(lib, o=None) == INVALID
+    assert chunk(lib, N=2) == INVALID                          # several sequences need cu_seqlens
+    assert chunk(lib, N=2, cu=p(7)) == WORKSPACE               # ... and a workspace
+    assert chunk(lib, N=2, cu=p(7), ws=p(8), wsb=16) == WORKSPACE
+    assert chunk(lib, o=p(0)) == INVALID                       # output aliases q
+    assert chunk(lib, fs=p(3)) == INVALID                      # final state aliases log_alpha
+    assert chunk(lib, s0=p(6), fs=ctypes.c_void_p(BASE + 6 * 64 * MB + 4)) == INVALID  # partial overlap
+    assert chunk(lib, N=2, cu=p(7), ws=p(0), wsb=256) == INVALID  # workspace aliases q
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [("conv_q_w", ctypes.c_void_p), ("conv_k_w", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+                ("norm_w", ctypes.c_void_p), ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+
+
+def test_chunk_validation_fused(lib):
+    o = Opts(None, None, p(5).value, None, 1e-6, 1e-6)        # gate aliases the output
+    assert chunk(lib, opts=ctypes.cast(ctypes.pointer(o), ctypes.c_void_p)) == INVALID
+    o2 = Opts(None, None, None, None, -1.0, 1e-6)             # negative epsilon
+    assert chunk(lib, opts=ctypes.cast(ctypes.pointer(o2), ctypes.c_void_p)) == INVALID
+
+
+def decode(lib, **kw):
+    a = dict(s=p(0), q=p(1), k=p(2), v=p(3), la=p(4), b=p(5), N=2, H=2, dk=128, dv=128, dt=BF16, o=p(6))
+    a.update(kw)
+    return lib.kda_decode_step(a["s"], a["q"], a["k"], a["v"], a["la"], a["b"], a["N"], a["H"], a["dk"], a["dv"],
+                               a["dt"], a["o"], None)
+
+
+def test_decode_validation(lib):
+    assert decode(lib, dk=64) == UNSUPPORTED
+    assert decode(lib, dt=5) == UNSUPPORTED
+    assert decode(lib, N=0) == INVALID
+    assert decode(lib, s=None) == INVALID
+    assert decode(lib, o=p(1)) == INVALID      # output aliases q
+    assert decode(lib, s=p(2)) == INVALID      # state aliases k
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import gated_delta_rule_25_amd as kda
+    x = torch.zeros(4, 2, 128)
+    with pytest.raises(ValueError):
+        kda.chunk_fwd(x, x, x, x, torch.zeros(4, 2))
+
+
+# ---------------------------------------------------------------------------
+# Input generator recipe
+# ---------------------------------------------------------------------------
+
+def test_generator_recipe_and_determinism():
+    import kda_inputs
+    a = kda_inputs.make_prefill(3, [40, 0, 25], "bf16", 0.02, False, "cpu", seed=1)
+    b = kda_inputs.make_prefill(3, [40, 0, 25], "bf16", 0.02, False, "cpu", seed=1)
+    for key in ("q", "k", "v", "log_alpha", "beta", "initial_state"):
+        assert torch.equal(a[key], b[key]), key
+    la = a["log_alpha"]
+    assert (la < 0).all() and (la > -5).all()
+    assert (a["beta"] > 0).all() and (a["beta"] < 1).all()
+    nq = a["q"].float().norm(dim=-1)
+    assert torch.allclose(nq, torch.ones_like(nq), atol=1e-2)
+    assert a["cu_host"].tolist() == [0, 40, 40, 65]
+    # 16-token tiles of the drawn decay stay inside the pages' (-80, 0] range
+    tiles = la[:32].reshape(2, 16, 3, 128).sum(1)
+    assert (tiles > -80).all() and (tiles <= 0).all()
+
+
+def test_varlen_lengths_loguniform():
+    import kda_inputs
+    L = kda_inputs.workload_lengths(4)
+    assert len(L) == 64 and min(L) >= 1024 and max(L) <= 65536
+    assert L == kda_inputs.workload_lengths(4)
+    s = sum(L)
+    assert 0.5e6 < s < 1.6e6

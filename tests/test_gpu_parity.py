@@ -1,0 +1,288 @@
+"""GPU parity of libkda.so against the fp64 oracle (run with -m gpu on an MI355X).
+
+Every case generates seeded inputs on the device, runs the HIP path through
+the C ABI (Python binding), reads back the exact input bytes, runs the
+oracle on them and compares slice by slice (tests/kda_testlib.py states the
+metric).  Bars: 2e-2 (bf16 inputs), 1e-4 (fp32 inputs).
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+import gated_delta_rule_25_amd as kda
+from kda_testlib import TOL, compare_prefill, library_inputs, to64, slice_err, sync
+import oracle
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_prefill(inp, **extra):
+    kw = library_inputs(inp)
+    kw.update(extra)
+    o, fs = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], **kw)
+    sync()
+    return o, fs
+
+
+PREFILL_CASES = [
+    # (name, H, lengths, dtype, s0_std)
+    ("f32_T1", 2, [1], "f32", 0.5),
+    ("f32_T33_ragged", 2, [33], "f32", 0.5),
+    ("f32_T256_cfg0shape", 2, [256], "f32", 0.0),
+    ("f32_varlen", 3, [5, 0, 64, 1, 100], "f32", 0.3),
+    ("bf16_T1", 4, [1], "bf16", 0.02),
+    ("bf16_T15", 4, [15], "bf16", 0.02),
+    ("bf16_T16", 4, [16], "bf16", 0.02),
+    ("bf16_T17", 4, [17], "bf16", 0.02),
+    ("bf16_T63", 4, [63], "bf16", 0.02),
+    ("bf16_T64", 4, [64], "bf16", 0.02),
+    ("bf16_T65", 4, [65], "bf16", 0.02),
+    ("bf16_T1000", 4, [1000], "bf16", 0.02),
+    ("bf16_varlen_empty_ones", 5, [0, 1, 130, 0, 77, 2], "bf16", 0.5),
+    ("bf16_many_units_nosplit", 96, [40, 70, 3], "bf16", 0.02),
+]
+
+
+@pytest.mark.parametrize("name,H,lengths,dtype,s0", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_parity(name, H, lengths, dtype, s0):
+    say("case %s H=%d lengths=%s dtype=%s" % (name, H, lengths, dtype))
+    inp = kda_inputs.make_prefill(H, lengths, dtype, s0, False, DEV, seed=zlib.crc32(name.encode()) & 0xFFFF)
+    o, fs = run_prefill(inp)
+    heads = range(H) if H <= 8 else [0, 1, 47, 95]
+    eo, es = compare_prefill(inp, o, fs, heads=heads)
+    say("  err_o %.3e err_state %.3e" % (eo, es))
+    assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fused_prologue_epilogue(dtype):
+    lengths = [70, 1, 0, 129, 5] if dtype == "bf16" else [40, 0, 33]
+    H = 3
+    say("case fused dtype=%s lengths=%s" % (dtype, lengths))
+    inp = kda_inputs.make_prefill(H, lengths, dtype, 0.0, True, DEV, seed=77)
+    inp["norm_w"] = 1.0 + 0.1 * torch.randn(128, device=DEV)
+    o, fs = run_prefill(inp)
+    eo, es = compare_prefill(inp, o, fs)
+    say("  err_o %.3e err_state %.3e" % (eo, es))
+    assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
+
+
+@pytest.mark.parametrize("which", ["q_only", "k_only", "gate_only"])
+def test_fused_partial_options(which):
+    H, lengths = 2, [37, 90]
+    say("case fused partial %s" % which)
+    inp = kda_inputs.make_prefill(H, lengths, "bf16", 0.02, True, DEV, seed=5)
+    if which != "q_only":
+        inp["conv_q_w"] = None
+    if which != "k_only":
+        inp["conv_k_w"] = None
+    if which != "gate_only":
+        inp["gate"] = None
+    if which != "q_only":  # raw q is not unit norm without its prologue; normalise it here
+        inp["q"] = (inp["q"].float() / inp["q"].float().norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    if which != "k_only":
+        inp["k"] = (inp["k"].float() / inp["k"].float().norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    o, fs = run_prefill(inp)
+    eo, es = compare_prefill(inp, o, fs)
+    say("  err_o %.3e err_state %.3e" % (eo, es))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
+
+
+def test_worst_case_decay_is_finite():
+    """log_alpha = -5 everywhere: the 16-token tile reaches the pages' e^80 bound."""
+    say("case worst-case decay")
+    inp = kda_inputs.make_prefill(4, [200, 64], "bf16", 0.02, False, DEV, seed=9)
+    inp["log_alpha"].fill_(-5.0)
+    o, fs = run_prefill(inp)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(fs).all()
+    eo, es = compare_prefill(inp, o, fs)
+    say("  err_o %.3e err_state %.3e" % (eo, es))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_no_decay_and_beta_extremes():
+    say("case alpha=1, beta in {0,1}")
+    inp = kda_inputs.make_prefill(2, [150], "bf16", 0.3, False, DEV, seed=10)
+    inp["log_alpha"].zero_()
+    inp["beta"].copy_((torch.arange(150, device=DEV)[:, None] % 3 == 0).float().expand(150, 2))
+    o, fs = run_prefill(inp)
+    eo, es = compare_prefill(inp, o, fs)
+    say("  err_o %.3e err_state %.3e" % (eo, es))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_initial_state_untouched_and_inplace_continuation():
+    say("case read-only initial state / in-place continuation")
+    inp = kda_inputs.make_prefill(3, [100, 31], "bf16", 0.5, False, DEV, seed=11)
+    s0 = inp["initial_state"]
+    before = s0.clone()
+    o1, fs1 = run_prefill(inp)
+    assert torch.equal(s0, before), "initial_state was modified"
+    # in place: final_state is the initial_state tensor
+    s_inplace = s0.clone()
+    kw = library_inputs(inp)
+    kw["initial_state"] = s_inplace
+    o2, fs2 = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], final_state=s_inplace,
+                            **kw)
+    sync()
+    assert fs2.data_ptr() == s_inplace.data_ptr()
+    assert torch.equal(fs2, fs1) and torch.equal(o2, o1)
+
+
+def test_deterministic():
+    say("case bitwise determinism")
+    inp = kda_inputs.make_prefill(8, [300, 77], "bf16", 0.02, False, DEV, seed=12)
+    o1, fs1 = run_prefill(inp)
+    o2, fs2 = run_prefill(inp)
+    assert torch.equal(o1, o2) and torch.equal(fs1, fs2)
+
+
+def test_split_resume_equals_single_run():
+    """Affine composition ("Kimi K3 架构…" section 7.1): running [0,t) then [t,T)
+    from the carried state equals one run, within the bf16 bar."""
+    say("case split/resume")
+    T, t = 333, 128
+    inp = kda_inputs.make_prefill(4, [T], "bf16", 0.02, False, DEV, seed=13)
+    o, fs = run_prefill(inp)
+    a = {k_: (v_[:t] if torch.is_tensor(v_) and v_.dim() >= 2 and v_.shape[0] == T else v_) for k_, v_ in inp.items()}
+    b = {k_: (v_[t:] if torch.is_tensor(v_) and v_.dim() >= 2 and v_.shape[0] == T else v_) for k_, v_ in inp.items()}
+    o1, fs1 = kda.chunk_fwd(a["q"].contiguous(), a["k"].contiguous(), a["v"].contiguous(),
+                            a["log_alpha"].contiguous(), a["beta"].contiguous(), initial_state=inp["initial_state"])
+    o2, fs2 = kda.chunk_fwd(b["q"].contiguous(), b["k"].contiguous(), b["v"].contiguous(),
+                            b["log_alpha"].contiguous(), b["beta"].contiguous(), initial_state=fs1)
+    sync()
+    oo = to64(torch.cat([o1, o2]))
+    ref = to64(o)
+    err = max(slice_err(oo[:, h], ref[:, h]) for h in range(4))
+    errs = max(slice_err(to64(fs2)[0, h], to64(fs)[0, h]) for h in range(4))
+    say("  err_o %.3e err_state %.3e" % (err, errs))
+    assert err <= TOL["bf16"] and errs <= TOL["bf16"]
+
+
+def test_varlen_equals_separate_calls():
+    say("case varlen vs separate")
+    lengths = [50, 0, 129, 7]
+    inp = kda_inputs.make_prefill(3, lengths, "bf16", 0.1, False, DEV, seed=14)
+    o, fs = run_prefill(inp)
+    cu = inp["cu_host"].tolist()
+    for n in range(len(lengths)):
+        a, e = cu[n], cu[n + 1]
+        on, fsn = kda.chunk_fwd(inp["q"][a:e], inp["k"][a:e], inp["v"][a:e], inp["log_alpha"][a:e],
+                                inp["beta"][a:e], initial_state=inp["initial_state"][n:n + 1].contiguous())
+        sync()
+        assert torch.equal(fsn[0], fs[n]), n
+        assert torch.equal(on, o[a:e]), n
+
+
+def test_poison_and_guard_bands():
+    """Outputs pre-filled with NaN must be fully overwritten; guard regions
+    around every output must stay untouched."""
+    say("case poison + guard bands")
+    H, lengths = 4, [70, 1, 45]
+    inp = kda_inputs.make_prefill(H, lengths, "bf16", 0.02, False, DEV, seed=15)
+    T, N = sum(lengths), len(lengths)
+    G = 4096
+    o_buf = torch.full((G + T * H * 128 + G,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    f_buf = torch.full((G + N * H * 128 * 128 + G,), float("nan"), dtype=torch.float32, device=DEV)
+    o_buf[:G] = 7.0
+    o_buf[-G:] = 7.0
+    f_buf[:G] = 7.0
+    f_buf[-G:] = 7.0
+    o = o_buf[G:G + T * H * 128].view(T, H, 128)
+    fs = f_buf[G:G + N * H * 128 * 128].view(N, H, 128, 128)
+    kw = library_inputs(inp)
+    kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], out=o, final_state=fs, **kw)
+    sync()
+    assert not torch.isnan(o.float()).any() and not torch.isnan(fs).any()
+    assert (o_buf[:G] == 7.0).all() and (o_buf[-G:] == 7.0).all()
+    assert (f_buf[:G] == 7.0).all() and (f_buf[-G:] == 7.0).all()
+
+
+def test_linear_in_q():
+    """o is linear in q (no hidden scale): scaling q by 0.5 halves o exactly in
+    exact arithmetic; the bf16 path agrees within its bar."""
+    say("case linear in q")
+    inp = kda_inputs.make_prefill(2, [90], "f32", 0.1, False, DEV, seed=16)
+    o1, _ = run_prefill(inp)
+    inp["q"] = inp["q"] * 0.5
+    o2, _ = run_prefill(inp)
+    a, b = to64(o1), to64(o2)
+    assert slice_err(2 * b, a) < 1e-5
+
+
+def test_api_errors_on_device():
+    inp = kda_inputs.make_prefill(2, [10, 5], "bf16", 0.0, False, DEV, seed=17)
+    with pytest.raises(kda.KDAError):
+        # output overlapping an input
+        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], cu_seqlens=inp["cu_seqlens"],
+                      out=inp["q"])
+
+
+# ---------------------------------------------------------------------------
+# Decode
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_parity_multistep(dtype):
+    N, H, steps = 3, 5, 8
+    say("case decode dtype=%s" % dtype)
+    inp = kda_inputs.make_decode(N, H, steps, dtype, 0.02, DEV, seed=21)
+    state = inp["state"].clone()
+    ref_state = to64(inp["state"]).copy()
+    worst = 0.0
+    for s in range(steps):
+        o = kda.decode_step(state, inp["q"][s], inp["k"][s], inp["v"][s], inp["log_alpha"][s], inp["beta"][s])
+        sync()
+        o_ref = oracle.decode_step(ref_state, to64(inp["q"][s]), to64(inp["k"][s]), to64(inp["v"][s]),
+                                   to64(inp["log_alpha"][s]), to64(inp["beta"][s]))
+        y = to64(o)
+        for n in range(N):
+            for h in range(H):
+                worst = max(worst, slice_err(y[n, h], o_ref[n, h]))
+    st = to64(state)
+    for n in range(N):
+        for h in range(H):
+            worst = max(worst, slice_err(st[n, h], ref_state[n, h]))
+    say("  worst %.3e" % worst)
+    assert worst <= TOL[dtype]
+
+
+def test_decode_steps_equal_prefill():
+    """Decoding token by token equals one prefill over the same tokens."""
+    say("case decode == prefill")
+    N, H, steps = 2, 3, 64
+    inp = kda_inputs.make_decode(N, H, steps, "f32", 0.02, DEV, seed=22)
+    state = inp["state"].clone()
+    outs = []
+    for s in range(steps):
+        outs.append(kda.decode_step(state, inp["q"][s], inp["k"][s], inp["v"][s], inp["log_alpha"][s],
+                                    inp["beta"][s]))
+    # the same tokens as a packed prefill: sequence n = tokens (s, n) for s in order
+    perm = lambda x: x.transpose(0, 1).reshape(N * steps, *x.shape[2:]).contiguous()
+    cu = torch.arange(0, N * steps + 1, steps, dtype=torch.int32, device=DEV)
+    o_pf, fs_pf = kda.chunk_fwd(perm(inp["q"]), perm(inp["k"]), perm(inp["v"]), perm(inp["log_alpha"]),
+                                perm(inp["beta"]), initial_state=inp["state"], cu_seqlens=cu)
+    sync()
+    o_dec = perm(torch.stack(outs))
+    err = max(slice_err(to64(o_dec)[:, h], to64(o_pf)[:, h]) for h in range(H))
+    errs = max(slice_err(to64(state)[n, h], to64(fs_pf)[n, h]) for n in range(N) for h in range(H))
+    say("  err_o %.3e err_state %.3e" % (err, errs))
+    assert err <= TOL["f32"] and errs <= TOL["f32"]
+
+
+def test_decode_guard_and_aliasing_errors():
+    N, H = 2, 2
+    inp = kda_inputs.make_decode(N, H, 1, "bf16", 0.02, DEV, seed=23)
+    with pytest.raises(kda.KDAError):
+        kda.decode_step(inp["state"], inp["q"][0], inp["k"][0], inp["v"][0], inp["log_alpha"][0], inp["beta"][0],
+                        out=inp["q"][0])
