@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-decode", action="store_true", help="time only the decode workload (profiling)")
+    ap.add_argument("--only-prefill", action="store_true", help="time only the prefill workload (profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -112,6 +115,16 @@ def main():
     stream = torch.cuda.current_stream(dev)
     w = kda_inputs.WORKLOADS[args.workload]
     result = {}
+    if args.only_prefill:
+        args.no_decode = True
+        args.no_cpu_baseline = True
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = src.numel() * 4
+        del src, dst
 
     if not args.only_decode:
         inp = kda_inputs.make_workload(args.workload, device=dev)

@@ -52,6 +52,10 @@ size_t elem_size(kda_dtype dt) { return dt == KDA_DTYPE_BF16 ? 2 : 4; }
 
 bool dtype_ok(kda_dtype dt) { return dt == KDA_DTYPE_F32 || dt == KDA_DTYPE_BF16; }
 
+// q, k, v, log_alpha, gate, o and the states move as 16-byte vectors; the
+// rest (beta, cu_seqlens, conv and norm weights, workspace) are read as scalars.
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
 }  // namespace
 
 extern "C" {
@@ -91,6 +95,14 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   const kda_fused_opts none = {nullptr, nullptr, nullptr, nullptr, 1e-6f, 1e-6f};
   const kda_fused_opts& f = opts ? *opts : none;
   if (!(f.l2_eps >= 0.f) || !(f.rms_eps >= 0.f)) return KDA_ERR_INVALID_ARG;
+  {
+    const void* vec[] = {q, k, v, log_alpha, initial_state, o, final_state, f.gate};
+    for (const void* ptr : vec)
+      if (!aligned(ptr, 16)) return KDA_ERR_INVALID_ARG;
+    const void* sca[] = {beta, cu_seqlens, f.conv_q_w, f.conv_k_w, f.norm_w, workspace};
+    for (const void* ptr : sca)
+      if (!aligned(ptr, 4)) return KDA_ERR_INVALID_ARG;
+  }
 
   const size_t need = kda_chunk_fwd_workspace_bytes(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, opts);
   if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
@@ -158,6 +170,12 @@ kda_status kda_decode_step(float* state, const void* q, const void* k, const voi
   if (num_seqs < 1 || num_heads < 1) return KDA_ERR_INVALID_ARG;
   if (d_k != kD || d_v != kD || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
   if (!state || !q || !k || !v || !log_alpha || !beta || !o) return KDA_ERR_INVALID_ARG;
+  {
+    if (!aligned(state, 16)) return KDA_ERR_INVALID_ARG;
+    const void* sca[] = {q, k, v, log_alpha, beta, o};
+    for (const void* ptr : sca)
+      if (!aligned(ptr, dtype == KDA_DTYPE_BF16 ? 2 : 4)) return KDA_ERR_INVALID_ARG;
+  }
   const int64_t units = (int64_t)num_seqs * num_heads;
   if (units > (int64_t)INT32_MAX) return KDA_ERR_INVALID_ARG;
   const size_t es = elem_size(dtype);

@@ -24,6 +24,8 @@ namespace kda {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;  // d_k = d_v
@@ -150,6 +152,51 @@ __device__ __forceinline__ void frag_split(Frag<__bf16>& hi, Frag<__bf16>& lo, c
     hi.v[j] = h;
     lo.v[j] = (__bf16)(x[j] - (float)h);
   }
+}
+
+}  // namespace kda
+
+namespace kda {
+
+// 16-deep contraction steps (v_mfma_f32_16x16x16_bf16 / four v_mfma_f32_16x16x4_f32):
+// lane (row or column l % 16, group g) carries contraction indices 4g .. 4g+3,
+// which is exactly the row set of one output tile held by that lane.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <typename E>
+struct Frag16;
+template <>
+struct Frag16<__bf16> {
+  bf16x4 v;
+};
+template <>
+struct Frag16<float> {
+  f32x4 v;
+};
+
+__device__ __forceinline__ void ld_frag16(Frag16<__bf16>& f, const __bf16* p) {
+  f.v = *reinterpret_cast<const bf16x4*>(p);
+}
+__device__ __forceinline__ void ld_frag16(Frag16<float>& f, const float* p) {
+  f.v = *reinterpret_cast<const f32x4*>(p);
+}
+__device__ __forceinline__ void frag16_from_acc(Frag16<__bf16>& f, f32x4 x) {
+  f.v = (bf16x4){(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+}
+__device__ __forceinline__ void frag16_from_acc(Frag16<float>& f, f32x4 x) { f.v = x; }
+__device__ __forceinline__ f32x4 frag16_to_f32(const Frag16<__bf16>& f) {
+  return (f32x4){(float)f.v[0], (float)f.v[1], (float)f.v[2], (float)f.v[3]};
+}
+__device__ __forceinline__ f32x4 frag16_to_f32(const Frag16<float>& f) { return f.v; }
+
+__device__ __forceinline__ f32x4 mma16(f32x4 acc, const Frag16<__bf16>& a, const Frag16<__bf16>& b) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a.v), __builtin_bit_cast(s16x4, b.v),
+                                                    acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(f32x4 acc, const Frag16<float>& a, const Frag16<float>& b) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+  return acc;
 }
 
 }  // namespace kda

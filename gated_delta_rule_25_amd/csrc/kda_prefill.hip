@@ -50,13 +50,13 @@ struct PrefillLayout {
   static constexpr int NOFF = NT * (NT - 1) / 2;  // strictly-lower tile pairs
   static constexpr int PAD = 16 / (int)sizeof(E);
   static constexpr int LDK = D + PAD;   // token-major [C][D] operand tiles
-  static constexpr int LDT = C + PAD;   // channel-major [D][C] / [DV][C] tiles, and [C][C] tiles
-  static constexpr int LDA = C + 1;     // [C][C] fp32 work tiles
+  // channel-major [D][C] / [DV][C] tiles and the [C][C] tiles; rows stay
+  // 16-byte aligned for the 16-byte operand reads
+  static constexpr int LDT = C + PAD;
   static constexpr size_t TOK = (size_t)C * LDK * sizeof(E);
   static constexpr size_t CHM = (size_t)D * LDT * sizeof(E);
   static constexpr size_t VTB = (size_t)DV * LDT * sizeof(E);
   static constexpr size_t CCE = (size_t)C * LDT * sizeof(E);
-  static constexpr size_t CCF = (size_t)C * LDA * 4;
   // Region R, during the Gram products: K_rel | K_inv (hi) | [K_inv lo] | Q_rel (hi) | [Q_rel lo].
   static constexpr size_t S_KR = 0;
   static constexpr size_t S_KIH = TOK;
@@ -64,31 +64,27 @@ struct PrefillLayout {
   static constexpr size_t S_QRH = (SPLIT ? 3 : 2) * TOK;
   static constexpr size_t S_QRL = 4 * TOK;
   static constexpr size_t R_BYTES = (SPLIT ? 5 : 3) * TOK;
-  // After them, [0, S_QRH) holds P | T | A (later W) | X, and the Q_rel slot is
-  // turned into Qt = Q (.) e^{g} in place.
+  // After them, [0, S_QRH) holds P | M | A_diag | W, and the Q_rel slot is
+  // turned into Qt = Q (.) e^{g} in place.  M holds the blocks of the
+  // triangular solve: -A_ab below the diagonal, (I + A_aa)^{-1} on it.
+  static constexpr size_t ADF = (size_t)NT * 16 * 17 * 4;  // fp32 diagonal blocks of A
   static constexpr size_t R_P = 0;
-  static constexpr size_t R_T = al16(CCE);
-  static constexpr size_t R_A = R_T + al16(CCE);
-  static constexpr size_t R_W = R_A;
-  static constexpr size_t R_X = R_A + al16(CCF);
-  static_assert(cmax(R_X + CCF, R_W + TOK) <= S_QRH, "post-Gram tiles overflow their region");
+  static constexpr size_t R_M = al16(CCE);
+  static constexpr size_t R_AD = R_M + al16(CCE);
+  static constexpr size_t R_W = R_AD + al16(ADF);
+  static_assert(R_W + TOK <= S_QRH, "post-Gram tiles overflow their region");
   static constexpr size_t O_KTT = R_BYTES;
   static constexpr size_t O_KBT = O_KTT + CHM;
   static constexpr size_t O_VT = O_KBT + CHM;
-  static constexpr size_t O_TOT = al16(O_VT + VTB);                 // f32 [NT][D]
-  static constexpr size_t O_EF = O_TOT + (size_t)NT * D * 4;         // f32 [NOFF][D]
+  static constexpr size_t O_TOT = al16(O_VT + VTB);                 // f32 [4][D] per-wave decay totals
+  static constexpr size_t O_EF = O_TOT + (size_t)4 * D * 4;          // f32 [NOFF][D]
   static constexpr size_t O_ERA = O_EF + (size_t)(NOFF > 0 ? NOFF : 1) * D * 4;  // f32 [NT][D]
   static constexpr size_t O_GAM = O_ERA + (size_t)NT * D * 4;        // f32 [D]
   static constexpr size_t O_BETA = O_GAM + (size_t)D * 4;            // f32 [C]
-  static constexpr size_t O_Y = O_BETA + (size_t)C * 4;              // f32 [NT-1][256]
-  static constexpr size_t O_NRM = O_Y + (size_t)(NT > 1 ? NT - 1 : 1) * 256 * 4;  // f32 [2][2][C]
-  static constexpr size_t O_SS = O_NRM + (size_t)4 * C * 4;          // f32 [4][C]
+  static constexpr size_t O_SS = O_BETA + (size_t)C * 4;             // f32 [4][C]
   static constexpr size_t BYTES = O_SS + (size_t)4 * C * 4;
 };
 
-// Tile pairs (a, b <= a) in the order (0,0) (1,0) (1,1) (2,0) ...
-__device__ __forceinline__ int pair_a(int p) { return p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3; }
-__device__ __forceinline__ int pair_b(int p) { const int a = pair_a(p); return p - a * (a + 1) / 2; }
 // Strictly-lower pairs (a, b < a) in the order (1,0) (2,0) (2,1) (3,0) ...
 __device__ __forceinline__ int off_a(int q) { return q < 1 ? 1 : q < 3 ? 2 : 3; }
 __device__ __forceinline__ int off_b(int q) { const int a = off_a(q); return q - a * (a - 1) / 2; }
@@ -120,39 +116,105 @@ __device__ __forceinline__ float butterfly_sum(float* x, int lane) {
   return r;
 }
 
-// Rows r0 .. r0+N-1 of a chunk (row stride rs elements) as fp32.  Rows at or
-// past nv read row nv-1 instead and are then zeroed, so the loads carry no
-// branches and are issued back to back.
-template <typename T, int N>
-__device__ __forceinline__ void load_rows(float* dst, const T* cbase, int64_t rs, int r0, int nv) {
-  T raw[N];
+// 8 consecutive channels of one row as fp32 (16-byte aligned for bf16, 32 for fp32).
+__device__ __forceinline__ void ld8(float* x, const __bf16* p) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
 #pragma unroll
-  for (int i = 0; i < N; ++i) raw[i] = cbase[(int64_t)min(r0 + i, nv - 1) * rs];
+  for (int j = 0; j < 8; ++j) x[j] = (float)v[j];
+}
+__device__ __forceinline__ void ld8(float* x, const float* p) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
 #pragma unroll
-  for (int i = 0; i < N; ++i) dst[i] = (r0 + i < nv) ? to_f32(raw[i]) : 0.f;
+  for (int j = 0; j < 4; ++j) {
+    x[j] = a[j];
+    x[j + 4] = b[j];
+  }
+}
+__device__ __forceinline__ void st8(__bf16* p, const float* x) {
+  Frag<__bf16> f;
+  frag_from_f32(f, x);
+  st_frag(p, f);
+}
+__device__ __forceinline__ void st8(float* p, const float* x) {
+  Frag<float> f;
+  frag_from_f32(f, x);
+  st_frag(p, f);
+}
+// 8 values and their bf16 residuals (x - hi); plain copy for fp32 operands.
+__device__ __forceinline__ void st8_split(__bf16* phi, __bf16* plo, const float* x) {
+  Frag<__bf16> hi, lo;
+  frag_split(hi, lo, x);
+  st_frag(phi, hi);
+  st_frag(plo, lo);
+}
+__device__ __forceinline__ void st8_split(float* phi, float*, const float* x) { st8(phi, x); }
+// N consecutive elements (N = 1, 2 or 4) of a channel-major row.
+template <int N>
+__device__ __forceinline__ void stN(__bf16* p, const float* x) {
+  if constexpr (N == 1) {
+    p[0] = (__bf16)x[0];
+  } else if constexpr (N == 2) {
+    *reinterpret_cast<uint32_t*>(p) = __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)x[0], (__bf16)x[1]});
+  } else {
+    *reinterpret_cast<bf16x4*>(p) = (bf16x4){(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+  }
+}
+template <int N>
+__device__ __forceinline__ void stN(float* p, const float* x) {
+  if constexpr (N == 1) {
+    p[0] = x[0];
+  } else if constexpr (N == 2) {
+    *reinterpret_cast<f32x2*>(p) = (f32x2){x[0], x[1]};
+  } else {
+    *reinterpret_cast<f32x4*>(p) = (f32x4){x[0], x[1], x[2], x[3]};
+  }
 }
 
-// Prologue for rows r0 .. r0+N-1: causal depthwise conv (4 taps; zero history
-// before the sequence start, chunk row `lo` = max(-3, bos - t0)) and SiLU.
+// Rows r0 .. r0+N-1 of a chunk, 8 channels each; rows at or past nv read row
+// nv-1 instead and are zeroed, so the loads carry no branches.
 template <typename T, int N>
-__device__ __forceinline__ void load_conv_silu(float* dst, const T* cbase, int64_t rs, int r0, int nv, int lo,
-                                               const float* w) {
-  T raw[N + 3];
+__device__ __forceinline__ void load_rows8(float (*dst)[8], const T* cbase, int64_t rs, int r0, int nv) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) ld8(dst[i], cbase + (int64_t)min(r0 + i, nv - 1) * rs);
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (r0 + i >= nv)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dst[i][j] = 0.f;
+}
+
+// Prologue for rows r0 .. r0+N-1, 8 channels: causal depthwise conv (4 taps,
+// zero history before the sequence start = chunk row `lo`), SiLU, then L2
+// normalisation over the 128 channels of the head, which are spread over the
+// 16 lanes of this lane's group.
+template <typename T, int N>
+__device__ __forceinline__ void load_prologue8(float (*dst)[8], const T* cbase, int64_t rs, int r0, int nv, int lo,
+                                               const float (*w)[4], float eps) {
+  float x[N + 3][8];
 #pragma unroll
   for (int i = 0; i < N + 3; ++i) {
     const int row = r0 - 3 + i;
-    raw[i] = cbase[(int64_t)min(max(row, lo), nv - 1) * rs];
-  }
-  float x[N + 3];
+    ld8(x[i], cbase + (int64_t)min(max(row, lo), nv - 1) * rs);
+    if (row < lo || row >= nv)
 #pragma unroll
-  for (int i = 0; i < N + 3; ++i) {
-    const int row = r0 - 3 + i;
-    x[i] = (row >= lo && row < nv) ? to_f32(raw[i]) : 0.f;
+      for (int j = 0; j < 8; ++j) x[i][j] = 0.f;
   }
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const float c = w[0] * x[i] + w[1] * x[i + 1] + w[2] * x[i + 2] + w[3] * x[i + 3];
-    dst[i] = c * sigmoidf_fast(c);
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float c = w[j][0] * x[i][j] + w[j][1] * x[i + 1][j] + w[j][2] * x[i + 2][j] + w[j][3] * x[i + 3][j];
+      const float sv = c * sigmoidf_fast(c);
+      dst[i][j] = sv;
+      ss += sv * sv;
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) ss += __shfl_xor(ss, m);
+    const float inv = rsqrtf(ss + eps);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dst[i][j] *= inv;
   }
 }
 
@@ -162,11 +224,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
   constexpr bool SPLIT = L::SPLIT;
   constexpr int NT = C / 16;     // 16-token tiles per chunk
   constexpr int KT = C / 32;     // 32-deep token steps per chunk
-  constexpr int HALF = C / 2;    // tokens per prep thread
-  constexpr int HT = HALF / 16;  // tiles per prep thread
   constexpr int NCW = DV / 4;    // value columns per wave
   constexpr int NCT = NCW / 16;  // 16-wide column tiles per wave
-  constexpr int LDK = L::LDK, LDT = L::LDT, LDA = L::LDA;
+  constexpr int LDK = L::LDK, LDT = L::LDT;
   static_assert(!EPI || DV == D, "the epilogue normalises whole heads");
   static_assert(NCT >= 1 && KT >= 1 && NT <= 4, "unsupported tile shape");
 
@@ -177,20 +237,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
   E* sQrh = reinterpret_cast<E*>(smem + L::S_QRH);   // Q_rel, then Qt in place
   E* sQrl = reinterpret_cast<E*>(smem + L::S_QRL);   // used only when SPLIT
   E* sP = reinterpret_cast<E*>(smem + L::R_P);
-  E* sT = reinterpret_cast<E*>(smem + L::R_T);
-  float* sA = reinterpret_cast<float*>(smem + L::R_A);
-  float* sX = reinterpret_cast<float*>(smem + L::R_X);
+  E* sM = reinterpret_cast<E*>(smem + L::R_M);
+  float* sAd = reinterpret_cast<float*>(smem + L::R_AD);
   E* sW = reinterpret_cast<E*>(smem + L::R_W);
-  E* sKtt = reinterpret_cast<E*>(smem + L::O_KTT);
+  E* sKtt = reinterpret_cast<E*>(smem + L::O_KTT);   // beta * Kt, channel-major
   E* sKbt = reinterpret_cast<E*>(smem + L::O_KBT);
-  E* sVt = reinterpret_cast<E*>(smem + L::O_VT);
+  E* sVt = reinterpret_cast<E*>(smem + L::O_VT);     // beta * V, column-major
   float* sTot = reinterpret_cast<float*>(smem + L::O_TOT);
   float* sEf = reinterpret_cast<float*>(smem + L::O_EF);
   float* sEra = reinterpret_cast<float*>(smem + L::O_ERA);
   float* sGam = reinterpret_cast<float*>(smem + L::O_GAM);
   float* sBeta = reinterpret_cast<float*>(smem + L::O_BETA);
-  float* sY = reinterpret_cast<float*>(smem + L::O_Y);
-  float* sNrm = reinterpret_cast<float*>(smem + L::O_NRM);
   float* sSS = reinterpret_cast<float*>(smem + L::O_SS);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
@@ -225,69 +282,90 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
         accS[rt8][ct][i] =
             p.init ? p.init[sbase + (size_t)(16 * rt8 + 4 * g + i) * D + col0 + 16 * ct + l16] : 0.f;
 
-  // Prep role: key channel ch, chunk tokens [rbase, rbase + HALF).
-  const int ch = tid & (D - 1), th = tid >> 7, rbase = th * HALF;
-  float wq[4] = {0.f, 0.f, 0.f, 1.f}, wk[4] = {0.f, 0.f, 0.f, 1.f};
+  // Prep role: channel group cg (channels 8cg .. 8cg+7) and token group tg
+  // (chunk rows TPL*tg .. +TPL-1).  The 16 lanes of a lane group hold one set
+  // of rows across all 128 channels; wave w holds rows 4*TPL*w .. +4*TPL-1,
+  // i.e. one 16-token tile (C = 64) or half of one (C = 32).
+  constexpr int TPL = C / 16;       // rows per prep thread
+  constexpr int WPT = 4 / TPL;      // waves per 16-token tile
+  const int cg = tid & 15, tg = tid >> 4, lg = g;
+  const int c8 = 8 * cg, r0 = TPL * tg;
+  float wq[8][4], wk[8][4];
   if (PRO) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      if (p.conv_q_w) wq[m] = p.conv_q_w[(hoff + ch) * 4 + m];
-      if (p.conv_k_w) wk[m] = p.conv_k_w[(hoff + ch) * 4 + m];
-    }
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        wq[j][m] = p.conv_q_w ? p.conv_q_w[(hoff + c8 + j) * 4 + m] : (m == 3 ? 1.f : 0.f);
+        wk[j][m] = p.conv_k_w ? p.conv_k_w[(hoff + c8 + j) * 4 + m] : (m == 3 ? 1.f : 0.f);
+      }
   }
 
   for (int64_t t0 = bos; t0 < eos; t0 += C) {
     const int nv = (int)((eos - t0) < C ? (eos - t0) : C);
     const int64_t cbase = t0 * rs + hoff;  // element offset of (token t0, head h, channel 0)
 
-    // ---- P1: in-tile inclusive prefix sums of the log-decay ----
-    float dl[HALF];
-    load_rows<float, HALF>(dl, p.log_alpha + cbase + ch, rs, rbase, nv);
-#pragma unroll
-    for (int i = 0; i < HALF; ++i)
-      if (i & 15) dl[i] += dl[i - 1];
-#pragma unroll
-    for (int j = 0; j < HT; ++j) sTot[(rbase / 16 + j) * D + ch] = dl[16 * j + 15];
-
-    // ---- P2: q and k columns (raw, or through conv + SiLU), V^T, beta ----
-    float qv[HALF], kv[HALF];
+    // ---- P1: log-decay prefix sums relative to the first row of this wave ----
+    float dl[TPL][8];
+    load_rows8<float, TPL>(dl, p.log_alpha + cbase + c8, rs, r0, nv);
     {
-      const E* qs = gq + cbase + ch;
-      const E* ks = gk + cbase + ch;
+#pragma unroll
+      for (int i = 1; i < TPL; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dl[i][j] += dl[i - 1][j];
+      // exclusive prefix over the four lane groups (same channels, earlier rows)
+      float inc[8], tot[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        tot[j] = dl[TPL - 1][j];
+        float x = tot[j];
+        const float y1 = __shfl_up(x, 16);
+        if (lg >= 1) x += y1;
+        const float y2 = __shfl_up(x, 32);
+        if (lg >= 2) x += y2;
+        inc[j] = x;
+      }
+#pragma unroll
+      for (int i = 0; i < TPL; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dl[i][j] += inc[j] - tot[j];
+      if (lg == 3) st8(sTot + wv * D + c8, inc);  // total of this wave's rows
+    }
+
+    // ---- P2: q and k rows (raw, or through the prologue), V^T, beta ----
+    float qv[TPL][8], kv[TPL][8];
+    {
+      const E* qs = gq + cbase + c8;
+      const E* ks = gk + cbase + c8;
       if (PRO) {
         const int64_t back = bos - t0;  // <= 0
         const int lo = back < -3 ? -3 : (int)back;
-        const int qh = wv & 1;  // which 64-channel half of the head this wave holds
-        if (p.conv_q_w) {
-          load_conv_silu<E, HALF>(qv, qs, rs, rbase, nv, lo, wq);
-          float sq[HALF];
-#pragma unroll
-          for (int i = 0; i < HALF; ++i) sq[i] = qv[i] * qv[i];
-          const float r = butterfly_sum<HALF>(sq, lane);
-          if ((lane % (64 / HALF)) == 0) sNrm[(0 * 2 + qh) * C + rbase + (lane / (64 / HALF)) % HALF] = r;
-        } else {
-          load_rows<E, HALF>(qv, qs, rs, rbase, nv);
-        }
-        if (p.conv_k_w) {
-          load_conv_silu<E, HALF>(kv, ks, rs, rbase, nv, lo, wk);
-          float sk[HALF];
-#pragma unroll
-          for (int i = 0; i < HALF; ++i) sk[i] = kv[i] * kv[i];
-          const float r = butterfly_sum<HALF>(sk, lane);
-          if ((lane % (64 / HALF)) == 0) sNrm[(1 * 2 + qh) * C + rbase + (lane / (64 / HALF)) % HALF] = r;
-        } else {
-          load_rows<E, HALF>(kv, ks, rs, rbase, nv);
-        }
+        if (p.conv_q_w)
+          load_prologue8<E, TPL>(qv, qs, rs, r0, nv, lo, wq, p.l2_eps);
+        else
+          load_rows8<E, TPL>(qv, qs, rs, r0, nv);
+        if (p.conv_k_w)
+          load_prologue8<E, TPL>(kv, ks, rs, r0, nv, lo, wk, p.l2_eps);
+        else
+          load_rows8<E, TPL>(kv, ks, rs, r0, nv);
       } else {
-        load_rows<E, HALF>(qv, qs, rs, rbase, nv);
-        load_rows<E, HALF>(kv, ks, rs, rbase, nv);
+        load_rows8<E, TPL>(qv, qs, rs, r0, nv);
+        load_rows8<E, TPL>(kv, ks, rs, r0, nv);
       }
-      constexpr int VPARTS = 256 / DV, VTOK = C / VPARTS;
-      const int vc = tid % DV, vp = tid / DV;
-      float vv[VTOK];
-      load_rows<E, VTOK>(vv, gv + cbase + cb * DV + vc, rs, vp * VTOK, nv);
+      // V^T: thread (vcg, vtg) moves columns 8 vcg .. +7 of rows VTPL*vtg .. +VTPL-1
+      constexpr int VCG = DV / 8, VTPL = C * VCG / 256;
+      const int vcg = tid % VCG, vtg = tid / VCG;
+      float vv[VTPL][8], vb[VTPL];
+      load_rows8<E, VTPL>(vv, gv + cbase + cb * DV + 8 * vcg, rs, VTPL * vtg, nv);
 #pragma unroll
-      for (int i = 0; i < VTOK; ++i) sVt[vc * LDT + vp * VTOK + i] = from_f32<E>(vv[i]);
+      for (int i = 0; i < VTPL; ++i) vb[i] = p.beta[(t0 + min(VTPL * vtg + i, nv - 1)) * H + h];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float col[VTPL];
+#pragma unroll
+        for (int i = 0; i < VTPL; ++i) col[i] = vv[i][j] * vb[i];   // rows past nv are already zero
+        stN<VTPL>(sVt + (8 * vcg + j) * LDT + VTPL * vtg, col);
+      }
       if (tid < C) {
         const float bb = p.beta[(t0 + min(tid, nv - 1)) * H + h];
         sBeta[tid] = (tid < nv) ? bb : 0.f;
@@ -297,78 +375,121 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
 
     // ---- P3: scaled operand tiles ----
     {
-      float rho[NT + 1];
-      rho[0] = 0.f;
+      // rho_a = cumulative log-decay before tile a, for this thread's 8 channels
+      float wt[4][8];
 #pragma unroll
-      for (int a = 0; a < NT; ++a) rho[a + 1] = rho[a] + sTot[a * D + ch];
-      const float gn = rho[NT];
-      float iq[HALF], ik[HALF];
+      for (int w = 0; w < 4; ++w) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(sTot + w * D + c8);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(sTot + w * D + c8 + 4);
 #pragma unroll
-      for (int i = 0; i < HALF; ++i) {
-        iq[i] = 1.f;
-        ik[i] = 1.f;
-      }
-      if (PRO) {
-#pragma unroll
-        for (int i = 0; i < HALF; ++i) {
-          const int rr = rbase + i;
-          if (p.conv_q_w) iq[i] = rsqrtf(sNrm[0 * C + rr] + sNrm[1 * C + rr] + p.l2_eps);
-          if (p.conv_k_w) ik[i] = rsqrtf(sNrm[2 * C + rr] + sNrm[3 * C + rr] + p.l2_eps);
+        for (int j = 0; j < 4; ++j) {
+          wt[w][j] = x0[j];
+          wt[w][j + 4] = x1[j];
         }
       }
+      float rho[NT + 1][8];
 #pragma unroll
-      for (int j = 0; j < HT; ++j) {
-        const int a = rbase / 16 + j;
-        float ra = rho[0];
+      for (int j = 0; j < 8; ++j) rho[0][j] = 0.f;
 #pragma unroll
-        for (int aa = 1; aa < NT; ++aa)
-          if (aa == a) ra = rho[aa];
-        const float ea = __expf(ra);       // e^{rho_a} <= 1
-        const float eb = __expf(gn - ra);  // e^{g_n - rho_a} <= 1
+      for (int a = 0; a < NT; ++a)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int idx = 16 * j + i, rr = rbase + idx;
-          const float qn = qv[idx] * iq[idx], kn = kv[idx] * ik[idx];
-          const float ep = __expf(dl[idx]);   // e^{g_r - rho_a}  in (e^-80, 1]
-          const float en = __expf(-dl[idx]);  // e^{rho_a - g_r}  in [1, e^80)
-          const float xq = qn * ep, xk = kn * ep, xi = kn * en;
-          const E qhi = from_f32<E>(xq), ihi = from_f32<E>(xi);
-          sQrh[rr * LDK + ch] = qhi;
-          sKih[rr * LDK + ch] = ihi;
-          if constexpr (SPLIT) {
-            sQrl[rr * LDK + ch] = from_f32<E>(xq - to_f32(qhi));
-            sKil[rr * LDK + ch] = from_f32<E>(xi - to_f32(ihi));
-          }
-          sKrel[rr * LDK + ch] = from_f32<E>(xk);
-          sKtt[ch * LDT + rr] = from_f32<E>(xk * ea);   // Kt = K e^{g}
-          sKbt[ch * LDT + rr] = from_f32<E>(xi * eb);   // Kb = K e^{g_n - g}
+        for (int j = 0; j < 8; ++j) {
+          float t = 0.f;
+#pragma unroll
+          for (int w = a * WPT; w < (a + 1) * WPT; ++w) t += wt[w][j];
+          rho[a + 1][j] = rho[a][j] + t;
         }
-      }
-      if (th == 0) {
-        sGam[ch] = __expf(gn);
+      const int my_a = wv / WPT;
+      float ra[8], intra[8];
 #pragma unroll
-        for (int a = 0; a < NT; ++a) sEra[a * D + ch] = __expf(rho[a]);
+      for (int j = 0; j < 8; ++j) {
+        ra[j] = rho[0][j];
+        intra[j] = 0.f;
+      }
+#pragma unroll
+      for (int a = 1; a < NT; ++a)
+        if (a == my_a)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ra[j] = rho[a][j];
+      if (WPT == 2 && (wv & 1))
+#pragma unroll
+        for (int j = 0; j < 8; ++j) intra[j] = wt[wv - 1][j];
+      float ea[8], eb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        ea[j] = __expf(ra[j]);                  // e^{rho_a} <= 1
+        eb[j] = __expf(rho[NT][j] - ra[j]);     // e^{g_n - rho_a} <= 1
+      }
+      float ktt[8][TPL], kbt[8][TPL];
+#pragma unroll
+      for (int i = 0; i < TPL; ++i) {
+        const int rr = r0 + i;
+        const float br = sBeta[rr];
+        float xq[8], xk[8], xi[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float d = dl[i][j] + intra[j];   // g_r - rho_a, in [-80, 0]
+          const float ep = __expf(d), en = __expf(-d);
+          xq[j] = qv[i][j] * ep;
+          xk[j] = kv[i][j] * ep;
+          xi[j] = kv[i][j] * en;
+          ktt[j][i] = xk[j] * ea[j] * br;   // beta Kt = beta K e^{g}
+          kbt[j][i] = xi[j] * eb[j];   // Kb = K e^{g_n - g}
+        }
+        st8_split(sQrh + rr * LDK + c8, sQrl + rr * LDK + c8, xq);
+        st8_split(sKih + rr * LDK + c8, sKil + rr * LDK + c8, xi);
+        st8(sKrel + rr * LDK + c8, xk);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        stN<TPL>(sKtt + (c8 + j) * LDT + r0, ktt[j]);
+        stN<TPL>(sKbt + (c8 + j) * LDT + r0, kbt[j]);
+      }
+      if (tg == 0) {
+        float v8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v8[j] = __expf(rho[NT][j]);
+        st8(sGam + c8, v8);
+#pragma unroll
+        for (int a = 0; a < NT; ++a) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v8[j] = __expf(rho[a][j]);
+          st8(sEra + a * D + c8, v8);
+        }
 #pragma unroll
         for (int a = 1; a < NT; ++a)
 #pragma unroll
-          for (int b = 0; b < a; ++b) sEf[off_idx(a, b) * D + ch] = __expf(rho[a] - rho[b]);
+          for (int b = 0; b < a; ++b) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v8[j] = __expf(rho[a][j] - rho[b][j]);
+            st8(sEf + off_idx(a, b) * D + c8, v8);
+          }
       }
     }
     __syncthreads();
 
-    // ---- P5: Gram tiles per tile pair (a, b <= a), pair p on wave p % 4:
-    //      A_ab = K_rel_a Kh_ab^T (bf16),  P_ab = Q_rel_a Kh_ab^T (hi/lo when SPLIT)
+    // ---- P5: Gram tiles per 16-token tile pair (a, b <= a):
+    //      A_ab = Krel_a Kh_ab^T,  P_ab = Qrel_a Kh_ab^T  with Kh_ab = K_inv_b (.) e^{rho_a - rho_b}.
+    //      Wave w takes the diagonal pair (w, w) and the strictly-lower pairs q = w, w + 4.
+    //      With bf16 operands P is formed from the hi + lo parts of Q_rel, and of
+    //      K_inv on the diagonal (where it is not rescaled).
     {
-      constexpr int NPAIR = NT * (NT + 1) / 2;
-      constexpr int PPW = (NPAIR + 3) / 4;
+      constexpr int NOFF = L::NOFF;
+      constexpr int PPW = 1 + (NOFF + 3) / 4;  // pairs per wave (first one diagonal)
       f32x4 ga[PPW], gp[PPW];
+      int pa[PPW], pb[PPW];
 #pragma unroll
       for (int j = 0; j < PPW; ++j) {
         ga[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
         gp[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        const int pr = wv + 4 * j;
-        if (pr < NPAIR) {
-          const int a = pair_a(pr), b = pair_b(pr);
+        const int q = wv + 4 * (j - 1);
+        const bool valid = (j == 0) ? (wv < NT) : (q < NOFF);
+        pa[j] = -1;
+        pb[j] = -1;
+        if (valid) {
+          const int a = (j == 0) ? wv : off_a(q), b = (j == 0) ? wv : off_b(q);
+          pa[j] = a;
+          pb[j] = b;
           const int arow = (16 * a + l16) * LDK + 8 * g, brow = (16 * b + l16) * LDK + 8 * g;
           const float* ef = sEf + (b < a ? off_idx(a, b) : 0) * D + 8 * g;
 #pragma unroll
@@ -377,32 +498,24 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
             ld_frag(fk, sKrel + arow + 32 * s);
             ld_frag(fq, sQrh + arow + 32 * s);
             ld_frag(fbh, sKih + brow + 32 * s);
+            if (b < a) {
+              float x[8];
+              frag_unpack(fbh, x);
+#pragma unroll
+              for (int jj = 0; jj < 8; ++jj) x[jj] *= ef[32 * s + jj];
+              frag_from_f32(fbh, x);
+            }
+            ga[j] = mma(ga[j], fk, fbh);
+            gp[j] = mma(gp[j], fq, fbh);
             if constexpr (SPLIT) {
-              Frag<E> fql, fbl;
+              Frag<E> fql;
               ld_frag(fql, sQrl + arow + 32 * s);
-              ld_frag(fbl, sKil + brow + 32 * s);
-              if (b < a) {
-                float hv[8], lv[8], x[8];
-                frag_unpack(fbh, hv);
-                frag_unpack(fbl, lv);
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) x[jj] = (hv[jj] + lv[jj]) * ef[32 * s + jj];
-                frag_split(fbh, fbl, x);
-              }
-              ga[j] = mma(ga[j], fk, fbh);
-              gp[j] = mma(gp[j], fq, fbh);
-              gp[j] = mma(gp[j], fq, fbl);
               gp[j] = mma(gp[j], fql, fbh);
-            } else {
-              if (b < a) {
-                float x[8];
-                frag_unpack(fbh, x);
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) x[jj] *= ef[32 * s + jj];
-                frag_from_f32(fbh, x);
+              if (b == a) {
+                Frag<E> fbl;
+                ld_frag(fbl, sKil + brow + 32 * s);
+                gp[j] = mma(gp[j], fq, fbl);
               }
-              ga[j] = mma(ga[j], fk, fbh);
-              gp[j] = mma(gp[j], fq, fbh);
             }
           }
         }
@@ -410,20 +523,24 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
       __syncthreads();  // every wave is done reading the Gram operands
 #pragma unroll
       for (int j = 0; j < PPW; ++j) {
-        const int pr = wv + 4 * j;
-        if (pr < NPAIR) {
-          const int a = pair_a(pr), b = pair_b(pr);
+        const int a = pa[j], b = pb[j];
+        if (a >= 0) {
           const int c = 16 * b + l16;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 16 * a + 4 * g + i;
-            sA[r * LDA + c] = ((b < a) || (c < r)) ? ga[j][i] * sBeta[r] : 0.f;
+            const float av = ga[j][i] * sBeta[r];   // row r of Diag(beta) Kt Kh^T
+            if (b == a) {
+              sAd[(a * 16 + 4 * g + i) * 17 + l16] = (c < r) ? av : 0.f;
+            } else {
+              sM[r * LDT + c] = from_f32<E>(-av);
+            }
             sP[r * LDT + c] = from_f32<E>(((b < a) || (c <= r)) ? gp[j][i] : 0.f);
           }
         }
       }
       // strictly-upper tiles of P are read by the 32-deep token steps: zero them
-      for (int e = tid; e < L::NOFF * 256; e += 256) {
+      for (int e = tid; e < NOFF * 256; e += 256) {
         const int q = e >> 8, a = off_a(q), b = off_b(q);
         sP[(16 * b + ((e >> 4) & 15)) * LDT + 16 * a + (e & 15)] = from_f32<E>(0.f);
       }
@@ -451,87 +568,71 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
     }
     __syncthreads();
 
-    // ---- P6: T = (I + A)^{-1} Diag(beta), blocked by 16-token tiles, fp32 ----
-    if (tid < 16 * NT) {
-      const int a = tid >> 4, j = tid & 15;
+    // ---- P6: (I + A_aa)^{-1} of the diagonal 16x16 blocks, fp32 forward
+    //      substitution; wave a, lane j < 16 solves column j of block a ----
+    if (wv < NT && lane < 16) {
+      const float* ab = sAd + wv * 16 * 17;
       float x[16];
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const float* arow = sA + (16 * a + rr) * LDA + 16 * a;
-        float s = (rr == j) ? 1.f : 0.f;
+      for (int r = 0; r < 16; ++r) {
+        float acc = (r == lane) ? 1.f : 0.f;
 #pragma unroll
-        for (int i = 0; i < rr; ++i) s -= arow[i] * x[i];
-        x[rr] = s;
+        for (int i = 0; i < r; ++i) acc -= ab[r * 17 + i] * x[i];
+        x[r] = acc;
       }
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) sX[(16 * a + rr) * LDA + 16 * a + j] = x[rr];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int dist = 1; dist < NT; ++dist) {
-      const int nb = NT - dist;
-      for (int e = tid; e < nb * 256; e += 256) {
-        const int blk = e >> 8, i = (e >> 4) & 15, jj = e & 15, b = blk, a = blk + dist;
-        float y = 0.f;
-        for (int c = b; c < a; ++c)
-#pragma unroll
-          for (int m = 0; m < 16; ++m) y += sA[(16 * a + i) * LDA + 16 * c + m] * sX[(16 * c + m) * LDA + 16 * b + jj];
-        sY[blk * 256 + i * 16 + jj] = y;
-      }
-      __syncthreads();
-      for (int e = tid; e < nb * 256; e += 256) {
-        const int blk = e >> 8, i = (e >> 4) & 15, jj = e & 15, b = blk, a = blk + dist;
-        float xx = 0.f;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) xx -= sX[(16 * a + i) * LDA + 16 * a + m] * sY[blk * 256 + m * 16 + jj];
-        sX[(16 * a + i) * LDA + 16 * b + jj] = xx;
-      }
-      __syncthreads();
-    }
-    for (int e = tid; e < C * C; e += 256) {
-      const int rr = e / C, cc = e % C;
-      sT[rr * LDT + cc] = from_f32<E>(cc <= rr ? sX[rr * LDA + cc] * sBeta[cc] : 0.f);
+      for (int r = 0; r < 16; ++r) sM[(16 * wv + r) * LDT + 16 * wv + lane] = from_f32<E>(x[r]);
     }
     __syncthreads();
 
-    // ---- P7: W = T Kt  (C x 128), stored token-major for the carried stage ----
-    {
-      constexpr int TPW = 2 * NT;  // tiles per wave: (C/16) * 8 / 4
-#pragma unroll
-      for (int j = 0; j < TPW; ++j) {
-        const int tile = wv * TPW + j, rt = tile >> 3, ct = tile & 7;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const int nks = (16 * rt + 15) / 32 + 1;
-        for (int ks = 0; ks < nks; ++ks) {
-          Frag<E> fa, fb;
-          ld_frag(fa, sT + (16 * rt + l16) * LDT + 32 * ks + 8 * g);
-          ld_frag(fb, sKtt + (16 * ct + l16) * LDT + 32 * ks + 8 * g);
-          acc = mma(acc, fa, fb);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sW[(16 * rt + 4 * g + i) * LDK + 16 * ct + l16] = from_f32<E>(acc[i]);
-      }
-    }
-    // ---- P8: U' = T V for this wave's columns (kept in registers) ----
+    // ---- P7: blocked forward substitution on the matrix cores,
+    //      (I + A) [W | U'] = Diag(beta) [Kt | V], tile row by tile row:
+    //      Y_a = (I + A_aa)^{-1} (beta R_a - sum_{b<a} A_ab Y_b).
+    //      Wave w solves W columns 32w .. 32w+31 and its own U' columns, so
+    //      every Y_b it needs is already in its registers. ----
     f32x4 accU[NT][NCT];
+    {
+      constexpr int NOWN = 2 + NCT;
+      f32x4 Y[NOWN][NT];
+      Frag16<E> Yb[NOWN][NT];
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt) {
+      for (int a = 0; a < NT; ++a) {
+        Frag16<E> xa;
+        ld_frag16(xa, sM + (16 * a + l16) * LDT + 16 * a + 4 * g);
+        f32x4 z[NOWN];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) accU[rt][ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      const int nks = (16 * rt + 15) / 32 + 1;
+        for (int o = 0; o < NOWN; ++o) {
+          const E* src = (o < 2) ? sKtt + (32 * wv + 16 * o + l16) * LDT : sVt + (wv * NCW + 16 * (o - 2) + l16) * LDT;
+          Frag16<E> r;
+          ld_frag16(r, src + 16 * a + 4 * g);
+          z[o] = frag16_to_f32(r);
+        }
 #pragma unroll
-      for (int ks = 0; ks < KT; ++ks) {
-        if (ks < nks) {
-          Frag<E> fa;
-          ld_frag(fa, sT + (16 * rt + l16) * LDT + 32 * ks + 8 * g);
+        for (int b = 0; b < a; ++b) {
+          Frag16<E> mab;
+          ld_frag16(mab, sM + (16 * a + l16) * LDT + 16 * b + 4 * g);
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) {
-            Frag<E> fb;
-            ld_frag(fb, sVt + (wv * NCW + 16 * ct + l16) * LDT + 32 * ks + 8 * g);
-            accU[rt][ct] = mma(accU[rt][ct], fa, fb);
-          }
+          for (int o = 0; o < NOWN; ++o) z[o] = mma16(z[o], mab, Yb[o][b]);
+        }
+#pragma unroll
+        for (int o = 0; o < NOWN; ++o) {
+          Frag16<E> zb;
+          frag16_from_acc(zb, z[o]);
+          Y[o][a] = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, xa, zb);
+          frag16_from_acc(Yb[o][a], Y[o][a]);
         }
       }
+#pragma unroll
+      for (int o = 0; o < 2; ++o)
+#pragma unroll
+        for (int a = 0; a < NT; ++a)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sW[(16 * a + 4 * g + i) * LDK + 32 * wv + 16 * o + l16] = from_f32<E>(Y[o][a][i]);
+#pragma unroll
+      for (int a = 0; a < NT; ++a)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) accU[a][ct] = Y[2 + ct][a];
     }
     __syncthreads();  // W visible to every wave
 

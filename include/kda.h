@@ -18,6 +18,10 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller, who keeps
  *     them alive until the work enqueued on `stream` has completed.  The
  *     library never allocates device memory.
+ *   - Alignment: q, k, v, log_alpha, gate, o and the state tensors of
+ *     kda_chunk_fwd, and the state of kda_decode_step, must be 16-byte
+ *     aligned (they move as 16-byte vectors); every other pointer needs its
+ *     element's alignment.  Violations return KDA_ERR_INVALID_ARG.
  *   - Layouts are dense row-major, token-major: q/k/v/log_alpha/o are
  *     [T_total, H, 128]; beta is [T_total, H]; states are [N, H, 128, 128]
  *     fp32 with S[n][h][i][j], i = key channel (row), j = value channel.

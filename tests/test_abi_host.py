@@ -107,6 +107,9 @@ def test_chunk_validation(lib):
     assert chunk(lib, fs=p(3)) == INVALID                      # final state aliases log_alpha
     assert chunk(lib, s0=p(6), fs=ctypes.c_void_p(BASE + 6 * 64 * MB + 4)) == INVALID  # partial overlap
     assert chunk(lib, N=2, cu=p(7), ws=p(0), wsb=256) == INVALID  # workspace aliases q
+    assert chunk(lib, q=ctypes.c_void_p(BASE + 8)) == INVALID  # not 16-byte aligned
+    assert chunk(lib, fs=ctypes.c_void_p(BASE + 6 * 64 * MB + 4)) == INVALID
+    assert chunk(lib, b=ctypes.c_void_p(BASE + 4 * 64 * MB + 2)) == INVALID  # beta not 4-byte aligned
 
 
 class Opts(ctypes.Structure):
@@ -135,6 +138,8 @@ def test_decode_validation(lib):
     assert decode(lib, s=None) == INVALID
     assert decode(lib, o=p(1)) == INVALID      # output aliases q
     assert decode(lib, s=p(2)) == INVALID      # state aliases k
+    assert decode(lib, s=ctypes.c_void_p(BASE + 8)) == INVALID  # state not 16-byte aligned
+    assert decode(lib, q=ctypes.c_void_p(BASE + 64 * MB + 1)) == INVALID  # not element aligned
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
