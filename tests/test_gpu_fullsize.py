@@ -1,0 +1,112 @@
+"""Parity at the full workload sizes (run with -m gpu on an MI355X).
+
+The library runs the whole workload exactly as bench.py launches it; the fp64
+oracle then recomputes sampled (sequence, head) slices from the same device
+bytes and every output of those slices is compared (metric and bars as in
+tests/kda_testlib.py).  Sizes:
+  - one K3 layer, H=96, T=8192, bf16, S0 ~ 0.02 N(0,1)     (3 heads sampled)
+  - long context, H=96, T=131072                            (1 head sampled)
+  - decode, N=256 x H=96, 64 in-place steps                 (16 (n,h) sampled)
+  - varlen 64 sequences (log-uniform 1K..64K), fused prologue/epilogue
+                                                            (4 (n,h) sampled)
+plus the small fp32 workload H=2, T=256 compared in full.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+import gated_delta_rule_25_amd as kda
+import oracle
+from kda_testlib import TOL, compare_prefill, library_inputs, slice_err, sync, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_workload(wid):
+    inp = kda_inputs.make_workload(wid, device=DEV)
+    sync()
+    o, fs = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], **library_inputs(inp))
+    sync()
+    return inp, o, fs
+
+
+def test_fp32_small_workload_full():
+    say("workload 0: fp32 H=2 T=256, all outputs")
+    inp, o, fs = run_workload(0)
+    eo, es = compare_prefill(inp, o, fs)
+    say("  err_o %.3e err_state %.3e" % (eo, es))
+    assert eo <= TOL["f32"] and es <= TOL["f32"]
+
+
+def test_one_layer_T8192_sampled_heads():
+    say("workload 1: bf16 H=96 T=8192, heads 0, 37, 95")
+    inp, o, fs = run_workload(1)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(fs).all()
+    eo, es = compare_prefill(inp, o, fs, heads=[0, 37, 95])
+    say("  err_o %.3e err_state %.3e" % (eo, es))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    del inp, o, fs
+    torch.cuda.empty_cache()
+
+
+def test_long_context_T131072_sampled_head():
+    say("workload 2: bf16 H=96 T=131072, head 61")
+    inp, o, fs = run_workload(2)
+    eo, es = compare_prefill(inp, o, fs, heads=[61])
+    say("  err_o %.3e err_state %.3e" % (eo, es))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    del inp, o, fs
+    torch.cuda.empty_cache()
+
+
+def test_decode_N256_H96_64_steps_sampled():
+    say("workload 3: decode N=256 H=96, 64 steps, 16 sampled (n, h)")
+    d = kda_inputs.make_workload(3, device=DEV)
+    rng = np.random.default_rng(3)
+    pairs = [(int(rng.integers(256)), int(rng.integers(96))) for _ in range(16)]
+    ns = [p[0] for p in pairs]
+    hs = [p[1] for p in pairs]
+    ref_state = np.ascontiguousarray(np.stack([to64(d["state"][n, h]) for n, h in pairs])[:, None])
+    state = d["state"]
+    worst = 0.0
+    for s in range(64):
+        o = kda.decode_step(state, d["q"][s], d["k"][s], d["v"][s], d["log_alpha"][s], d["beta"][s])
+        sync()
+        sel = lambda t: to64(t[s][ns, hs])[:, None]
+        o_ref = oracle.decode_step(ref_state, sel(d["q"]), sel(d["k"]), sel(d["v"]), sel(d["log_alpha"]),
+                                   to64(d["beta"][s][ns, hs])[:, None])
+        y = to64(o[ns, hs])
+        for j in range(len(pairs)):
+            worst = max(worst, slice_err(y[j], o_ref[j, 0]))
+    st = to64(state[ns, hs])
+    for j in range(len(pairs)):
+        worst = max(worst, slice_err(st[j], ref_state[j, 0]))
+    say("  worst %.3e" % worst)
+    assert worst <= TOL["bf16"]
+    del d, state
+    torch.cuda.empty_cache()
+
+
+def test_varlen_fused_64_sequences_sampled():
+    say("workload 4: varlen 64 sequences, fused prologue/epilogue")
+    inp, o, fs = run_workload(4)
+    lengths = inp["lengths"]
+    longest = int(np.argmax(lengths))
+    shortest = int(np.argmin(lengths))
+    say("  T=%d, longest %d, shortest %d" % (inp["T"], lengths[longest], lengths[shortest]))
+    eo1, es1 = compare_prefill(inp, o, fs, heads=[5], seqs=[longest])
+    eo2, es2 = compare_prefill(inp, o, fs, heads=[90], seqs=[shortest, 0])
+    eo, es = max(eo1, eo2), max(es1, es2)
+    say("  err_o %.3e err_state %.3e" % (eo, es))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    del inp, o, fs
+    torch.cuda.empty_cache()
