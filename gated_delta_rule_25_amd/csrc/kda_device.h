@@ -73,6 +73,17 @@ __device__ __forceinline__ void ld_frag_perm(Frag<float>& f, const float* p) {
   f.hi = *reinterpret_cast<const f32x4*>(p + 16);
 }
 
+// d-permuted index set from two separate 4-element pieces (k0 + 4g and k0 + 16 + 4g).
+__device__ __forceinline__ void ld_frag_pair(Frag<__bf16>& f, const __bf16* lo, const __bf16* hi) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(lo);
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(hi);
+  f.v = (bf16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ void ld_frag_pair(Frag<float>& f, const float* lo, const float* hi) {
+  f.lo = *reinterpret_cast<const f32x4*>(lo);
+  f.hi = *reinterpret_cast<const f32x4*>(hi);
+}
+
 // B operand from two stacked fp32 output tiles held by this lane.
 __device__ __forceinline__ void frag_from_acc(Frag<__bf16>& f, f32x4 x0, f32x4 x1) {
   f.v = (bf16x8){(__bf16)x0[0], (__bf16)x0[1], (__bf16)x0[2], (__bf16)x0[3],
@@ -130,6 +141,10 @@ __device__ __forceinline__ f32x4 mma(f32x4 acc, const Frag<float>& a, const Frag
 }
 
 __device__ __forceinline__ float sigmoidf_fast(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// 2^x with the hardware exp unit (inputs here lie in [-128, 128]; results
+// below the normal range flush toward zero, which is the intended limit).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace kda
 

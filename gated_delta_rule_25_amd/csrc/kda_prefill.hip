@@ -67,7 +67,8 @@ struct PrefillLayout {
   // After them, [0, S_QRH) holds P | M | A_diag | W, and the Q_rel slot is
   // turned into Qt = Q (.) e^{g} in place.  M holds the blocks of the
   // triangular solve: -A_ab below the diagonal, (I + A_aa)^{-1} on it.
-  static constexpr size_t ADF = (size_t)NT * 16 * 17 * 4;  // fp32 diagonal blocks of A
+  static constexpr int AST = 20;  // row stride of the fp32 diagonal blocks (16-byte aligned rows)
+  static constexpr size_t ADF = (size_t)NT * 16 * AST * 4;  // fp32 diagonal blocks of A
   static constexpr size_t R_P = 0;
   static constexpr size_t R_M = al16(CCE);
   static constexpr size_t R_AD = R_M + al16(CCE);
@@ -82,13 +83,29 @@ struct PrefillLayout {
   static constexpr size_t O_GAM = O_ERA + (size_t)NT * D * 4;        // f32 [D]
   static constexpr size_t O_BETA = O_GAM + (size_t)D * 4;            // f32 [C]
   static constexpr size_t O_SS = O_BETA + (size_t)C * 4;             // f32 [4][C]
-  static constexpr size_t BYTES = O_SS + (size_t)4 * C * 4;
+  static constexpr size_t BASE_BYTES = O_SS + (size_t)4 * C * 4;
+  // Qt gets its own tile (written straight from fp32 in the operand stage)
+  // when it fits; otherwise it is formed in place over Q_rel after the Gram.
+  static constexpr bool QT_OWN = BASE_BYTES + TOK <= 160 * 1024;
+  static constexpr size_t O_QT = BASE_BYTES;
+  static constexpr size_t BYTES = BASE_BYTES + (QT_OWN ? TOK : 0);
 };
 
 // Strictly-lower pairs (a, b < a) in the order (1,0) (2,0) (2,1) (3,0) ...
 __device__ __forceinline__ int off_a(int q) { return q < 1 ? 1 : q < 3 ? 2 : 3; }
 __device__ __forceinline__ int off_b(int q) { const int a = off_a(q); return q - a * (a - 1) / 2; }
 __device__ __forceinline__ int off_idx(int a, int b) { return a * (a - 1) / 2 + b; }
+
+// Element offset of (row, token) in a channel-major [rows][C] tile.  Tokens
+// are grouped in 8-token units whose order within a row is XOR-permuted by
+// row / 8: the operand stage stores 16 lanes on rows 8 apart at once, which
+// would otherwise all land on the same LDS banks.  Every access of up to 4
+// aligned tokens stays inside one unit.
+template <int C, int LDT>
+__device__ __forceinline__ int cm_off(int row, int tok) {
+  constexpr int NU = C / 8;
+  return row * LDT + ((((tok >> 3) ^ (row >> 3)) & (NU - 1)) << 3) + (tok & 7);
+}
 
 // Reduce-scatter of V per-lane values over the 64 lanes of a wave: on return
 // x[0] of every lane holds the 64-lane sum of value (lane / (64 / V)) % V
@@ -171,31 +188,64 @@ __device__ __forceinline__ void stN(float* p, const float* x) {
   }
 }
 
-// Rows r0 .. r0+N-1 of a chunk, 8 channels each; rows at or past nv read row
-// nv-1 instead and are zeroed, so the loads carry no branches.
-template <typename T, int N>
-__device__ __forceinline__ void load_rows8(float (*dst)[8], const T* cbase, int64_t rs, int r0, int nv) {
+// Raw 8-element row pieces as loaded from global memory.  A chunk's inputs are
+// loaded into these while the previous chunk is still in its carried stage,
+// and only converted (and masked past the sequence end) when the chunk starts.
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<__bf16> {
+  bf16x8 v;
+};
+template <>
+struct Raw8<float> {
+  f32x4 a, b;
+};
+__device__ __forceinline__ void ld_raw8(Raw8<__bf16>& r, const __bf16* p) {
+  r.v = *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void ld_raw8(Raw8<float>& r, const float* p) {
+  r.a = *reinterpret_cast<const f32x4*>(p);
+  r.b = *reinterpret_cast<const f32x4*>(p + 4);
+}
+__device__ __forceinline__ void cvt_raw8(float* x, const Raw8<__bf16>& r) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) ld8(dst[i], cbase + (int64_t)min(r0 + i, nv - 1) * rs);
+  for (int j = 0; j < 8; ++j) x[j] = (float)r.v[j];
+}
+__device__ __forceinline__ void cvt_raw8(float* x, const Raw8<float>& r) {
 #pragma unroll
-  for (int i = 0; i < N; ++i)
-    if (r0 + i >= nv)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dst[i][j] = 0.f;
+  for (int j = 0; j < 4; ++j) {
+    x[j] = r.a[j];
+    x[j + 4] = r.b[j];
+  }
 }
 
-// Prologue for rows r0 .. r0+N-1, 8 channels: causal depthwise conv (4 taps,
-// zero history before the sequence start = chunk row `lo`), SiLU, then L2
-// normalisation over the 128 channels of the head, which are spread over the
-// 16 lanes of this lane's group.
+// Rows r0 .. r0+N-1 as fp32, zero at or past nv (the raw loads read row nv-1 there).
 template <typename T, int N>
-__device__ __forceinline__ void load_prologue8(float (*dst)[8], const T* cbase, int64_t rs, int r0, int nv, int lo,
-                                               const float (*w)[4], float eps) {
+__device__ __forceinline__ void rows_from_raw(float (*dst)[8], const Raw8<T>* raw, int r0, int nv, bool full) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) cvt_raw8(dst[i], raw[i]);
+  if (!full) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (r0 + i >= nv)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dst[i][j] = 0.f;
+  }
+}
+
+// Prologue for rows r0 .. r0+N-1, 8 channels, from raw rows r0-3 .. r0+N-1:
+// causal depthwise conv (4 taps; zero history before the sequence start,
+// chunk row `lo`), SiLU, then L2 normalisation over the 128 channels of the
+// head, which are spread over the 16 lanes of this lane's group.
+template <typename T, int N>
+__device__ __forceinline__ void prologue_from_raw(float (*dst)[8], const Raw8<T>* raw, int r0, int nv, int lo,
+                                                  const float (*w)[4], float eps) {
   float x[N + 3][8];
 #pragma unroll
   for (int i = 0; i < N + 3; ++i) {
     const int row = r0 - 3 + i;
-    ld8(x[i], cbase + (int64_t)min(max(row, lo), nv - 1) * rs);
+    cvt_raw8(x[i], raw[i]);
     if (row < lo || row >= nv)
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[i][j] = 0.f;
@@ -243,6 +293,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
   E* sKtt = reinterpret_cast<E*>(smem + L::O_KTT);   // beta * Kt, channel-major
   E* sKbt = reinterpret_cast<E*>(smem + L::O_KBT);
   E* sVt = reinterpret_cast<E*>(smem + L::O_VT);     // beta * V, column-major
+  E* sQt = L::QT_OWN ? reinterpret_cast<E*>(smem + L::O_QT) : sQrh;
   float* sTot = reinterpret_cast<float*>(smem + L::O_TOT);
   float* sEf = reinterpret_cast<float*>(smem + L::O_EF);
   float* sEra = reinterpret_cast<float*>(smem + L::O_ERA);
@@ -301,13 +352,48 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
       }
   }
 
+  // Global inputs of one chunk held by this thread (see Raw8).
+  constexpr int QR = TPL + (PRO ? 3 : 0);  // q / k rows (with conv history)
+  constexpr int VCG = DV / 8, VTPL = C * VCG / 256;
+  const int vcg = tid % VCG, vtg = tid / VCG;
+  Raw8<float> rla[TPL];
+  Raw8<E> rq[QR], rk[QR], rv[VTPL];
+  float rvb[VTPL], rb = 0.f;
+  auto issue_loads = [&](int64_t tc) {
+    const int nvc = (int)((eos - tc) < C ? (eos - tc) : C);
+    const int64_t cb0 = tc * rs + hoff;
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) ld_raw8(rla[i], p.log_alpha + cb0 + (int64_t)min(r0 + i, nvc - 1) * rs + c8);
+    const int64_t back = bos - tc;  // <= 0
+    const int loc = back < -3 ? -3 : (int)back;
+#pragma unroll
+    for (int i = 0; i < QR; ++i) {
+      const int row = PRO ? min(max(r0 - 3 + i, loc), nvc - 1) : min(r0 + i, nvc - 1);
+      ld_raw8(rq[i], gq + cb0 + (int64_t)row * rs + c8);
+      ld_raw8(rk[i], gk + cb0 + (int64_t)row * rs + c8);
+    }
+#pragma unroll
+    for (int i = 0; i < VTPL; ++i) {
+      const int row = min(VTPL * vtg + i, nvc - 1);
+      ld_raw8(rv[i], gv + cb0 + (int64_t)row * rs + cb * DV + 8 * vcg);
+      rvb[i] = p.beta[(tc + row) * H + h];
+    }
+    if (tid < C) rb = p.beta[(tc + min(tid, nvc - 1)) * H + h];
+  };
+  if (bos < eos) issue_loads(bos);
+
   for (int64_t t0 = bos; t0 < eos; t0 += C) {
     const int nv = (int)((eos - t0) < C ? (eos - t0) : C);
-    const int64_t cbase = t0 * rs + hoff;  // element offset of (token t0, head h, channel 0)
 
     // ---- P1: log-decay prefix sums relative to the first row of this wave ----
+    // decay kept in log2 units: every factor below is one exp2
+    const bool full = (nv == C);
     float dl[TPL][8];
-    load_rows8<float, TPL>(dl, p.log_alpha + cbase + c8, rs, r0, nv);
+    rows_from_raw<float, TPL>(dl, rla, r0, nv, full);
+#pragma unroll
+    for (int i = 0; i < TPL; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dl[i][j] *= 1.4426950408889634f;
     {
 #pragma unroll
       for (int i = 1; i < TPL; ++i)
@@ -332,44 +418,35 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
       if (lg == 3) st8(sTot + wv * D + c8, inc);  // total of this wave's rows
     }
 
-    // ---- P2: q and k rows (raw, or through the prologue), V^T, beta ----
+    // ---- P2: q and k rows (raw, or through the prologue), beta V^T, beta ----
     float qv[TPL][8], kv[TPL][8];
     {
-      const E* qs = gq + cbase + c8;
-      const E* ks = gk + cbase + c8;
       if (PRO) {
         const int64_t back = bos - t0;  // <= 0
         const int lo = back < -3 ? -3 : (int)back;
         if (p.conv_q_w)
-          load_prologue8<E, TPL>(qv, qs, rs, r0, nv, lo, wq, p.l2_eps);
+          prologue_from_raw<E, TPL>(qv, rq, r0, nv, lo, wq, p.l2_eps);
         else
-          load_rows8<E, TPL>(qv, qs, rs, r0, nv);
+          rows_from_raw<E, TPL>(qv, rq + (QR - TPL), r0, nv, full);
         if (p.conv_k_w)
-          load_prologue8<E, TPL>(kv, ks, rs, r0, nv, lo, wk, p.l2_eps);
+          prologue_from_raw<E, TPL>(kv, rk, r0, nv, lo, wk, p.l2_eps);
         else
-          load_rows8<E, TPL>(kv, ks, rs, r0, nv);
+          rows_from_raw<E, TPL>(kv, rk + (QR - TPL), r0, nv, full);
       } else {
-        load_rows8<E, TPL>(qv, qs, rs, r0, nv);
-        load_rows8<E, TPL>(kv, ks, rs, r0, nv);
+        rows_from_raw<E, TPL>(qv, rq, r0, nv, full);
+        rows_from_raw<E, TPL>(kv, rk, r0, nv, full);
       }
-      // V^T: thread (vcg, vtg) moves columns 8 vcg .. +7 of rows VTPL*vtg .. +VTPL-1
-      constexpr int VCG = DV / 8, VTPL = C * VCG / 256;
-      const int vcg = tid % VCG, vtg = tid / VCG;
-      float vv[VTPL][8], vb[VTPL];
-      load_rows8<E, VTPL>(vv, gv + cbase + cb * DV + 8 * vcg, rs, VTPL * vtg, nv);
-#pragma unroll
-      for (int i = 0; i < VTPL; ++i) vb[i] = p.beta[(t0 + min(VTPL * vtg + i, nv - 1)) * H + h];
+      // beta V^T: thread (vcg, vtg) moves columns 8 vcg .. +7 of rows VTPL*vtg .. +VTPL-1
+      float vv[VTPL][8];
+      rows_from_raw<E, VTPL>(vv, rv, VTPL * vtg, nv, full);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float col[VTPL];
 #pragma unroll
-        for (int i = 0; i < VTPL; ++i) col[i] = vv[i][j] * vb[i];   // rows past nv are already zero
-        stN<VTPL>(sVt + (8 * vcg + j) * LDT + VTPL * vtg, col);
+        for (int i = 0; i < VTPL; ++i) col[i] = vv[i][j] * rvb[i];   // rows past nv are already zero
+        stN<VTPL>(sVt + cm_off<C, LDT>(8 * vcg + j, VTPL * vtg), col);
       }
-      if (tid < C) {
-        const float bb = p.beta[(t0 + min(tid, nv - 1)) * H + h];
-        sBeta[tid] = (tid < nv) ? bb : 0.f;
-      }
+      if (tid < C) sBeta[tid] = (tid < nv) ? rb : 0.f;
     }
     __syncthreads();
 
@@ -417,8 +494,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
       float ea[8], eb[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        ea[j] = __expf(ra[j]);                  // e^{rho_a} <= 1
-        eb[j] = __expf(rho[NT][j] - ra[j]);     // e^{g_n - rho_a} <= 1
+        ea[j] = exp2_fast(ra[j]);                  // e^{rho_a} <= 1
+        eb[j] = exp2_fast(rho[NT][j] - ra[j]);     // e^{g_n - rho_a} <= 1
       }
       float ktt[8][TPL], kbt[8][TPL];
 #pragma unroll
@@ -429,7 +506,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float d = dl[i][j] + intra[j];   // g_r - rho_a, in [-80, 0]
-          const float ep = __expf(d), en = __expf(-d);
+          const float ep = exp2_fast(d), en = exp2_fast(-d);
           xq[j] = qv[i][j] * ep;
           xk[j] = kv[i][j] * ep;
           xi[j] = kv[i][j] * en;
@@ -437,23 +514,29 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
           kbt[j][i] = xi[j] * eb[j];   // Kb = K e^{g_n - g}
         }
         st8_split(sQrh + rr * LDK + c8, sQrl + rr * LDK + c8, xq);
+        if constexpr (L::QT_OWN) {
+          float xt[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xt[j] = xq[j] * ea[j];   // Qt = Q e^{g}
+          st8(sQt + rr * LDK + c8, xt);
+        }
         st8_split(sKih + rr * LDK + c8, sKil + rr * LDK + c8, xi);
         st8(sKrel + rr * LDK + c8, xk);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        stN<TPL>(sKtt + (c8 + j) * LDT + r0, ktt[j]);
-        stN<TPL>(sKbt + (c8 + j) * LDT + r0, kbt[j]);
+        stN<TPL>(sKtt + cm_off<C, LDT>(c8 + j, r0), ktt[j]);
+        stN<TPL>(sKbt + cm_off<C, LDT>(c8 + j, r0), kbt[j]);
       }
       if (tg == 0) {
         float v8[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v8[j] = __expf(rho[NT][j]);
+        for (int j = 0; j < 8; ++j) v8[j] = exp2_fast(rho[NT][j]);
         st8(sGam + c8, v8);
 #pragma unroll
         for (int a = 0; a < NT; ++a) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) v8[j] = __expf(rho[a][j]);
+          for (int j = 0; j < 8; ++j) v8[j] = exp2_fast(rho[a][j]);
           st8(sEra + a * D + c8, v8);
         }
 #pragma unroll
@@ -461,7 +544,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
 #pragma unroll
           for (int b = 0; b < a; ++b) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v8[j] = __expf(rho[a][j] - rho[b][j]);
+            for (int j = 0; j < 8; ++j) v8[j] = exp2_fast(rho[a][j] - rho[b][j]);
             st8(sEf + off_idx(a, b) * D + c8, v8);
           }
       }
@@ -531,7 +614,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
             const int r = 16 * a + 4 * g + i;
             const float av = ga[j][i] * sBeta[r];   // row r of Diag(beta) Kt Kh^T
             if (b == a) {
-              sAd[(a * 16 + 4 * g + i) * 17 + l16] = (c < r) ? av : 0.f;
+              sAd[(a * 16 + 4 * g + i) * L::AST + l16] = (c < r) ? av : 0.f;
             } else {
               sM[r * LDT + c] = from_f32<E>(-av);
             }
@@ -545,6 +628,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
         sP[(16 * b + ((e >> 4) & 15)) * LDT + 16 * a + (e & 15)] = from_f32<E>(0.f);
       }
       // Qt = (Q_rel hi + lo) e^{rho_a}, in place over the Q_rel slot (8 elements per step)
+      if constexpr (!L::QT_OWN)
       for (int e = tid; e < C * (D / 8); e += 256) {
         const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
         float x[8];
@@ -571,14 +655,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
     // ---- P6: (I + A_aa)^{-1} of the diagonal 16x16 blocks, fp32 forward
     //      substitution; wave a, lane j < 16 solves column j of block a ----
     if (wv < NT && lane < 16) {
-      const float* ab = sAd + wv * 16 * 17;
+      const float* ab = sAd + wv * 16 * L::AST;
       float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float acc = (r == lane) ? 1.f : 0.f;
+        // four partial sums keep the dependency chains short
+        float part[4] = {(r == lane) ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < r; ++i) acc -= ab[r * 17 + i] * x[i];
-        x[r] = acc;
+        for (int q4 = 0; q4 < (r + 3) / 4; ++q4) {
+          const f32x4 av = *reinterpret_cast<const f32x4*>(ab + r * L::AST + 4 * q4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * q4 + e < r) part[e] -= av[e] * x[4 * q4 + e];
+        }
+        x[r] = (part[0] + part[1]) + (part[2] + part[3]);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sM[(16 * wv + r) * LDT + 16 * wv + lane] = from_f32<E>(x[r]);
@@ -602,9 +692,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
         f32x4 z[NOWN];
 #pragma unroll
         for (int o = 0; o < NOWN; ++o) {
-          const E* src = (o < 2) ? sKtt + (32 * wv + 16 * o + l16) * LDT : sVt + (wv * NCW + 16 * (o - 2) + l16) * LDT;
+          const E* src = (o < 2) ? sKtt + cm_off<C, LDT>(32 * wv + 16 * o + l16, 16 * a + 4 * g)
+                                 : sVt + cm_off<C, LDT>(wv * NCW + 16 * (o - 2) + l16, 16 * a + 4 * g);
           Frag16<E> r;
-          ld_frag16(r, src + 16 * a + 4 * g);
+          ld_frag16(r, src);
           z[o] = frag16_to_f32(r);
         }
 #pragma unroll
@@ -636,6 +727,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
     }
     __syncthreads();  // W visible to every wave
 
+    // the next chunk's inputs are loaded while this chunk's carried stage runs
+    if (t0 + C < eos) issue_loads(t0 + C);
+
     // ---- S1: U = U' - W S ----
     Frag<E> sf[4][NCT];
 #pragma unroll
@@ -664,7 +758,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         Frag<E> fa;
-        ld_frag_perm(fa, sQrh + (16 * rt + l16) * LDK + 32 * ks + 4 * g);
+        ld_frag_perm(fa, sQt + (16 * rt + l16) * LDK + 32 * ks + 4 * g);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) accO[rt][ct] = mma(accO[rt][ct], fa, sf[ks][ct]);
       }
@@ -741,7 +835,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         Frag<E> fa;
-        ld_frag_perm(fa, sKbt + (16 * rt8 + l16) * LDT + 32 * kt + 4 * g);
+        ld_frag_pair(fa, sKbt + cm_off<C, LDT>(16 * rt8 + l16, 32 * kt + 4 * g),
+                     sKbt + cm_off<C, LDT>(16 * rt8 + l16, 32 * kt + 16 + 4 * g));
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) accS[rt8][ct] = mma(accS[rt8][ct], fa, uf[kt][ct]);
       }
