@@ -64,15 +64,12 @@ struct PrefillLayout {
   static constexpr size_t S_QRH = (SPLIT ? 3 : 2) * TOK;
   static constexpr size_t S_QRL = 4 * TOK;
   static constexpr size_t R_BYTES = (SPLIT ? 5 : 3) * TOK;
-  // After them, [0, S_QRH) holds P | M | A_diag | W, and the Q_rel slot is
+  // After them, [0, S_QRH) holds P | M | W, and the Q_rel slot is
   // turned into Qt = Q (.) e^{g} in place.  M holds the blocks of the
   // triangular solve: -A_ab below the diagonal, (I + A_aa)^{-1} on it.
-  static constexpr int AST = 20;  // row stride of the fp32 diagonal blocks (16-byte aligned rows)
-  static constexpr size_t ADF = (size_t)NT * 16 * AST * 4;  // fp32 diagonal blocks of A
   static constexpr size_t R_P = 0;
   static constexpr size_t R_M = al16(CCE);
-  static constexpr size_t R_AD = R_M + al16(CCE);
-  static constexpr size_t R_W = R_AD + al16(ADF);
+  static constexpr size_t R_W = R_M + al16(CCE);
   static_assert(R_W + TOK <= S_QRH, "post-Gram tiles overflow their region");
   static constexpr size_t O_KTT = R_BYTES;
   static constexpr size_t O_KBT = O_KTT + CHM;
@@ -83,7 +80,11 @@ struct PrefillLayout {
   static constexpr size_t O_GAM = O_ERA + (size_t)NT * D * 4;        // f32 [D]
   static constexpr size_t O_BETA = O_GAM + (size_t)D * 4;            // f32 [C]
   static constexpr size_t O_SS = O_BETA + (size_t)C * 4;             // f32 [4][C]
-  static constexpr size_t BASE_BYTES = O_SS + (size_t)4 * C * 4;
+  // fp32 diagonal 16x16 blocks of A (outside region R, so each wave can solve
+  // its own block before the others finish reading the Gram operands)
+  static constexpr int AST = 16;
+  static constexpr size_t O_AD = O_SS + (size_t)4 * C * 4;           // f32 [NT][16][AST]
+  static constexpr size_t BASE_BYTES = O_AD + (size_t)NT * 16 * AST * 4;
   // Qt gets its own tile (written straight from fp32 in the operand stage)
   // when it fits; otherwise it is formed in place over Q_rel after the Gram.
   static constexpr bool QT_OWN = BASE_BYTES + TOK <= 160 * 1024;
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
   E* sQrl = reinterpret_cast<E*>(smem + L::S_QRL);   // used only when SPLIT
   E* sP = reinterpret_cast<E*>(smem + L::R_P);
   E* sM = reinterpret_cast<E*>(smem + L::R_M);
-  float* sAd = reinterpret_cast<float*>(smem + L::R_AD);
+  float* sAd = reinterpret_cast<float*>(smem + L::O_AD);
   E* sW = reinterpret_cast<E*>(smem + L::R_W);
   E* sKtt = reinterpret_cast<E*>(smem + L::O_KTT);   // beta * Kt, channel-major
   E* sKbt = reinterpret_cast<E*>(smem + L::O_KBT);
@@ -556,6 +557,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
     //      Wave w takes the diagonal pair (w, w) and the strictly-lower pairs q = w, w + 4.
     //      With bf16 operands P is formed from the hi + lo parts of Q_rel, and of
     //      K_inv on the diagonal (where it is not rescaled).
+    // ---- P6: each wave then inverts its own diagonal block, (I + A_ww)^{-1},
+    //      by fp32 forward substitution (lane j < 16 solves column j) while the
+    //      other waves are still on their Gram products.
     {
       constexpr int NOFF = L::NOFF;
       constexpr int PPW = 1 + (NOFF + 3) / 4;  // pairs per wave (first one diagonal)
@@ -601,9 +605,40 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
               }
             }
           }
+          if (j == 0) {
+            // Diag(beta) A_ww, strictly lower, to this wave's own fp32 block
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 16 * a + 4 * g + i;
+              sAd[(a * 16 + 4 * g + i) * L::AST + l16] = (l16 < 4 * g + i) ? ga[0][i] * sBeta[r] : 0.f;
+            }
+          }
+        }
+      }
+      float xinv[16];  // column `lane` of (I + A_ww)^{-1} (lanes < 16 of waves < NT)
+      if (wv < NT && lane < 16) {
+        const float* ab = sAd + wv * 16 * L::AST;
+        f32x4 av[16][4];
+#pragma unroll
+        for (int r = 1; r < 16; ++r)
+#pragma unroll
+          for (int q4 = 0; q4 < (r + 3) / 4; ++q4) av[r][q4] = *reinterpret_cast<const f32x4*>(ab + r * L::AST + 4 * q4);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          // four partial sums keep the dependency chains short
+          float part[4] = {(r == lane) ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int q4 = 0; q4 < (r + 3) / 4; ++q4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (4 * q4 + e < r) part[e] -= av[r][q4][e] * xinv[4 * q4 + e];
+          xinv[r] = (part[0] + part[1]) + (part[2] + part[3]);
         }
       }
       __syncthreads();  // every wave is done reading the Gram operands
+      if (wv < NT && lane < 16)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sM[(16 * wv + r) * LDT + 16 * wv + lane] = from_f32<E>(xinv[r]);
 #pragma unroll
       for (int j = 0; j < PPW; ++j) {
         const int a = pa[j], b = pb[j];
@@ -612,12 +647,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 16 * a + 4 * g + i;
-            const float av = ga[j][i] * sBeta[r];   // row r of Diag(beta) Kt Kh^T
-            if (b == a) {
-              sAd[(a * 16 + 4 * g + i) * L::AST + l16] = (c < r) ? av : 0.f;
-            } else {
-              sM[r * LDT + c] = from_f32<E>(-av);
-            }
+            if (b < a) sM[r * LDT + c] = from_f32<E>(-ga[j][i] * sBeta[r]);   // -(Diag(beta) A)_ab
             sP[r * LDT + c] = from_f32<E>(((b < a) || (c <= r)) ? gp[j][i] : 0.f);
           }
         }
@@ -652,29 +682,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
     }
     __syncthreads();
 
-    // ---- P6: (I + A_aa)^{-1} of the diagonal 16x16 blocks, fp32 forward
-    //      substitution; wave a, lane j < 16 solves column j of block a ----
-    if (wv < NT && lane < 16) {
-      const float* ab = sAd + wv * 16 * L::AST;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // four partial sums keep the dependency chains short
-        float part[4] = {(r == lane) ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q4 = 0; q4 < (r + 3) / 4; ++q4) {
-          const f32x4 av = *reinterpret_cast<const f32x4*>(ab + r * L::AST + 4 * q4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (4 * q4 + e < r) part[e] -= av[e] * x[4 * q4 + e];
-        }
-        x[r] = (part[0] + part[1]) + (part[2] + part[3]);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sM[(16 * wv + r) * LDT + 16 * wv + lane] = from_f32<E>(x[r]);
-    }
-    __syncthreads();
-
     // ---- P7: blocked forward substitution on the matrix cores,
     //      (I + A) [W | U'] = Diag(beta) [Kt | V], tile row by tile row:
     //      Y_a = (I + A_aa)^{-1} (beta R_a - sum_{b<a} A_ab Y_b).
@@ -683,33 +690,36 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
     f32x4 accU[NT][NCT];
     {
       constexpr int NOWN = 2 + NCT;
+      // all LDS operands of the solve are fetched up front
+      Frag16<E> mfr[NT][NT], rfr[NOWN][NT];
+#pragma unroll
+      for (int a = 0; a < NT; ++a)
+#pragma unroll
+        for (int b = 0; b <= a; ++b) ld_frag16(mfr[a][b], sM + (16 * a + l16) * LDT + 16 * b + 4 * g);
+#pragma unroll
+      for (int o = 0; o < NOWN; ++o)
+#pragma unroll
+        for (int a = 0; a < NT; ++a) {
+          const E* src = (o < 2) ? sKtt + cm_off<C, LDT>(32 * wv + 16 * o + l16, 16 * a + 4 * g)
+                                 : sVt + cm_off<C, LDT>(wv * NCW + 16 * (o - 2) + l16, 16 * a + 4 * g);
+          ld_frag16(rfr[o][a], src);
+        }
       f32x4 Y[NOWN][NT];
       Frag16<E> Yb[NOWN][NT];
 #pragma unroll
       for (int a = 0; a < NT; ++a) {
-        Frag16<E> xa;
-        ld_frag16(xa, sM + (16 * a + l16) * LDT + 16 * a + 4 * g);
         f32x4 z[NOWN];
 #pragma unroll
-        for (int o = 0; o < NOWN; ++o) {
-          const E* src = (o < 2) ? sKtt + cm_off<C, LDT>(32 * wv + 16 * o + l16, 16 * a + 4 * g)
-                                 : sVt + cm_off<C, LDT>(wv * NCW + 16 * (o - 2) + l16, 16 * a + 4 * g);
-          Frag16<E> r;
-          ld_frag16(r, src);
-          z[o] = frag16_to_f32(r);
-        }
+        for (int o = 0; o < NOWN; ++o) z[o] = frag16_to_f32(rfr[o][a]);
 #pragma unroll
-        for (int b = 0; b < a; ++b) {
-          Frag16<E> mab;
-          ld_frag16(mab, sM + (16 * a + l16) * LDT + 16 * b + 4 * g);
+        for (int b = 0; b < a; ++b)
 #pragma unroll
-          for (int o = 0; o < NOWN; ++o) z[o] = mma16(z[o], mab, Yb[o][b]);
-        }
+          for (int o = 0; o < NOWN; ++o) z[o] = mma16(z[o], mfr[a][b], Yb[o][b]);
 #pragma unroll
         for (int o = 0; o < NOWN; ++o) {
           Frag16<E> zb;
           frag16_from_acc(zb, z[o]);
-          Y[o][a] = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, xa, zb);
+          Y[o][a] = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, mfr[a][a], zb);
           frag16_from_acc(Yb[o][a], Y[o][a]);
         }
       }
