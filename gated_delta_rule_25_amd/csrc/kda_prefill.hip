@@ -385,6 +385,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
 
   for (int64_t t0 = bos; t0 < eos; t0 += C) {
     const int nv = (int)((eos - t0) < C ? (eos - t0) : C);
+    // Per-lane indices are re-derived from an opaque copy of the thread id in
+    // every chunk, so the LDS address arithmetic of the unrolled stages stays
+    // inside the loop instead of being hoisted into registers for the whole
+    // sequence.
+    int tidv = tid;
+    asm volatile("" : "+v"(tidv));
+    const int lane = tidv & 63, l16 = lane & 15, g = lane >> 4;
+    const int cg = tidv & 15, tg = tidv >> 4, lg = g;
+    const int c8 = 8 * cg, r0 = TPL * tg;
+    const int vcg = tidv % VCG, vtg = tidv / VCG;
 
     // ---- P1: log-decay prefix sums relative to the first row of this wave ----
     // decay kept in log2 units: every factor below is one exp2
@@ -686,7 +696,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
     //      (I + A) [W | U'] = Diag(beta) [Kt | V], tile row by tile row:
     //      Y_a = (I + A_aa)^{-1} (beta R_a - sum_{b<a} A_ab Y_b).
     //      Wave w solves W columns 32w .. 32w+31 and its own U' columns, so
-    //      every Y_b it needs is already in its registers. ----
+    //      every Y_b it needs is already in its registers.  W is stored
+    //      negated for the carried stage. ----
     f32x4 accU[NT][NCT];
     {
       constexpr int NOWN = 2 + NCT;
@@ -729,7 +740,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
         for (int a = 0; a < NT; ++a)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            sW[(16 * a + 4 * g + i) * LDK + 32 * wv + 16 * o + l16] = from_f32<E>(Y[o][a][i]);
+            sW[(16 * a + 4 * g + i) * LDK + 32 * wv + 16 * o + l16] = from_f32<E>(-Y[o][a][i]);
 #pragma unroll
       for (int a = 0; a < NT; ++a)
 #pragma unroll
@@ -751,8 +762,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         Frag<E> fa;
-        ld_frag_perm(fa, sW + (16 * rt + l16) * LDK + 32 * ks + 4 * g);
-        fa = frag_neg(fa);
+        ld_frag_perm(fa, sW + (16 * rt + l16) * LDK + 32 * ks + 4 * g);   // W is stored negated
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) accU[rt][ct] = mma(accU[rt][ct], fa, sf[ks][ct]);
       }
