@@ -46,6 +46,26 @@ def decode_algorithmic_bytes(N: int, H: int, es: int) -> int:
     return N * H * (2 * d * d * 4 + 3 * d * es + d * 4 + 4 + d * es)
 
 
+def measured_traffic(kernel: str):
+    """HBM bytes per launch recorded in profiles/hbm_traffic.json (rocprofv3
+    FETCH_SIZE / WRITE_SIZE, copy-calibrated), or None when the kernel's
+    sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    if rec is None:
+        return None
+    src = {"prefill_kernel": ["kda_prefill.hip", "kda_device.h", "kda_internal.h"],
+           "decode_kernel": ["kda_decode.hip", "kda_device.h", "kda_internal.h"]}[kernel]
+    m = hashlib.sha256()
+    for f in src:
+        with open(os.path.join(ROOT, "gated_delta_rule_25_amd", "csrc", f), "rb") as fh:
+            m.update(fh.read())
+    return rec["bytes"] if m.hexdigest()[:16] == rec["source_sha256_16"] else None
+
+
 def time_events(fn, steps, stream):
     import torch
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -172,7 +192,7 @@ def main():
             "config": {"workload": w["name"], "N": N, "H": H, "T": T, "d": 128, "chunk": 64 if es == 2 else 32,
                        "fused_prologue_epilogue": bool(w["fused"])},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                         "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic("prefill_kernel"),
                          "kernel": "prefill_kernel", "kernel_ms_avg": ms_avg, "algorithmic_bytes": algo},
         })
         if not args.no_cpu_baseline:
@@ -206,6 +226,7 @@ def main():
                             "tokens_per_s": wd["N"] * 1e3 / ms_avg, "steps": args.decode_steps,
                             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                          "frac": ach / HBM_PEAK_GBPS, "algorithmic_bytes": dbytes,
+                                         "traffic": measured_traffic("decode_kernel"),
                                          "kernel": "decode_kernel", "kernel_ms_min": min(per)}}
         if args.only_decode:
             result.update({"metric": "KDA decode steps/s", "value": 1e3 / ms_avg, "unit": "steps/s"})
