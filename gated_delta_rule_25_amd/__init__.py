@@ -38,7 +38,8 @@ class KDAError(RuntimeError):
 
 class _FusedOpts(ctypes.Structure):
     _fields_ = [("conv_q_w", ctypes.c_void_p), ("conv_k_w", ctypes.c_void_p), ("gate", ctypes.c_void_p),
-                ("norm_w", ctypes.c_void_p), ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+                ("norm_w", ctypes.c_void_p), ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("segment_tokens", ctypes.c_int)]
 
 
 def library_path() -> str:
@@ -93,9 +94,16 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 def chunk_fwd_workspace_bytes(num_seqs: int, total_tokens: int, num_heads: int,
-                              dtype: torch.dtype = torch.bfloat16) -> int:
+                              dtype: torch.dtype = torch.bfloat16, *, gated: bool = False,
+                              segment_tokens: int = 0) -> int:
+    """Workspace bytes of chunk_fwd on the current device.  Of the fused
+    options only whether an output gate is given matters (gated=True); the
+    address passed for it here is a placeholder that is never read."""
+    opts = None
+    if gated or segment_tokens != 0:
+        opts = ctypes.byref(_FusedOpts(None, None, 16 if gated else None, None, 1e-6, 1e-6, int(segment_tokens)))
     return int(_load().kda_chunk_fwd_workspace_bytes(num_seqs, total_tokens, num_heads, D, D,
-                                                     _DTYPES[dtype], None))
+                                                     _DTYPES[dtype], opts))
 
 
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor, beta: torch.Tensor,
@@ -104,15 +112,19 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
               gate: Optional[torch.Tensor] = None, norm_w: Optional[torch.Tensor] = None,
               l2_eps: float = 1e-6, rms_eps: float = 1e-6, out: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
-              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              workspace: Optional[torch.Tensor] = None,
+              segment_tokens: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """KDA prefill over a packed batch (kda_chunk_fwd).
 
     q, k, v: [T, H, 128] float32 or bfloat16; log_alpha [T, H, 128] float32;
     beta [T, H] float32; initial_state [N, H, 128, 128] float32 or None;
     cu_seqlens int32 [N+1] on the device or None.  Optional fused prologue
     (conv_q_w / conv_k_w [H*128, 4] float32) and epilogue (gate [T, H, 128],
-    norm_w [128] float32).  Returns (o, final_state); final_state may be the
-    same tensor as initial_state (in-place continuation).
+    norm_w [128] float32).  segment_tokens: 0 lets the library choose between
+    the sequential and the segmented schedule, a positive multiple of 64
+    forces segments of that length, a negative value keeps the sequential
+    one.  Returns (o, final_state); final_state may be the same tensor as
+    initial_state (in-place continuation).
     """
     lib = _load()
     if q.dim() != 3 or q.shape[2] != D:
@@ -154,9 +166,9 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
         _check(final_state, "final_state", (N, H, D, D), torch.float32, dev)
     dtc = _DTYPES[dt]
     opts = None
-    if any(x is not None for x in (conv_q_w, conv_k_w, gate, norm_w)):
+    if any(x is not None for x in (conv_q_w, conv_k_w, gate, norm_w)) or segment_tokens != 0:
         opts = _FusedOpts(_ptr(conv_q_w), _ptr(conv_k_w), _ptr(gate), _ptr(norm_w), float(l2_eps),
-                          float(rms_eps))
+                          float(rms_eps), int(segment_tokens))
     opts_p = ctypes.byref(opts) if opts is not None else None
     need = int(lib.kda_chunk_fwd_workspace_bytes(N, T, H, D, D, dtc, opts_p))
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):

@@ -56,6 +56,69 @@ bool dtype_ok(kda_dtype dt) { return dt == KDA_DTYPE_F32 || dt == KDA_DTYPE_BF16
 // rest (beta, cu_seqlens, conv and norm weights, workspace) are read as scalars.
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+constexpr int kMinAutoSegment = 512;
+
+// Segment length of the segmented schedule, or 0 for the sequential one.
+// Automatic choice: only when the sequential schedule's workgroups fill less
+// than a third of the compute units; then enough segments to fill them once
+// (the segmented form does about twice the state work, so it pays from about
+// three segments per chain on).
+int64_t choose_segment_tokens(int num_seqs, int64_t total_tokens, int num_heads, const kda_fused_opts& f,
+                              int cus) {
+  if (f.segment_tokens < 0) return 0;
+  if (f.segment_tokens > 0) return f.segment_tokens;
+  const int64_t per_chain = f.gate ? 1 : 2;  // workgroups per (sequence, head)
+  const int64_t blocks = (int64_t)num_seqs * num_heads * per_chain;
+  if (3 * blocks > cus) return 0;
+  const int64_t target = (cus + num_heads * per_chain - 1) / (num_heads * per_chain);
+  int64_t seg = (total_tokens + target - 1) / target;
+  seg = (seg + 63) / 64 * 64;
+  if (seg < kMinAutoSegment) seg = kMinAutoSegment;
+  if ((int64_t)num_seqs * seg >= total_tokens) return 0;  // sequences already about one segment long
+  return seg;
+}
+
+// Workspace layout.  Sequential: the longest-first order (N > 1 only).
+// Segmented: seq_first [N+1], seg_count, seg_list [2 cap], pairs
+// [cap][H][2][128][128] fp32, each piece 256-byte aligned; cap bounds the
+// number of segments: sum_n ceil(L_n / seg) <= T / seg + N.
+struct Plan {
+  int64_t seg_len = 0;
+  int64_t cap = 0;
+  size_t off_count = 0, off_list = 0, off_pairs = 0, bytes = 0;
+};
+
+Plan make_plan(int num_seqs, int64_t total_tokens, int num_heads, const kda_fused_opts& f, int cus) {
+  Plan pl;
+  pl.seg_len = choose_segment_tokens(num_seqs, total_tokens, num_heads, f, cus);
+  if (pl.seg_len == 0) {
+    pl.bytes = num_seqs > 1 ? align256((size_t)num_seqs * sizeof(int32_t)) : 0;
+    return pl;
+  }
+  pl.cap = total_tokens / pl.seg_len + num_seqs;
+  pl.off_count = align256((size_t)(num_seqs + 1) * sizeof(int32_t));
+  pl.off_list = pl.off_count + 256;
+  pl.off_pairs = pl.off_list + align256((size_t)pl.cap * 2 * sizeof(int32_t));
+  pl.bytes = pl.off_pairs + (size_t)pl.cap * num_heads * 2 * kD * kD * sizeof(float);
+  return pl;
+}
+
+const kda_fused_opts kNoOpts = {nullptr, nullptr, nullptr, nullptr, 1e-6f, 1e-6f, 0};
+
+bool sizes_ok(int num_seqs, int64_t total_tokens, int num_heads) {
+  return num_seqs >= 1 && num_heads >= 1 && total_tokens >= 0 &&
+         (int64_t)num_seqs * num_heads <= (int64_t)INT32_MAX / 2 && total_tokens <= (int64_t)INT32_MAX;
+}
+
+// A forced segment length must be a multiple of 64, and the segment list must
+// fit the launch grid.
+bool segments_ok(const Plan& pl, int num_heads, const kda_fused_opts& f) {
+  if (f.segment_tokens > 0 && f.segment_tokens % 64 != 0) return false;
+  return pl.seg_len == 0 || pl.cap * num_heads <= (int64_t)INT32_MAX / 8;
+}
+
 }  // namespace
 
 extern "C" {
@@ -73,12 +136,11 @@ const char* kda_status_string(kda_status s) {
 
 size_t kda_chunk_fwd_workspace_bytes(int num_seqs, int64_t total_tokens, int num_heads, int d_k, int d_v,
                                      kda_dtype dtype, const kda_fused_opts* opts) {
-  (void)opts;
-  if (num_seqs < 1 || total_tokens < 0 || num_heads < 1 || d_k != kD || d_v != kD || !dtype_ok(dtype))
-    return 0;
-  if (num_seqs == 1) return 0;
-  // int32 sequence order, longest first
-  return ((size_t)num_seqs * sizeof(int32_t) + 255) & ~(size_t)255;
+  if (!sizes_ok(num_seqs, total_tokens, num_heads) || d_k != kD || d_v != kD || !dtype_ok(dtype)) return 0;
+  const kda_fused_opts& f = opts ? *opts : kNoOpts;
+  const Plan pl = make_plan(num_seqs, total_tokens, num_heads, f, cu_count_for_current_device());
+  if (!segments_ok(pl, num_heads, f)) return 0;
+  return pl.bytes;
 }
 
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
@@ -89,22 +151,23 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   if (num_seqs < 1 || num_heads < 1 || total_tokens < 0) return KDA_ERR_INVALID_ARG;
   if (d_k != kD || d_v != kD || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
   if (!cu_seqlens && num_seqs != 1) return KDA_ERR_INVALID_ARG;
-  if ((int64_t)num_seqs * num_heads > (int64_t)INT32_MAX / 2) return KDA_ERR_INVALID_ARG;
-  if (total_tokens > (int64_t)INT32_MAX) return KDA_ERR_INVALID_ARG;  // cu_seqlens is int32
+  // cu_seqlens is int32; work items are counted in int32
+  if (!sizes_ok(num_seqs, total_tokens, num_heads)) return KDA_ERR_INVALID_ARG;
   if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_INVALID_ARG;
-  const kda_fused_opts none = {nullptr, nullptr, nullptr, nullptr, 1e-6f, 1e-6f};
-  const kda_fused_opts& f = opts ? *opts : none;
+  const kda_fused_opts& f = opts ? *opts : kNoOpts;
   if (!(f.l2_eps >= 0.f) || !(f.rms_eps >= 0.f)) return KDA_ERR_INVALID_ARG;
   {
-    const void* vec[] = {q, k, v, log_alpha, initial_state, o, final_state, f.gate};
+    const void* vec[] = {q, k, v, log_alpha, initial_state, o, final_state, f.gate, workspace};
     for (const void* ptr : vec)
       if (!aligned(ptr, 16)) return KDA_ERR_INVALID_ARG;
-    const void* sca[] = {beta, cu_seqlens, f.conv_q_w, f.conv_k_w, f.norm_w, workspace};
+    const void* sca[] = {beta, cu_seqlens, f.conv_q_w, f.conv_k_w, f.norm_w};
     for (const void* ptr : sca)
       if (!aligned(ptr, 4)) return KDA_ERR_INVALID_ARG;
   }
 
-  const size_t need = kda_chunk_fwd_workspace_bytes(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, opts);
+  const Plan pl = make_plan(num_seqs, total_tokens, num_heads, f, cu_count_for_current_device());
+  if (!segments_ok(pl, num_heads, f)) return KDA_ERR_INVALID_ARG;
+  const size_t need = pl.bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
 
   const size_t es = elem_size(dtype);
@@ -157,10 +220,56 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   // cannot occupy the GPU; the epilogue normalises whole heads, so it keeps one.
   a.col_split = (!f.gate && a.units <= cu_count_for_current_device()) ? 2 : 1;
 
-  if (num_seqs > 1) {
-    if (kda::launch_worklist(cu_seqlens, num_seqs, a.order, stream) != hipSuccess) return KDA_ERR_HIP;
+  if (pl.seg_len == 0) {
+    if (num_seqs > 1) {
+      if (kda::launch_worklist(cu_seqlens, num_seqs, a.order, stream) != hipSuccess) return KDA_ERR_HIP;
+    }
+    if (kda::launch_prefill(a, stream) != hipSuccess) return KDA_ERR_HIP;
+    return KDA_OK;
   }
-  if (kda::launch_prefill(a, stream) != hipSuccess) return KDA_ERR_HIP;
+
+  // Segmented schedule: segment table, per-segment affine pairs, the scan over
+  // segments, then the outputs of every segment from its incoming state.
+  char* ws = static_cast<char*>(workspace);
+  int32_t* seq_first = reinterpret_cast<int32_t*>(ws);
+  int32_t* seg_count = reinterpret_cast<int32_t*>(ws + pl.off_count);
+  int32_t* seg_list = reinterpret_cast<int32_t*>(ws + pl.off_list);
+  float* pairs = reinterpret_cast<float*>(ws + pl.off_pairs);
+  if (kda::launch_segment_table(cu_seqlens, num_seqs, total_tokens, (int)pl.seg_len, (int)pl.cap, seq_first,
+                                seg_list, seg_count, stream) != hipSuccess)
+    return KDA_ERR_HIP;
+
+  a.order = nullptr;
+  a.seg_len = (int)pl.seg_len;
+  a.seg_list = seg_list;
+  a.seg_count = seg_count;
+  a.pairs = pairs;
+  a.units = (int)(pl.cap * num_heads);
+
+  kda::PrefillArgs a1 = a;  // pairs: B (value columns) and M (identity columns)
+  a1.mode = 1;
+  a1.col_split = 2;
+  a1.init = nullptr;
+  a1.fin = nullptr;
+  a1.gate = nullptr;
+  a1.norm_w = nullptr;
+  if (kda::launch_prefill(a1, stream) != hipSuccess) return KDA_ERR_HIP;
+
+  kda::ScanArgs sc;
+  sc.pairs = pairs;
+  sc.seq_first = seq_first;
+  sc.init = initial_state;
+  sc.fin = final_state;
+  sc.num_seqs = num_seqs;
+  sc.num_heads = num_heads;
+  if (kda::launch_scan(sc, stream) != hipSuccess) return KDA_ERR_HIP;
+
+  kda::PrefillArgs a2 = a;  // outputs
+  a2.mode = 2;
+  a2.col_split = f.gate ? 1 : 2;
+  a2.init = nullptr;
+  a2.fin = nullptr;
+  if (kda::launch_prefill(a2, stream) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
 }
 

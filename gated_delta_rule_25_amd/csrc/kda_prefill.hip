@@ -310,12 +310,29 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
   if (u >= p.units) return;
   const int H = p.num_heads;
   const int rnk = u / H, h = u % H;
-  const int n = p.order ? p.order[rnk] : rnk;
-  const int64_t bos = p.cu ? (int64_t)p.cu[n] : 0;
-  const int64_t eos = p.cu ? (int64_t)p.cu[n + 1] : p.total_tokens;
+  int n = rnk, seg = 0;
+  if (p.mode == 0) {
+    if (p.order) n = p.order[rnk];
+  } else {
+    if (rnk >= *p.seg_count) return;
+    n = p.seg_list[2 * rnk];
+    seg = p.seg_list[2 * rnk + 1];
+  }
+  const int64_t seq_bos = p.cu ? (int64_t)p.cu[n] : 0;
+  const int64_t seq_eos = p.cu ? (int64_t)p.cu[n + 1] : p.total_tokens;
+  // this work item's token range: the whole sequence, or one segment of it
+  const int64_t bos = p.mode == 0 ? seq_bos : seq_bos + (int64_t)seg * p.seg_len;
+  const int64_t eos = p.mode == 0 ? seq_eos : min(seq_eos, bos + (int64_t)p.seg_len);
   const int64_t rs = (int64_t)H * D;  // elements between consecutive tokens
   const int64_t hoff = (int64_t)h * D;
-  const int col0 = cb * DV + wv * NCW;  // first value column owned by this wave
+  // mode 1: blocks [0, col_split/2) carry V from a zero state (B); the others
+  // carry the identity with V = 0 (M)
+  const int half = p.mode == 1 ? p.col_split / 2 : p.col_split;
+  const int cbv = cb % half;
+  const bool mpart = p.mode == 1 && cb >= half;
+  const bool write_o = p.mode != 1;
+  const size_t pair_base = ((size_t)rnk * H + h) * (size_t)(2 * D * D);
+  const int col0 = cbv * DV + wv * NCW;  // first value column owned by this wave
 
   const E* gq = static_cast<const E*>(p.q);
   const E* gk = static_cast<const E*>(p.k);
@@ -325,14 +342,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
   // State slice: tile (rt8, ct) holds rows 16 rt8 + 4g + i, column col0 + 16 ct + l16.
   f32x4 accS[8][NCT];
   const size_t sbase = ((size_t)n * H + h) * (size_t)(D * D);
+  const float* init = p.mode == 0 ? (p.init ? p.init + sbase : nullptr)
+                    : p.mode == 2 ? p.pairs + pair_base : nullptr;
+  float* fin = p.mode == 0 ? (p.fin ? p.fin + sbase : nullptr)
+             : p.mode == 1 ? p.pairs + pair_base + (mpart ? D * D : 0) : nullptr;
 #pragma unroll
   for (int rt8 = 0; rt8 < 8; ++rt8)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        accS[rt8][ct][i] =
-            p.init ? p.init[sbase + (size_t)(16 * rt8 + 4 * g + i) * D + col0 + 16 * ct + l16] : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * rt8 + 4 * g + i, col = col0 + 16 * ct + l16;
+        accS[rt8][ct][i] = init ? init[(size_t)row * D + col] : ((mpart && row == col) ? 1.f : 0.f);
+      }
 
   // Prep role: channel group cg (channels 8cg .. 8cg+7) and token group tg
   // (chunk rows TPL*tg .. +TPL-1).  The 16 lanes of a lane group hold one set
@@ -365,7 +387,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
     const int64_t cb0 = tc * rs + hoff;
 #pragma unroll
     for (int i = 0; i < TPL; ++i) ld_raw8(rla[i], p.log_alpha + cb0 + (int64_t)min(r0 + i, nvc - 1) * rs + c8);
-    const int64_t back = bos - tc;  // <= 0
+    const int64_t back = seq_bos - tc;  // <= 0
     const int loc = back < -3 ? -3 : (int)back;
 #pragma unroll
     for (int i = 0; i < QR; ++i) {
@@ -376,7 +398,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
 #pragma unroll
     for (int i = 0; i < VTPL; ++i) {
       const int row = min(VTPL * vtg + i, nvc - 1);
-      ld_raw8(rv[i], gv + cb0 + (int64_t)row * rs + cb * DV + 8 * vcg);
+      ld_raw8(rv[i], gv + cb0 + (int64_t)row * rs + cbv * DV + 8 * vcg);
       rvb[i] = p.beta[(tc + row) * H + h];
     }
     if (tid < C) rb = p.beta[(tc + min(tid, nvc - 1)) * H + h];
@@ -433,7 +455,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
     float qv[TPL][8], kv[TPL][8];
     {
       if (PRO) {
-        const int64_t back = bos - t0;  // <= 0
+        const int64_t back = seq_bos - t0;  // <= 0
         const int lo = back < -3 ? -3 : (int)back;
         if (p.conv_q_w)
           prologue_from_raw<E, TPL>(qv, rq, r0, nv, lo, wq, p.l2_eps);
@@ -454,7 +476,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
       for (int j = 0; j < 8; ++j) {
         float col[VTPL];
 #pragma unroll
-        for (int i = 0; i < VTPL; ++i) col[i] = vv[i][j] * rvb[i];   // rows past nv are already zero
+        for (int i = 0; i < VTPL; ++i) col[i] = mpart ? 0.f : vv[i][j] * rvb[i];   // rows past nv are already zero
         stN<VTPL>(sVt + cm_off<C, LDT>(8 * vcg + j, VTPL * vtg), col);
       }
       if (tid < C) sBeta[tid] = (tid < nv) ? rb : 0.f;
@@ -799,7 +821,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
         }
       }
 
-    if (EPI) {
+    if (EPI && write_o) {
       // head-wise RMSNorm over the 128 value channels, then the sigmoid gate
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt)
@@ -832,7 +854,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
             }
           }
         }
-    } else {
+    } else if (write_o) {
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
@@ -863,14 +885,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs p) {
     }
   }
 
-  if (p.fin) {
+  if (fin) {
 #pragma unroll
     for (int rt8 = 0; rt8 < 8; ++rt8)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          p.fin[sbase + (size_t)(16 * rt8 + 4 * g + i) * D + col0 + 16 * ct + l16] = accS[rt8][ct][i];
+          fin[(size_t)(16 * rt8 + 4 * g + i) * D + col0 + 16 * ct + l16] = accS[rt8][ct][i];
   }
 }
 
@@ -918,8 +940,10 @@ static hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
 template <typename E, int C>
 static hipError_t launch_dtype(const PrefillArgs& a, hipStream_t stream) {
   const bool pro = a.conv_q_w != nullptr || a.conv_k_w != nullptr;
-  const bool epi = a.gate != nullptr;
-  if (a.col_split == 2) {
+  const bool epi = a.gate != nullptr && a.mode != 1;
+  // value-column blocks per work item (mode 1 runs two sets: B and M)
+  const int blocks = a.mode == 1 ? a.col_split / 2 : a.col_split;
+  if (blocks == 2) {
     if (epi) return hipErrorInvalidValue;
     return pro ? launch_t<E, C, 64, true, false>(a, stream) : launch_t<E, C, 64, false, false>(a, stream);
   }

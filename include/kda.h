@@ -18,10 +18,10 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller, who keeps
  *     them alive until the work enqueued on `stream` has completed.  The
  *     library never allocates device memory.
- *   - Alignment: q, k, v, log_alpha, gate, o and the state tensors of
- *     kda_chunk_fwd, and the state of kda_decode_step, must be 16-byte
- *     aligned (they move as 16-byte vectors); every other pointer needs its
- *     element's alignment.  Violations return KDA_ERR_INVALID_ARG.
+ *   - Alignment: q, k, v, log_alpha, gate, o, the state tensors and the
+ *     workspace of kda_chunk_fwd, and the state of kda_decode_step, must be
+ *     16-byte aligned (they move as 16-byte vectors); every other pointer
+ *     needs its element's alignment.  Violations return KDA_ERR_INVALID_ARG.
  *   - Layouts are dense row-major, token-major: q/k/v/log_alpha/o are
  *     [T_total, H, 128]; beta is [T_total, H]; states are [N, H, 128, 128]
  *     fp32 with S[n][h][i][j], i = key channel (row), j = value channel.
@@ -74,6 +74,20 @@ typedef enum {
  *   gate  [T_total, H, 128] logits in the I/O dtype.  When given, the stored
  *       output is  y_t = o_t / sqrt(mean_j o_t[j]^2 + rms_eps) * norm_w * sigmoid(gate_t).
  *   norm_w  [128] fp32 RMSNorm weight; NULL means all ones.  Used only with gate.
+ *   segment_tokens  scheduling of long sequences when there are too few
+ *       (sequence, head) pairs to occupy the GPU: 0 lets the library decide
+ *       (it segments only when the sequential schedule would leave more than
+ *       two thirds of the compute units idle); a positive multiple of 64
+ *       forces the segmented form with segments of that many tokens (any
+ *       other positive value is KDA_ERR_INVALID_ARG); a negative value
+ *       disables it.  The segmented form needs a workspace of about
+ *       (T_total / segment_tokens + N) * H * 128 KiB.  The segmented form
+ *       ("Kimi K3 架构…" section 7.1, in-device context parallelism) runs every
+ *       segment from a zero state and, with V = 0, from the identity, which
+ *       gives the affine pair (M_j, B_j) with S_out = M_j S_in + B_j; a scan
+ *       composes the pairs into each segment's incoming state; a last pass
+ *       writes the outputs.  Results agree with the sequential form up to
+ *       rounding.
  */
 typedef struct {
   const float* conv_q_w;
@@ -82,11 +96,13 @@ typedef struct {
   const float* norm_w;
   float l2_eps;
   float rms_eps;
+  int segment_tokens;
 } kda_fused_opts;
 
 /*
- * Bytes of device workspace kda_chunk_fwd needs for these sizes (host-only
- * computation, no device access).  Returns 0 for invalid sizes.
+ * Bytes of device workspace kda_chunk_fwd needs for these sizes and options
+ * (host-side computation; it reads the current device's compute-unit count,
+ * which the segmented form depends on).  Returns 0 for invalid sizes.
  */
 size_t kda_chunk_fwd_workspace_bytes(int num_seqs, int64_t total_tokens, int num_heads, int d_k,
                                      int d_v, kda_dtype dtype, const kda_fused_opts* opts);
@@ -110,7 +126,8 @@ size_t kda_chunk_fwd_workspace_bytes(int num_seqs, int64_t total_tokens, int num
  *   o              [T_total, H, 128] dtype output; must not overlap any input.
  *   final_state    [N, H, 128, 128] fp32 output or NULL (not written).
  *   workspace      device scratch of at least kda_chunk_fwd_workspace_bytes()
- *                  bytes (may be NULL when that is 0).  Contents on entry are
+ *                  bytes for the same sizes and options on the same device
+ *                  (may be NULL when that is 0).  Contents on entry are
  *                  ignored; it must not be in use by other work on the GPU.
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,

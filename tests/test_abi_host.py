@@ -110,17 +110,54 @@ def test_chunk_validation(lib):
     assert chunk(lib, q=ctypes.c_void_p(BASE + 8)) == INVALID  # not 16-byte aligned
     assert chunk(lib, fs=ctypes.c_void_p(BASE + 6 * 64 * MB + 4)) == INVALID
     assert chunk(lib, b=ctypes.c_void_p(BASE + 4 * 64 * MB + 2)) == INVALID  # beta not 4-byte aligned
+    assert chunk(lib, N=2, cu=p(7), ws=ctypes.c_void_p(BASE + 8 * 64 * MB + 4), wsb=256) == INVALID  # workspace
 
 
 class Opts(ctypes.Structure):
     _fields_ = [("conv_q_w", ctypes.c_void_p), ("conv_k_w", ctypes.c_void_p), ("gate", ctypes.c_void_p),
-                ("norm_w", ctypes.c_void_p), ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+                ("norm_w", ctypes.c_void_p), ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("segment_tokens", ctypes.c_int)]
+
+
+def opts_p(o):
+    return ctypes.cast(ctypes.pointer(o), ctypes.c_void_p)
+
+
+def test_workspace_bytes_segmented(lib):
+    # forced segments of 64 tokens, N=1, T=1000, H=2: cap = 1000 // 64 + 1 = 16 segments;
+    # seq_first (256 B), seg_count (256 B), seg_list (256 B), then 16 * 2 * 2 * 128 * 128 fp32
+    o = Opts(None, None, None, None, 1e-6, 1e-6, 64)
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 1000, 2, 128, 128, BF16, opts_p(o)) == 768 + 16 * 2 * 2 * 65536
+    o.segment_tokens = 100                                     # not a multiple of 64
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 1000, 2, 128, 128, BF16, opts_p(o)) == 0
+    o.segment_tokens = -1                                      # sequential schedule forced
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 8, 128, 128, BF16, opts_p(o)) == 0
+    # automatic choice (256 compute units when no device is visible): H=8 leaves
+    # 16 of 256 workgroups busy, so 16 segments of 512 tokens; cap 17
+    o.segment_tokens = 0
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 8, 128, 128, BF16, opts_p(o)) == 768 + 17 * 8 * 2 * 65536
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 8, 128, 128, BF16, None) == 768 + 17 * 8 * 2 * 65536
+    # H=96 fills the GPU: sequential, no workspace for one sequence
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, None) == 0
+    # short sequences are not split
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 512, 8, 128, 128, BF16, None) == 0
+
+
+def test_chunk_validation_segmented(lib):
+    o = Opts(None, None, None, None, 1e-6, 1e-6, 100)
+    assert chunk(lib, opts=opts_p(o)) == INVALID                # segment length not a multiple of 64
+    o.segment_tokens = 64
+    assert chunk(lib, opts=opts_p(o)) == WORKSPACE              # the segmented form needs a workspace
+    need = lib.kda_chunk_fwd_workspace_bytes(1, 10, 2, 128, 128, BF16, opts_p(o))
+    assert chunk(lib, opts=opts_p(o), ws=p(8), wsb=need - 1) == WORKSPACE
+    assert chunk(lib, opts=opts_p(o), ws=ctypes.c_void_p(BASE + 8 * 64 * MB + 4), wsb=need) == INVALID  # alignment
+    assert chunk(lib, opts=opts_p(o), ws=p(5), wsb=need) == INVALID  # workspace aliases the output
 
 
 def test_chunk_validation_fused(lib):
-    o = Opts(None, None, p(5).value, None, 1e-6, 1e-6)        # gate aliases the output
+    o = Opts(None, None, p(5).value, None, 1e-6, 1e-6, 0)     # gate aliases the output
     assert chunk(lib, opts=ctypes.cast(ctypes.pointer(o), ctypes.c_void_p)) == INVALID
-    o2 = Opts(None, None, None, None, -1.0, 1e-6)             # negative epsilon
+    o2 = Opts(None, None, None, None, -1.0, 1e-6, 0)          # negative epsilon
     assert chunk(lib, opts=ctypes.cast(ctypes.pointer(o2), ctypes.c_void_p)) == INVALID
 
 
