@@ -5,7 +5,9 @@
 // allocated and the host never waits on the device.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 
@@ -59,6 +61,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int kMinAutoSegment = 512;
+constexpr int kPrepChunksPerBlock = 4;
 
 // Segment length of the segmented schedule, or 0 for the sequential one.
 // Automatic choice: only when the sequential schedule's workgroups fill less
@@ -80,21 +83,52 @@ int64_t choose_segment_tokens(int num_seqs, int64_t total_tokens, int num_heads,
   return seg;
 }
 
-// Workspace layout.  Sequential: the longest-first order (N > 1 only).
-// Segmented: seq_first [N+1], seg_count, seg_list [2 cap], pairs
-// [cap][H][2][128][128] fp32, each piece 256-byte aligned; cap bounds the
-// number of segments: sum_n ceil(L_n / seg) <= T / seg + N.
+// Factor store budget of the two-kernel schedule; longer inputs run in
+// several windows.
+constexpr size_t kFactorBudget = (size_t)4 << 30;
+
+// Workspace layout, each piece 256-byte aligned.
+// Two-kernel schedule: the longest-first order [N] (N > 1), the window table
+// (seq_first [N+1], seq_c0 [N], seq_c1 [N]), a state buffer [N,H,128,128]
+// fp32 carried between windows (more than one window only), and the factor
+// store [slots][H] blocks.  slots bounds the chunks of one window:
+// sum_n ceil(G_n / nw) <= (T / C + N) / nw + N, with G_n = ceil(L_n / C).
+// Segmented schedule: seq_first [N+1], seg_count, seg_list [2 cap], pairs
+// [cap][H][2][128][128] fp32; cap bounds the number of segments:
+// sum_n ceil(L_n / seg) <= T / seg + N.
 struct Plan {
   int64_t seg_len = 0;
   int64_t cap = 0;
-  size_t off_count = 0, off_list = 0, off_pairs = 0, bytes = 0;
+  size_t off_count = 0, off_list = 0, off_pairs = 0;
+  int nw = 1;
+  int64_t slots = 0;
+  size_t off_first = 0, off_c0 = 0, off_c1 = 0, off_state = 0, off_factors = 0;
+  size_t bytes = 0;
 };
 
-Plan make_plan(int num_seqs, int64_t total_tokens, int num_heads, const kda_fused_opts& f, int cus) {
+Plan make_plan(int num_seqs, int64_t total_tokens, int num_heads, kda_dtype dtype, const kda_fused_opts& f,
+               int cus) {
   Plan pl;
   pl.seg_len = choose_segment_tokens(num_seqs, total_tokens, num_heads, f, cus);
   if (pl.seg_len == 0) {
-    pl.bytes = num_seqs > 1 ? align256((size_t)num_seqs * sizeof(int32_t)) : 0;
+    const bool bf = dtype == KDA_DTYPE_BF16;
+    const int64_t C = kda::chunk_len(bf);
+    const size_t fb = kda::factor_block_bytes(bf);
+    const int64_t chunks = total_tokens / C + num_seqs;
+    const double total = (double)chunks * num_heads * fb;
+    pl.nw = (int)std::max<double>(1.0, std::ceil(total / (double)kFactorBudget));
+    pl.slots = chunks / pl.nw + num_seqs + 1;
+    size_t off = num_seqs > 1 ? align256((size_t)num_seqs * sizeof(int32_t)) : 0;
+    pl.off_first = off;
+    off += align256((size_t)(num_seqs + 1) * sizeof(int32_t));
+    pl.off_c0 = off;
+    off += align256((size_t)num_seqs * sizeof(int32_t));
+    pl.off_c1 = off;
+    off += align256((size_t)num_seqs * sizeof(int32_t));
+    pl.off_state = off;
+    if (pl.nw > 1) off += (size_t)num_seqs * num_heads * kD * kD * sizeof(float);
+    pl.off_factors = off;
+    pl.bytes = off + (size_t)pl.slots * num_heads * fb;
     return pl;
   }
   pl.cap = total_tokens / pl.seg_len + num_seqs;
@@ -116,7 +150,8 @@ bool sizes_ok(int num_seqs, int64_t total_tokens, int num_heads) {
 // fit the launch grid.
 bool segments_ok(const Plan& pl, int num_heads, const kda_fused_opts& f) {
   if (f.segment_tokens > 0 && f.segment_tokens % 64 != 0) return false;
-  return pl.seg_len == 0 || pl.cap * num_heads <= (int64_t)INT32_MAX / 8;
+  if (pl.seg_len == 0) return pl.slots <= (int64_t)INT32_MAX / 2 && pl.slots * num_heads <= (int64_t)UINT32_MAX;
+  return pl.cap * num_heads <= (int64_t)INT32_MAX / 8;
 }
 
 }  // namespace
@@ -138,7 +173,7 @@ size_t kda_chunk_fwd_workspace_bytes(int num_seqs, int64_t total_tokens, int num
                                      kda_dtype dtype, const kda_fused_opts* opts) {
   if (!sizes_ok(num_seqs, total_tokens, num_heads) || d_k != kD || d_v != kD || !dtype_ok(dtype)) return 0;
   const kda_fused_opts& f = opts ? *opts : kNoOpts;
-  const Plan pl = make_plan(num_seqs, total_tokens, num_heads, f, cu_count_for_current_device());
+  const Plan pl = make_plan(num_seqs, total_tokens, num_heads, dtype, f, cu_count_for_current_device());
   if (!segments_ok(pl, num_heads, f)) return 0;
   return pl.bytes;
 }
@@ -165,7 +200,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
       if (!aligned(ptr, 4)) return KDA_ERR_INVALID_ARG;
   }
 
-  const Plan pl = make_plan(num_seqs, total_tokens, num_heads, f, cu_count_for_current_device());
+  const Plan pl = make_plan(num_seqs, total_tokens, num_heads, dtype, f, cu_count_for_current_device());
   if (!segments_ok(pl, num_heads, f)) return KDA_ERR_INVALID_ARG;
   const size_t need = pl.bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
@@ -221,10 +256,65 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   a.col_split = (!f.gate && a.units <= cu_count_for_current_device()) ? 2 : 1;
 
   if (pl.seg_len == 0) {
+    // Two-kernel schedule: per window, the window table, the factor blocks of
+    // every (chunk, head), then the state walk over them.
+    char* ws = static_cast<char*>(workspace);
+    int32_t* order = num_seqs > 1 ? reinterpret_cast<int32_t*>(ws) : nullptr;
+    int32_t* seq_first = reinterpret_cast<int32_t*>(ws + pl.off_first);
+    int32_t* seq_c0 = reinterpret_cast<int32_t*>(ws + pl.off_c0);
+    int32_t* seq_c1 = reinterpret_cast<int32_t*>(ws + pl.off_c1);
+    float* carry_buf = final_state ? final_state : reinterpret_cast<float*>(ws + pl.off_state);
+    void* factors = ws + pl.off_factors;
     if (num_seqs > 1) {
-      if (kda::launch_worklist(cu_seqlens, num_seqs, a.order, stream) != hipSuccess) return KDA_ERR_HIP;
+      if (kda::launch_worklist(cu_seqlens, num_seqs, order, stream) != hipSuccess) return KDA_ERR_HIP;
     }
-    if (kda::launch_prefill(a, stream) != hipSuccess) return KDA_ERR_HIP;
+    kda::PrepArgs pa;
+    std::memset(&pa, 0, sizeof(pa));
+    pa.q = q;
+    pa.k = k;
+    pa.v = v;
+    pa.log_alpha = log_alpha;
+    pa.beta = beta;
+    pa.cu = cu_seqlens;
+    pa.conv_q_w = f.conv_q_w;
+    pa.conv_k_w = f.conv_k_w;
+    pa.l2_eps = f.l2_eps;
+    pa.num_seqs = num_seqs;
+    pa.num_heads = num_heads;
+    pa.total_tokens = total_tokens;
+    pa.bf16 = a.bf16;
+    pa.seq_first = seq_first;
+    pa.seq_c0 = seq_c0;
+    pa.cap = (int)pl.slots;
+    pa.chunks_per_block = kPrepChunksPerBlock;
+    pa.factors = factors;
+    kda::CarryArgs ca;
+    std::memset(&ca, 0, sizeof(ca));
+    ca.factors = factors;
+    ca.cu = cu_seqlens;
+    ca.order = order;
+    ca.seq_first = seq_first;
+    ca.seq_c0 = seq_c0;
+    ca.seq_c1 = seq_c1;
+    ca.gate = f.gate;
+    ca.norm_w = f.norm_w;
+    ca.rms_eps = f.rms_eps;
+    ca.o = o;
+    ca.num_seqs = num_seqs;
+    ca.num_heads = num_heads;
+    ca.total_tokens = total_tokens;
+    ca.units = num_seqs * num_heads;
+    ca.col_split = a.col_split;
+    ca.bf16 = a.bf16;
+    for (int w = 0; w < pl.nw; ++w) {
+      if (kda::launch_window_table(cu_seqlens, num_seqs, total_tokens, kda::chunk_len(a.bf16), pl.nw, w,
+                                   (int)pl.slots, seq_first, seq_c0, seq_c1, stream) != hipSuccess)
+        return KDA_ERR_HIP;
+      if (kda::launch_prep(pa, stream) != hipSuccess) return KDA_ERR_HIP;
+      ca.state_in = (w == 0) ? initial_state : carry_buf;
+      ca.state_out = (w == pl.nw - 1) ? final_state : carry_buf;
+      if (kda::launch_carry(ca, stream) != hipSuccess) return KDA_ERR_HIP;
+    }
     return KDA_OK;
   }
 

@@ -65,6 +65,88 @@ struct ScanArgs {
   int num_heads;
 };
 
+// ---------------------------------------------------------------------------
+// Two-kernel chunked prefill.  The prep kernel turns every (chunk, head) of
+// the inputs into a factor block, independently of the state; the carry
+// kernel walks each (sequence, head) through its chunks with the state.
+// Chunk length: 64 tokens for bf16 I/O, 32 for fp32.
+// Factor block of one (chunk, head), ES = element bytes of the I/O dtype:
+//   W  [C][128]  -W, token-major                       (ES each)
+//   Q  [C][128]  Qt = Q (.) e^{g}, token-major          (ES)
+//   P  [C][C]    lower-incl(Qt Kh^T), upper part zero   (ES)
+//   K  [128][C]  Kb^T channel-major; the 8-token units of row r are in the
+//                XOR order of the LDS tile (unit u stored at u ^ (r / 8))  (ES)
+//   G  [128]     e^{g_n} per key channel                (fp32)
+//   U  [C/16][8][64][4]  U' = T V in MFMA accumulator order: token tile a,
+//                column tile ct, lane, element i = (token 16a + 4(lane/16) + i,
+//                column 16 ct + lane % 16)              (fp32)
+template <int ES, int C>
+struct FactorBlock {
+  static constexpr size_t W = 0;
+  static constexpr size_t Q = (size_t)C * 128 * ES;
+  static constexpr size_t P = 2 * (size_t)C * 128 * ES;
+  static constexpr size_t K = P + (size_t)C * C * ES;
+  static constexpr size_t G = K + (size_t)128 * C * ES;
+  static constexpr size_t U = G + 128 * 4;
+  static constexpr size_t BYTES = (U + (size_t)C * 128 * 4 + 255) & ~(size_t)255;
+};
+constexpr int chunk_len(bool bf16) { return bf16 ? 64 : 32; }
+constexpr size_t factor_block_bytes(bool bf16) {
+  return bf16 ? FactorBlock<2, 64>::BYTES : FactorBlock<4, 32>::BYTES;
+}
+
+// Factor store of one window: slot s of head h at ((s * H) + h) * block bytes.
+// A window holds, for every sequence n, chunks [c0_n, c1_n) in slots
+// [seq_first[n], seq_first[n] + c1_n - c0_n); seq_first[N] is the slot count.
+struct PrepArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_alpha;
+  const float* beta;
+  const int32_t* cu;
+  const float* conv_q_w;
+  const float* conv_k_w;
+  float l2_eps;
+  int num_seqs;
+  int num_heads;
+  int64_t total_tokens;
+  bool bf16;
+  const int32_t* seq_first;  // [N+1]
+  const int32_t* seq_c0;     // [N]
+  int cap;                   // slots the store can hold
+  int chunks_per_block;      // consecutive slots per workgroup
+  void* factors;
+};
+
+struct CarryArgs {
+  const void* factors;
+  const int32_t* cu;
+  const int32_t* order;      // sequences longest first, or null (identity)
+  const int32_t* seq_first;
+  const int32_t* seq_c0;
+  const int32_t* seq_c1;
+  const float* state_in;     // [N,H,128,128] or null (zero)
+  float* state_out;          // [N,H,128,128] or null (not written)
+  const void* gate;          // [T,H,128] or null
+  const float* norm_w;
+  float rms_eps;
+  void* o;
+  int num_seqs;
+  int num_heads;
+  int64_t total_tokens;
+  int units;                 // num_seqs * num_heads
+  int col_split;             // 1 or 2 value-column blocks per (sequence, head)
+  bool bf16;
+};
+
+// Window w of nw: sequence n of G_n chunks gets chunks
+// [min(w Q_n, G_n), min((w + 1) Q_n, G_n)) with Q_n = ceil(G_n / nw).
+hipError_t launch_window_table(const int32_t* cu, int num_seqs, int64_t total_tokens, int chunk, int nw, int w,
+                               int cap, int32_t* seq_first, int32_t* seq_c0, int32_t* seq_c1, hipStream_t stream);
+hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
+hipError_t launch_carry(const CarryArgs& a, hipStream_t stream);
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // Longest-first ordering of the packed sequences (device-side, no host sync).

@@ -67,9 +67,17 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, None) == 0
-    assert lib.kda_chunk_fwd_workspace_bytes(64, 10 ** 6, 96, 128, 128, BF16, None) == 256
-    assert lib.kda_chunk_fwd_workspace_bytes(65, 10 ** 6, 96, 128, 128, BF16, None) == 512
+    # the two-kernel schedule keeps a factor store in the workspace: it grows
+    # with the number of (chunk, head) blocks and is capped (long inputs run in
+    # windows), so a one-layer 1M-token input still needs only a few GiB
+    w8k = lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, None)
+    w16k = lib.kda_chunk_fwd_workspace_bytes(1, 16384, 96, 128, 128, BF16, None)
+    assert w8k > 0 and w16k > w8k
+    assert w8k % 256 == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 1 << 20, 96, 128, 128, BF16, None) < 6 << 30
+    assert lib.kda_chunk_fwd_workspace_bytes(64, 10 ** 6, 96, 128, 128, BF16, None) < 6 << 30
+    # fp32 chunks are half as long, so more blocks
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, 0, None) > w8k
     assert lib.kda_chunk_fwd_workspace_bytes(2, 10, 2, 64, 128, BF16, None) == 0  # invalid sizes
     assert lib.kda_chunk_fwd_workspace_bytes(0, 10, 2, 128, 128, BF16, None) == 0
 
@@ -85,7 +93,7 @@ def p(i):
 
 def chunk(lib, **kw):
     a = dict(q=p(0), k=p(1), v=p(2), la=p(3), b=p(4), s0=None, cu=None, N=1, T=10, H=2, dk=128, dv=128,
-             dt=BF16, opts=None, o=p(5), fs=p(6), ws=None, wsb=0)
+             dt=BF16, opts=None, o=p(5), fs=p(6), ws=p(8), wsb=32 * MB)
     a.update(kw)
     return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["la"], a["b"], a["s0"], a["cu"], a["N"], a["T"], a["H"],
                              a["dk"], a["dv"], a["dt"], a["opts"], a["o"], a["fs"], a["ws"], a["wsb"], None)
@@ -101,16 +109,20 @@ def test_chunk_validation(lib):
     assert chunk(lib, q=None) == INVALID
     assert chunk(lib, o=None) == INVALID
     assert chunk(lib, N=2) == INVALID                          # several sequences need cu_seqlens
-    assert chunk(lib, N=2, cu=p(7)) == WORKSPACE               # ... and a workspace
+    assert chunk(lib, N=2, cu=p(7), ws=None, wsb=0) == WORKSPACE  # ... and a workspace
     assert chunk(lib, N=2, cu=p(7), ws=p(8), wsb=16) == WORKSPACE
     assert chunk(lib, o=p(0)) == INVALID                       # output aliases q
     assert chunk(lib, fs=p(3)) == INVALID                      # final state aliases log_alpha
     assert chunk(lib, s0=p(6), fs=ctypes.c_void_p(BASE + 6 * 64 * MB + 4)) == INVALID  # partial overlap
-    assert chunk(lib, N=2, cu=p(7), ws=p(0), wsb=256) == INVALID  # workspace aliases q
+    need2 = lib.kda_chunk_fwd_workspace_bytes(2, 10, 2, 128, 128, BF16, None)
+    assert chunk(lib, N=2, cu=p(7), ws=p(0), wsb=need2) == INVALID  # workspace aliases q
+    need1 = lib.kda_chunk_fwd_workspace_bytes(1, 10, 2, 128, 128, BF16, None)
+    assert chunk(lib, ws=None, wsb=0) == WORKSPACE             # the factor store is always needed
+    assert chunk(lib, ws=p(8), wsb=need1 - 1) == WORKSPACE
     assert chunk(lib, q=ctypes.c_void_p(BASE + 8)) == INVALID  # not 16-byte aligned
     assert chunk(lib, fs=ctypes.c_void_p(BASE + 6 * 64 * MB + 4)) == INVALID
     assert chunk(lib, b=ctypes.c_void_p(BASE + 4 * 64 * MB + 2)) == INVALID  # beta not 4-byte aligned
-    assert chunk(lib, N=2, cu=p(7), ws=ctypes.c_void_p(BASE + 8 * 64 * MB + 4), wsb=256) == INVALID  # workspace
+    assert chunk(lib, N=2, cu=p(7), ws=ctypes.c_void_p(BASE + 8 * 64 * MB + 4), wsb=need2) == INVALID  # workspace
 
 
 class Opts(ctypes.Structure):
@@ -131,23 +143,27 @@ def test_workspace_bytes_segmented(lib):
     o.segment_tokens = 100                                     # not a multiple of 64
     assert lib.kda_chunk_fwd_workspace_bytes(1, 1000, 2, 128, 128, BF16, opts_p(o)) == 0
     o.segment_tokens = -1                                      # sequential schedule forced
-    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 8, 128, 128, BF16, opts_p(o)) == 0
+    seq8 = lib.kda_chunk_fwd_workspace_bytes(1, 8192, 8, 128, 128, BF16, opts_p(o))
+    assert seq8 > 0 and seq8 != 768 + 17 * 8 * 2 * 65536
     # automatic choice (256 compute units when no device is visible): H=8 leaves
     # 16 of 256 workgroups busy, so 16 segments of 512 tokens; cap 17
     o.segment_tokens = 0
     assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 8, 128, 128, BF16, opts_p(o)) == 768 + 17 * 8 * 2 * 65536
     assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 8, 128, 128, BF16, None) == 768 + 17 * 8 * 2 * 65536
-    # H=96 fills the GPU: sequential, no workspace for one sequence
-    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, None) == 0
+    # H=96 fills the GPU: the two-kernel schedule, the same plan as when forced
+    o.segment_tokens = -1
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, None) == \
+        lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, opts_p(o))
     # short sequences are not split
-    assert lib.kda_chunk_fwd_workspace_bytes(1, 512, 8, 128, 128, BF16, None) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 512, 8, 128, 128, BF16, None) == \
+        lib.kda_chunk_fwd_workspace_bytes(1, 512, 8, 128, 128, BF16, opts_p(o))
 
 
 def test_chunk_validation_segmented(lib):
     o = Opts(None, None, None, None, 1e-6, 1e-6, 100)
     assert chunk(lib, opts=opts_p(o)) == INVALID                # segment length not a multiple of 64
     o.segment_tokens = 64
-    assert chunk(lib, opts=opts_p(o)) == WORKSPACE              # the segmented form needs a workspace
+    assert chunk(lib, opts=opts_p(o), ws=None, wsb=0) == WORKSPACE  # the segmented form needs a workspace
     need = lib.kda_chunk_fwd_workspace_bytes(1, 10, 2, 128, 128, BF16, opts_p(o))
     assert chunk(lib, opts=opts_p(o), ws=p(8), wsb=need - 1) == WORKSPACE
     assert chunk(lib, opts=opts_p(o), ws=ctypes.c_void_p(BASE + 8 * 64 * MB + 4), wsb=need) == INVALID  # alignment
