@@ -48,8 +48,9 @@ def decode_algorithmic_bytes(N: int, H: int, es: int) -> int:
 
 def measured_traffic(kernel: str):
     """HBM bytes per launch recorded in profiles/hbm_traffic.json (rocprofv3
-    FETCH_SIZE / WRITE_SIZE, copy-calibrated), or None when the kernel's
-    sources have changed since the counters were taken."""
+    FETCH_SIZE / WRITE_SIZE, copy-calibrated; for kda_chunk_fwd the sum over
+    its kernels), or None when the kernel's sources have changed since the
+    counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
@@ -57,7 +58,7 @@ def measured_traffic(kernel: str):
     rec = json.load(open(path)).get(kernel)
     if rec is None:
         return None
-    src = {"prefill_kernel": ["kda_prefill.hip", "kda_device.h", "kda_internal.h"],
+    src = {"kda_chunk_fwd": ["kda_chunk.hip", "kda_chunk_util.h", "kda_device.h", "kda_internal.h", "kda_api.hip"],
            "decode_kernel": ["kda_decode.hip", "kda_device.h", "kda_internal.h"]}[kernel]
     m = hashlib.sha256()
     for f in src:
@@ -192,8 +193,9 @@ def main():
             "config": {"workload": w["name"], "N": N, "H": H, "T": T, "d": 128, "chunk": 64 if es == 2 else 32,
                        "fused_prologue_epilogue": bool(w["fused"])},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic("prefill_kernel"),
-                         "kernel": "prefill_kernel", "kernel_ms_avg": ms_avg, "algorithmic_bytes": algo},
+                         "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic("kda_chunk_fwd"),
+                         "kernel": "kda_chunk_fwd = window_table_kernel + prep_kernel + carry_kernel",
+                         "kernel_ms_avg": ms_avg, "algorithmic_bytes": algo},
         })
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(inp)
