@@ -61,7 +61,10 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int kMinAutoSegment = 512;
-constexpr int kPrepChunksPerBlock = 4;
+#ifndef KDA_PREP_CHUNKS_PER_BLOCK
+#define KDA_PREP_CHUNKS_PER_BLOCK 4
+#endif
+constexpr int kPrepChunksPerBlock = KDA_PREP_CHUNKS_PER_BLOCK;
 
 // Segment length of the segmented schedule, or 0 for the sequential one.
 // Automatic choice: only when the sequential schedule's workgroups fill less
@@ -85,7 +88,10 @@ int64_t choose_segment_tokens(int num_seqs, int64_t total_tokens, int num_heads,
 
 // Factor store budget of the two-kernel schedule; longer inputs run in
 // several windows.
-constexpr size_t kFactorBudget = (size_t)4 << 30;
+#ifndef KDA_FACTOR_BUDGET_MIB
+#define KDA_FACTOR_BUDGET_MIB 4096
+#endif
+constexpr size_t kFactorBudget = (size_t)KDA_FACTOR_BUDGET_MIB << 20;
 
 // Workspace layout, each piece 256-byte aligned.
 // Two-kernel schedule: the longest-first order [N] (N > 1), the window table

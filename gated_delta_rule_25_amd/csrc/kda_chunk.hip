@@ -81,595 +81,17 @@ hipError_t launch_window_table(const int32_t* cu, int num_seqs, int64_t total_to
   return hipGetLastError();
 }
 
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-// Raw buffer view of `bytes` bytes at p (word 3: the raw 32-bit access format).
-__device__ __forceinline__ Rsrc make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 buf_ld16(Rsrc r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
-}
-__device__ __forceinline__ void buf_st16(u32x4 v, Rsrc r, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, 0);
-}
-
-// ---------------------------------------------------------------------------
-// Prep kernel.  Workgroup (range r, head h) handles the consecutive slots
-// [r * chunks_per_block, ...) of head h; the inputs of its next slot are
-// loaded while the current factor block is written out.
-// ---------------------------------------------------------------------------
-template <typename E, int C, bool PRO>
-__global__ __launch_bounds__(256) void prep_kernel(const PrepArgs p) {
-  constexpr int DV = D;
-  using L = PrefillLayout<E, C, DV>;
-  using F = FactorBlock<(int)sizeof(E), C>;
-  constexpr bool SPLIT = L::SPLIT;
-  constexpr int NT = C / 16;     // 16-token tiles per chunk
-  constexpr int NCW = DV / 4;    // U' columns per wave
-  constexpr int NCT = NCW / 16;  // 16-wide column tiles per wave
-  constexpr int LDK = L::LDK, LDT = L::LDT;
-  static_assert(NCT >= 1 && NT <= 4, "unsupported tile shape");
-
-  extern __shared__ __align__(16) unsigned char smem[];
-  E* sKrel = reinterpret_cast<E*>(smem + L::S_KR);
-  E* sKih = reinterpret_cast<E*>(smem + L::S_KIH);
-  E* sKil = reinterpret_cast<E*>(smem + L::S_KIL);   // used only when SPLIT
-  E* sQrh = reinterpret_cast<E*>(smem + L::S_QRH);   // Q_rel, then Qt in place
-  E* sQrl = reinterpret_cast<E*>(smem + L::S_QRL);   // used only when SPLIT
-  E* sP = reinterpret_cast<E*>(smem + L::R_P);
-  E* sM = reinterpret_cast<E*>(smem + L::R_M);
-  float* sAd = reinterpret_cast<float*>(smem + L::O_AD);
-  E* sW = reinterpret_cast<E*>(smem + L::R_W);
-  E* sKtt = reinterpret_cast<E*>(smem + L::O_KTT);   // beta * Kt, channel-major
-  E* sKbt = reinterpret_cast<E*>(smem + L::O_KBT);
-  E* sVt = reinterpret_cast<E*>(smem + L::O_VT);     // beta * V, column-major
-  E* sQt = L::QT_OWN ? reinterpret_cast<E*>(smem + L::O_QT) : sQrh;
-  float* sTot = reinterpret_cast<float*>(smem + L::O_TOT);
-  float* sEf = reinterpret_cast<float*>(smem + L::O_EF);
-  float* sEra = reinterpret_cast<float*>(smem + L::O_ERA);
-  float* sGam = reinterpret_cast<float*>(smem + L::O_GAM);
-  float* sBeta = reinterpret_cast<float*>(smem + L::O_BETA);
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4;
-  const int H = p.num_heads, N = p.num_seqs;
-  const int h = blockIdx.x % H;
-  const int count = p.seq_first[N];
-  const int s_begin = (blockIdx.x / H) * p.chunks_per_block;
-  if (s_begin >= count) return;
-  const int s_end = min(count, s_begin + p.chunks_per_block);
-  const int64_t rs = (int64_t)H * D;  // elements between consecutive tokens
-  const int64_t hoff = (int64_t)h * D;
-  // Per-thread byte offsets of the factor-block pieces this thread stores.
-  constexpr int ES = (int)sizeof(E);
-  constexpr int PE = 16 / ES;              // elements per 16-byte piece
-  constexpr int RD = D / PE, RC = C / PE;  // pieces per [.][D] / [.][C] row
-  static_assert((C * RD) % 256 == 0 && (D * RC) % 256 == 0 && (C * RC) % 256 == 0, "piece counts");
-  const uint32_t utid = (uint32_t)tid;
-  const uint32_t g_off = utid * 16;
-  const uint32_t w_lds = (utid / RD) * (LDK * ES) + (utid % RD) * 16;
-  constexpr uint32_t W_STEP = (256 / RD) * LDK * ES;
-  const uint32_t c_lds = (utid / RC) * (LDT * ES) + (utid % RC) * 16;
-  constexpr uint32_t C_STEP = (256 / RC) * LDT * ES;
-  const uint32_t u_off = (uint32_t)(((2 * wv) * 64 + lane) * 16);
-  const E* gq = static_cast<const E*>(p.q);
-  const E* gk = static_cast<const E*>(p.k);
-  const E* gv = static_cast<const E*>(p.v);
-
-  // sequence of slot s: the largest n with seq_first[n] <= s (seq_first[N] > s)
-  auto seq_of = [&](int s) {
-    int lo = 0, hi = N;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.seq_first[mid] <= s) lo = mid;
-      else hi = mid;
-    }
-    return lo;
-  };
-  // token range of slot s (nn: a sequence at or before the one holding s)
-  auto slot_range = [&](int s, int& nn, int64_t& t0, int64_t& eos, int64_t& sbos) {
-    while (p.seq_first[nn + 1] <= s) ++nn;
-    const int64_t b = p.cu ? (int64_t)p.cu[nn] : 0;
-    const int64_t e = p.cu ? (int64_t)p.cu[nn + 1] : p.total_tokens;
-    t0 = b + (int64_t)(p.seq_c0[nn] + (s - p.seq_first[nn])) * C;
-    eos = min(e, t0 + C);
-    sbos = b;
-  };
-
-  // Prep role: channel group cg (channels 8cg .. 8cg+7) and token group tg
-  // (chunk rows TPL*tg .. +TPL-1).  The 16 lanes of a lane group hold one set
-  // of rows across all 128 channels; wave w holds rows 4*TPL*w .. +4*TPL-1,
-  // i.e. one 16-token tile (C = 64) or half of one (C = 32).
-  constexpr int TPL = C / 16;       // rows per prep thread
-  constexpr int WPT = 4 / TPL;      // waves per 16-token tile
-  const int cg = tid & 15, tg = tid >> 4, lg = g;
-  const int c8 = 8 * cg, r0 = TPL * tg;
-  float wq[8][4], wk[8][4];
-  if (PRO) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        wq[j][m] = p.conv_q_w ? p.conv_q_w[(hoff + c8 + j) * 4 + m] : (m == 3 ? 1.f : 0.f);
-        wk[j][m] = p.conv_k_w ? p.conv_k_w[(hoff + c8 + j) * 4 + m] : (m == 3 ? 1.f : 0.f);
-      }
-  }
-
-  // Global inputs of one chunk held by this thread (see Raw8).
-  constexpr int QR = TPL + (PRO ? 3 : 0);  // q / k rows (with conv history)
-  constexpr int VCG = DV / 8, VTPL = C * VCG / 256;
-  const int vcg = tid % VCG, vtg = tid / VCG;
-  Raw8<float> rla[TPL];
-  Raw8<E> rq[QR], rk[QR], rv[VTPL];
-  float rvb[VTPL], rb = 0.f;
-  auto issue_loads = [&](int64_t tc, int64_t eos, int64_t seq_bos) {
-    const int nvc = (int)((eos - tc) < C ? (eos - tc) : C);
-    const int64_t cb0 = tc * rs + hoff;
-#pragma unroll
-    for (int i = 0; i < TPL; ++i) ld_raw8(rla[i], p.log_alpha + cb0 + (int64_t)min(r0 + i, nvc - 1) * rs + c8);
-    const int64_t back = seq_bos - tc;  // <= 0
-    const int loc = back < -3 ? -3 : (int)back;
-#pragma unroll
-    for (int i = 0; i < QR; ++i) {
-      const int row = PRO ? min(max(r0 - 3 + i, loc), nvc - 1) : min(r0 + i, nvc - 1);
-      ld_raw8(rq[i], gq + cb0 + (int64_t)row * rs + c8);
-      ld_raw8(rk[i], gk + cb0 + (int64_t)row * rs + c8);
-    }
-#pragma unroll
-    for (int i = 0; i < VTPL; ++i) {
-      const int row = min(VTPL * vtg + i, nvc - 1);
-      ld_raw8(rv[i], gv + cb0 + (int64_t)row * rs + 8 * vcg);
-      rvb[i] = p.beta[(tc + row) * H + h];
-    }
-    if (tid < C) rb = p.beta[(tc + min(tid, nvc - 1)) * H + h];
-  };
-  int n = seq_of(s_begin);
-  int64_t t0, eos, seq_bos;
-  slot_range(s_begin, n, t0, eos, seq_bos);
-  issue_loads(t0, eos, seq_bos);
-
-  for (int s = s_begin; s < s_end; ++s) {
-    const int nv = (int)(eos - t0);
-    // Per-lane indices are re-derived from an opaque copy of the thread id in
-    // every chunk, so the LDS address arithmetic of the unrolled stages stays
-    // inside the loop instead of being hoisted into registers for the whole
-    // sequence.
-    int tidv = tid;
-    asm volatile("" : "+v"(tidv));
-    const int lane = tidv & 63, l16 = lane & 15, g = lane >> 4;
-    const int cg = tidv & 15, tg = tidv >> 4, lg = g;
-    const int c8 = 8 * cg, r0 = TPL * tg;
-    const int vcg = tidv % VCG, vtg = tidv / VCG;
-
-    // ---- P1: log-decay prefix sums relative to the first row of this wave ----
-    // decay kept in log2 units: every factor below is one exp2
-    const bool full = (nv == C);
-    float dl[TPL][8];
-    rows_from_raw<float, TPL>(dl, rla, r0, nv, full);
-#pragma unroll
-    for (int i = 0; i < TPL; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dl[i][j] *= 1.4426950408889634f;
-    {
-#pragma unroll
-      for (int i = 1; i < TPL; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dl[i][j] += dl[i - 1][j];
-      // exclusive prefix over the four lane groups (same channels, earlier rows)
-      float inc[8], tot[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        tot[j] = dl[TPL - 1][j];
-        float x = tot[j];
-        const float y1 = __shfl_up(x, 16);
-        if (lg >= 1) x += y1;
-        const float y2 = __shfl_up(x, 32);
-        if (lg >= 2) x += y2;
-        inc[j] = x;
-      }
-#pragma unroll
-      for (int i = 0; i < TPL; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dl[i][j] += inc[j] - tot[j];
-      if (lg == 3) st8(sTot + wv * D + c8, inc);  // total of this wave's rows
-    }
-
-    // ---- P2: q and k rows (raw, or through the prologue), beta V^T, beta ----
-    float qv[TPL][8], kv[TPL][8];
-    {
-      if (PRO) {
-        const int64_t back = seq_bos - t0;  // <= 0
-        const int lo = back < -3 ? -3 : (int)back;
-        if (p.conv_q_w)
-          prologue_from_raw<E, TPL>(qv, rq, r0, nv, lo, wq, p.l2_eps);
-        else
-          rows_from_raw<E, TPL>(qv, rq + (QR - TPL), r0, nv, full);
-        if (p.conv_k_w)
-          prologue_from_raw<E, TPL>(kv, rk, r0, nv, lo, wk, p.l2_eps);
-        else
-          rows_from_raw<E, TPL>(kv, rk + (QR - TPL), r0, nv, full);
-      } else {
-        rows_from_raw<E, TPL>(qv, rq, r0, nv, full);
-        rows_from_raw<E, TPL>(kv, rk, r0, nv, full);
-      }
-      // beta V^T: thread (vcg, vtg) moves columns 8 vcg .. +7 of rows VTPL*vtg .. +VTPL-1
-      float vv[VTPL][8];
-      rows_from_raw<E, VTPL>(vv, rv, VTPL * vtg, nv, full);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float col[VTPL];
-#pragma unroll
-        for (int i = 0; i < VTPL; ++i) col[i] = vv[i][j] * rvb[i];   // rows past nv are already zero
-        stN<VTPL>(sVt + cm_off<C, LDT>(8 * vcg + j, VTPL * vtg), col);
-      }
-      if (tid < C) sBeta[tid] = (tid < nv) ? rb : 0.f;
-    }
-    __syncthreads();
-
-    // the next slot's inputs load while this one is processed
-    int64_t t0n = 0, eosn = 0, bosn = 0;
-    if (s + 1 < s_end) {
-      slot_range(s + 1, n, t0n, eosn, bosn);
-      issue_loads(t0n, eosn, bosn);
-    }
-
-    // ---- P3: scaled operand tiles ----
-    {
-      // rho_a = cumulative log-decay before tile a, for this thread's 8 channels
-      float wt[4][8];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(sTot + w * D + c8);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(sTot + w * D + c8 + 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          wt[w][j] = x0[j];
-          wt[w][j + 4] = x1[j];
-        }
-      }
-      float rho[NT + 1][8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) rho[0][j] = 0.f;
-#pragma unroll
-      for (int a = 0; a < NT; ++a)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float t = 0.f;
-#pragma unroll
-          for (int w = a * WPT; w < (a + 1) * WPT; ++w) t += wt[w][j];
-          rho[a + 1][j] = rho[a][j] + t;
-        }
-      const int my_a = wv / WPT;
-      float ra[8], intra[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        ra[j] = rho[0][j];
-        intra[j] = 0.f;
-      }
-#pragma unroll
-      for (int a = 1; a < NT; ++a)
-        if (a == my_a)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) ra[j] = rho[a][j];
-      if (WPT == 2 && (wv & 1))
-#pragma unroll
-        for (int j = 0; j < 8; ++j) intra[j] = wt[wv - 1][j];
-      float ea[8], eb[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        ea[j] = exp2_fast(ra[j]);                  // e^{rho_a} <= 1
-        eb[j] = exp2_fast(rho[NT][j] - ra[j]);     // e^{g_n - rho_a} <= 1
-      }
-      float ktt[8][TPL], kbt[8][TPL];
-#pragma unroll
-      for (int i = 0; i < TPL; ++i) {
-        const int rr = r0 + i;
-        const float br = sBeta[rr];
-        float xq[8], xk[8], xi[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float d = dl[i][j] + intra[j];   // g_r - rho_a, in [-80, 0]
-          const float ep = exp2_fast(d), en = exp2_fast(-d);
-          xq[j] = qv[i][j] * ep;
-          xk[j] = kv[i][j] * ep;
-          xi[j] = kv[i][j] * en;
-          ktt[j][i] = xk[j] * ea[j] * br;   // beta Kt = beta K e^{g}
-          kbt[j][i] = xi[j] * eb[j];   // Kb = K e^{g_n - g}
-        }
-        st8_split(sQrh + rr * LDK + c8, sQrl + rr * LDK + c8, xq);
-        if constexpr (L::QT_OWN) {
-          float xt[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) xt[j] = xq[j] * ea[j];   // Qt = Q e^{g}
-          st8(sQt + rr * LDK + c8, xt);
-        }
-        st8_split(sKih + rr * LDK + c8, sKil + rr * LDK + c8, xi);
-        st8(sKrel + rr * LDK + c8, xk);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        stN<TPL>(sKtt + cm_off<C, LDT>(c8 + j, r0), ktt[j]);
-        stN<TPL>(sKbt + cm_off<C, LDT>(c8 + j, r0), kbt[j]);
-      }
-      // factor rows, one per token group: e^{g_n} (gamma), e^{rho_a} and
-      // e^{rho_a - rho_b} for b < a
-      static_assert(1 + NT + L::NOFF <= 16, "factor rows exceed the token groups");
-#pragma unroll
-      for (int idx = 0; idx < 1 + NT + L::NOFF; ++idx) {
-        if (tg == idx) {
-          float v8[8];
-          if (idx == 0) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v8[j] = exp2_fast(rho[NT][j]);
-            st8(sGam + c8, v8);
-          } else if (idx <= NT) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v8[j] = exp2_fast(rho[idx - 1][j]);
-            st8(sEra + (idx - 1) * D + c8, v8);
-          } else {
-            const int q = idx - 1 - NT, a = off_a(q), b = off_b(q);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v8[j] = exp2_fast(rho[a][j] - rho[b][j]);
-            st8(sEf + q * D + c8, v8);
-          }
-        }
-      }
-    }
-    __syncthreads();
-
-    // ---- P5: Gram tiles per 16-token tile pair (a, b <= a):
-    //      A_ab = Krel_a Kh_ab^T,  P_ab = Qrel_a Kh_ab^T  with Kh_ab = K_inv_b (.) e^{rho_a - rho_b}.
-    //      Wave w takes the diagonal pair (w, w) and the strictly-lower pairs q = w, w + 4.
-    //      With bf16 operands P is formed from the hi + lo parts of Q_rel, and of
-    //      K_inv on the diagonal (where it is not rescaled).
-    // ---- P6: each wave then inverts its own diagonal block, (I + A_ww)^{-1},
-    //      by fp32 forward substitution (lane j < 16 solves column j) while the
-    //      other waves are still on their Gram products.
-    {
-      constexpr int NOFF = L::NOFF;
-      constexpr int PPW = 1 + (NOFF + 3) / 4;  // pairs per wave (first one diagonal)
-      f32x4 ga[PPW], gp[PPW];
-      int pa[PPW], pb[PPW];
-#pragma unroll
-      for (int j = 0; j < PPW; ++j) {
-        ga[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        gp[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        const int q = wv + 4 * (j - 1);
-        const bool valid = (j == 0) ? (wv < NT) : (q < NOFF);
-        pa[j] = -1;
-        pb[j] = -1;
-        if (valid) {
-          const int a = (j == 0) ? wv : off_a(q), b = (j == 0) ? wv : off_b(q);
-          pa[j] = a;
-          pb[j] = b;
-          const int arow = (16 * a + l16) * LDK + 8 * g, brow = (16 * b + l16) * LDK + 8 * g;
-          const float* ef = sEf + (b < a ? off_idx(a, b) : 0) * D + 8 * g;
-#pragma unroll
-          for (int s = 0; s < D / 32; ++s) {
-            Frag<E> fk, fq, fbh;
-            ld_frag(fk, sKrel + arow + 32 * s);
-            ld_frag(fq, sQrh + arow + 32 * s);
-            ld_frag(fbh, sKih + brow + 32 * s);
-            if (b < a) {
-              float x[8];
-              frag_unpack(fbh, x);
-#pragma unroll
-              for (int jj = 0; jj < 8; ++jj) x[jj] *= ef[32 * s + jj];
-              frag_from_f32(fbh, x);
-            }
-            ga[j] = mma(ga[j], fk, fbh);
-            gp[j] = mma(gp[j], fq, fbh);
-            if constexpr (SPLIT) {
-              Frag<E> fql;
-              ld_frag(fql, sQrl + arow + 32 * s);
-              gp[j] = mma(gp[j], fql, fbh);
-              if (b == a) {
-                Frag<E> fbl;
-                ld_frag(fbl, sKil + brow + 32 * s);
-                gp[j] = mma(gp[j], fq, fbl);
-              }
-            }
-          }
-          if (j == 0) {
-            // Diag(beta) A_ww, strictly lower, to this wave's own fp32 block
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 16 * a + 4 * g + i;
-              sAd[(a * 16 + 4 * g + i) * L::AST + l16] = (l16 < 4 * g + i) ? ga[0][i] * sBeta[r] : 0.f;
-            }
-          }
-        }
-      }
-      float xinv[16];  // column `lane` of (I + A_ww)^{-1} (lanes < 16 of waves < NT)
-      if (wv < NT && lane < 16) {
-        const float* ab = sAd + wv * 16 * L::AST;
-        f32x4 av[16][4];
-#pragma unroll
-        for (int r = 1; r < 16; ++r)
-#pragma unroll
-          for (int q4 = 0; q4 < (r + 3) / 4; ++q4) av[r][q4] = *reinterpret_cast<const f32x4*>(ab + r * L::AST + 4 * q4);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          // four partial sums keep the dependency chains short
-          float part[4] = {(r == lane) ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int q4 = 0; q4 < (r + 3) / 4; ++q4)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (4 * q4 + e < r) part[e] -= av[r][q4][e] * xinv[4 * q4 + e];
-          xinv[r] = (part[0] + part[1]) + (part[2] + part[3]);
-        }
-      }
-      __syncthreads();  // every wave is done reading the Gram operands
-      if (wv < NT && lane < 16)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sM[(16 * wv + r) * LDT + 16 * wv + lane] = from_f32<E>(xinv[r]);
-#pragma unroll
-      for (int j = 0; j < PPW; ++j) {
-        const int a = pa[j], b = pb[j];
-        if (a >= 0) {
-          const int c = 16 * b + l16;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * a + 4 * g + i;
-            if (b < a) sM[r * LDT + c] = from_f32<E>(-ga[j][i] * sBeta[r]);   // -(Diag(beta) A)_ab
-            sP[r * LDT + c] = from_f32<E>(((b < a) || (c <= r)) ? gp[j][i] : 0.f);
-          }
-        }
-      }
-      // strictly-upper tiles of P are read by the 32-deep token steps: zero them
-      for (int e = tid; e < NOFF * 256; e += 256) {
-        const int q = e >> 8, a = off_a(q), b = off_b(q);
-        sP[(16 * b + ((e >> 4) & 15)) * LDT + 16 * a + (e & 15)] = from_f32<E>(0.f);
-      }
-      // Qt = (Q_rel hi + lo) e^{rho_a}, in place over the Q_rel slot (8 elements per step)
-      if constexpr (!L::QT_OWN)
-      for (int e = tid; e < C * (D / 8); e += 256) {
-        const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
-        float x[8];
-        Frag<E> f;
-        ld_frag(f, sQrh + r * LDK + c8);
-        frag_unpack(f, x);
-        if constexpr (SPLIT) {
-          float lv[8];
-          Frag<E> fl;
-          ld_frag(fl, sQrl + r * LDK + c8);
-          frag_unpack(fl, lv);
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) x[jj] += lv[jj];
-        }
-        const float* er = sEra + (r >> 4) * D + c8;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) x[jj] *= er[jj];
-        frag_from_f32(f, x);
-        st_frag(sQrh + r * LDK + c8, f);
-      }
-    }
-    __syncthreads();
-
-    // ---- P7: blocked forward substitution on the matrix cores,
-    //      (I + A) [W | U'] = Diag(beta) [Kt | V], tile row by tile row:
-    //      Y_a = (I + A_aa)^{-1} (beta R_a - sum_{b<a} A_ab Y_b).
-    //      Wave w solves W columns 32w .. 32w+31 and its own U' columns, so
-    //      every Y_b it needs is already in its registers.  W is stored
-    //      negated for the carried stage. ----
-    f32x4 accU[NT][NCT];
-    {
-      constexpr int NOWN = 2 + NCT;
-      // all LDS operands of the solve are fetched up front
-      Frag16<E> mfr[NT][NT], rfr[NOWN][NT];
-#pragma unroll
-      for (int a = 0; a < NT; ++a)
-#pragma unroll
-        for (int b = 0; b <= a; ++b) ld_frag16(mfr[a][b], sM + (16 * a + l16) * LDT + 16 * b + 4 * g);
-#pragma unroll
-      for (int o = 0; o < NOWN; ++o)
-#pragma unroll
-        for (int a = 0; a < NT; ++a) {
-          const E* src = (o < 2) ? sKtt + cm_off<C, LDT>(32 * wv + 16 * o + l16, 16 * a + 4 * g)
-                                 : sVt + cm_off<C, LDT>(wv * NCW + 16 * (o - 2) + l16, 16 * a + 4 * g);
-          ld_frag16(rfr[o][a], src);
-        }
-      f32x4 Y[NOWN][NT];
-      Frag16<E> Yb[NOWN][NT];
-#pragma unroll
-      for (int a = 0; a < NT; ++a) {
-        f32x4 z[NOWN];
-#pragma unroll
-        for (int o = 0; o < NOWN; ++o) z[o] = frag16_to_f32(rfr[o][a]);
-#pragma unroll
-        for (int b = 0; b < a; ++b)
-#pragma unroll
-          for (int o = 0; o < NOWN; ++o) z[o] = mma16(z[o], mfr[a][b], Yb[o][b]);
-#pragma unroll
-        for (int o = 0; o < NOWN; ++o) {
-          Frag16<E> zb;
-          frag16_from_acc(zb, z[o]);
-          Y[o][a] = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, mfr[a][a], zb);
-          frag16_from_acc(Yb[o][a], Y[o][a]);
-        }
-      }
-#pragma unroll
-      for (int o = 0; o < 2; ++o)
-#pragma unroll
-        for (int a = 0; a < NT; ++a)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sW[(16 * a + 4 * g + i) * LDK + 32 * wv + 16 * o + l16] = from_f32<E>(-Y[o][a][i]);
-#pragma unroll
-      for (int a = 0; a < NT; ++a)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) accU[a][ct] = Y[2 + ct][a];
-    }
-    __syncthreads();  // W visible to every wave
-
-    // ---- the factor block, as 16-byte pieces (piece tid + 256 j of each tile) ----
-    {
-      const Rsrc fb = make_rsrc(static_cast<char*>(p.factors) + ((size_t)s * H + h) * F::BYTES, (uint32_t)F::BYTES);
-#pragma unroll
-      for (int j = 0; j < C * RD / 256; ++j) {
-        buf_st16(*reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(sW) + w_lds + j * W_STEP),
-                 fb, g_off, (uint32_t)(F::W + 4096 * j));
-        buf_st16(*reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(sQt) + w_lds + j * W_STEP),
-                 fb, g_off, (uint32_t)(F::Q + 4096 * j));
-      }
-#pragma unroll
-      for (int j = 0; j < C * RC / 256; ++j)
-        buf_st16(*reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(sP) + c_lds + j * C_STEP),
-                 fb, g_off, (uint32_t)(F::P + 4096 * j));
-#pragma unroll
-      for (int j = 0; j < D * RC / 256; ++j)
-        buf_st16(*reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(sKbt) + c_lds + j * C_STEP),
-                 fb, g_off, (uint32_t)(F::K + 4096 * j));
-      if (tid < D / 4) buf_st16(*reinterpret_cast<const u32x4*>(sGam + 4 * tid), fb, g_off, (uint32_t)F::G);
-#pragma unroll
-      for (int a = 0; a < NT; ++a)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          buf_st16(__builtin_bit_cast(u32x4, accU[a][ct]), fb, u_off, (uint32_t)(F::U + (a * 8 + ct) * 1024));
-    }
-    t0 = t0n;
-    eos = eosn;
-    seq_bos = bosn;
-  }
-}
-
-template <typename E, int C, bool PRO>
-static hipError_t launch_prep_t(const PrepArgs& a, hipStream_t stream) {
-  constexpr size_t lds = PrefillLayout<E, C, D>::BYTES;
-  static_assert(lds <= 160 * 1024, "LDS budget exceeded");
-  auto fn = prep_kernel<E, C, PRO>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  const int64_t ranges = ((int64_t)a.cap + a.chunks_per_block - 1) / a.chunks_per_block;
-  const int64_t grid = ranges * a.num_heads;
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), lds, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
-  const bool pro = a.conv_q_w != nullptr || a.conv_k_w != nullptr;
-  if (a.bf16) return pro ? launch_prep_t<__bf16, 64, true>(a, stream) : launch_prep_t<__bf16, 64, false>(a, stream);
-  return pro ? launch_prep_t<float, 32, true>(a, stream) : launch_prep_t<float, 32, false>(a, stream);
-}
-
 // ---------------------------------------------------------------------------
 // Carry kernel.
 // ---------------------------------------------------------------------------
 template <typename E, int C, int DV>
 struct CarryLayout {
+  using F = FactorBlock<(int)sizeof(E), C>;
   static constexpr int PAD = 16 / (int)sizeof(E);
-  static constexpr int LDK = D + PAD;  // as the prep tiles, so the same operand reads apply
-  static constexpr int LDT = C + PAD;
   static constexpr int LDO = DV + PAD;
-  // one factor-block half
-  static constexpr size_t W = 0;
-  static constexpr size_t Q = al16(W + (size_t)C * LDK * sizeof(E));
-  static constexpr size_t P = al16(Q + (size_t)C * LDK * sizeof(E));
-  static constexpr size_t K = al16(P + (size_t)C * LDT * sizeof(E));
-  static constexpr size_t G = al16(K + (size_t)D * LDT * sizeof(E));
-  static constexpr size_t BUF = al16(G + (size_t)D * 4);
+  // one buffer: the factor block's operand part [0, F::U) copied verbatim
+  // (fragment order), rounded up to whole 4 KiB copy rounds
+  static constexpr size_t BUF = ((size_t)F::U + 4095) & ~(size_t)4095;
   // two output staging tiles [C][LDO] (chunk i in tile i % 2)
   static constexpr size_t OST = al16((size_t)C * LDO * sizeof(E));
   static constexpr size_t O = 2 * BUF;
@@ -685,15 +107,15 @@ __global__ __launch_bounds__(256) void carry_kernel(const CarryArgs p) {
   constexpr int KT = C / 32;     // 32-deep token steps per chunk
   constexpr int NCW = DV / 4;    // value columns per wave
   constexpr int NCT = NCW / 16;  // 16-wide column tiles per wave
-  constexpr int LDK = L::LDK, LDT = L::LDT, LDO = L::LDO;
+  constexpr int LDO = L::LDO;
   constexpr int ES = (int)sizeof(E);
   constexpr int PE = 16 / ES;                 // elements per 16-byte piece
-  constexpr int RD = D / PE, RC = C / PE;     // pieces per [.][D] / [.][C] row
   constexpr int RO = DV / PE;                 // pieces per output row of this block
-  constexpr int NWP = C * RD / 256, NPP = (C * RC + 255) / 256, NKP = D * RC / 256, NOP = C * RO / 256;
+  constexpr int NBP = (int)(L::BUF / 4096);   // 16-byte pieces per thread in one copy
+  constexpr int NOP = C * RO / 256;
   static_assert(!EPI || DV == D, "the epilogue normalises whole heads");
   static_assert(NCT >= 1 && KT >= 1 && NT <= 4, "unsupported tile shape");
-  static_assert((C * RD) % 256 == 0 && (D * RC) % 256 == 0 && (C * RO) % 256 == 0, "piece counts");
+  static_assert((C * RO) % 256 == 0, "piece counts");
   static_assert(L::BYTES <= 160 * 1024, "LDS budget exceeded");
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -717,6 +139,7 @@ __global__ __launch_bounds__(256) void carry_kernel(const CarryArgs p) {
   const int col0 = cb * DV + wv * NCW;  // first value column owned by this wave
   E* go = static_cast<E*>(p.o);
   const char* fbase = static_cast<const char*>(p.factors);
+  const uint32_t lane_fr = (uint32_t)lane * 8 * ES;
 
   // State slice: tile (rt8, ct) holds rows 16 rt8 + 4g + i, column col0 + 16 ct + l16.
   f32x4 accS[8][NCT];
@@ -730,37 +153,21 @@ __global__ __launch_bounds__(256) void carry_kernel(const CarryArgs p) {
         accS[rt8][ct][i] =
             p.state_in ? p.state_in[sbase + (size_t)(16 * rt8 + 4 * g + i) * D + col0 + 16 * ct + l16] : 0.f;
 
-  // Per-thread byte offsets of the 16-byte pieces this thread moves (piece
-  // tid + 256 j of each tile), in the factor block and in an LDS half.
-  const uint32_t utid = (uint32_t)tid;
-  const uint32_t g_off = utid * 16;
-  const uint32_t w_lds = (utid / RD) * (LDK * ES) + (utid % RD) * 16;
-  constexpr uint32_t W_STEP = (256 / RD) * LDK * ES;
-  const uint32_t c_lds = (utid / RC) * (LDT * ES) + (utid % RC) * 16;
-  constexpr uint32_t C_STEP = (256 / RC) * LDT * ES;
+  // One chunk's factor block in flight: the operand part as 16-byte pieces
+  // (piece tid + 256 j), and this wave's U' columns in accumulator order.
+  const uint32_t p_off = (uint32_t)tid * 16;
   const uint32_t u_off = (uint32_t)(((col0 / 16) * 64 + lane) * 16);
-
-  // One chunk's factor block in flight: 16-byte pieces of the tiles, and this
-  // wave's U' columns in accumulator order.
-  u32x4 rW[NWP], rQ[NWP], rP[NPP], rK[NKP], rG;
+  u32x4 rB[NBP];
   f32x4 rU[NT][NCT];
   auto load_block = [&](int ci) {
-    const Rsrc rb = make_rsrc(fbase + ((size_t)(slot0 + ci) * H + h) * F::BYTES, (uint32_t)F::BYTES);
+    const Rsrc rb = make_rsrc(fbase + ((size_t)(slot0 + ci) * H + h) * F::BYTES, F::BYTES);
 #pragma unroll
-    for (int j = 0; j < NWP; ++j) {
-      rW[j] = buf_ld16(rb, g_off, (uint32_t)(F::W + 4096 * j));
-      rQ[j] = buf_ld16(rb, g_off, (uint32_t)(F::Q + 4096 * j));
-    }
-#pragma unroll
-    for (int j = 0; j < NPP; ++j) rP[j] = buf_ld16(rb, g_off, (uint32_t)(F::P + 4096 * j));  // past the tile: 0
-#pragma unroll
-    for (int j = 0; j < NKP; ++j) rK[j] = buf_ld16(rb, g_off, (uint32_t)(F::K + 4096 * j));
-    rG = buf_ld16(rb, g_off, (uint32_t)F::G);  // threads >= 32 read U' bytes, unused
+    for (int j = 0; j < NBP; ++j) rB[j] = buf_ld16(rb, p_off, (uint32_t)(4096 * j));
 #pragma unroll
     for (int a = 0; a < NT; ++a)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
-        rU[a][ct] = __builtin_bit_cast(f32x4, buf_ld16(rb, u_off, (uint32_t)(F::U + (a * 8 + ct) * 1024)));
+        rU[a][ct] = __builtin_bit_cast(f32x4, buf_ld16(rb, u_off, F::U + (uint32_t)(a * 8 + ct) * 1024));
   };
   // Output rows of chunk ci (staged in LDS tile ci % 2) to global memory.
   auto flush_o = [&](int ci) {
@@ -781,27 +188,18 @@ __global__ __launch_bounds__(256) void carry_kernel(const CarryArgs p) {
     const int64_t t0 = seq_bos + (int64_t)(c0 + ci) * C;
     const int nv = (int)min((int64_t)C, seq_eos - t0);
     unsigned char* buf = smem + (ci & 1) * L::BUF;
-    E* sW = reinterpret_cast<E*>(buf + L::W);
-    E* sQt = reinterpret_cast<E*>(buf + L::Q);
-    E* sP = reinterpret_cast<E*>(buf + L::P);
-    E* sKbt = reinterpret_cast<E*>(buf + L::K);
-    float* sGam = reinterpret_cast<float*>(buf + L::G);
+    const E* sW = reinterpret_cast<const E*>(buf + F::W + lane_fr);
+    const E* sQt = reinterpret_cast<const E*>(buf + F::Q + lane_fr);
+    const E* sP = reinterpret_cast<const E*>(buf + F::P + lane_fr);
+    const E* sKbt = reinterpret_cast<const E*>(buf + F::K + lane_fr);
+    const float* sGam = reinterpret_cast<const float*>(buf + F::G);
+    constexpr int FRE = (int)F::FR / ES;  // elements per fragment
     E* sO = reinterpret_cast<E*>(smem + L::O + (ci & 1) * L::OST);
 
     // ---- factor block into this chunk's LDS half (the other half may still
     //      be read by waves finishing the previous chunk) ----
 #pragma unroll
-    for (int j = 0; j < NWP; ++j) {
-      *reinterpret_cast<u32x4*>(buf + L::W + w_lds + j * W_STEP) = rW[j];
-      *reinterpret_cast<u32x4*>(buf + L::Q + w_lds + j * W_STEP) = rQ[j];
-    }
-#pragma unroll
-    for (int j = 0; j < NPP; ++j)
-      if ((C * RC) % 256 == 0 || tid + 256 * j < C * RC)
-        *reinterpret_cast<u32x4*>(buf + L::P + c_lds + j * C_STEP) = rP[j];
-#pragma unroll
-    for (int j = 0; j < NKP; ++j) *reinterpret_cast<u32x4*>(buf + L::K + c_lds + j * C_STEP) = rK[j];
-    if (tid < D / 4) *reinterpret_cast<u32x4*>(buf + L::G + g_off) = rG;
+    for (int j = 0; j < NBP; ++j) *reinterpret_cast<u32x4*>(buf + p_off + 4096 * j) = rB[j];
     f32x4 accU[NT][NCT];
 #pragma unroll
     for (int a = 0; a < NT; ++a)
@@ -822,7 +220,7 @@ __global__ __launch_bounds__(256) void carry_kernel(const CarryArgs p) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         Frag<E> fa;
-        ld_frag_perm(fa, sW + (16 * rt + l16) * LDK + 32 * ks + 4 * g);   // W is stored negated
+        ld_frag(fa, sW + (rt * 4 + ks) * FRE);   // W is stored negated
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) accU[rt][ct] = mma(accU[rt][ct], fa, sf[ks][ct]);
       }
@@ -838,7 +236,7 @@ __global__ __launch_bounds__(256) void carry_kernel(const CarryArgs p) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         Frag<E> fa;
-        ld_frag_perm(fa, sQt + (16 * rt + l16) * LDK + 32 * ks + 4 * g);
+        ld_frag(fa, sQt + (rt * 4 + ks) * FRE);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) accO[rt][ct] = mma(accO[rt][ct], fa, sf[ks][ct]);
       }
@@ -853,7 +251,7 @@ __global__ __launch_bounds__(256) void carry_kernel(const CarryArgs p) {
       for (int kt = 0; kt < KT; ++kt) {
         if (kt <= (16 * rt + 15) / 32) {
           Frag<E> fa;
-          ld_frag_perm(fa, sP + (16 * rt + l16) * LDT + 32 * kt + 4 * g);
+          ld_frag(fa, sP + F::p_frag(rt, kt) * FRE);
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) accO[rt][ct] = mma(accO[rt][ct], fa, uf[kt][ct]);
         }
@@ -908,8 +306,7 @@ __global__ __launch_bounds__(256) void carry_kernel(const CarryArgs p) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         Frag<E> fa;
-        ld_frag_pair(fa, sKbt + cm_off<C, LDT>(16 * rt8 + l16, 32 * kt + 4 * g),
-                     sKbt + cm_off<C, LDT>(16 * rt8 + l16, 32 * kt + 16 + 4 * g));
+        ld_frag(fa, sKbt + (rt8 * KT + kt) * FRE);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) accS[rt8][ct] = mma(accS[rt8][ct], fa, uf[kt][ct]);
       }

@@ -7,6 +7,26 @@
 
 namespace kda {
 
+// Raw buffer views: out-of-range offsets read zero and drop writes.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// `bytes` bytes at p (word 3: the raw 32-bit access format).
+__device__ __forceinline__ Rsrc make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld16(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ void buf_st16(u32x4 v, Rsrc r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ void buf_st8(u32x2 v, Rsrc r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ void buf_st4(float v, Rsrc r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)voff, (int)soff, 0);
+}
+
 __host__ __device__ constexpr size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
 __host__ __device__ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 

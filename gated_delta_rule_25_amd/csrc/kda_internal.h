@@ -69,26 +69,46 @@ struct ScanArgs {
 // Two-kernel chunked prefill.  The prep kernel turns every (chunk, head) of
 // the inputs into a factor block, independently of the state; the carry
 // kernel walks each (sequence, head) through its chunks with the state.
-// Chunk length: 64 tokens for bf16 I/O, 32 for fp32.
-// Factor block of one (chunk, head), ES = element bytes of the I/O dtype:
-//   W  [C][128]  -W, token-major                       (ES each)
-//   Q  [C][128]  Qt = Q (.) e^{g}, token-major          (ES)
-//   P  [C][C]    lower-incl(Qt Kh^T), upper part zero   (ES)
-//   K  [128][C]  Kb^T channel-major; the 8-token units of row r are in the
-//                XOR order of the LDS tile (unit u stored at u ^ (r / 8))  (ES)
-//   G  [128]     e^{g_n} per key channel                (fp32)
-//   U  [C/16][8][64][4]  U' = T V in MFMA accumulator order: token tile a,
-//                column tile ct, lane, element i = (token 16a + 4(lane/16) + i,
-//                column 16 ct + lane % 16)              (fp32)
+// Chunk length C: 64 tokens for bf16 I/O, 32 for fp32 (NT = C / 16 token tiles).
+//
+// Factor block of one (chunk, head).  Every matrix operand is stored in the
+// order in which the carry kernel's matrix-core steps consume it: a fragment
+// is 64 lanes x 8 elements of the I/O dtype, lane-linear (FR bytes).  Lane l
+// (row l % 16 of a 16-row tile, group g = l / 16) of a fragment over the
+// 32-deep contraction step k0 holds the contraction indices
+// k0 + 4g + {0..3} (elements 0..3) and k0 + 16 + 4g + {0..3} (elements 4..7).
+//   W  [NT][4]    -W (W = T Kt): row tile rt = tokens 16 rt + l % 16,
+//                 step ks over the key channels
+//   Q  [NT][4]    Qt = Q (.) e^{g}, same order
+//   P  [NP]       lower-incl(Qt Kh^T): (rt, kt) for kt <= rt / 2 in that
+//                 order; rows tokens of tile rt, step kt over the tokens
+//                 (entries above the diagonal are zero)
+//   K  [8][C/32]  Kb^T: row tile rt8 = key channels 16 rt8 + l % 16, step kt
+//                 over the tokens
+//   G  [128]      e^{g_n} per key channel (fp32)
+//   U  [NT][8][64][4]  U' = T V in accumulator order: token tile a, column
+//                 tile ct, lane, element i = (token 16 a + 4 (lane / 16) + i,
+//                 column 16 ct + lane % 16)  (fp32)
 template <int ES, int C>
 struct FactorBlock {
-  static constexpr size_t W = 0;
-  static constexpr size_t Q = (size_t)C * 128 * ES;
-  static constexpr size_t P = 2 * (size_t)C * 128 * ES;
-  static constexpr size_t K = P + (size_t)C * C * ES;
-  static constexpr size_t G = K + (size_t)128 * C * ES;
-  static constexpr size_t U = G + 128 * 4;
-  static constexpr size_t BYTES = (U + (size_t)C * 128 * 4 + 255) & ~(size_t)255;
+  static constexpr int NT = C / 16;
+  static constexpr int KT = C / 32;
+  static constexpr uint32_t FR = 512u * ES;
+  __host__ __device__ static constexpr int p_before(int rt) {
+    int n = 0;
+    for (int r = 0; r < rt; ++r) n += (r / 2 + 1 < KT) ? (r / 2 + 1) : KT;
+    return n;
+  }
+  static constexpr int NP = p_before(NT);
+  // fragment index of P (rt, kt), kt <= rt / 2
+  __host__ __device__ static constexpr int p_frag(int rt, int kt) { return p_before(rt) + kt; }
+  static constexpr uint32_t W = 0;
+  static constexpr uint32_t Q = W + NT * 4 * FR;
+  static constexpr uint32_t P = Q + NT * 4 * FR;
+  static constexpr uint32_t K = P + NP * FR;
+  static constexpr uint32_t G = K + 8 * KT * FR;
+  static constexpr uint32_t U = G + 128 * 4;
+  static constexpr uint32_t BYTES = (U + NT * 8 * 1024 + 255) & ~255u;
 };
 constexpr int chunk_len(bool bf16) { return bf16 ? 64 : 32; }
 constexpr size_t factor_block_bytes(bool bf16) {

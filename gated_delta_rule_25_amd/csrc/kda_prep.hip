@@ -1,0 +1,641 @@
+// kda_prep.hip — token-parallel stage of the two-kernel chunked prefill (gfx950).
+//
+// Method ("Kimi K3 架构、训练与系统全景解析", section 4.2.4: the chunkwise form
+// with the UT transform; section 4.2.5: the decay lower bound that keeps every
+// exponent of a 16-token tile in [-80, 0]).  For a chunk of C tokens with
+// per-channel cumulative log-decay g (within the chunk):
+//   Kt = K (.) e^{g},  Qt = Q (.) e^{g},  Kh = K (.) e^{-g},  Kb = K (.) e^{g_n - g}
+//   A  = strictly-lower( Diag(beta) Kt Kh^T ),   (I + A) [W | U'] = Diag(beta) [Kt | V]
+//   P  = lower-incl( Qt Kh^T )
+// None of it depends on the state, so every (chunk, head) is done at once here
+// and written to the factor store; the carry kernel applies the state.
+//
+// Work split.  A workgroup of NT waves (NT = C / 16: four for bf16 I/O with
+// 64-token chunks, two for fp32 with 32-token chunks) handles a run of chunks
+// of one head.  Wave w owns token tile w.  Lane (r = l % 16, g = l / 16)
+// holds token 16 w + r and the 32 channels
+//     ch(s, e) = 32 s + 4 g + (e & 3) + 16 (e >> 2),    s = 0..3, e = 0..7,
+// which is the operand fragment of a 32-deep matrix-core step over the
+// channels (kda_device.h, d-permuted set).  So:
+//   - the Gram products A_ab, P_ab (row tile a, column tile b <= a) take the
+//     row tile's operands from registers; column tiles b < a come through LDS
+//     once, pre-scaled by the producing wave;
+//   - Qt leaves in exactly the carry kernel's fragment order;
+//   - transposes (token-per-lane <-> channel-per-lane) run on the matrix cores
+//     as products with 0/1 selection matrices, which are exact.
+// Exponents: a tile's rows are referenced to the decay before the tile (rho_a)
+// or after it (rho_{a+1}), so every factor formed is <= 1 except the diagonal
+// tile's e^{rho_a - g} <= e^{80}, which is exactly the pages' bound.
+//
+// Per chunk: loads and the in-tile decay scan (DPP row shifts); barrier;
+// per-channel factors (e^{tot_a}, e^{rho_a}, e^{g_n - rho_{a+1}}, e^{g_n});
+// barrier; operand fragments, Qt and Kb^T stores, scaled column-tile copies
+// and the solve's right-hand sides to LDS; barrier; Gram products and the
+// fp32 inverse of the diagonal block; P stores and the solve's blocks to LDS;
+// barrier; blocked forward substitution on the matrix cores, -W and U' stores.
+#include <type_traits>
+
+#include "kda_chunk_util.h"
+
+namespace kda {
+
+namespace {
+
+// 4 consecutive elements of one row: 8 bytes (bf16) or 16 bytes (fp32).
+template <typename E>
+struct Raw4;
+template <>
+struct Raw4<__bf16> {
+  bf16x4 v;
+};
+template <>
+struct Raw4<float> {
+  f32x4 v;
+};
+__device__ __forceinline__ void ld_raw4(Raw4<__bf16>& x, const __bf16* p) { x.v = *reinterpret_cast<const bf16x4*>(p); }
+__device__ __forceinline__ void ld_raw4(Raw4<float>& x, const float* p) { x.v = *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void cvt_raw4(float* y, const Raw4<__bf16>& x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = (float)x.v[i];
+}
+__device__ __forceinline__ void cvt_raw4(float* y, const Raw4<float>& x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = x.v[i];
+}
+
+// Inclusive prefix sum over the 16 lanes of a row (DPP row shifts, zero fill).
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row_scan(float x) {
+  x += row_shr<1>(x);
+  x += row_shr<2>(x);
+  x += row_shr<4>(x);
+  x += row_shr<8>(x);
+  return x;
+}
+
+// Piece pc = 2 s + h of a lane's channels: channels 32 s + 16 h + 4 g + {0..3}.
+__device__ __forceinline__ int piece_ch(int pc, int g) { return 32 * (pc >> 1) + 16 * (pc & 1) + 4 * g; }
+
+// Fragment of step s from the lane's per-piece values x[8][4].
+__device__ __forceinline__ void frag_step(Frag<__bf16>& f, const float (&x)[8][4], int s) {
+  f.v = (bf16x8){(__bf16)x[2 * s][0], (__bf16)x[2 * s][1], (__bf16)x[2 * s][2], (__bf16)x[2 * s][3],
+                 (__bf16)x[2 * s + 1][0], (__bf16)x[2 * s + 1][1], (__bf16)x[2 * s + 1][2], (__bf16)x[2 * s + 1][3]};
+}
+__device__ __forceinline__ void frag_step(Frag<float>& f, const float (&x)[8][4], int s) {
+  f.lo = (f32x4){x[2 * s][0], x[2 * s][1], x[2 * s][2], x[2 * s][3]};
+  f.hi = (f32x4){x[2 * s + 1][0], x[2 * s + 1][1], x[2 * s + 1][2], x[2 * s + 1][3]};
+}
+// hi + lo split of the same step (bf16); fp32 operands are exact, lo unused.
+__device__ __forceinline__ void frag_step_split(Frag<__bf16>& hi, Frag<__bf16>& lo, const float (&x)[8][4], int s) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float v = x[2 * s + (e >> 2)][e & 3];
+    const __bf16 b = (__bf16)v;
+    hi.v[e] = b;
+    lo.v[e] = (__bf16)(v - (float)b);
+  }
+}
+__device__ __forceinline__ void frag_step_split(Frag<float>& hi, Frag<float>&, const float (&x)[8][4], int s) {
+  frag_step(hi, x, s);
+}
+
+// B operand that picks channel 32 s + 16 h + (l % 16) out of an x32 step:
+// lane (j, g) has a one at element 4 h + (j - 4 g) when 0 <= j - 4 g < 4.
+template <typename E>
+__device__ __forceinline__ Frag<E> select_frag(int h, int lane) {
+  float x[8];
+  const int j = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = ((e >> 2) == h && 4 * g + (e & 3) == j) ? 1.f : 0.f;
+  Frag<E> f;
+  frag_from_f32(f, x);
+  return f;
+}
+// 16 x 16 identity as the B operand of an x16 step.
+template <typename E>
+__device__ __forceinline__ Frag16<E> ident16(int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  f32x4 x;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = (4 * g + e == j) ? 1.f : 0.f;
+  Frag16<E> f;
+  frag16_from_acc(f, x);
+  return f;
+}
+
+// Stores into the factor block (buffer view: out-of-range offsets are dropped).
+__device__ __forceinline__ void st_frag_g(Rsrc rb, uint32_t off, const Frag<__bf16>& f) {
+  buf_st16(__builtin_bit_cast(u32x4, f.v), rb, off, 0);
+}
+__device__ __forceinline__ void st_frag_g(Rsrc rb, uint32_t off, const Frag<float>& f) {
+  buf_st16(__builtin_bit_cast(u32x4, f.lo), rb, off, 0);
+  buf_st16(__builtin_bit_cast(u32x4, f.hi), rb, off + 16, 0);
+}
+// Four values as one half of a lane's fragment entry.
+__device__ __forceinline__ void st_half_g(Rsrc rb, uint32_t off, f32x4 x, __bf16*) {
+  const bf16x4 b = (bf16x4){(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+  buf_st8(__builtin_bit_cast(u32x2, b), rb, off, 0);
+}
+__device__ __forceinline__ void st_half_g(Rsrc rb, uint32_t off, f32x4 x, float*) {
+  buf_st16(__builtin_bit_cast(u32x4, x), rb, off, 0);
+}
+
+template <typename E, int C>
+struct PrepLayout {
+  static constexpr int NT = C / 16;
+  static constexpr int NPAIR = NT * (NT - 1) / 2;
+  static constexpr int ES = (int)sizeof(E);
+  static constexpr int LDM = C + 16 / ES;                      // sM row stride (elements)
+  static constexpr size_t TOT = 0;                             // f32 [NT][128] tile decay totals (log2)
+  static constexpr size_t FE = TOT + (size_t)NT * 128 * 4;     // f32 [NT][128] e^{tot_a}
+  static constexpr size_t FA = FE + (size_t)NT * 128 * 4;      // f32 [NT][128] e^{rho_a}
+  static constexpr size_t FB = FA + (size_t)NT * 128 * 4;      // f32 [NT][128] e^{g_n - rho_{a+1}}
+  static constexpr size_t BETA = FB + (size_t)NT * 128 * 4;    // f32 [C]
+  static constexpr size_t KE = BETA + (size_t)C * 4;           // [NPAIR][4][64] fragments
+  static constexpr size_t R = KE + (size_t)NPAIR * 4 * 64 * 8 * ES;  // [16][NT][64][4] right-hand sides
+  static constexpr size_t AD = R + (size_t)16 * NT * 64 * 4 * ES;    // f32 [NT][16][16] diagonal blocks
+  static constexpr size_t M = AD + (size_t)NT * 256 * 4;             // E [C][LDM] solve blocks
+  static constexpr size_t BYTES = M + (size_t)C * LDM * ES;
+};
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Workgroup (range, head h) handles the consecutive slots
+// [range * chunks_per_block, ...) of head h.
+// ---------------------------------------------------------------------------
+template <typename E, int C, bool PRO>
+__global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
+  using L = PrepLayout<E, C>;
+  using F = FactorBlock<(int)sizeof(E), C>;
+  constexpr int NT = C / 16;          // token tiles = waves
+  constexpr int NTH = 64 * NT;
+  constexpr int CPW = 8 / NT;         // W (and U') column tiles per wave in the solve
+  constexpr int NOWN = 2 * CPW;
+  constexpr bool SPLIT = sizeof(E) == 2;
+  constexpr int ES = (int)sizeof(E);
+  constexpr float LOG2E = 1.4426950408889634f;
+  static_assert(NT == 2 || NT == 4, "chunk of 32 or 64 tokens");
+  static_assert(L::BYTES <= 80 * 1024, "two workgroups per compute unit");
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* sTot = reinterpret_cast<float*>(smem + L::TOT);
+  float* sFE = reinterpret_cast<float*>(smem + L::FE);
+  float* sFA = reinterpret_cast<float*>(smem + L::FA);
+  float* sFB = reinterpret_cast<float*>(smem + L::FB);
+  float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
+  unsigned char* sKE = smem + L::KE;
+  unsigned char* sR = smem + L::R;
+  float* sAd = reinterpret_cast<float*>(smem + L::AD);
+  E* sM = reinterpret_cast<E*>(smem + L::M);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
+  const int H = p.num_heads, N = p.num_seqs;
+  const int h = blockIdx.x % H;
+  const int count = p.seq_first[N];
+  const int s_begin = (blockIdx.x / H) * p.chunks_per_block;
+  if (s_begin >= count) return;
+  const int s_end = min(count, s_begin + p.chunks_per_block);
+  const int64_t rs = (int64_t)H * D;  // elements between consecutive tokens
+  const int64_t hoff = (int64_t)h * D;
+  const E* gq = static_cast<const E*>(p.q);
+  const E* gk = static_cast<const E*>(p.k);
+  const E* gv = static_cast<const E*>(p.v);
+  const int tok = 16 * w + r;  // this lane's token within the chunk
+  const uint32_t lane_fr = (uint32_t)lane * 8 * ES;  // lane's entry in a fragment
+
+  // sequence of slot s: the largest n with seq_first[n] <= s (seq_first[N] > s)
+  int n = 0;
+  {
+    int hi = N;
+    while (hi - n > 1) {
+      const int mid = (n + hi) >> 1;
+      if (p.seq_first[mid] <= s_begin) n = mid;
+      else hi = mid;
+    }
+  }
+
+  for (int s = s_begin; s < s_end; ++s) {
+    while (p.seq_first[n + 1] <= s) ++n;
+    const int64_t seq_bos = p.cu ? (int64_t)p.cu[n] : 0;
+    const int64_t seq_eos = p.cu ? (int64_t)p.cu[n + 1] : p.total_tokens;
+    const int64_t t0 = seq_bos + (int64_t)(p.seq_c0[n] + (s - p.seq_first[n])) * C;
+    const int nv = (int)min((int64_t)C, seq_eos - t0);
+    const bool valid = tok < nv;
+    const int64_t row = t0 + min(tok, nv - 1);
+    const int64_t base = row * rs + hoff;
+    const Rsrc fb = make_rsrc(static_cast<char*>(p.factors) + ((size_t)s * H + h) * F::BYTES, F::BYTES);
+
+    // ---- inputs of this lane's token (q and k after the prologue when it
+    //      runs; kept in the input dtype otherwise) ----
+    using QK = std::conditional_t<PRO, Raw4<float>, Raw4<E>>;
+    QK rq[8], rk[8];
+    Raw4<E> rv[8];
+    float dl[8][4];
+    {
+      Raw4<float> rla[8];
+#pragma unroll
+      for (int pc = 0; pc < 8; ++pc) {
+        ld_raw4(rla[pc], p.log_alpha + base + piece_ch(pc, g));
+        ld_raw4(rv[pc], gv + base + piece_ch(pc, g));
+      }
+      if constexpr (PRO) {
+        // causal depthwise conv over rows tok-3 .. tok (zero before the
+        // sequence start), SiLU, then L2 over the head's 128 channels
+        const int lo = (int)(seq_bos - t0);  // first row of the sequence, <= 0
+        auto prologue = [&](QK (&y)[8], const E* src, const float* wconv) {
+          float ss = 0.f;
+#pragma unroll
+          for (int pc = 0; pc < 8; ++pc) {
+            Raw4<E> raw[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              const int rr = min(max(tok - 3 + m, lo), nv - 1);
+              ld_raw4(raw[m], src + (t0 + rr) * rs + hoff + piece_ch(pc, g));
+            }
+            float x[4][4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              cvt_raw4(x[m], raw[m]);
+              if (tok - 3 + m < lo)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[m][i] = 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float c = x[3][i];
+              if (wconv) {
+                const float* wc = wconv + (hoff + piece_ch(pc, g) + i) * 4;
+                c = wc[0] * x[0][i] + wc[1] * x[1][i] + wc[2] * x[2][i] + wc[3] * x[3][i];
+                c = c * sigmoidf_fast(c);
+                ss += c * c;
+              }
+              y[pc].v[i] = c;
+            }
+          }
+          if (wconv) {
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
+            const float inv = rsqrtf(ss + p.l2_eps);
+#pragma unroll
+            for (int pc = 0; pc < 8; ++pc) y[pc].v *= inv;
+          }
+        };
+        prologue(rq, gq, p.conv_q_w);
+        prologue(rk, gk, p.conv_k_w);
+      } else {
+#pragma unroll
+        for (int pc = 0; pc < 8; ++pc) {
+          ld_raw4(rq[pc], gq + base + piece_ch(pc, g));
+          ld_raw4(rk[pc], gk + base + piece_ch(pc, g));
+        }
+      }
+#pragma unroll
+      for (int pc = 0; pc < 8; ++pc) cvt_raw4(dl[pc], rla[pc]);
+    }
+    const float bt = valid ? p.beta[row * H + h] : 0.f;
+    if (!valid) {
+#pragma unroll
+      for (int pc = 0; pc < 8; ++pc) {
+        rq[pc].v = 0;
+        rk[pc].v = 0;
+        rv[pc].v = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dl[pc][i] = 0.f;
+      }
+    }
+
+    // ---- decay, in log2 units, relative to the start of this lane's tile ----
+#pragma unroll
+    for (int pc = 0; pc < 8; ++pc)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dl[pc][i] = row_scan(dl[pc][i] * LOG2E);
+    if (r == 15)
+#pragma unroll
+      for (int pc = 0; pc < 8; ++pc)
+        *reinterpret_cast<f32x4*>(sTot + w * 128 + piece_ch(pc, g)) =
+            (f32x4){dl[pc][0], dl[pc][1], dl[pc][2], dl[pc][3]};
+    if (g == 0) sBeta[tok] = bt;
+    __syncthreads();
+
+    // ---- per-channel factors (rho_a: decay before tile a; rho_NT = g_n) ----
+    for (int idx = tid; idx < 256; idx += NTH) {
+      const int c = idx & 127, part = idx >> 7;
+      float rho[NT + 1];
+      rho[0] = 0.f;
+#pragma unroll
+      for (int a = 0; a < NT; ++a) rho[a + 1] = rho[a] + sTot[a * 128 + c];
+      if (part == 0) {
+#pragma unroll
+        for (int a = 0; a < NT; ++a) sFE[a * 128 + c] = exp2_fast(rho[a + 1] - rho[a]);
+        buf_st4(exp2_fast(rho[NT]), fb, F::G + 4 * c, 0);  // gamma = e^{g_n}
+      } else {
+#pragma unroll
+        for (int a = 0; a < NT; ++a) {
+          sFA[a * 128 + c] = exp2_fast(rho[a]);
+          sFB[a * 128 + c] = exp2_fast(rho[NT] - rho[a + 1]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- per 32-channel step: operand fragments of the own tile, Qt, Kb^T,
+    //      scaled column-tile copies, right-hand sides ----
+    Frag<E> kr[4], qh[4], ql[4], kih[4], kil[4];
+    {
+      const Frag<E> sel0 = select_frag<E>(0, lane), sel1 = select_frag<E>(1, lane);
+      // the step's 8 channels of a [128] factor table
+      auto fac8 = [&](float (&y)[8], const float* v, int st) {
+        const f32x4 t0v = *reinterpret_cast<const f32x4*>(v + piece_ch(2 * st, g));
+        const f32x4 t1v = *reinterpret_cast<const f32x4*>(v + piece_ch(2 * st + 1, g));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          y[i] = t0v[i];
+          y[4 + i] = t1v[i];
+        }
+      };
+      auto frag8 = [](Frag<E>& f, const float (&x)[8]) { frag_from_f32(f, x); };
+      // channel-per-lane copy of 16 of the step's channels (half hh) via a
+      // selection product: lane (channel 32 st + 16 hh + l % 16, tokens 4g..4g+3)
+      auto select = [&](const Frag<E>& a, int hh) {
+        return mma((f32x4){0.f, 0.f, 0.f, 0.f}, a, hh ? sel1 : sel0);
+      };
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        float q8[8], k8[8], v8[8], ep[8], en[8], fac[8], x[8], y[8];
+        cvt_raw4(q8, rq[2 * st]);
+        cvt_raw4(q8 + 4, rq[2 * st + 1]);
+        cvt_raw4(k8, rk[2 * st]);
+        cvt_raw4(k8 + 4, rk[2 * st + 1]);
+        cvt_raw4(v8, rv[2 * st]);
+        cvt_raw4(v8 + 4, rv[2 * st + 1]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float d = dl[2 * st + (e >> 2)][e & 3];
+          ep[e] = exp2_fast(d);    // e^{g - rho_w} <= 1
+          en[e] = exp2_fast(-d);   // e^{rho_w - g} <= e^{80}
+        }
+        // K_rel (A operand of the Gram products); beta Kt = beta K_rel e^{rho_w}
+        // and beta V as channel-per-lane right-hand sides, sR[ct][w]
+        fac8(fac, sFA + w * 128, st);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = k8[e] * ep[e];
+        frag8(kr[st], x);
+        Frag<E> a;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = x[e] * fac[e] * bt;
+        frag8(a, y);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          Frag16<E> b;
+          frag16_from_acc(b, select(a, hh));
+          *reinterpret_cast<decltype(b.v)*>(sR + ((size_t)((2 * st + hh) * NT + w) * 64 + lane) * 4 * ES) = b.v;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = v8[e] * bt;
+        frag8(a, y);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          Frag16<E> b;
+          frag16_from_acc(b, select(a, hh));
+          *reinterpret_cast<decltype(b.v)*>(sR + ((size_t)((8 + 2 * st + hh) * NT + w) * 64 + lane) * 4 * ES) = b.v;
+        }
+        // Q_rel (hi + lo) and Qt = Q_rel e^{rho_w}, already in the carry's order
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = q8[e] * ep[e];
+        {
+          float xs[8][4];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xs[2 * st + (e >> 2)][e & 3] = x[e];
+          frag_step_split(qh[st], ql[st], xs, st);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = x[e] * fac[e];
+        frag8(a, y);
+        st_frag_g(fb, F::Q + (uint32_t)(w * 4 + st) * F::FR + lane_fr, a);
+        // K_inv (hi + lo): B operand of the diagonal pair
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = k8[e] * en[e];
+        {
+          float xs[8][4];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xs[2 * st + (e >> 2)][e & 3] = x[e];
+          frag_step_split(kih[st], kil[st], xs, st);
+        }
+        // K_end = K e^{rho_{w+1} - g} <= 1; Kb = K_end e^{g_n - rho_{w+1}} as
+        // channel-per-lane halves of the Kb^T fragments (rt8, kt = w / 2, half w % 2)
+        fac8(fac, sFE + w * 128, st);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= fac[e];
+        fac8(fac, sFB + w * 128, st);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = x[e] * fac[e];
+        frag8(a, y);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          st_half_g(fb, F::K + (uint32_t)((2 * st + hh) * F::KT + (w >> 1)) * F::FR + lane_fr + (uint32_t)(w & 1) * 4 * ES,
+                    select(a, hh), (E*)nullptr);
+        // column-tile copies for the later row tiles a > w, scaled by
+        // e^{rho_a - rho_{w+1}} = prod_{w < c < a} e^{tot_c}
+        for (int at = w + 1; at < NT; ++at) {
+          if (at > w + 1) {
+            fac8(fac, sFE + (at - 1) * 128, st);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] *= fac[e];
+          }
+          frag8(a, x);
+          const int q = at * (at - 1) / 2 + w;
+          *reinterpret_cast<Frag<E>*>(sKE + ((size_t)(q * 4 + st) * 64 + lane) * 8 * ES) = a;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- Gram tiles of row tile a = w: (a, a) from registers, (a, b < a) with
+    //      the scaled column tile from LDS.  P uses the hi + lo parts of Q_rel
+    //      (and of K_inv on the diagonal) when the operands are bf16. ----
+    f32x4 ga[NT], gp[NT];
+#pragma unroll
+    for (int b = 0; b < NT; ++b) {
+      ga[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      gp[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      ga[NT - 1] = mma(ga[NT - 1], kr[st], kih[st]);  // diagonal kept in slot NT-1
+      gp[NT - 1] = mma(gp[NT - 1], qh[st], kih[st]);
+      if constexpr (SPLIT) {
+        gp[NT - 1] = mma(gp[NT - 1], ql[st], kih[st]);
+        gp[NT - 1] = mma(gp[NT - 1], qh[st], kil[st]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NT - 1; ++b) {
+      if (b < w) {
+        const int q = w * (w - 1) / 2 + b;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const Frag<E> kb = *reinterpret_cast<const Frag<E>*>(sKE + ((size_t)(q * 4 + st) * 64 + lane) * 8 * ES);
+          ga[b] = mma(ga[b], kr[st], kb);
+          gp[b] = mma(gp[b], qh[st], kb);
+          if constexpr (SPLIT) gp[b] = mma(gp[b], ql[st], kb);
+        }
+      }
+    }
+
+    // ---- (I + Diag(beta) A_ww)^{-1} in fp32: lane j < 16 solves column j by
+    //      forward substitution over this wave's own 16 x 16 block ----
+    {
+      float* ab = sAd + w * 256;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * g + i;
+        ab[rr * 16 + r] = (r < rr) ? ga[NT - 1][i] * sBeta[16 * w + rr] : 0.f;
+      }
+      float xinv[16];
+      if (lane < 16) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          float part[4] = {(rr == lane) ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int q4 = 0; q4 < (rr + 3) / 4; ++q4) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(ab + rr * 16 + 4 * q4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (4 * q4 + e < rr) part[e] -= av[e] * xinv[4 * q4 + e];
+          }
+          xinv[rr] = (part[0] + part[1]) + (part[2] + part[3]);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) sM[(16 * w + rr) * L::LDM + 16 * w + lane] = from_f32<E>(xinv[rr]);
+      }
+    }
+    // -(Diag(beta) A)_wb below the diagonal into the solve blocks
+#pragma unroll
+    for (int b = 0; b < NT - 1; ++b) {
+      if (b < w) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 16 * w + 4 * g + i;
+          sM[rr * L::LDM + 16 * b + r] = from_f32<E>(-ga[b][i] * sBeta[rr]);
+        }
+      }
+    }
+    // P tiles: transposed on the matrix cores into the carry's fragment order
+    // (lane = token of tile w, four tokens of tile b); the diagonal tile keeps
+    // its lower triangle; the tile right of an even diagonal is zero.
+    {
+      const Frag16<E> id = ident16<E>(lane);
+#pragma unroll
+      for (int b = 0; b < NT; ++b) {
+        if (b <= w) {
+          f32x4 pv = gp[b == w ? NT - 1 : b];
+          if (b == w)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (r > 4 * g + i) pv[i] = 0.f;  // column r above row 4g+i
+          Frag16<E> a;
+          frag16_from_acc(a, pv);
+          const f32x4 t = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, a, id);
+          st_half_g(fb, F::P + (uint32_t)F::p_frag(w, b >> 1) * F::FR + lane_fr + (uint32_t)(b & 1) * 4 * ES, t,
+                    (E*)nullptr);
+        }
+      }
+      if ((w & 1) == 0)
+        st_half_g(fb, F::P + (uint32_t)F::p_frag(w, w >> 1) * F::FR + lane_fr + 4 * ES, (f32x4){0.f, 0.f, 0.f, 0.f},
+                  (E*)nullptr);
+    }
+    __syncthreads();
+
+    // ---- blocked forward substitution on the matrix cores:
+    //      Y_a = (I + A_aa)^{-1} (beta R_a - sum_{b<a} A_ab Y_b), tile row by
+    //      tile row.  Wave w solves W column tiles CPW w .. and U' column tiles
+    //      CPW w .., every Y_b it needs already in its registers. ----
+    {
+      Frag16<E> mfr[NT][NT], rfr[NOWN][NT];
+#pragma unroll
+      for (int a = 0; a < NT; ++a)
+#pragma unroll
+        for (int b = 0; b <= a; ++b) ld_frag16(mfr[a][b], sM + (16 * a + r) * L::LDM + 16 * b + 4 * g);
+#pragma unroll
+      for (int o = 0; o < NOWN; ++o) {
+        const int ct = (o < CPW) ? CPW * w + o : 8 + CPW * w + (o - CPW);
+#pragma unroll
+        for (int a = 0; a < NT; ++a)
+          rfr[o][a].v = *reinterpret_cast<const decltype(rfr[o][a].v)*>(sR + ((size_t)(ct * NT + a) * 64 + lane) * 4 * ES);
+      }
+      f32x4 Y[NOWN][NT];
+      Frag16<E> Yb[NOWN][NT];
+#pragma unroll
+      for (int a = 0; a < NT; ++a) {
+        f32x4 z[NOWN];
+#pragma unroll
+        for (int o = 0; o < NOWN; ++o) z[o] = frag16_to_f32(rfr[o][a]);
+#pragma unroll
+        for (int b = 0; b < a; ++b)
+#pragma unroll
+          for (int o = 0; o < NOWN; ++o) z[o] = mma16(z[o], mfr[a][b], Yb[o][b]);
+#pragma unroll
+        for (int o = 0; o < NOWN; ++o) {
+          Frag16<E> zb;
+          frag16_from_acc(zb, z[o]);
+          Y[o][a] = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, mfr[a][a], zb);
+          frag16_from_acc(Yb[o][a], Y[o][a]);
+        }
+      }
+      // -W: each 16 x 16 tile transposed on the matrix cores to lane = token,
+      // four channels; column tile ct is half ct % 2 of key step ct / 2
+      const Frag16<E> id = ident16<E>(lane);
+#pragma unroll
+      for (int a = 0; a < NT; ++a)
+#pragma unroll
+        for (int o = 0; o < CPW; ++o) {
+          Frag16<E> yn;
+          frag16_from_acc(yn, -Y[o][a]);
+          const f32x4 t = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, yn, id);
+          const int ct = CPW * w + o;
+          st_half_g(fb, F::W + (uint32_t)(a * 4 + (ct >> 1)) * F::FR + lane_fr + (uint32_t)(ct & 1) * 4 * ES, t,
+                    (E*)nullptr);
+        }
+      // U' in accumulator order
+#pragma unroll
+      for (int a = 0; a < NT; ++a)
+#pragma unroll
+        for (int o = CPW; o < NOWN; ++o) {
+          const int ct = CPW * w + (o - CPW);
+          buf_st16(__builtin_bit_cast(u32x4, Y[o][a]), fb, F::U + (uint32_t)((a * 8 + ct) * 64 + lane) * 16, 0);
+        }
+    }
+    // the next chunk rewrites sTot, sBeta and the factor tables only after the
+    // next barrier; every LDS area written before that barrier is read-only here
+  }
+}
+
+namespace {
+
+template <typename E, int C, bool PRO>
+hipError_t launch_prep_t(const PrepArgs& a, hipStream_t stream) {
+  constexpr size_t lds = PrepLayout<E, C>::BYTES;
+  auto fn = prep_kernel<E, C, PRO>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t ranges = ((int64_t)a.cap + a.chunks_per_block - 1) / a.chunks_per_block;
+  const int64_t grid = ranges * a.num_heads;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(4 * C), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
+  const bool pro = a.conv_q_w != nullptr || a.conv_k_w != nullptr;
+  if (a.bf16) return pro ? launch_prep_t<__bf16, 64, true>(a, stream) : launch_prep_t<__bf16, 64, false>(a, stream);
+  return pro ? launch_prep_t<float, 32, true>(a, stream) : launch_prep_t<float, 32, false>(a, stream);
+}
+
+}  // namespace kda
