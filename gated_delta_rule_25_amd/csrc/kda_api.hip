@@ -62,7 +62,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int kMinAutoSegment = 512;
 #ifndef KDA_PREP_CHUNKS_PER_BLOCK
-#define KDA_PREP_CHUNKS_PER_BLOCK 4
+#define KDA_PREP_CHUNKS_PER_BLOCK 8
 #endif
 constexpr int kPrepChunksPerBlock = KDA_PREP_CHUNKS_PER_BLOCK;
 
@@ -257,9 +257,9 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   a.total_tokens = total_tokens;
   a.units = num_seqs * num_heads;
   a.bf16 = (dtype == KDA_DTYPE_BF16);
-  // Split the value columns in two when the (sequence, head) chains alone
-  // cannot occupy the GPU; the epilogue normalises whole heads, so it keeps one.
-  a.col_split = (!f.gate && a.units <= cu_count_for_current_device()) ? 2 : 1;
+  // Two value-column blocks per (sequence, head); the epilogue normalises
+  // whole heads, so it keeps one.
+  a.col_split = f.gate ? 1 : 2;
 
   if (pl.seg_len == 0) {
     // Two-kernel schedule: per window, the window table, the factor blocks of

@@ -87,41 +87,52 @@ hipError_t launch_window_table(const int32_t* cu, int num_seqs, int64_t total_to
 template <typename E, int C, int DV>
 struct CarryLayout {
   using F = FactorBlock<(int)sizeof(E), C>;
-  static constexpr int PAD = 16 / (int)sizeof(E);
-  static constexpr int LDO = DV + PAD;
-  // one buffer: the factor block's operand part [0, F::U) copied verbatim
-  // (fragment order), rounded up to whole 4 KiB copy rounds
-  static constexpr size_t BUF = ((size_t)F::U + 4095) & ~(size_t)4095;
-  // two output staging tiles [C][LDO] (chunk i in tile i % 2)
-  static constexpr size_t OST = al16((size_t)C * LDO * sizeof(E));
-  static constexpr size_t O = 2 * BUF;
-  static constexpr size_t SS = O + 2 * OST;              // f32 [4][C] row sums of squares
-  static constexpr size_t BYTES = SS + (size_t)4 * C * 4;
+  // One LDS slot holds the parts of a factor block every compute wave reads
+  // in full: -W, Qt, Kb^T and gamma (P and U' go to registers).  Slot
+  // offsets, with the block offset each 1 KiB piece is copied from:
+  static constexpr uint32_t W = 0;                        // <- F::W
+  static constexpr uint32_t Q = W + F::NT * 4 * F::FR;    // <- F::Q
+  static constexpr uint32_t K = Q + F::NT * 4 * F::FR;    // <- F::K
+  static constexpr uint32_t G = K + 8 * F::KT * F::FR;    // <- F::G (one piece)
+  static constexpr uint32_t SLOT = G + 1024;
+  static constexpr int PIECES = SLOT / 1024;
+  static_assert(F::K % 1024 == 0 && F::G % 1024 == 0 && Q % 1024 == 0 && K % 1024 == 0, "1 KiB pieces");
+  static constexpr int NBUF = 3;                          // chunks in flight
+  static constexpr size_t SS = (size_t)NBUF * SLOT;       // f32 [DV / 16][C] row sums of squares
+  static constexpr size_t BYTES = SS + (size_t)(DV / 16) * C * 4;
+  // block offset of slot piece j
+
 };
 
+// Number of vector-memory operations allowed to stay outstanding in s_waitcnt.
+__host__ __device__ constexpr int vmcnt_wait(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
+
+// Workgroup of DV / 16 compute waves plus one loader wave.  Compute wave w
+// owns value columns 16 w .. 16 w + 15 of the block and keeps that slice of
+// the fp32 state in MFMA accumulators.  The loader wave copies each chunk's
+// factor block (its -W, Qt, Kb^T and gamma part) straight from global memory
+// into LDS slot ci % 3, two chunks ahead, so the compute waves never wait
+// behind the vector memory unit; they fetch P and U' one chunk ahead into
+// registers and store their outputs directly.  One barrier per chunk hands
+// the slots over: after barrier ci, slot ci % 3 holds chunk ci, and every
+// wave is past chunk ci - 1, so the loader may refill slot (ci + 2) % 3.
 template <typename E, int C, int DV, bool EPI>
-__global__ __launch_bounds__(256) void carry_kernel(const CarryArgs p) {
+__global__ __launch_bounds__(64 * (DV / 16 + 1)) void carry_kernel(const CarryArgs p) {
   using L = CarryLayout<E, C, DV>;
   using F = FactorBlock<(int)sizeof(E), C>;
   constexpr int NT = C / 16;     // 16-token tiles per chunk
   constexpr int KT = C / 32;     // 32-deep token steps per chunk
-  constexpr int NCW = DV / 4;    // value columns per wave
-  constexpr int NCT = NCW / 16;  // 16-wide column tiles per wave
-  constexpr int LDO = L::LDO;
+  constexpr int NWC = DV / 16;   // compute waves; wave NWC is the loader
   constexpr int ES = (int)sizeof(E);
-  constexpr int PE = 16 / ES;                 // elements per 16-byte piece
-  constexpr int RO = DV / PE;                 // pieces per output row of this block
-  constexpr int NBP = (int)(L::BUF / 4096);   // 16-byte pieces per thread in one copy
-  constexpr int NOP = C * RO / 256;
   static_assert(!EPI || DV == D, "the epilogue normalises whole heads");
-  static_assert(NCT >= 1 && KT >= 1 && NT <= 4, "unsupported tile shape");
-  static_assert((C * RO) % 256 == 0, "piece counts");
+  static_assert(KT >= 1 && NT <= 4, "unsupported tile shape");
   static_assert(L::BYTES <= 160 * 1024, "LDS budget exceeded");
+  static_assert(L::PIECES <= 63, "copy exceeds the outstanding-load counter");
 
   extern __shared__ __align__(16) unsigned char smem[];
   float* sSS = reinterpret_cast<float*>(smem + L::SS);
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   // XCD-aware decode of the work item: blocks b and b + 8 run on the same XCD,
   // so the column blocks of one (sequence, head) share that XCD's L2.
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -136,195 +147,228 @@ __global__ __launch_bounds__(256) void carry_kernel(const CarryArgs p) {
   const int c0 = p.seq_c0[n], nch = p.seq_c1[n] - c0, slot0 = p.seq_first[n];
   const int64_t rs = (int64_t)H * D;
   const int64_t hoff = (int64_t)h * D;
-  const int col0 = cb * DV + wv * NCW;  // first value column owned by this wave
-  E* go = static_cast<E*>(p.o);
   const char* fbase = static_cast<const char*>(p.factors);
-  const uint32_t lane_fr = (uint32_t)lane * 8 * ES;
+  auto block_of = [&](int ci) { return fbase + ((size_t)(slot0 + ci) * H + h) * F::BYTES; };
 
-  // State slice: tile (rt8, ct) holds rows 16 rt8 + 4g + i, column col0 + 16 ct + l16.
-  f32x4 accS[8][NCT];
+  if (wv == NWC) {
+    // ---- loader wave ----
+    auto copy_block = [&](int ci) {
+      const char* blk = block_of(ci);
+      unsigned char* dst = smem + (ci % L::NBUF) * L::SLOT;
+      constexpr uint32_t kSlotK = L::K, kBlockK = F::K;
+#pragma unroll
+      for (int j = 0; j < L::PIECES; ++j)
+        __builtin_amdgcn_global_load_lds(blk + (j * 1024u < kSlotK ? j * 1024u : kBlockK + (j * 1024u - kSlotK)) + lane * 16,
+                                         (__attribute__((address_space(3))) void*)(dst + j * 1024), 16, 0, 0);
+    };
+    if (nch > 0) copy_block(0);
+    if (nch > 1) copy_block(1);
+    for (int ci = 0; ci < nch; ++ci) {
+      // chunk ci's copy has landed; the one of chunk ci + 1 may be in flight
+      if (ci + 1 < nch) __builtin_amdgcn_s_waitcnt(vmcnt_wait(L::PIECES));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+      __syncthreads();
+      if (ci + 2 < nch) copy_block(ci + 2);
+      if (EPI) __syncthreads();  // the compute waves' row-sum exchange
+    }
+    return;
+  }
+
+  // ---- compute waves ----
+  const int col0 = cb * DV + 16 * wv;  // first value column owned by this wave
+  E* go = static_cast<E*>(p.o);
+  const float norm_w = (EPI && p.norm_w) ? p.norm_w[col0 + (lane & 15)] : 1.f;
+
+  // State slice: tile rt8 holds rows 16 rt8 + 4g + i, column col0 + l16.
+  f32x4 accS[8];
   const size_t sbase = ((size_t)n * H + h) * (size_t)(D * D);
+  {
+    const int l16 = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int rt8 = 0; rt8 < 8; ++rt8)
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    for (int rt8 = 0; rt8 < 8; ++rt8)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        accS[rt8][ct][i] =
-            p.state_in ? p.state_in[sbase + (size_t)(16 * rt8 + 4 * g + i) * D + col0 + 16 * ct + l16] : 0.f;
+        accS[rt8][i] = p.state_in ? p.state_in[sbase + (size_t)(16 * rt8 + 4 * g + i) * D + col0 + l16] : 0.f;
+  }
 
-  // One chunk's factor block in flight: the operand part as 16-byte pieces
-  // (piece tid + 256 j), and this wave's U' columns in accumulator order.
-  const uint32_t p_off = (uint32_t)tid * 16;
-  const uint32_t u_off = (uint32_t)(((col0 / 16) * 64 + lane) * 16);
-  u32x4 rB[NBP];
-  f32x4 rU[NT][NCT];
-  auto load_block = [&](int ci) {
-    const Rsrc rb = make_rsrc(fbase + ((size_t)(slot0 + ci) * H + h) * F::BYTES, F::BYTES);
+  // P fragments and this wave's U' columns (accumulator order) of the next
+  // chunk, fetched into registers one chunk ahead (U' right after the
+  // barrier, P once the current chunk's P has been used).
+  Frag<E> rP[F::NP];
+  f32x4 rU[NT];
+  auto load_u = [&](int ci) {
+    const Rsrc rb = make_rsrc(block_of(ci), F::BYTES);
+    const uint32_t u_off = (uint32_t)(((col0 / 16) * 64 + lane) * 16);
 #pragma unroll
-    for (int j = 0; j < NBP; ++j) rB[j] = buf_ld16(rb, p_off, (uint32_t)(4096 * j));
-#pragma unroll
-    for (int a = 0; a < NT; ++a)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        rU[a][ct] = __builtin_bit_cast(f32x4, buf_ld16(rb, u_off, F::U + (uint32_t)(a * 8 + ct) * 1024));
+    for (int a = 0; a < NT; ++a) rU[a] = __builtin_bit_cast(f32x4, buf_ld16(rb, u_off, F::U + (uint32_t)(a * 8) * 1024));
   };
-  // Output rows of chunk ci (staged in LDS tile ci % 2) to global memory.
-  auto flush_o = [&](int ci) {
-    const int64_t t0 = seq_bos + (int64_t)(c0 + ci) * C;
-    const int nv = (int)min((int64_t)C, seq_eos - t0);
-    const E* so = reinterpret_cast<const E*>(smem + L::O + (ci & 1) * L::OST);
+  auto load_p = [&](int ci) {
+    const Rsrc rb = make_rsrc(block_of(ci), F::BYTES);
+    const uint32_t lane_fr = (uint32_t)lane * 8 * ES;
 #pragma unroll
-    for (int j = 0; j < NOP; ++j) {
-      const int pc = tid + 256 * j, r = pc / RO, c = (pc % RO) * PE;
-      if (r < nv)
-        *reinterpret_cast<u32x4*>(go + (t0 + r) * rs + hoff + cb * DV + c) =
-            *reinterpret_cast<const u32x4*>(so + r * LDO + c);
+    for (int f = 0; f < F::NP; ++f) {
+      if constexpr (ES == 2) {
+        rP[f].v = __builtin_bit_cast(bf16x8, buf_ld16(rb, lane_fr, F::P + f * F::FR));
+      } else {
+        rP[f].lo = __builtin_bit_cast(f32x4, buf_ld16(rb, lane_fr, F::P + f * F::FR));
+        rP[f].hi = __builtin_bit_cast(f32x4, buf_ld16(rb, lane_fr + 16, F::P + f * F::FR));
+      }
     }
   };
-  if (nch > 0) load_block(0);
+  // Whole-head blocks with the epilogue run nine waves, whose register budget
+  // has no room for P in flight: they fetch P at the top of each chunk.
+  constexpr bool PF_P = !EPI;
+  if (nch > 0) {
+    load_u(0);
+    if (PF_P) load_p(0);
+  }
 
   for (int ci = 0; ci < nch; ++ci) {
+    // lane indices from an opaque copy of the thread id, so the per-lane
+    // address arithmetic stays inside the loop rather than in registers
+    int tidv = tid;
+    asm volatile("" : "+v"(tidv));
+    const int lane = tidv & 63, l16 = lane & 15, g = lane >> 4;
+    const uint32_t lane_fr = (uint32_t)lane * 8 * ES;
     const int64_t t0 = seq_bos + (int64_t)(c0 + ci) * C;
     const int nv = (int)min((int64_t)C, seq_eos - t0);
-    unsigned char* buf = smem + (ci & 1) * L::BUF;
-    const E* sW = reinterpret_cast<const E*>(buf + F::W + lane_fr);
-    const E* sQt = reinterpret_cast<const E*>(buf + F::Q + lane_fr);
-    const E* sP = reinterpret_cast<const E*>(buf + F::P + lane_fr);
-    const E* sKbt = reinterpret_cast<const E*>(buf + F::K + lane_fr);
-    const float* sGam = reinterpret_cast<const float*>(buf + F::G);
+    const unsigned char* buf = smem + (ci % L::NBUF) * L::SLOT;
+    const E* sW = reinterpret_cast<const E*>(buf + L::W + lane_fr);
+    const E* sQt = reinterpret_cast<const E*>(buf + L::Q + lane_fr);
+    const E* sKbt = reinterpret_cast<const E*>(buf + L::K + lane_fr);
+    const float* sGam = reinterpret_cast<const float*>(buf + L::G);
     constexpr int FRE = (int)F::FR / ES;  // elements per fragment
-    E* sO = reinterpret_cast<E*>(smem + L::O + (ci & 1) * L::OST);
 
-    // ---- factor block into this chunk's LDS half (the other half may still
-    //      be read by waves finishing the previous chunk) ----
+    f32x4 accU[NT];
 #pragma unroll
-    for (int j = 0; j < NBP; ++j) *reinterpret_cast<u32x4*>(buf + p_off + 4096 * j) = rB[j];
-    f32x4 accU[NT][NCT];
-#pragma unroll
-    for (int a = 0; a < NT; ++a)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) accU[a][ct] = rU[a][ct];
+    for (int a = 0; a < NT; ++a) accU[a] = rU[a];
     __syncthreads();
-    if (ci > 0) flush_o(ci - 1);
-    if (ci + 1 < nch) load_block(ci + 1);
+    if (!PF_P) load_p(ci);
+    if (ci + 1 < nch) load_u(ci + 1);
 
+    // Each stage first issues all of its LDS fragment reads (the scheduling
+    // barrier keeps them ahead of the matrix-core work, so they are in
+    // flight together instead of one at a time), then runs its products
+    // with the independent accumulators interleaved.  The nine-wave
+    // whole-head blocks lack the registers and read them one at a time.
     // ---- S1: U = U' - W S ----
-    Frag<E> sf[4][NCT];
+    Frag<E> sf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) frag_from_acc(sf[ks], accS[2 * ks], accS[2 * ks + 1]);
+    constexpr bool BATCH = NWC == 4;
+    Frag<E> fa[16];
+#pragma unroll
+    for (int i = 0; i < 4 * NT; ++i) ld_frag(fa[i], sW + i * FRE);   // W is stored negated
+    if (BATCH) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) frag_from_acc(sf[ks][ct], accS[2 * ks][ct], accS[2 * ks + 1][ct]);
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        Frag<E> fa;
-        ld_frag(fa, sW + (rt * 4 + ks) * FRE);   // W is stored negated
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) accU[rt][ct] = mma(accU[rt][ct], fa, sf[ks][ct]);
-      }
+      for (int rt = 0; rt < NT; ++rt) accU[rt] = mma(accU[rt], fa[rt * 4 + ks], sf[ks]);
 
     // ---- S2: O = Qt S + P U ----
-    f32x4 accO[NT][NCT];
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt)
+    for (int i = 0; i < 4 * NT; ++i) ld_frag(fa[i], sQt + i * FRE);
+    if (BATCH) __builtin_amdgcn_sched_barrier(0);
+    f32x4 accO[NT];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) accO[rt][ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < NT; ++rt) accO[rt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt)
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        Frag<E> fa;
-        ld_frag(fa, sQt + (rt * 4 + ks) * FRE);
+      for (int rt = 0; rt < NT; ++rt) accO[rt] = mma(accO[rt], fa[rt * 4 + ks], sf[ks]);
+    Frag<E> uf[KT];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) accO[rt][ct] = mma(accO[rt][ct], fa, sf[ks][ct]);
-      }
-    Frag<E> uf[KT][NCT];
+    for (int kt = 0; kt < KT; ++kt) frag_from_acc(uf[kt], accU[2 * kt], accU[2 * kt + 1]);
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) frag_from_acc(uf[kt][ct], accU[2 * kt][ct], accU[2 * kt + 1][ct]);
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        if (kt <= (16 * rt + 15) / 32) {
-          Frag<E> fa;
-          ld_frag(fa, sP + F::p_frag(rt, kt) * FRE);
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) accO[rt][ct] = mma(accO[rt][ct], fa, uf[kt][ct]);
-        }
-      }
+      for (int rt = 0; rt < NT; ++rt)
+        if (kt <= rt / 2) accO[rt] = mma(accO[rt], rP[F::p_frag(rt, kt)], uf[kt]);
+    if (PF_P && ci + 1 < nch) load_p(ci + 1);
 
     if (EPI) {
-      // head-wise RMSNorm over the 128 value channels, then the sigmoid gate
+      // head-wise RMSNorm over the 128 value channels, then the sigmoid gate;
+      // the gate logits of this chunk are read through a buffer view with
+      // 32-bit offsets (rows past the sequence end read its last row)
+      const Rsrc gr = make_rsrc(static_cast<const E*>(p.gate) + t0 * rs, (uint32_t)(C * rs * ES));
+      float gl[NT][4];
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float ss = 0.f;
+          const int tok = min(16 * rt + 4 * g + i, nv - 1);
+          gl[rt][i] = buf_ld_elem(gr, (uint32_t)((tok * rs + hoff + col0 + l16) * ES), (E*)nullptr);
+        }
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) ss += accO[rt][ct][i] * accO[rt][ct][i];
+      for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float ss = accO[rt][i] * accO[rt][i];
 #pragma unroll
           for (int m = 1; m < 16; m <<= 1) ss += __shfl_xor(ss, m);
           if (l16 == 0) sSS[wv * C + 16 * rt + 4 * g + i] = ss;
         }
       __syncthreads();
-      const E* gg = static_cast<const E*>(p.gate);
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tok = 16 * rt + 4 * g + i;
-          const float ms = (sSS[tok] + sSS[C + tok] + sSS[2 * C + tok] + sSS[3 * C + tok]) * (1.f / D);
-          const float inv = rsqrtf(ms + p.rms_eps);
-          const int64_t row = (t0 + min(tok, nv - 1)) * rs + hoff;
+          float ms = 0.f;
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) {
-            const int col = col0 + 16 * ct + l16;
-            const float w = p.norm_w ? p.norm_w[col] : 1.f;
-            accO[rt][ct][i] *= inv * w * sigmoidf_fast(to_f32(gg[row + col]));
-          }
+          for (int q = 0; q < NWC; ++q) ms += sSS[q * C + tok];
+          const float inv = rsqrtf(ms * (1.f / D) + p.rms_eps);
+          accO[rt][i] *= inv * norm_w * sigmoidf_fast(gl[rt][i]);
         }
     }
-    // outputs to this chunk's staging tile; written out after the next barrier
+    // outputs: each 16 x 16 tile transposed on the matrix cores to lane =
+    // token, four consecutive columns, and stored straight to global memory
+    {
+      Frag16<E> id;
+      {
+        f32x4 x;
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt)
+        for (int e = 0; e < 4; ++e) x[e] = (4 * g + e == l16) ? 1.f : 0.f;
+        frag16_from_acc(id, x);
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          sO[(16 * rt + 4 * g + i) * LDO + wv * NCW + 16 * ct + l16] = from_f32<E>(accO[rt][ct][i]);
+      for (int rt = 0; rt < NT; ++rt) {
+        Frag16<E> a;
+        frag16_from_acc(a, accO[rt]);
+        const f32x4 t = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, a, id);
+        const int tok = 16 * rt + l16;
+        if (tok < nv) {
+          E* dst = go + (t0 + tok) * rs + hoff + col0 + 4 * g;
+          if constexpr (ES == 2)
+            *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
+          else
+            *reinterpret_cast<f32x4*>(dst) = t;
+        }
+      }
+    }
 
     // ---- S3: S <- Diag(e^{g_n}) S + Kb^T U ----
 #pragma unroll
-    for (int rt8 = 0; rt8 < 8; ++rt8) {
-      const f32x4 gam = *reinterpret_cast<const f32x4*>(sGam + 16 * rt8 + 4 * g);
+    for (int i = 0; i < 8 * KT; ++i) ld_frag(fa[i], sKbt + i * FRE);
+    f32x4 gam[8];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) accS[rt8][ct] *= gam;
+    for (int rt8 = 0; rt8 < 8; ++rt8) gam[rt8] = *reinterpret_cast<const f32x4*>(sGam + 16 * rt8 + 4 * g);
+    if (BATCH) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        Frag<E> fa;
-        ld_frag(fa, sKbt + (rt8 * KT + kt) * FRE);
+    for (int rt8 = 0; rt8 < 8; ++rt8) accS[rt8] *= gam[rt8];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) accS[rt8][ct] = mma(accS[rt8][ct], fa, uf[kt][ct]);
-      }
-    }
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int rt8 = 0; rt8 < 8; ++rt8) accS[rt8] = mma(accS[rt8], fa[rt8 * KT + kt], uf[kt]);
   }
 
-  if (nch > 0) {
-    __syncthreads();
-    flush_o(nch - 1);
-  }
   if (p.state_out) {
+    const int l16 = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int rt8 = 0; rt8 < 8; ++rt8)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          p.state_out[sbase + (size_t)(16 * rt8 + 4 * g + i) * D + col0 + 16 * ct + l16] = accS[rt8][ct][i];
+      for (int i = 0; i < 4; ++i)
+        p.state_out[sbase + (size_t)(16 * rt8 + 4 * g + i) * D + col0 + l16] = accS[rt8][i];
   }
 }
 
@@ -339,19 +383,16 @@ static hipError_t launch_carry_t(const CarryArgs& a, hipStream_t stream) {
   const int groups = (a.units + 7) / 8;
   const unsigned grid = (unsigned)(8 * a.col_split * groups);
   if (a.units <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(256), lds, stream, a);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * (DV / 16 + 1)), lds, stream, a);
   return hipGetLastError();
 }
 
 template <typename E, int C>
 static hipError_t launch_carry_dtype(const CarryArgs& a, hipStream_t stream) {
-  if (a.gate) {
-    if (a.col_split != 1) return hipErrorInvalidValue;
-    return launch_carry_t<E, C, 128, true>(a, stream);
-  }
-  if (a.col_split == 2) return launch_carry_t<E, C, 64, false>(a, stream);
-  if (a.col_split == 1) return launch_carry_t<E, C, 128, false>(a, stream);
-  return hipErrorInvalidValue;
+  // whole heads (the epilogue normalises over all 128 value columns), else
+  // two 64-column blocks per head that share the factor reads through L2
+  if (a.gate) return a.col_split == 1 ? launch_carry_t<E, C, 128, true>(a, stream) : hipErrorInvalidValue;
+  return a.col_split == 2 ? launch_carry_t<E, C, 64, false>(a, stream) : hipErrorInvalidValue;
 }
 
 hipError_t launch_carry(const CarryArgs& a, hipStream_t stream) {

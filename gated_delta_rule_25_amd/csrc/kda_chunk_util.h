@@ -27,6 +27,15 @@ __device__ __forceinline__ void buf_st4(float v, Rsrc r, uint32_t voff, uint32_t
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)voff, (int)soff, 0);
 }
 
+// One element of the I/O dtype at byte offset off, as fp32.
+__device__ __forceinline__ float buf_ld_elem(Rsrc r, uint32_t off, __bf16*) {
+  const unsigned short v = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+  return (float)__builtin_bit_cast(__bf16, v);
+}
+__device__ __forceinline__ float buf_ld_elem(Rsrc r, uint32_t off, float*) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
 __host__ __device__ constexpr size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
 __host__ __device__ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 

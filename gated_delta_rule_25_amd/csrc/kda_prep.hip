@@ -218,30 +218,58 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
     }
   }
 
-  for (int s = s_begin; s < s_end; ++s) {
+  // Inputs of one chunk for this lane's token: q and k (after the prologue
+  // when it runs; in the input dtype otherwise), v, log_alpha, beta.  For
+  // plain bf16 inputs the next chunk's loads are issued as soon as the
+  // current chunk's operands are formed, so they overlap its Gram products
+  // and solve (the fp32 and prologue forms lack the registers for it).
+  constexpr bool PREFETCH = !PRO && sizeof(E) == 2;
+  using QK = std::conditional_t<PRO, Raw4<float>, Raw4<E>>;
+  QK rq[8], rk[8];
+  Raw4<E> rv[8];
+  Raw4<float> rla[8];
+  float rbt = 0.f;
+  auto slot_range = [&](int s, int64_t& t0, int64_t& bos, int& nv) {
     while (p.seq_first[n + 1] <= s) ++n;
-    const int64_t seq_bos = p.cu ? (int64_t)p.cu[n] : 0;
-    const int64_t seq_eos = p.cu ? (int64_t)p.cu[n + 1] : p.total_tokens;
-    const int64_t t0 = seq_bos + (int64_t)(p.seq_c0[n] + (s - p.seq_first[n])) * C;
-    const int nv = (int)min((int64_t)C, seq_eos - t0);
-    const bool valid = tok < nv;
+    bos = p.cu ? (int64_t)p.cu[n] : 0;
+    const int64_t eos = p.cu ? (int64_t)p.cu[n + 1] : p.total_tokens;
+    t0 = bos + (int64_t)(p.seq_c0[n] + (s - p.seq_first[n])) * C;
+    nv = (int)min((int64_t)C, eos - t0);
+  };
+  auto issue_loads = [&](int64_t t0, int nv) {
     const int64_t row = t0 + min(tok, nv - 1);
     const int64_t base = row * rs + hoff;
+#pragma unroll
+    for (int pc = 0; pc < 8; ++pc) {
+      ld_raw4(rla[pc], p.log_alpha + base + piece_ch(pc, g));
+      ld_raw4(rv[pc], gv + base + piece_ch(pc, g));
+      if constexpr (!PRO) {
+        ld_raw4(rq[pc], gq + base + piece_ch(pc, g));
+        ld_raw4(rk[pc], gk + base + piece_ch(pc, g));
+      }
+    }
+    rbt = p.beta[row * H + h];
+  };
+  int64_t t0 = 0, seq_bos = 0;
+  int nv = 0;
+  slot_range(s_begin, t0, seq_bos, nv);
+  if (PREFETCH) issue_loads(t0, nv);
+
+  for (int s = s_begin; s < s_end; ++s) {
+    // Lane indices re-derived from an opaque copy of the thread id in every
+    // chunk: the address arithmetic of the unrolled stages then stays inside
+    // the loop instead of occupying registers for the whole run.
+    int tidv = tid;
+    asm volatile("" : "+v"(tidv));
+    const int lane = tidv & 63, w = tidv >> 6, r = lane & 15, g = lane >> 4;
+    const int tok = 16 * w + r;
+    const uint32_t lane_fr = (uint32_t)lane * 8 * ES;  // lane's entry in a fragment
+    const bool valid = tok < nv;
+    if (!PREFETCH) issue_loads(t0, nv);
     const Rsrc fb = make_rsrc(static_cast<char*>(p.factors) + ((size_t)s * H + h) * F::BYTES, F::BYTES);
 
-    // ---- inputs of this lane's token (q and k after the prologue when it
-    //      runs; kept in the input dtype otherwise) ----
-    using QK = std::conditional_t<PRO, Raw4<float>, Raw4<E>>;
-    QK rq[8], rk[8];
-    Raw4<E> rv[8];
     float dl[8][4];
     {
-      Raw4<float> rla[8];
-#pragma unroll
-      for (int pc = 0; pc < 8; ++pc) {
-        ld_raw4(rla[pc], p.log_alpha + base + piece_ch(pc, g));
-        ld_raw4(rv[pc], gv + base + piece_ch(pc, g));
-      }
       if constexpr (PRO) {
         // causal depthwise conv over rows tok-3 .. tok (zero before the
         // sequence start), SiLU, then L2 over the head's 128 channels
@@ -286,17 +314,11 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
         };
         prologue(rq, gq, p.conv_q_w);
         prologue(rk, gk, p.conv_k_w);
-      } else {
-#pragma unroll
-        for (int pc = 0; pc < 8; ++pc) {
-          ld_raw4(rq[pc], gq + base + piece_ch(pc, g));
-          ld_raw4(rk[pc], gk + base + piece_ch(pc, g));
-        }
       }
 #pragma unroll
       for (int pc = 0; pc < 8; ++pc) cvt_raw4(dl[pc], rla[pc]);
     }
-    const float bt = valid ? p.beta[row * H + h] : 0.f;
+    const float bt = valid ? rbt : 0.f;
     if (!valid) {
 #pragma unroll
       for (int pc = 0; pc < 8; ++pc) {
@@ -452,6 +474,13 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
         }
       }
     }
+    // the next chunk's inputs (they land while this chunk is finished)
+    int64_t t0n = 0, bosn = 0;
+    int nvn = 0;
+    if (s + 1 < s_end) {
+      slot_range(s + 1, t0n, bosn, nvn);
+      if (PREFETCH) issue_loads(t0n, nvn);
+    }
     __syncthreads();
 
     // ---- Gram tiles of row tile a = w: (a, a) from registers, (a, b < a) with
@@ -555,62 +584,55 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
     //      tile row.  Wave w solves W column tiles CPW w .. and U' column tiles
     //      CPW w .., every Y_b it needs already in its registers. ----
     {
-      Frag16<E> mfr[NT][NT], rfr[NOWN][NT];
-#pragma unroll
-      for (int a = 0; a < NT; ++a)
-#pragma unroll
-        for (int b = 0; b <= a; ++b) ld_frag16(mfr[a][b], sM + (16 * a + r) * L::LDM + 16 * b + 4 * g);
-#pragma unroll
-      for (int o = 0; o < NOWN; ++o) {
-        const int ct = (o < CPW) ? CPW * w + o : 8 + CPW * w + (o - CPW);
-#pragma unroll
-        for (int a = 0; a < NT; ++a)
-          rfr[o][a].v = *reinterpret_cast<const decltype(rfr[o][a].v)*>(sR + ((size_t)(ct * NT + a) * 64 + lane) * 4 * ES);
-      }
-      f32x4 Y[NOWN][NT];
+      const Frag16<E> id = ident16<E>(lane);
       Frag16<E> Yb[NOWN][NT];
 #pragma unroll
       for (int a = 0; a < NT; ++a) {
         f32x4 z[NOWN];
 #pragma unroll
-        for (int o = 0; o < NOWN; ++o) z[o] = frag16_to_f32(rfr[o][a]);
+        for (int o = 0; o < NOWN; ++o) {
+          const int ct = (o < CPW) ? CPW * w + o : 8 + CPW * w + (o - CPW);
+          Frag16<E> rf;
+          rf.v = *reinterpret_cast<const decltype(rf.v)*>(sR + ((size_t)(ct * NT + a) * 64 + lane) * 4 * ES);
+          z[o] = frag16_to_f32(rf);
+        }
 #pragma unroll
-        for (int b = 0; b < a; ++b)
+        for (int b = 0; b < a; ++b) {
+          Frag16<E> mf;
+          ld_frag16(mf, sM + (16 * a + r) * L::LDM + 16 * b + 4 * g);
 #pragma unroll
-          for (int o = 0; o < NOWN; ++o) z[o] = mma16(z[o], mfr[a][b], Yb[o][b]);
+          for (int o = 0; o < NOWN; ++o) z[o] = mma16(z[o], mf, Yb[o][b]);
+        }
+        Frag16<E> md;
+        ld_frag16(md, sM + (16 * a + r) * L::LDM + 16 * a + 4 * g);
 #pragma unroll
         for (int o = 0; o < NOWN; ++o) {
           Frag16<E> zb;
           frag16_from_acc(zb, z[o]);
-          Y[o][a] = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, mfr[a][a], zb);
-          frag16_from_acc(Yb[o][a], Y[o][a]);
+          const f32x4 y = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, md, zb);
+          frag16_from_acc(Yb[o][a], y);
+          if (o < CPW) {
+            // -W: the 16 x 16 tile transposed on the matrix cores to lane =
+            // token, four channels; channel tile ct is half ct % 2 of key step ct / 2
+            Frag16<E> yn;
+            frag16_from_acc(yn, -y);
+            const f32x4 t = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, yn, id);
+            const int ct = CPW * w + o;
+            st_half_g(fb, F::W + (uint32_t)(a * 4 + (ct >> 1)) * F::FR + lane_fr + (uint32_t)(ct & 1) * 4 * ES, t,
+                      (E*)nullptr);
+          } else {
+            // U' in accumulator order
+            const int ct = CPW * w + (o - CPW);
+            buf_st16(__builtin_bit_cast(u32x4, y), fb, F::U + (uint32_t)((a * 8 + ct) * 64 + lane) * 16, 0);
+          }
         }
       }
-      // -W: each 16 x 16 tile transposed on the matrix cores to lane = token,
-      // four channels; column tile ct is half ct % 2 of key step ct / 2
-      const Frag16<E> id = ident16<E>(lane);
-#pragma unroll
-      for (int a = 0; a < NT; ++a)
-#pragma unroll
-        for (int o = 0; o < CPW; ++o) {
-          Frag16<E> yn;
-          frag16_from_acc(yn, -Y[o][a]);
-          const f32x4 t = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, yn, id);
-          const int ct = CPW * w + o;
-          st_half_g(fb, F::W + (uint32_t)(a * 4 + (ct >> 1)) * F::FR + lane_fr + (uint32_t)(ct & 1) * 4 * ES, t,
-                    (E*)nullptr);
-        }
-      // U' in accumulator order
-#pragma unroll
-      for (int a = 0; a < NT; ++a)
-#pragma unroll
-        for (int o = CPW; o < NOWN; ++o) {
-          const int ct = CPW * w + (o - CPW);
-          buf_st16(__builtin_bit_cast(u32x4, Y[o][a]), fb, F::U + (uint32_t)((a * 8 + ct) * 64 + lane) * 16, 0);
-        }
     }
     // the next chunk rewrites sTot, sBeta and the factor tables only after the
     // next barrier; every LDS area written before that barrier is read-only here
+    t0 = t0n;
+    seq_bos = bosn;
+    nv = nvn;
   }
 }
 
