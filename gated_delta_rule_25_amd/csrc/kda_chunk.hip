@@ -198,9 +198,17 @@ __global__ __launch_bounds__(64 * (DV / 16 + 1)) void carry_kernel(const CarryAr
   f32x4 rU[NT];
   auto load_u = [&](int ci) {
     const Rsrc rb = make_rsrc(block_of(ci), F::BYTES);
-    const uint32_t u_off = (uint32_t)(((col0 / 16) * 64 + lane) * 16);
+    const uint32_t u_off = (uint32_t)((col0 / 16) * F::UT + lane * 4 * ES);
 #pragma unroll
-    for (int a = 0; a < NT; ++a) rU[a] = __builtin_bit_cast(f32x4, buf_ld16(rb, u_off, F::U + (uint32_t)(a * 8) * 1024));
+    for (int a = 0; a < NT; ++a) {
+      if constexpr (ES == 2) {
+        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)u_off, (int)(F::U + a * 8 * F::UT), 0);
+        const bf16x4 b = __builtin_bit_cast(bf16x4, x);
+        rU[a] = (f32x4){(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+      } else {
+        rU[a] = __builtin_bit_cast(f32x4, buf_ld16(rb, u_off, F::U + a * 8 * F::UT));
+      }
+    }
   };
   auto load_p = [&](int ci) {
     const Rsrc rb = make_rsrc(block_of(ci), F::BYTES);

@@ -88,7 +88,8 @@ struct ScanArgs {
 //   G  [128]      e^{g_n} per key channel (fp32)
 //   U  [NT][8][64][4]  U' = T V in accumulator order: token tile a, column
 //                 tile ct, lane, element i = (token 16 a + 4 (lane / 16) + i,
-//                 column 16 ct + lane % 16)  (fp32)
+//                 column 16 ct + lane % 16), in the I/O dtype (the carry
+//                 rounds U = U' - W S to it for its products anyway)
 template <int ES, int C>
 struct FactorBlock {
   static constexpr int NT = C / 16;
@@ -108,7 +109,8 @@ struct FactorBlock {
   static constexpr uint32_t K = P + NP * FR;
   static constexpr uint32_t G = K + 8 * KT * FR;
   static constexpr uint32_t U = G + 128 * 4;
-  static constexpr uint32_t BYTES = (U + NT * 8 * 1024 + 255) & ~255u;
+  static constexpr uint32_t UT = 256u * ES;  // one U' tile: 64 lanes x 4 elements
+  static constexpr uint32_t BYTES = (U + NT * 8 * UT + 255) & ~255u;
 };
 constexpr int chunk_len(bool bf16) { return bf16 ? 64 : 32; }
 constexpr size_t factor_block_bytes(bool bf16) {

@@ -621,9 +621,9 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
             st_half_g(fb, F::W + (uint32_t)(a * 4 + (ct >> 1)) * F::FR + lane_fr + (uint32_t)(ct & 1) * 4 * ES, t,
                       (E*)nullptr);
           } else {
-            // U' in accumulator order
+            // U' in accumulator order, in the I/O dtype
             const int ct = CPW * w + (o - CPW);
-            buf_st16(__builtin_bit_cast(u32x4, y), fb, F::U + (uint32_t)((a * 8 + ct) * 64 + lane) * 16, 0);
+            st_half_g(fb, F::U + (uint32_t)(a * 8 + ct) * F::UT + (uint32_t)lane * 4 * ES, y, (E*)nullptr);
           }
         }
       }
