@@ -58,7 +58,8 @@ def measured_traffic(kernel: str):
     rec = json.load(open(path)).get(kernel)
     if rec is None:
         return None
-    src = {"kda_chunk_fwd": ["kda_chunk.hip", "kda_chunk_util.h", "kda_device.h", "kda_internal.h", "kda_api.hip"],
+    src = {"kda_chunk_fwd": ["kda_chunk.hip", "kda_prep.hip", "kda_chunk_util.h", "kda_device.h", "kda_internal.h",
+                             "kda_api.hip"],
            "decode_kernel": ["kda_decode.hip", "kda_device.h", "kda_internal.h"]}[kernel]
     m = hashlib.sha256()
     for f in src:
@@ -111,7 +112,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 4])
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-decode", action="store_true")

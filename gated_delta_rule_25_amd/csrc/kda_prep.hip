@@ -196,7 +196,10 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
   const int H = p.num_heads, N = p.num_seqs;
   const int h = blockIdx.x % H;
   const int count = p.seq_first[N];
-  const int s_begin = (blockIdx.x / H) * p.chunks_per_block;
+  // Ranges are handed out last-chunk-first: the carry kernel starts with the
+  // first chunks, which the prep then has written most recently.
+  const int nranges = (p.cap + p.chunks_per_block - 1) / p.chunks_per_block;
+  const int s_begin = (nranges - 1 - (int)(blockIdx.x / H)) * p.chunks_per_block;
   if (s_begin >= count) return;
   const int s_end = min(count, s_begin + p.chunks_per_block);
   const int64_t rs = (int64_t)H * D;  // elements between consecutive tokens
