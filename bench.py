@@ -46,7 +46,7 @@ def decode_algorithmic_bytes(N: int, H: int, es: int) -> int:
     return N * H * (2 * d * d * 4 + 3 * d * es + d * 4 + 4 + d * es)
 
 
-def measured_traffic(kernel: str):
+def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch recorded in profiles/hbm_traffic.json (rocprofv3
     FETCH_SIZE / WRITE_SIZE, copy-calibrated; for kda_chunk_fwd the sum over
     its kernels), or None when the kernel's sources have changed since the
@@ -56,7 +56,7 @@ def measured_traffic(kernel: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(kernel)
-    if rec is None:
+    if rec is None or rec.get("workload") != workload:
         return None
     src = {"kda_chunk_fwd": ["kda_chunk.hip", "kda_prep.hip", "kda_chunk_util.h", "kda_device.h", "kda_internal.h",
                              "kda_api.hip"],
@@ -194,7 +194,7 @@ def main():
             "config": {"workload": w["name"], "N": N, "H": H, "T": T, "d": 128, "chunk": 64 if es == 2 else 32,
                        "fused_prologue_epilogue": bool(w["fused"])},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic("kda_chunk_fwd"),
+                         "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic("kda_chunk_fwd", w["name"]),
                          "kernel": "kda_chunk_fwd = window_table_kernel + prep_kernel + carry_kernel",
                          "kernel_ms_avg": ms_avg, "algorithmic_bytes": algo},
         })
@@ -229,7 +229,7 @@ def main():
                             "tokens_per_s": wd["N"] * 1e3 / ms_avg, "steps": args.decode_steps,
                             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                          "frac": ach / HBM_PEAK_GBPS, "algorithmic_bytes": dbytes,
-                                         "traffic": measured_traffic("decode_kernel"),
+                                         "traffic": measured_traffic("decode_kernel", wd["name"]),
                                          "kernel": "decode_kernel", "kernel_ms_min": min(per)}}
         if args.only_decode:
             result.update({"metric": "KDA decode steps/s", "value": 1e3 / ms_avg, "unit": "steps/s"})

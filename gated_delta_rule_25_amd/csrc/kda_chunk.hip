@@ -254,36 +254,54 @@ __global__ __launch_bounds__(64 * (DV / 16 + 1)) void carry_kernel(const CarryAr
     if (!PF_P) load_p(ci);
     if (ci + 1 < nch) load_u(ci + 1);
 
-    // Each stage first issues all of its LDS fragment reads (the scheduling
-    // barrier keeps them ahead of the matrix-core work, so they are in
-    // flight together instead of one at a time), then runs its products
-    // with the independent accumulators interleaved.  The nine-wave
-    // whole-head blocks lack the registers and read them one at a time.
-    // ---- S1: U = U' - W S ----
+    // Four-wave blocks: each stage first issues all of its LDS fragment
+    // reads (the scheduling barrier keeps them ahead of the matrix-core work,
+    // so they are in flight together instead of one at a time), then runs its
+    // products with the independent accumulators interleaved.  The nine-wave
+    // whole-head blocks lack the registers and stream one fragment at a time.
+    constexpr bool BATCH = NWC == 4;
     Frag<E> sf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) frag_from_acc(sf[ks], accS[2 * ks], accS[2 * ks + 1]);
-    constexpr bool BATCH = NWC == 4;
-    Frag<E> fa[16];
-#pragma unroll
-    for (int i = 0; i < 4 * NT; ++i) ld_frag(fa[i], sW + i * FRE);   // W is stored negated
-    if (BATCH) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int rt = 0; rt < NT; ++rt) accU[rt] = mma(accU[rt], fa[rt * 4 + ks], sf[ks]);
-
-    // ---- S2: O = Qt S + P U ----
-#pragma unroll
-    for (int i = 0; i < 4 * NT; ++i) ld_frag(fa[i], sQt + i * FRE);
-    if (BATCH) __builtin_amdgcn_sched_barrier(0);
     f32x4 accO[NT];
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) accO[rt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if constexpr (BATCH) {
+      // ---- S1: U = U' - W S ----
+      Frag<E> fa[4 * NT];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+      for (int i = 0; i < 4 * NT; ++i) ld_frag(fa[i], sW + i * FRE);   // W is stored negated
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int rt = 0; rt < NT; ++rt) accO[rt] = mma(accO[rt], fa[rt * 4 + ks], sf[ks]);
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) accU[rt] = mma(accU[rt], fa[rt * 4 + ks], sf[ks]);
+      // ---- S2: O = Qt S (+ P U below) ----
+#pragma unroll
+      for (int i = 0; i < 4 * NT; ++i) ld_frag(fa[i], sQt + i * FRE);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) accO[rt] = mma(accO[rt], fa[rt * 4 + ks], sf[ks]);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+          Frag<E> fa;
+          ld_frag(fa, sW + (rt * 4 + ks) * FRE);
+          accU[rt] = mma(accU[rt], fa, sf[ks]);
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+          Frag<E> fa;
+          ld_frag(fa, sQt + (rt * 4 + ks) * FRE);
+          accO[rt] = mma(accO[rt], fa, sf[ks]);
+        }
+    }
     Frag<E> uf[KT];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) frag_from_acc(uf[kt], accU[2 * kt], accU[2 * kt + 1]);
@@ -356,18 +374,32 @@ __global__ __launch_bounds__(64 * (DV / 16 + 1)) void carry_kernel(const CarryAr
     }
 
     // ---- S3: S <- Diag(e^{g_n}) S + Kb^T U ----
+    if constexpr (BATCH) {
+      Frag<E> fa[8 * KT];
 #pragma unroll
-    for (int i = 0; i < 8 * KT; ++i) ld_frag(fa[i], sKbt + i * FRE);
-    f32x4 gam[8];
+      for (int i = 0; i < 8 * KT; ++i) ld_frag(fa[i], sKbt + i * FRE);
+      f32x4 gam[8];
 #pragma unroll
-    for (int rt8 = 0; rt8 < 8; ++rt8) gam[rt8] = *reinterpret_cast<const f32x4*>(sGam + 16 * rt8 + 4 * g);
-    if (BATCH) __builtin_amdgcn_sched_barrier(0);
+      for (int rt8 = 0; rt8 < 8; ++rt8) gam[rt8] = *reinterpret_cast<const f32x4*>(sGam + 16 * rt8 + 4 * g);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int rt8 = 0; rt8 < 8; ++rt8) accS[rt8] *= gam[rt8];
+      for (int rt8 = 0; rt8 < 8; ++rt8) accS[rt8] *= gam[rt8];
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-      for (int rt8 = 0; rt8 < 8; ++rt8) accS[rt8] = mma(accS[rt8], fa[rt8 * KT + kt], uf[kt]);
+        for (int rt8 = 0; rt8 < 8; ++rt8) accS[rt8] = mma(accS[rt8], fa[rt8 * KT + kt], uf[kt]);
+    } else {
+#pragma unroll
+      for (int rt8 = 0; rt8 < 8; ++rt8) {
+        accS[rt8] *= *reinterpret_cast<const f32x4*>(sGam + 16 * rt8 + 4 * g);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          Frag<E> fa;
+          ld_frag(fa, sKbt + (rt8 * KT + kt) * FRE);
+          accS[rt8] = mma(accS[rt8], fa, uf[kt]);
+        }
+      }
+    }
   }
 
   if (p.state_out) {
