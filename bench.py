@@ -2,13 +2,16 @@
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 1]
                     [--no-decode] [--no-cpu-baseline] [--decode-steps 64]
+                    [--extra-workloads 2,4] [--extra-steps 3]
 
 A step is one kda_chunk_fwd over one layer of the workload (all heads, all
 tokens, inputs already resident in HBM): by default the one-layer K3 shape
 H=96, d=128, T=8192 with a carried fp32 state.  `value` is prefill tokens/s.
 The decode workload (256 sequences x 96 heads, 64 in-place kda_decode_step
-calls) is timed after it and reported under "decode".  Kernel durations come
-from HIP events on the stream the kernels run on.
+calls) is timed after it and reported under "decode"; the long-context (T=131072)
+and the varlen fused prologue/epilogue workloads are timed with fewer steps and
+reported under "workloads".  Kernel durations come from HIP events on the
+stream the kernels run on.
 
 Prints one JSON line.  Only the optional CPU-baseline leg touches the oracle.
 """
@@ -108,6 +111,56 @@ def cpu_baseline(inp, max_seconds_hint=20.0):
                       % (nh, H, T, dt, H)}
 
 
+def time_prefill(kda, kda_inputs, wid, steps, warmup, dev, stream):
+    """Time `steps` kda_chunk_fwd calls over prefill workload `wid` (inputs
+    generated on the device first): wall clock around the steps, HIP events
+    per call, and the algorithmic-byte roofline."""
+    import torch
+    w = kda_inputs.WORKLOADS[wid]
+    inp = kda_inputs.make_workload(wid, device=dev)
+    T, H, N = inp["T"], inp["H"], inp["N"]
+    es = 2 if w["dtype"] == "bf16" else 4
+    kw = dict(initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"])
+    for key in ("conv_q_w", "conv_k_w", "gate", "norm_w"):
+        if inp.get(key) is not None:
+            kw[key] = inp[key]
+    o = torch.empty_like(inp["v"])
+    fs = torch.empty((N, H, 128, 128), dtype=torch.float32, device=dev)
+    ws_bytes = kda.chunk_fwd_workspace_bytes(N, T, H, inp["q"].dtype)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], out=o, final_state=fs,
+                      workspace=ws, **kw)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    per = time_events(step, steps, stream)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_avg = sum(per) / len(per)
+    algo = prefill_algorithmic_bytes(T, H, N, es, w["fused"], inp["initial_state"] is not None, True)
+    achieved = algo / (ms_avg * 1e-3) / 1e9
+    del o, fs, ws
+    return inp, {
+        "tokens_per_s": T / (wall / steps),
+        "ms_per_step": wall / steps * 1e3,
+        "steps": steps,
+        "dtype": w["dtype"],
+        "config": {"workload": w["name"], "N": N, "H": H, "T": T, "d": 128, "chunk": 64 if es == 2 else 32,
+                   "fused_prologue_epilogue": bool(w["fused"])},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic("kda_chunk_fwd", w["name"]),
+                     "kernel": "kda_chunk_fwd = window_table_kernel + prep_kernel + carry_kernel",
+                     "kernel_ms_avg": ms_avg, "algorithmic_bytes": algo},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +168,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 4])
     ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--extra-workloads", default="2,4",
+                    help="other prefill workloads timed after the main one and reported under 'workloads' ('' = none)")
+    ap.add_argument("--extra-steps", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-decode", action="store_true", help="time only the decode workload (profiling)")
@@ -135,11 +191,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
-    w = kda_inputs.WORKLOADS[args.workload]
     result = {}
     if args.only_prefill:
         args.no_decode = True
         args.no_cpu_baseline = True
+    if args.only_prefill or args.only_decode:
+        args.extra_workloads = ""
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -149,59 +206,39 @@ def main():
         del src, dst
 
     if not args.only_decode:
-        inp = kda_inputs.make_workload(args.workload, device=dev)
-        T, H, N = inp["T"], inp["H"], inp["N"]
-        es = 2 if w["dtype"] == "bf16" else 4
-        kw = dict(initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"])
-        for key in ("conv_q_w", "conv_k_w", "gate", "norm_w"):
-            if inp.get(key) is not None:
-                kw[key] = inp[key]
-        o = torch.empty_like(inp["v"])
-        fs = torch.empty((N, H, 128, 128), dtype=torch.float32, device=dev)
-        ws_bytes = kda.chunk_fwd_workspace_bytes(N, T, H, inp["q"].dtype)
-        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-
-        def step():
-            kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], out=o, final_state=fs,
-                          workspace=ws, **kw)
-
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        per = time_events(step, args.steps, stream)
-        torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        for _ in range(args.steps):
-            step()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t_start
-        ms_avg = sum(per) / len(per)
-        algo = prefill_algorithmic_bytes(T, H, N, es, w["fused"], inp["initial_state"] is not None, True)
-        achieved = algo / (ms_avg * 1e-3) / 1e9
+        inp, tm = time_prefill(kda, kda_inputs, args.workload, args.steps, args.warmup, dev, stream)
         result.update({
             "metric": "KDA prefill tokens/s (H=96,d=128,T=8K) + decode steps/s; % of roofline",
-            "value": T / (wall / args.steps),
+            "value": tm["tokens_per_s"],
             "unit": "tokens/s",
             "n_gpus": 1,
             "steps": args.steps,
             "warmup": args.warmup,
-            "ms_per_step": wall / args.steps * 1e3,
+            "ms_per_step": tm["ms_per_step"],
             "higher_is_better": True,
             "scaling": "weak",
             "vs_baseline": None,
-            "dtype": w["dtype"],
+            "dtype": tm["dtype"],
             "data": "synthetic",
-            "config": {"workload": w["name"], "N": N, "H": H, "T": T, "d": 128, "chunk": 64 if es == 2 else 32,
-                       "fused_prologue_epilogue": bool(w["fused"])},
-            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic("kda_chunk_fwd", w["name"]),
-                         "kernel": "kda_chunk_fwd = window_table_kernel + prep_kernel + carry_kernel",
-                         "kernel_ms_avg": ms_avg, "algorithmic_bytes": algo},
+            "config": tm["config"],
+            "roofline": tm["roofline"],
         })
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(inp)
-        del inp, o, fs, ws
+        del inp
         torch.cuda.empty_cache()
+        # the other prefill workloads (long context; varlen with the fused
+        # prologue and epilogue), fewer steps each, reported beside the line
+        extra = [int(x) for x in args.extra_workloads.split(",") if x.strip()] if args.extra_workloads else []
+        if extra:
+            result["workloads"] = {}
+        for wid in extra:
+            if wid == args.workload:
+                continue
+            inp, tm = time_prefill(kda, kda_inputs, wid, args.extra_steps, 1, dev, stream)
+            result["workloads"][tm["config"]["workload"]] = tm
+            del inp
+            torch.cuda.empty_cache()
 
     if not args.no_decode or args.only_decode:
         wd = kda_inputs.WORKLOADS[3]

@@ -18,10 +18,9 @@
 //   carry_kernel  one workgroup per (sequence, head, value-column block)
 //                 walks the chunks in order with the fp32 state in MFMA
 //                 accumulators: U = U' - W S, O = Qt S + P U, the optional
-//                 RMSNorm x sigmoid-gate epilogue, and the state update.  The
-//                 next chunk's factor block is loaded into registers while
-//                 the current one is computed and lands in the other half of
-//                 a double-buffered LDS area.
+//                 RMSNorm x sigmoid-gate epilogue, and the state update.  A
+//                 loader wave copies the factor blocks into a three-slot LDS
+//                 ring two chunks ahead of the compute waves.
 // Long inputs are processed in windows (every sequence advances by the same
 // fraction of its chunks per window) so the factor store stays bounded; the
 // state crosses windows through the final-state buffer.
@@ -84,7 +83,7 @@ hipError_t launch_window_table(const int32_t* cu, int num_seqs, int64_t total_to
 // ---------------------------------------------------------------------------
 // Carry kernel.
 // ---------------------------------------------------------------------------
-template <typename E, int C, int DV>
+template <typename E, int C, int NWC>
 struct CarryLayout {
   using F = FactorBlock<(int)sizeof(E), C>;
   // One LDS slot holds the parts of a factor block every compute wave reads
@@ -98,32 +97,33 @@ struct CarryLayout {
   static constexpr int PIECES = SLOT / 1024;
   static_assert(F::K % 1024 == 0 && F::G % 1024 == 0 && Q % 1024 == 0 && K % 1024 == 0, "1 KiB pieces");
   static constexpr int NBUF = 3;                          // chunks in flight
-  static constexpr size_t SS = (size_t)NBUF * SLOT;       // f32 [DV / 16][C] row sums of squares
-  static constexpr size_t BYTES = SS + (size_t)(DV / 16) * C * 4;
-  // block offset of slot piece j
-
+  static constexpr size_t SS = (size_t)NBUF * SLOT;       // f32 [NWC][C] per-wave row sums of squares
+  static constexpr size_t BYTES = SS + (size_t)NWC * C * 4;
 };
 
 // Number of vector-memory operations allowed to stay outstanding in s_waitcnt.
 __host__ __device__ constexpr int vmcnt_wait(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
 
-// Workgroup of DV / 16 compute waves plus one loader wave.  Compute wave w
-// owns value columns 16 w .. 16 w + 15 of the block and keeps that slice of
-// the fp32 state in MFMA accumulators.  The loader wave copies each chunk's
-// factor block (its -W, Qt, Kb^T and gamma part) straight from global memory
-// into LDS slot ci % 3, two chunks ahead, so the compute waves never wait
-// behind the vector memory unit; they fetch P and U' one chunk ahead into
-// registers and store their outputs directly.  One barrier per chunk hands
-// the slots over: after barrier ci, slot ci % 3 holds chunk ci, and every
-// wave is past chunk ci - 1, so the loader may refill slot (ci + 2) % 3.
-template <typename E, int C, int DV, bool EPI>
-__global__ __launch_bounds__(64 * (DV / 16 + 1)) void carry_kernel(const CarryArgs p) {
-  using L = CarryLayout<E, C, DV>;
+// Workgroup of NWC = DV / (16 CT) compute waves plus one loader wave.
+// Compute wave w owns the CT 16-column tiles of value columns
+// 16 CT w .. 16 CT (w + 1) - 1 of the block and keeps that slice of the fp32
+// state in MFMA accumulators; every -W, Qt or Kb^T fragment it reads from LDS
+// feeds CT products.  The loader wave copies each chunk's factor block (its
+// -W, Qt, Kb^T and gamma part) straight from global memory into LDS slot
+// ci % 3, two chunks ahead, so the compute waves never wait behind the
+// vector memory unit; they fetch P and U' one chunk ahead into registers and
+// store their outputs directly.  One barrier per chunk hands the slots over:
+// after barrier ci, slot ci % 3 holds chunk ci, and every wave is past chunk
+// ci - 1, so the loader may refill slot (ci + 2) % 3.
+template <typename E, int C, int DV, bool EPI, int CT>
+__global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const CarryArgs p) {
+  constexpr int NWC = DV / (16 * CT);  // compute waves; wave NWC is the loader
+  using L = CarryLayout<E, C, NWC>;
   using F = FactorBlock<(int)sizeof(E), C>;
   constexpr int NT = C / 16;     // 16-token tiles per chunk
   constexpr int KT = C / 32;     // 32-deep token steps per chunk
-  constexpr int NWC = DV / 16;   // compute waves; wave NWC is the loader
   constexpr int ES = (int)sizeof(E);
+  static_assert(NWC * 16 * CT == DV, "column tiles must cover the block");
   static_assert(!EPI || DV == D, "the epilogue normalises whole heads");
   static_assert(KT >= 1 && NT <= 4, "unsupported tile shape");
   static_assert(L::BYTES <= 160 * 1024, "LDS budget exceeded");
@@ -175,39 +175,60 @@ __global__ __launch_bounds__(64 * (DV / 16 + 1)) void carry_kernel(const CarryAr
   }
 
   // ---- compute waves ----
-  const int col0 = cb * DV + 16 * wv;  // first value column owned by this wave
+  const int col0 = cb * DV + 16 * CT * wv;  // first value column owned by this wave
   E* go = static_cast<E*>(p.o);
-  const float norm_w = (EPI && p.norm_w) ? p.norm_w[col0 + (lane & 15)] : 1.f;
+  // RMSNorm weights of the columns this lane stores (col0 + 16 c + 4 g + e)
+  f32x4 nw[CT];
+  {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) nw[c][e] = (EPI && p.norm_w) ? p.norm_w[col0 + 16 * c + 4 * g + e] : 1.f;
+  }
 
-  // State slice: tile rt8 holds rows 16 rt8 + 4g + i, column col0 + l16.
-  f32x4 accS[8];
+  // State slice: tile (c, rt8) holds rows 16 rt8 + 4g + i, column col0 + 16 c + l16.
+  f32x4 accS[CT][8];
   const size_t sbase = ((size_t)n * H + h) * (size_t)(D * D);
   {
     const int l16 = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int rt8 = 0; rt8 < 8; ++rt8)
+    for (int c = 0; c < CT; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        accS[rt8][i] = p.state_in ? p.state_in[sbase + (size_t)(16 * rt8 + 4 * g + i) * D + col0 + l16] : 0.f;
+      for (int rt8 = 0; rt8 < 8; ++rt8)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          accS[c][rt8][i] =
+              p.state_in ? p.state_in[sbase + (size_t)(16 * rt8 + 4 * g + i) * D + col0 + 16 * c + l16] : 0.f;
   }
 
-  // P fragments and this wave's U' columns (accumulator order) of the next
-  // chunk, fetched into registers one chunk ahead (U' right after the
-  // barrier, P once the current chunk's P has been used).
+  // P fragments and this wave's U' tiles (accumulator order, I/O dtype) of
+  // the next chunk, fetched into registers one chunk ahead (U' right after
+  // the barrier, P once the current chunk's P has been used).
+  using Raw = std::conditional_t<ES == 2, u32x2, f32x4>;  // four I/O-dtype values
+  auto raw_f32 = [](Raw x) -> f32x4 {
+    if constexpr (ES == 2) {
+      const bf16x4 b = __builtin_bit_cast(bf16x4, x);
+      return (f32x4){(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+    } else {
+      return x;
+    }
+  };
+  auto buf_ld_raw = [](Rsrc rb, uint32_t voff, uint32_t soff) -> Raw {
+    if constexpr (ES == 2)
+      return __builtin_amdgcn_raw_buffer_load_b64(rb, (int)voff, (int)soff, 0);
+    else
+      return __builtin_bit_cast(f32x4, buf_ld16(rb, voff, soff));
+  };
   Frag<E> rP[F::NP];
-  f32x4 rU[NT];
+  Raw rU[CT][NT];
   auto load_u = [&](int ci) {
     const Rsrc rb = make_rsrc(block_of(ci), F::BYTES);
-    const uint32_t u_off = (uint32_t)((col0 / 16) * F::UT + lane * 4 * ES);
 #pragma unroll
-    for (int a = 0; a < NT; ++a) {
-      if constexpr (ES == 2) {
-        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)u_off, (int)(F::U + a * 8 * F::UT), 0);
-        const bf16x4 b = __builtin_bit_cast(bf16x4, x);
-        rU[a] = (f32x4){(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
-      } else {
-        rU[a] = __builtin_bit_cast(f32x4, buf_ld16(rb, u_off, F::U + a * 8 * F::UT));
-      }
+    for (int c = 0; c < CT; ++c) {
+      const uint32_t u_off = (uint32_t)((col0 / 16 + c) * F::UT + lane * 4 * ES);
+#pragma unroll
+      for (int a = 0; a < NT; ++a) rU[c][a] = buf_ld_raw(rb, u_off, F::U + a * 8 * F::UT);
     }
   };
   auto load_p = [&](int ci) {
@@ -223,8 +244,20 @@ __global__ __launch_bounds__(64 * (DV / 16 + 1)) void carry_kernel(const CarryAr
       }
     }
   };
-  // Whole-head blocks with the epilogue run nine waves, whose register budget
-  // has no room for P in flight: they fetch P at the top of each chunk.
+  // Epilogue gate logits of the current chunk in the output layout
+  // (lane = token, four consecutive columns), through a buffer view with
+  // 32-bit offsets whose rows past the sequence end read zero.
+  Raw rG[EPI ? CT : 1][EPI ? NT : 1];
+  auto load_gate = [&](int64_t t0, int nv) {
+    const Rsrc gr = make_rsrc(static_cast<const E*>(p.gate) + t0 * rs, (uint32_t)((int64_t)nv * rs * ES));
+    const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt)
+        rG[c][rt] = buf_ld_raw(gr, (uint32_t)(((16 * rt + l16) * rs + hoff + col0 + 16 * c + 4 * g) * ES), 0);
+  };
+  // Whole-head epilogue blocks keep P out of flight (register budget).
   constexpr bool PF_P = !EPI;
   if (nch > 0) {
     load_u(0);
@@ -247,25 +280,33 @@ __global__ __launch_bounds__(64 * (DV / 16 + 1)) void carry_kernel(const CarryAr
     const float* sGam = reinterpret_cast<const float*>(buf + L::G);
     constexpr int FRE = (int)F::FR / ES;  // elements per fragment
 
-    f32x4 accU[NT];
+    f32x4 accU[CT][NT];
 #pragma unroll
-    for (int a = 0; a < NT; ++a) accU[a] = rU[a];
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int a = 0; a < NT; ++a) accU[c][a] = raw_f32(rU[c][a]);
     __syncthreads();
+    if (EPI) load_gate(t0, nv);
     if (!PF_P) load_p(ci);
     if (ci + 1 < nch) load_u(ci + 1);
 
-    // Four-wave blocks: each stage first issues all of its LDS fragment
-    // reads (the scheduling barrier keeps them ahead of the matrix-core work,
-    // so they are in flight together instead of one at a time), then runs its
-    // products with the independent accumulators interleaved.  The nine-wave
-    // whole-head blocks lack the registers and stream one fragment at a time.
-    constexpr bool BATCH = NWC == 4;
-    Frag<E> sf[4];
+    // Four-wave single-tile blocks: each stage first issues all of its LDS
+    // fragment reads (the scheduling barrier keeps them ahead of the
+    // matrix-core work, so they are in flight together instead of one at a
+    // time), then runs its products with the independent accumulators
+    // interleaved.  Two-tile waves lack the registers for that and stream one
+    // fragment at a time, each feeding both of their tiles.
+    constexpr bool BATCH = NWC == 4 && CT == 1;
+    Frag<E> sf[CT][4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) frag_from_acc(sf[ks], accS[2 * ks], accS[2 * ks + 1]);
-    f32x4 accO[NT];
+    for (int c = 0; c < CT; ++c)
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt) accO[rt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < 4; ++ks) frag_from_acc(sf[c][ks], accS[c][2 * ks], accS[c][2 * ks + 1]);
+    f32x4 accO[CT][NT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) accO[c][rt] = (f32x4){0.f, 0.f, 0.f, 0.f};
     if constexpr (BATCH) {
       // ---- S1: U = U' - W S ----
       Frag<E> fa[4 * NT];
@@ -275,7 +316,7 @@ __global__ __launch_bounds__(64 * (DV / 16 + 1)) void carry_kernel(const CarryAr
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int rt = 0; rt < NT; ++rt) accU[rt] = mma(accU[rt], fa[rt * 4 + ks], sf[ks]);
+        for (int rt = 0; rt < NT; ++rt) accU[0][rt] = mma(accU[0][rt], fa[rt * 4 + ks], sf[0][ks]);
       // ---- S2: O = Qt S (+ P U below) ----
 #pragma unroll
       for (int i = 0; i < 4 * NT; ++i) ld_frag(fa[i], sQt + i * FRE);
@@ -283,7 +324,7 @@ __global__ __launch_bounds__(64 * (DV / 16 + 1)) void carry_kernel(const CarryAr
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int rt = 0; rt < NT; ++rt) accO[rt] = mma(accO[rt], fa[rt * 4 + ks], sf[ks]);
+        for (int rt = 0; rt < NT; ++rt) accO[0][rt] = mma(accO[0][rt], fa[rt * 4 + ks], sf[0][ks]);
     } else {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
@@ -291,7 +332,8 @@ __global__ __launch_bounds__(64 * (DV / 16 + 1)) void carry_kernel(const CarryAr
         for (int rt = 0; rt < NT; ++rt) {
           Frag<E> fa;
           ld_frag(fa, sW + (rt * 4 + ks) * FRE);
-          accU[rt] = mma(accU[rt], fa, sf[ks]);
+#pragma unroll
+          for (int c = 0; c < CT; ++c) accU[c][rt] = mma(accU[c][rt], fa, sf[c][ks]);
         }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
@@ -299,56 +341,28 @@ __global__ __launch_bounds__(64 * (DV / 16 + 1)) void carry_kernel(const CarryAr
         for (int rt = 0; rt < NT; ++rt) {
           Frag<E> fa;
           ld_frag(fa, sQt + (rt * 4 + ks) * FRE);
-          accO[rt] = mma(accO[rt], fa, sf[ks]);
+#pragma unroll
+          for (int c = 0; c < CT; ++c) accO[c][rt] = mma(accO[c][rt], fa, sf[c][ks]);
         }
     }
-    Frag<E> uf[KT];
+    Frag<E> uf[CT][KT];
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) frag_from_acc(uf[kt], accU[2 * kt], accU[2 * kt + 1]);
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) frag_from_acc(uf[c][kt], accU[c][2 * kt], accU[c][2 * kt + 1]);
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt)
-        if (kt <= rt / 2) accO[rt] = mma(accO[rt], rP[F::p_frag(rt, kt)], uf[kt]);
+        if (kt <= rt / 2)
+#pragma unroll
+          for (int c = 0; c < CT; ++c) accO[c][rt] = mma(accO[c][rt], rP[F::p_frag(rt, kt)], uf[c][kt]);
     if (PF_P && ci + 1 < nch) load_p(ci + 1);
 
-    if (EPI) {
-      // head-wise RMSNorm over the 128 value channels, then the sigmoid gate;
-      // the gate logits of this chunk are read through a buffer view with
-      // 32-bit offsets (rows past the sequence end read its last row)
-      const Rsrc gr = make_rsrc(static_cast<const E*>(p.gate) + t0 * rs, (uint32_t)(C * rs * ES));
-      float gl[NT][4];
-#pragma unroll
-      for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = min(16 * rt + 4 * g + i, nv - 1);
-          gl[rt][i] = buf_ld_elem(gr, (uint32_t)((tok * rs + hoff + col0 + l16) * ES), (E*)nullptr);
-        }
-#pragma unroll
-      for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float ss = accO[rt][i] * accO[rt][i];
-#pragma unroll
-          for (int m = 1; m < 16; m <<= 1) ss += __shfl_xor(ss, m);
-          if (l16 == 0) sSS[wv * C + 16 * rt + 4 * g + i] = ss;
-        }
-      __syncthreads();
-#pragma unroll
-      for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = 16 * rt + 4 * g + i;
-          float ms = 0.f;
-#pragma unroll
-          for (int q = 0; q < NWC; ++q) ms += sSS[q * C + tok];
-          const float inv = rsqrtf(ms * (1.f / D) + p.rms_eps);
-          accO[rt][i] *= inv * norm_w * sigmoidf_fast(gl[rt][i]);
-        }
-    }
     // outputs: each 16 x 16 tile transposed on the matrix cores to lane =
-    // token, four consecutive columns, and stored straight to global memory
+    // token, four consecutive columns, then (with the epilogue) the head-wise
+    // RMSNorm over the 128 value columns and the sigmoid gate, and stored
+    // straight to global memory
     {
       Frag16<E> id;
       {
@@ -357,19 +371,59 @@ __global__ __launch_bounds__(64 * (DV / 16 + 1)) void carry_kernel(const CarryAr
         for (int e = 0; e < 4; ++e) x[e] = (4 * g + e == l16) ? 1.f : 0.f;
         frag16_from_acc(id, x);
       }
-#pragma unroll
-      for (int rt = 0; rt < NT; ++rt) {
-        Frag16<E> a;
-        frag16_from_acc(a, accO[rt]);
-        const f32x4 t = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, a, id);
+      auto store = [&](const f32x4& t, int c, int rt) {
         const int tok = 16 * rt + l16;
         if (tok < nv) {
-          E* dst = go + (t0 + tok) * rs + hoff + col0 + 4 * g;
+          E* dst = go + (t0 + tok) * rs + hoff + col0 + 16 * c + 4 * g;
           if constexpr (ES == 2)
             *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
           else
             *reinterpret_cast<f32x4*>(dst) = t;
         }
+      };
+      if constexpr (EPI) {
+        f32x4 ot[CT][NT];
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+          float ss = 0.f;
+#pragma unroll
+          for (int c = 0; c < CT; ++c) {
+            Frag16<E> a;
+            frag16_from_acc(a, accO[c][rt]);
+            ot[c][rt] = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, a, id);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss += ot[c][rt][e] * ot[c][rt][e];
+          }
+          ss += __shfl_xor(ss, 16);
+          ss += __shfl_xor(ss, 32);
+          if (g == 0) sSS[wv * C + 16 * rt + l16] = ss;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+          const int tok = 16 * rt + l16;
+          float ms = 0.f;
+#pragma unroll
+          for (int q = 0; q < NWC; ++q) ms += sSS[q * C + tok];
+          const float inv = rsqrtf(ms * (1.f / D) + p.rms_eps);
+#pragma unroll
+          for (int c = 0; c < CT; ++c) {
+            const f32x4 gl = raw_f32(rG[c][rt]);
+            f32x4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = ot[c][rt][e] * (inv * nw[c][e] * sigmoidf_fast(gl[e]));
+            store(y, c, rt);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+          for (int c = 0; c < CT; ++c) {
+            Frag16<E> a;
+            frag16_from_acc(a, accO[c][rt]);
+            store(mma16((f32x4){0.f, 0.f, 0.f, 0.f}, a, id), c, rt);
+          }
       }
     }
 
@@ -383,20 +437,23 @@ __global__ __launch_bounds__(64 * (DV / 16 + 1)) void carry_kernel(const CarryAr
       for (int rt8 = 0; rt8 < 8; ++rt8) gam[rt8] = *reinterpret_cast<const f32x4*>(sGam + 16 * rt8 + 4 * g);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int rt8 = 0; rt8 < 8; ++rt8) accS[rt8] *= gam[rt8];
+      for (int rt8 = 0; rt8 < 8; ++rt8) accS[0][rt8] *= gam[rt8];
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int rt8 = 0; rt8 < 8; ++rt8) accS[rt8] = mma(accS[rt8], fa[rt8 * KT + kt], uf[kt]);
+        for (int rt8 = 0; rt8 < 8; ++rt8) accS[0][rt8] = mma(accS[0][rt8], fa[rt8 * KT + kt], uf[0][kt]);
     } else {
 #pragma unroll
       for (int rt8 = 0; rt8 < 8; ++rt8) {
-        accS[rt8] *= *reinterpret_cast<const f32x4*>(sGam + 16 * rt8 + 4 * g);
+        const f32x4 gam = *reinterpret_cast<const f32x4*>(sGam + 16 * rt8 + 4 * g);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) accS[c][rt8] *= gam;
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
           Frag<E> fa;
           ld_frag(fa, sKbt + (rt8 * KT + kt) * FRE);
-          accS[rt8] = mma(accS[rt8], fa, uf[kt]);
+#pragma unroll
+          for (int c = 0; c < CT; ++c) accS[c][rt8] = mma(accS[c][rt8], fa, uf[c][kt]);
         }
       }
     }
@@ -405,34 +462,38 @@ __global__ __launch_bounds__(64 * (DV / 16 + 1)) void carry_kernel(const CarryAr
   if (p.state_out) {
     const int l16 = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int rt8 = 0; rt8 < 8; ++rt8)
+    for (int c = 0; c < CT; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        p.state_out[sbase + (size_t)(16 * rt8 + 4 * g + i) * D + col0 + l16] = accS[rt8][i];
+      for (int rt8 = 0; rt8 < 8; ++rt8)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          p.state_out[sbase + (size_t)(16 * rt8 + 4 * g + i) * D + col0 + 16 * c + l16] = accS[c][rt8][i];
   }
 }
 
-template <typename E, int C, int DV, bool EPI>
+template <typename E, int C, int DV, bool EPI, int CT>
 static hipError_t launch_carry_t(const CarryArgs& a, hipStream_t stream) {
-  constexpr size_t lds = CarryLayout<E, C, DV>::BYTES;
+  constexpr int NWC = DV / (16 * CT);
+  constexpr size_t lds = CarryLayout<E, C, NWC>::BYTES;
   static_assert(lds <= 160 * 1024, "LDS budget exceeded");
-  auto fn = carry_kernel<E, C, DV, EPI>;
+  auto fn = carry_kernel<E, C, DV, EPI, CT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int groups = (a.units + 7) / 8;
   const unsigned grid = (unsigned)(8 * a.col_split * groups);
   if (a.units <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * (DV / 16 + 1)), lds, stream, a);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * (NWC + 1)), lds, stream, a);
   return hipGetLastError();
 }
 
 template <typename E, int C>
 static hipError_t launch_carry_dtype(const CarryArgs& a, hipStream_t stream) {
-  // whole heads (the epilogue normalises over all 128 value columns), else
-  // two 64-column blocks per head that share the factor reads through L2
-  if (a.gate) return a.col_split == 1 ? launch_carry_t<E, C, 128, true>(a, stream) : hipErrorInvalidValue;
-  return a.col_split == 2 ? launch_carry_t<E, C, 64, false>(a, stream) : hipErrorInvalidValue;
+  // whole heads (the epilogue normalises over all 128 value columns) on four
+  // two-tile waves, else two 64-column blocks per head on four one-tile
+  // waves, the blocks sharing the factor reads through L2
+  if (a.gate) return a.col_split == 1 ? launch_carry_t<E, C, 128, true, 2>(a, stream) : hipErrorInvalidValue;
+  return a.col_split == 2 ? launch_carry_t<E, C, 64, false, 1>(a, stream) : hipErrorInvalidValue;
 }
 
 hipError_t launch_carry(const CarryArgs& a, hipStream_t stream) {

@@ -79,6 +79,68 @@ __device__ __forceinline__ float row_scan(float x) {
 // Piece pc = 2 s + h of a lane's channels: channels 32 s + 16 h + 4 g + {0..3}.
 __device__ __forceinline__ int piece_ch(int pc, int g) { return 32 * (pc >> 1) + 16 * (pc & 1) + 4 * g; }
 
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// 32-bit DPP moves within 16-lane rows: shift right by N (zero fill), rotate
+// right by N, broadcast of lane N.
+template <int N>
+__device__ __forceinline__ uint32_t dpp_shr(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x110 + N, 0xf, 0xf, true);
+}
+template <int N>
+__device__ __forceinline__ uint32_t dpp_ror(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x120 + N, 0xf, 0xf, false);
+}
+// Shift right by N; lanes with no source (the first N of a row) keep `old`.
+template <int N>
+__device__ __forceinline__ uint32_t dpp_shr_or(uint32_t old, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, 0x110 + N, 0xf, 0xf, false);
+}
+template <int N>
+__device__ __forceinline__ float dpp_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, false));
+}
+
+// Rows tok - 1 .. tok - 3 of a piece, for the lane at row position r: from
+// lane r - s of the own rows when r >= s, else from lane r - s + 16 of the
+// halo rows (row tok - 16 there).  x[s][0..3] receives row tok - s.  Both
+// moves run in every lane (a DPP read from a lane switched off by a branch
+// would return zero): the rotated halo is the shift's fallback value.
+template <typename R>
+__device__ __forceinline__ void shifted_rows(float (&x)[4][4], const R& own, const R& halo) {
+  constexpr int NW = (int)sizeof(own.v) / 4;
+  const auto ow = __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(NW))), own.v);
+  const auto hw = __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(NW))), halo.v);
+  static_for<1, 4>([&](auto sc) {
+    constexpr int s = decltype(sc)::value;
+    uint32_t __attribute__((ext_vector_type(NW))) y;
+#pragma unroll
+    for (int j = 0; j < NW; ++j) y[j] = dpp_shr_or<s>(dpp_ror<s>(hw[j]), ow[j]);
+    R t;
+    t.v = __builtin_bit_cast(decltype(own.v), y);
+    cvt_raw4(x[s], t);
+  });
+}
+
+// The four taps of channel piece_ch(pc, g) + i from lane 2 pc + i / 2 of the
+// lane's row, which holds them at (i % 2) * 4 + m.
+__device__ __forceinline__ void tap_bcast(float (&wt)[4], const float (&wl)[8], int pc, int i) {
+  static_for<0, 16>([&](auto nc) {
+    constexpr int n = decltype(nc)::value;
+    if (n == 2 * pc + (i >> 1)) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) wt[m] = dpp_bcast<n>(wl[(i & 1) * 4 + m]);
+    }
+  });
+}
+
 // Fragment of step s from the lane's per-piece values x[8][4].
 __device__ __forceinline__ void frag_step(Frag<__bf16>& f, const float (&x)[8][4], int s) {
   f.v = (bf16x8){(__bf16)x[2 * s][0], (__bf16)x[2 * s][1], (__bf16)x[2 * s][2], (__bf16)x[2 * s][3],
@@ -257,6 +319,19 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
   int nv = 0;
   slot_range(s_begin, t0, seq_bos, nv);
   if (PREFETCH) issue_loads(t0, nv);
+  // Prologue taps: lane (r, g) keeps those of channels piece_ch(r / 2, g)
+  // + 2 (r % 2) + {0, 1} (four each), the lanes of a 16-lane row together
+  // holding the taps of every channel that row uses.
+  float wlq[8], wlk[8];
+  if constexpr (PRO) {
+    auto load_taps = [&](float (&wl)[8], const float* wc) {
+      const int64_t ch = hoff + piece_ch(r >> 1, g) + 2 * (r & 1);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wl[j] = wc ? wc[ch * 4 + j] : 0.f;
+    };
+    load_taps(wlq, p.conv_q_w);
+    load_taps(wlk, p.conv_k_w);
+  }
 
   for (int s = s_begin; s < s_end; ++s) {
     // Lane indices re-derived from an opaque copy of the thread id in every
@@ -275,39 +350,51 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
     {
       if constexpr (PRO) {
         // causal depthwise conv over rows tok-3 .. tok (zero before the
-        // sequence start), SiLU, then L2 over the head's 128 channels
+        // sequence start), SiLU, then L2 over the head's 128 channels.  Each
+        // lane loads its own row; rows tok-1 .. tok-3 come from the lanes
+        // below it in the same 16-lane row (DPP row shifts), and for the
+        // first three tokens of a tile from the halo row tok-16 that lanes
+        // 13..15 load (DPP row rotates).  The taps come from the lanes that
+        // hold them (row broadcasts).
         const int lo = (int)(seq_bos - t0);  // first row of the sequence, <= 0
-        auto prologue = [&](QK (&y)[8], const E* src, const float* wconv) {
+        const int64_t own_row = t0 + min(tok, nv - 1);
+        const bool has_halo = r >= 13 && tok - 16 >= lo;
+        const int64_t halo_row = t0 + min(tok - 16, nv - 1);
+        Raw4<E> oq[8], hq[8], ok[8], hk[8];
+        auto load_rows = [&](Raw4<E> (&own)[8], Raw4<E> (&halo)[8], const E* src) {
+#pragma unroll
+          for (int pc = 0; pc < 8; ++pc) {
+            ld_raw4(own[pc], src + own_row * rs + hoff + piece_ch(pc, g));
+            halo[pc].v = 0;
+          }
+          if (has_halo)
+#pragma unroll
+            for (int pc = 0; pc < 8; ++pc) ld_raw4(halo[pc], src + halo_row * rs + hoff + piece_ch(pc, g));
+        };
+        load_rows(oq, hq, gq);
+        load_rows(ok, hk, gk);
+        auto prologue = [&](QK (&y)[8], const Raw4<E> (&own)[8], const Raw4<E> (&halo)[8], const float (&wl)[8],
+                            bool conv) {
           float ss = 0.f;
 #pragma unroll
           for (int pc = 0; pc < 8; ++pc) {
-            Raw4<E> raw[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              const int rr = min(max(tok - 3 + m, lo), nv - 1);
-              ld_raw4(raw[m], src + (t0 + rr) * rs + hoff + piece_ch(pc, g));
-            }
-            float x[4][4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              cvt_raw4(x[m], raw[m]);
-              if (tok - 3 + m < lo)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x[m][i] = 0.f;
-            }
+            float x[4][4];  // x[s] = row tok - s
+            cvt_raw4(x[0], own[pc]);
+            shifted_rows(x, own[pc], halo[pc]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              float c = x[3][i];
-              if (wconv) {
-                const float* wc = wconv + (hoff + piece_ch(pc, g) + i) * 4;
-                c = wc[0] * x[0][i] + wc[1] * x[1][i] + wc[2] * x[2][i] + wc[3] * x[3][i];
+              float c = x[0][i];
+              if (conv) {
+                float wt[4];
+                tap_bcast(wt, wl, pc, i);
+                c = wt[0] * x[3][i] + wt[1] * x[2][i] + wt[2] * x[1][i] + wt[3] * x[0][i];
                 c = c * sigmoidf_fast(c);
                 ss += c * c;
               }
               y[pc].v[i] = c;
             }
           }
-          if (wconv) {
+          if (conv) {
             ss += __shfl_xor(ss, 16);
             ss += __shfl_xor(ss, 32);
             const float inv = rsqrtf(ss + p.l2_eps);
@@ -315,8 +402,8 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
             for (int pc = 0; pc < 8; ++pc) y[pc].v *= inv;
           }
         };
-        prologue(rq, gq, p.conv_q_w);
-        prologue(rk, gk, p.conv_k_w);
+        prologue(rq, oq, hq, wlq, p.conv_q_w != nullptr);
+        prologue(rk, ok, hk, wlk, p.conv_k_w != nullptr);
       }
 #pragma unroll
       for (int pc = 0; pc < 8; ++pc) cvt_raw4(dl[pc], rla[pc]);
