@@ -276,7 +276,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
     const unsigned char* buf = smem + (ci % L::NBUF) * L::SLOT;
     const E* sW = reinterpret_cast<const E*>(buf + L::W + lane_fr);
     const E* sQt = reinterpret_cast<const E*>(buf + L::Q + lane_fr);
-    const E* sKbt = reinterpret_cast<const E*>(buf + L::K + lane_fr);
+    const E* sKbt = reinterpret_cast<const E*>(buf + L::K + lane * 4 * ES);  // fragments split in halves
     const float* sGam = reinterpret_cast<const float*>(buf + L::G);
     constexpr int FRE = (int)F::FR / ES;  // elements per fragment
 
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
     if constexpr (BATCH) {
       Frag<E> fa[8 * KT];
 #pragma unroll
-      for (int i = 0; i < 8 * KT; ++i) ld_frag(fa[i], sKbt + i * FRE);
+      for (int i = 0; i < 8 * KT; ++i) ld_frag_pair(fa[i], sKbt + i * FRE, sKbt + i * FRE + FRE / 2);
       f32x4 gam[8];
 #pragma unroll
       for (int rt8 = 0; rt8 < 8; ++rt8) gam[rt8] = *reinterpret_cast<const f32x4*>(sGam + 16 * rt8 + 4 * g);
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
           Frag<E> fa;
-          ld_frag(fa, sKbt + (rt8 * KT + kt) * FRE);
+          ld_frag_pair(fa, sKbt + (rt8 * KT + kt) * FRE, sKbt + (rt8 * KT + kt) * FRE + FRE / 2);
 #pragma unroll
           for (int c = 0; c < CT; ++c) accS[c][rt8] = mma(accS[c][rt8], fa, uf[c][kt]);
         }

@@ -84,7 +84,9 @@ struct ScanArgs {
 //                 order; rows tokens of tile rt, step kt over the tokens
 //                 (entries above the diagonal are zero)
 //   K  [8][C/32]  Kb^T: row tile rt8 = key channels 16 rt8 + l % 16, step kt
-//                 over the tokens
+//                 over the tokens; each fragment split in halves, [2][64][4]
+//                 (elements 0..3 of every lane, then elements 4..7), as the
+//                 two token tiles of a step come from different prep waves
 //   G  [128]      e^{g_n} per key channel (fp32)
 //   U  [NT][8][64][4]  U' = T V in accumulator order: token tile a, column
 //                 tile ct, lane, element i = (token 16 a + 4 (lane / 16) + i,

@@ -204,6 +204,16 @@ __device__ __forceinline__ void st_half_g(Rsrc rb, uint32_t off, f32x4 x, __bf16
 __device__ __forceinline__ void st_half_g(Rsrc rb, uint32_t off, f32x4 x, float*) {
   buf_st16(__builtin_bit_cast(u32x4, x), rb, off, 0);
 }
+// Both halves of a lane's fragment entry (first half lo, second half hi).
+__device__ __forceinline__ void st_pair_g(Rsrc rb, uint32_t off, f32x4 lo, f32x4 hi, __bf16*) {
+  const bf16x8 b = {(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
+                    (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
+  buf_st16(__builtin_bit_cast(u32x4, b), rb, off, 0);
+}
+__device__ __forceinline__ void st_pair_g(Rsrc rb, uint32_t off, f32x4 lo, f32x4 hi, float*) {
+  buf_st16(__builtin_bit_cast(u32x4, lo), rb, off, 0);
+  buf_st16(__builtin_bit_cast(u32x4, hi), rb, off + 16, 0);
+}
 
 template <typename E, int C>
 struct PrepLayout {
@@ -220,7 +230,9 @@ struct PrepLayout {
   static constexpr size_t R = KE + (size_t)NPAIR * 4 * 64 * 8 * ES;  // [16][NT][64][4] right-hand sides
   static constexpr size_t AD = R + (size_t)16 * NT * 64 * 4 * ES;    // f32 [NT][16][16] diagonal blocks
   static constexpr size_t M = AD + (size_t)NT * 256 * 4;             // E [C][LDM] solve blocks
-  static constexpr size_t BYTES = M + (size_t)C * LDM * ES;
+  static constexpr int MAXR = 16;                                    // chunks per workgroup, at most
+  static constexpr size_t RNG = (M + (size_t)C * LDM * ES + 7) & ~(size_t)7;  // i64 [MAXR][3] t0, bos, nv
+  static constexpr size_t BYTES = RNG + (size_t)MAXR * 3 * 8;
 };
 
 }  // namespace
@@ -236,6 +248,7 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
   constexpr int NT = C / 16;          // token tiles = waves
   constexpr int NTH = 64 * NT;
   constexpr int CPW = 8 / NT;         // W (and U') column tiles per wave in the solve
+  static_assert(CPW % 2 == 0, "a wave stores whole -W fragments");
   constexpr int NOWN = 2 * CPW;
   constexpr bool SPLIT = sizeof(E) == 2;
   constexpr int ES = (int)sizeof(E);
@@ -272,16 +285,27 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
   const int tok = 16 * w + r;  // this lane's token within the chunk
   const uint32_t lane_fr = (uint32_t)lane * 8 * ES;  // lane's entry in a fragment
 
-  // sequence of slot s: the largest n with seq_first[n] <= s (seq_first[N] > s)
-  int n = 0;
-  {
-    int hi = N;
+  // Token range of every slot of this workgroup, found once up front and
+  // kept in LDS: global loads in the chunk loop would make its waits drain
+  // the factor stores in flight (loads and stores share one counter).
+  int64_t* sRng = reinterpret_cast<int64_t*>(smem + L::RNG);
+  if (tid < s_end - s_begin) {
+    const int s = s_begin + tid;
+    // sequence of slot s: the largest n with seq_first[n] <= s (seq_first[N] > s)
+    int n = 0, hi = N;
     while (hi - n > 1) {
       const int mid = (n + hi) >> 1;
-      if (p.seq_first[mid] <= s_begin) n = mid;
+      if (p.seq_first[mid] <= s) n = mid;
       else hi = mid;
     }
+    const int64_t bos = p.cu ? (int64_t)p.cu[n] : 0;
+    const int64_t eos = p.cu ? (int64_t)p.cu[n + 1] : p.total_tokens;
+    const int64_t t0 = bos + (int64_t)(p.seq_c0[n] + (s - p.seq_first[n])) * C;
+    sRng[3 * tid] = t0;
+    sRng[3 * tid + 1] = bos;
+    sRng[3 * tid + 2] = min((int64_t)C, eos - t0);
   }
+  __syncthreads();
 
   // Inputs of one chunk for this lane's token: q and k (after the prologue
   // when it runs; in the input dtype otherwise), v, log_alpha, beta.  For
@@ -295,11 +319,10 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
   Raw4<float> rla[8];
   float rbt = 0.f;
   auto slot_range = [&](int s, int64_t& t0, int64_t& bos, int& nv) {
-    while (p.seq_first[n + 1] <= s) ++n;
-    bos = p.cu ? (int64_t)p.cu[n] : 0;
-    const int64_t eos = p.cu ? (int64_t)p.cu[n + 1] : p.total_tokens;
-    t0 = bos + (int64_t)(p.seq_c0[n] + (s - p.seq_first[n])) * C;
-    nv = (int)min((int64_t)C, eos - t0);
+    const int j = s - s_begin;
+    t0 = sRng[3 * j];
+    bos = sRng[3 * j + 1];
+    nv = (int)sRng[3 * j + 2];
   };
   auto issue_loads = [&](int64_t t0, int nv) {
     const int64_t row = t0 + min(tok, nv - 1);
@@ -538,7 +561,8 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
           frag_step_split(kih[st], kil[st], xs, st);
         }
         // K_end = K e^{rho_{w+1} - g} <= 1; Kb = K_end e^{g_n - rho_{w+1}} as
-        // channel-per-lane halves of the Kb^T fragments (rt8, kt = w / 2, half w % 2)
+        // channel-per-lane halves of the Kb^T fragments (rt8, kt = w / 2, half
+        // w % 2), each half a contiguous 64-lane block
         fac8(fac, sFE + w * 128, st);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] *= fac[e];
@@ -548,7 +572,8 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
         frag8(a, y);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
-          st_half_g(fb, F::K + (uint32_t)((2 * st + hh) * F::KT + (w >> 1)) * F::FR + lane_fr + (uint32_t)(w & 1) * 4 * ES,
+          st_half_g(fb, F::K + (uint32_t)((2 * st + hh) * F::KT + (w >> 1)) * F::FR + (uint32_t)(w & 1) * (F::FR / 2) +
+                            (uint32_t)lane * 4 * ES,
                     select(a, hh), (E*)nullptr);
         // column-tile copies for the later row tiles a > w, scaled by
         // e^{rho_a - rho_{w+1}} = prod_{w < c < a} e^{tot_c}
@@ -645,27 +670,26 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
     }
     // P tiles: transposed on the matrix cores into the carry's fragment order
     // (lane = token of tile w, four tokens of tile b); the diagonal tile keeps
-    // its lower triangle; the tile right of an even diagonal is zero.
+    // its lower triangle; the tile right of an even diagonal is zero.  Tiles
+    // 2 kt and 2 kt + 1 are the two halves of fragment (w, kt), stored together.
     {
       const Frag16<E> id = ident16<E>(lane);
+      auto ptile = [&](int b) -> f32x4 {
+        if (b > w) return (f32x4){0.f, 0.f, 0.f, 0.f};
+        f32x4 pv = gp[b == w ? NT - 1 : b];
+        if (b == w)
 #pragma unroll
-      for (int b = 0; b < NT; ++b) {
-        if (b <= w) {
-          f32x4 pv = gp[b == w ? NT - 1 : b];
-          if (b == w)
+          for (int i = 0; i < 4; ++i)
+            if (r > 4 * g + i) pv[i] = 0.f;  // column r above row 4g+i
+        Frag16<E> a;
+        frag16_from_acc(a, pv);
+        return mma16((f32x4){0.f, 0.f, 0.f, 0.f}, a, id);
+      };
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (r > 4 * g + i) pv[i] = 0.f;  // column r above row 4g+i
-          Frag16<E> a;
-          frag16_from_acc(a, pv);
-          const f32x4 t = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, a, id);
-          st_half_g(fb, F::P + (uint32_t)F::p_frag(w, b >> 1) * F::FR + lane_fr + (uint32_t)(b & 1) * 4 * ES, t,
+      for (int kt = 0; kt < NT / 2; ++kt)
+        if (2 * kt <= w)
+          st_pair_g(fb, F::P + (uint32_t)F::p_frag(w, kt) * F::FR + lane_fr, ptile(2 * kt), ptile(2 * kt + 1),
                     (E*)nullptr);
-        }
-      }
-      if ((w & 1) == 0)
-        st_half_g(fb, F::P + (uint32_t)F::p_frag(w, w >> 1) * F::FR + lane_fr + 4 * ES, (f32x4){0.f, 0.f, 0.f, 0.f},
-                  (E*)nullptr);
     }
     __syncthreads();
 
@@ -679,6 +703,7 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
 #pragma unroll
       for (int a = 0; a < NT; ++a) {
         f32x4 z[NOWN];
+        f32x4 w_even = (f32x4){0.f, 0.f, 0.f, 0.f};  // -W of the even channel tile, stored with the odd one
 #pragma unroll
         for (int o = 0; o < NOWN; ++o) {
           const int ct = (o < CPW) ? CPW * w + o : 8 + CPW * w + (o - CPW);
@@ -703,13 +728,16 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
           frag16_from_acc(Yb[o][a], y);
           if (o < CPW) {
             // -W: the 16 x 16 tile transposed on the matrix cores to lane =
-            // token, four channels; channel tile ct is half ct % 2 of key step ct / 2
+            // token, four channels; channel tile ct is half ct % 2 of key step
+            // ct / 2, and this wave owns both tiles of its steps (CPW is even)
             Frag16<E> yn;
             frag16_from_acc(yn, -y);
             const f32x4 t = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, yn, id);
             const int ct = CPW * w + o;
-            st_half_g(fb, F::W + (uint32_t)(a * 4 + (ct >> 1)) * F::FR + lane_fr + (uint32_t)(ct & 1) * 4 * ES, t,
-                      (E*)nullptr);
+            if ((o & 1) == 0)
+              w_even = t;
+            else
+              st_pair_g(fb, F::W + (uint32_t)(a * 4 + (ct >> 1)) * F::FR + lane_fr, w_even, t, (E*)nullptr);
           } else {
             // U' in accumulator order, in the I/O dtype
             const int ct = CPW * w + (o - CPW);
@@ -735,6 +763,7 @@ hipError_t launch_prep_t(const PrepArgs& a, hipStream_t stream) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
+  if (a.chunks_per_block < 1 || a.chunks_per_block > PrepLayout<E, C>::MAXR) return hipErrorInvalidValue;
   const int64_t ranges = ((int64_t)a.cap + a.chunks_per_block - 1) / a.chunks_per_block;
   const int64_t grid = ranges * a.num_heads;
   if (grid <= 0) return hipSuccess;
