@@ -2,15 +2,15 @@
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 1]
                     [--no-decode] [--no-cpu-baseline] [--decode-steps 64]
-                    [--extra-workloads 2,4] [--extra-steps 3]
+                    [--extra-workloads 2,4,5] [--extra-steps 3]
 
 A step is one kda_chunk_fwd over one layer of the workload (all heads, all
 tokens, inputs already resident in HBM): by default the one-layer K3 shape
 H=96, d=128, T=8192 with a carried fp32 state.  `value` is prefill tokens/s.
 The decode workload (256 sequences x 96 heads, 64 in-place kda_decode_step
-calls) is timed after it and reported under "decode"; the long-context (T=131072)
-and the varlen fused prologue/epilogue workloads are timed with fewer steps and
-reported under "workloads".  Kernel durations come from HIP events on the
+calls) is timed after it and reported under "decode"; the long-context (T=131072),
+the varlen fused prologue/epilogue and the few-head (H=8, T=131072, segmented
+schedule) workloads are timed with fewer steps and reported under "workloads".  Kernel durations come from HIP events on the
 stream the kernels run on.
 
 Prints one JSON line.  Only the optional CPU-baseline leg touches the oracle.
@@ -111,22 +111,25 @@ def cpu_baseline(inp, max_seconds_hint=20.0):
                       % (nh, H, T, dt, H)}
 
 
-def time_prefill(kda, kda_inputs, wid, steps, warmup, dev, stream):
+def time_prefill(kda, kda_inputs, wid, steps, warmup, dev, stream, inp=None, **call_kw):
     """Time `steps` kda_chunk_fwd calls over prefill workload `wid` (inputs
-    generated on the device first): wall clock around the steps, HIP events
-    per call, and the algorithmic-byte roofline."""
+    generated on the device first unless given): wall clock around the
+    steps, HIP events per call, and the algorithmic-byte roofline."""
     import torch
     w = kda_inputs.WORKLOADS[wid]
-    inp = kda_inputs.make_workload(wid, device=dev)
+    if inp is None:
+        inp = kda_inputs.make_workload(wid, device=dev)
     T, H, N = inp["T"], inp["H"], inp["N"]
     es = 2 if w["dtype"] == "bf16" else 4
     kw = dict(initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"])
     for key in ("conv_q_w", "conv_k_w", "gate", "norm_w"):
         if inp.get(key) is not None:
             kw[key] = inp[key]
+    kw.update(call_kw)
     o = torch.empty_like(inp["v"])
     fs = torch.empty((N, H, 128, 128), dtype=torch.float32, device=dev)
-    ws_bytes = kda.chunk_fwd_workspace_bytes(N, T, H, inp["q"].dtype)
+    ws_bytes = kda.chunk_fwd_workspace_bytes(N, T, H, inp["q"].dtype, gated=kw.get("gate") is not None,
+                                             segment_tokens=int(kw.get("segment_tokens", 0)))
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     def step():
@@ -166,9 +169,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 4])
+    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 4, 5])
     ap.add_argument("--decode-steps", type=int, default=64)
-    ap.add_argument("--extra-workloads", default="2,4",
+    ap.add_argument("--extra-workloads", default="2,4,5",
                     help="other prefill workloads timed after the main one and reported under 'workloads' ('' = none)")
     ap.add_argument("--extra-steps", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
@@ -236,6 +239,12 @@ def main():
             if wid == args.workload:
                 continue
             inp, tm = time_prefill(kda, kda_inputs, wid, args.extra_steps, 1, dev, stream)
+            if wid == 5:
+                # the same call forced onto the sequential schedule, for comparison
+                _, seq = time_prefill(kda, kda_inputs, wid, args.extra_steps, 1, dev, stream, inp=inp,
+                                      segment_tokens=-1)
+                tm["sequential_schedule"] = {"tokens_per_s": seq["tokens_per_s"],
+                                             "kernel_ms_avg": seq["roofline"]["kernel_ms_avg"]}
             result["workloads"][tm["config"]["workload"]] = tm
             del inp
             torch.cuda.empty_cache()

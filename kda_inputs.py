@@ -32,7 +32,8 @@ import torch
 D = 128
 SEED_BASE = 0x4B444100
 
-# The five workloads: shapes of one K3 KDA layer (and the small fp32 case).
+# The five workloads (shapes of one K3 KDA layer, and the small fp32 case),
+# plus a few-head long prefill that exercises the segmented schedule.
 WORKLOADS = {
     0: dict(name="kda_fp32_H2_T256", kind="prefill", dtype="f32", H=2, lengths=[256], s0_std=0.0,
             fused=False),
@@ -44,6 +45,10 @@ WORKLOADS = {
             s0_std=0.02),
     4: dict(name="kda_varlen64_fused_H96", kind="prefill", dtype="bf16", H=96, lengths="loguniform64",
             s0_std=0.0, fused=True),
+    # few chains: 8 heads of one long sequence fill 16 of 256 compute units
+    # sequentially, so the library cuts the sequence into segments
+    5: dict(name="kda_prefill_H8_T131072", kind="prefill", dtype="bf16", H=8, lengths=[131072],
+            s0_std=0.02, fused=False),
 }
 
 
@@ -146,7 +151,7 @@ def make_decode(N, H, steps, dtype="bf16", s0_std=0.02, device="cpu", seed=SEED_
 
 
 def make_workload(wid: int, device="cpu", **overrides):
-    """Inputs of one of the five workloads (overrides: e.g. lengths or steps)."""
+    """Inputs of one of the workloads above (overrides: e.g. lengths or steps)."""
     w = dict(WORKLOADS[wid])
     w.update(overrides)
     seed = SEED_BASE + wid
