@@ -93,55 +93,64 @@ int64_t choose_segment_tokens(int num_seqs, int64_t total_tokens, int num_heads,
 #endif
 constexpr size_t kFactorBudget = (size_t)KDA_FACTOR_BUDGET_MIB << 20;
 
-// Workspace layout, each piece 256-byte aligned.
-// Two-kernel schedule: the longest-first order [N] (N > 1), the window table
-// (seq_first [N+1], seq_c0 [N], seq_c1 [N]), a state buffer [N,H,128,128]
-// fp32 carried between windows (more than one window only), and the factor
-// store [slots][H] blocks.  slots bounds the chunks of one window:
-// sum_n ceil(G_n / nw) <= (T / C + N) / nw + N, with G_n = ceil(L_n / C).
-// Segmented schedule: seq_first [N+1], seg_count, seg_list [2 cap], pairs
-// [cap][H][2][128][128] fp32; cap bounds the number of segments:
-// sum_n ceil(L_n / seg) <= T / seg + N.
+// Workspace layout, each piece 256-byte aligned: the longest-first order [N]
+// (N > 1), the window table (seq_first [N+1], seq_c0 [N], seq_c1 [N]); for
+// the segmented schedule the window's segment table (seg_first [N+1],
+// seg_count, seg_list [2 cap]) and the affine pairs [cap][H][2][128][128]
+// fp32; a state buffer [N,H,128,128] fp32 carried between windows (more than
+// one window only); the factor store [slots][H] blocks.
+// slots bounds the chunks of one window:
+//   sum_n ceil(G_n / nw) <= (T / C + N) / nw + N,  G_n = ceil(L_n / C);
+// cap bounds the segments of one window: sum_n ceil(W_n / s) <= slots / s + N
+// for window ranges W_n and s chunks per segment.
 struct Plan {
-  int64_t seg_len = 0;
-  int64_t cap = 0;
-  size_t off_count = 0, off_list = 0, off_pairs = 0;
   int nw = 1;
   int64_t slots = 0;
-  size_t off_first = 0, off_c0 = 0, off_c1 = 0, off_state = 0, off_factors = 0;
+  int64_t seg_chunks = 0;  // 0: sequential schedule
+  int64_t cap = 0;
+  size_t off_first = 0, off_c0 = 0, off_c1 = 0;
+  size_t off_segfirst = 0, off_count = 0, off_list = 0, off_pairs = 0;
+  size_t off_state = 0, off_factors = 0;
   size_t bytes = 0;
 };
 
 Plan make_plan(int num_seqs, int64_t total_tokens, int num_heads, kda_dtype dtype, const kda_fused_opts& f,
                int cus) {
   Plan pl;
-  pl.seg_len = choose_segment_tokens(num_seqs, total_tokens, num_heads, f, cus);
-  if (pl.seg_len == 0) {
-    const bool bf = dtype == KDA_DTYPE_BF16;
-    const int64_t C = kda::chunk_len(bf);
-    const size_t fb = kda::factor_block_bytes(bf);
-    const int64_t chunks = total_tokens / C + num_seqs;
-    const double total = (double)chunks * num_heads * fb;
-    pl.nw = (int)std::max<double>(1.0, std::ceil(total / (double)kFactorBudget));
-    pl.slots = chunks / pl.nw + num_seqs + 1;
-    size_t off = num_seqs > 1 ? align256((size_t)num_seqs * sizeof(int32_t)) : 0;
-    pl.off_first = off;
-    off += align256((size_t)(num_seqs + 1) * sizeof(int32_t));
-    pl.off_c0 = off;
-    off += align256((size_t)num_seqs * sizeof(int32_t));
-    pl.off_c1 = off;
-    off += align256((size_t)num_seqs * sizeof(int32_t));
-    pl.off_state = off;
-    if (pl.nw > 1) off += (size_t)num_seqs * num_heads * kD * kD * sizeof(float);
-    pl.off_factors = off;
-    pl.bytes = off + (size_t)pl.slots * num_heads * fb;
-    return pl;
+  const bool bf = dtype == KDA_DTYPE_BF16;
+  const int64_t C = kda::chunk_len(bf);
+  const size_t fb = kda::factor_block_bytes(bf);
+  const int64_t chunks = total_tokens / C + num_seqs;
+  const double total = (double)chunks * num_heads * fb;
+  pl.nw = (int)std::max<double>(1.0, std::ceil(total / (double)kFactorBudget));
+  pl.slots = chunks / pl.nw + num_seqs + 1;
+  // segments are cut from each window's share of the tokens
+  const int64_t seg = choose_segment_tokens(num_seqs, (total_tokens + pl.nw - 1) / pl.nw, num_heads, f, cus);
+  if (seg > 0) {
+    pl.seg_chunks = seg / C;
+    pl.cap = pl.slots / pl.seg_chunks + num_seqs + 1;
   }
-  pl.cap = total_tokens / pl.seg_len + num_seqs;
-  pl.off_count = align256((size_t)(num_seqs + 1) * sizeof(int32_t));
-  pl.off_list = pl.off_count + 256;
-  pl.off_pairs = pl.off_list + align256((size_t)pl.cap * 2 * sizeof(int32_t));
-  pl.bytes = pl.off_pairs + (size_t)pl.cap * num_heads * 2 * kD * kD * sizeof(float);
+  size_t off = num_seqs > 1 ? align256((size_t)num_seqs * sizeof(int32_t)) : 0;
+  pl.off_first = off;
+  off += align256((size_t)(num_seqs + 1) * sizeof(int32_t));
+  pl.off_c0 = off;
+  off += align256((size_t)num_seqs * sizeof(int32_t));
+  pl.off_c1 = off;
+  off += align256((size_t)num_seqs * sizeof(int32_t));
+  if (pl.seg_chunks > 0) {
+    pl.off_segfirst = off;
+    off += align256((size_t)(num_seqs + 1) * sizeof(int32_t));
+    pl.off_count = off;
+    off += 256;
+    pl.off_list = off;
+    off += align256((size_t)pl.cap * 2 * sizeof(int32_t));
+    pl.off_pairs = off;
+    off += (size_t)pl.cap * num_heads * 2 * kD * kD * sizeof(float);
+  }
+  pl.off_state = off;
+  if (pl.nw > 1) off += (size_t)num_seqs * num_heads * kD * kD * sizeof(float);
+  pl.off_factors = off;
+  pl.bytes = off + (size_t)pl.slots * num_heads * fb;
   return pl;
 }
 
@@ -156,8 +165,8 @@ bool sizes_ok(int num_seqs, int64_t total_tokens, int num_heads) {
 // fit the launch grid.
 bool segments_ok(const Plan& pl, int num_heads, const kda_fused_opts& f) {
   if (f.segment_tokens > 0 && f.segment_tokens % 64 != 0) return false;
-  if (pl.seg_len == 0) return pl.slots <= (int64_t)INT32_MAX / 2 && pl.slots * num_heads <= (int64_t)UINT32_MAX;
-  return pl.cap * num_heads <= (int64_t)INT32_MAX / 8;
+  if (!(pl.slots <= (int64_t)INT32_MAX / 2 && pl.slots * num_heads <= (int64_t)UINT32_MAX)) return false;
+  return pl.seg_chunks == 0 || pl.cap * num_heads <= (int64_t)INT32_MAX / 8;
 }
 
 }  // namespace
@@ -234,86 +243,66 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   }
   if (overlap(r_o, r_fs) || overlap(r_o, r_ws) || overlap(r_fs, r_ws)) return KDA_ERR_INVALID_ARG;
 
-  kda::PrefillArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.log_alpha = log_alpha;
-  a.beta = beta;
-  a.init = initial_state;
-  a.cu = cu_seqlens;
-  a.order = (num_seqs > 1) ? static_cast<int32_t*>(workspace) : nullptr;
-  a.o = o;
-  a.fin = final_state;
-  a.conv_q_w = f.conv_q_w;
-  a.conv_k_w = f.conv_k_w;
-  a.gate = f.gate;
-  a.norm_w = f.norm_w;
-  a.l2_eps = f.l2_eps;
-  a.rms_eps = f.rms_eps;
-  a.num_seqs = num_seqs;
-  a.num_heads = num_heads;
-  a.total_tokens = total_tokens;
-  a.units = num_seqs * num_heads;
-  a.bf16 = (dtype == KDA_DTYPE_BF16);
-  // Two value-column blocks per (sequence, head); the epilogue normalises
-  // whole heads, so it keeps one.
-  a.col_split = f.gate ? 1 : 2;
+  const bool bf16 = dtype == KDA_DTYPE_BF16;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* order = num_seqs > 1 ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  int32_t* seq_first = reinterpret_cast<int32_t*>(ws + pl.off_first);
+  int32_t* seq_c0 = reinterpret_cast<int32_t*>(ws + pl.off_c0);
+  int32_t* seq_c1 = reinterpret_cast<int32_t*>(ws + pl.off_c1);
+  float* carry_buf = final_state ? final_state : reinterpret_cast<float*>(ws + pl.off_state);
+  void* factors = ws + pl.off_factors;
+  const bool segmented = pl.seg_chunks > 0;
+  if (num_seqs > 1 && !segmented) {
+    if (kda::launch_worklist(cu_seqlens, num_seqs, order, stream) != hipSuccess) return KDA_ERR_HIP;
+  }
 
-  if (pl.seg_len == 0) {
-    // Two-kernel schedule: per window, the window table, the factor blocks of
-    // every (chunk, head), then the state walk over them.
-    char* ws = static_cast<char*>(workspace);
-    int32_t* order = num_seqs > 1 ? reinterpret_cast<int32_t*>(ws) : nullptr;
-    int32_t* seq_first = reinterpret_cast<int32_t*>(ws + pl.off_first);
-    int32_t* seq_c0 = reinterpret_cast<int32_t*>(ws + pl.off_c0);
-    int32_t* seq_c1 = reinterpret_cast<int32_t*>(ws + pl.off_c1);
-    float* carry_buf = final_state ? final_state : reinterpret_cast<float*>(ws + pl.off_state);
-    void* factors = ws + pl.off_factors;
-    if (num_seqs > 1) {
-      if (kda::launch_worklist(cu_seqlens, num_seqs, order, stream) != hipSuccess) return KDA_ERR_HIP;
-    }
-    kda::PrepArgs pa;
-    std::memset(&pa, 0, sizeof(pa));
-    pa.q = q;
-    pa.k = k;
-    pa.v = v;
-    pa.log_alpha = log_alpha;
-    pa.beta = beta;
-    pa.cu = cu_seqlens;
-    pa.conv_q_w = f.conv_q_w;
-    pa.conv_k_w = f.conv_k_w;
-    pa.l2_eps = f.l2_eps;
-    pa.num_seqs = num_seqs;
-    pa.num_heads = num_heads;
-    pa.total_tokens = total_tokens;
-    pa.bf16 = a.bf16;
-    pa.seq_first = seq_first;
-    pa.seq_c0 = seq_c0;
-    pa.cap = (int)pl.slots;
-    pa.chunks_per_block = kPrepChunksPerBlock;
-    pa.factors = factors;
-    kda::CarryArgs ca;
-    std::memset(&ca, 0, sizeof(ca));
-    ca.factors = factors;
-    ca.cu = cu_seqlens;
-    ca.order = order;
-    ca.seq_first = seq_first;
-    ca.seq_c0 = seq_c0;
-    ca.seq_c1 = seq_c1;
-    ca.gate = f.gate;
-    ca.norm_w = f.norm_w;
-    ca.rms_eps = f.rms_eps;
-    ca.o = o;
-    ca.num_seqs = num_seqs;
-    ca.num_heads = num_heads;
-    ca.total_tokens = total_tokens;
+  kda::PrepArgs pa;
+  std::memset(&pa, 0, sizeof(pa));
+  pa.q = q;
+  pa.k = k;
+  pa.v = v;
+  pa.log_alpha = log_alpha;
+  pa.beta = beta;
+  pa.cu = cu_seqlens;
+  pa.conv_q_w = f.conv_q_w;
+  pa.conv_k_w = f.conv_k_w;
+  pa.l2_eps = f.l2_eps;
+  pa.num_seqs = num_seqs;
+  pa.num_heads = num_heads;
+  pa.total_tokens = total_tokens;
+  pa.bf16 = bf16;
+  pa.seq_first = seq_first;
+  pa.seq_c0 = seq_c0;
+  pa.cap = (int)pl.slots;
+  pa.chunks_per_block = kPrepChunksPerBlock;
+  pa.factors = factors;
+
+  kda::CarryArgs ca;
+  std::memset(&ca, 0, sizeof(ca));
+  ca.factors = factors;
+  ca.cu = cu_seqlens;
+  ca.order = segmented ? nullptr : order;
+  ca.seq_first = seq_first;
+  ca.seq_c0 = seq_c0;
+  ca.seq_c1 = seq_c1;
+  ca.gate = f.gate;
+  ca.norm_w = f.norm_w;
+  ca.rms_eps = f.rms_eps;
+  ca.o = o;
+  ca.num_seqs = num_seqs;
+  ca.num_heads = num_heads;
+  ca.total_tokens = total_tokens;
+  ca.bf16 = bf16;
+  // Two value-column blocks per work item; the epilogue normalises whole
+  // heads, so it keeps one.
+  ca.col_split = f.gate ? 1 : 2;
+
+  if (!segmented) {
+    // Per window: the window table, the factor blocks of every (chunk, head),
+    // then the state walk over them.
     ca.units = num_seqs * num_heads;
-    ca.col_split = a.col_split;
-    ca.bf16 = a.bf16;
     for (int w = 0; w < pl.nw; ++w) {
-      if (kda::launch_window_table(cu_seqlens, num_seqs, total_tokens, kda::chunk_len(a.bf16), pl.nw, w,
+      if (kda::launch_window_table(cu_seqlens, num_seqs, total_tokens, kda::chunk_len(bf16), pl.nw, w,
                                    (int)pl.slots, seq_first, seq_c0, seq_c1, stream) != hipSuccess)
         return KDA_ERR_HIP;
       if (kda::launch_prep(pa, stream) != hipSuccess) return KDA_ERR_HIP;
@@ -324,48 +313,46 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     return KDA_OK;
   }
 
-  // Segmented schedule: segment table, per-segment affine pairs, the scan over
-  // segments, then the outputs of every segment from its incoming state.
-  char* ws = static_cast<char*>(workspace);
-  int32_t* seq_first = reinterpret_cast<int32_t*>(ws);
+  // Segmented schedule, per window: the window table and the factor blocks as
+  // above; the window's segments; per segment the affine pair (B from a zero
+  // state, M from the identity with V = 0); the scan over each sequence's
+  // segments from the window's incoming state; then the outputs of every
+  // segment from its incoming state.
+  int32_t* seg_first = reinterpret_cast<int32_t*>(ws + pl.off_segfirst);
   int32_t* seg_count = reinterpret_cast<int32_t*>(ws + pl.off_count);
   int32_t* seg_list = reinterpret_cast<int32_t*>(ws + pl.off_list);
   float* pairs = reinterpret_cast<float*>(ws + pl.off_pairs);
-  if (kda::launch_segment_table(cu_seqlens, num_seqs, total_tokens, (int)pl.seg_len, (int)pl.cap, seq_first,
-                                seg_list, seg_count, stream) != hipSuccess)
-    return KDA_ERR_HIP;
-
-  a.order = nullptr;
-  a.seg_len = (int)pl.seg_len;
-  a.seg_list = seg_list;
-  a.seg_count = seg_count;
-  a.pairs = pairs;
-  a.units = (int)(pl.cap * num_heads);
-
-  kda::PrefillArgs a1 = a;  // pairs: B (value columns) and M (identity columns)
-  a1.mode = 1;
-  a1.col_split = 2;
-  a1.init = nullptr;
-  a1.fin = nullptr;
-  a1.gate = nullptr;
-  a1.norm_w = nullptr;
-  if (kda::launch_prefill(a1, stream) != hipSuccess) return KDA_ERR_HIP;
-
+  ca.units = (int)(pl.cap * num_heads);
+  ca.seg_list = seg_list;
+  ca.seg_count = seg_count;
+  ca.seg_chunks = (int)pl.seg_chunks;
+  ca.pairs = pairs;
+  kda::CarryArgs c1 = ca;
+  c1.pass = 1;
+  c1.col_split = 4;
+  c1.gate = nullptr;
+  c1.norm_w = nullptr;
+  kda::CarryArgs c2 = ca;
+  c2.pass = 2;
   kda::ScanArgs sc;
   sc.pairs = pairs;
-  sc.seq_first = seq_first;
-  sc.init = initial_state;
-  sc.fin = final_state;
+  sc.seq_first = seg_first;
   sc.num_seqs = num_seqs;
   sc.num_heads = num_heads;
-  if (kda::launch_scan(sc, stream) != hipSuccess) return KDA_ERR_HIP;
-
-  kda::PrefillArgs a2 = a;  // outputs
-  a2.mode = 2;
-  a2.col_split = f.gate ? 1 : 2;
-  a2.init = nullptr;
-  a2.fin = nullptr;
-  if (kda::launch_prefill(a2, stream) != hipSuccess) return KDA_ERR_HIP;
+  for (int w = 0; w < pl.nw; ++w) {
+    if (kda::launch_window_table(cu_seqlens, num_seqs, total_tokens, kda::chunk_len(bf16), pl.nw, w,
+                                 (int)pl.slots, seq_first, seq_c0, seq_c1, stream) != hipSuccess)
+      return KDA_ERR_HIP;
+    if (kda::launch_prep(pa, stream) != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_window_segments(seq_c0, seq_c1, num_seqs, (int)pl.seg_chunks, (int)pl.cap, seg_first, seg_list,
+                                    seg_count, stream) != hipSuccess)
+      return KDA_ERR_HIP;
+    if (kda::launch_carry(c1, stream) != hipSuccess) return KDA_ERR_HIP;
+    sc.init = (w == 0) ? initial_state : carry_buf;
+    sc.fin = (w == pl.nw - 1) ? final_state : carry_buf;
+    if (kda::launch_scan(sc, stream) != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_carry(c2, stream) != hipSuccess) return KDA_ERR_HIP;
+  }
   return KDA_OK;
 }
 

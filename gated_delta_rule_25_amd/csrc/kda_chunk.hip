@@ -29,6 +29,33 @@
 namespace kda {
 
 // ---------------------------------------------------------------------------
+// Varlen work list: sequence indices ordered longest first (ties by index),
+// so the longest chains start first.  One workgroup; O(N^2 / 1024) compares.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void worklist_kernel(const int32_t* __restrict__ cu, int N,
+                                                         int32_t* __restrict__ order, int sort) {
+  for (int i = threadIdx.x; i < N; i += blockDim.x) {
+    if (!sort) {
+      order[i] = i;
+      continue;
+    }
+    const int Li = cu[i + 1] - cu[i];
+    int rank = 0;
+    for (int m = 0; m < N; ++m) {
+      const int Lm = cu[m + 1] - cu[m];
+      rank += (Lm > Li) || (Lm == Li && m < i);
+    }
+    order[rank] = i;
+  }
+}
+
+hipError_t launch_worklist(const int32_t* cu, int num_seqs, int32_t* order, hipStream_t stream) {
+  const int sort = num_seqs <= 16384 ? 1 : 0;
+  hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, stream, cu, num_seqs, order, sort);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Window table: per sequence, its chunk range in window w and the first slot
 // of that range in the factor store (exclusive prefix sum), clamped to `cap`
 // slots so that inconsistent cu_seqlens cannot index past the store.
@@ -81,6 +108,61 @@ hipError_t launch_window_table(const int32_t* cu, int num_seqs, int64_t total_to
 }
 
 // ---------------------------------------------------------------------------
+// Segments of a window: sequence n's chunks [seq_c0[n], seq_c1[n]) cut into
+// runs of seg_chunks; one workgroup, sequences 1024 at a time with a
+// block-wide scan of the counts, entries clamped to cap.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void window_segments_kernel(const int32_t* __restrict__ seq_c0,
+                                                                const int32_t* __restrict__ seq_c1, int N,
+                                                                int seg_chunks, int cap,
+                                                                int32_t* __restrict__ seg_first,
+                                                                int32_t* __restrict__ seg_list,
+                                                                int32_t* __restrict__ seg_count) {
+  __shared__ int32_t part[1024];
+  const int tid = threadIdx.x;
+  int carry = 0;
+  for (int base = 0; base < N; base += 1024) {
+    const int n = base + tid;
+    int G = 0;
+    if (n < N) {
+      const int len = seq_c1[n] - seq_c0[n];
+      G = len > 0 ? (len + seg_chunks - 1) / seg_chunks : 0;
+    }
+    part[tid] = G;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int x = tid >= off ? part[tid - off] : 0;
+      __syncthreads();
+      part[tid] += x;
+      __syncthreads();
+    }
+    if (n < N) {
+      const int first = min(carry + part[tid] - G, cap);
+      const int cnt = min(G, cap - first);
+      seg_first[n] = first;
+      for (int j = 0; j < cnt; ++j) {
+        seg_list[2 * (first + j)] = n;
+        seg_list[2 * (first + j) + 1] = j;
+      }
+    }
+    carry = min(carry + part[1023], cap);
+    __syncthreads();  // part[] is rewritten by the next round
+  }
+  if (tid == 0) {
+    seg_first[N] = carry;
+    *seg_count = carry;
+  }
+}
+
+hipError_t launch_window_segments(const int32_t* seq_c0, const int32_t* seq_c1, int num_seqs, int seg_chunks,
+                                  int cap, int32_t* seg_first, int32_t* seg_list, int32_t* seg_count,
+                                  hipStream_t stream) {
+  hipLaunchKernelGGL(window_segments_kernel, dim3(1), dim3(1024), 0, stream, seq_c0, seq_c1, num_seqs, seg_chunks,
+                     cap, seg_first, seg_list, seg_count);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Carry kernel.
 // ---------------------------------------------------------------------------
 template <typename E, int C, int NWC>
@@ -115,7 +197,7 @@ __host__ __device__ constexpr int vmcnt_wait(int n) { return ((n >> 4) << 14) | 
 // store their outputs directly.  One barrier per chunk hands the slots over:
 // after barrier ci, slot ci % 3 holds chunk ci, and every wave is past chunk
 // ci - 1, so the loader may refill slot (ci + 2) % 3.
-template <typename E, int C, int DV, bool EPI, int CT>
+template <typename E, int C, int DV, bool EPI, int CT, int PASS>
 __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const CarryArgs p) {
   constexpr int NWC = DV / (16 * CT);  // compute waves; wave NWC is the loader
   using L = CarryLayout<E, C, NWC>;
@@ -125,6 +207,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
   constexpr int ES = (int)sizeof(E);
   static_assert(NWC * 16 * CT == DV, "column tiles must cover the block");
   static_assert(!EPI || DV == D, "the epilogue normalises whole heads");
+  static_assert(!EPI || PASS != 1, "the pairs pass writes no outputs");
   static_assert(KT >= 1 && NT <= 4, "unsupported tile shape");
   static_assert(L::BYTES <= 160 * 1024, "LDS budget exceeded");
   static_assert(L::PIECES <= 63, "copy exceeds the outstanding-load counter");
@@ -136,15 +219,37 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
   // XCD-aware decode of the work item: blocks b and b + 8 run on the same XCD,
   // so the column blocks of one (sequence, head) share that XCD's L2.
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int cb = slot % p.col_split;
+  const int cb_all = slot % p.col_split;
   const int u = (slot / p.col_split) * 8 + xcd;
   if (u >= p.units) return;
   const int H = p.num_heads;
   const int rnk = u / H, h = u % H;
-  const int n = p.order ? p.order[rnk] : rnk;
+  // work item: sequence n, chunks [c0, c0 + nch) of it, factor slots from slot0
+  int n, c0, nch, slot0;
+  if constexpr (PASS == 0) {
+    n = p.order ? p.order[rnk] : rnk;
+    c0 = p.seq_c0[n];
+    nch = p.seq_c1[n] - c0;
+    slot0 = p.seq_first[n];
+  } else {
+    if (rnk >= *p.seg_count) return;
+    n = p.seg_list[2 * rnk];
+    const int first = p.seq_c0[n] + p.seg_list[2 * rnk + 1] * p.seg_chunks;
+    c0 = first;
+    nch = max(0, min(p.seq_c1[n], first + p.seg_chunks) - first);
+    slot0 = p.seq_first[n] + (first - p.seq_c0[n]);
+  }
+  // pass 1: the second half of the blocks traces M (identity start, U' = 0)
+  const bool mpart = PASS == 1 && cb_all >= p.col_split / 2;
+  const int cb = PASS == 1 ? cb_all % (p.col_split / 2) : cb_all;
+  constexpr bool write_o = PASS != 1;
+  const size_t pair_base = ((size_t)rnk * H + h) * 2 * (size_t)(D * D);
+  const float* s_in = PASS == 0 ? (p.state_in ? p.state_in + ((size_t)n * H + h) * (size_t)(D * D) : nullptr)
+                    : PASS == 2 ? p.pairs + pair_base : nullptr;
+  float* s_out = PASS == 0 ? (p.state_out ? p.state_out + ((size_t)n * H + h) * (size_t)(D * D) : nullptr)
+               : PASS == 1 ? p.pairs + pair_base + (mpart ? (size_t)(D * D) : 0) : nullptr;
   const int64_t seq_bos = p.cu ? (int64_t)p.cu[n] : 0;
   const int64_t seq_eos = p.cu ? (int64_t)p.cu[n + 1] : p.total_tokens;
-  const int c0 = p.seq_c0[n], nch = p.seq_c1[n] - c0, slot0 = p.seq_first[n];
   const int64_t rs = (int64_t)H * D;
   const int64_t hoff = (int64_t)h * D;
   const char* fbase = static_cast<const char*>(p.factors);
@@ -187,9 +292,9 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
       for (int e = 0; e < 4; ++e) nw[c][e] = (EPI && p.norm_w) ? p.norm_w[col0 + 16 * c + 4 * g + e] : 1.f;
   }
 
-  // State slice: tile (c, rt8) holds rows 16 rt8 + 4g + i, column col0 + 16 c + l16.
+  // State slice: tile (c, rt8) holds rows 16 rt8 + 4g + i, column col0 + 16 c + l16
+  // (zero, the identity's columns for M, or the given state).
   f32x4 accS[CT][8];
-  const size_t sbase = ((size_t)n * H + h) * (size_t)(D * D);
   {
     const int l16 = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -197,9 +302,10 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
 #pragma unroll
       for (int rt8 = 0; rt8 < 8; ++rt8)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          accS[c][rt8][i] =
-              p.state_in ? p.state_in[sbase + (size_t)(16 * rt8 + 4 * g + i) * D + col0 + 16 * c + l16] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * rt8 + 4 * g + i, col = col0 + 16 * c + l16;
+          accS[c][rt8][i] = s_in ? s_in[(size_t)row * D + col] : (mpart && row == col) ? 1.f : 0.f;
+        }
   }
 
   // P fragments and this wave's U' tiles (accumulator order, I/O dtype) of
@@ -223,6 +329,13 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
   Frag<E> rP[F::NP];
   Raw rU[CT][NT];
   auto load_u = [&](int ci) {
+    if (mpart) {
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int a = 0; a < NT; ++a) rU[c][a] = Raw{};
+      return;
+    }
     const Rsrc rb = make_rsrc(block_of(ci), F::BYTES);
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
@@ -261,7 +374,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
   constexpr bool PF_P = !EPI;
   if (nch > 0) {
     load_u(0);
-    if (PF_P) load_p(0);
+    if (PF_P && write_o) load_p(0);
   }
 
   for (int ci = 0; ci < nch; ++ci) {
@@ -287,7 +400,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
       for (int a = 0; a < NT; ++a) accU[c][a] = raw_f32(rU[c][a]);
     __syncthreads();
     if (EPI) load_gate(t0, nv);
-    if (!PF_P) load_p(ci);
+    if (!PF_P && write_o) load_p(ci);
     if (ci + 1 < nch) load_u(ci + 1);
 
     // Four-wave single-tile blocks: each stage first issues all of its LDS
@@ -318,13 +431,15 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) accU[0][rt] = mma(accU[0][rt], fa[rt * 4 + ks], sf[0][ks]);
       // ---- S2: O = Qt S (+ P U below) ----
+      if constexpr (write_o) {
 #pragma unroll
-      for (int i = 0; i < 4 * NT; ++i) ld_frag(fa[i], sQt + i * FRE);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 4 * NT; ++i) ld_frag(fa[i], sQt + i * FRE);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int rt = 0; rt < NT; ++rt) accO[0][rt] = mma(accO[0][rt], fa[rt * 4 + ks], sf[0][ks]);
+          for (int rt = 0; rt < NT; ++rt) accO[0][rt] = mma(accO[0][rt], fa[rt * 4 + ks], sf[0][ks]);
+      }
     } else {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
@@ -335,35 +450,37 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
 #pragma unroll
           for (int c = 0; c < CT; ++c) accU[c][rt] = mma(accU[c][rt], fa, sf[c][ks]);
         }
+      if constexpr (write_o)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int rt = 0; rt < NT; ++rt) {
-          Frag<E> fa;
-          ld_frag(fa, sQt + (rt * 4 + ks) * FRE);
+          for (int rt = 0; rt < NT; ++rt) {
+            Frag<E> fa;
+            ld_frag(fa, sQt + (rt * 4 + ks) * FRE);
 #pragma unroll
-          for (int c = 0; c < CT; ++c) accO[c][rt] = mma(accO[c][rt], fa, sf[c][ks]);
-        }
+            for (int c = 0; c < CT; ++c) accO[c][rt] = mma(accO[c][rt], fa, sf[c][ks]);
+          }
     }
     Frag<E> uf[CT][KT];
 #pragma unroll
     for (int c = 0; c < CT; ++c)
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) frag_from_acc(uf[c][kt], accU[c][2 * kt], accU[c][2 * kt + 1]);
+    if constexpr (write_o)
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-      for (int rt = 0; rt < NT; ++rt)
-        if (kt <= rt / 2)
+        for (int rt = 0; rt < NT; ++rt)
+          if (kt <= rt / 2)
 #pragma unroll
-          for (int c = 0; c < CT; ++c) accO[c][rt] = mma(accO[c][rt], rP[F::p_frag(rt, kt)], uf[c][kt]);
-    if (PF_P && ci + 1 < nch) load_p(ci + 1);
+            for (int c = 0; c < CT; ++c) accO[c][rt] = mma(accO[c][rt], rP[F::p_frag(rt, kt)], uf[c][kt]);
+    if (PF_P && write_o && ci + 1 < nch) load_p(ci + 1);
 
     // outputs: each 16 x 16 tile transposed on the matrix cores to lane =
     // token, four consecutive columns, then (with the epilogue) the head-wise
     // RMSNorm over the 128 value columns and the sigmoid gate, and stored
     // straight to global memory
-    {
+    if constexpr (write_o) {
       Frag16<E> id;
       {
         f32x4 x;
@@ -459,7 +576,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
     }
   }
 
-  if (p.state_out) {
+  if (s_out) {
     const int l16 = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int c = 0; c < CT; ++c)
@@ -467,16 +584,16 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
       for (int rt8 = 0; rt8 < 8; ++rt8)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          p.state_out[sbase + (size_t)(16 * rt8 + 4 * g + i) * D + col0 + 16 * c + l16] = accS[c][rt8][i];
+          s_out[(size_t)(16 * rt8 + 4 * g + i) * D + col0 + 16 * c + l16] = accS[c][rt8][i];
   }
 }
 
-template <typename E, int C, int DV, bool EPI, int CT>
+template <typename E, int C, int DV, bool EPI, int CT, int PASS>
 static hipError_t launch_carry_t(const CarryArgs& a, hipStream_t stream) {
   constexpr int NWC = DV / (16 * CT);
   constexpr size_t lds = CarryLayout<E, C, NWC>::BYTES;
   static_assert(lds <= 160 * 1024, "LDS budget exceeded");
-  auto fn = carry_kernel<E, C, DV, EPI, CT>;
+  auto fn = carry_kernel<E, C, DV, EPI, CT, PASS>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -490,10 +607,19 @@ static hipError_t launch_carry_t(const CarryArgs& a, hipStream_t stream) {
 template <typename E, int C>
 static hipError_t launch_carry_dtype(const CarryArgs& a, hipStream_t stream) {
   // whole heads (the epilogue normalises over all 128 value columns) on four
-  // two-tile waves, else two 64-column blocks per head on four one-tile
-  // waves, the blocks sharing the factor reads through L2
-  if (a.gate) return a.col_split == 1 ? launch_carry_t<E, C, 128, true, 2>(a, stream) : hipErrorInvalidValue;
-  return a.col_split == 2 ? launch_carry_t<E, C, 64, false, 1>(a, stream) : hipErrorInvalidValue;
+  // two-tile waves, else 64-column blocks on four one-tile waves (two per
+  // work item, four in the pass that traces B and M), the blocks sharing the
+  // factor reads through L2
+  if (a.gate) {
+    if (a.col_split != 1) return hipErrorInvalidValue;
+    if (a.pass == 0) return launch_carry_t<E, C, 128, true, 2, 0>(a, stream);
+    if (a.pass == 2) return launch_carry_t<E, C, 128, true, 2, 2>(a, stream);
+    return hipErrorInvalidValue;
+  }
+  if (a.pass == 0 && a.col_split == 2) return launch_carry_t<E, C, 64, false, 1, 0>(a, stream);
+  if (a.pass == 1 && a.col_split == 4) return launch_carry_t<E, C, 64, false, 1, 1>(a, stream);
+  if (a.pass == 2 && a.col_split == 2) return launch_carry_t<E, C, 64, false, 1, 2>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_carry(const CarryArgs& a, hipStream_t stream) {

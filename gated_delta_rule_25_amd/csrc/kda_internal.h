@@ -19,43 +19,6 @@ struct DecodeArgs {
   bool bf16;
 };
 
-struct PrefillArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const float* log_alpha;
-  const float* beta;
-  const float* init;        // [N,H,128,128] or null
-  const int32_t* cu;        // [N+1] or null (one sequence of total_tokens)
-  int32_t* order;           // workspace: N sequence indices, longest first (null if N == 1)
-  void* o;
-  float* fin;               // [N,H,128,128] or null
-  const float* conv_q_w;    // [H*128,4] or null
-  const float* conv_k_w;    // [H*128,4] or null
-  const void* gate;         // [T,H,128] or null
-  const float* norm_w;      // [128] or null
-  float l2_eps;
-  float rms_eps;
-  int num_seqs;
-  int num_heads;
-  int64_t total_tokens;
-  int units;                // work items: num_seqs * num_heads, or segments * num_heads
-  int col_split;            // column blocks per work item (see mode)
-  bool bf16;
-  // Segmented form (in-device context parallelism).  mode 0: plain.  mode 1:
-  // per segment, column blocks [0, col_split/2) run the value columns from a
-  // zero state (B) and the rest run the identity with V = 0 (M); the final
-  // states go to `pairs` [seg][H][2][128][128] (B first, then M) and no
-  // outputs are written.  mode 2: per segment, start from `pairs` slot B
-  // (the scan overwrites B_j with the segment's incoming state) and write
-  // the outputs only.  mode 1 and 2 list their work in seg_list.
-  int mode;
-  int seg_len;              // tokens per segment (multiple of the chunk)
-  const int32_t* seg_list;  // [2 * max segments]: sequence, segment index
-  const int32_t* seg_count; // device: number of segments
-  float* pairs;
-};
-
 struct ScanArgs {
   float* pairs;             // [seg][H][2][128][128]: B_j (overwritten by S_in(j)), then M_j
   const int32_t* seq_first; // [N+1]: first segment of each sequence (exclusive prefix sum)
@@ -159,27 +122,42 @@ struct CarryArgs {
   int num_seqs;
   int num_heads;
   int64_t total_tokens;
-  int units;                 // num_seqs * num_heads
-  int col_split;             // 1 or 2 value-column blocks per (sequence, head)
+  int units;                 // num_seqs * num_heads, or (segments bound) * num_heads
+  int col_split;             // value-column blocks per work item (pass 1: B blocks then M blocks)
   bool bf16;
+  // Segmented form (in-device context parallelism) over the window's chunks.
+  // pass 0: one work item per (sequence, head), state_in -> state_out.
+  // pass 1: one per (segment, head): blocks [0, col_split/2) run the value
+  //   columns from a zero state (B), the others the identity with U' = 0 (M);
+  //   the end states go to pairs[seg][h][0 or 1], no outputs are written.
+  // pass 2: one per (segment, head): from pairs[seg][h][0] (which the scan
+  //   has overwritten with the segment's incoming state), outputs only.
+  int pass;
+  const int32_t* seg_list;   // [2 * segments]: sequence, segment index within the window's range
+  const int32_t* seg_count;  // device: number of segments
+  int seg_chunks;            // chunks per segment
+  float* pairs;              // [segments][H][2][128][128] fp32
 };
 
 // Window w of nw: sequence n of G_n chunks gets chunks
 // [min(w Q_n, G_n), min((w + 1) Q_n, G_n)) with Q_n = ceil(G_n / nw).
 hipError_t launch_window_table(const int32_t* cu, int num_seqs, int64_t total_tokens, int chunk, int nw, int w,
                                int cap, int32_t* seq_first, int32_t* seq_c0, int32_t* seq_c1, hipStream_t stream);
+// Segments of the window: sequence n's chunks [seq_c0[n], seq_c1[n]) in runs
+// of seg_chunks; seg_first [N+1] is the exclusive prefix sum of the counts and
+// seg_list lists (n, j); at most cap entries.
+hipError_t launch_window_segments(const int32_t* seq_c0, const int32_t* seq_c1, int num_seqs, int seg_chunks,
+                                  int cap, int32_t* seg_first, int32_t* seg_list, int32_t* seg_count,
+                                  hipStream_t stream);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
 hipError_t launch_carry(const CarryArgs& a, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // Longest-first ordering of the packed sequences (device-side, no host sync).
 hipError_t launch_worklist(const int32_t* cu, int num_seqs, int32_t* order, hipStream_t stream);
 // Segment table: per-sequence segment counts, their exclusive prefix sum
 // (seq_first, [N+1]), the (sequence, segment) list and the total count.
 // At most `cap` segments are listed.
-hipError_t launch_segment_table(const int32_t* cu, int num_seqs, int64_t total_tokens, int seg_len, int cap,
-                                int32_t* seq_first, int32_t* seg_list, int32_t* seg_count, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 
 }  // namespace kda

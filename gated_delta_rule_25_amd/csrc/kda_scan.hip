@@ -8,71 +8,18 @@
 // "Kimi K3 架构、训练与系统全景解析", section 7.1 (in-device context
 // parallelism), splits long sequences this way so that segments run in
 // parallel; the incoming states then follow from a sequential composition of
-// the pairs, and a last pass writes the outputs from them.
-//
-// This file holds the two small kernels of that form:
-//   segment_table_kernel  per-sequence segment counts, their exclusive prefix
-//                         sum and the (sequence, segment) work list;
-//   scan_kernel           one workgroup per (sequence, head) composes the
-//                         pairs in order: S_in(j) overwrites B_j in place and
-//                         the state after the last segment is the final state.
+// the pairs, and a last pass writes the outputs from them.  The pairs and the
+// outputs come from the carry kernel (passes 1 and 2, kda_chunk.hip); this
+// file holds the composition:
+//   scan_kernel  one workgroup per (sequence, head) composes the pairs in
+//                order: S_in(j) overwrites B_j in place and the state after
+//                the last segment is the final state.
 #include <hip/hip_runtime.h>
 
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
-
-// One workgroup of 1024 threads; sequences are taken 1024 at a time with a
-// block-wide inclusive scan of the segment counts.  Writes are clamped to
-// `cap` entries so that inconsistent cu_seqlens cannot write out of bounds.
-__global__ __launch_bounds__(1024) void segment_table_kernel(const int32_t* __restrict__ cu, int N,
-                                                              int64_t total_tokens, int seg_len, int cap,
-                                                              int32_t* __restrict__ seq_first,
-                                                              int32_t* __restrict__ seg_list,
-                                                              int32_t* __restrict__ seg_count) {
-  __shared__ int32_t part[1024];
-  const int tid = threadIdx.x;
-  int carry = 0;
-  for (int base = 0; base < N; base += 1024) {
-    const int n = base + tid;
-    int G = 0;
-    if (n < N) {
-      const int64_t L = cu ? (int64_t)cu[n + 1] - (int64_t)cu[n] : total_tokens;
-      G = L > 0 ? (int)((L + seg_len - 1) / seg_len) : 0;
-    }
-    part[tid] = G;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int x = tid >= off ? part[tid - off] : 0;
-      __syncthreads();
-      part[tid] += x;
-      __syncthreads();
-    }
-    if (n < N) {
-      const int first = min(carry + part[tid] - G, cap);
-      const int cnt = min(G, cap - first);
-      seq_first[n] = first;
-      for (int s = 0; s < cnt; ++s) {
-        seg_list[2 * (first + s)] = n;
-        seg_list[2 * (first + s) + 1] = s;
-      }
-    }
-    carry = min(carry + part[1023], cap);
-    __syncthreads();  // part[] is rewritten by the next round
-  }
-  if (tid == 0) {
-    seq_first[N] = carry;
-    *seg_count = carry;
-  }
-}
-
-hipError_t launch_segment_table(const int32_t* cu, int num_seqs, int64_t total_tokens, int seg_len, int cap,
-                                int32_t* seq_first, int32_t* seg_list, int32_t* seg_count, hipStream_t stream) {
-  hipLaunchKernelGGL(segment_table_kernel, dim3(1), dim3(1024), 0, stream, cu, num_seqs, total_tokens, seg_len,
-                     cap, seq_first, seg_list, seg_count);
-  return hipGetLastError();
-}
 
 // One workgroup (4 waves) per (sequence, head).  Wave w keeps state columns
 // 32w .. 32w+31 in the accumulator layout of the 16x16 fp32 MFMA tile (lane

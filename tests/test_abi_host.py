@@ -135,21 +135,39 @@ def opts_p(o):
     return ctypes.cast(ctypes.pointer(o), ctypes.c_void_p)
 
 
+FB_BF16 = 72192  # factor block of one (64-token chunk, head), bf16 I/O
+
+
+def a256(x):
+    return (x + 255) // 256 * 256
+
+
+def two_kernel_ws(N, T, H, seg_tokens=0, C=64, fb=FB_BF16):
+    """Workspace of one factor-store window (the layout kda_api.hip documents):
+    longest-first order (N > 1), window table, [segment table and affine
+    pairs], factor store of `slots` chunks."""
+    slots = T // C + N + N + 1
+    b = (a256(4 * N) if N > 1 else 0) + a256(4 * (N + 1)) + 2 * a256(4 * N)
+    if seg_tokens:
+        cap = slots // (seg_tokens // C) + N + 1
+        b += a256(4 * (N + 1)) + 256 + a256(8 * cap) + cap * H * 2 * 65536
+    return b + slots * H * fb
+
+
 def test_workspace_bytes_segmented(lib):
-    # forced segments of 64 tokens, N=1, T=1000, H=2: cap = 1000 // 64 + 1 = 16 segments;
-    # seq_first (256 B), seg_count (256 B), seg_list (256 B), then 16 * 2 * 2 * 128 * 128 fp32
+    # forced segments of 64 tokens, N=1, T=1000, H=2: 18 factor slots, at most 20 segments
     o = Opts(None, None, None, None, 1e-6, 1e-6, 64)
-    assert lib.kda_chunk_fwd_workspace_bytes(1, 1000, 2, 128, 128, BF16, opts_p(o)) == 768 + 16 * 2 * 2 * 65536
+    assert two_kernel_ws(1, 1000, 2, 64) == 768 + 768 + 20 * 2 * 2 * 65536 + 18 * 2 * FB_BF16
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 1000, 2, 128, 128, BF16, opts_p(o)) == two_kernel_ws(1, 1000, 2, 64)
     o.segment_tokens = 100                                     # not a multiple of 64
     assert lib.kda_chunk_fwd_workspace_bytes(1, 1000, 2, 128, 128, BF16, opts_p(o)) == 0
     o.segment_tokens = -1                                      # sequential schedule forced
-    seq8 = lib.kda_chunk_fwd_workspace_bytes(1, 8192, 8, 128, 128, BF16, opts_p(o))
-    assert seq8 > 0 and seq8 != 768 + 17 * 8 * 2 * 65536
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 8, 128, 128, BF16, opts_p(o)) == two_kernel_ws(1, 8192, 8)
     # automatic choice (256 compute units when no device is visible): H=8 leaves
-    # 16 of 256 workgroups busy, so 16 segments of 512 tokens; cap 17
+    # 16 of 256 workgroups busy, so 16 segments of 512 tokens
     o.segment_tokens = 0
-    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 8, 128, 128, BF16, opts_p(o)) == 768 + 17 * 8 * 2 * 65536
-    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 8, 128, 128, BF16, None) == 768 + 17 * 8 * 2 * 65536
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 8, 128, 128, BF16, opts_p(o)) == two_kernel_ws(1, 8192, 8, 512)
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 8, 128, 128, BF16, None) == two_kernel_ws(1, 8192, 8, 512)
     # H=96 fills the GPU: the two-kernel schedule, the same plan as when forced
     o.segment_tokens = -1
     assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, None) == \
