@@ -83,32 +83,44 @@ def time_events(fn, steps, stream):
     return [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
 
-def cpu_baseline(inp, max_seconds_hint=20.0):
-    """Time the fp64 oracle on a bounded sample of the same workload: the first
-    `nh` heads over all tokens, OpenMP over heads on the host cores."""
+def cpu_baseline(inp, budget_s=20.0):
+    """Time the fp64 oracle (OpenMP over heads on the host cores) on the same
+    workload: first on 2 x threads heads over all tokens; if the whole layer
+    then fits the time budget, on every head (no scaling), else on as many
+    heads as fit, scaled to the layer."""
     import numpy as np
     import oracle
 
     threads = oracle.max_threads()
     H, T = inp["H"], inp["T"]
-    nh = max(1, min(H, 2 * threads))
 
     def f64(t):
         return t.detach().float().cpu().double().numpy()
 
-    hs = slice(0, nh)
-    q, k, v = f64(inp["q"][:, hs]), f64(inp["k"][:, hs]), f64(inp["v"][:, hs])
-    la, b = f64(inp["log_alpha"][:, hs]), f64(inp["beta"][:, hs])
-    s0 = None if inp["initial_state"] is None else f64(inp["initial_state"][:, hs])
-    t0 = time.perf_counter()
-    oracle.chunk_fwd(q, k, v, la, b, initial_state=s0, threads=threads)
-    dt = time.perf_counter() - t0
-    # whole-layer rate: the sample covers nh of H heads for all T tokens
+    def run(nh):
+        hs = slice(0, nh)
+        q, k, v = f64(inp["q"][:, hs]), f64(inp["k"][:, hs]), f64(inp["v"][:, hs])
+        la, b = f64(inp["log_alpha"][:, hs]), f64(inp["beta"][:, hs])
+        s0 = None if inp["initial_state"] is None else f64(inp["initial_state"][:, hs])
+        t0 = time.perf_counter()
+        oracle.chunk_fwd(q, k, v, la, b, initial_state=s0, threads=threads)
+        return time.perf_counter() - t0
+
+    nh = max(1, min(H, 2 * threads))
+    dt = run(nh)
+    per_head = dt / nh
+    if nh < H:
+        full = per_head * H
+        nh2 = H if full <= budget_s else max(nh, min(H, int(budget_s / per_head) // threads * threads))
+        if nh2 > nh:
+            nh = nh2
+            dt = run(nh)
+    # layer rate: the sample covers nh of H heads for all T tokens
     rate = T * nh / H / dt
     used = min(threads, nh)
-    return {"value": rate, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": "fp64 oracle on %d of %d heads x %d tokens (%.1f s), scaled to the full %d-head layer"
-                      % (nh, H, T, dt, H)}
+    what = ("the whole layer, %d heads x %d tokens (%.1f s)" % (H, T, dt) if nh == H else
+            "%d of %d heads x %d tokens (%.1f s), scaled to the full %d-head layer" % (nh, H, T, dt, H))
+    return {"value": rate, "unit": "tokens/s", "cores": used, "kind": "oracle", "sample": "fp64 oracle on " + what}
 
 
 def time_prefill(kda, kda_inputs, wid, steps, warmup, dev, stream, inp=None, **call_kw):
