@@ -9,6 +9,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "kda.h"
@@ -87,11 +88,21 @@ int64_t choose_segment_tokens(int num_seqs, int64_t total_tokens, int num_heads,
 }
 
 // Factor store budget of the two-kernel schedule; longer inputs run in
-// several windows.
+// several windows.  The environment variable KDA_FACTOR_BUDGET_MIB (read at
+// every call) sets another budget in MiB.
 #ifndef KDA_FACTOR_BUDGET_MIB
 #define KDA_FACTOR_BUDGET_MIB 4096
 #endif
 constexpr size_t kFactorBudget = (size_t)KDA_FACTOR_BUDGET_MIB << 20;
+
+size_t factor_budget() {
+  if (const char* e = std::getenv("KDA_FACTOR_BUDGET_MIB")) {
+    char* end = nullptr;
+    const long long mib = std::strtoll(e, &end, 10);
+    if (end != e && *end == '\0' && mib > 0 && mib < (1LL << 24)) return (size_t)mib << 20;
+  }
+  return kFactorBudget;
+}
 
 // Workspace layout, each piece 256-byte aligned: the longest-first order [N]
 // (N > 1), the window table (seq_first [N+1], seq_c0 [N], seq_c1 [N]); for
@@ -122,7 +133,7 @@ Plan make_plan(int num_seqs, int64_t total_tokens, int num_heads, kda_dtype dtyp
   const size_t fb = kda::factor_block_bytes(bf);
   const int64_t chunks = total_tokens / C + num_seqs;
   const double total = (double)chunks * num_heads * fb;
-  pl.nw = (int)std::max<double>(1.0, std::ceil(total / (double)kFactorBudget));
+  pl.nw = (int)std::max<double>(1.0, std::ceil(total / (double)factor_budget()));
   pl.slots = chunks / pl.nw + num_seqs + 1;
   // segments are cut from each window's share of the tokens
   const int64_t seg = choose_segment_tokens(num_seqs, (total_tokens + pl.nw - 1) / pl.nw, num_heads, f, cus);

@@ -80,8 +80,9 @@ typedef enum {
  *       two thirds of the compute units idle); a positive multiple of 64
  *       forces the segmented form with segments of that many tokens (any
  *       other positive value is KDA_ERR_INVALID_ARG); a negative value
- *       disables it.  The segmented form needs a workspace of about
- *       (T_total / segment_tokens + N) * H * 128 KiB.  The segmented form
+ *       disables it.  The segmented form needs about
+ *       (T_total / segment_tokens + N) * H * 128 KiB of workspace on top of
+ *       the factor store (see kda_chunk_fwd_workspace_bytes).  It
  *       ("Kimi K3 架构…" section 7.1, in-device context parallelism) runs every
  *       segment from a zero state and, with V = 0, from the identity, which
  *       gives the affine pair (M_j, B_j) with S_out = M_j S_in + B_j; a scan
@@ -103,6 +104,11 @@ typedef struct {
  * Bytes of device workspace kda_chunk_fwd needs for these sizes and options
  * (host-side computation; it reads the current device's compute-unit count,
  * which the segmented form depends on).  Returns 0 for invalid sizes.
+ * Most of it is the factor store: a 70.5 KiB block per (64-token chunk, head)
+ * for bf16 I/O, 68.5 KiB per (32-token chunk, head) for fp32.  It is capped at
+ * 4 GiB; longer inputs run in several windows.  The environment variable
+ * KDA_FACTOR_BUDGET_MIB, read at every call, sets another cap in MiB; it
+ * must be the same for this query and the kda_chunk_fwd call it sizes.
  */
 size_t kda_chunk_fwd_workspace_bytes(int num_seqs, int64_t total_tokens, int num_heads, int d_k,
                                      int d_v, kda_dtype dtype, const kda_fused_opts* opts);

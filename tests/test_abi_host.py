@@ -82,6 +82,21 @@ def test_workspace_bytes(lib):
     assert lib.kda_chunk_fwd_workspace_bytes(0, 10, 2, 128, 128, BF16, None) == 0
 
 
+def test_workspace_factor_budget_env(lib, monkeypatch):
+    # KDA_FACTOR_BUDGET_MIB caps one window's factor store at run time:
+    # 129 chunk slots x 96 heads x 70.5 KiB fit 4 GiB; a 64 MiB cap needs 14
+    # windows of 129 // 14 + 2 = 11 slots; an unparsable or zero value keeps the default
+    one = lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, None)
+    assert one == two_kernel_ws(1, 8192, 96)
+    monkeypatch.setenv("KDA_FACTOR_BUDGET_MIB", "64")
+    capped = lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, None)
+    assert capped == 768 + 96 * 128 * 128 * 4 + 11 * 96 * FB_BF16  # + the state carried between windows
+    monkeypatch.setenv("KDA_FACTOR_BUDGET_MIB", "not a number")
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, None) == one
+    monkeypatch.setenv("KDA_FACTOR_BUDGET_MIB", "0")
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, None) == one
+
+
 # Fake, never-dereferenced device addresses for validation-only calls.
 BASE = 0x7F0000000000
 MB = 1 << 20

@@ -100,3 +100,39 @@ def test_automatic_segmentation_few_heads():
     eo, es = compare_prefill(inp, o, fs, heads=[0, 5])
     say("  err_o %.3e err_state %.3e" % (eo, es))
     assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
+
+
+WINDOW_CASES = [
+    # (name, H, lengths, dtype, s0_std, fused, segment_tokens): run with a 1 MiB
+    # factor-store budget, so every case spans several windows
+    ("bf16_T3000_windows_seg256", 3, [3000], "bf16", 0.3, False, 256),
+    ("bf16_varlen_windows_seg64", 2, [1000, 0, 2500, 70], "bf16", 0.3, False, 64),
+    ("bf16_fused_windows_seg128", 2, [900, 300], "bf16", 0.0, True, 128),
+    ("f32_T700_windows_seg64", 2, [700], "f32", 0.3, False, 64),
+    ("bf16_varlen_windows_sequential", 2, [2000, 333], "bf16", 0.3, False, -1),
+]
+
+
+@pytest.mark.parametrize("name,H,lengths,dtype,s0,fused,seg", WINDOW_CASES, ids=[c[0] for c in WINDOW_CASES])
+def test_windows_parity(name, H, lengths, dtype, s0, fused, seg, monkeypatch):
+    """Inputs longer than the factor-store budget run in windows; the state
+    crosses them through the final-state buffer (or the workspace), and in the
+    segmented form each window scans its own segments from that state."""
+    monkeypatch.setenv("KDA_FACTOR_BUDGET_MIB", "1")
+    say("case %s H=%d lengths=%s dtype=%s fused=%s segment_tokens=%d budget 1 MiB"
+        % (name, H, lengths, dtype, fused, seg))
+    inp = kda_inputs.make_prefill(H, lengths, dtype, s0, fused, DEV, seed=zlib.crc32(name.encode()) & 0xFFFF)
+    if fused:
+        inp["norm_w"] = 1.0 + 0.1 * torch.randn(128, device=DEV)
+    T = sum(lengths)
+    big = kda.chunk_fwd_workspace_bytes(len(lengths), T, H, kda_inputs.torch_dtype(dtype), gated=fused,
+                                        segment_tokens=seg)
+    monkeypatch.delenv("KDA_FACTOR_BUDGET_MIB")
+    one = kda.chunk_fwd_workspace_bytes(len(lengths), T, H, kda_inputs.torch_dtype(dtype), gated=fused,
+                                        segment_tokens=seg)
+    monkeypatch.setenv("KDA_FACTOR_BUDGET_MIB", "1")
+    assert big < one, (big, one)  # several windows: a smaller factor store
+    o, fs = run(inp, segment_tokens=seg)
+    eo, es = compare_prefill(inp, o, fs)
+    say("  err_o %.3e err_state %.3e" % (eo, es))
+    assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
