@@ -79,6 +79,23 @@ __device__ __forceinline__ float row_scan(float x) {
 // Piece pc = 2 s + h of a lane's channels: channels 32 s + 16 h + 4 g + {0..3}.
 __device__ __forceinline__ int piece_ch(int pc, int g) { return 32 * (pc >> 1) + 16 * (pc & 1) + 4 * g; }
 
+// bf16 rows are read 16 bytes per lane: for 32-channel step st, lane group g
+// loads channels wide_ch(st, g) .. + 7, so that the four groups of a token
+// read its 64 contiguous bytes.  Group g then holds (in dwords 0-1 | 2-3)
+//   g = 0: pieces (2 st, g 0) | (2 st, g 1)    g = 1: (2 st + 1, g 0) | (2 st + 1, g 1)
+//   g = 2: pieces (2 st, g 2) | (2 st, g 3)    g = 3: (2 st + 1, g 2) | (2 st + 1, g 3)
+// and one row swap (v_permlane16_swap: the odd rows of the first operand
+// trade places with the even rows of the second, lane j with lane 16 + j)
+// per dword leaves every group with its own pieces 2 st | 2 st + 1.
+__device__ __forceinline__ int wide_ch(int st, int g) { return 32 * st + 16 * (g & 1) + 8 * (g >> 1); }
+__device__ __forceinline__ u32x4 ld_wide(const __bf16* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void unpack_wide(Raw4<__bf16>& lo, Raw4<__bf16>& hi, u32x4 w) {
+  const auto a = __builtin_amdgcn_permlane16_swap(w[0], w[2], false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(w[1], w[3], false, false);
+  lo.v = __builtin_bit_cast(bf16x4, (u32x2){a[0], b[0]});
+  hi.v = __builtin_bit_cast(bf16x4, (u32x2){a[1], b[1]});
+}
+
 // Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.
 template <int B, int E, typename Fn>
 __device__ __forceinline__ void static_for(Fn&& f) {
@@ -324,20 +341,35 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
     bos = sRng[3 * j + 1];
     nv = (int)sRng[3 * j + 2];
   };
+  constexpr bool WIDE = sizeof(E) == 2;  // bf16 rows: 16-byte loads, then a row swap
+  u32x4 wq[WIDE ? 4 : 1], wk[WIDE ? 4 : 1], wv[WIDE ? 4 : 1];
   auto issue_loads = [&](int64_t t0, int nv) {
     const int64_t row = t0 + min(tok, nv - 1);
     const int64_t base = row * rs + hoff;
 #pragma unroll
-    for (int pc = 0; pc < 8; ++pc) {
-      ld_raw4(rla[pc], p.log_alpha + base + piece_ch(pc, g));
-      ld_raw4(rv[pc], gv + base + piece_ch(pc, g));
-      if constexpr (!PRO) {
-        ld_raw4(rq[pc], gq + base + piece_ch(pc, g));
-        ld_raw4(rk[pc], gk + base + piece_ch(pc, g));
+    for (int pc = 0; pc < 8; ++pc) ld_raw4(rla[pc], p.log_alpha + base + piece_ch(pc, g));
+    if constexpr (WIDE) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        wv[st] = ld_wide(gv + base + wide_ch(st, g));
+        if constexpr (!PRO) {
+          wq[st] = ld_wide(gq + base + wide_ch(st, g));
+          wk[st] = ld_wide(gk + base + wide_ch(st, g));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int pc = 0; pc < 8; ++pc) {
+        ld_raw4(rv[pc], gv + base + piece_ch(pc, g));
+        if constexpr (!PRO) {
+          ld_raw4(rq[pc], gq + base + piece_ch(pc, g));
+          ld_raw4(rk[pc], gk + base + piece_ch(pc, g));
+        }
       }
     }
     rbt = p.beta[row * H + h];
   };
+
   int64_t t0 = 0, seq_bos = 0;
   int nv = 0;
   slot_range(s_begin, t0, seq_bos, nv);
@@ -384,18 +416,42 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
         const bool has_halo = r >= 13 && tok - 16 >= lo;
         const int64_t halo_row = t0 + min(tok - 16, nv - 1);
         Raw4<E> oq[8], hq[8], ok[8], hk[8];
-        auto load_rows = [&](Raw4<E> (&own)[8], Raw4<E> (&halo)[8], const E* src) {
+        if constexpr (WIDE) {
+          u32x4 woq[4], whq[4], wok[4], whk[4];
 #pragma unroll
-          for (int pc = 0; pc < 8; ++pc) {
-            ld_raw4(own[pc], src + own_row * rs + hoff + piece_ch(pc, g));
-            halo[pc].v = 0;
+          for (int st = 0; st < 4; ++st) {
+            woq[st] = ld_wide(gq + own_row * rs + hoff + wide_ch(st, g));
+            wok[st] = ld_wide(gk + own_row * rs + hoff + wide_ch(st, g));
+            whq[st] = (u32x4){0u, 0u, 0u, 0u};
+            whk[st] = (u32x4){0u, 0u, 0u, 0u};
           }
           if (has_halo)
 #pragma unroll
-            for (int pc = 0; pc < 8; ++pc) ld_raw4(halo[pc], src + halo_row * rs + hoff + piece_ch(pc, g));
-        };
-        load_rows(oq, hq, gq);
-        load_rows(ok, hk, gk);
+            for (int st = 0; st < 4; ++st) {
+              whq[st] = ld_wide(gq + halo_row * rs + hoff + wide_ch(st, g));
+              whk[st] = ld_wide(gk + halo_row * rs + hoff + wide_ch(st, g));
+            }
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            unpack_wide(oq[2 * st], oq[2 * st + 1], woq[st]);
+            unpack_wide(hq[2 * st], hq[2 * st + 1], whq[st]);
+            unpack_wide(ok[2 * st], ok[2 * st + 1], wok[st]);
+            unpack_wide(hk[2 * st], hk[2 * st + 1], whk[st]);
+          }
+        } else {
+          auto load_rows = [&](Raw4<E> (&own)[8], Raw4<E> (&halo)[8], const E* src) {
+#pragma unroll
+            for (int pc = 0; pc < 8; ++pc) {
+              ld_raw4(own[pc], src + own_row * rs + hoff + piece_ch(pc, g));
+              halo[pc].v = 0;
+            }
+            if (has_halo)
+#pragma unroll
+              for (int pc = 0; pc < 8; ++pc) ld_raw4(halo[pc], src + halo_row * rs + hoff + piece_ch(pc, g));
+          };
+          load_rows(oq, hq, gq);
+          load_rows(ok, hk, gk);
+        }
         auto prologue = [&](QK (&y)[8], const Raw4<E> (&own)[8], const Raw4<E> (&halo)[8], const float (&wl)[8],
                             bool conv) {
           float ss = 0.f;
@@ -433,6 +489,7 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
     }
     const float bt = valid ? rbt : 0.f;
     if (!valid) {
+      // (a 16-byte row piece is swapped only between lanes of the same token)
 #pragma unroll
       for (int pc = 0; pc < 8; ++pc) {
         rq[pc].v = 0;
@@ -441,6 +498,13 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) dl[pc][i] = 0.f;
       }
+      if constexpr (WIDE)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          wq[st] = (u32x4){0u, 0u, 0u, 0u};
+          wk[st] = (u32x4){0u, 0u, 0u, 0u};
+          wv[st] = (u32x4){0u, 0u, 0u, 0u};
+        }
     }
 
     // ---- decay, in log2 units, relative to the start of this lane's tile ----
@@ -501,12 +565,23 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         float q8[8], k8[8], v8[8], ep[8], en[8], fac[8], x[8], y[8];
-        cvt_raw4(q8, rq[2 * st]);
-        cvt_raw4(q8 + 4, rq[2 * st + 1]);
-        cvt_raw4(k8, rk[2 * st]);
-        cvt_raw4(k8 + 4, rk[2 * st + 1]);
-        cvt_raw4(v8, rv[2 * st]);
-        cvt_raw4(v8 + 4, rv[2 * st + 1]);
+        // this step's pieces 2 st, 2 st + 1 (bf16 rows: row swap of the 16-byte loads)
+        auto pieces = [&](float (&x)[8], const auto (&rp)[8], const u32x4 (&wp)[WIDE ? 4 : 1], bool wide) {
+          if constexpr (WIDE) {
+            if (wide) {
+              Raw4<E> a, b;
+              unpack_wide(a, b, wp[st]);
+              cvt_raw4(x, a);
+              cvt_raw4(x + 4, b);
+              return;
+            }
+          }
+          cvt_raw4(x, rp[2 * st]);
+          cvt_raw4(x + 4, rp[2 * st + 1]);
+        };
+        pieces(q8, rq, wq, !PRO);
+        pieces(k8, rk, wk, !PRO);
+        pieces(v8, rv, wv, true);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float d = dl[2 * st + (e >> 2)][e & 3];
