@@ -23,7 +23,12 @@
 //                 ring two chunks ahead of the compute waves.
 // Long inputs are processed in windows (every sequence advances by the same
 // fraction of its chunks per window) so the factor store stays bounded; the
-// state crosses windows through the final-state buffer.
+// state crosses windows through the final-state buffer.  With too few
+// (sequence, head) chains to fill the GPU, the carry runs in two passes over
+// segments of each window instead (section 7.1's in-device context
+// parallelism): pass 1 traces each segment's affine pair from a zero state
+// and from the identity, scan_kernel (kda_scan.hip) composes the pairs into
+// incoming states, and pass 2 writes the outputs from them.
 #include "kda_chunk_util.h"
 
 namespace kda {

@@ -62,17 +62,6 @@ __device__ __forceinline__ void ld_frag(Frag<float>& f, const float* p) {
   f.hi = *reinterpret_cast<const f32x4*>(p + 4);
 }
 
-// d-permuted index set: p points at k0 + 4g; the second half is 16 further.
-__device__ __forceinline__ void ld_frag_perm(Frag<__bf16>& f, const __bf16* p) {
-  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
-  const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 16);
-  f.v = (bf16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-__device__ __forceinline__ void ld_frag_perm(Frag<float>& f, const float* p) {
-  f.lo = *reinterpret_cast<const f32x4*>(p);
-  f.hi = *reinterpret_cast<const f32x4*>(p + 16);
-}
-
 // d-permuted index set from two separate 4-element pieces (k0 + 4g and k0 + 16 + 4g).
 __device__ __forceinline__ void ld_frag_pair(Frag<__bf16>& f, const __bf16* lo, const __bf16* hi) {
   const bf16x4 a = *reinterpret_cast<const bf16x4*>(lo);
@@ -104,30 +93,6 @@ __device__ __forceinline__ void frag_from_f32(Frag<float>& f, const float* x) {
   f.hi = (f32x4){x[4], x[5], x[6], x[7]};
 }
 
-__device__ __forceinline__ void frag_unpack(const Frag<__bf16>& f, float* x) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) x[j] = (float)f.v[j];
-}
-__device__ __forceinline__ void frag_unpack(const Frag<float>& f, float* x) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    x[j] = f.lo[j];
-    x[j + 4] = f.hi[j];
-  }
-}
-
-__device__ __forceinline__ Frag<__bf16> frag_neg(Frag<__bf16> f) {
-  u32x4 bits = __builtin_bit_cast(u32x4, f.v);
-  bits ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-  f.v = __builtin_bit_cast(bf16x8, bits);
-  return f;
-}
-__device__ __forceinline__ Frag<float> frag_neg(Frag<float> f) {
-  f.lo = -f.lo;
-  f.hi = -f.hi;
-  return f;
-}
-
 // acc += A * B over one 32-deep contraction step.
 __device__ __forceinline__ f32x4 mma(f32x4 acc, const Frag<__bf16>& a, const Frag<__bf16>& b) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
@@ -145,29 +110,6 @@ __device__ __forceinline__ float sigmoidf_fast(float x) { return 1.0f / (1.0f + 
 // 2^x with the hardware exp unit (inputs here lie in [-128, 128]; results
 // below the normal range flush toward zero, which is the intended limit).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-}  // namespace kda
-
-namespace kda {
-
-// Store 8 consecutive operand values; p must be 16-byte aligned.
-__device__ __forceinline__ void st_frag(__bf16* p, const Frag<__bf16>& f) {
-  *reinterpret_cast<bf16x8*>(p) = f.v;
-}
-__device__ __forceinline__ void st_frag(float* p, const Frag<float>& f) {
-  *reinterpret_cast<f32x4*>(p) = f.lo;
-  *reinterpret_cast<f32x4*>(p + 4) = f.hi;
-}
-
-// x ~= hi + lo with both parts in bf16 (lo carries the next 8 significant bits).
-__device__ __forceinline__ void frag_split(Frag<__bf16>& hi, Frag<__bf16>& lo, const float* x) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const __bf16 h = (__bf16)x[j];
-    hi.v[j] = h;
-    lo.v[j] = (__bf16)(x[j] - (float)h);
-  }
-}
 
 }  // namespace kda
 
