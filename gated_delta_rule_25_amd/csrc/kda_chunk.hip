@@ -261,21 +261,24 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
   auto block_of = [&](int ci) { return fbase + ((size_t)(slot0 + ci) * H + h) * F::BYTES; };
 
   if (wv == NWC) {
-    // ---- loader wave ----
+    // ---- loader wave (the pairs pass forms no outputs and skips Qt) ----
+    constexpr uint32_t kSlotQ = L::Q, kSlotK = L::K, kBlockK = F::K;
+    constexpr int NPC = PASS == 1 ? L::PIECES - (int)((kSlotK - kSlotQ) / 1024) : L::PIECES;  // pieces per chunk
     auto copy_block = [&](int ci) {
       const char* blk = block_of(ci);
       unsigned char* dst = smem + (ci % L::NBUF) * L::SLOT;
-      constexpr uint32_t kSlotK = L::K, kBlockK = F::K;
 #pragma unroll
-      for (int j = 0; j < L::PIECES; ++j)
+      for (int j = 0; j < L::PIECES; ++j) {
+        if (PASS == 1 && j * 1024u >= kSlotQ && j * 1024u < kSlotK) continue;
         __builtin_amdgcn_global_load_lds(blk + (j * 1024u < kSlotK ? j * 1024u : kBlockK + (j * 1024u - kSlotK)) + lane * 16,
                                          (__attribute__((address_space(3))) void*)(dst + j * 1024), 16, 0, 0);
+      }
     };
     if (nch > 0) copy_block(0);
     if (nch > 1) copy_block(1);
     for (int ci = 0; ci < nch; ++ci) {
       // chunk ci's copy has landed; the one of chunk ci + 1 may be in flight
-      if (ci + 1 < nch) __builtin_amdgcn_s_waitcnt(vmcnt_wait(L::PIECES));
+      if (ci + 1 < nch) __builtin_amdgcn_s_waitcnt(vmcnt_wait(NPC));
       else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
       __syncthreads();
       if (ci + 2 < nch) copy_block(ci + 2);
