@@ -27,6 +27,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+MFMA_FP32_PEAK_TFLOPS = 157.3
 
 
 def prefill_algorithmic_bytes(T: int, H: int, N: int, es: int, fused: bool, with_state_in: bool,
@@ -41,6 +43,14 @@ def prefill_algorithmic_bytes(T: int, H: int, N: int, es: int, fused: bool, with
     if with_state_out:
         b += N * H * d * d * 4
     return b
+
+
+def prefill_algorithmic_flops(T: int, H: int, C: int) -> float:
+    """Flops of the chunked recurrence per layer, triangular-aware, per
+    token-head: 6 d^2 (W S, Qt S, Kb^T U) + 5 C d (the Gram tiles, T Kt, T V,
+    P U) + C^2 / 3 (the solve) + d^2 / C (the state decay)."""
+    d = 128
+    return T * H * (6 * d * d + 5 * C * d + C * C / 3 + d * d / C)
 
 
 def decode_algorithmic_bytes(N: int, H: int, es: int) -> int:
@@ -161,6 +171,12 @@ def time_prefill(kda, kda_inputs, wid, steps, warmup, dev, stream, inp=None, **c
     ms_avg = sum(per) / len(per)
     algo = prefill_algorithmic_bytes(T, H, N, es, w["fused"], inp["initial_state"] is not None, True)
     achieved = algo / (ms_avg * 1e-3) / 1e9
+    C = 64 if es == 2 else 32
+    flops = prefill_algorithmic_flops(T, H, C)
+    tflops = flops / (ms_avg * 1e-3) / 1e12
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if es == 2 else MFMA_FP32_PEAK_TFLOPS
+    # attainable = min(matrix peak, intensity x HBM peak): the roofline's own bound
+    attainable = min(mfma_peak, flops / algo * HBM_PEAK_GBPS / 1e3)
     del o, fs, ws
     return inp, {
         "tokens_per_s": T / (wall / steps),
@@ -173,6 +189,9 @@ def time_prefill(kda, kda_inputs, wid, steps, warmup, dev, stream, inp=None, **c
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic("kda_chunk_fwd", w["name"]),
                      "kernel": "kda_chunk_fwd = window_table_kernel + prep_kernel + carry_kernel",
                      "kernel_ms_avg": ms_avg, "algorithmic_bytes": algo},
+        "mfma": {"algorithmic_flops": flops, "chunk": C, "achieved_tflops": tflops, "peak_tflops": mfma_peak,
+                 "frac_of_peak": tflops / mfma_peak, "attainable_tflops": attainable,
+                 "frac_of_attainable": tflops / attainable},
     }
 
 
@@ -237,6 +256,7 @@ def main():
             "data": "synthetic",
             "config": tm["config"],
             "roofline": tm["roofline"],
+            "mfma": tm["mfma"],
         })
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(inp)
