@@ -326,10 +326,12 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
 
   // Inputs of one chunk for this lane's token: q and k (after the prologue
   // when it runs; in the input dtype otherwise), v, log_alpha, beta.  For
-  // plain bf16 inputs the next chunk's loads are issued as soon as the
-  // current chunk's operands are formed, so they overlap its Gram products
-  // and solve (the fp32 and prologue forms lack the registers for it).
+  // bf16 inputs the next chunk's loads are issued as soon as the current
+  // chunk's operands are formed, so they overlap its Gram products and solve:
+  // all of them for plain inputs, log_alpha and beta with the prologue (its
+  // raw rows would not fit the registers); fp32 inputs are loaded in place.
   constexpr bool PREFETCH = !PRO && sizeof(E) == 2;
+  constexpr bool PREFETCH_LA = sizeof(E) == 2;
   using QK = std::conditional_t<PRO, Raw4<float>, Raw4<E>>;
   QK rq[8], rk[8];
   Raw4<E> rv[8];
@@ -343,11 +345,16 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
   };
   constexpr bool WIDE = sizeof(E) == 2;  // bf16 rows: 16-byte loads, then a row swap
   u32x4 wq[WIDE ? 4 : 1], wk[WIDE ? 4 : 1], wv[WIDE ? 4 : 1];
-  auto issue_loads = [&](int64_t t0, int nv) {
+  auto issue_la = [&](int64_t t0, int nv) {
     const int64_t row = t0 + min(tok, nv - 1);
     const int64_t base = row * rs + hoff;
 #pragma unroll
     for (int pc = 0; pc < 8; ++pc) ld_raw4(rla[pc], p.log_alpha + base + piece_ch(pc, g));
+    rbt = p.beta[row * H + h];
+  };
+  auto issue_rows = [&](int64_t t0, int nv) {
+    const int64_t row = t0 + min(tok, nv - 1);
+    const int64_t base = row * rs + hoff;
     if constexpr (WIDE) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
@@ -367,13 +374,13 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
         }
       }
     }
-    rbt = p.beta[row * H + h];
   };
 
   int64_t t0 = 0, seq_bos = 0;
   int nv = 0;
   slot_range(s_begin, t0, seq_bos, nv);
-  if (PREFETCH) issue_loads(t0, nv);
+  if (PREFETCH_LA) issue_la(t0, nv);
+  if (PREFETCH) issue_rows(t0, nv);
   // Prologue taps: lane (r, g) keeps those of channels piece_ch(r / 2, g)
   // + 2 (r % 2) + {0, 1} (four each), the lanes of a 16-lane row together
   // holding the taps of every channel that row uses.
@@ -398,7 +405,8 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
     const int tok = 16 * w + r;
     const uint32_t lane_fr = (uint32_t)lane * 8 * ES;  // lane's entry in a fragment
     const bool valid = tok < nv;
-    if (!PREFETCH) issue_loads(t0, nv);
+    if (!PREFETCH_LA) issue_la(t0, nv);
+    if (!PREFETCH) issue_rows(t0, nv);
     const Rsrc fb = make_rsrc(static_cast<char*>(p.factors) + ((size_t)s * H + h) * F::BYTES, F::BYTES);
 
     float dl[8][4];
@@ -669,7 +677,8 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
     int nvn = 0;
     if (s + 1 < s_end) {
       slot_range(s + 1, t0n, bosn, nvn);
-      if (PREFETCH) issue_loads(t0n, nvn);
+      if (PREFETCH_LA) issue_la(t0n, nvn);
+      if (PREFETCH) issue_rows(t0n, nvn);
     }
     __syncthreads();
 
