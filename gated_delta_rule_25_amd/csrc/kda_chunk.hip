@@ -378,11 +378,9 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
       for (int rt = 0; rt < NT; ++rt)
         rG[c][rt] = buf_ld_raw(gr, (uint32_t)(((16 * rt + l16) * rs + hoff + col0 + 16 * c + 4 * g) * ES), 0);
   };
-  // Whole-head epilogue blocks keep P out of flight (register budget).
-  constexpr bool PF_P = !EPI;
   if (nch > 0) {
     load_u(0);
-    if (PF_P && write_o) load_p(0);
+    if (write_o) load_p(0);
   }
 
   for (int ci = 0; ci < nch; ++ci) {
@@ -408,7 +406,6 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
       for (int a = 0; a < NT; ++a) accU[c][a] = raw_f32(rU[c][a]);
     __syncthreads();
     if (EPI) load_gate(t0, nv);
-    if (!PF_P && write_o) load_p(ci);
     if (ci + 1 < nch) load_u(ci + 1);
 
     // Four-wave single-tile blocks: each stage first issues all of its LDS
@@ -482,7 +479,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
           if (kt <= rt / 2)
 #pragma unroll
             for (int c = 0; c < CT; ++c) accO[c][rt] = mma(accO[c][rt], rP[F::p_frag(rt, kt)], uf[c][kt]);
-    if (PF_P && write_o && ci + 1 < nch) load_p(ci + 1);
+    if (write_o && ci + 1 < nch) load_p(ci + 1);
 
     // outputs: each 16 x 16 tile transposed on the matrix cores to lane =
     // token, four consecutive columns, then (with the epilogue) the head-wise
