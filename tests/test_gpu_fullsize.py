@@ -5,10 +5,14 @@ oracle then recomputes sampled (sequence, head) slices from the same device
 bytes and every output of those slices is compared (metric and bars as in
 tests/kda_testlib.py).  Sizes:
   - one K3 layer, H=96, T=8192, bf16, S0 ~ 0.02 N(0,1)     (3 heads sampled)
+  - the same with log_alpha scaled into (-0.01, 0)          (2 heads sampled)
   - long context, H=96, T=131072                            (1 head sampled)
   - decode, N=256 x H=96, 64 in-place steps                 (16 (n,h) sampled)
   - varlen 64 sequences (log-uniform 1K..64K), fused prologue/epilogue
                                                             (4 (n,h) sampled)
+  - few heads, H=8, T=131072 (segmented schedule)           (1 head sampled; all
+                                                            heads vs the sequential schedule),
+    with the workload's decay and with a ~5000x slower one
 plus the small fp32 workload H=2, T=256 compared in full.
 """
 import sys
@@ -58,6 +62,22 @@ def test_one_layer_T8192_sampled_heads():
     torch.cuda.empty_cache()
 
 
+def test_one_layer_T8192_slow_decay_sampled_heads():
+    """The layer's shape with log_alpha scaled into (-0.01, 0): the carried
+    state spans all 128 chunks (with the workloads' decay a chunk forgets it)."""
+    say("workload 1 with slow decay: bf16 H=96 T=8192, heads 11, 80")
+    inp = kda_inputs.make_workload(1, device=DEV)
+    inp["log_alpha"].mul_(0.002)
+    sync()
+    o, fs = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], **library_inputs(inp))
+    sync()
+    eo, es = compare_prefill(inp, o, fs, heads=[11, 80])
+    say("  err_o %.3e err_state %.3e" % (eo, es))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    del inp, o, fs
+    torch.cuda.empty_cache()
+
+
 def test_long_context_T131072_sampled_head():
     say("workload 2: bf16 H=96 T=131072, head 61")
     inp, o, fs = run_workload(2)
@@ -65,6 +85,56 @@ def test_long_context_T131072_sampled_head():
     say("  err_o %.3e err_state %.3e" % (eo, es))
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
     del inp, o, fs
+    torch.cuda.empty_cache()
+
+
+def test_few_heads_T131072_segmented_sampled():
+    """H=8, T=131072: the library picks the segmented schedule (16 segments
+    per head); one head against the oracle, every head against the same call
+    forced onto the sequential schedule.  With this decay (log_alpha =
+    -5 sigmoid(N(0,1))) a segment's transition M_j underflows to zero, so the
+    two schedules agree to the bit; the slow-decay test below covers M_j != 0."""
+    say("workload 5: bf16 H=8 T=131072 (segmented), head 3; all heads vs sequential")
+    inp = kda_inputs.make_workload(5, device=DEV)
+    sync()
+    kw = library_inputs(inp)
+    o, fs = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], **kw)
+    o_seq, fs_seq = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], segment_tokens=-1,
+                                  **kw)
+    sync()
+    eo, es = compare_prefill(inp, o, fs, heads=[3])
+    worst = 0.0
+    for h in range(inp["H"]):
+        worst = max(worst, slice_err(to64(o[:, h]), to64(o_seq[:, h])), slice_err(to64(fs[0, h]), to64(fs_seq[0, h])))
+    say("  err_o %.3e err_state %.3e | segmented vs sequential worst %.3e" % (eo, es, worst))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"] and worst <= TOL["bf16"]
+    del inp, o, fs, o_seq, fs_seq
+    torch.cuda.empty_cache()
+
+
+def test_few_heads_T131072_segmented_slow_decay():
+    """As above with log_alpha scaled into (-0.001, 0): a segment of 8192
+    tokens then decays by about e^-4 instead of underflowing, so every
+    segment's incoming state comes from the scan over the pairs (M_j, B_j).
+    (With the workload's own decay M_j is exactly zero in fp32 and both
+    schedules give the same bits.)"""
+    say("workload 5 with slow decay: bf16 H=8 T=131072 (segmented), head 6; all heads vs sequential")
+    inp = kda_inputs.make_workload(5, device=DEV)
+    inp["log_alpha"].mul_(0.0002)
+    sync()
+    kw = library_inputs(inp)
+    o, fs = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], **kw)
+    o_seq, fs_seq = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], segment_tokens=-1,
+                                  **kw)
+    sync()
+    eo, es = compare_prefill(inp, o, fs, heads=[6])
+    worst = 0.0
+    for h in range(inp["H"]):
+        worst = max(worst, slice_err(to64(o[:, h]), to64(o_seq[:, h])), slice_err(to64(fs[0, h]), to64(fs_seq[0, h])))
+    say("  err_o %.3e err_state %.3e | segmented vs sequential worst %.3e" % (eo, es, worst))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"] and worst <= TOL["bf16"]
+    assert worst > 0.0  # the schedules really differ here
+    del inp, o, fs, o_seq, fs_seq
     torch.cuda.empty_cache()
 
 
