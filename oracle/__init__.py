@@ -10,8 +10,9 @@ time); this module only builds it with gcc, loads it with ctypes and
 marshals numpy arrays.  See that file's header for what is computed and the
 passages of the pages it follows.
 
-Pins (tests/test_oracle_pins.py) tie it to the pages' worked examples,
-closed forms and brute-force products.  The prologue/epilogue epsilon values
+Pins (tests/test_oracle_pins.py, tests/test_oracle_replay_pins.py) tie it
+to the pages' worked examples, closed forms, brute-force products and, for
+the multi-token decode, to the prefill run over the same tokens.  The prologue/epilogue epsilon values
 and the convolution tap order are fixed only by our own reading of the pages
 (they print no numbers for them): parity unpinned for those constants.
 """
@@ -53,6 +54,11 @@ def _load():
         lib.kda_oracle_decode_step.restype = ctypes.c_int
         lib.kda_oracle_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int, ctypes.c_int, dp, ctypes.c_int]
+        lib.kda_oracle_decode_multi.restype = ctypes.c_int
+        lib.kda_oracle_decode_multi.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.POINTER(ctypes.c_int64),
+                                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, dp, dp, dp, dp, dp, dp, ctypes.c_double,
+                                                ctypes.c_double, dp, dp, dp, dp, ctypes.c_int]
         lib.kda_oracle_max_threads.restype = ctypes.c_int
         lib.kda_oracle_max_threads.argtypes = []
         _lib = lib
@@ -135,3 +141,55 @@ def decode_step(state, q, k, v, log_alpha, beta, threads=0):
     if rc != 0:
         raise RuntimeError("kda_oracle_decode_step failed with code %d" % rc)
     return o
+
+
+def decode_multi(state, q, k, v, log_alpha, beta, num_tokens=None, *, conv_q_w=None, conv_k_w=None,
+                 conv_q_hist=None, conv_k_hist=None, gate=None, norm_w=None, l2_eps=1e-6, rms_eps=1e-6,
+                 threads=0):
+    """Multi-token decode (speculative-decoding replay) from cached inputs.
+
+    state: [N, H, dk, dv] or None (zeros); q, k, log_alpha: [N, L, H, dk];
+    v (and gate): [N, L, H, dv]; beta: [N, L, H]; num_tokens: [N] tokens to
+    run per sequence (clamped to [0, L]) or None (all L); conv_*_hist:
+    [N, 3, H, dk] raw rows before token 0, oldest first, or None (zeros).
+    Returns (o [N, L, H, dv] with zero rows past each sequence's count,
+    state after the tokens [N, H, dk, dv], q history and k history after
+    them [N, 3, H, dk]).
+    """
+    lib = _load()
+    q, k, v, la, b = _f64(q), _f64(k), _f64(v), _f64(log_alpha), _f64(beta)
+    N, L, H, dk = q.shape
+    dv = v.shape[3]
+    assert k.shape == (N, L, H, dk) and la.shape == (N, L, H, dk) and v.shape == (N, L, H, dv)
+    assert b.shape == (N, L, H)
+    s0 = _f64(state)
+    if s0 is not None:
+        assert s0.shape == (N, H, dk, dv)
+    nt = None
+    if num_tokens is not None:
+        nt = np.ascontiguousarray(np.asarray(num_tokens, dtype=np.int64))
+        assert nt.shape == (N,)
+    cq, ck, hq, hk = _f64(conv_q_w), _f64(conv_k_w), _f64(conv_q_hist), _f64(conv_k_hist)
+    g, nw = _f64(gate), _f64(norm_w)
+    for w_ in (cq, ck):
+        if w_ is not None:
+            assert w_.shape == (H * dk, 4)
+    for h_ in (hq, hk):
+        if h_ is not None:
+            assert h_.shape == (N, 3, H, dk)
+    if g is not None:
+        assert g.shape == (N, L, H, dv)
+    if nw is not None:
+        assert nw.shape == (dv,)
+    o = np.zeros((N, L, H, dv), dtype=np.float64)
+    s1 = np.zeros((N, H, dk, dv), dtype=np.float64)
+    oq = np.zeros((N, 3, H, dk), dtype=np.float64)
+    ok = np.zeros((N, 3, H, dk), dtype=np.float64)
+    nt_p = None if nt is None else nt.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    rc = lib.kda_oracle_decode_multi(_ptr(s0), _ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(b), nt_p, N, L, H,
+                                     dk, dv, _ptr(cq), _ptr(ck), _ptr(hq), _ptr(hk), _ptr(g), _ptr(nw),
+                                     float(l2_eps), float(rms_eps), _ptr(o), _ptr(s1), _ptr(oq), _ptr(ok),
+                                     int(threads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_decode_multi failed with code %d" % rc)
+    return o, s1, oq, ok

@@ -62,16 +62,15 @@ static void kda_token(double* S, int dk, int dv, const double* q, const double* 
     for (int j = 0; j < dv; ++j) o[j] += S[(size_t)i * dv + j] * q[i];
 }
 
-/* ShortConv(4) + SiLU + L2 for token t (absolute index) of a sequence starting at bos. */
-static void prologue(const double* x, const double* w, int64_t bos, int64_t t, int H, int h, int d,
-                     double eps, double* out) {
+/* ShortConv(4) + SiLU + L2 of one token: rows[m] is the raw row x_{t-3+m}
+ * (NULL before the sequence start, i.e. zero), w the head's taps [d][4]. */
+static void conv_silu_l2(const double* const rows[4], const double* w, int d, double eps, double* out) {
   double ss = 0.0;
   for (int j = 0; j < d; ++j) {
     double c = 0.0;
     for (int m = 0; m < 4; ++m) {
-      const int64_t src = t - 3 + m;
-      if (src < bos) continue;
-      c += w[((size_t)h * d + j) * 4 + m] * x[((size_t)src * H + h) * d + j];
+      if (!rows[m]) continue;
+      c += w[(size_t)j * 4 + m] * rows[m][j];
     }
     const double s = c / (1.0 + exp(-c));
     out[j] = s;
@@ -79,6 +78,17 @@ static void prologue(const double* x, const double* w, int64_t bos, int64_t t, i
   }
   const double inv = 1.0 / sqrt(ss + eps);
   for (int j = 0; j < d; ++j) out[j] *= inv;
+}
+
+/* The prologue for token t (absolute index) of a packed sequence starting at bos. */
+static void prologue(const double* x, const double* w, int64_t bos, int64_t t, int H, int h, int d,
+                     double eps, double* out) {
+  const double* rows[4];
+  for (int m = 0; m < 4; ++m) {
+    const int64_t src = t - 3 + m;
+    rows[m] = src < bos ? NULL : x + ((size_t)src * H + h) * d;
+  }
+  conv_silu_l2(rows, w + (size_t)h * d * 4, d, eps, out);
 }
 
 static void epilogue(double* o, const double* gate, const double* norm_w, int dv, double eps) {
@@ -165,6 +175,96 @@ int kda_oracle_decode_step(double* state, const double* q, const double* k, cons
     kda_token(state + (size_t)u * dk * dv, dk, dv, q + (size_t)u * dk, k + (size_t)u * dk,
               v + (size_t)u * dv, log_alpha + (size_t)u * dk, beta[u], tmp, o + (size_t)u * dv);
     free(tmp);
+  }
+  return err;
+}
+
+/* Multi-token decode from cached per-token inputs: the replay of accepted
+ * draft tokens in speculative decoding ("Kimi K3 架构、训练与系统全景解析",
+ * section 7.4, KDA state replay under speculative decoding: keep the small
+ * per-token inputs instead of one state per draft position, replay the
+ * accepted prefix from the verified state, write back only the final state;
+ * the short convolution, the norms, the gate and the recurrence run together).
+ *
+ * For each (n, h): from state_in (zeros if NULL), the token body above over
+ * tokens 0 .. nt-1 of sequence n's L cached tokens, nt = ntok[n] clamped to
+ * [0, L] (L when ntok is NULL).  The prologue's convolution of token t reads
+ * raw rows t-3 .. t; rows before token 0 come from the history [N, 3, H, dk]
+ * (oldest first; a NULL history is zeros, as at a sequence start).
+ * Layouts: q, k, log_alpha [N, L, H, dk]; v, gate, o [N, L, H, dv];
+ * beta [N, L, H]; states [N, H, dk, dv].  Writes o for the tokens run (the
+ * other rows are not touched), the state after them (state_out, if given) and
+ * the raw rows just before token nt (conv_*_out, if given: the history the
+ * next call continues from). */
+static const double* raw_row(const double* x, const double* hist, int n, int L, int H, int h, int d, int pos) {
+  if (pos >= 0) return x + (((size_t)n * L + pos) * H + h) * d;
+  if (!hist) return NULL;
+  return hist + (((size_t)n * 3 + (3 + pos)) * H + h) * d;
+}
+
+int kda_oracle_decode_multi(const double* state_in, const double* q, const double* k, const double* v,
+                            const double* log_alpha, const double* beta, const int64_t* ntok, int num_seqs,
+                            int L, int H, int dk, int dv, const double* conv_q_w, const double* conv_k_w,
+                            const double* conv_q_hist, const double* conv_k_hist, const double* gate,
+                            const double* norm_w, double l2_eps, double rms_eps, double* o, double* state_out,
+                            double* conv_q_out, double* conv_k_out, int num_threads) {
+  if (num_seqs < 1 || L < 1 || H < 1 || dk < 1 || dv < 1) return 1;
+  const int64_t units = (int64_t)num_seqs * H;
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#else
+  (void)num_threads;
+#endif
+  int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < units; ++u) {
+    const int n = (int)(u / H), h = (int)(u % H);
+    int nt = L;
+    if (ntok) nt = ntok[n] < 0 ? 0 : (ntok[n] > L ? L : (int)ntok[n]);
+    double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+    double* tmp = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* qb = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* kb = (double*)malloc(sizeof(double) * (size_t)dk);
+    if (!S || !tmp || !qb || !kb) {
+#pragma omp atomic write
+      err = 2;
+      free(S); free(tmp); free(qb); free(kb);
+      continue;
+    }
+    const size_t soff = (size_t)u * dk * dv;
+    if (state_in)
+      memcpy(S, state_in + soff, sizeof(double) * (size_t)dk * dv);
+    else
+      memset(S, 0, sizeof(double) * (size_t)dk * dv);
+    for (int t = 0; t < nt; ++t) {
+      const size_t tk = (((size_t)n * L + t) * H + h) * dk, tv = (((size_t)n * L + t) * H + h) * dv;
+      const double* qt = q + tk;
+      const double* kt = k + tk;
+      const double* rows[4];
+      if (conv_q_w) {
+        for (int m = 0; m < 4; ++m) rows[m] = raw_row(q, conv_q_hist, n, L, H, h, dk, t - 3 + m);
+        conv_silu_l2(rows, conv_q_w + (size_t)h * dk * 4, dk, l2_eps, qb);
+        qt = qb;
+      }
+      if (conv_k_w) {
+        for (int m = 0; m < 4; ++m) rows[m] = raw_row(k, conv_k_hist, n, L, H, h, dk, t - 3 + m);
+        conv_silu_l2(rows, conv_k_w + (size_t)h * dk * 4, dk, l2_eps, kb);
+        kt = kb;
+      }
+      kda_token(S, dk, dv, qt, kt, v + tv, log_alpha + tk, beta[((size_t)n * L + t) * H + h], tmp, o + tv);
+      if (gate) epilogue(o + tv, gate + tv, norm_w, dv, rms_eps);
+    }
+    if (state_out) memcpy(state_out + soff, S, sizeof(double) * (size_t)dk * dv);
+    for (int r = 0; r < 3; ++r) {
+      const size_t hoff = (((size_t)n * 3 + r) * H + h) * dk;
+      const double* sq = raw_row(q, conv_q_hist, n, L, H, h, dk, nt - 3 + r);
+      const double* sk = raw_row(k, conv_k_hist, n, L, H, h, dk, nt - 3 + r);
+      for (int j = 0; j < dk; ++j) {
+        if (conv_q_out) conv_q_out[hoff + j] = sq ? sq[j] : 0.0;
+        if (conv_k_out) conv_k_out[hoff + j] = sk ? sk[j] : 0.0;
+      }
+    }
+    free(S); free(tmp); free(qb); free(kb);
   }
   return err;
 }
