@@ -9,6 +9,7 @@ library is not built this module raises on first use.
 
     o, final_state = chunk_fwd(q, k, v, log_alpha, beta, initial_state, cu_seqlens)
     o = decode_step(state, q, k, v, log_alpha, beta)      # state updated in place
+    o, state_out = decode_replay(state, q, k, v, log_alpha, beta, num_tokens, state_out=state)
 """
 from __future__ import annotations
 
@@ -18,10 +19,11 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "decode_step", "chunk_fwd_workspace_bytes", "status_string", "KDAError",
-           "library_path", "D"]
+__all__ = ["chunk_fwd", "decode_step", "decode_replay", "chunk_fwd_workspace_bytes", "status_string", "KDAError",
+           "library_path", "D", "REPLAY_MAX_TOKENS"]
 
 D = 128
+REPLAY_MAX_TOKENS = 16
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda.so")
 _lib = None
@@ -64,6 +66,9 @@ def _load():
                                   sz, vp]
     lib.kda_decode_step.restype = i32
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    lib.kda_decode_replay.restype = i32
+    lib.kda_decode_replay.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp,
+                                      vp, vp]
     _lib = lib
     return lib
 
@@ -211,3 +216,73 @@ def decode_step(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.
     if rc != KDA_OK:
         raise KDAError(rc, "kda_decode_step")
     return out
+
+
+def decode_replay(state_in: Optional[torch.Tensor], q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  log_alpha: torch.Tensor, beta: torch.Tensor, num_tokens: Optional[torch.Tensor] = None, *,
+                  state_out=None, conv_q_w: Optional[torch.Tensor] = None,
+                  conv_k_w: Optional[torch.Tensor] = None, conv_q_state: Optional[torch.Tensor] = None,
+                  conv_k_state: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
+                  norm_w: Optional[torch.Tensor] = None, l2_eps: float = 1e-6, rms_eps: float = 1e-6,
+                  out=None) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """Multi-token decode from cached token inputs (kda_decode_replay).
+
+    q, k, v: [N, L, H, 128] float32 or bfloat16 (L <= 16), log_alpha
+    [N, L, H, 128] float32, beta [N, L, H] float32; num_tokens int32 [N] on the
+    device (tokens to run per sequence, clamped to [0, L]) or None (all L).
+    state_in [N, H, 128, 128] float32 or None (zeros).  state_out: None (the
+    state is not written: a verification pass), a tensor (may be state_in
+    itself) or the string "new" to allocate one.  conv_*_state [N, 3, H, 128]
+    in the I/O dtype hold the raw rows before token 0 and are advanced in
+    place when state_out is given.  out: None allocates the outputs, False
+    skips them.  Returns (o or None, state_out or None).
+    """
+    lib = _load()
+    if q.dim() != 4 or q.shape[3] != D:
+        raise ValueError("q must be [N, L, H, 128]")
+    N, L, H, _ = q.shape
+    dev, dt = q.device, q.dtype
+    if dt not in _DTYPES:
+        raise TypeError("q/k/v must be float32 or bfloat16")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, (N, L, H, D), dt, dev)
+    _check(log_alpha, "log_alpha", (N, L, H, D), torch.float32, dev)
+    _check(beta, "beta", (N, L, H), torch.float32, dev)
+    if num_tokens is not None:
+        _check(num_tokens, "num_tokens", (N,), torch.int32, dev)
+    if state_in is not None:
+        _check(state_in, "state_in", (N, H, D, D), torch.float32, dev)
+    if isinstance(state_out, str):
+        if state_out != "new":
+            raise ValueError('state_out must be None, a tensor or "new"')
+        state_out = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    elif state_out is not None:
+        _check(state_out, "state_out", (N, H, D, D), torch.float32, dev)
+    for name, t in (("conv_q_w", conv_q_w), ("conv_k_w", conv_k_w)):
+        if t is not None:
+            _check(t, name, (H * D, 4), torch.float32, dev)
+    for name, t in (("conv_q_state", conv_q_state), ("conv_k_state", conv_k_state)):
+        if t is not None:
+            _check(t, name, (N, 3, H, D), dt, dev)
+    if gate is not None:
+        _check(gate, "gate", (N, L, H, D), dt, dev)
+    if norm_w is not None:
+        _check(norm_w, "norm_w", (D,), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, L, H, D), dtype=dt, device=dev)
+    elif out is False:
+        out = None
+    else:
+        _check(out, "out", (N, L, H, D), dt, dev)
+    opts = None
+    if any(x is not None for x in (conv_q_w, conv_k_w, gate, norm_w)):
+        opts = ctypes.byref(_FusedOpts(_ptr(conv_q_w), _ptr(conv_k_w), _ptr(gate), _ptr(norm_w), float(l2_eps),
+                                       float(rms_eps), 0))
+    rc = lib.kda_decode_replay(_ptr(state_in), _ptr(state_out), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                               _ptr(beta), _ptr(num_tokens), N, L, H, D, D, _DTYPES[dt], opts,
+                               _ptr(conv_q_state), _ptr(conv_k_state), _ptr(out), _stream(dev))
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_decode_replay")
+    return out, state_out

@@ -408,4 +408,83 @@ kda_status kda_decode_step(float* state, const void* q, const void* k, const voi
   return KDA_OK;
 }
 
+kda_status kda_decode_replay(const float* state_in, float* state_out, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta, const int32_t* num_tokens, int num_seqs,
+                             int max_tokens, int num_heads, int d_k, int d_v, kda_dtype dtype,
+                             const kda_fused_opts* opts, void* conv_q_state, void* conv_k_state, void* o,
+                             hipStream_t stream) {
+  if (num_seqs < 1 || num_heads < 1 || max_tokens < 1) return KDA_ERR_INVALID_ARG;
+  if (d_k != kD || d_v != kD || !dtype_ok(dtype) || max_tokens > kda::kReplayMaxTokens) return KDA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !log_alpha || !beta) return KDA_ERR_INVALID_ARG;
+  const kda_fused_opts& f = opts ? *opts : kNoOpts;
+  if (!(f.l2_eps >= 0.f) || !(f.rms_eps >= 0.f)) return KDA_ERR_INVALID_ARG;
+  if ((f.conv_q_w && !conv_q_state) || (f.conv_k_w && !conv_k_state)) return KDA_ERR_INVALID_ARG;
+  // a history without its convolution is neither read nor written
+  if (!f.conv_q_w) conv_q_state = nullptr;
+  if (!f.conv_k_w) conv_k_state = nullptr;
+  {
+    const void* vec[] = {state_in, state_out, q, k, v, log_alpha, f.gate, o, conv_q_state, conv_k_state};
+    for (const void* ptr : vec)
+      if (!aligned(ptr, 16)) return KDA_ERR_INVALID_ARG;
+    const void* sca[] = {beta, num_tokens, f.conv_q_w, f.conv_k_w, f.norm_w};
+    for (const void* ptr : sca)
+      if (!aligned(ptr, 4)) return KDA_ERR_INVALID_ARG;
+  }
+  const int64_t units = (int64_t)num_seqs * num_heads;
+  if (units > (int64_t)INT32_MAX || units * max_tokens > (int64_t)INT32_MAX) return KDA_ERR_INVALID_ARG;
+  if (!o && !state_out) return KDA_OK;  // nothing to produce
+
+  const size_t es = elem_size(dtype);
+  const size_t tok_elems = (size_t)units * max_tokens * kD;
+  const size_t state_bytes = (size_t)units * kD * kD * sizeof(float);
+  const size_t hist_bytes = (size_t)units * 3 * kD * es;
+  const Range r_s0 = range_of(state_in, state_bytes), r_s1 = range_of(state_out, state_bytes);
+  const Range r_q = range_of(q, tok_elems * es), r_k = range_of(k, tok_elems * es), r_v = range_of(v, tok_elems * es);
+  const Range r_la = range_of(log_alpha, tok_elems * sizeof(float));
+  const Range r_b = range_of(beta, (size_t)units * max_tokens * sizeof(float));
+  const Range r_nt = range_of(num_tokens, num_tokens ? (size_t)num_seqs * sizeof(int32_t) : 0);
+  const Range r_g = range_of(f.gate, f.gate ? tok_elems * es : 0);
+  const Range r_cq = range_of(f.conv_q_w, f.conv_q_w ? (size_t)num_heads * kD * 4 * sizeof(float) : 0);
+  const Range r_ck = range_of(f.conv_k_w, f.conv_k_w ? (size_t)num_heads * kD * 4 * sizeof(float) : 0);
+  const Range r_nw = range_of(f.norm_w, f.norm_w ? kD * sizeof(float) : 0);
+  const Range r_hq = range_of(conv_q_state, conv_q_state ? hist_bytes : 0);
+  const Range r_hk = range_of(conv_k_state, conv_k_state ? hist_bytes : 0);
+  const Range r_o = range_of(o, o ? tok_elems * es : 0);
+  const Range inputs[] = {r_s0, r_q, r_k, r_v, r_la, r_b, r_nt, r_g, r_cq, r_ck, r_nw};
+  for (const Range& in : inputs) {
+    if (overlap(r_o, in) || overlap(r_hq, in) || overlap(r_hk, in)) return KDA_ERR_INVALID_ARG;
+    const bool exact_alias = in.lo == r_s0.lo && in.hi == r_s0.hi && r_s1.lo == r_s0.lo && r_s1.hi == r_s0.hi;
+    if (overlap(r_s1, in) && !exact_alias) return KDA_ERR_INVALID_ARG;
+  }
+  if (overlap(r_o, r_s1) || overlap(r_o, r_hq) || overlap(r_o, r_hk) || overlap(r_s1, r_hq) ||
+      overlap(r_s1, r_hk) || overlap(r_hq, r_hk))
+    return KDA_ERR_INVALID_ARG;
+
+  kda::ReplayArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.state_in = state_in;
+  a.state_out = state_out;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_alpha = log_alpha;
+  a.beta = beta;
+  a.num_tokens = num_tokens;
+  a.conv_q_w = f.conv_q_w;
+  a.conv_k_w = f.conv_k_w;
+  a.conv_q_state = conv_q_state;
+  a.conv_k_state = conv_k_state;
+  a.gate = f.gate;
+  a.norm_w = f.norm_w;
+  a.l2_eps = f.l2_eps;
+  a.rms_eps = f.rms_eps;
+  a.o = o;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.max_tokens = max_tokens;
+  a.bf16 = (dtype == KDA_DTYPE_BF16);
+  if (kda::launch_replay(a, stream) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
 }  // extern "C"

@@ -19,6 +19,30 @@ struct DecodeArgs {
   bool bf16;
 };
 
+// Multi-token decode from cached token inputs (speculative-decoding replay).
+struct ReplayArgs {
+  const float* state_in;     // [N,H,128,128] or null (zeros)
+  float* state_out;          // [N,H,128,128] or null (not written); may equal state_in
+  const void* q;             // [N,L,H,128] (raw rows when the q convolution runs)
+  const void* k;
+  const void* v;
+  const float* log_alpha;    // [N,L,H,128]
+  const float* beta;         // [N,L,H]
+  const int32_t* num_tokens; // [N] tokens to run, clamped to [0, L]; null = L
+  const float* conv_q_w;     // [H*128,4] or null
+  const float* conv_k_w;
+  void* conv_q_state;        // [N,3,H,128] raw rows before token 0; advanced when state_out is set
+  void* conv_k_state;
+  const void* gate;          // [N,L,H,128] or null
+  const float* norm_w;       // [128] or null
+  float l2_eps, rms_eps;
+  void* o;                   // [N,L,H,128] or null
+  int num_seqs;
+  int num_heads;
+  int max_tokens;            // L
+  bool bf16;
+};
+
 struct ScanArgs {
   float* pairs;             // [seg][H][2][128][128]: B_j (overwritten by S_in(j)), then M_j
   const int32_t* seq_first; // [N+1]: first segment of each sequence (exclusive prefix sum)
@@ -153,6 +177,8 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
 hipError_t launch_carry(const CarryArgs& a, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+constexpr int kReplayMaxTokens = 16;
+hipError_t launch_replay(const ReplayArgs& a, hipStream_t stream);
 // Longest-first ordering of the packed sequences (device-side, no host sync).
 hipError_t launch_worklist(const int32_t* cu, int num_seqs, int32_t* order, hipStream_t stream);
 // Segment table: per-sequence segment counts, their exclusive prefix sum

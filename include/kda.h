@@ -156,6 +156,58 @@ kda_status kda_decode_step(float* state, const void* q, const void* k, const voi
                            const float* log_alpha, const float* beta, int num_seqs, int num_heads,
                            int d_k, int d_v, kda_dtype dtype, void* o, hipStream_t stream);
 
+/*
+ * Multi-token decode from cached per-token inputs: the replay step of
+ * speculative decoding ("Kimi K3 架构…" section 7.4, KDA state replay under
+ * speculative decoding: the per-token inputs of the draft tokens are kept
+ * instead of one state per draft position; after verification the accepted
+ * prefix is replayed from the verified state on chip, with the short
+ * convolution, the norms and the output gate in the same kernel, and only the
+ * final state is written back).  For each sequence n and head h, runs the
+ * recurrence above over tokens 0 .. nt-1 of the sequence's max_tokens cached
+ * tokens, starting from state_in, where nt = num_tokens[n] clamped to
+ * [0, max_tokens] (all of them when num_tokens is NULL).  The state is read
+ * once and written at most once, so its HBM traffic per token falls with nt.
+ *
+ * Typical use: a verification pass over all draft tokens with state_out NULL
+ * (outputs only, nothing committed), then a commit pass with num_tokens =
+ * accepted + 1 (the accepted drafts and the bonus token) and state_out ==
+ * state_in, o NULL.
+ *
+ *   state_in      [N, H, 128, 128] fp32, read only, or NULL for zeros.
+ *   state_out     [N, H, 128, 128] fp32 state after the nt tokens, or NULL
+ *                 (not written).  May be exactly state_in (in place); any
+ *                 other overlap with a buffer is KDA_ERR_INVALID_ARG.
+ *   q, k, v       [N, max_tokens, H, 128] dtype (raw q / k rows when their
+ *                 convolution runs); log_alpha [N, max_tokens, H, 128] fp32;
+ *                 beta [N, max_tokens, H] fp32.  Rows of tokens past nt are
+ *                 not read.
+ *   num_tokens    device int32 [N] or NULL.
+ *   max_tokens    1 .. 16 (larger values are KDA_ERR_UNSUPPORTED).
+ *   opts          NULL or the fused options of kda_chunk_fwd: conv_q_w /
+ *                 conv_k_w, gate ([N, max_tokens, H, 128] dtype logits),
+ *                 norm_w, l2_eps, rms_eps; segment_tokens is ignored.
+ *   conv_q_state, conv_k_state
+ *                 [N, 3, H, 128] dtype: the raw q (k) rows of the three
+ *                 positions before token 0, oldest first (zeros at a
+ *                 sequence start).  Required when the matching convolution
+ *                 weight is given, ignored otherwise.  They are read in every
+ *                 call and, only when state_out is given, overwritten with
+ *                 the raw rows of the three positions before token nt (the
+ *                 history the next call continues from).
+ *   o             [N, max_tokens, H, 128] dtype outputs of tokens 0 .. nt-1
+ *                 (rows past nt are not written), or NULL.  Must not overlap
+ *                 any other buffer.
+ * Every pointer needs 16-byte alignment except beta, num_tokens, the
+ * convolution weights and norm_w (4 bytes).  Calls whose buffers overlap
+ * must not run concurrently.
+ */
+kda_status kda_decode_replay(const float* state_in, float* state_out, const void* q, const void* k,
+                             const void* v, const float* log_alpha, const float* beta,
+                             const int32_t* num_tokens, int num_seqs, int max_tokens, int num_heads,
+                             int d_k, int d_v, kda_dtype dtype, const kda_fused_opts* opts,
+                             void* conv_q_state, void* conv_k_state, void* o, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* kda_status_string(kda_status s);
 

@@ -21,6 +21,15 @@ is deterministic for a given device type):
   epilogue gate logits N(0,1) in the I/O dtype, norm weight = ones (None).
   varlen   L_n = floor(1024 * 64**u_n), u_n ~ U[0,1) from numpy's Philox
            generator (log-uniform in [1024, 65536]).
+  replay   (multi-token decode of cached draft tokens, "Kimi K3 架构…"
+           section 7.4; drafts of up to 7 steps: the study notes' section
+           4-7, EAGLE-3-style draft model, and "Kimi K3 架构…" section 4.9)
+           N sequences x L = 8 cached tokens (7 drafts and the bonus token), [N, L, H, 128] token-major per sequence, drawn
+           like the prefill inputs with the prologue (raw q, k); convolution
+           histories [N, 3, H, 128] N(0,1) in the I/O dtype (the raw rows
+           before the drafts); S0 std * N(0,1).  Tokens run per sequence on
+           commit: uniform on {1, ..., L} from numpy's Philox generator (the
+           pages give no acceptance rate).
 """
 from __future__ import annotations
 
@@ -49,6 +58,10 @@ WORKLOADS = {
     # sequentially, so the library cuts the sequence into segments
     5: dict(name="kda_prefill_H8_T131072", kind="prefill", dtype="bf16", H=8, lengths=[131072],
             s0_std=0.02, fused=False),
+    # speculative decoding at the decode workload's batch: a verification
+    # pass over 7 draft tokens + the bonus token, then the replay commit
+    6: dict(name="kda_replay_N256_H96_L8", kind="replay", dtype="bf16", N=256, H=96, L=8, s0_std=0.02,
+            fused=True),
 }
 
 
@@ -150,6 +163,43 @@ def make_decode(N, H, steps, dtype="bf16", s0_std=0.02, device="cpu", seed=SEED_
                 beta=beta)
 
 
+def accepted_counts(seed: int, n: int, L: int) -> list:
+    """Tokens run per sequence on commit: uniform on {1, ..., L}."""
+    rng = np.random.Generator(np.random.Philox(seed))
+    return [int(x) for x in rng.integers(1, L + 1, size=n)]
+
+
+def make_replay(N, H, L, dtype="bf16", s0_std=0.02, fused=True, device="cpu", seed=SEED_BASE):
+    """Cached draft-token inputs [N, L, H, 128] plus the verified state, the
+    convolution histories and the per-sequence counts of tokens to commit."""
+    dt = torch_dtype(dtype)
+    g = _gen(device, seed)
+    out = {"N": N, "H": H, "L": L, "dtype": dtype, "fused": fused}
+    out["state"] = s0_std * _randn((N, H, D, D), g, device) if s0_std > 0 else None
+    rows = N * L
+    q = torch.empty((rows, H, D), dtype=dt, device=device)
+    k = torch.empty((rows, H, D), dtype=dt, device=device)
+    v = torch.empty((rows, H, D), dtype=dt, device=device)
+    _fill_unit(q, g, device, not fused, 16384)
+    _fill_unit(k, g, device, not fused, 16384)
+    _fill_unit(v, g, device, False, 16384)
+    la = -5.0 * torch.sigmoid(_randn((N, L, H, D), g, device))
+    beta = torch.sigmoid(_randn((N, L, H), g, device))
+    out.update(q=q.view(N, L, H, D), k=k.view(N, L, H, D), v=v.view(N, L, H, D), log_alpha=la, beta=beta)
+    if fused:
+        out["conv_q_w"] = 0.5 * _randn((H * D, 4), g, device)
+        out["conv_k_w"] = 0.5 * _randn((H * D, 4), g, device)
+        out["conv_q_state"] = _randn((N, 3, H, D), g, device).to(dt)
+        out["conv_k_state"] = _randn((N, 3, H, D), g, device).to(dt)
+        gate = torch.empty((rows, H, D), dtype=dt, device=device)
+        _fill_unit(gate, g, device, False, 16384)
+        out["gate"] = gate.view(N, L, H, D)
+        out["norm_w"] = None
+    out["num_tokens_host"] = accepted_counts(seed, N, L)
+    out["num_tokens"] = torch.tensor(out["num_tokens_host"], dtype=torch.int32, device=device)
+    return out
+
+
 def make_workload(wid: int, device="cpu", **overrides):
     """Inputs of one of the workloads above (overrides: e.g. lengths or steps)."""
     w = dict(WORKLOADS[wid])
@@ -157,5 +207,7 @@ def make_workload(wid: int, device="cpu", **overrides):
     seed = SEED_BASE + wid
     if w["kind"] == "decode":
         return make_decode(w["N"], w["H"], w["steps"], w["dtype"], w["s0_std"], device, seed)
+    if w["kind"] == "replay":
+        return make_replay(w["N"], w["H"], w["L"], w["dtype"], w["s0_std"], w["fused"], device, seed)
     lengths = w["lengths"] if w["lengths"] != "loguniform64" else varlen_lengths(seed)
     return make_prefill(w["H"], lengths, w["dtype"], w["s0_std"], w["fused"], device, seed)

@@ -39,6 +39,8 @@ def lib():
     L.kda_chunk_fwd.argtypes = [vp] * 7 + [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.kda_decode_step.restype = i32
     L.kda_decode_step.argtypes = [vp] * 6 + [i32, i32, i32, i32, i32, vp, vp]
+    L.kda_decode_replay.restype = i32
+    L.kda_decode_replay.argtypes = [vp] * 8 + [i32] * 6 + [vp] * 5
     return L
 
 
@@ -51,7 +53,7 @@ def declared_functions():
 def test_header_symbols_exported(lib):
     names = declared_functions()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_decode_step",
-                          "kda_status_string"}
+                          "kda_decode_replay", "kda_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s+(kda_\w+)", out))
     for n in names:
@@ -226,6 +228,40 @@ def test_decode_validation(lib):
     assert decode(lib, s=p(2)) == INVALID      # state aliases k
     assert decode(lib, s=ctypes.c_void_p(BASE + 8)) == INVALID  # state not 16-byte aligned
     assert decode(lib, q=ctypes.c_void_p(BASE + 64 * MB + 1)) == INVALID  # not element aligned
+
+
+def replay(lib, **kw):
+    a = dict(s0=p(0), s1=p(0), q=p(1), k=p(2), v=p(3), la=p(4), b=p(5), nt=p(7), N=2, L=4, H=2, dk=128, dv=128,
+             dt=BF16, opts=None, hq=None, hk=None, o=p(6))
+    a.update(kw)
+    return lib.kda_decode_replay(a["s0"], a["s1"], a["q"], a["k"], a["v"], a["la"], a["b"], a["nt"], a["N"],
+                                 a["L"], a["H"], a["dk"], a["dv"], a["dt"], a["opts"], a["hq"], a["hk"], a["o"],
+                                 None)
+
+
+def test_replay_validation(lib):
+    assert replay(lib, L=17) == UNSUPPORTED                  # more cached tokens than supported
+    assert replay(lib, dk=64) == UNSUPPORTED
+    assert replay(lib, L=0) == INVALID
+    assert replay(lib, N=0) == INVALID
+    assert replay(lib, q=None) == INVALID
+    assert replay(lib, o=p(3)) == INVALID                    # output aliases v
+    assert replay(lib, s1=p(1)) == INVALID                   # state output aliases q
+    assert replay(lib, s1=ctypes.c_void_p(BASE + 4096)) == INVALID  # partial overlap with state_in
+    assert replay(lib, s1=p(6)) == INVALID                   # state output aliases o
+    assert replay(lib, s0=ctypes.c_void_p(BASE + 8), s1=None) == INVALID  # not 16-byte aligned
+    assert replay(lib, nt=ctypes.c_void_p(BASE + 7 * 64 * MB + 2)) == INVALID  # counts not 4-byte aligned
+    wq = Opts(p(8).value, None, None, None, 1e-6, 1e-6, 0)
+    assert replay(lib, opts=opts_p(wq)) == INVALID           # convolution without its history
+    assert replay(lib, opts=opts_p(wq), hq=p(6)) == INVALID  # history aliases o
+    assert replay(lib, opts=opts_p(wq), hq=p(8)) == INVALID  # history aliases the weights
+    assert replay(lib, opts=opts_p(wq), hq=ctypes.c_void_p(BASE + 9 * 64 * MB + 8)) == INVALID  # alignment
+    g = Opts(None, None, p(6).value, None, 1e-6, 1e-6, 0)
+    assert replay(lib, opts=opts_p(g)) == INVALID            # gate aliases o
+    neg = Opts(None, None, None, None, 1e-6, -1.0, 0)
+    assert replay(lib, opts=opts_p(neg)) == INVALID          # negative epsilon
+    # nothing to produce: accepted without launching anything
+    assert replay(lib, s1=None, o=None) == OK
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
