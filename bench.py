@@ -3,6 +3,7 @@
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 1]
                     [--no-decode] [--no-cpu-baseline] [--decode-steps 64]
                     [--extra-workloads 2,4,5] [--extra-steps 3]
+                    [--no-replay] [--replay-rounds 16]
 
 A step is one kda_chunk_fwd over one layer of the workload (all heads, all
 tokens, inputs already resident in HBM): by default the one-layer K3 shape
@@ -10,8 +11,12 @@ H=96, d=128, T=8192 with a carried fp32 state.  `value` is prefill tokens/s.
 The decode workload (256 sequences x 96 heads, 64 in-place kda_decode_step
 calls) is timed after it and reported under "decode"; the long-context (T=131072),
 the varlen fused prologue/epilogue and the few-head (H=8, T=131072, segmented
-schedule) workloads are timed with fewer steps and reported under "workloads".  Kernel durations come from HIP events on the
-stream the kernels run on.
+schedule) workloads are timed with fewer steps and reported under "workloads".
+The speculative-decoding replay (the same 256 x 96 batch with 8 cached tokens
+per sequence: a verification pass over all of them, then the in-place commit
+of the drawn accepted counts, both kda_decode_replay with the fused
+prologue/epilogue) is reported under "replay".  Kernel durations come from
+HIP events on the stream the kernels run on.
 
 Prints one JSON line.  Only the optional CPU-baseline leg touches the oracle.
 """
@@ -59,6 +64,19 @@ def decode_algorithmic_bytes(N: int, H: int, es: int) -> int:
     return N * H * (2 * d * d * 4 + 3 * d * es + d * 4 + 4 + d * es)
 
 
+def replay_algorithmic_bytes(N: int, H: int, L: int, counts, es: int, commit: bool) -> int:
+    """One kda_decode_replay launch with the fused options.  Verification:
+    state read, every cached token's raw q, k, v, log_alpha, beta and gate,
+    o written, both convolution histories read.  Commit: state read + write,
+    the inputs of the tokens run, histories read + written, no o."""
+    d = 128
+    tok_in = 3 * d * es + d * 4 + 4 + d * es
+    hist = 2 * 3 * d * es
+    if not commit:
+        return N * H * (d * d * 4 + hist) + N * H * L * (tok_in + d * es)
+    return N * H * (2 * d * d * 4 + 2 * hist) + H * int(sum(counts)) * tok_in
+
+
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch recorded in profiles/hbm_traffic.json (rocprofv3
     FETCH_SIZE / WRITE_SIZE, copy-calibrated; for kda_chunk_fwd the sum over
@@ -73,7 +91,9 @@ def measured_traffic(kernel: str, workload: str):
         return None
     src = {"kda_chunk_fwd": ["kda_chunk.hip", "kda_prep.hip", "kda_chunk_util.h", "kda_device.h", "kda_internal.h",
                              "kda_api.hip"],
-           "decode_kernel": ["kda_decode.hip", "kda_device.h", "kda_internal.h"]}[kernel]
+           "decode_kernel": ["kda_decode.hip", "kda_device.h", "kda_internal.h"],
+           "replay_verify": ["kda_replay.hip", "kda_device.h", "kda_internal.h"],
+           "replay_commit": ["kda_replay.hip", "kda_device.h", "kda_internal.h"]}[kernel]
     m = hashlib.sha256()
     for f in src:
         with open(os.path.join(ROOT, "gated_delta_rule_25_amd", "csrc", f), "rb") as fh:
@@ -206,6 +226,9 @@ def main():
                     help="other prefill workloads timed after the main one and reported under 'workloads' ('' = none)")
     ap.add_argument("--extra-steps", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-replay", action="store_true")
+    ap.add_argument("--replay-rounds", type=int, default=16)
+    ap.add_argument("--only-replay", action="store_true", help="time only the replay workload (profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-decode", action="store_true", help="time only the decode workload (profiling)")
     ap.add_argument("--only-prefill", action="store_true", help="time only the prefill workload (profiling)")
@@ -229,8 +252,14 @@ def main():
     if args.only_prefill:
         args.no_decode = True
         args.no_cpu_baseline = True
-    if args.only_prefill or args.only_decode:
+    if args.only_prefill or args.only_decode or args.only_replay:
         args.extra_workloads = ""
+    if args.only_decode or args.only_replay:
+        args.no_cpu_baseline = True
+    if args.only_prefill or args.only_replay:
+        args.no_decode = True
+    if args.only_prefill or args.only_decode:
+        args.no_replay = True
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -239,7 +268,7 @@ def main():
         result["copy_calibration_bytes"] = src.numel() * 4
         del src, dst
 
-    if not args.only_decode:
+    if not (args.only_decode or args.only_replay):
         inp, tm = time_prefill(kda, kda_inputs, args.workload, args.steps, args.warmup, dev, stream)
         result.update({
             "metric": "KDA prefill tokens/s (H=96,d=128,T=8K) + decode steps/s; % of roofline",
@@ -312,7 +341,79 @@ def main():
                                          "kernel": "decode_kernel", "kernel_ms_min": min(per)}}
         if args.only_decode:
             result.update({"metric": "KDA decode steps/s", "value": 1e3 / ms_avg, "unit": "steps/s"})
+        del d, state, outs
+        torch.cuda.empty_cache()
+
+    if not args.no_replay:
+        result["replay"] = time_replay(kda, kda_inputs, args.replay_rounds, dev, stream,
+                                       result.get("decode", {}).get("ms_per_step"))
+        if args.only_replay:
+            result.update({"metric": "KDA replay committed tokens/s", "unit": "tokens/s",
+                           "value": result["replay"]["committed_tokens_per_s"]})
     print(json.dumps(result), flush=True)
+
+
+def time_replay(kda, kda_inputs, rounds, dev, stream, decode_ms=None):
+    """Speculative-decoding rounds at the decode batch (256 sequences x 96
+    heads, 8 cached tokens: 7 drafts + the bonus token, fused prologue and
+    epilogue): a verification pass over every cached token (outputs only),
+    then the commit of the drawn token counts, state and histories in place.
+    Each launch is bracketed by HIP events on the stream it runs on."""
+    import torch
+    wr = kda_inputs.WORKLOADS[6]
+    r = kda_inputs.make_workload(6, device=dev)
+    N, L, H = r["N"], r["L"], r["H"]
+    counts = r["num_tokens_host"]
+    state, hq, hk = r["state"], r["conv_q_state"], r["conv_k_state"]
+    kw = dict(conv_q_w=r["conv_q_w"], conv_k_w=r["conv_k_w"], gate=r["gate"])
+    o = torch.empty_like(r["v"])
+
+    def verify(st, a, b):
+        kda.decode_replay(st, r["q"], r["k"], r["v"], r["log_alpha"], r["beta"], conv_q_state=a, conv_k_state=b,
+                          out=o, **kw)
+
+    def commit(st, a, b):
+        kda.decode_replay(st, r["q"], r["k"], r["v"], r["log_alpha"], r["beta"], r["num_tokens"], state_out=st,
+                          conv_q_state=a, conv_k_state=b, out=False, **kw)
+
+    # warm-up rounds on scratch copies; the timed rounds then start from the drawn state
+    scratch, sa, sb = state.clone(), hq.clone(), hk.clone()
+    for _ in range(2):
+        verify(scratch, sa, sb)
+        commit(scratch, sa, sb)
+    torch.cuda.synchronize()
+    del scratch, sa, sb
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * rounds + 1)]
+    ev[0].record(stream)
+    for i in range(rounds):
+        verify(state, hq, hk)
+        ev[2 * i + 1].record(stream)
+        commit(state, hq, hk)
+        ev[2 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    ver = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(rounds)]
+    com = [ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(rounds)]
+    ms_round = ev[0].elapsed_time(ev[-1]) / rounds
+    vb = replay_algorithmic_bytes(N, H, L, counts, 2, False)
+    cb = replay_algorithmic_bytes(N, H, L, counts, 2, True)
+
+    def roof(b, ms, name):
+        ach = b / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                "algorithmic_bytes": b, "traffic": measured_traffic(name, wr["name"]), "kernel": "replay_kernel",
+                "kernel_ms_avg": ms}
+
+    v_ms, c_ms = sum(ver) / rounds, sum(com) / rounds
+    out = {"workload": wr["name"], "rounds": rounds, "ms_per_round": ms_round, "rounds_per_s": 1e3 / ms_round,
+           "committed_tokens_per_round": int(sum(counts)),
+           "committed_tokens_per_s": sum(counts) * 1e3 / ms_round,
+           "verified_tokens_per_s": N * L * 1e3 / ms_round,
+           "verify": roof(vb, v_ms, "replay_verify"), "commit": roof(cb, c_ms, "replay_commit"),
+           "finite": bool(torch.isfinite(state).all().item())}
+    if decode_ms:
+        # the same commit made of one single-token decode step per token
+        out["commit_as_decode_steps_ms"] = decode_ms * sum(counts) / N
+    return out
 
 
 if __name__ == "__main__":
