@@ -188,9 +188,6 @@ struct CarryLayout {
   static constexpr size_t BYTES = SS + (size_t)NWC * C * 4;
 };
 
-// Number of vector-memory operations allowed to stay outstanding in s_waitcnt.
-__host__ __device__ constexpr int vmcnt_wait(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
-
 // Workgroup of NWC = DV / (16 CT) compute waves plus one loader wave.
 // Compute wave w owns the CT 16-column tiles of value columns
 // 16 CT w .. 16 CT (w + 1) - 1 of the block and keeps that slice of the fp32

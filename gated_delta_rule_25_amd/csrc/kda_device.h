@@ -107,6 +107,9 @@ __device__ __forceinline__ f32x4 mma(f32x4 acc, const Frag<float>& a, const Frag
 
 __device__ __forceinline__ float sigmoidf_fast(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
+// s_waitcnt operand that lets n vector-memory operations stay outstanding.
+__host__ __device__ constexpr int vmcnt_wait(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
+
 // 2^x with the hardware exp unit (inputs here lie in [-128, 128]; results
 // below the normal range flush toward zero, which is the intended limit).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

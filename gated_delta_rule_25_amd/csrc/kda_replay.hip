@@ -10,23 +10,39 @@
 // is written back.  The same kernel without the state write is the
 // verification pass over every draft token.
 //
-// Per (sequence n, head h) one 256-thread workgroup:
-//   1. issues the 64 KiB state load (thread t owns columns 4(t%32)..+3 and
-//      rows 16(t/32)..+15, as in the single-token decode) and every cached
-//      input of the tokens it runs (16-byte pieces: q and k rows with their
-//      three history rows when the convolution runs, v, log_alpha, gate),
-//      all in flight together, the inputs staged in LDS;
-//   2. forms per token the decay a = exp(log_alpha), the prologue
-//      (ShortConv4 + SiLU, then L2 over the head's channels; "Kimi K3 架构…"
-//      section 4.2.3) and the products a*q', a*k', k', q'.k';
-//   3. runs the tokens one after another on the register-resident state:
-//      x = sum_i a_i k_i S[i,:], y = sum_i a_i q_i S[i,:] (one LDS exchange
-//      across the four waves), u = beta (v - x), S <- a S + k u^T,
-//      o = y + (k.q) u, then RMSNorm x sigmoid(gate) (section 4.2.6);
-//   4. writes the state and the three raw rows before the next token only
-//      when a state output is given.
-// The state is read once and written at most once however many tokens run,
-// so the HBM bytes per token fall with the number of tokens.
+// The nt <= 16 tokens of one (sequence n, head h) are taken as one block of
+// the chunkwise form (section 4.2.4): with D_t = prod_{s<=t} alpha_s per key
+// channel, K~ = D k, Q~ = D q, K^ = k / D, Kb = (D_last / D) k,
+//     X = K~ S0,  Y = Q~ S0,  G = [K~; Q~] K^^T            (matrix products)
+//     u_t = beta_t (v_t - X_t - sum_{s<t} G[t][s] u_s)       (forward substitution)
+//     o_t = Y_t + sum_{s<=t} G[LP+t][s] u_s
+//     S   = Diag(D_last) S0 + Kb^T U
+// which is the token-by-token recurrence regrouped.  The decay lower bound
+// (log alpha >= -5, section 4.2.5: over 16 tokens the reciprocal stays
+// below e^80, inside the fp32 range) keeps every factor finite; that bound is
+// why a block holds at most 16 tokens.
+//
+// One 256-thread workgroup per (n, h).  Wave w owns value columns 32w..32w+31
+// as two 16-column MFMA tiles (tile C holds columns 32w + 2c + C, c = lane %
+// 16) over all 128 rows, so the state sits in registers in the MFMA
+// accumulator layout; that layout is also the B operand of a 16-deep fp32
+// MFMA step, so X, Y and the state update read the state where it is.
+// Steps:
+//   1. the state load (8-byte pieces, two columns) and every cached input of
+//      the tokens run (16-byte pieces: q and k rows with their three history
+//      rows when the convolution runs, v, log_alpha, gate), all in flight
+//      together; the inputs are staged in LDS;
+//   2. per channel: the prologue (ShortConv4 + SiLU, then L2 over the head's
+//      channels; section 4.2.3) and the decay products D_t, giving K~, Q~,
+//      K^ (and Kb, D_last when committing);
+//   3. [X; Y] = [K~; Q~] S0 and G on fp32 MFMA (v_mfma_f32_16x16x4_f32);
+//      per column the substitution for u and the outputs, then RMSNorm x
+//      sigmoid(gate) (section 4.2.6);
+//   4. when a state output is given: S = Diag(D_last) S0 + Kb^T U on MFMA,
+//      the state store, and the three raw rows before the next token.
+// All arithmetic is fp32.  The state is read once and written at most once
+// however many tokens run.
+#include "kda_chunk_util.h"
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -34,25 +50,32 @@ namespace kda {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kNonTemporal = 2;  // cache-policy operand of a streaming buffer access
+constexpr int PS = D + 4;   // padded row stride (floats) of the MFMA A / B operand arrays
 
-// Dynamic LDS of one workgroup for L cached tokens (byte offsets, all
-// multiples of 16).
+// Dynamic LDS of one workgroup for L cached tokens, LP = 8 or 16 block rows
+// (byte offsets, all multiples of 16).
 struct ReplayLayout {
-  uint32_t RQ, RK, RV, RG, RLA, A, AQ, KP, AK, SC, PART, BYTES;
-  __host__ __device__ ReplayLayout(int L, int es, bool gate) {
+  uint32_t RQ, RK, SGP, SG, RV, RG, RLA, PX, PY, SP, SKH, SGAM, SSC, SSS, BYTES;
+  __host__ __device__ ReplayLayout(int L, int es, bool gate, int LP) {
     const uint32_t rb = 128u * (uint32_t)es;
-    RQ = 0;                                   // E [3 + L][128]: raw q, history rows then tokens
-    RK = RQ + (3u + L) * rb;                  // E [3 + L][128]: raw k
-    RV = RK + (3u + L) * rb;                  // E [L][128]
-    RG = RV + (uint32_t)L * rb;               // E [L][128] gate logits
-    RLA = RG + (gate ? (uint32_t)L * rb : 0u);  // f32 [L][128] log_alpha
-    A = RLA + (uint32_t)L * 512u;             // f32 [L][128] a = exp(log_alpha)
-    AQ = A + (uint32_t)L * 512u;              // f32 [L][128] q before L2, then a * q'
-    KP = AQ + (uint32_t)L * 512u;             // f32 [L][128] k before L2, then k'
-    AK = KP + (uint32_t)L * 512u;             // f32 [L][128] a * k'
-    SC = AK + (uint32_t)L * 512u;             // f32 [L][4]  1/|q|, 1/|k|, q'.k', beta
-    PART = SC + (uint32_t)L * 16u;            // f32 [2][4 waves][2][128] column-sum exchange
-    BYTES = PART + 2u * 4u * 2u * 128u * 4u;
+    RQ = 0;                                       // E [3 + L][128]: raw q, history rows then tokens
+    RK = RQ + (3u + L) * rb;                      // E [3 + L][128]: raw k
+    // once the prologue has read the raw rows, the same bytes hold the Gram products
+    SGP = 0;                                      // f32 [4 waves][2LP][16] partial G
+    SG = SGP + 4u * (uint32_t)(2 * LP) * 64u;     // f32 [2LP][16] G
+    const uint32_t u0 = 2u * (3u + L) * rb, u1 = SG + (uint32_t)(2 * LP) * 64u;
+    RV = u0 > u1 ? u0 : u1;                       // E [L][128]
+    RG = RV + (uint32_t)L * rb;                   // E [L][128] gate logits
+    RLA = RG + (gate ? (uint32_t)L * rb : 0u);    // f32 [L][128] log_alpha
+    PX = RLA + (uint32_t)L * 512u;                // f32 [LP][128] q before L2, then X
+    PY = PX + (uint32_t)LP * 512u;                // f32 [LP][128] k before L2, then Y
+    SP = PY + (uint32_t)LP * 512u;                // f32 [2LP][PS] K~ then Q~; later U [LP][128]
+    SKH = SP + (uint32_t)(2 * LP) * PS * 4u;      // f32 [LP][PS] K^ (rows >= nt zero)
+    SGAM = SKH + (uint32_t)LP * PS * 4u;          // f32 [128] D_last
+    SSC = SGAM + 512u;                            // f32 [LP][4] 1/|q|, 1/|k|, -, beta
+    SSS = SSC + (uint32_t)LP * 16u;               // f32 [2][LP] sums of squares of o
+    BYTES = SSS + (uint32_t)LP * 8u;
   }
 };
 
@@ -61,84 +84,70 @@ __device__ __forceinline__ float lds_elem(const unsigned char* base, int row, in
   return to_f32(reinterpret_cast<const E*>(base)[row * D + j]);
 }
 
-template <typename E>
-__device__ __forceinline__ void store4(E* dst, const f32x4& x);
-template <>
-__device__ __forceinline__ void store4<float>(float* dst, const f32x4& x) {
-  *reinterpret_cast<f32x4*>(dst) = x;
-}
-template <>
-__device__ __forceinline__ void store4<__bf16>(__bf16* dst, const f32x4& x) {
-  const bf16x4 b = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
-  *reinterpret_cast<bf16x4*>(dst) = b;
-}
-
-template <typename E, bool PRO, bool EPI>
+template <typename E, int LP, bool PRO, bool EPI>
 __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
   constexpr int ES = (int)sizeof(E);
   constexpr int RP = D * ES / 16;  // 16-byte pieces of one row in the I/O dtype
-  constexpr int LP = D * 4 / 16;   // pieces of one log_alpha row
+  constexpr int LP4 = D * 4 / 16;  // pieces of one log_alpha row
+  constexpr int NR = 2 * LP / 16;  // MFMA row tiles of [K~; Q~]
+  constexpr float LOG2E = 1.4426950408889634f;
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int L = p.max_tokens, H = p.num_heads;
-  const ReplayLayout lay(L, ES, EPI);
+  const ReplayLayout lay(L, ES, EPI, LP);
   const int64_t u = blockIdx.x;  // n * H + h
   const int n = (int)(u / H), h = (int)(u % H);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int cg = tid & 31;  // columns 4cg .. 4cg+3
-  const int rg = tid >> 5;  // rows 16rg .. 16rg+15
+  const int c16 = lane & 15, g4 = lane >> 4;  // MFMA lane coordinates
   int nt = p.num_tokens ? p.num_tokens[n] : L;
   nt = min(max(nt, 0), L);
+  const bool commit = p.state_out != nullptr;
 
-  // ---- 1. state and token inputs in flight together ----
-  f32x4 st[16];
-  if (p.state_in) {
-    const float* S = p.state_in + u * (D * D);
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      st[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (16 * rg + i) * D + 4 * cg));
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) st[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  }
-
+  // ---- 1. token inputs, then the state, all in flight together ----
   const bool cq = PRO && p.conv_q_w, ck = PRO && p.conv_k_w;
   const size_t rowb = (size_t)D * ES;
-  // Staging: one guarded loop per input, each a fixed number of 16-byte
-  // pieces per thread, every load issued before the first LDS store.
-  // q / k: staged row r holds the history (rows 0..2, oldest first) or token
-  // r - 3; without the convolution only rows 3 .. 3 + nt - 1 are loaded.
+  // The cached inputs go straight from global memory into LDS (16-byte
+  // pieces, piece pc of an input at byte 16 pc of its LDS array, so one
+  // instruction of wave w writes 64 consecutive pieces at a wave-uniform
+  // base).  q / k: staged row r holds the history (rows 0..2, oldest first)
+  // or token r - 3; without the convolution only rows 3 .. 3 + nt - 1 are
+  // loaded.
   constexpr int QKS = ((3 + kReplayMaxTokens) * RP + kThreads - 1) / kThreads;
   constexpr int VS = (kReplayMaxTokens * RP + kThreads - 1) / kThreads;
-  constexpr int LS = (kReplayMaxTokens * LP + kThreads - 1) / kThreads;
-  u32x4 rq[QKS], rk[QKS], rv[VS], rl[LS], rgt[EPI ? VS : 1];
+  constexpr int LS = (kReplayMaxTokens * LP4 + kThreads - 1) / kThreads;
+  const int wu = __builtin_amdgcn_readfirstlane(wv);
   auto qk_src = [&](const void* tok, const void* hist, int r, int w) {
     const char* b = r < 3 ? static_cast<const char*>(hist) + ((size_t)(n * 3 + r) * H + h) * rowb
                           : static_cast<const char*>(tok) + ((size_t)(n * L + r - 3) * H + h) * rowb;
-    return reinterpret_cast<const u32x4*>(b + w * 16);
+    return b + w * 16;
   };
   auto tok_src = [&](const void* base, size_t rb, int t, int w) {
-    return reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + ((size_t)(n * L + t) * H + h) * rb +
-                                          w * 16);
+    return static_cast<const char*>(base) + ((size_t)(n * L + t) * H + h) * rb + w * 16;
+  };
+  auto to_lds = [&](const char* g, uint32_t wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(smem + wave_base), 16, 0, 0);
   };
   const int q0 = cq ? 0 : 3, k0 = ck ? 0 : 3;  // first staged row
-  const int nq = (3 + nt - q0) * RP, nk = (3 + nt - k0) * RP, ntp = nt * RP, nlp = nt * LP;
+  const int nq = (3 + nt - q0) * RP, nk = (3 + nt - k0) * RP, ntp = nt * RP, nlp = nt * LP4;
 #pragma unroll
   for (int i = 0; i < QKS; ++i) {
     const int pc = tid + kThreads * i;
-    if (pc < nq) rq[i] = *qk_src(p.q, p.conv_q_state, q0 + pc / RP, pc % RP);
-    if (pc < nk) rk[i] = *qk_src(p.k, p.conv_k_state, k0 + pc / RP, pc % RP);
+    const uint32_t pw = (uint32_t)(kThreads * i + 64 * wu) * 16u;  // this wave's first piece
+    if (pc < nq) to_lds(qk_src(p.q, p.conv_q_state, q0 + pc / RP, pc % RP), lay.RQ + (uint32_t)(q0 * RP) * 16u + pw);
+    if (pc < nk) to_lds(qk_src(p.k, p.conv_k_state, k0 + pc / RP, pc % RP), lay.RK + (uint32_t)(k0 * RP) * 16u + pw);
   }
 #pragma unroll
   for (int i = 0; i < VS; ++i) {
     const int pc = tid + kThreads * i;
-    if (pc < ntp) rv[i] = *tok_src(p.v, rowb, pc / RP, pc % RP);
-    if (EPI && pc < ntp) rgt[i] = *tok_src(p.gate, rowb, pc / RP, pc % RP);
+    const uint32_t pw = (uint32_t)(kThreads * i + 64 * wu) * 16u;
+    if (pc < ntp) to_lds(tok_src(p.v, rowb, pc / RP, pc % RP), lay.RV + pw);
+    if (EPI && pc < ntp) to_lds(tok_src(p.gate, rowb, pc / RP, pc % RP), lay.RG + pw);
   }
 #pragma unroll
   for (int i = 0; i < LS; ++i) {
     const int pc = tid + kThreads * i;
-    if (pc < nlp) rl[i] = *tok_src(p.log_alpha, D * 4, pc / LP, pc % LP);
+    const uint32_t pw = (uint32_t)(kThreads * i + 64 * wu) * 16u;
+    if (pc < nlp) to_lds(tok_src(p.log_alpha, D * 4, pc / LP4, pc % LP4), lay.RLA + pw);
   }
   float bt = 0.f;
   if (tid < nt) bt = p.beta[((size_t)n * L + tid) * H + h];
@@ -152,38 +161,48 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) w4[m] = cw[m];
   }
-  auto put = [&](uint32_t off, const u32x4& x) { *reinterpret_cast<u32x4*>(smem + off) = x; };
+  // The state, issued last: its 32 loads per lane stay in flight through the
+  // prologue while the wait below covers only what was issued before them.
+  // st[T][C][e] = S0[16T + 4 g4 + e][32 wv + 2 c16 + C]
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 st[8][2];
+  const int col0 = 32 * wv + 2 * c16;
+  {
+    // a buffer view of the (n, h) state; with no state given its range is
+    // empty and every load returns zero
+    const Rsrc rs = make_rsrc(p.state_in ? p.state_in + u * (D * D) : nullptr, p.state_in ? D * D * 4 : 0);
 #pragma unroll
-  for (int i = 0; i < QKS; ++i) {
-    const int pc = tid + kThreads * i;
-    if (pc < nq) put(lay.RQ + (uint32_t)(q0 * RP + pc) * 16u, rq[i]);
-    if (pc < nk) put(lay.RK + (uint32_t)(k0 * RP + pc) * 16u, rk[i]);
-  }
+    for (int T = 0; T < 8; ++T)
 #pragma unroll
-  for (int i = 0; i < VS; ++i) {
-    const int pc = tid + kThreads * i;
-    if (pc < ntp) put(lay.RV + (uint32_t)pc * 16u, rv[i]);
-    if (EPI && pc < ntp) put(lay.RG + (uint32_t)pc * 16u, rgt[i]);
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 x = __builtin_bit_cast(
+            f32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, ((16 * T + 4 * g4 + e) * D + col0) * 4, 0, kNonTemporal));
+        st[T][0][e] = x[0];
+        st[T][1][e] = x[1];
+      }
   }
-#pragma unroll
-  for (int i = 0; i < LS; ++i) {
-    const int pc = tid + kThreads * i;
-    if (pc < nlp) put(lay.RLA + (uint32_t)pc * 16u, rl[i]);
-  }
-  float* sA = reinterpret_cast<float*>(smem + lay.A);
-  float* sAQ = reinterpret_cast<float*>(smem + lay.AQ);
-  float* sKP = reinterpret_cast<float*>(smem + lay.KP);
-  float* sAK = reinterpret_cast<float*>(smem + lay.AK);
-  float* sSC = reinterpret_cast<float*>(smem + lay.SC);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(32));
+  float* sX = reinterpret_cast<float*>(smem + lay.PX);  // pre-norm q, then X
+  float* sY = reinterpret_cast<float*>(smem + lay.PY);  // pre-norm k, then Y
+  float* sP = reinterpret_cast<float*>(smem + lay.SP);
+  float* sKh = reinterpret_cast<float*>(smem + lay.SKH);
+  float* sGam = reinterpret_cast<float*>(smem + lay.SGAM);
+  float* sSC = reinterpret_cast<float*>(smem + lay.SSC);
+  float* sGP = reinterpret_cast<float*>(smem + lay.SGP);
+  float* sG = reinterpret_cast<float*>(smem + lay.SG);
+  float* sSS = reinterpret_cast<float*>(smem + lay.SSS);
+  const float* sLA = reinterpret_cast<const float*>(smem + lay.RLA);
   if (tid < nt) sSC[4 * tid + 3] = bt;
   __syncthreads();
 
-  // ---- 2. per-token operands ----
+  // ---- 2. per-channel operands ----
+  // raw rows t-3, t-2, t-1 of channel j; after the loop the three rows
+  // before token nt, which a commit writes back as the new history
+  float x0 = 0.f, x1 = 0.f, x2 = 0.f;
   {
     const unsigned char* rows = smem + (isk ? lay.RK : lay.RQ);
-    float* pre = isk ? sKP : sAQ;  // before the L2 scale
-    const float* sla = reinterpret_cast<const float*>(smem + lay.RLA);
-    float x0 = 0.f, x1 = 0.f, x2 = 0.f;  // raw rows t-3, t-2, t-1 of channel j
+    float* pre = isk ? sY : sX;  // before the L2 scale
     if (conv) {
       x0 = lds_elem<E>(rows, 0, j);
       x1 = lds_elem<E>(rows, 1, j);
@@ -200,134 +219,210 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
         x2 = x3;
       }
       pre[t * D + j] = s;
-      if (!isk) sA[t * D + j] = __expf(sla[t * D + j]);
     }
   }
   __syncthreads();
-  // squared norms and q.k of every token (wave wv takes tokens wv, wv + 4, ...)
-  for (int t = wv; t < nt; t += 4) {
-    const float q0 = sAQ[t * D + lane], q1 = sAQ[t * D + 64 + lane];
-    const float k0 = sKP[t * D + lane], k1 = sKP[t * D + 64 + lane];
-    float sq = q0 * q0 + q1 * q1, sk = k0 * k0 + k1 * k1, qk = q0 * k0 + q1 * k1;
+  // squared norms of every token's q and k (wave wv takes tokens wv, wv + 4, ...)
+  if (cq || ck) {
+    for (int t = wv; t < nt; t += 4) {
+      const float q0v = sX[t * D + lane], q1v = sX[t * D + 64 + lane];
+      const float k0v = sY[t * D + lane], k1v = sY[t * D + 64 + lane];
+      float sq = q0v * q0v + q1v * q1v, sk = k0v * k0v + k1v * k1v;
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      sq += __shfl_xor(sq, m);
-      sk += __shfl_xor(sk, m);
-      qk += __shfl_xor(qk, m);
-    }
-    if (lane == 0) {
-      const float iq = cq ? rsqrtf(sq + p.l2_eps) : 1.f;
-      const float ik = ck ? rsqrtf(sk + p.l2_eps) : 1.f;
-      sSC[4 * t] = iq;
-      sSC[4 * t + 1] = ik;
-      sSC[4 * t + 2] = qk * iq * ik;
-    }
-  }
-  __syncthreads();
-  for (int t = 0; t < nt; ++t) {
-    const float a = sA[t * D + j];
-    if (!isk) {
-      sAQ[t * D + j] = a * (sAQ[t * D + j] * sSC[4 * t]);
-    } else {
-      const float kv = sKP[t * D + j] * sSC[4 * t + 1];
-      sKP[t * D + j] = kv;
-      sAK[t * D + j] = a * kv;
-    }
-  }
-  __syncthreads();
-
-  // ---- 3. the tokens, in order, on the register-resident state ----
-  E* go = static_cast<E*>(p.o);
-  const E* sV = reinterpret_cast<const E*>(smem + lay.RV);
-  const E* sG = reinterpret_cast<const E*>(smem + lay.RG);
-  float* part = reinterpret_cast<float*>(smem + lay.PART);
-  f32x4 nw = {1.f, 1.f, 1.f, 1.f};
-  if (EPI && p.norm_w) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) nw[e] = p.norm_w[4 * cg + e];
-  }
-  for (int t = 0; t < nt; ++t) {
-    const f32x4* ak4 = reinterpret_cast<const f32x4*>(sAK + t * D + 16 * rg);
-    const f32x4* aq4 = reinterpret_cast<const f32x4*>(sAQ + t * D + 16 * rg);
-    f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 ka = ak4[i4], qa = aq4[i4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x += ka[e] * st[4 * i4 + e];
-        y += qa[e] * st[4 * i4 + e];
+      for (int m = 32; m >= 1; m >>= 1) {
+        sq += __shfl_xor(sq, m);
+        sk += __shfl_xor(sk, m);
       }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[e] += __shfl_xor(x[e], 32);
-      y[e] += __shfl_xor(y[e], 32);
-    }
-    float* pp = part + (t & 1) * (4 * 2 * D);
-    if ((tid & 32) == 0) {
-      *reinterpret_cast<f32x4*>(pp + wv * 2 * D + 4 * cg) = x;
-      *reinterpret_cast<f32x4*>(pp + wv * 2 * D + D + 4 * cg) = y;
+      if (lane == 0) {
+        sSC[4 * t] = cq ? rsqrtf(sq + p.l2_eps) : 1.f;
+        sSC[4 * t + 1] = ck ? rsqrtf(sk + p.l2_eps) : 1.f;
+      }
     }
     __syncthreads();
-    x = *reinterpret_cast<const f32x4*>(pp + 4 * cg);
-    y = *reinterpret_cast<const f32x4*>(pp + D + 4 * cg);
+  }
+  {
+    // D_t = prod_{s<=t} alpha_s and its reciprocal, from exp2 of each step
+    float Dt = 1.f, Di = 1.f;
+    if (!isk) {
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
-      x += *reinterpret_cast<const f32x4*>(pp + w * 2 * D + 4 * cg);
-      y += *reinterpret_cast<const f32x4*>(pp + w * 2 * D + D + 4 * cg);
+      for (int t = 0; t < LP; ++t) {
+        float qt = 0.f;
+        if (t < nt) {
+          Dt *= exp2_fast(sLA[t * D + j] * LOG2E);
+          qt = sX[t * D + j] * ((cq || ck) ? sSC[4 * t] : 1.f) * Dt;
+        }
+        sP[(LP + t) * PS + j] = qt;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < LP; ++t) {
+        float kt = 0.f, kh = 0.f;
+        if (t < nt) {
+          const float x = sLA[t * D + j] * LOG2E;
+          Dt *= exp2_fast(x);
+          Di *= exp2_fast(-x);
+          const float kv = sY[t * D + j] * ((cq || ck) ? sSC[4 * t + 1] : 1.f);
+          kt = kv * Dt;
+          kh = kv * Di;
+        }
+        sP[t * PS + j] = kt;
+        sKh[t * PS + j] = kh;
+      }
+      sGam[j] = Dt;  // D_last: the decay over all tokens run
     }
-    const f32x4 sc = *reinterpret_cast<const f32x4*>(sSC + 4 * t);  // 1/|q|, 1/|k|, q'.k', beta
-    f32x4 vv;
+  }
+  __syncthreads();
+
+  // ---- 3. [X; Y] = [K~; Q~] S0 and the partial Gram products on MFMA ----
+  {
+    f32x4 acc[NR][2], gacc[NR];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vv[e] = to_f32(sV[t * D + 4 * cg + e]);
-    const f32x4 uu = sc[3] * (vv - x);
-    const f32x4* a4 = reinterpret_cast<const f32x4*>(sA + t * D + 16 * rg);
-    const f32x4* k4 = reinterpret_cast<const f32x4*>(sKP + t * D + 16 * rg);
+    for (int R = 0; R < NR; ++R) acc[R][0] = acc[R][1] = gacc[R] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 a = a4[i4], kk = k4[i4];
+    for (int T = 0; T < 8; ++T) {
+      Frag16<float> a[NR];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) st[4 * i4 + e] = a[e] * st[4 * i4 + e] + kk[e] * uu;
+      for (int R = 0; R < NR; ++R)
+        a[R].v = *reinterpret_cast<const f32x4*>(sP + (16 * R + c16) * PS + 16 * T + 4 * g4);
+#pragma unroll
+      for (int C = 0; C < 2; ++C) {
+        Frag16<float> b;
+        b.v = st[T][C];
+#pragma unroll
+        for (int R = 0; R < NR; ++R) acc[R][C] = mma16(acc[R][C], a[R], b);
+      }
+      if ((T >> 1) == wv) {  // this wave's quarter of the Gram contraction
+        Frag16<float> b;
+        b.v = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (c16 < LP) b.v = *reinterpret_cast<const f32x4*>(sKh + c16 * PS + 16 * T + 4 * g4);
+#pragma unroll
+        for (int R = 0; R < NR; ++R) gacc[R] = mma16(gacc[R], a[R], b);
+      }
     }
-    if (wv == 0 && go) {
-      // lanes 32..63 hold the same columns as lanes 0..31
-      f32x4 oo = y + sc[2] * uu;
+    // rows 0..LP-1 of the block are X (K~ rows), LP..2LP-1 are Y (Q~ rows)
+#pragma unroll
+    for (int R = 0; R < NR; ++R)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * R + 4 * g4 + e;
+        float* dst = row < LP ? sX + row * D : sY + (row - LP) * D;
+        *reinterpret_cast<f32x2*>(dst + col0) = (f32x2){acc[R][0][e], acc[R][1][e]};
+        sGP[(wv * 2 * LP + row) * 16 + c16] = gacc[R][e];
+      }
+  }
+  __syncthreads();
+  for (int i = tid; i < 2 * LP * 16; i += kThreads)
+    sG[i] = sGP[i] + sGP[2 * LP * 16 + i] + sGP[4 * LP * 16 + i] + sGP[6 * LP * 16 + i];
+  __syncthreads();
+
+  // per column: u by forward substitution, then the outputs
+  E* go = static_cast<E*>(p.o);
+  const E* sV = reinterpret_cast<const E*>(smem + lay.RV);
+  const E* sGt = reinterpret_cast<const E*>(smem + lay.RG);
+  float* sU = sP;  // [LP][128]: the [K~; Q~] block is no longer read
+  float ov[LP];
+  if (tid < D) {
+    const int c = tid;
+    float uu[LP];
+#pragma unroll
+    for (int t = 0; t < LP; ++t) {
+      float s = 0.f;
+      if (t < nt) {
+        s = to_f32(sV[t * D + c]) - sX[t * D + c];
+#pragma unroll
+        for (int r = 0; r < t; ++r) s -= sG[t * 16 + r] * uu[r];
+        s *= sSC[4 * t + 3];
+      }
+      uu[t] = s;
+    }
+#pragma unroll
+    for (int t = 0; t < LP; ++t) sU[t * D + c] = uu[t];
+    if (go) {
+#pragma unroll
+      for (int t = 0; t < LP; ++t) {
+        float o = 0.f;
+        if (t < nt) {
+          o = sY[t * D + c];
+#pragma unroll
+          for (int r = 0; r <= t; ++r) o += sG[(LP + t) * 16 + r] * uu[r];
+        }
+        ov[t] = o;
+      }
       if (EPI) {
-        float ss = oo[0] * oo[0] + oo[1] * oo[1] + oo[2] * oo[2] + oo[3] * oo[3];
 #pragma unroll
-        for (int m = 16; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
-        const float inv = rsqrtf(ss * (1.f / D) + p.rms_eps);
+        for (int t = 0; t < LP; ++t) {
+          float ss = ov[t] * ov[t];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float gl = to_f32(sG[t * D + 4 * cg + e]);
-          oo[e] = oo[e] * inv * nw[e] / (1.f + __expf(-gl));
+          for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+          if (lane == 0) sSS[wv * LP + t] = ss;
         }
       }
-      if (rg == 0) store4<E>(go + ((size_t)(n * L + t) * H + h) * D + 4 * cg, oo);
+    }
+  }
+  __syncthreads();
+  if (tid < D && go) {
+    const int c = tid;
+    float nw = 1.f;
+    if (EPI && p.norm_w) nw = p.norm_w[c];
+#pragma unroll
+    for (int t = 0; t < LP; ++t) {
+      if (t < nt) {
+        float o = ov[t];
+        if (EPI) {
+          const float inv = rsqrtf((sSS[t] + sSS[LP + t]) * (1.f / D) + p.rms_eps);
+          o = o * inv * nw / (1.f + __expf(-to_f32(sGt[t * D + c])));
+        }
+        go[((size_t)(n * L + t) * H + h) * D + c] = from_f32<E>(o);
+      }
     }
   }
 
-  // ---- 4. commit ----
-  if (p.state_out) {
-    float* S = p.state_out + u * (D * D);
+  // ---- 4. commit: S = Diag(D_last) S0 + Kb^T U ----
+  // The contraction runs over the LP block rows, four per instruction: lane
+  // group g4 carries rows g4 + 4 jj.  Kb^T[i][t] = K^[t][i] D_last[i].
+  if (commit) {
+    constexpr int NJ = LP / 4;
+    float bu[2][NJ];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      __builtin_nontemporal_store(st[i], reinterpret_cast<f32x4*>(S + (16 * rg + i) * D + 4 * cg));
+    for (int jj = 0; jj < NJ; ++jj) {
+      const f32x2 x = *reinterpret_cast<const f32x2*>(sU + (g4 + 4 * jj) * D + col0);
+      bu[0][jj] = x[0];
+      bu[1][jj] = x[1];
+    }
+    float* S = p.state_out + u * (D * D) + col0;
+#pragma unroll
+    for (int T = 0; T < 8; ++T) {
+      const f32x4 gam = *reinterpret_cast<const f32x4*>(sGam + 16 * T + 4 * g4);
+      const float gi = sGam[16 * T + c16];
+      float a[NJ];
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) a[jj] = sKh[(g4 + 4 * jj) * PS + 16 * T + c16] * gi;
+#pragma unroll
+      for (int C = 0; C < 2; ++C) {
+        f32x4 acc = gam * st[T][C];
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[jj], bu[C][jj], acc, 0, 0, 0);
+        st[T][C] = acc;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        __builtin_nontemporal_store((f32x2){st[T][0][e], st[T][1][e]},
+                                    reinterpret_cast<f32x2*>(S + (16 * T + 4 * g4 + e) * D));
+    }
     if (conv) {
-      // raw rows nt-3 .. nt-1 are staged rows nt .. nt+2; only this thread read channel j of them
       E* hs = static_cast<E*>(isk ? p.conv_k_state : p.conv_q_state);
-      const E* rows = reinterpret_cast<const E*>(smem + (isk ? lay.RK : lay.RQ));
-#pragma unroll
-      for (int m = 0; m < 3; ++m) hs[((size_t)(n * 3 + m) * H + h) * D + j] = rows[(nt + m) * D + j];
+      const size_t hb = ((size_t)n * 3 * H + h) * D + j;
+      hs[hb] = from_f32<E>(x0);
+      hs[hb + (size_t)H * D] = from_f32<E>(x1);
+      hs[hb + (size_t)2 * H * D] = from_f32<E>(x2);
     }
   }
 }
 
-template <typename E, bool PRO, bool EPI>
+template <typename E, int LP, bool PRO, bool EPI>
 hipError_t launch_replay_t(const ReplayArgs& a, hipStream_t stream) {
-  const ReplayLayout lay(a.max_tokens, (int)sizeof(E), EPI);
-  auto fn = replay_kernel<E, PRO, EPI>;
+  const ReplayLayout lay(a.max_tokens, (int)sizeof(E), EPI, LP);
+  auto fn = replay_kernel<E, LP, PRO, EPI>;
   if (lay.BYTES > 64u * 1024u) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lay.BYTES);
@@ -338,13 +433,19 @@ hipError_t launch_replay_t(const ReplayArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename E, int LP>
+hipError_t launch_replay_lp(const ReplayArgs& a, hipStream_t stream) {
+  const bool pro = a.conv_q_w || a.conv_k_w, epi = a.gate != nullptr;
+  if (pro && epi) return launch_replay_t<E, LP, true, true>(a, stream);
+  if (pro) return launch_replay_t<E, LP, true, false>(a, stream);
+  if (epi) return launch_replay_t<E, LP, false, true>(a, stream);
+  return launch_replay_t<E, LP, false, false>(a, stream);
+}
+
 template <typename E>
 hipError_t launch_replay_e(const ReplayArgs& a, hipStream_t stream) {
-  const bool pro = a.conv_q_w || a.conv_k_w, epi = a.gate != nullptr;
-  if (pro && epi) return launch_replay_t<E, true, true>(a, stream);
-  if (pro) return launch_replay_t<E, true, false>(a, stream);
-  if (epi) return launch_replay_t<E, false, true>(a, stream);
-  return launch_replay_t<E, false, false>(a, stream);
+  if (a.max_tokens <= 8) return launch_replay_lp<E, 8>(a, stream);
+  return launch_replay_lp<E, 16>(a, stream);
 }
 
 }  // namespace
