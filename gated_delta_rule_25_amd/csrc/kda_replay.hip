@@ -79,6 +79,23 @@ struct ReplayLayout {
   }
 };
 
+// Sum over the 64 lanes of a wave, returned in every lane: prefix sums
+// within each 16-lane row (DPP row shifts), then row 0 into row 1 and row 2
+// into row 3 (row_bcast:15), then lane 31 into rows 2 and 3 (row_bcast:31);
+// lane 63 ends with the total.  Every lane of the wave must be active.
+__device__ __forceinline__ float wave_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+// 1 / (1 + e^-x) with the hardware reciprocal
+__device__ __forceinline__ float sigmoid_rcp(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+
 template <typename E>
 __device__ __forceinline__ float lds_elem(const unsigned char* base, int row, int j) {
   return to_f32(reinterpret_cast<const E*>(base)[row * D + j]);
@@ -151,6 +168,10 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
   }
   float bt = 0.f;
   if (tid < nt) bt = p.beta[((size_t)n * L + tid) * H + h];
+  // RMSNorm weight of column tid (read here so that the output stores at
+  // the end never wait behind a late load)
+  float nw = 1.f;
+  if (EPI && p.norm_w && tid < D) nw = p.norm_w[tid];
   // convolution taps of channel j of the branch this thread forms (q: threads 0..127, k: 128..255)
   const int j = tid & 127;
   const bool isk = tid >= 128;
@@ -213,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
       float s = x3;
       if (conv) {
         const float c = w4[0] * x0 + w4[1] * x1 + w4[2] * x2 + w4[3] * x3;
-        s = c / (1.f + __expf(-c));
+        s = c * sigmoid_rcp(c);
         x0 = x1;
         x1 = x2;
         x2 = x3;
@@ -227,12 +248,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
     for (int t = wv; t < nt; t += 4) {
       const float q0v = sX[t * D + lane], q1v = sX[t * D + 64 + lane];
       const float k0v = sY[t * D + lane], k1v = sY[t * D + 64 + lane];
-      float sq = q0v * q0v + q1v * q1v, sk = k0v * k0v + k1v * k1v;
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        sq += __shfl_xor(sq, m);
-        sk += __shfl_xor(sk, m);
-      }
+      const float sq = wave_sum(q0v * q0v + q1v * q1v), sk = wave_sum(k0v * k0v + k1v * k1v);
       if (lane == 0) {
         sSC[4 * t] = cq ? rsqrtf(sq + p.l2_eps) : 1.f;
         sSC[4 * t + 1] = ck ? rsqrtf(sk + p.l2_eps) : 1.f;
@@ -351,9 +367,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
       if (EPI) {
 #pragma unroll
         for (int t = 0; t < LP; ++t) {
-          float ss = ov[t] * ov[t];
-#pragma unroll
-          for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+          const float ss = wave_sum(ov[t] * ov[t]);
           if (lane == 0) sSS[wv * LP + t] = ss;
         }
       }
@@ -362,15 +376,13 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
   __syncthreads();
   if (tid < D && go) {
     const int c = tid;
-    float nw = 1.f;
-    if (EPI && p.norm_w) nw = p.norm_w[c];
 #pragma unroll
     for (int t = 0; t < LP; ++t) {
       if (t < nt) {
         float o = ov[t];
         if (EPI) {
           const float inv = rsqrtf((sSS[t] + sSS[LP + t]) * (1.f / D) + p.rms_eps);
-          o = o * inv * nw / (1.f + __expf(-to_f32(sGt[t * D + c])));
+          o = o * inv * nw * sigmoid_rcp(to_f32(sGt[t * D + c]));
         }
         go[((size_t)(n * L + t) * H + h) * D + c] = from_f32<E>(o);
       }
