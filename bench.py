@@ -92,8 +92,8 @@ def measured_traffic(kernel: str, workload: str):
     src = {"kda_chunk_fwd": ["kda_chunk.hip", "kda_prep.hip", "kda_chunk_util.h", "kda_device.h", "kda_internal.h",
                              "kda_api.hip"],
            "decode_kernel": ["kda_decode.hip", "kda_device.h", "kda_internal.h"],
-           "replay_verify": ["kda_replay.hip", "kda_device.h", "kda_internal.h"],
-           "replay_commit": ["kda_replay.hip", "kda_device.h", "kda_internal.h"]}[kernel]
+           "replay_verify": ["kda_replay.hip", "kda_chunk_util.h", "kda_device.h", "kda_internal.h"],
+           "replay_commit": ["kda_replay.hip", "kda_chunk_util.h", "kda_device.h", "kda_internal.h"]}[kernel]
     m = hashlib.sha256()
     for f in src:
         with open(os.path.join(ROOT, "gated_delta_rule_25_amd", "csrc", f), "rb") as fh:
