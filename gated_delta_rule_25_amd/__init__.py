@@ -20,6 +20,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["chunk_fwd", "decode_step", "decode_replay", "chunk_fwd_workspace_bytes", "status_string", "KDAError",
+           "last_precondition_flags",
            "library_path", "D", "REPLAY_MAX_TOKENS"]
 
 D = 128
@@ -28,7 +29,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda.so")
 _lib = None
 
-KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP, KDA_ERR_PRECONDITION = range(6)
+# KDA_DEBUG_CHECKS precondition bits (kda_last_precondition_flags)
+CHECK_LOG_ALPHA, CHECK_BETA, CHECK_Q_NORM, CHECK_K_NORM, CHECK_CU_SEQLENS = 1, 2, 4, 8, 16
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 
@@ -66,6 +69,8 @@ def _load():
                                   sz, vp]
     lib.kda_decode_step.restype = i32
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    lib.kda_last_precondition_flags.restype = ctypes.c_uint32
+    lib.kda_last_precondition_flags.argtypes = []
     lib.kda_decode_replay.restype = i32
     lib.kda_decode_replay.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp,
                                       vp, vp]
@@ -75,6 +80,12 @@ def _load():
 
 def status_string(code: int) -> str:
     return _load().kda_status_string(int(code)).decode()
+
+
+def last_precondition_flags() -> int:
+    """CHECK_* bits that failed in this thread's last call made with the
+    environment variable KDA_DEBUG_CHECKS set (0 when all passed)."""
+    return int(_load().kda_last_precondition_flags())
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -167,6 +167,24 @@ Plan make_plan(int num_seqs, int64_t total_tokens, int num_heads, kda_dtype dtyp
 
 const kda_fused_opts kNoOpts = {nullptr, nullptr, nullptr, nullptr, 1e-6f, 1e-6f, 0};
 
+// Optional precondition checks: the environment variable KDA_DEBUG_CHECKS
+// (read at every call) switches them on; the failed checks of the calling
+// thread's last checked call are kept for kda_last_precondition_flags().
+bool debug_checks() {
+  const char* e = std::getenv("KDA_DEBUG_CHECKS");
+  return e && *e && std::strcmp(e, "0") != 0;
+}
+thread_local uint32_t t_check_flags = 0;
+
+// Runs the checks when they are on: KDA_OK to go ahead, otherwise the status to return.
+kda_status checked(const kda::CheckArgs& a, hipStream_t stream) {
+  if (!debug_checks()) return KDA_OK;
+  uint32_t flags = 0;
+  if (kda::run_checks(a, stream, &flags) != hipSuccess) return KDA_ERR_HIP;
+  t_check_flags = flags;
+  return flags ? KDA_ERR_PRECONDITION : KDA_OK;
+}
+
 bool sizes_ok(int num_seqs, int64_t total_tokens, int num_heads) {
   return num_seqs >= 1 && num_heads >= 1 && total_tokens >= 0 &&
          (int64_t)num_seqs * num_heads <= (int64_t)INT32_MAX / 2 && total_tokens <= (int64_t)INT32_MAX;
@@ -191,9 +209,13 @@ const char* kda_status_string(kda_status s) {
     case KDA_ERR_UNSUPPORTED: return "unsupported configuration (d_k and d_v must be 128; dtype f32 or bf16)";
     case KDA_ERR_WORKSPACE: return "workspace missing or smaller than kda_chunk_fwd_workspace_bytes()";
     case KDA_ERR_HIP: return "HIP runtime or launch error";
+    case KDA_ERR_PRECONDITION:
+      return "input outside the documented preconditions (KDA_DEBUG_CHECKS; see kda_last_precondition_flags())";
   }
   return "unknown kda_status";
 }
+
+uint32_t kda_last_precondition_flags(void) { return t_check_flags; }
 
 size_t kda_chunk_fwd_workspace_bytes(int num_seqs, int64_t total_tokens, int num_heads, int d_k, int d_v,
                                      kda_dtype dtype, const kda_fused_opts* opts) {
@@ -255,6 +277,23 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   if (overlap(r_o, r_fs) || overlap(r_o, r_ws) || overlap(r_fs, r_ws)) return KDA_ERR_INVALID_ARG;
 
   const bool bf16 = dtype == KDA_DTYPE_BF16;
+  {
+    kda::CheckArgs chk;
+    std::memset(&chk, 0, sizeof(chk));
+    chk.rows = total_tokens * num_heads;
+    chk.heads = num_heads;
+    chk.tokens_per_seq = 1;
+    chk.log_alpha = log_alpha;
+    chk.beta = beta;
+    chk.q = f.conv_q_w ? nullptr : q;
+    chk.k = f.conv_k_w ? nullptr : k;
+    chk.cu = cu_seqlens;
+    chk.num_seqs = num_seqs;
+    chk.total_tokens = total_tokens;
+    chk.bf16 = bf16;
+    const kda_status cs = checked(chk, stream);
+    if (cs != KDA_OK) return cs;
+  }
   char* ws = static_cast<char*>(workspace);
   int32_t* order = num_seqs > 1 ? reinterpret_cast<int32_t*>(ws) : nullptr;
   int32_t* seq_first = reinterpret_cast<int32_t*>(ws + pl.off_first);
@@ -392,6 +431,20 @@ kda_status kda_decode_step(float* state, const void* q, const void* k, const voi
   for (const Range& in : inputs)
     if (overlap(r_o, in) || overlap(r_s, in)) return KDA_ERR_INVALID_ARG;
   if (overlap(r_o, r_s)) return KDA_ERR_INVALID_ARG;
+  {
+    kda::CheckArgs chk;
+    std::memset(&chk, 0, sizeof(chk));
+    chk.rows = units;
+    chk.heads = num_heads;
+    chk.tokens_per_seq = 1;
+    chk.log_alpha = log_alpha;
+    chk.beta = beta;
+    chk.q = q;
+    chk.k = k;
+    chk.bf16 = dtype == KDA_DTYPE_BF16;
+    const kda_status cs = checked(chk, stream);
+    if (cs != KDA_OK) return cs;
+  }
 
   kda::DecodeArgs a;
   a.state = state;
@@ -459,6 +512,21 @@ kda_status kda_decode_replay(const float* state_in, float* state_out, const void
   if (overlap(r_o, r_s1) || overlap(r_o, r_hq) || overlap(r_o, r_hk) || overlap(r_s1, r_hq) ||
       overlap(r_s1, r_hk) || overlap(r_hq, r_hk))
     return KDA_ERR_INVALID_ARG;
+  {
+    kda::CheckArgs chk;
+    std::memset(&chk, 0, sizeof(chk));
+    chk.rows = units * max_tokens;
+    chk.heads = num_heads;
+    chk.tokens_per_seq = max_tokens;
+    chk.counts = num_tokens;
+    chk.log_alpha = log_alpha;
+    chk.beta = beta;
+    chk.q = f.conv_q_w ? nullptr : q;
+    chk.k = f.conv_k_w ? nullptr : k;
+    chk.bf16 = dtype == KDA_DTYPE_BF16;
+    const kda_status cs = checked(chk, stream);
+    if (cs != KDA_OK) return cs;
+  }
 
   kda::ReplayArgs a;
   std::memset(&a, 0, sizeof(a));

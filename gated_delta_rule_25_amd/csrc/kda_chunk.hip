@@ -77,7 +77,9 @@ __global__ __launch_bounds__(1024) void window_table_kernel(const int32_t* __res
     const int n = base + tid;
     int len = 0, c0 = 0;
     if (n < N) {
-      const int64_t L = cu ? (int64_t)cu[n + 1] - (int64_t)cu[n] : T;
+      int64_t bos, eos;
+      seq_range(cu, n, T, bos, eos);
+      const int64_t L = eos - bos;
       const int64_t G = L > 0 ? (L + C - 1) / C : 0;
       const int64_t Q = (G + nw - 1) / nw;
       const int64_t a = min((int64_t)w * Q, G), b = min(a + Q, G);
@@ -250,8 +252,8 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
                     : PASS == 2 ? p.pairs + pair_base : nullptr;
   float* s_out = PASS == 0 ? (p.state_out ? p.state_out + ((size_t)n * H + h) * (size_t)(D * D) : nullptr)
                : PASS == 1 ? p.pairs + pair_base + (mpart ? (size_t)(D * D) : 0) : nullptr;
-  const int64_t seq_bos = p.cu ? (int64_t)p.cu[n] : 0;
-  const int64_t seq_eos = p.cu ? (int64_t)p.cu[n + 1] : p.total_tokens;
+  int64_t seq_bos, seq_eos;
+  seq_range(p.cu, n, p.total_tokens, seq_bos, seq_eos);
   const int64_t rs = (int64_t)H * D;
   const int64_t hoff = (int64_t)h * D;
   const char* fbase = static_cast<const char*>(p.factors);

@@ -43,6 +43,22 @@ struct ReplayArgs {
   bool bf16;
 };
 
+// Inputs of the optional precondition checks (kda_debug.hip).
+struct CheckArgs {
+  int64_t rows;              // (token, head) rows of log_alpha / beta / q / k
+  int heads;                 // H
+  int tokens_per_seq;        // L for [N, L, H] inputs with counts, else 1
+  const int32_t* counts;     // [N] rows t >= counts[n] are not checked, or null
+  const float* log_alpha;    // [rows, 128]
+  const float* beta;         // [rows]
+  const void* q;             // [rows, 128] or null (not checked)
+  const void* k;
+  const int32_t* cu;         // [N+1] or null
+  int num_seqs;
+  int64_t total_tokens;
+  bool bf16;
+};
+
 struct ScanArgs {
   float* pairs;             // [seg][H][2][128][128]: B_j (overwritten by S_in(j)), then M_j
   const int32_t* seq_first; // [N+1]: first segment of each sequence (exclusive prefix sum)
@@ -102,6 +118,20 @@ struct FactorBlock {
   static constexpr uint32_t BYTES = (U + NT * 8 * UT + 255) & ~255u;
 };
 constexpr int chunk_len(bool bf16) { return bf16 ? 64 : 32; }
+
+// Token range [bos, eos) of sequence n (all T tokens without cu_seqlens),
+// clamped into [0, T] with eos >= bos: cu_seqlens outside its preconditions
+// then gives wrong results but never addresses a token outside the inputs.
+__device__ __forceinline__ void seq_range(const int32_t* cu, int n, int64_t T, int64_t& bos, int64_t& eos) {
+  if (!cu) {
+    bos = 0;
+    eos = T;
+    return;
+  }
+  const int64_t a = cu[n], b = cu[n + 1];
+  bos = a < 0 ? 0 : (a > T ? T : a);
+  eos = b < bos ? bos : (b > T ? T : b);
+}
 constexpr size_t factor_block_bytes(bool bf16) {
   return bf16 ? FactorBlock<2, 64>::BYTES : FactorBlock<4, 32>::BYTES;
 }
@@ -179,6 +209,8 @@ hipError_t launch_carry(const CarryArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 constexpr int kReplayMaxTokens = 16;
 hipError_t launch_replay(const ReplayArgs& a, hipStream_t stream);
+// Runs the checks on `stream`, waits, and returns the KDA_CHECK_* bits that failed.
+hipError_t run_checks(const CheckArgs& a, hipStream_t stream, uint32_t* flags);
 // Longest-first ordering of the packed sequences (device-side, no host sync).
 hipError_t launch_worklist(const int32_t* cu, int num_seqs, int32_t* order, hipStream_t stream);
 // Segment table: per-sequence segment counts, their exclusive prefix sum

@@ -315,8 +315,8 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
       if (p.seq_first[mid] <= s) n = mid;
       else hi = mid;
     }
-    const int64_t bos = p.cu ? (int64_t)p.cu[n] : 0;
-    const int64_t eos = p.cu ? (int64_t)p.cu[n + 1] : p.total_tokens;
+    int64_t bos, eos;
+    seq_range(p.cu, n, p.total_tokens, bos, eos);
     const int64_t t0 = bos + (int64_t)(p.seq_c0[n] + (s - p.seq_first[n])) * C;
     sRng[3 * tid] = t0;
     sRng[3 * tid + 1] = bos;

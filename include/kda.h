@@ -52,8 +52,25 @@ typedef enum {
   KDA_ERR_INVALID_ARG = 1, /* NULL where required, bad sizes, illegal overlap */
   KDA_ERR_UNSUPPORTED = 2, /* d_k or d_v other than 128, unknown dtype       */
   KDA_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required        */
-  KDA_ERR_HIP = 4          /* a HIP launch or runtime call failed            */
+  KDA_ERR_HIP = 4,         /* a HIP launch or runtime call failed            */
+  KDA_ERR_PRECONDITION = 5 /* an input outside the preconditions (only with KDA_DEBUG_CHECKS) */
 } kda_status;
+
+/*
+ * Precondition checks.  With the environment variable KDA_DEBUG_CHECKS set to
+ * anything but "" or "0" (read at every call), each compute entry point first
+ * checks the preconditions listed above on the device, waits for the result
+ * (a host synchronisation of `stream`, so not under graph capture) and, when
+ * one fails, returns KDA_ERR_PRECONDITION without launching its kernels.
+ * kda_last_precondition_flags() then gives the failed checks:
+ */
+enum {
+  KDA_CHECK_LOG_ALPHA = 1,  /* a log_alpha value outside [-5, 0] or not finite          */
+  KDA_CHECK_BETA = 2,       /* a beta value outside [0, 1] or not finite               */
+  KDA_CHECK_Q_NORM = 4,     /* a q row (no prologue on q) whose norm is not 1 +- 0.02   */
+  KDA_CHECK_K_NORM = 8,     /* a k row (no prologue on k) whose norm is not 1 +- 0.02   */
+  KDA_CHECK_CU_SEQLENS = 16 /* cu_seqlens not non-decreasing from 0 to total_tokens    */
+};
 
 typedef enum {
   KDA_DTYPE_F32 = 0,  /* q, k, v, gate and o are float                      */
@@ -207,6 +224,9 @@ kda_status kda_decode_replay(const float* state_in, float* state_out, const void
                              const int32_t* num_tokens, int num_seqs, int max_tokens, int num_heads,
                              int d_k, int d_v, kda_dtype dtype, const kda_fused_opts* opts,
                              void* conv_q_state, void* conv_k_state, void* o, hipStream_t stream);
+
+/* KDA_CHECK_* bits of the last checked call on the calling thread (0 when it passed). */
+uint32_t kda_last_precondition_flags(void);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* kda_status_string(kda_status s);

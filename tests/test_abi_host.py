@@ -53,7 +53,7 @@ def declared_functions():
 def test_header_symbols_exported(lib):
     names = declared_functions()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_decode_step",
-                          "kda_decode_replay", "kda_status_string"}
+                          "kda_decode_replay", "kda_last_precondition_flags", "kda_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s+(kda_\w+)", out))
     for n in names:
@@ -62,7 +62,7 @@ def test_header_symbols_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         s = lib.kda_status_string(code).decode()
         assert s and s != "unknown kda_status"
     assert lib.kda_status_string(99).decode() == "unknown kda_status"
@@ -262,6 +262,13 @@ def test_replay_validation(lib):
     assert replay(lib, opts=opts_p(neg)) == INVALID          # negative epsilon
     # nothing to produce: accepted without launching anything
     assert replay(lib, s1=None, o=None) == OK
+
+
+def test_precondition_flags_start_clear(lib):
+    L = ctypes.CDLL(LIB)
+    L.kda_last_precondition_flags.restype = ctypes.c_uint32
+    assert L.kda_last_precondition_flags() == 0
+    assert "KDA_DEBUG_CHECKS" in lib.kda_status_string(5).decode()
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
