@@ -50,6 +50,7 @@ PREFILL_CASES = [
     ("bf16_T1000", 4, [1000], "bf16", 0.02),
     ("bf16_varlen_empty_ones", 5, [0, 1, 130, 0, 77, 2], "bf16", 0.5),
     ("bf16_many_units_nosplit", 96, [40, 70, 3], "bf16", 0.02),
+    ("bf16_H1_T200", 1, [200], "bf16", 0.02),
 ]
 
 
@@ -62,6 +63,20 @@ def test_prefill_parity(name, H, lengths, dtype, s0):
     eo, es = compare_prefill(inp, o, fs, heads=heads)
     say("  err_o %.3e err_state %.3e" % (eo, es))
     assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
+
+
+def test_more_than_1024_sequences():
+    """1100 short sequences (lengths 0..40, some empty): the work-list order and
+    the window table's prefix sum run over more than one 1024-thread block,
+    with the fused prologue and epilogue."""
+    rng = np.random.Generator(np.random.Philox(1100))
+    lengths = [int(x) for x in rng.integers(0, 41, size=1100)]
+    say("case 1100 sequences, T=%d" % sum(lengths))
+    inp = kda_inputs.make_prefill(2, lengths, "bf16", 0.0, True, DEV, seed=1100)
+    o, fs = run_prefill(inp)
+    eo, es = compare_prefill(inp, o, fs)
+    say("  err_o %.3e err_state %.3e" % (eo, es))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
