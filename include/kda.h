@@ -62,7 +62,9 @@ typedef enum {
  * checks the preconditions listed above on the device, waits for the result
  * (a host synchronisation of `stream`, so not under graph capture) and, when
  * one fails, returns KDA_ERR_PRECONDITION without launching its kernels.
- * kda_last_precondition_flags() then gives the failed checks:
+ * kda_last_precondition_flags() then gives the failed checks.  The checks
+ * of all calls on a device share one device word, so checked calls must not
+ * run concurrently on different streams.
  */
 enum {
   KDA_CHECK_LOG_ALPHA = 1,  /* a log_alpha value outside [-5, 0] or not finite          */

@@ -1,11 +1,12 @@
-"""The compute entry points under HIP graph capture.
+"""The compute entry points under HIP graph capture and on concurrent streams.
 
 Every compute path of the library only launches kernels on the caller's
 stream (no memsets, copies or host waits), so a serving loop can capture it
-once and replay it.  Each case captures one call, then replays the graph
-several times with eager work and synchronisations in between, and checks
-every replay bit for bit against the same call run eagerly (the kernels are
-deterministic).
+once and replay it.  Each graph case captures one call, then replays the
+graph several times with eager work and synchronisations in between, and
+checks every replay bit for bit against the same call run eagerly (the
+kernels are deterministic).  The last case runs calls on three streams at
+once: the library keeps no state between calls.
 """
 import sys
 
@@ -114,3 +115,35 @@ def test_decode_replay_graph():
         assert torch.equal(o_g, o_e), i
         assert torch.equal(st_g, st_e), i
         assert torch.equal(hq_g, hq_e) and torch.equal(hk_g, hk_e), i
+
+
+def test_concurrent_streams():
+    """Two prefill calls with their own workspaces on two streams (default
+    priority) at once, plus a replay on a third: the library keeps no state
+    between calls, so each matches the same call run alone."""
+    say("case two streams")
+    a = kda_inputs.make_prefill(4, [500, 200], "bf16", 0.02, False, DEV, seed=94)
+    b = kda_inputs.make_prefill(3, [700], "bf16", 0.02, True, DEV, seed=95)
+    r = kda_inputs.make_replay(4, 2, 8, "bf16", 0.02, True, DEV, seed=96)
+    kw_b = dict(conv_q_w=b["conv_q_w"], conv_k_w=b["conv_k_w"], gate=b["gate"])
+    kw_r = dict(conv_q_w=r["conv_q_w"], conv_k_w=r["conv_k_w"], gate=r["gate"], conv_q_state=r["conv_q_state"],
+                conv_k_state=r["conv_k_state"])
+    ref_a = kda.chunk_fwd(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["initial_state"], a["cu_seqlens"])
+    ref_b = kda.chunk_fwd(b["q"], b["k"], b["v"], b["log_alpha"], b["beta"], **kw_b)
+    ref_r, _ = kda.decode_replay(r["state"], r["q"], r["k"], r["v"], r["log_alpha"], r["beta"], **kw_r)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        with torch.cuda.stream(streams[0]):
+            out_a = kda.chunk_fwd(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["initial_state"],
+                                  a["cu_seqlens"])
+        with torch.cuda.stream(streams[1]):
+            out_b = kda.chunk_fwd(b["q"], b["k"], b["v"], b["log_alpha"], b["beta"], **kw_b)
+        with torch.cuda.stream(streams[2]):
+            out_r, _ = kda.decode_replay(r["state"], r["q"], r["k"], r["v"], r["log_alpha"], r["beta"], **kw_r)
+        torch.cuda.synchronize()
+        assert torch.equal(out_a[0], ref_a[0]) and torch.equal(out_a[1], ref_a[1])
+        assert torch.equal(out_b[0], ref_b[0]) and torch.equal(out_b[1], ref_b[1])
+        assert torch.equal(out_r, ref_r)
