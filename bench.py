@@ -127,13 +127,13 @@ def cpu_baseline(inp, budget_s=20.0):
     def f64(t):
         return t.detach().float().cpu().double().numpy()
 
-    def run(nh):
+    def run(nh, nthreads=threads):
         hs = slice(0, nh)
         q, k, v = f64(inp["q"][:, hs]), f64(inp["k"][:, hs]), f64(inp["v"][:, hs])
         la, b = f64(inp["log_alpha"][:, hs]), f64(inp["beta"][:, hs])
         s0 = None if inp["initial_state"] is None else f64(inp["initial_state"][:, hs])
         t0 = time.perf_counter()
-        oracle.chunk_fwd(q, k, v, la, b, initial_state=s0, threads=threads)
+        oracle.chunk_fwd(q, k, v, la, b, initial_state=s0, threads=nthreads)
         return time.perf_counter() - t0
 
     nh = max(1, min(H, 2 * threads))
@@ -150,7 +150,12 @@ def cpu_baseline(inp, budget_s=20.0):
     used = min(threads, nh)
     what = ("the whole layer, %d heads x %d tokens (%.1f s)" % (H, T, dt) if nh == H else
             "%d of %d heads x %d tokens (%.1f s), scaled to the full %d-head layer" % (nh, H, T, dt, H))
-    return {"value": rate, "unit": "tokens/s", "cores": used, "kind": "oracle", "sample": "fp64 oracle on " + what}
+    # one thread on one head, extrapolated to the layer
+    dt1 = run(1, 1)
+    single = {"value": T / H / dt1, "unit": "tokens/s", "cores": 1,
+              "sample": "1 head x %d tokens on one thread (%.2f s), extrapolated to the %d-head layer" % (T, dt1, H)}
+    return {"value": rate, "unit": "tokens/s", "cores": used, "kind": "oracle", "sample": "fp64 oracle on " + what,
+            "single_thread": single}
 
 
 def time_prefill(kda, kda_inputs, wid, steps, warmup, dev, stream, inp=None, **call_kw):

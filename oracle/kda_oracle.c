@@ -44,6 +44,17 @@
 #include <omp.h>
 #endif
 
+/* Threads of one parallel region: num_threads if positive, else the OpenMP
+ * default (set per region, so a call never changes the default of the next). */
+static int team_size(int num_threads) {
+#ifdef _OPENMP
+  return num_threads > 0 ? num_threads : omp_get_max_threads();
+#else
+  (void)num_threads;
+  return 1;
+#endif
+}
+
 /* One token of the recurrence on a dk x dv state S (row-major). */
 static void kda_token(double* S, int dk, int dv, const double* q, const double* k, const double* v,
                       const double* log_alpha, double beta, double* vhat, double* o) {
@@ -111,13 +122,10 @@ int kda_oracle_chunk_fwd(const double* q, const double* k, const double* v, cons
   if (num_seqs < 1 || H < 1 || dk < 1 || dv < 1 || total_tokens < 0) return 1;
   if (!cu_seqlens && num_seqs != 1) return 1;
   const int64_t units = (int64_t)num_seqs * H;
-#ifdef _OPENMP
-  if (num_threads > 0) omp_set_num_threads(num_threads);
-#else
-  (void)num_threads;
-#endif
+  const int nth = team_size(num_threads);
+  (void)nth; /* used by the parallel-for clause */
   int err = 0;
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nth)
   for (int64_t u = 0; u < units; ++u) {
     const int n = (int)(u / H), h = (int)(u % H);
     const int64_t bos = cu_seqlens ? cu_seqlens[n] : 0;
@@ -158,13 +166,10 @@ int kda_oracle_decode_step(double* state, const double* q, const double* k, cons
                            int dv, double* o, int num_threads) {
   if (num_seqs < 1 || H < 1 || dk < 1 || dv < 1) return 1;
   const int64_t units = (int64_t)num_seqs * H;
-#ifdef _OPENMP
-  if (num_threads > 0) omp_set_num_threads(num_threads);
-#else
-  (void)num_threads;
-#endif
+  const int nth = team_size(num_threads);
+  (void)nth; /* used by the parallel-for clause */
   int err = 0;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) num_threads(nth)
   for (int64_t u = 0; u < units; ++u) {
     double* tmp = (double*)malloc(sizeof(double) * (size_t)dv);
     if (!tmp) {
@@ -210,13 +215,10 @@ int kda_oracle_decode_multi(const double* state_in, const double* q, const doubl
                             double* conv_q_out, double* conv_k_out, int num_threads) {
   if (num_seqs < 1 || L < 1 || H < 1 || dk < 1 || dv < 1) return 1;
   const int64_t units = (int64_t)num_seqs * H;
-#ifdef _OPENMP
-  if (num_threads > 0) omp_set_num_threads(num_threads);
-#else
-  (void)num_threads;
-#endif
+  const int nth = team_size(num_threads);
+  (void)nth; /* used by the parallel-for clause */
   int err = 0;
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nth)
   for (int64_t u = 0; u < units; ++u) {
     const int n = (int)(u / H), h = (int)(u % H);
     int nt = L;
