@@ -247,3 +247,29 @@ def test_replay_errors():
                           conv_q_w=inp["conv_q_w"])
     with pytest.raises(kda.KDAError):  # output aliases v
         kda.decode_replay(inp["state"], inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], out=inp["v"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_replay_decay_at_the_bound(dtype):
+    """log_alpha = -5 on every channel of 16 tokens: the block's decay factors
+    reach e^{+-80}, the range the lower-bounded decay guarantees ("Kimi K3
+    架构…" section 4.2.5).  The result stays finite and within tolerance."""
+    say("case replay worst decay L=16 %s" % dtype)
+    r = kda_inputs.make_replay(2, 2, 16, dtype, 0.5, True, DEV, seed=101)
+    r["log_alpha"].fill_(-5.0)
+    res = run_lib(r, None, True)
+    assert torch.isfinite(res[1]).all() and torch.isfinite(res[0]).all()
+    compare(r, None, res, run_oracle(r, None), True, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_replay_no_decay_and_beta_extremes(dtype):
+    """No decay (log_alpha = 0) with beta alternating between 0 and 1."""
+    say("case replay no decay, beta 0/1 %s" % dtype)
+    r = kda_inputs.make_replay(3, 2, 8, dtype, 0.5, False, DEV, seed=102)
+    r["log_alpha"].zero_()
+    r["beta"].copy_((torch.arange(8, device=DEV) % 2).float().view(1, 8, 1).expand(3, 8, 2))
+    counts = [8, 5, 1]
+    nt = torch.tensor(counts, dtype=torch.int32, device=DEV)
+    res = run_lib(r, nt, True)
+    compare(r, counts, res, run_oracle(r, counts), True, dtype)
