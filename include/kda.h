@@ -19,9 +19,10 @@
  *     them alive until the work enqueued on `stream` has completed.  The
  *     library never allocates device memory.
  *   - Alignment: q, k, v, log_alpha, gate, o, the state tensors and the
- *     workspace of kda_chunk_fwd, and the state of kda_decode_step, must be
- *     16-byte aligned (they move as 16-byte vectors); every other pointer
- *     needs its element's alignment.  Violations return KDA_ERR_INVALID_ARG.
+ *     workspace of kda_chunk_fwd, the state of kda_decode_step, and the
+ *     tensors of kda_decode_replay listed with it, must be 16-byte aligned
+ *     (they move as 16-byte vectors); every other pointer needs its
+ *     element's alignment.  Violations return KDA_ERR_INVALID_ARG.
  *   - Layouts are dense row-major, token-major: q/k/v/log_alpha/o are
  *     [T_total, H, 128]; beta is [T_total, H]; states are [N, H, 128, 128]
  *     fp32 with S[n][h][i][j], i = key channel (row), j = value channel.
@@ -29,7 +30,8 @@
  *   - Work is asynchronous on `stream` (0 = the null stream); no host sync.
  *     Argument errors are detected on the host and returned before anything
  *     is enqueued.  A failed launch returns KDA_ERR_HIP.
- *   - Preconditions that are documented but not checked: log_alpha in
+ *   - Preconditions that the fast path does not check (KDA_DEBUG_CHECKS
+ *     below checks them on request): log_alpha in
  *     [-5, 0] (the lower-bounded decay of "Kimi K3 架构…" section 4.2.5,
  *     gate_lower_bound = -5 of section 2.1); beta in [0, 1]; ||q||, ||k||
  *     about 1 per head when no prologue runs; cu_seqlens non-decreasing from
