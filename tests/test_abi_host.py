@@ -306,3 +306,19 @@ def test_varlen_lengths_loguniform():
     assert L == kda_inputs.workload_lengths(4)
     s = sum(L)
     assert 0.5e6 < s < 1.6e6
+
+
+def test_c_consumer_compiles_as_c99(lib, tmp_path):
+    """include/kda.h is valid C99: the plain C test program that calls every
+    compute entry point compiles with gcc -std=c99 -Wall -Wextra -Werror and
+    links against libkda.so and the HIP runtime (it is not run here)."""
+    import sys
+    sys.path.insert(0, os.path.join(ROOT, "tests", "c_abi"))
+    import build_abi_check
+    out = str(tmp_path / "abi_check")
+    try:
+        build_abi_check.build(out)
+    except subprocess.CalledProcessError as e:
+        pytest.fail("gcc failed:\n" + e.stderr)
+    dyn = subprocess.run(["readelf", "-d", out], check=True, capture_output=True, text=True).stdout
+    assert "libkda.so" in dyn and "libamdhip64" in dyn
