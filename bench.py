@@ -2,7 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 1]
                     [--no-decode] [--no-cpu-baseline] [--decode-steps 64]
-                    [--extra-workloads 2,4,5] [--extra-steps 3]
+                    [--extra-workloads 2,4,5,7] [--extra-steps 3]
                     [--no-replay] [--replay-rounds 16]
 
 A step is one kda_chunk_fwd over one layer of the workload (all heads, all
@@ -10,8 +10,10 @@ tokens, inputs already resident in HBM): by default the one-layer K3 shape
 H=96, d=128, T=8192 with a carried fp32 state.  `value` is prefill tokens/s.
 The decode workload (256 sequences x 96 heads, 64 in-place kda_decode_step
 calls) is timed after it and reported under "decode"; the long-context (T=131072),
-the varlen fused prologue/epilogue and the few-head (H=8, T=131072, segmented
-schedule) workloads are timed with fewer steps and reported under "workloads".
+the varlen fused prologue/epilogue, the few-head (H=8, T=131072, segmented
+schedule) and the unbounded-decay (the one-layer shape with Kimi Linear's
+negative-softplus decay, per-position diagonal tiles) workloads are timed with
+fewer steps and reported under "workloads".
 The speculative-decoding replay (the same 256 x 96 batch with 8 cached tokens
 per sequence: a verification pass over all of them, then the in-place commit
 of the drawn accepted counts, both kda_decode_replay with the fused
@@ -89,8 +91,8 @@ def measured_traffic(kernel: str, workload: str):
     rec = json.load(open(path)).get(kernel)
     if rec is None or rec.get("workload") != workload:
         return None
-    src = {"kda_chunk_fwd": ["kda_chunk.hip", "kda_prep.hip", "kda_chunk_util.h", "kda_device.h", "kda_internal.h",
-                             "kda_api.hip"],
+    chunk_src = ["kda_chunk.hip", "kda_prep.hip", "kda_chunk_util.h", "kda_device.h", "kda_internal.h", "kda_api.hip"]
+    src = {"kda_chunk_fwd": chunk_src, "kda_chunk_fwd_unbounded": chunk_src,
            "decode_kernel": ["kda_decode.hip", "kda_device.h", "kda_internal.h"],
            "replay_verify": ["kda_replay.hip", "kda_chunk_util.h", "kda_device.h", "kda_internal.h"],
            "replay_commit": ["kda_replay.hip", "kda_chunk_util.h", "kda_device.h", "kda_internal.h"]}[kernel]
@@ -172,6 +174,9 @@ def time_prefill(kda, kda_inputs, wid, steps, warmup, dev, stream, inp=None, **c
     for key in ("conv_q_w", "conv_k_w", "gate", "norm_w"):
         if inp.get(key) is not None:
             kw[key] = inp[key]
+    unbounded = w.get("decay", "bounded") == "softplus"
+    if unbounded:
+        kw["unbounded_decay"] = True
     kw.update(call_kw)
     o = torch.empty_like(inp["v"])
     fs = torch.empty((N, H, 128, 128), dtype=torch.float32, device=dev)
@@ -209,9 +214,12 @@ def time_prefill(kda, kda_inputs, wid, steps, warmup, dev, stream, inp=None, **c
         "steps": steps,
         "dtype": w["dtype"],
         "config": {"workload": w["name"], "N": N, "H": H, "T": T, "d": 128, "chunk": 64 if es == 2 else 32,
-                   "fused_prologue_epilogue": bool(w["fused"])},
+                   "fused_prologue_epilogue": bool(w["fused"]),
+                   "decay": ("unbounded negative softplus: per-position diagonal tiles" if unbounded
+                             else "bounded [-5, 0]: dense tiles")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic("kda_chunk_fwd", w["name"]),
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic("kda_chunk_fwd_unbounded" if unbounded else "kda_chunk_fwd",
+                                                                w["name"]),
                      "kernel": "kda_chunk_fwd = window_table_kernel + prep_kernel + carry_kernel",
                      "kernel_ms_avg": ms_avg, "algorithmic_bytes": algo},
         "mfma": {"algorithmic_flops": flops, "chunk": C, "achieved_tflops": tflops, "peak_tflops": mfma_peak,
@@ -225,9 +233,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 4, 5])
+    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 4, 5, 7])
     ap.add_argument("--decode-steps", type=int, default=64)
-    ap.add_argument("--extra-workloads", default="2,4,5",
+    ap.add_argument("--extra-workloads", default="2,4,5,7",
                     help="other prefill workloads timed after the main one and reported under 'workloads' ('' = none)")
     ap.add_argument("--extra-steps", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
@@ -304,7 +312,10 @@ def main():
         for wid in extra:
             if wid == args.workload:
                 continue
-            inp, tm = time_prefill(kda, kda_inputs, wid, args.extra_steps, 1, dev, stream)
+            # one-layer shapes are short: more steps for the same GPU time
+            short = kda_inputs.WORKLOADS[wid]["lengths"] == [8192]
+            inp, tm = time_prefill(kda, kda_inputs, wid, max(args.extra_steps, 10) if short else args.extra_steps,
+                                   3 if short else 1, dev, stream)
             if wid == 5:
                 # the same call forced onto the sequential schedule, for comparison
                 _, seq = time_prefill(kda, kda_inputs, wid, args.extra_steps, 1, dev, stream, inp=inp,

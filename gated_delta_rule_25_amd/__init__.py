@@ -44,7 +44,7 @@ class KDAError(RuntimeError):
 class _FusedOpts(ctypes.Structure):
     _fields_ = [("conv_q_w", ctypes.c_void_p), ("conv_k_w", ctypes.c_void_p), ("gate", ctypes.c_void_p),
                 ("norm_w", ctypes.c_void_p), ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float),
-                ("segment_tokens", ctypes.c_int)]
+                ("segment_tokens", ctypes.c_int), ("unbounded_decay", ctypes.c_int)]
 
 
 def library_path() -> str:
@@ -129,7 +129,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
               l2_eps: float = 1e-6, rms_eps: float = 1e-6, out: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
               workspace: Optional[torch.Tensor] = None,
-              segment_tokens: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              segment_tokens: int = 0, unbounded_decay: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """KDA prefill over a packed batch (kda_chunk_fwd).
 
     q, k, v: [T, H, 128] float32 or bfloat16; log_alpha [T, H, 128] float32;
@@ -139,8 +139,10 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
     norm_w [128] float32).  segment_tokens: 0 lets the library choose between
     the sequential and the segmented schedule, a positive multiple of 64
     forces segments of that length, a negative value keeps the sequential
-    one.  Returns (o, final_state); final_state may be the same tensor as
-    initial_state (in-place continuation).
+    one.  unbounded_decay: accept any log_alpha <= 0 (the negative-softplus
+    decay) instead of the bound [-5, 0]; the diagonal tiles then run position
+    pair by position pair.  Returns (o, final_state); final_state may be the
+    same tensor as initial_state (in-place continuation).
     """
     lib = _load()
     if q.dim() != 3 or q.shape[2] != D:
@@ -182,9 +184,9 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
         _check(final_state, "final_state", (N, H, D, D), torch.float32, dev)
     dtc = _DTYPES[dt]
     opts = None
-    if any(x is not None for x in (conv_q_w, conv_k_w, gate, norm_w)) or segment_tokens != 0:
+    if any(x is not None for x in (conv_q_w, conv_k_w, gate, norm_w)) or segment_tokens != 0 or unbounded_decay:
         opts = _FusedOpts(_ptr(conv_q_w), _ptr(conv_k_w), _ptr(gate), _ptr(norm_w), float(l2_eps),
-                          float(rms_eps), int(segment_tokens))
+                          float(rms_eps), int(segment_tokens), int(bool(unbounded_decay)))
     opts_p = ctypes.byref(opts) if opts is not None else None
     need = int(lib.kda_chunk_fwd_workspace_bytes(N, T, H, D, D, dtc, opts_p))
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):

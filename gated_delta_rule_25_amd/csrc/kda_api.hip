@@ -165,7 +165,8 @@ Plan make_plan(int num_seqs, int64_t total_tokens, int num_heads, kda_dtype dtyp
   return pl;
 }
 
-const kda_fused_opts kNoOpts = {nullptr, nullptr, nullptr, nullptr, 1e-6f, 1e-6f, 0};
+const kda_fused_opts kNoOpts = {nullptr, nullptr, nullptr, nullptr, 1e-6f, 1e-6f, 0, 0};
+constexpr float kBoundedLaMin = -5.f;  // the K3 decay bound the tile paths rely on
 
 // Optional precondition checks: the environment variable KDA_DEBUG_CHECKS
 // (read at every call) switches them on; the failed checks of the calling
@@ -291,6 +292,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     chk.num_seqs = num_seqs;
     chk.total_tokens = total_tokens;
     chk.bf16 = bf16;
+    chk.la_min = f.unbounded_decay ? -INFINITY : kBoundedLaMin;
     const kda_status cs = checked(chk, stream);
     if (cs != KDA_OK) return cs;
   }
@@ -326,6 +328,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   pa.cap = (int)pl.slots;
   pa.chunks_per_block = kPrepChunksPerBlock;
   pa.factors = factors;
+  pa.unbounded = f.unbounded_decay != 0;
 
   kda::CarryArgs ca;
   std::memset(&ca, 0, sizeof(ca));
@@ -442,6 +445,7 @@ kda_status kda_decode_step(float* state, const void* q, const void* k, const voi
     chk.q = q;
     chk.k = k;
     chk.bf16 = dtype == KDA_DTYPE_BF16;
+    chk.la_min = -INFINITY;  // one token at a time: no bound needed
     const kda_status cs = checked(chk, stream);
     if (cs != KDA_OK) return cs;
   }
@@ -470,6 +474,7 @@ kda_status kda_decode_replay(const float* state_in, float* state_out, const void
   if (d_k != kD || d_v != kD || !dtype_ok(dtype) || max_tokens > kda::kReplayMaxTokens) return KDA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !log_alpha || !beta) return KDA_ERR_INVALID_ARG;
   const kda_fused_opts& f = opts ? *opts : kNoOpts;
+  if (f.unbounded_decay) return KDA_ERR_UNSUPPORTED;  // the block form needs the decay bound
   if (!(f.l2_eps >= 0.f) || !(f.rms_eps >= 0.f)) return KDA_ERR_INVALID_ARG;
   if ((f.conv_q_w && !conv_q_state) || (f.conv_k_w && !conv_k_state)) return KDA_ERR_INVALID_ARG;
   // a history without its convolution is neither read nor written
@@ -524,6 +529,7 @@ kda_status kda_decode_replay(const float* state_in, float* state_out, const void
     chk.q = f.conv_q_w ? nullptr : q;
     chk.k = f.conv_k_w ? nullptr : k;
     chk.bf16 = dtype == KDA_DTYPE_BF16;
+    chk.la_min = kBoundedLaMin;
     const kda_status cs = checked(chk, stream);
     if (cs != KDA_OK) return cs;
   }

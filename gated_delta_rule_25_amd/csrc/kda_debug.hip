@@ -4,7 +4,8 @@
 // The entry points document preconditions that the fast path does not check:
 // log_alpha in [-5, 0] (the lower-bounded decay with bound -5 of
 // "Kimi K3 架构、训练与系统全景解析", sections 2.1 and 4.2.5, which the chunked
-// kernels' exponent ranges rely on), beta in [0, 1], q and k of unit norm per
+// kernels' exponent ranges rely on), or only <= 0 where a call accepts
+// unbounded decay, beta in [0, 1], q and k of unit norm per
 // (token, head) when no prologue normalises them (the L2-normalised inputs of
 // section 4.2.3), and cu_seqlens non-decreasing from 0 to total_tokens.  With
 // the checks switched on, a call first runs them on its stream, waits for
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void check_rows_kernel(const CheckArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const float x = la[lane + 64 * i];
-      if (!(x >= -5.f && x <= 0.f)) bad |= KDA_CHECK_LOG_ALPHA;
+      if (!(x >= a.la_min && x <= 0.f)) bad |= KDA_CHECK_LOG_ALPHA;
     }
     if (lane == 0) {
       const float b = a.beta[row];

@@ -57,6 +57,7 @@ struct CheckArgs {
   int num_seqs;
   int64_t total_tokens;
   bool bf16;
+  float la_min;              // log_alpha must lie in [la_min, 0] (-inf: any value <= 0)
 };
 
 struct ScanArgs {
@@ -158,6 +159,7 @@ struct PrepArgs {
   int cap;                   // slots the store can hold
   int chunks_per_block;      // consecutive slots per workgroup
   void* factors;
+  bool unbounded;            // log_alpha not bounded below: per-position diagonal tiles
 };
 
 struct CarryArgs {

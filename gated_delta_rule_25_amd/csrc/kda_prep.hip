@@ -26,6 +26,14 @@
 // Exponents: a tile's rows are referenced to the decay before the tile (rho_a)
 // or after it (rho_{a+1}), so every factor formed is <= 1 except the diagonal
 // tile's e^{rho_a - g} <= e^{80}, which is exactly the pages' bound.
+// Unbounded decay (the negative-softplus gate the same section describes for
+// Kimi Linear, where that factor can overflow): the UNB variant forms the
+// diagonal tile's entries position by position instead,
+//   A_ij = sum_c k_ic k_jc e^{g_ic - g_jc},  P_ij = sum_c q_ic k_jc e^{g_ic - g_jc},
+// with e^{g_i - g_j} = alpha_i alpha_{i-1} ... alpha_{j+1} built up one DPP row
+// shift at a time (every partial product is <= 1), and K_end from an in-tile
+// suffix sum; every other factor is a sum of same-sign log-decays, so no
+// exponent exceeds 0 and no difference of large sums is taken.
 //
 // Per chunk: loads and the in-tile decay scan (DPP row shifts); barrier;
 // per-channel factors (e^{tot_a}, e^{rho_a}, e^{g_n - rho_{a+1}}, e^{g_n});
@@ -73,6 +81,21 @@ __device__ __forceinline__ float row_scan(float x) {
   x += row_shr<2>(x);
   x += row_shr<4>(x);
   x += row_shr<8>(x);
+  return x;
+}
+// Exclusive suffix sum over the 16 lanes of a row: lane r gets the sum over
+// lanes r + 1 .. 15 (DPP row shifts left, zero fill).  Every term has the
+// sign of the inputs, so nothing cancels.
+template <int N>
+__device__ __forceinline__ float row_shl(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x100 + N, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row_suffix_excl(float x) {
+  x = row_shl<1>(x);
+  x += row_shl<1>(x);
+  x += row_shl<2>(x);
+  x += row_shl<4>(x);
+  x += row_shl<8>(x);
   return x;
 }
 
@@ -258,7 +281,7 @@ struct PrepLayout {
 // Workgroup (range, head h) handles the consecutive slots
 // [range * chunks_per_block, ...) of head h.
 // ---------------------------------------------------------------------------
-template <typename E, int C, bool PRO>
+template <typename E, int C, bool PRO, bool UNB>
 __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
   using L = PrepLayout<E, C>;
   using F = FactorBlock<(int)sizeof(E), C>;
@@ -515,16 +538,91 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
         }
     }
 
-    // ---- decay, in log2 units, relative to the start of this lane's tile ----
+    // ---- unbounded decay: the diagonal tile position by position (lane r =
+    //      token i of tile w; lane group g = a quarter of the channels) ----
+    f32x4 gp_diag = (f32x4){0.f, 0.f, 0.f, 0.f};  // P_ww in the accumulator layout
+    if constexpr (UNB) {
+      float ga_d[16], gp_d[16];  // [delta]: A(i, i - delta), P(i, i - delta) over the lane's channels
 #pragma unroll
-    for (int pc = 0; pc < 8; ++pc)
+      for (int d = 0; d < 16; ++d) {
+        ga_d[d] = 0.f;
+        gp_d[d] = 0.f;
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dl[pc][i] = row_scan(dl[pc][i] * LOG2E);
-    if (r == 15)
+      for (int st = 0; st < 4; ++st) {
+        float q8[8], k8[8];
+        auto unpack = [&](float (&x)[8], const auto (&rp)[8], const u32x4 (&wp)[WIDE ? 4 : 1], bool wide) {
+          if constexpr (WIDE) {
+            if (wide) {
+              Raw4<E> a, b;
+              unpack_wide(a, b, wp[st]);
+              cvt_raw4(x, a);
+              cvt_raw4(x + 4, b);
+              return;
+            }
+          }
+          cvt_raw4(x, rp[2 * st]);
+          cvt_raw4(x + 4, rp[2 * st + 1]);
+        };
+        unpack(q8, rq, wq, !PRO);
+        unpack(k8, rk, wk, !PRO);
 #pragma unroll
-      for (int pc = 0; pc < 8; ++pc)
-        *reinterpret_cast<f32x4*>(sTot + w * 128 + piece_ch(pc, g)) =
-            (f32x4){dl[pc][0], dl[pc][1], dl[pc][2], dl[pc][3]};
+        for (int e = 0; e < 8; ++e) {
+          const float al = exp2_fast(dl[2 * st + (e >> 2)][e & 3] * LOG2E);  // alpha_i
+          float ed = al;                                                      // e^{g_i - g_{i-1}}
+          gp_d[0] += q8[e] * k8[e];
+          static_for<1, 16>([&](auto D) {
+            constexpr int d = decltype(D)::value;
+            if constexpr (d >= 2) ed *= row_shr<d - 1>(al);  // e^{g_i - g_{i-d}}
+            const float t = row_shr<d>(k8[e]) * ed;          // k_{i-d} e^{g_i - g_{i-d}}
+            ga_d[d] += k8[e] * t;
+            gp_d[d] += q8[e] * t;
+          });
+        }
+      }
+#pragma unroll
+      for (int d = 0; d < 16; ++d) {
+        ga_d[d] += __shfl_xor(ga_d[d], 16);
+        ga_d[d] += __shfl_xor(ga_d[d], 32);
+        gp_d[d] += __shfl_xor(gp_d[d], 16);
+        gp_d[d] += __shfl_xor(gp_d[d], 32);
+      }
+      // P_ww rows through this wave's diagonal block into the accumulator
+      // layout (lane: column r, rows 4 g .. 4 g + 3; above the diagonal is
+      // masked where it is used), then the block of Diag(beta) A_ww that the
+      // inverse below reads
+      float* ab = sAd + w * 256;
+      if (g == 0)
+        static_for<0, 16>([&](auto D) {
+          constexpr int d = decltype(D)::value;
+          if (d <= r) ab[r * 16 + r - d] = gp_d[d];
+        });
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gp_diag[i] = ab[(4 * g + i) * 16 + r];
+      if (g == 0) {
+        static_for<1, 16>([&](auto D) {
+          constexpr int d = decltype(D)::value;
+          if (d <= r) ab[r * 16 + r - d] = ga_d[d] * bt;
+        });
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+          if (c >= r) ab[r * 16 + c] = 0.f;
+      }
+    }
+
+    // ---- decay, in log2 units, relative to the start of this lane's tile
+    //      (unbounded decay: only the tile totals here; dl keeps the raw
+    //      log-decays and each step below forms its prefix and suffix sums) ----
+#pragma unroll
+    for (int pc = 0; pc < 8; ++pc) {
+      f32x4 tv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        tv[i] = row_scan(dl[pc][i] * LOG2E);
+        if constexpr (!UNB) dl[pc][i] = tv[i];
+      }
+      if (r == 15) *reinterpret_cast<f32x4*>(sTot + w * 128 + piece_ch(pc, g)) = tv;
+    }
     if (g == 0) sBeta[tok] = bt;
     __syncthreads();
 
@@ -535,15 +633,18 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
       rho[0] = 0.f;
 #pragma unroll
       for (int a = 0; a < NT; ++a) rho[a + 1] = rho[a] + sTot[a * 128 + c];
+      // (tile totals and their prefix and suffix sums: no differences)
       if (part == 0) {
 #pragma unroll
-        for (int a = 0; a < NT; ++a) sFE[a * 128 + c] = exp2_fast(rho[a + 1] - rho[a]);
+        for (int a = 0; a < NT; ++a) sFE[a * 128 + c] = exp2_fast(sTot[a * 128 + c]);
         buf_st4(exp2_fast(rho[NT]), fb, F::G + 4 * c, 0);  // gamma = e^{g_n}
       } else {
+        float after = 0.f;  // g_n - rho_{a+1}
 #pragma unroll
-        for (int a = 0; a < NT; ++a) {
+        for (int a = NT - 1; a >= 0; --a) {
           sFA[a * 128 + c] = exp2_fast(rho[a]);
-          sFB[a * 128 + c] = exp2_fast(rho[NT] - rho[a + 1]);
+          sFB[a * 128 + c] = exp2_fast(after);
+          after += sTot[a * 128 + c];
         }
       }
     }
@@ -590,11 +691,17 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
         pieces(q8, rq, wq, !PRO);
         pieces(k8, rk, wk, !PRO);
         pieces(v8, rv, wv, true);
+        float sx[8];  // unbounded decay: rho_{w+1} - g, from the suffix sum
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float d = dl[2 * st + (e >> 2)][e & 3];
-          ep[e] = exp2_fast(d);    // e^{g - rho_w} <= 1
-          en[e] = exp2_fast(-d);   // e^{rho_w - g} <= e^{80}
+          float d = dl[2 * st + (e >> 2)][e & 3];
+          if constexpr (UNB) {
+            const float l2 = d * LOG2E;
+            d = row_scan(l2);
+            sx[e] = row_suffix_excl(l2);
+          }
+          ep[e] = exp2_fast(d);                       // e^{g - rho_w} <= 1
+          if constexpr (!UNB) en[e] = exp2_fast(-d);  // e^{rho_w - g} <= e^{80}
         }
         // K_rel (A operand of the Gram products); beta Kt = beta K_rel e^{rho_w}
         // and beta V as channel-per-lane right-hand sides, sR[ct][w]
@@ -634,21 +741,29 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
         for (int e = 0; e < 8; ++e) y[e] = x[e] * fac[e];
         frag8(a, y);
         st_frag_g(fb, F::Q + (uint32_t)(w * 4 + st) * F::FR + lane_fr, a);
-        // K_inv (hi + lo): B operand of the diagonal pair
+        if constexpr (!UNB) {
+          // K_inv (hi + lo): B operand of the diagonal pair
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = k8[e] * en[e];
-        {
-          float xs[8][4];
+          for (int e = 0; e < 8; ++e) x[e] = k8[e] * en[e];
+          {
+            float xs[8][4];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xs[2 * st + (e >> 2)][e & 3] = x[e];
-          frag_step_split(kih[st], kil[st], xs, st);
+            for (int e = 0; e < 8; ++e) xs[2 * st + (e >> 2)][e & 3] = x[e];
+            frag_step_split(kih[st], kil[st], xs, st);
+          }
         }
-        // K_end = K e^{rho_{w+1} - g} <= 1; Kb = K_end e^{g_n - rho_{w+1}} as
-        // channel-per-lane halves of the Kb^T fragments (rt8, kt = w / 2, half
-        // w % 2), each half a contiguous 64-lane block
-        fac8(fac, sFE + w * 128, st);
+        // K_end = K e^{rho_{w+1} - g} <= 1 (K_inv e^{tot_w}, or from the
+        // in-tile suffix sum when the decay is unbounded); Kb = K_end
+        // e^{g_n - rho_{w+1}} as channel-per-lane halves of the Kb^T fragments
+        // (rt8, kt = w / 2, half w % 2), each half a contiguous 64-lane block
+        if constexpr (UNB) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] *= fac[e];
+          for (int e = 0; e < 8; ++e) x[e] = k8[e] * exp2_fast(sx[e]);
+        } else {
+          fac8(fac, sFE + w * 128, st);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] *= fac[e];
+        }
         fac8(fac, sFB + w * 128, st);
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = x[e] * fac[e];
@@ -691,13 +806,17 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
       ga[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
       gp[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
+    if constexpr (UNB) {
+      gp[NT - 1] = gp_diag;  // (Diag(beta) A_ww is already in the wave's diagonal block)
+    } else {
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      ga[NT - 1] = mma(ga[NT - 1], kr[st], kih[st]);  // diagonal kept in slot NT-1
-      gp[NT - 1] = mma(gp[NT - 1], qh[st], kih[st]);
-      if constexpr (SPLIT) {
-        gp[NT - 1] = mma(gp[NT - 1], ql[st], kih[st]);
-        gp[NT - 1] = mma(gp[NT - 1], qh[st], kil[st]);
+      for (int st = 0; st < 4; ++st) {
+        ga[NT - 1] = mma(ga[NT - 1], kr[st], kih[st]);  // diagonal kept in slot NT-1
+        gp[NT - 1] = mma(gp[NT - 1], qh[st], kih[st]);
+        if constexpr (SPLIT) {
+          gp[NT - 1] = mma(gp[NT - 1], ql[st], kih[st]);
+          gp[NT - 1] = mma(gp[NT - 1], qh[st], kil[st]);
+        }
       }
     }
 #pragma unroll
@@ -718,11 +837,12 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
     //      forward substitution over this wave's own 16 x 16 block ----
     {
       float* ab = sAd + w * 256;
+      if constexpr (!UNB)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = 4 * g + i;
-        ab[rr * 16 + r] = (r < rr) ? ga[NT - 1][i] * sBeta[16 * w + rr] : 0.f;
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 4 * g + i;
+          ab[rr * 16 + r] = (r < rr) ? ga[NT - 1][i] * sBeta[16 * w + rr] : 0.f;
+        }
       float xinv[16];
       if (lane < 16) {
 #pragma unroll
@@ -840,10 +960,10 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
 
 namespace {
 
-template <typename E, int C, bool PRO>
+template <typename E, int C, bool PRO, bool UNB>
 hipError_t launch_prep_t(const PrepArgs& a, hipStream_t stream) {
   constexpr size_t lds = PrepLayout<E, C>::BYTES;
-  auto fn = prep_kernel<E, C, PRO>;
+  auto fn = prep_kernel<E, C, PRO, UNB>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -857,10 +977,16 @@ hipError_t launch_prep_t(const PrepArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
+template <typename E, int C, bool UNB>
+hipError_t launch_prep_pro(const PrepArgs& a, hipStream_t stream) {
   const bool pro = a.conv_q_w != nullptr || a.conv_k_w != nullptr;
-  if (a.bf16) return pro ? launch_prep_t<__bf16, 64, true>(a, stream) : launch_prep_t<__bf16, 64, false>(a, stream);
-  return pro ? launch_prep_t<float, 32, true>(a, stream) : launch_prep_t<float, 32, false>(a, stream);
+  return pro ? launch_prep_t<E, C, true, UNB>(a, stream) : launch_prep_t<E, C, false, UNB>(a, stream);
+}
+
+hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
+  if (a.bf16)
+    return a.unbounded ? launch_prep_pro<__bf16, 64, true>(a, stream) : launch_prep_pro<__bf16, 64, false>(a, stream);
+  return a.unbounded ? launch_prep_pro<float, 32, true>(a, stream) : launch_prep_pro<float, 32, false>(a, stream);
 }
 
 }  // namespace kda

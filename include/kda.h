@@ -33,7 +33,10 @@
  *   - Preconditions that the fast path does not check (KDA_DEBUG_CHECKS
  *     below checks them on request): log_alpha in
  *     [-5, 0] (the lower-bounded decay of "Kimi K3 架构…" section 4.2.5,
- *     gate_lower_bound = -5 of section 2.1); beta in [0, 1]; ||q||, ||k||
+ *     gate_lower_bound = -5 of section 2.1) for kda_chunk_fwd and
+ *     kda_decode_replay, or any value <= 0 (-inf included, NaN not) for
+ *     kda_decode_step and for kda_chunk_fwd with unbounded_decay set;
+ *     beta in [0, 1]; ||q||, ||k||
  *     about 1 per head when no prologue runs; cu_seqlens non-decreasing from
  *     0 to total_tokens.  Outside them the results are undefined (they may
  *     overflow) but every access stays in bounds.
@@ -69,7 +72,7 @@ typedef enum {
  * run concurrently on different streams.
  */
 enum {
-  KDA_CHECK_LOG_ALPHA = 1,  /* a log_alpha value outside [-5, 0] or not finite          */
+  KDA_CHECK_LOG_ALPHA = 1,  /* a log_alpha value outside the call's range (above), or NaN */
   KDA_CHECK_BETA = 2,       /* a beta value outside [0, 1] or not finite               */
   KDA_CHECK_Q_NORM = 4,     /* a q row (no prologue on q) whose norm is not 1 +- 0.02   */
   KDA_CHECK_K_NORM = 8,     /* a k row (no prologue on k) whose norm is not 1 +- 0.02   */
@@ -95,6 +98,15 @@ typedef enum {
  *   gate  [T_total, H, 128] logits in the I/O dtype.  When given, the stored
  *       output is  y_t = o_t / sqrt(mean_j o_t[j]^2 + rms_eps) * norm_w * sigmoid(gate_t).
  *   norm_w  [128] fp32 RMSNorm weight; NULL means all ones.  Used only with gate.
+ *   unbounded_decay  0: log_alpha in [-5, 0] (the K3 bound), where every
+ *       16-token tile of the chunked prefill runs as dense matrix-core
+ *       products.  Nonzero: kda_chunk_fwd accepts any log_alpha <= 0, the
+ *       unbounded negative-softplus decay of Kimi Linear ("Kimi K3 架构…"
+ *       section 4.2.5); the diagonal 16-token tiles are then formed position
+ *       pair by position pair (e^{g_i - g_j} as a running product of the
+ *       alphas between the two tokens, never above 1), which is slower.
+ *       kda_decode_replay returns KDA_ERR_UNSUPPORTED when it is set;
+ *       kda_decode_step needs no flag (it accepts any log_alpha <= 0).
  *   segment_tokens  scheduling of long sequences when there are too few
  *       (sequence, head) pairs to occupy the GPU: 0 lets the library decide
  *       (it segments only when the sequential schedule would leave more than
@@ -119,6 +131,7 @@ typedef struct {
   float l2_eps;
   float rms_eps;
   int segment_tokens;
+  int unbounded_decay;
 } kda_fused_opts;
 
 /*

@@ -16,6 +16,13 @@ is deterministic for a given device type):
   v        N(0,1), cast to the I/O dtype.
   beta     sigmoid(N(0,1)) fp32, [T, H].
   log_alpha  -5 * sigmoid(N(0,1)) fp32, [T, H, 128]  (values in (-5, 0)).
+           Unbounded variant (decay="softplus"): -a_h * softplus(N(0,1)),
+           the negative-softplus gate that "Kimi K3 架构…" section 4.2.5
+           attributes to Kimi Linear (its formula is lost from the page; read
+           as Mamba-2's form, a positive per-head rate times a softplus), with
+           a_h = 16**u_h, u_h ~ U[0,1) per head from a generator of its own
+           (so every other tensor matches the bounded draw); values reach
+           about -60 per token, and a 16-token tile's sum goes far below -80.
   S0       std * N(0,1) fp32 [N, H, 128, 128], or None (zeros) when std = 0.
   prologue conv weights 0.5 * N(0,1) fp32 [H*128, 4] for each of q and k.
   epilogue gate logits N(0,1) in the I/O dtype, norm weight = ones (None).
@@ -62,6 +69,10 @@ WORKLOADS = {
     # pass over 7 draft tokens + the bonus token, then the replay commit
     6: dict(name="kda_replay_N256_H96_L8", kind="replay", dtype="bf16", N=256, H=96, L=8, s0_std=0.02,
             fused=True),
+    # the K3 layer shape with Kimi Linear's unbounded negative-softplus decay
+    # (the per-position diagonal tiles that the decay bound removes)
+    7: dict(name="kda_prefill_H96_T8192_softplus", kind="prefill", dtype="bf16", H=96, lengths=[8192],
+            s0_std=0.02, fused=False, decay="softplus"),
 }
 
 
@@ -106,8 +117,11 @@ def _fill_unit(dst, g, device, normalise, slab):
 
 
 def make_prefill(H, lengths, dtype="bf16", s0_std=0.0, fused=False, device="cpu", seed=SEED_BASE,
-                 slab_tokens=16384):
-    """Packed prefill inputs.  Returns a dict of tensors on ``device``."""
+                 slab_tokens=16384, decay="bounded"):
+    """Packed prefill inputs.  Returns a dict of tensors on ``device``.
+    decay: "bounded" (-5 sigmoid) or "softplus" (unbounded, see the recipe)."""
+    if decay not in ("bounded", "softplus"):
+        raise ValueError("decay must be 'bounded' or 'softplus'")
     dt = torch_dtype(dtype)
     g = _gen(device, seed)
     lengths = [int(x) for x in lengths]
@@ -122,15 +136,20 @@ def make_prefill(H, lengths, dtype="bf16", s0_std=0.0, fused=False, device="cpu"
     _fill_unit(q, g, device, not fused, slab_tokens)
     _fill_unit(k, g, device, not fused, slab_tokens)
     _fill_unit(v, g, device, False, slab_tokens)
+    rate = None
+    if decay == "softplus":
+        rate = torch.pow(16.0, torch.rand((H, 1), generator=_gen(device, seed + 0x5F0), device=device))
     for a in range(0, T, slab_tokens):
         e = min(T, a + slab_tokens)
-        la[a:e] = -5.0 * torch.sigmoid(_randn((e - a, H, D), g, device))
+        z = _randn((e - a, H, D), g, device)
+        la[a:e] = -5.0 * torch.sigmoid(z) if rate is None else -rate * torch.nn.functional.softplus(z)
+        del z
     beta = torch.sigmoid(_randn((T, H), g, device))
     s0 = None
     if s0_std > 0:
         s0 = s0_std * _randn((N, H, D, D), g, device)
     out.update(q=q, k=k, v=v, log_alpha=la, beta=beta, initial_state=s0,
-               cu_seqlens=cu.to(device) if N > 1 else None, cu_host=cu)
+               cu_seqlens=cu.to(device) if N > 1 else None, cu_host=cu, decay=decay)
     if fused:
         out["conv_q_w"] = 0.5 * _randn((H * D, 4), g, device)
         out["conv_k_w"] = 0.5 * _randn((H * D, 4), g, device)
@@ -210,4 +229,5 @@ def make_workload(wid: int, device="cpu", **overrides):
     if w["kind"] == "replay":
         return make_replay(w["N"], w["H"], w["L"], w["dtype"], w["s0_std"], w["fused"], device, seed)
     lengths = w["lengths"] if w["lengths"] != "loguniform64" else varlen_lengths(seed)
-    return make_prefill(w["H"], lengths, w["dtype"], w["s0_std"], w["fused"], device, seed)
+    return make_prefill(w["H"], lengths, w["dtype"], w["s0_std"], w["fused"], device, seed,
+                        decay=w.get("decay", "bounded"))

@@ -145,7 +145,7 @@ def test_chunk_validation(lib):
 class Opts(ctypes.Structure):
     _fields_ = [("conv_q_w", ctypes.c_void_p), ("conv_k_w", ctypes.c_void_p), ("gate", ctypes.c_void_p),
                 ("norm_w", ctypes.c_void_p), ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float),
-                ("segment_tokens", ctypes.c_int)]
+                ("segment_tokens", ctypes.c_int), ("unbounded_decay", ctypes.c_int)]
 
 
 def opts_p(o):
@@ -260,6 +260,8 @@ def test_replay_validation(lib):
     assert replay(lib, opts=opts_p(g)) == INVALID            # gate aliases o
     neg = Opts(None, None, None, None, 1e-6, -1.0, 0)
     assert replay(lib, opts=opts_p(neg)) == INVALID          # negative epsilon
+    unb = Opts(None, None, None, None, 1e-6, 1e-6, 0, 1)
+    assert replay(lib, opts=opts_p(unb)) == UNSUPPORTED      # the block form needs the decay bound
     # nothing to produce: accepted without launching anything
     assert replay(lib, s1=None, o=None) == OK
 
