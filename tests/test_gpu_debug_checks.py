@@ -136,3 +136,30 @@ def test_checks_off_by_default(monkeypatch):
     kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], b, initial_state=inp["initial_state"],
                   cu_seqlens=inp["cu_seqlens"])
     sync()
+
+
+def test_unbounded_decay_range(checks_on):
+    """With unbounded_decay the prefill accepts any log_alpha <= 0 (-inf
+    included) and still flags NaN and positive values; without it a value
+    below -5 is flagged.  A decode step takes any log_alpha <= 0."""
+    say("case debug checks: unbounded decay range")
+    inp = prefill_inputs()
+    inp["log_alpha"][5, 1, 3] = -40.0
+    inp["log_alpha"][7, 0, 0] = float("-inf")
+    out = torch.full((inp["T"], inp["H"], 128), 7.0, dtype=torch.bfloat16, device=DEV)
+    expect_flags(lambda: run_prefill(inp, out=out), kda.CHECK_LOG_ALPHA, out)
+    run_prefill(inp, unbounded_decay=True)
+    assert kda.last_precondition_flags() == 0
+    inp["log_alpha"][9, 2, 1] = float("nan")
+    out.fill_(7.0)
+    expect_flags(lambda: run_prefill(inp, out=out, unbounded_decay=True), kda.CHECK_LOG_ALPHA, out)
+    inp["log_alpha"][9, 2, 1] = 0.25
+    out.fill_(7.0)
+    expect_flags(lambda: run_prefill(inp, out=out, unbounded_decay=True), kda.CHECK_LOG_ALPHA, out)
+    d = kda_inputs.make_decode(2, 3, 1, "bf16", 0.02, DEV, seed=87)
+    la = d["log_alpha"][0].clone()
+    la[0, 1, :8] = -60.0
+    la[1, 2, 4] = float("-inf")
+    kda.decode_step(d["state"].clone(), d["q"][0], d["k"][0], d["v"][0], la, d["beta"][0])
+    sync()
+    assert kda.last_precondition_flags() == 0

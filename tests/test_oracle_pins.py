@@ -365,3 +365,39 @@ def test_tile_decay_bound(golden):
     ex = golden["tile_decay_bound"]
     la = np.full(ex["tile_tokens"], ex["log_decay_lower_bound"])
     assert np.cumsum(la)[-1] == ex["cumulative_range"][0]
+
+
+def test_unbounded_decay_reset_and_deep_decay():
+    """Unbounded decay ("Kimi K3 架构…" section 4.2.5, Kimi Linear's
+    negative-softplus gate): log_alpha = -inf on every channel is alpha = 0,
+    so the token first erases the whole state and S_t = beta_t k_t v_t^T
+    exactly, after which the run continues as one started from a zero state;
+    on a single channel it zeroes that key row only.  A finite decay far past
+    the bound, -700 per token, still follows the closed form of the beta = 0
+    read (o = S0^T (exp(g) * q)) without overflow."""
+    T, d = 7, 6
+    q = unit_rows(RNG.standard_normal((T, d)))
+    k = unit_rows(RNG.standard_normal((T, d)))
+    v = RNG.standard_normal((T, d))
+    la = -3.0 * RNG.random((T, d))
+    b = RNG.random(T)
+    s0 = RNG.standard_normal((1, 1, d, d))
+    la_r = la.copy()
+    la_r[3] = -np.inf
+    o, fs = oracle.chunk_fwd(*one_head(q, k, v, la_r, b), initial_state=s0)
+    assert np.isfinite(o).all() and np.isfinite(fs).all()
+    o_tail, fs_tail = oracle.chunk_fwd(*one_head(q[3:], k[3:], v[3:], la_r[3:], b[3:]))
+    np.testing.assert_allclose(o[3:, 0], o_tail[:, 0], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(fs, fs_tail, rtol=1e-13, atol=1e-14)
+    # one channel reset: row 2 of the state before token 0's erase is gone
+    la_c = np.zeros((1, d))
+    la_c[0, 2] = -np.inf
+    _, fs1 = oracle.chunk_fwd(*one_head(q[:1], k[:1], v[:1], la_c, np.zeros(1)), initial_state=s0)
+    expect = s0[0, 0].copy()
+    expect[2] = 0.0
+    np.testing.assert_array_equal(fs1[0, 0], expect)
+    # deep finite decay with beta = 0
+    la_d = -700.0 * RNG.random((T, d))
+    o2, _ = oracle.chunk_fwd(*one_head(q, k, v, la_d, np.zeros(T)), initial_state=s0)
+    g = np.cumsum(la_d, axis=0)
+    np.testing.assert_allclose(o2[:, 0], (np.exp(g) * q) @ s0[0, 0], rtol=1e-13, atol=1e-300)
