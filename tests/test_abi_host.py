@@ -324,3 +324,21 @@ def test_c_consumer_compiles_as_c99(lib, tmp_path):
         pytest.fail("gcc failed:\n" + e.stderr)
     dyn = subprocess.run(["readelf", "-d", out], check=True, capture_output=True, text=True).stdout
     assert "libkda.so" in dyn and "libamdhip64" in dyn
+
+
+def test_fused_opts_layout_matches_header():
+    """The ctypes mirrors of kda_fused_opts (the binding's and this file's)
+    list the header's fields in order with matching C types, so a field added
+    to the header cannot be read past the end of a Python-built struct."""
+    import gated_delta_rule_25_amd as kda
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} kda_fused_opts;", text, re.S).group(1)
+    fields = re.findall(r"^\s*(const \w+\*|\w+)\s+(\w+);", body, re.M)
+    kinds = {"const float*": ctypes.c_void_p, "const void*": ctypes.c_void_p, "float": ctypes.c_float,
+             "int": ctypes.c_int}
+    want = [(name, kinds[t]) for t, name in fields]
+    assert [n for n, _ in want] == ["conv_q_w", "conv_k_w", "gate", "norm_w", "l2_eps", "rms_eps",
+                                    "segment_tokens", "unbounded_decay"]
+    for mirror in (kda._FusedOpts, Opts):
+        assert [(n, t) for n, t in mirror._fields_] == want, mirror
+        assert ctypes.sizeof(mirror) == 48
