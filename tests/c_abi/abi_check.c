@@ -10,6 +10,8 @@
  *   2. kda_decode_step on the prefill's final state, one token;
  *   3. kda_decode_replay, 5 cached tokens per sequence, ragged counts, in-place
  *      commit;
+ *   4. kda_chunk_fwd again with kda_fused_opts.unbounded_decay = 1 and
+ *      log_alpha = -20 softplus(z) (far below the -5 bound), one sequence;
  * and compares each output slice (per sequence and head) with the oracle by
  * max|y - r| / max|r| against 1e-4.  Exit status 0 when everything passes.
  * Inputs come from a fixed linear congruential generator (q, k normalised
@@ -226,6 +228,57 @@ int main(void) {
     check("decode_replay o", ro, rro, rt * D);
     check("decode_replay state", st2, rst, st);
     free(ws); free(rro); free(rst); free(wq); free(wk); free(wv); free(wla); free(wb);
+  }
+
+  /* ---- 4. prefill with unbounded decay, set through the options struct ---- */
+  {
+    const int Tu = 150;
+    const size_t tu = (size_t)Tu * H;
+    float *uq = malloc(tu * D * 4), *uk = malloc(tu * D * 4), *uv = malloc(tu * D * 4), *ula = malloc(tu * D * 4);
+    float *ub = malloc(tu * 4), *uo = malloc(tu * D * 4), *ufs = malloc((size_t)H * D * D * 4);
+    fill_rows(uq, tu, 1);
+    fill_rows(uk, tu, 1);
+    fill_rows(uv, tu, 0);
+    for (size_t i = 0; i < tu * D; ++i) ula[i] = (float)(-20.0 * log1p(exp(normal())));
+    fill_beta(ub, tu);
+    void *eq = dev_copy(uq, tu * D * 4), *ek = dev_copy(uk, tu * D * 4), *ev = dev_copy(uv, tu * D * 4);
+    void *ela = dev_copy(ula, tu * D * 4), *eb = dev_copy(ub, tu * 4), *eo = dev_copy(NULL, tu * D * 4);
+    void* efs = dev_copy(NULL, (size_t)H * D * D * 4);
+    if (!eq || !ek || !ev || !ela || !eb || !eo || !efs) return 2;
+    kda_fused_opts opts;
+    memset(&opts, 0, sizeof opts);
+    opts.l2_eps = 1e-6f;
+    opts.rms_eps = 1e-6f;
+    opts.unbounded_decay = 1;
+    const size_t wsu = kda_chunk_fwd_workspace_bytes(1, Tu, H, D, D, KDA_DTYPE_F32, &opts);
+    void* dwsu = wsu ? dev_copy(NULL, wsu) : NULL;
+    KDA_OK_(kda_chunk_fwd(eq, ek, ev, ela, eb, NULL, NULL, 1, Tu, H, D, D, KDA_DTYPE_F32, &opts, eo, efs, dwsu, wsu, 0));
+    HIP_OK(hipMemcpy(uo, eo, tu * D * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(ufs, efs, (size_t)H * D * D * 4, hipMemcpyDeviceToHost));
+    double *wq = widen(uq, tu * D), *wk = widen(uk, tu * D), *wv = widen(uv, tu * D), *wla = widen(ula, tu * D);
+    double *wb = widen(ub, tu), *ro = malloc(tu * D * 8), *rfs = malloc((size_t)H * D * D * 8);
+    int64_t cu1[2] = {0, Tu};
+    if (kda_oracle_chunk_fwd(wq, wk, wv, wla, wb, NULL, cu1, 1, Tu, H, D, D, NULL, NULL, NULL, NULL, 1e-6, 1e-6, ro,
+                             rfs, 0) != 0)
+      return 4;
+    for (int h = 0; h < H; ++h) {
+      size_t m = (size_t)Tu * D;
+      float* y = malloc(m * 4);
+      double* r = malloc(m * 8);
+      for (int t = 0; t < Tu; ++t)
+        for (int j = 0; j < D; ++j) {
+          y[(size_t)t * D + j] = uo[((size_t)t * H + h) * D + j];
+          r[(size_t)t * D + j] = ro[((size_t)t * H + h) * D + j];
+        }
+      char name[64];
+      snprintf(name, sizeof name, "unbounded chunk_fwd o   (head %d)", h);
+      check(name, y, r, m);
+      snprintf(name, sizeof name, "unbounded chunk_fwd S_T (head %d)", h);
+      check(name, ufs + (size_t)h * D * D, rfs + (size_t)h * D * D, (size_t)D * D);
+      free(y);
+      free(r);
+    }
+    free(wq); free(wk); free(wv); free(wla); free(wb); free(ro); free(rfs);
   }
 
   /* an argument error comes back before anything is launched */
