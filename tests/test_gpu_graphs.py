@@ -2,7 +2,7 @@
 
 Every compute path of the library only launches kernels on the caller's
 stream (no memsets, copies or host waits), so a serving loop can capture it
-once and replay it.  Each graph case captures one call, then replays the
+once and replay it (the unbounded-decay prefill included).  Each graph case captures one call, then replays the
 graph several times with eager work and synchronisations in between, and
 checks every replay bit for bit against the same call run eagerly (the
 kernels are deterministic).  The last case runs calls on three streams at
@@ -62,10 +62,11 @@ def test_decode_step_graph():
         assert torch.equal(st_g, st_e), i
 
 
-@pytest.mark.parametrize("segment_tokens", [0, 64])
-def test_chunk_fwd_graph(segment_tokens):
-    say("case graph: chunk_fwd segment_tokens=%d" % segment_tokens)
-    inp = kda_inputs.make_prefill(3, [300, 37], "bf16", 0.02, False, DEV, seed=92)
+@pytest.mark.parametrize("segment_tokens,unbounded", [(0, False), (64, False), (0, True)])
+def test_chunk_fwd_graph(segment_tokens, unbounded):
+    say("case graph: chunk_fwd segment_tokens=%d unbounded_decay=%s" % (segment_tokens, unbounded))
+    inp = kda_inputs.make_prefill(3, [300, 37], "bf16", 0.02, False, DEV, seed=92,
+                                  decay="softplus" if unbounded else "bounded")
     N, T, H = inp["N"], inp["T"], inp["H"]
     ws = torch.empty(max(1, kda.chunk_fwd_workspace_bytes(N, T, H, torch.bfloat16, segment_tokens=segment_tokens)),
                      dtype=torch.uint8, device=DEV)
@@ -74,7 +75,8 @@ def test_chunk_fwd_graph(segment_tokens):
 
     def call(warm):
         kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["initial_state"],
-                      inp["cu_seqlens"], out=o_g, final_state=fs_g, workspace=ws, segment_tokens=segment_tokens)
+                      inp["cu_seqlens"], out=o_g, final_state=fs_g, workspace=ws, segment_tokens=segment_tokens,
+                      unbounded_decay=unbounded)
 
     g = capture(call)
     for i in range(REPLAYS):
@@ -82,7 +84,7 @@ def test_chunk_fwd_graph(segment_tokens):
         fs_g.zero_()
         g.replay()
         o_e, fs_e = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["initial_state"],
-                                  inp["cu_seqlens"], segment_tokens=segment_tokens)
+                                  inp["cu_seqlens"], segment_tokens=segment_tokens, unbounded_decay=unbounded)
         torch.cuda.synchronize()
         assert torch.equal(o_g, o_e), i
         assert torch.equal(fs_g, fs_e), i
