@@ -542,12 +542,18 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
     //      token i of tile w; lane group g = a quarter of the channels) ----
     f32x4 gp_diag = (f32x4){0.f, 0.f, 0.f, 0.f};  // P_ww in the accumulator layout
     if constexpr (UNB) {
-      float ga_d[16], gp_d[16];  // [delta]: A(i, i - delta), P(i, i - delta) over the lane's channels
+      // Pairs in the same 8-token half: running alpha products over DPP row
+      // shifts (distances 1..7).  Pairs across the halves (rows 8..15,
+      // columns 0..7): one 8 x 8 block on the matrix cores with both sides
+      // referenced to the decay through token 7, e^{g_i - g_7} (a prefix sum
+      // from token 8) and e^{g_7 - g_j} (a suffix sum up to token 7), both <= 1.
+      float ga_d[8], gp_d[8];  // [delta]: A(i, i - delta), P(i, i - delta) over the lane's channels
 #pragma unroll
-      for (int d = 0; d < 16; ++d) {
+      for (int d = 0; d < 8; ++d) {
         ga_d[d] = 0.f;
         gp_d[d] = 0.f;
       }
+      f32x4 ga_m = (f32x4){0.f, 0.f, 0.f, 0.f}, gp_m = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         float q8[8], k8[8];
@@ -566,12 +572,21 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
         };
         unpack(q8, rq, wq, !PRO);
         unpack(k8, rk, wk, !PRO);
+        float xr[8], xs_q[8][4], xs_c[8][4];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float al = exp2_fast(dl[2 * st + (e >> 2)][e & 3] * LOG2E);  // alpha_i
-          float ed = al;                                                      // e^{g_i - g_{i-1}}
+          const float l2 = dl[2 * st + (e >> 2)][e & 3] * LOG2E;
+          const float pre = row_scan(r >= 8 ? l2 : 0.f);         // g_i - g_7, rows 8..15
+          const float suf = row_suffix_excl(r < 8 ? l2 : 0.f);  // g_7 - g_j, columns 0..7
+          const float fr = r >= 8 ? exp2_fast(pre) : 0.f;
+          const float fc = r < 8 ? exp2_fast(suf) : 0.f;
+          xr[e] = k8[e] * fr;
+          xs_q[2 * st + (e >> 2)][e & 3] = q8[e] * fr;
+          xs_c[2 * st + (e >> 2)][e & 3] = k8[e] * fc;
+          const float al = exp2_fast(l2);  // alpha_i
+          float ed = al;                   // e^{g_i - g_{i-1}}
           gp_d[0] += q8[e] * k8[e];
-          static_for<1, 16>([&](auto D) {
+          static_for<1, 8>([&](auto D) {
             constexpr int d = decltype(D)::value;
             if constexpr (d >= 2) ed *= row_shr<d - 1>(al);  // e^{g_i - g_{i-d}}
             const float t = row_shr<d>(k8[e]) * ed;          // k_{i-d} e^{g_i - g_{i-d}}
@@ -579,35 +594,44 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
             gp_d[d] += q8[e] * t;
           });
         }
+        Frag<E> mk, mqh, mql, mch, mcl;
+        frag_from_f32(mk, xr);
+        frag_step_split(mqh, mql, xs_q, st);
+        frag_step_split(mch, mcl, xs_c, st);
+        ga_m = mma(ga_m, mk, mch);
+        gp_m = mma(gp_m, mqh, mch);
+        if constexpr (SPLIT) {
+          gp_m = mma(gp_m, mql, mch);
+          gp_m = mma(gp_m, mqh, mcl);
+        }
       }
 #pragma unroll
-      for (int d = 0; d < 16; ++d) {
+      for (int d = 0; d < 8; ++d) {
         ga_d[d] += __shfl_xor(ga_d[d], 16);
         ga_d[d] += __shfl_xor(ga_d[d], 32);
         gp_d[d] += __shfl_xor(gp_d[d], 16);
         gp_d[d] += __shfl_xor(gp_d[d], 32);
       }
-      // P_ww rows through this wave's diagonal block into the accumulator
-      // layout (lane: column r, rows 4 g .. 4 g + 3; above the diagonal is
-      // masked where it is used), then the block of Diag(beta) A_ww that the
-      // inverse below reads
+      // P_ww rows (same-half entries; zero elsewhere) through this wave's
+      // diagonal block into the accumulator layout (lane: column r, rows
+      // 4 g .. 4 g + 3), plus the cross-half block; then Diag(beta) A_ww the
+      // same way, into the block the inverse below reads
       float* ab = sAd + w * 256;
-      if (g == 0)
-        static_for<0, 16>([&](auto D) {
-          constexpr int d = decltype(D)::value;
-          if (d <= r) ab[r * 16 + r - d] = gp_d[d];
-        });
+      const bool upper = r >= 8;
+      auto same_half_rows = [&](const float (&v)[8], int d0, float scale) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) gp_diag[i] = ab[(4 * g + i) * 16 + r];
-      if (g == 0) {
-        static_for<1, 16>([&](auto D) {
+        for (int c = 0; c < 16; ++c) ab[r * 16 + c] = 0.f;
+        static_for<0, 8>([&](auto D) {
           constexpr int d = decltype(D)::value;
-          if (d <= r) ab[r * 16 + r - d] = ga_d[d] * bt;
+          if (d >= d0 && d <= r && (!upper || r - d >= 8)) ab[r * 16 + r - d] = v[d] * scale;
         });
+      };
+      if (g == 0) same_half_rows(gp_d, 0, 1.f);
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
-          if (c >= r) ab[r * 16 + c] = 0.f;
-      }
+      for (int i = 0; i < 4; ++i) gp_diag[i] = ab[(4 * g + i) * 16 + r] + gp_m[i];
+      if (g == 0) same_half_rows(ga_d, 1, bt);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ab[(4 * g + i) * 16 + r] += ga_m[i] * __shfl(bt, 4 * g + i);
     }
 
     // ---- decay, in log2 units, relative to the start of this lane's tile
