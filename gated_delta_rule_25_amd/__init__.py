@@ -44,7 +44,8 @@ class KDAError(RuntimeError):
 class _FusedOpts(ctypes.Structure):
     _fields_ = [("conv_q_w", ctypes.c_void_p), ("conv_k_w", ctypes.c_void_p), ("gate", ctypes.c_void_p),
                 ("norm_w", ctypes.c_void_p), ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float),
-                ("segment_tokens", ctypes.c_int), ("unbounded_decay", ctypes.c_int)]
+                ("segment_tokens", ctypes.c_int), ("unbounded_decay", ctypes.c_int),
+                ("factor_budget_mib", ctypes.c_int)]
 
 
 def library_path() -> str:
@@ -111,13 +112,14 @@ def _stream(device) -> ctypes.c_void_p:
 
 def chunk_fwd_workspace_bytes(num_seqs: int, total_tokens: int, num_heads: int,
                               dtype: torch.dtype = torch.bfloat16, *, gated: bool = False,
-                              segment_tokens: int = 0) -> int:
+                              segment_tokens: int = 0, factor_budget_mib: int = 0) -> int:
     """Workspace bytes of chunk_fwd on the current device.  Of the fused
     options only whether an output gate is given matters (gated=True); the
     address passed for it here is a placeholder that is never read."""
     opts = None
-    if gated or segment_tokens != 0:
-        opts = ctypes.byref(_FusedOpts(None, None, 16 if gated else None, None, 1e-6, 1e-6, int(segment_tokens)))
+    if gated or segment_tokens != 0 or factor_budget_mib != 0:
+        opts = ctypes.byref(_FusedOpts(None, None, 16 if gated else None, None, 1e-6, 1e-6, int(segment_tokens),
+                                       0, int(factor_budget_mib)))
     return int(_load().kda_chunk_fwd_workspace_bytes(num_seqs, total_tokens, num_heads, D, D,
                                                      _DTYPES[dtype], opts))
 
@@ -129,7 +131,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
               l2_eps: float = 1e-6, rms_eps: float = 1e-6, out: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
               workspace: Optional[torch.Tensor] = None,
-              segment_tokens: int = 0, unbounded_decay: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              segment_tokens: int = 0, unbounded_decay: bool = False,
+              factor_budget_mib: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """KDA prefill over a packed batch (kda_chunk_fwd).
 
     q, k, v: [T, H, 128] float32 or bfloat16; log_alpha [T, H, 128] float32;
@@ -141,8 +144,10 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
     forces segments of that length, a negative value keeps the sequential
     one.  unbounded_decay: accept any log_alpha <= 0 (the negative-softplus
     decay) instead of the bound [-5, 0]; the diagonal tiles then run position
-    pair by position pair.  Returns (o, final_state); final_state may be the
-    same tensor as initial_state (in-place continuation).
+    pair by position pair.  factor_budget_mib: cap on one window's factor
+    store in MiB (0: 4096); longer inputs run in several windows.  Returns
+    (o, final_state); final_state may be the same tensor as initial_state
+    (in-place continuation).
     """
     lib = _load()
     if q.dim() != 3 or q.shape[2] != D:
@@ -184,9 +189,10 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
         _check(final_state, "final_state", (N, H, D, D), torch.float32, dev)
     dtc = _DTYPES[dt]
     opts = None
-    if any(x is not None for x in (conv_q_w, conv_k_w, gate, norm_w)) or segment_tokens != 0 or unbounded_decay:
+    if (any(x is not None for x in (conv_q_w, conv_k_w, gate, norm_w)) or segment_tokens != 0 or unbounded_decay
+            or factor_budget_mib != 0):
         opts = _FusedOpts(_ptr(conv_q_w), _ptr(conv_k_w), _ptr(gate), _ptr(norm_w), float(l2_eps),
-                          float(rms_eps), int(segment_tokens), int(bool(unbounded_decay)))
+                          float(rms_eps), int(segment_tokens), int(bool(unbounded_decay)), int(factor_budget_mib))
     opts_p = ctypes.byref(opts) if opts is not None else None
     need = int(lib.kda_chunk_fwd_workspace_bytes(N, T, H, D, D, dtc, opts_p))
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):

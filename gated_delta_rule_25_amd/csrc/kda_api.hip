@@ -88,20 +88,13 @@ int64_t choose_segment_tokens(int num_seqs, int64_t total_tokens, int num_heads,
 }
 
 // Factor store budget of the two-kernel schedule; longer inputs run in
-// several windows.  The environment variable KDA_FACTOR_BUDGET_MIB (read at
-// every call) sets another budget in MiB.
-#ifndef KDA_FACTOR_BUDGET_MIB
-#define KDA_FACTOR_BUDGET_MIB 4096
-#endif
-constexpr size_t kFactorBudget = (size_t)KDA_FACTOR_BUDGET_MIB << 20;
+// several windows.  kda_fused_opts::factor_budget_mib sets a smaller budget.
+constexpr int64_t kFactorBudgetMiB = 4096;
 
-size_t factor_budget() {
-  if (const char* e = std::getenv("KDA_FACTOR_BUDGET_MIB")) {
-    char* end = nullptr;
-    const long long mib = std::strtoll(e, &end, 10);
-    if (end != e && *end == '\0' && mib > 0 && mib < (1LL << 24)) return (size_t)mib << 20;
-  }
-  return kFactorBudget;
+size_t factor_budget(const kda_fused_opts& f) {
+  const int64_t mib = f.factor_budget_mib > 0 ? std::min<int64_t>(f.factor_budget_mib, kFactorBudgetMiB)
+                                              : kFactorBudgetMiB;
+  return (size_t)mib << 20;
 }
 
 // Workspace layout, each piece 256-byte aligned: the longest-first order [N]
@@ -133,7 +126,7 @@ Plan make_plan(int num_seqs, int64_t total_tokens, int num_heads, kda_dtype dtyp
   const size_t fb = kda::factor_block_bytes(bf);
   const int64_t chunks = total_tokens / C + num_seqs;
   const double total = (double)chunks * num_heads * fb;
-  pl.nw = (int)std::max<double>(1.0, std::ceil(total / (double)factor_budget()));
+  pl.nw = (int)std::max<double>(1.0, std::ceil(total / (double)factor_budget(f)));
   pl.slots = chunks / pl.nw + num_seqs + 1;
   // segments are cut from each window's share of the tokens
   const int64_t seg = choose_segment_tokens(num_seqs, (total_tokens + pl.nw - 1) / pl.nw, num_heads, f, cus);
@@ -165,7 +158,7 @@ Plan make_plan(int num_seqs, int64_t total_tokens, int num_heads, kda_dtype dtyp
   return pl;
 }
 
-const kda_fused_opts kNoOpts = {nullptr, nullptr, nullptr, nullptr, 1e-6f, 1e-6f, 0, 0};
+const kda_fused_opts kNoOpts = {nullptr, nullptr, nullptr, nullptr, 1e-6f, 1e-6f, 0, 0, 0};
 constexpr float kBoundedLaMin = -5.f;  // the K3 decay bound the tile paths rely on
 
 // Optional precondition checks: the environment variable KDA_DEBUG_CHECKS
@@ -195,6 +188,7 @@ bool sizes_ok(int num_seqs, int64_t total_tokens, int num_heads) {
 // fit the launch grid.
 bool segments_ok(const Plan& pl, int num_heads, const kda_fused_opts& f) {
   if (f.segment_tokens > 0 && f.segment_tokens % 64 != 0) return false;
+  if (f.factor_budget_mib < 0) return false;
   if (!(pl.slots <= (int64_t)INT32_MAX / 2 && pl.slots * num_heads <= (int64_t)UINT32_MAX)) return false;
   return pl.seg_chunks == 0 || pl.cap * num_heads <= (int64_t)INT32_MAX / 8;
 }
@@ -269,12 +263,14 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
   const Range r_o = range_of(o, tok_elems * es);
   const Range r_fs = range_of(final_state, final_state ? state_bytes : 0);
   const Range r_ws = range_of(workspace, need);
+  // final_state may be exactly initial_state (in-place continuation); any
+  // other overlap of an output with an input or another output is refused.
   const Range inputs[] = {r_q, r_k, r_v, r_la, r_b, r_s0, r_cu, r_g, r_cq, r_ck, r_nw};
   for (const Range& in : inputs) {
     if (overlap(r_o, in) || overlap(r_ws, in)) return KDA_ERR_INVALID_ARG;
-    const bool exact_alias = (in.lo == r_s0.lo && in.hi == r_s0.hi && r_fs.lo == r_s0.lo && r_fs.hi == r_s0.hi);
-    if (overlap(r_fs, in) && !exact_alias) return KDA_ERR_INVALID_ARG;
+    if (&in != &inputs[5] && overlap(r_fs, in)) return KDA_ERR_INVALID_ARG;
   }
+  if (overlap(r_fs, r_s0) && !(r_fs.lo == r_s0.lo && r_fs.hi == r_s0.hi)) return KDA_ERR_INVALID_ARG;
   if (overlap(r_o, r_fs) || overlap(r_o, r_ws) || overlap(r_fs, r_ws)) return KDA_ERR_INVALID_ARG;
 
   const bool bf16 = dtype == KDA_DTYPE_BF16;
@@ -508,12 +504,14 @@ kda_status kda_decode_replay(const float* state_in, float* state_out, const void
   const Range r_hq = range_of(conv_q_state, conv_q_state ? hist_bytes : 0);
   const Range r_hk = range_of(conv_k_state, conv_k_state ? hist_bytes : 0);
   const Range r_o = range_of(o, o ? tok_elems * es : 0);
+  // state_out may be exactly state_in (in place); any other overlap of an
+  // output with an input or another output is refused.
   const Range inputs[] = {r_s0, r_q, r_k, r_v, r_la, r_b, r_nt, r_g, r_cq, r_ck, r_nw};
   for (const Range& in : inputs) {
     if (overlap(r_o, in) || overlap(r_hq, in) || overlap(r_hk, in)) return KDA_ERR_INVALID_ARG;
-    const bool exact_alias = in.lo == r_s0.lo && in.hi == r_s0.hi && r_s1.lo == r_s0.lo && r_s1.hi == r_s0.hi;
-    if (overlap(r_s1, in) && !exact_alias) return KDA_ERR_INVALID_ARG;
+    if (&in != &inputs[0] && overlap(r_s1, in)) return KDA_ERR_INVALID_ARG;
   }
+  if (overlap(r_s1, r_s0) && !(r_s1.lo == r_s0.lo && r_s1.hi == r_s0.hi)) return KDA_ERR_INVALID_ARG;
   if (overlap(r_o, r_s1) || overlap(r_o, r_hq) || overlap(r_o, r_hk) || overlap(r_s1, r_hq) ||
       overlap(r_s1, r_hk) || overlap(r_hq, r_hk))
     return KDA_ERR_INVALID_ARG;

@@ -122,6 +122,13 @@ typedef enum {
  *       composes the pairs into each segment's incoming state; a last pass
  *       writes the outputs.  Results agree with the sequential form up to
  *       rounding.
+ *   factor_budget_mib  cap, in MiB, on the factor store of one window of
+ *       kda_chunk_fwd (the bulk of its workspace): 0 means the largest, 4096;
+ *       values above 4096 are taken as 4096; negative values are
+ *       KDA_ERR_INVALID_ARG.  Inputs whose factor blocks exceed the cap run in
+ *       several windows, one after another on the stream, with the same
+ *       results up to rounding.  The workspace query and the call must be
+ *       given the same value.  kda_decode_replay ignores it.
  */
 typedef struct {
   const float* conv_q_w;
@@ -132,6 +139,7 @@ typedef struct {
   float rms_eps;
   int segment_tokens;
   int unbounded_decay;
+  int factor_budget_mib;
 } kda_fused_opts;
 
 /*
@@ -140,9 +148,9 @@ typedef struct {
  * which the segmented form depends on).  Returns 0 for invalid sizes.
  * Most of it is the factor store: a 70.5 KiB block per (64-token chunk, head)
  * for bf16 I/O, 68.5 KiB per (32-token chunk, head) for fp32.  It is capped at
- * 4 GiB; longer inputs run in several windows.  The environment variable
- * KDA_FACTOR_BUDGET_MIB, read at every call, sets another cap in MiB; it
- * must be the same for this query and the kda_chunk_fwd call it sizes.
+ * 4 GiB, or at opts->factor_budget_mib; longer inputs run in several windows.
+ * The query depends on no environment variable: the same sizes and options
+ * give the same value on the same device.
  */
 size_t kda_chunk_fwd_workspace_bytes(int num_seqs, int64_t total_tokens, int num_heads, int d_k,
                                      int d_v, kda_dtype dtype, const kda_fused_opts* opts);

@@ -84,18 +84,20 @@ def test_workspace_bytes(lib):
     assert lib.kda_chunk_fwd_workspace_bytes(0, 10, 2, 128, 128, BF16, None) == 0
 
 
-def test_workspace_factor_budget_env(lib, monkeypatch):
-    # KDA_FACTOR_BUDGET_MIB caps one window's factor store at run time:
+def test_workspace_factor_budget_field(lib, monkeypatch):
+    # kda_fused_opts.factor_budget_mib caps one window's factor store:
     # 129 chunk slots x 96 heads x 70.5 KiB fit 4 GiB; a 64 MiB cap needs 14
-    # windows of 129 // 14 + 2 = 11 slots; an unparsable or zero value keeps the default
+    # windows of 129 // 14 + 2 = 11 slots; 0 and anything above 4096 keep the
+    # default; a negative cap is refused.  No environment variable changes it.
     one = lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, None)
     assert one == two_kernel_ws(1, 8192, 96)
-    monkeypatch.setenv("KDA_FACTOR_BUDGET_MIB", "64")
-    capped = lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, None)
+    capped = lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, opts_p(Opts(factor_budget_mib=64)))
     assert capped == 768 + 96 * 128 * 128 * 4 + 11 * 96 * FB_BF16  # + the state carried between windows
-    monkeypatch.setenv("KDA_FACTOR_BUDGET_MIB", "not a number")
-    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, None) == one
-    monkeypatch.setenv("KDA_FACTOR_BUDGET_MIB", "0")
+    for mib in (0, 4096, 1 << 20):
+        assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16,
+                                                 opts_p(Opts(factor_budget_mib=mib))) == one
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, opts_p(Opts(factor_budget_mib=-1))) == 0
+    monkeypatch.setenv("KDA_FACTOR_BUDGET_MIB", "64")
     assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, None) == one
 
 
@@ -131,6 +133,11 @@ def test_chunk_validation(lib):
     assert chunk(lib, o=p(0)) == INVALID                       # output aliases q
     assert chunk(lib, fs=p(3)) == INVALID                      # final state aliases log_alpha
     assert chunk(lib, s0=p(6), fs=ctypes.c_void_p(BASE + 6 * 64 * MB + 4)) == INVALID  # partial overlap
+    # in-place continuation exempts initial_state only: q spanning exactly the
+    # bytes of initial_state == final_state (T=256, H=2, bf16: 128 KiB each)
+    # is still an input that the final state would overwrite
+    assert chunk(lib, T=256, s0=p(0), fs=p(0)) == INVALID
+    assert chunk(lib, T=128, dt=0, s0=p(3), fs=p(3)) == INVALID  # ... and so is log_alpha (fp32, 128 KiB)
     need2 = lib.kda_chunk_fwd_workspace_bytes(2, 10, 2, 128, 128, BF16, None)
     assert chunk(lib, N=2, cu=p(7), ws=p(0), wsb=need2) == INVALID  # workspace aliases q
     need1 = lib.kda_chunk_fwd_workspace_bytes(1, 10, 2, 128, 128, BF16, None)
@@ -145,7 +152,8 @@ def test_chunk_validation(lib):
 class Opts(ctypes.Structure):
     _fields_ = [("conv_q_w", ctypes.c_void_p), ("conv_k_w", ctypes.c_void_p), ("gate", ctypes.c_void_p),
                 ("norm_w", ctypes.c_void_p), ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float),
-                ("segment_tokens", ctypes.c_int), ("unbounded_decay", ctypes.c_int)]
+                ("segment_tokens", ctypes.c_int), ("unbounded_decay", ctypes.c_int),
+                ("factor_budget_mib", ctypes.c_int)]
 
 
 def opts_p(o):
@@ -248,6 +256,7 @@ def test_replay_validation(lib):
     assert replay(lib, o=p(3)) == INVALID                    # output aliases v
     assert replay(lib, s1=p(1)) == INVALID                   # state output aliases q
     assert replay(lib, s1=ctypes.c_void_p(BASE + 4096)) == INVALID  # partial overlap with state_in
+    assert replay(lib, s0=p(1), s1=p(1)) == INVALID          # in place, but the state is also q
     assert replay(lib, s1=p(6)) == INVALID                   # state output aliases o
     assert replay(lib, s0=ctypes.c_void_p(BASE + 8), s1=None) == INVALID  # not 16-byte aligned
     assert replay(lib, nt=ctypes.c_void_p(BASE + 7 * 64 * MB + 2)) == INVALID  # counts not 4-byte aligned
@@ -338,7 +347,7 @@ def test_fused_opts_layout_matches_header():
              "int": ctypes.c_int}
     want = [(name, kinds[t]) for t, name in fields]
     assert [n for n, _ in want] == ["conv_q_w", "conv_k_w", "gate", "norm_w", "l2_eps", "rms_eps",
-                                    "segment_tokens", "unbounded_decay"]
+                                    "segment_tokens", "unbounded_decay", "factor_budget_mib"]
     for mirror in (kda._FusedOpts, Opts):
         assert [(n, t) for n, t in mirror._fields_] == want, mirror
-        assert ctypes.sizeof(mirror) == 48
+        assert ctypes.sizeof(mirror) == 56

@@ -114,11 +114,10 @@ WINDOW_CASES = [
 
 
 @pytest.mark.parametrize("name,H,lengths,dtype,s0,fused,seg", WINDOW_CASES, ids=[c[0] for c in WINDOW_CASES])
-def test_windows_parity(name, H, lengths, dtype, s0, fused, seg, monkeypatch):
+def test_windows_parity(name, H, lengths, dtype, s0, fused, seg):
     """Inputs longer than the factor-store budget run in windows; the state
     crosses them through the final-state buffer (or the workspace), and in the
     segmented form each window scans its own segments from that state."""
-    monkeypatch.setenv("KDA_FACTOR_BUDGET_MIB", "1")
     say("case %s H=%d lengths=%s dtype=%s fused=%s segment_tokens=%d budget 1 MiB"
         % (name, H, lengths, dtype, fused, seg))
     inp = kda_inputs.make_prefill(H, lengths, dtype, s0, fused, DEV, seed=zlib.crc32(name.encode()) & 0xFFFF)
@@ -126,13 +125,11 @@ def test_windows_parity(name, H, lengths, dtype, s0, fused, seg, monkeypatch):
         inp["norm_w"] = 1.0 + 0.1 * torch.randn(128, device=DEV)
     T = sum(lengths)
     big = kda.chunk_fwd_workspace_bytes(len(lengths), T, H, kda_inputs.torch_dtype(dtype), gated=fused,
-                                        segment_tokens=seg)
-    monkeypatch.delenv("KDA_FACTOR_BUDGET_MIB")
+                                        segment_tokens=seg, factor_budget_mib=1)
     one = kda.chunk_fwd_workspace_bytes(len(lengths), T, H, kda_inputs.torch_dtype(dtype), gated=fused,
                                         segment_tokens=seg)
-    monkeypatch.setenv("KDA_FACTOR_BUDGET_MIB", "1")
     assert big < one, (big, one)  # several windows: a smaller factor store
-    o, fs = run(inp, segment_tokens=seg)
+    o, fs = run(inp, segment_tokens=seg, factor_budget_mib=1)
     eo, es = compare_prefill(inp, o, fs)
     say("  err_o %.3e err_state %.3e" % (eo, es))
     assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
@@ -151,16 +148,14 @@ SLOW_CASES = [
 
 
 @pytest.mark.parametrize("name,H,lengths,dtype,seg,budget", SLOW_CASES, ids=[c[0] for c in SLOW_CASES])
-def test_slow_decay_parity(name, H, lengths, dtype, seg, budget, monkeypatch):
+def test_slow_decay_parity(name, H, lengths, dtype, seg, budget):
     """With the workloads' decay (log_alpha = -5 sigmoid(N(0,1))) a 64-token
     chunk decays by ~e^-160, so little state crosses chunk boundaries; here
     the decay is ~500x slower and the carried state dominates the outputs."""
-    if budget:
-        monkeypatch.setenv("KDA_FACTOR_BUDGET_MIB", budget)
     say("case %s H=%d lengths=%s dtype=%s segment_tokens=%d budget %s" % (name, H, lengths, dtype, seg, budget))
     inp = kda_inputs.make_prefill(H, lengths, dtype, 0.3, False, DEV, seed=zlib.crc32(name.encode()) & 0xFFFF)
     inp["log_alpha"].mul_(0.002)
-    o, fs = run(inp, segment_tokens=seg)
+    o, fs = run(inp, segment_tokens=seg, factor_budget_mib=int(budget or 0))
     eo, es = compare_prefill(inp, o, fs)
     say("  err_o %.3e err_state %.3e" % (eo, es))
     assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
