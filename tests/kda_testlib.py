@@ -4,7 +4,9 @@ the same bytes and compare with the tolerance metric.
 Tolerance metric: for each (sequence, head) slice of an output tensor,
 max|y - r| / max|r| (normwise relative error of the slice).  Bars: 2e-2 for
 bf16 inputs, 1e-4 for fp32 inputs.  A pure elementwise relative error is not
-used: outputs that are near zero would dominate it.
+used: outputs that are near zero would dominate it.  A secondary elementwise
+figure is reported beside it: max over elements of |y - r| / (|r| + rms(r)),
+with rms(r) the root mean square of the slice.
 """
 from __future__ import annotations
 
@@ -29,6 +31,17 @@ def slice_err(y, r):
     if den == 0.0:
         return 0.0 if num == 0.0 else float("inf")
     return float(num / den)
+
+
+def elem_err(y, r):
+    """Secondary elementwise figure of one slice: max |y - r| / (|r| + rms(r))."""
+    if r.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(np.square(r))))
+    d = np.abs(y - r)
+    if rms == 0.0:
+        return 0.0 if float(d.max()) == 0.0 else float("inf")
+    return float((d / (np.abs(r) + rms)).max())
 
 
 def prefill_errors(o, fs, o_ref, fs_ref, cu):
@@ -88,22 +101,46 @@ def library_inputs(inp):
     return kw
 
 
-def compare_prefill(inp, o, fs, heads=None, seqs=None):
-    """Compare library outputs against the oracle; returns (err_o, err_state)."""
+def compare_prefill_full(inp, o, fs, heads=None, seqs=None):
+    """Compare library outputs against the oracle: the normwise slice errors
+    (err_o, err_state) and the secondary elementwise ones (elem_o, elem_state)."""
     ref, hs = oracle_prefill(inp, heads, seqs)
     cu = inp["cu_host"].numpy()
-    eo, es = 0.0, 0.0
+    r = dict(err_o=0.0, err_state=0.0, elem_o=0.0, elem_state=0.0)
     for n, (o_ref, fs_ref) in ref.items():
         a, e = int(cu[n]), int(cu[n + 1])
         if e > a:
             y = to64(o[a:e][:, hs])
             for j in range(len(hs)):
-                eo = max(eo, slice_err(y[:, j], o_ref[:, j]))
+                r["err_o"] = max(r["err_o"], slice_err(y[:, j], o_ref[:, j]))
+                r["elem_o"] = max(r["elem_o"], elem_err(y[:, j], o_ref[:, j]))
         if fs is not None:
             ys = to64(fs[n][hs])
             for j in range(len(hs)):
-                es = max(es, slice_err(ys[j], fs_ref[j]))
-    return eo, es
+                r["err_state"] = max(r["err_state"], slice_err(ys[j], fs_ref[j]))
+                r["elem_state"] = max(r["elem_state"], elem_err(ys[j], fs_ref[j]))
+    return r
+
+
+def compare_prefill(inp, o, fs, heads=None, seqs=None):
+    """Compare library outputs against the oracle; returns (err_o, err_state)."""
+    r = compare_prefill_full(inp, o, fs, heads, seqs)
+    return r["err_o"], r["err_state"]
+
+
+def compare_all_heads(inp, o, fs, seqs=None, group=16, say=None):
+    """compare_prefill_full over every head, `group` heads per oracle call (so
+    host memory stays bounded at long contexts); the worst of each figure."""
+    H = inp["H"]
+    worst = dict(err_o=0.0, err_state=0.0, elem_o=0.0, elem_state=0.0)
+    for h0 in range(0, H, group):
+        r = compare_prefill_full(inp, o, fs, heads=range(h0, min(H, h0 + group)), seqs=seqs)
+        for key in worst:
+            worst[key] = max(worst[key], r[key])
+        if say:
+            say("  heads %d..%d: err_o %.3e err_state %.3e (elementwise %.3e / %.3e)"
+                % (h0, min(H, h0 + group) - 1, r["err_o"], r["err_state"], r["elem_o"], r["elem_state"]))
+    return worst
 
 
 def sync():
