@@ -10,9 +10,11 @@ time); this module only builds it with gcc, loads it with ctypes and
 marshals numpy arrays.  See that file's header for what is computed and the
 passages of the pages it follows.
 
-Pins (tests/test_oracle_pins.py, tests/test_oracle_replay_pins.py) tie it
-to the pages' worked examples, closed forms, brute-force products and, for
-the multi-token decode, to the prefill run over the same tokens.  The prologue/epilogue epsilon values
+Pins (tests/test_oracle_pins.py, tests/test_oracle_replay_pins.py,
+tests/test_oracle_bwd_pins.py) tie it to the pages' worked examples, closed
+forms, brute-force products, for the multi-token decode to the prefill run
+over the same tokens, and for the backward pass to central finite
+differences of the forward, closed forms and exact homogeneity identities.  The prologue/epilogue epsilon values
 and the convolution tap order are fixed only by our own reading of the pages
 (they print no numbers for them): parity unpinned for those constants.
 """
@@ -59,6 +61,10 @@ def _load():
                                                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                 ctypes.c_int, dp, dp, dp, dp, dp, dp, ctypes.c_double,
                                                 ctypes.c_double, dp, dp, dp, dp, ctypes.c_int]
+        lib.kda_oracle_chunk_bwd.restype = ctypes.c_int
+        lib.kda_oracle_chunk_bwd.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.POINTER(ctypes.c_int64), ctypes.c_int,
+                                             ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp, dp,
+                                             dp, dp, dp, dp, dp, ctypes.c_int]
         lib.kda_oracle_max_threads.restype = ctypes.c_int
         lib.kda_oracle_max_threads.argtypes = []
         _lib = lib
@@ -122,6 +128,44 @@ def chunk_fwd(q, k, v, log_alpha, beta, initial_state=None, cu_seqlens=None, *, 
     if rc != 0:
         raise RuntimeError("kda_oracle_chunk_fwd failed with code %d" % rc)
     return o, fs
+
+
+def chunk_bwd(q, k, v, log_alpha, beta, d_o, initial_state=None, cu_seqlens=None, d_final_state=None,
+              threads=0):
+    """Gradients of L = sum_t <d_o_t, o_t> + <d_final_state, S_T> through the
+    per-token recurrence (no prologue or epilogue).
+
+    Shapes as chunk_fwd; d_o [T, H, dv]; d_final_state [N, H, dk, dv] or None
+    (zero).  Returns (dq, dk, dv, dlog_alpha, dbeta, d_initial_state) with the
+    shapes of q, k, v, log_alpha, beta and [N, H, dk, dv].
+    """
+    lib = _load()
+    q, k, v, la, b, do = _f64(q), _f64(k), _f64(v), _f64(log_alpha), _f64(beta), _f64(d_o)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    assert k.shape == (T, H, dk) and la.shape == (T, H, dk) and v.shape == (T, H, dv)
+    assert b.shape == (T, H) and do.shape == (T, H, dv)
+    if cu_seqlens is None:
+        N, cu = 1, None
+    else:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        N = cu.shape[0] - 1
+        assert cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
+    s0, dsT = _f64(initial_state), _f64(d_final_state)
+    for x in (s0, dsT):
+        if x is not None:
+            assert x.shape == (N, H, dk, dv)
+    gq, gk, gla = (np.zeros((T, H, dk)) for _ in range(3))
+    gv = np.zeros((T, H, dv))
+    gb = np.zeros((T, H))
+    gs0 = np.zeros((N, H, dk, dv))
+    cu_p = None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    rc = lib.kda_oracle_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(b), _ptr(s0), cu_p, N, T, H, dk, dv,
+                                  _ptr(do), _ptr(dsT), _ptr(gq), _ptr(gk), _ptr(gv), _ptr(gla), _ptr(gb),
+                                  _ptr(gs0), int(threads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_chunk_bwd failed with code %d" % rc)
+    return gq, gk, gv, gla, gb, gs0
 
 
 def decode_step(state, q, k, v, log_alpha, beta, threads=0):

@@ -271,6 +271,165 @@ int kda_oracle_decode_multi(const double* state_in, const double* q, const doubl
   return err;
 }
 
+/* Backward pass (gradients) of the per-token recurrence above, without the
+ * prologue and epilogue.  "Kimi K3 架构、训练与系统全景解析", section 7.1
+ * (FlashKDA): the chunked KDA kernel serves training as well as prefill, so
+ * the recurrence needs its gradients.  The pages give no formula for them;
+ * this is the exact derivative of the forward definition for the loss
+ *
+ *   L = sum_t <do_t, o_t> + <dS_T, S_T>        (dS_T = d_final_state, or 0)
+ *
+ * taken by reverse accumulation through the token body's own steps.  With
+ * S the state before token t, Sp = Diag(a) S, vhat = Sp^T k, u = beta (v - vhat),
+ * S_t = Sp + k u^T and o_t = S_t^T q, and dS the gradient reaching S_t:
+ *
+ *   dq   = S_t do                     dS  += q do^T
+ *   dk   = dS u                       du   = dS^T k
+ *   dbeta = <du, v - vhat>            dv   = beta du          dvhat = -beta du
+ *   dSp  = dS + k dvhat^T             dk  += Sp dvhat
+ *   dlog_alpha_i = a_i sum_j dSp[i][j] S[i][j]                (a_i = exp(log_alpha_i))
+ *   gradient reaching S:  Diag(a) dSp
+ *
+ * and d_initial_state is the gradient that reaches S_0.  States are
+ * recomputed forward from checkpoints every BWD_SEG tokens (the recurrence
+ * cannot be run backwards: beta = 1 erases).  Layouts as the forward;
+ * d_o [T,H,dv], d_final_state [N,H,dk,dv] or NULL (zero); outputs dq, dk,
+ * dlog_alpha [T,H,dk], dv [T,H,dv], dbeta [T,H], d_initial_state
+ * [N,H,dk,dv] (or NULL: not written).  OpenMP over (sequence, head). */
+#define BWD_SEG 64
+
+int kda_oracle_chunk_bwd(const double* q, const double* k, const double* v, const double* log_alpha,
+                         const double* beta, const double* initial_state, const int64_t* cu_seqlens,
+                         int num_seqs, int64_t total_tokens, int H, int dk, int dv, const double* d_o,
+                         const double* d_final_state, double* dq, double* dkk, double* dvv, double* dlog_alpha,
+                         double* dbeta, double* d_initial_state, int num_threads) {
+  if (num_seqs < 1 || H < 1 || dk < 1 || dv < 1 || total_tokens < 0) return 1;
+  if (!cu_seqlens && num_seqs != 1) return 1;
+  const int64_t units = (int64_t)num_seqs * H;
+  const size_t SZ = (size_t)dk * dv;
+  const int nth = team_size(num_threads);
+  (void)nth; /* used by the parallel-for clause */
+  int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nth)
+  for (int64_t un = 0; un < units; ++un) {
+    const int n = (int)(un / H), h = (int)(un % H);
+    const int64_t bos = cu_seqlens ? cu_seqlens[n] : 0;
+    const int64_t eos = cu_seqlens ? cu_seqlens[n + 1] : total_tokens;
+    const int64_t len = eos - bos;
+    const int64_t nseg = (len + BWD_SEG - 1) / BWD_SEG;
+    /* checkpoints: the state before each segment; states of one segment */
+    double* ck = (double*)malloc(sizeof(double) * SZ * (size_t)(nseg > 0 ? nseg : 1));
+    double* st = (double*)malloc(sizeof(double) * SZ * (BWD_SEG + 1));
+    double* dS = (double*)malloc(sizeof(double) * SZ);
+    double* Sp = (double*)malloc(sizeof(double) * SZ);
+    double* w = (double*)malloc(sizeof(double) * (size_t)(3 * dv + dk));
+    if (!ck || !st || !dS || !Sp || !w) {
+#pragma omp atomic write
+      err = 2;
+      free(ck); free(st); free(dS); free(Sp); free(w);
+      continue;
+    }
+    double *vhat = w, *u = w + dv, *du = w + 2 * dv, *dvhat = du; /* dvhat reuses du's slot after use */
+    double* scratch_k = w + 3 * dv;
+    (void)scratch_k;
+    const size_t soff = ((size_t)n * H + h) * SZ;
+    /* forward sweep: checkpoints only */
+    double* S = st;
+    if (initial_state)
+      memcpy(S, initial_state + soff, sizeof(double) * SZ);
+    else
+      memset(S, 0, sizeof(double) * SZ);
+    for (int64_t sg = 0; sg < nseg; ++sg) {
+      memcpy(ck + (size_t)sg * SZ, S, sizeof(double) * SZ);
+      const int64_t t1 = bos + (sg + 1) * BWD_SEG < eos ? bos + (sg + 1) * BWD_SEG : eos;
+      for (int64_t t = bos + sg * BWD_SEG; t < t1; ++t) {
+        const size_t tk = ((size_t)t * H + h) * dk, tv = ((size_t)t * H + h) * dv;
+        kda_token(S, dk, dv, q + tk, k + tk, v + tv, log_alpha + tk, beta[(size_t)t * H + h], vhat, u);
+      }
+    }
+    /* reverse sweep */
+    if (d_final_state)
+      memcpy(dS, d_final_state + soff, sizeof(double) * SZ);
+    else
+      memset(dS, 0, sizeof(double) * SZ);
+    for (int64_t sg = nseg - 1; sg >= 0; --sg) {
+      const int64_t t0 = bos + sg * BWD_SEG;
+      const int64_t t1 = t0 + BWD_SEG < eos ? t0 + BWD_SEG : eos;
+      /* st[i] = state before token t0 + i, st[i + 1] = after it */
+      memcpy(st, ck + (size_t)sg * SZ, sizeof(double) * SZ);
+      for (int64_t t = t0; t < t1; ++t) {
+        const size_t tk = ((size_t)t * H + h) * dk, tv = ((size_t)t * H + h) * dv;
+        double* nxt = st + (size_t)(t - t0 + 1) * SZ;
+        memcpy(nxt, st + (size_t)(t - t0) * SZ, sizeof(double) * SZ);
+        kda_token(nxt, dk, dv, q + tk, k + tk, v + tv, log_alpha + tk, beta[(size_t)t * H + h], vhat, u);
+      }
+      for (int64_t t = t1 - 1; t >= t0; --t) {
+        const size_t tk = ((size_t)t * H + h) * dk, tv = ((size_t)t * H + h) * dv;
+        const double* S0 = st + (size_t)(t - t0) * SZ;     /* before token t */
+        const double* S1 = st + (size_t)(t - t0 + 1) * SZ; /* after token t  */
+        const double* qt = q + tk;
+        const double* kt = k + tk;
+        const double* vt = v + tv;
+        const double* la = log_alpha + tk;
+        const double* dot = d_o + tv;
+        const double bt = beta[(size_t)t * H + h];
+        /* recompute Sp, vhat, u of this token */
+        for (int i = 0; i < dk; ++i) {
+          const double a = exp(la[i]);
+          for (int j = 0; j < dv; ++j) Sp[(size_t)i * dv + j] = a * S0[(size_t)i * dv + j];
+        }
+        for (int j = 0; j < dv; ++j) vhat[j] = 0.0;
+        for (int i = 0; i < dk; ++i)
+          for (int j = 0; j < dv; ++j) vhat[j] += Sp[(size_t)i * dv + j] * kt[i];
+        for (int j = 0; j < dv; ++j) u[j] = bt * (vt[j] - vhat[j]);
+        /* o_t = S_t^T q:  dq = S_t do,  dS += q do^T */
+        for (int i = 0; i < dk; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < dv; ++j) acc += S1[(size_t)i * dv + j] * dot[j];
+          dq[tk + i] = acc;
+          for (int j = 0; j < dv; ++j) dS[(size_t)i * dv + j] += qt[i] * dot[j];
+        }
+        /* S_t = Sp + k u^T:  dk = dS u,  du = dS^T k */
+        for (int j = 0; j < dv; ++j) du[j] = 0.0;
+        for (int i = 0; i < dk; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < dv; ++j) {
+            acc += dS[(size_t)i * dv + j] * u[j];
+            du[j] += dS[(size_t)i * dv + j] * kt[i];
+          }
+          dkk[tk + i] = acc;
+        }
+        /* u = beta (v - vhat) */
+        double db = 0.0;
+        for (int j = 0; j < dv; ++j) {
+          db += du[j] * (vt[j] - vhat[j]);
+          dvv[tv + j] = bt * du[j];
+          dvhat[j] = -bt * du[j]; /* overwrites du in place */
+        }
+        dbeta[(size_t)t * H + h] = db;
+        /* vhat = Sp^T k:  dSp = dS + k dvhat^T,  dk += Sp dvhat */
+        for (int i = 0; i < dk; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < dv; ++j) acc += Sp[(size_t)i * dv + j] * dvhat[j];
+          dkk[tk + i] += acc;
+          for (int j = 0; j < dv; ++j) dS[(size_t)i * dv + j] += kt[i] * dvhat[j];
+        }
+        /* Sp = Diag(a) S:  dlog_alpha_i = a_i <dSp[i], S[i]>,  dS <- Diag(a) dSp */
+        for (int i = 0; i < dk; ++i) {
+          const double a = exp(la[i]);
+          double acc = 0.0;
+          for (int j = 0; j < dv; ++j) acc += dS[(size_t)i * dv + j] * S0[(size_t)i * dv + j];
+          dlog_alpha[tk + i] = a * acc;
+          for (int j = 0; j < dv; ++j) dS[(size_t)i * dv + j] *= a;
+        }
+      }
+    }
+    if (d_initial_state) memcpy(d_initial_state + soff, dS, sizeof(double) * SZ);
+    free(ck); free(st); free(dS); free(Sp); free(w);
+  }
+  return err;
+}
+
 /* Number of threads an OpenMP parallel region would use (1 without OpenMP). */
 int kda_oracle_max_threads(void) {
 #ifdef _OPENMP
