@@ -19,7 +19,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "decode_step", "decode_replay", "chunk_fwd_workspace_bytes", "status_string", "KDAError",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "decode_step", "decode_replay", "chunk_fwd_workspace_bytes", "status_string", "KDAError",
            "last_precondition_flags",
            "library_path", "D", "REPLAY_MAX_TOKENS"]
 
@@ -29,7 +29,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda.so")
 _lib = None
 
-KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP, KDA_ERR_PRECONDITION = range(6)
+(KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP, KDA_ERR_PRECONDITION,
+ KDA_ERR_SCRATCH) = range(7)
+# size of the device scratch array behind chunk_fwd_noalloc (KDA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 128 << 20
 # KDA_DEBUG_CHECKS precondition bits (kda_last_precondition_flags)
 CHECK_LOG_ALPHA, CHECK_BETA, CHECK_Q_NORM, CHECK_K_NORM, CHECK_CU_SEQLENS = 1, 2, 4, 8, 16
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
@@ -68,6 +71,8 @@ def _load():
     lib.kda_chunk_fwd.restype = i32
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, vp, vp, vp, vp,
                                   sz, vp]
+    lib.kda_chunk_fwd_noalloc.restype = i32
+    lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.kda_decode_step.restype = i32
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.kda_last_precondition_flags.restype = ctypes.c_uint32
@@ -150,6 +155,54 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
     (in-place continuation).
     """
     lib = _load()
+    a = _prefill_args(q, k, v, log_alpha, beta, initial_state, cu_seqlens, conv_q_w, conv_k_w, gate, norm_w,
+                      l2_eps, rms_eps, out, final_state, output_final_state, segment_tokens, unbounded_decay,
+                      factor_budget_mib)
+    N, T, H, dtc, opts_p = a["N"], a["T"], a["H"], a["dtc"], a["opts_p"]
+    dev = q.device
+    need = int(lib.kda_chunk_fwd_workspace_bytes(N, T, H, D, D, dtc, opts_p))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
+                           _ptr(cu_seqlens), N, T, H, D, D, dtc, opts_p, _ptr(a["out"]), _ptr(a["final_state"]),
+                           _ptr(workspace), ws_bytes, _stream(dev))
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_chunk_fwd")
+    return a["out"], a["final_state"]
+
+
+def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+                      beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                      cu_seqlens: Optional[torch.Tensor] = None, *, out: torch.Tensor,
+                      final_state: Optional[torch.Tensor] = None, conv_q_w: Optional[torch.Tensor] = None,
+                      conv_k_w: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
+                      norm_w: Optional[torch.Tensor] = None, l2_eps: float = 1e-6, rms_eps: float = 1e-6,
+                      segment_tokens: int = 0, unbounded_decay: bool = False,
+                      factor_budget_mib: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """chunk_fwd without a workspace (kda_chunk_fwd_noalloc): the library's
+    own NOALLOC_SCRATCH_BYTES device array takes its place and the factor
+    store runs in windows that fit it.  The caller passes the outputs (`out`,
+    and `final_state` or None), so this function allocates nothing on the
+    device.  Calls that overlap in time on one GPU share that GPU's array and
+    race.  Raises KDAError with KDA_ERR_SCRATCH when the sizes need more."""
+    lib = _load()
+    a = _prefill_args(q, k, v, log_alpha, beta, initial_state, cu_seqlens, conv_q_w, conv_k_w, gate, norm_w,
+                      l2_eps, rms_eps, out, final_state, False, segment_tokens, unbounded_decay,
+                      factor_budget_mib)
+    rc = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
+                                   _ptr(cu_seqlens), a["N"], a["T"], a["H"], D, D, a["dtc"], a["opts_p"],
+                                   _ptr(a["out"]), _ptr(a["final_state"]), _stream(q.device))
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_chunk_fwd_noalloc")
+    return a["out"], a["final_state"]
+
+
+def _prefill_args(q, k, v, log_alpha, beta, initial_state, cu_seqlens, conv_q_w, conv_k_w, gate, norm_w, l2_eps,
+                  rms_eps, out, final_state, output_final_state, segment_tokens, unbounded_decay,
+                  factor_budget_mib) -> dict:
+    """Checks the prefill's tensors, allocates the outputs the caller left
+    out (only when asked) and builds the options struct."""
     if q.dim() != 3 or q.shape[2] != D:
         raise ValueError("q must be [T, H, 128]")
     T, H, _ = q.shape
@@ -187,23 +240,14 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
         final_state = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
     elif final_state is not None:
         _check(final_state, "final_state", (N, H, D, D), torch.float32, dev)
-    dtc = _DTYPES[dt]
     opts = None
     if (any(x is not None for x in (conv_q_w, conv_k_w, gate, norm_w)) or segment_tokens != 0 or unbounded_decay
             or factor_budget_mib != 0):
         opts = _FusedOpts(_ptr(conv_q_w), _ptr(conv_k_w), _ptr(gate), _ptr(norm_w), float(l2_eps),
                           float(rms_eps), int(segment_tokens), int(bool(unbounded_decay)), int(factor_budget_mib))
-    opts_p = ctypes.byref(opts) if opts is not None else None
-    need = int(lib.kda_chunk_fwd_workspace_bytes(N, T, H, D, D, dtc, opts_p))
-    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
-                           _ptr(cu_seqlens), N, T, H, D, D, dtc, opts_p, _ptr(out), _ptr(final_state),
-                           _ptr(workspace), ws_bytes, _stream(dev))
-    if rc != KDA_OK:
-        raise KDAError(rc, "kda_chunk_fwd")
-    return out, final_state
+    # the struct must outlive the call: keep it in the returned dict
+    return dict(N=N, T=T, H=H, dtc=_DTYPES[dt], opts=opts, opts_p=ctypes.byref(opts) if opts is not None else None,
+                out=out, final_state=final_state)
 
 
 def decode_step(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

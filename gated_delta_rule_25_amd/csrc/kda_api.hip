@@ -11,6 +11,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "kda.h"
 #include "kda_internal.h"
@@ -193,6 +194,33 @@ bool segments_ok(const Plan& pl, int num_heads, const kda_fused_opts& f) {
   return pl.seg_chunks == 0 || pl.cap * num_heads <= (int64_t)INT32_MAX / 8;
 }
 
+// Scratch of kda_chunk_fwd_noalloc.  Each GPU holds its own copy at its own
+// address; in host code the array's name is only a stand-in, so the address
+// passed to kernels is the one hipGetSymbolAddress gives for the current device.
+__device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device.
+hipError_t scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -206,6 +234,8 @@ const char* kda_status_string(kda_status s) {
     case KDA_ERR_HIP: return "HIP runtime or launch error";
     case KDA_ERR_PRECONDITION:
       return "input outside the documented preconditions (KDA_DEBUG_CHECKS; see kda_last_precondition_flags())";
+    case KDA_ERR_SCRATCH:
+      return "sizes need more device scratch than kda_chunk_fwd_noalloc holds (KDA_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown kda_status";
 }
@@ -403,6 +433,39 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     if (kda::launch_carry(c2, stream) != hipSuccess) return KDA_ERR_HIP;
   }
   return KDA_OK;
+}
+
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* log_alpha,
+                                 const float* beta, const float* initial_state, const int32_t* cu_seqlens,
+                                 int num_seqs, int64_t total_tokens, int num_heads, int d_k, int d_v,
+                                 kda_dtype dtype, const kda_fused_opts* opts, void* o, float* final_state,
+                                 hipStream_t stream) {
+  if (num_seqs < 1 || num_heads < 1 || total_tokens < 0) return KDA_ERR_INVALID_ARG;
+  if (d_k != kD || d_v != kD || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+  if (!sizes_ok(num_seqs, total_tokens, num_heads)) return KDA_ERR_INVALID_ARG;
+  const kda_fused_opts& f = opts ? *opts : kNoOpts;
+  if (f.factor_budget_mib < 0) return KDA_ERR_INVALID_ARG;
+  // The largest window budget whose whole plan fits the scratch array: each
+  // step lowers the budget by at least the plan's excess (the plan shrinks by
+  // at most that much per MiB of budget), down to 1 MiB.
+  constexpr size_t kScratch = KDA_NOALLOC_SCRATCH_BYTES;
+  constexpr int64_t kScratchMiB = (int64_t)(kScratch >> 20);
+  int64_t mib = f.factor_budget_mib > 0 ? std::min<int64_t>(f.factor_budget_mib, kScratchMiB) : kScratchMiB;
+  const int cus = cu_count_for_current_device();
+  kda_fused_opts g = f;
+  for (;;) {
+    g.factor_budget_mib = (int)mib;
+    const Plan pl = make_plan(num_seqs, total_tokens, num_heads, dtype, g, cus);
+    if (!segments_ok(pl, num_heads, g)) return KDA_ERR_INVALID_ARG;
+    if (pl.bytes <= kScratch) break;
+    if (mib == 1) return KDA_ERR_SCRATCH;
+    const int64_t over = (int64_t)((pl.bytes - kScratch + (1u << 20) - 1) >> 20);
+    mib = std::max<int64_t>(1, mib - std::max<int64_t>(1, over));
+  }
+  void* ws = nullptr;
+  if (scratch_for_current_device(&ws) != hipSuccess) return KDA_ERR_HIP;
+  return kda_chunk_fwd(q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, d_k,
+                       d_v, dtype, &g, o, final_state, ws, kScratch, stream);
 }
 
 kda_status kda_decode_step(float* state, const void* q, const void* k, const void* v, const float* log_alpha,

@@ -58,7 +58,8 @@ typedef enum {
   KDA_ERR_UNSUPPORTED = 2, /* d_k or d_v other than 128, unknown dtype       */
   KDA_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required        */
   KDA_ERR_HIP = 4,         /* a HIP launch or runtime call failed            */
-  KDA_ERR_PRECONDITION = 5 /* an input outside the preconditions (only with KDA_DEBUG_CHECKS) */
+  KDA_ERR_PRECONDITION = 5, /* an input outside the preconditions (only with KDA_DEBUG_CHECKS) */
+  KDA_ERR_SCRATCH = 6       /* kda_chunk_fwd_noalloc: the sizes need more than its scratch array */
 } kda_status;
 
 /*
@@ -183,6 +184,43 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          int num_seqs, int64_t total_tokens, int num_heads, int d_k, int d_v,
                          kda_dtype dtype, const kda_fused_opts* opts, void* o, float* final_state,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Bytes of the device scratch array behind kda_chunk_fwd_noalloc: one copy on
+ * every GPU the library runs on, held until the process ends.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/*
+ * kda_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, semantics and results are those of kda_chunk_fwd without the
+ * workspace; the library's own scratch array of KDA_NOALLOC_SCRATCH_BYTES on
+ * the current device takes its place.  The factor store is cut into as many
+ * windows as it takes to fit that array (opts->factor_budget_mib, when
+ * positive, caps each window further), so large inputs run in more, smaller
+ * windows than kda_chunk_fwd would use.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); its first call on a
+ * device looks up that device's copy of the array.
+ *
+ * Errors: those of kda_chunk_fwd (never KDA_ERR_WORKSPACE), plus
+ * KDA_ERR_SCRATCH, returned before anything is enqueued, when even the
+ * smallest windows do not fit: the floor is about (N + 2) * H * 70.5 KiB of
+ * factor blocks (bf16; 68.5 KiB for fp32) plus N * H * 64 KiB for the state
+ * carried between windows, so for example N = 1 fits up to H of about 500 and
+ * H = 96 up to N of about 9.
+ *
+ * Every call on one GPU uses that GPU's one array and leaves its contents
+ * behind.  Nothing in it needs to start at zero (each byte a call reads was
+ * written earlier in the same call), but calls that overlap in time on one
+ * GPU (on different streams, or from different threads) race on it and give
+ * wrong results: serialise them.
+ */
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* log_alpha,
+                                 const float* beta, const float* initial_state, const int32_t* cu_seqlens,
+                                 int num_seqs, int64_t total_tokens, int num_heads, int d_k, int d_v,
+                                 kda_dtype dtype, const kda_fused_opts* opts, void* o, float* final_state,
+                                 hipStream_t stream);
 
 /*
  * One decode step for N independent sequences: each (n, h) state advances by

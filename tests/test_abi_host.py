@@ -20,7 +20,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LIB = os.path.join(ROOT, "gated_delta_rule_25_amd", "libkda.so")
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = range(5)
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR, PRECONDITION, SCRATCH = range(7)
 F32, BF16 = 0, 1
 
 
@@ -37,6 +37,8 @@ def lib():
     L.kda_chunk_fwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32, vp]
     L.kda_chunk_fwd.restype = i32
     L.kda_chunk_fwd.argtypes = [vp] * 7 + [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.kda_chunk_fwd_noalloc.restype = i32
+    L.kda_chunk_fwd_noalloc.argtypes = [vp] * 7 + [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp]
     L.kda_decode_step.restype = i32
     L.kda_decode_step.argtypes = [vp] * 6 + [i32, i32, i32, i32, i32, vp, vp]
     L.kda_decode_replay.restype = i32
@@ -52,7 +54,7 @@ def declared_functions():
 
 def test_header_symbols_exported(lib):
     names = declared_functions()
-    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_decode_step",
+    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_workspace_bytes", "kda_decode_step",
                           "kda_decode_replay", "kda_last_precondition_flags", "kda_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s+(kda_\w+)", out))
@@ -62,7 +64,7 @@ def test_header_symbols_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(6):
+    for code in range(7):
         s = lib.kda_status_string(code).decode()
         assert s and s != "unknown kda_status"
     assert lib.kda_status_string(99).decode() == "unknown kda_status"
@@ -218,6 +220,30 @@ def test_chunk_validation_fused(lib):
     assert chunk(lib, opts=ctypes.cast(ctypes.pointer(o), ctypes.c_void_p)) == INVALID
     o2 = Opts(None, None, None, None, -1.0, 1e-6, 0)          # negative epsilon
     assert chunk(lib, opts=ctypes.cast(ctypes.pointer(o2), ctypes.c_void_p)) == INVALID
+
+
+def test_noalloc_limits(lib):
+    """kda_chunk_fwd_noalloc: its scratch size in the binding matches the
+    header, and sizes whose smallest windows exceed the array are refused on
+    the host (64 sequences x 96 heads need ~65 x 96 factor blocks of 70.5 KiB
+    plus the carried states, far past 128 MiB), as are bad sizes."""
+    import gated_delta_rule_25_amd as kda
+    m = re.search(r"#define KDA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert kda.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+
+    def na(**kw):
+        a = dict(q=p(0), k=p(1), v=p(2), la=p(3), b=p(4), s0=None, cu=p(7), N=64, T=256, H=96, dk=128, dv=128,
+                 dt=BF16, opts=None, o=p(5), fs=None)
+        a.update(kw)
+        return lib.kda_chunk_fwd_noalloc(a["q"], a["k"], a["v"], a["la"], a["b"], a["s0"], a["cu"], a["N"], a["T"],
+                                         a["H"], a["dk"], a["dv"], a["dt"], a["opts"], a["o"], a["fs"], None)
+    assert na() == SCRATCH
+    assert na(N=1, cu=None, H=2000) == SCRATCH
+    assert na(dk=64) == UNSUPPORTED
+    assert na(N=0) == INVALID
+    assert na(T=-1) == INVALID
+    assert na(opts=opts_p(Opts(factor_budget_mib=-5))) == INVALID
+    assert na(N=1, cu=None, H=2, opts=opts_p(Opts(segment_tokens=100))) == INVALID
 
 
 def decode(lib, **kw):
