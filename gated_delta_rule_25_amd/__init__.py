@@ -8,6 +8,7 @@ runs in the HIP kernels of libkda.so; there is no fallback path.  If the
 library is not built this module raises on first use.
 
     o, final_state = chunk_fwd(q, k, v, log_alpha, beta, initial_state, cu_seqlens)
+    dq, dk, dv, dlog_alpha, dbeta, d_initial_state = chunk_bwd(q, k, v, log_alpha, beta, d_o, ...)
     o = decode_step(state, q, k, v, log_alpha, beta)      # state updated in place
     o, state_out = decode_replay(state, q, k, v, log_alpha, beta, num_tokens, state_out=state)
 """
@@ -19,7 +20,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "decode_step", "decode_replay", "chunk_fwd_workspace_bytes", "status_string", "KDAError",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_bwd", "chunk_bwd_workspace_bytes", "decode_step", "decode_replay", "chunk_fwd_workspace_bytes", "status_string", "KDAError",
            "last_precondition_flags",
            "library_path", "D", "REPLAY_MAX_TOKENS"]
 
@@ -73,6 +74,10 @@ def _load():
                                   sz, vp]
     lib.kda_chunk_fwd_noalloc.restype = i32
     lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.kda_chunk_bwd_workspace_bytes.restype = sz
+    lib.kda_chunk_bwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32]
+    lib.kda_chunk_bwd.restype = i32
+    lib.kda_chunk_bwd.argtypes = [vp] * 9 + [i32, i64, i32, i32, i32, i32] + [vp] * 7 + [sz, vp]
     lib.kda_decode_step.restype = i32
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.kda_last_precondition_flags.restype = ctypes.c_uint32
@@ -196,6 +201,66 @@ def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alp
     if rc != KDA_OK:
         raise KDAError(rc, "kda_chunk_fwd_noalloc")
     return a["out"], a["final_state"]
+
+
+def chunk_bwd_workspace_bytes(num_seqs: int, total_tokens: int, num_heads: int,
+                              dtype: torch.dtype = torch.bfloat16) -> int:
+    """Workspace bytes of chunk_bwd (every chunk of the input at once)."""
+    return int(_load().kda_chunk_bwd_workspace_bytes(num_seqs, total_tokens, num_heads, D, D, _DTYPES[dtype]))
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor, beta: torch.Tensor,
+              d_o: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, d_final_state: Optional[torch.Tensor] = None, *,
+              need_d_initial_state: bool = True, workspace: Optional[torch.Tensor] = None):
+    """Gradients of sum <d_o, o> + <d_final_state, S_T> through chunk_fwd
+    (kda_chunk_bwd; no fused prologue or epilogue, log_alpha in [-5, 0]).
+
+    Inputs as chunk_fwd; d_o [T, H, 128] in the I/O dtype; d_final_state
+    [N, H, 128, 128] float32 or None (zero).  Returns (dq, dk, dv, dlog_alpha,
+    dbeta, d_initial_state) with the shapes and dtypes of q, k, v, log_alpha,
+    beta and the initial state (float32; None when need_d_initial_state is
+    False)."""
+    lib = _load()
+    if q.dim() != 3 or q.shape[2] != D:
+        raise ValueError("q must be [T, H, 128]")
+    T, H, _ = q.shape
+    dev, dt = q.device, q.dtype
+    if dt not in _DTYPES:
+        raise TypeError("q/k/v must be float32 or bfloat16")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    for name, t in (("q", q), ("k", k), ("v", v), ("d_o", d_o)):
+        _check(t, name, (T, H, D), dt, dev)
+    _check(log_alpha, "log_alpha", (T, H, D), torch.float32, dev)
+    _check(beta, "beta", (T, H), torch.float32, dev)
+    if cu_seqlens is None:
+        N = 1
+    else:
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be [N+1]")
+        N = cu_seqlens.numel() - 1
+        _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if t is not None:
+            _check(t, name, (N, H, D, D), torch.float32, dev)
+    dq, dk, dv = (torch.empty((T, H, D), dtype=dt, device=dev) for _ in range(3))
+    dla = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    db = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ds0 = torch.empty((N, H, D, D), dtype=torch.float32, device=dev) if need_d_initial_state else None
+    dtc = _DTYPES[dt]
+    need = int(lib.kda_chunk_bwd_workspace_bytes(N, T, H, D, D, dtc))
+    if need == 0:
+        raise ValueError("chunk_bwd: unsupported sizes")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    rc = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
+                           _ptr(cu_seqlens), _ptr(d_o), _ptr(d_final_state), N, T, H, D, D, dtc, _ptr(dq), _ptr(dk),
+                           _ptr(dv), _ptr(dla), _ptr(db), _ptr(ds0), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(dev))
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_chunk_bwd")
+    return dq, dk, dv, dla, db, ds0
 
 
 def _prefill_args(q, k, v, log_alpha, beta, initial_state, cu_seqlens, conv_q_w, conv_k_w, gate, norm_w, l2_eps,

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libkda.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_replay.hip", "kda_debug.hip", "kda_scan.hip", "kda_chunk.hip", "kda_prep.hip"]
+SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_replay.hip", "kda_debug.hip", "kda_scan.hip", "kda_chunk.hip", "kda_prep.hip", "kda_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

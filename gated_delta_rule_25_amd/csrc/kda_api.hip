@@ -194,6 +194,54 @@ bool segments_ok(const Plan& pl, int num_heads, const kda_fused_opts& f) {
   return pl.seg_chunks == 0 || pl.cap * num_heads <= (int64_t)INT32_MAX / 8;
 }
 
+// Workspace of kda_chunk_bwd: one window holding every chunk (slot = global
+// chunk index).  Pieces, each 256-byte aligned: the longest-first order [N]
+// (N > 1), the chunk table (seq_first [N+1], seq_c0 [N], seq_c1 [N]), the
+// forward factor blocks and the reverse-carry blocks [slots][H], then per
+// (slot, head) the chunk's incoming state and the gradient at its end
+// ([128][128] fp32 each) and U and dU ([C][128] fp32 each).
+struct BwdPlan {
+  int64_t slots = 0;
+  size_t off_first = 0, off_c0 = 0, off_c1 = 0, off_factors = 0, off_dblocks = 0;
+  size_t off_states = 0, off_u = 0, off_ds = 0, off_du = 0;
+  size_t bytes = 0;
+};
+
+BwdPlan make_bwd_plan(int num_seqs, int64_t total_tokens, int num_heads, kda_dtype dtype) {
+  BwdPlan pl;
+  const bool bf = dtype == KDA_DTYPE_BF16;
+  const int64_t C = kda::chunk_len(bf);
+  pl.slots = total_tokens / C + num_seqs + 1;
+  const size_t units = (size_t)pl.slots * num_heads;
+  size_t off = num_seqs > 1 ? align256((size_t)num_seqs * sizeof(int32_t)) : 0;
+  pl.off_first = off;
+  off += align256((size_t)(num_seqs + 1) * sizeof(int32_t));
+  pl.off_c0 = off;
+  off += align256((size_t)num_seqs * sizeof(int32_t));
+  pl.off_c1 = off;
+  off += align256((size_t)num_seqs * sizeof(int32_t));
+  pl.off_factors = off;
+  off += units * kda::factor_block_bytes(bf);
+  pl.off_dblocks = off;
+  off += units * kda::dcarry_block_bytes(bf);
+  pl.off_states = off;
+  off += units * kD * kD * sizeof(float);
+  pl.off_ds = off;
+  off += units * kD * kD * sizeof(float);
+  pl.off_u = off;
+  off += units * (size_t)C * kD * sizeof(float);
+  pl.off_du = off;
+  off += units * (size_t)C * kD * sizeof(float);
+  pl.bytes = off;
+  return pl;
+}
+
+bool bwd_sizes_ok(int num_seqs, int64_t total_tokens, int num_heads, kda_dtype dtype) {
+  if (!sizes_ok(num_seqs, total_tokens, num_heads)) return false;
+  const int64_t slots = total_tokens / kda::chunk_len(dtype == KDA_DTYPE_BF16) + num_seqs + 1;
+  return slots <= (int64_t)INT32_MAX / 2 && slots * num_heads <= (int64_t)UINT32_MAX;
+}
+
 // Scratch of kda_chunk_fwd_noalloc.  Each GPU holds its own copy at its own
 // address; in host code the array's name is only a stand-in, so the address
 // passed to kernels is the one hipGetSymbolAddress gives for the current device.
@@ -466,6 +514,163 @@ kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, co
   if (scratch_for_current_device(&ws) != hipSuccess) return KDA_ERR_HIP;
   return kda_chunk_fwd(q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, d_k,
                        d_v, dtype, &g, o, final_state, ws, kScratch, stream);
+}
+
+size_t kda_chunk_bwd_workspace_bytes(int num_seqs, int64_t total_tokens, int num_heads, int d_k, int d_v,
+                                     kda_dtype dtype) {
+  if (d_k != kD || d_v != kD || !dtype_ok(dtype) || !bwd_sizes_ok(num_seqs, total_tokens, num_heads, dtype)) return 0;
+  return make_bwd_plan(num_seqs, total_tokens, num_heads, dtype).bytes;
+}
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                         const float* initial_state, const int32_t* cu_seqlens, const void* d_o,
+                         const float* d_final_state, int num_seqs, int64_t total_tokens, int num_heads, int d_k,
+                         int d_v, kda_dtype dtype, void* dq, void* dk, void* dv, float* dlog_alpha, float* dbeta,
+                         float* d_initial_state, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (num_seqs < 1 || num_heads < 1 || total_tokens < 0) return KDA_ERR_INVALID_ARG;
+  if (d_k != kD || d_v != kD || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+  if (!cu_seqlens && num_seqs != 1) return KDA_ERR_INVALID_ARG;
+  if (!bwd_sizes_ok(num_seqs, total_tokens, num_heads, dtype)) return KDA_ERR_INVALID_ARG;
+  if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !d_o || !dq || !dk || !dv || !dlog_alpha ||
+                           !dbeta))
+    return KDA_ERR_INVALID_ARG;
+  {
+    const void* vec[] = {q, k, v, log_alpha, initial_state, d_o, d_final_state, dq, dk, dv, dlog_alpha,
+                         d_initial_state, workspace};
+    for (const void* ptr : vec)
+      if (!aligned(ptr, 16)) return KDA_ERR_INVALID_ARG;
+    const void* sca[] = {beta, cu_seqlens, dbeta};
+    for (const void* ptr : sca)
+      if (!aligned(ptr, 4)) return KDA_ERR_INVALID_ARG;
+  }
+  const BwdPlan pl = make_bwd_plan(num_seqs, total_tokens, num_heads, dtype);
+  if (!workspace || workspace_bytes < pl.bytes) return KDA_ERR_WORKSPACE;
+
+  const size_t es = elem_size(dtype);
+  const size_t tok_elems = (size_t)total_tokens * num_heads * kD;
+  const size_t state_bytes = (size_t)num_seqs * num_heads * kD * kD * sizeof(float);
+  const size_t beta_bytes = (size_t)total_tokens * num_heads * sizeof(float);
+  const Range ins[] = {range_of(q, tok_elems * es), range_of(k, tok_elems * es), range_of(v, tok_elems * es),
+                       range_of(log_alpha, tok_elems * sizeof(float)), range_of(beta, beta_bytes),
+                       range_of(initial_state, state_bytes),
+                       range_of(cu_seqlens, cu_seqlens ? (size_t)(num_seqs + 1) * sizeof(int32_t) : 0),
+                       range_of(d_o, tok_elems * es), range_of(d_final_state, d_final_state ? state_bytes : 0)};
+  const Range outs[] = {range_of(dq, tok_elems * es), range_of(dk, tok_elems * es), range_of(dv, tok_elems * es),
+                        range_of(dlog_alpha, tok_elems * sizeof(float)), range_of(dbeta, beta_bytes),
+                        range_of(d_initial_state, d_initial_state ? state_bytes : 0),
+                        range_of(workspace, pl.bytes)};
+  constexpr int kOuts = sizeof(outs) / sizeof(outs[0]);
+  for (int i = 0; i < kOuts; ++i) {
+    for (const Range& in : ins)
+      if (overlap(outs[i], in)) return KDA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < kOuts; ++j)
+      if (overlap(outs[i], outs[j])) return KDA_ERR_INVALID_ARG;
+  }
+  const bool bf16 = dtype == KDA_DTYPE_BF16;
+  {
+    kda::CheckArgs chk;
+    std::memset(&chk, 0, sizeof(chk));
+    chk.rows = total_tokens * num_heads;
+    chk.heads = num_heads;
+    chk.tokens_per_seq = 1;
+    chk.log_alpha = log_alpha;
+    chk.beta = beta;
+    chk.q = q;
+    chk.k = k;
+    chk.cu = cu_seqlens;
+    chk.num_seqs = num_seqs;
+    chk.total_tokens = total_tokens;
+    chk.bf16 = bf16;
+    chk.la_min = kBoundedLaMin;
+    const kda_status cs = checked(chk, stream);
+    if (cs != KDA_OK) return cs;
+  }
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* order = num_seqs > 1 ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  int32_t* seq_first = reinterpret_cast<int32_t*>(ws + pl.off_first);
+  int32_t* seq_c0 = reinterpret_cast<int32_t*>(ws + pl.off_c0);
+  int32_t* seq_c1 = reinterpret_cast<int32_t*>(ws + pl.off_c1);
+  void* factors = ws + pl.off_factors;
+  float* chunk_states = reinterpret_cast<float*>(ws + pl.off_states);
+  float* chunk_u = reinterpret_cast<float*>(ws + pl.off_u);
+  if (num_seqs > 1 && kda::launch_worklist(cu_seqlens, num_seqs, order, stream) != hipSuccess) return KDA_ERR_HIP;
+  if (kda::launch_window_table(cu_seqlens, num_seqs, total_tokens, kda::chunk_len(bf16), 1, 0, (int)pl.slots,
+                               seq_first, seq_c0, seq_c1, stream) != hipSuccess)
+    return KDA_ERR_HIP;
+  // forward factors and, per chunk, the incoming state and U (states pass)
+  kda::PrepArgs pa;
+  std::memset(&pa, 0, sizeof(pa));
+  pa.q = q;
+  pa.k = k;
+  pa.v = v;
+  pa.log_alpha = log_alpha;
+  pa.beta = beta;
+  pa.cu = cu_seqlens;
+  pa.l2_eps = 1e-6f;
+  pa.num_seqs = num_seqs;
+  pa.num_heads = num_heads;
+  pa.total_tokens = total_tokens;
+  pa.bf16 = bf16;
+  pa.seq_first = seq_first;
+  pa.seq_c0 = seq_c0;
+  pa.cap = (int)pl.slots;
+  pa.chunks_per_block = kPrepChunksPerBlock;
+  pa.factors = factors;
+  if (kda::launch_prep(pa, stream) != hipSuccess) return KDA_ERR_HIP;
+  kda::CarryArgs ca;
+  std::memset(&ca, 0, sizeof(ca));
+  ca.factors = factors;
+  ca.cu = cu_seqlens;
+  ca.order = order;
+  ca.seq_first = seq_first;
+  ca.seq_c0 = seq_c0;
+  ca.seq_c1 = seq_c1;
+  ca.state_in = initial_state;
+  ca.num_seqs = num_seqs;
+  ca.num_heads = num_heads;
+  ca.total_tokens = total_tokens;
+  ca.units = num_seqs * num_heads;
+  ca.col_split = 2;
+  ca.bf16 = bf16;
+  ca.pass = 3;
+  ca.chunk_states = chunk_states;
+  ca.chunk_u = chunk_u;
+  if (kda::launch_carry(ca, stream) != hipSuccess) return KDA_ERR_HIP;
+  // reverse-carry blocks, the reverse carry, the gradients
+  kda::BwdArgs ba;
+  std::memset(&ba, 0, sizeof(ba));
+  ba.q = q;
+  ba.k = k;
+  ba.v = v;
+  ba.log_alpha = log_alpha;
+  ba.beta = beta;
+  ba.d_o = d_o;
+  ba.d_final_state = d_final_state;
+  ba.cu = cu_seqlens;
+  ba.order = order;
+  ba.seq_first = seq_first;
+  ba.num_seqs = num_seqs;
+  ba.num_heads = num_heads;
+  ba.total_tokens = total_tokens;
+  ba.slots = (int)pl.slots;
+  ba.bf16 = bf16;
+  ba.factors = factors;
+  ba.dblocks = ws + pl.off_dblocks;
+  ba.chunk_states = chunk_states;
+  ba.chunk_u = chunk_u;
+  ba.chunk_ds = reinterpret_cast<float*>(ws + pl.off_ds);
+  ba.chunk_du = reinterpret_cast<float*>(ws + pl.off_du);
+  ba.dq = dq;
+  ba.dk = dk;
+  ba.dv = dv;
+  ba.dlog_alpha = dlog_alpha;
+  ba.dbeta = dbeta;
+  ba.d_initial_state = d_initial_state;
+  if (kda::launch_bwd_prep(ba, stream) != hipSuccess) return KDA_ERR_HIP;
+  if (kda::launch_bwd_carry(ba, stream) != hipSuccess) return KDA_ERR_HIP;
+  if (kda::launch_bwd_grad(ba, stream) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
 }
 
 kda_status kda_decode_step(float* state, const void* q, const void* k, const void* v, const float* log_alpha,

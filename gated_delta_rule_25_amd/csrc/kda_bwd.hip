@@ -1,0 +1,957 @@
+// kda_bwd.hip — backward pass of the chunked KDA prefill for gfx950.
+//
+// "Kimi K3 架构、训练与系统全景解析", section 7.1 (FlashKDA): the chunked
+// kernel serves training as well as prefill, so the recurrence needs its
+// gradients.  The pages print no backward formulas; what follows is the exact
+// derivative of the chunkwise form of section 4.2.4 (written out in
+// kda_chunk.hip) for the loss  sum_t <dO_t, o_t> + <dS_T, S_T>.  Per chunk,
+// with incoming state S, outgoing-state gradient dS' and U = U' - W S:
+//
+//   dU  = P^T dO + Kb dS'                      dS  = Diag(gamma) dS' + Qt^T dO - W^T dU
+//   dQt = dO S^T          dW = -dU S^T          dKb = U dS'^T       dgamma = rowsum(dS' (.) S)
+//   dP  = lower(dO U^T)   dT = dW Kt^T + dU V^T dKt = T^T dW        dV = T^T dU
+//   T = M Diag(beta), M = (I + A)^{-1}:  dM = dT Diag(beta), dbeta_j += sum_r M_rj dT_rj,
+//   dA = strictly-lower(-M^T dM M^T),  A = Diag(beta) B:  dB = Diag(beta) dA, dbeta_i += sum_j dA_ij B_ij
+//
+// and the Gram products B = Kt Kh^T, P = Qt Kh^T give the rest.  Every
+// product that involves K e^{-g} is formed per 16-token tile against the
+// tile's reference rho (the decay before the tile), exactly as the forward
+// does, so no factor exceeds e^{80} under the decay bound [-5, 0]:
+//   row tile a:    dK_t += e^{g_t - rho_a} (dB Kh_a)_t,  dQ_t += e^{g_t - rho_a} (dP Kh_a)_t
+//   column tile b: dK_s += e^{rho_b - g_s} (dB^T K_b + dP^T Q_b)_s
+// with Kh_a = K e^{rho_a - g} over tokens up to tile a and K_b, Q_b = (K, Q) e^{g - rho_b}
+// over tokens from tile b on.  The log-decay gradient collects
+//   dg_t = dQt (.) Qt + dKt (.) Kt - dKb (.) Kb + (tile terms) ,   dG = sum_t dKb (.) Kb + dgamma (.) gamma
+// and dlog_alpha_t = sum_{t' >= t} dg_t' + dG  (g_t is the inclusive cumulative
+// log-decay, G = g at the chunk's last token).
+//
+// Kernels, after the forward's prep kernel and its carry kernel in the states
+// pass (which store S and U of every chunk):
+//   bwd_prep_kernel   every (chunk, head): from the forward factor block and
+//                     dO, the reverse carry's block (Kb and -W^T as operand
+//                     fragments, P^T dO, Qt^T dO, gamma).
+//   bwd_carry_kernel  one workgroup per (sequence, head, 64 value columns):
+//                     walks the chunks backwards with dS in MFMA
+//                     accumulators, storing dS' and dU of every chunk; the
+//                     gradient reaching the first chunk is d_initial_state.
+//   bwd_grad_kernel   every (chunk, head): all per-token gradients.
+#include "kda_chunk_util.h"
+
+namespace kda {
+namespace {
+
+// The sequence that owns slot s: the largest n with seq_first[n] <= s (empty
+// sequences share their first slot with the next one and are skipped).
+__device__ __forceinline__ int slot_seq(const int32_t* seq_first, int N, int s) {
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seq_first[mid] <= s)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// Position of contraction index c (0..31 within a 32-deep step) in a lane's
+// 8 fragment elements: lane group g = (c % 16) / 4, element (c % 4) + 4 (c / 16).
+__device__ __forceinline__ int frag_elem(int c, int& grp) {
+  grp = (c & 15) >> 2;
+  return (c & 3) + ((c >> 4) << 2);
+}
+
+// Elements of a forward factor block held in LDS (layout in kda_internal.h).
+template <typename E, int C>
+struct FactorView {
+  using F = FactorBlock<(int)sizeof(E), C>;
+  static constexpr int KT = C / 32;
+  const unsigned char* b;
+  // -W[t][i] (W and Qt: row tile of 16 tokens, 32-deep steps over the keys)
+  __device__ float neg_w(int t, int i) const { return at(F::W, t, i); }
+  __device__ float qt(int t, int i) const { return at(F::Q, t, i); }
+  __device__ float at(uint32_t base, int t, int i) const {
+    int grp;
+    const int e = frag_elem(i & 31, grp);
+    const int idx = (((t >> 4) * 4 + (i >> 5)) * 64 + grp * 16 + (t & 15)) * 8 + e;
+    return to_f32(reinterpret_cast<const E*>(b + base)[idx]);
+  }
+  // P[t][s] (zero above the diagonal; fragments only for 32-token steps that reach t)
+  __device__ float p(int t, int s) const {
+    const int rt = t >> 4, kt = s >> 5;
+    if (kt > rt / 2) return 0.f;
+    int grp;
+    const int e = frag_elem(s & 31, grp);
+    const int idx = (F::p_frag(rt, kt) * 64 + grp * 16 + (t & 15)) * 8 + e;
+    return to_f32(reinterpret_cast<const E*>(b + F::P)[idx]);
+  }
+  // Kb[t][i], stored as Kb^T fragments split in halves
+  __device__ float kb(int t, int i) const {
+    const int c = t & 31;
+    const int idx = (((i >> 4) * KT + (t >> 5)) * 2 + (c >> 4)) * 256 + (((c & 15) >> 2) * 16 + (i & 15)) * 4 + (c & 3);
+    return to_f32(reinterpret_cast<const E*>(b + F::K)[idx]);
+  }
+  __device__ float gamma(int i) const { return reinterpret_cast<const float*>(b + F::G)[i]; }
+};
+
+template <typename E>
+__device__ __forceinline__ void store4(E* dst, f32x4 x) {
+  if constexpr (sizeof(E) == 2)
+    *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+  else
+    *reinterpret_cast<f32x4*>(dst) = x;
+}
+
+// ---------------------------------------------------------------------------
+// bwd_prep_kernel: one workgroup of four waves per (slot, head).
+// ---------------------------------------------------------------------------
+template <typename E, int C>
+struct PrepBwdLayout {
+  using F = FactorBlock<(int)sizeof(E), C>;
+  static constexpr int PD = D + 4;                       // dO row pitch (floats)
+  static constexpr size_t DO = F::BYTES;                 // f32 [C][PD]
+  static constexpr size_t BYTES = DO + (size_t)C * PD * 4;
+};
+
+template <typename E, int C>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
+  constexpr int ES = (int)sizeof(E);
+  using F = FactorBlock<ES, C>;
+  using DB = DCarryBlock<ES, C>;
+  using L = PrepBwdLayout<E, C>;
+  constexpr int NT = C / 16, KT = C / 32, PD = L::PD;
+  static_assert(L::BYTES <= 160 * 1024, "LDS budget exceeded");
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* sDO = reinterpret_cast<float*>(smem + L::DO);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  const int H = p.num_heads, h = blockIdx.x % H, slot = blockIdx.x / H;
+  if (slot >= p.seq_first[p.num_seqs]) return;
+  const int n = slot_seq(p.seq_first, p.num_seqs, slot);
+  int64_t bos, eos;
+  seq_range(p.cu, n, p.total_tokens, bos, eos);
+  const int64_t t0 = bos + (int64_t)(slot - p.seq_first[n]) * C;
+  const int nv = (int)max((int64_t)0, min((int64_t)C, eos - t0));
+  const size_t blk = (size_t)slot * H + h;
+
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(p.factors) + blk * F::BYTES);
+    for (int i = tid; i < (int)(F::BYTES / 16); i += 256) reinterpret_cast<u32x4*>(smem)[i] = src[i];
+    const E* gdo = static_cast<const E*>(p.d_o);
+    const int64_t rs = (int64_t)H * D;
+    for (int i = tid; i < C * D; i += 256) {
+      const int t = i / D, c = i % D;
+      sDO[t * PD + c] = t < nv ? to_f32(gdo[(t0 + t) * rs + (int64_t)h * D + c]) : 0.f;
+    }
+  }
+  __syncthreads();
+  const FactorView<E, C> fv{smem};
+  char* dst = static_cast<char*>(p.dblocks) + blk * DB::BYTES;
+
+  // X = P^T dO: tile (token tile sa, column tile jt); P[t][s] is zero for t < s
+  E* dX = reinterpret_cast<E*>(dst + DB::X);
+  for (int ti = wv; ti < NT * 8; ti += 4) {
+    const int sa = ti / 8, jt = ti % 8;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = sa; kb < NT; ++kb) {
+      Frag16<float> A, B;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * kb + 4 * g + e;
+        A.v[e] = fv.p(t, 16 * sa + l16);
+        B.v[e] = sDO[t * PD + 16 * jt + l16];
+      }
+      acc = mma16(acc, A, B);
+    }
+    store4(dX + ((size_t)ti * 64 + lane) * 4, acc);
+  }
+  // Y = Qt^T dO: tile (key tile it, column tile jt)
+  E* dY = reinterpret_cast<E*>(dst + DB::Y);
+  for (int ti = wv; ti < 64; ti += 4) {
+    const int it = ti / 8, jt = ti % 8;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < NT; ++kb) {
+      Frag16<float> A, B;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * kb + 4 * g + e;
+        A.v[e] = fv.qt(t, 16 * it + l16);
+        B.v[e] = sDO[t * PD + 16 * jt + l16];
+      }
+      acc = mma16(acc, A, B);
+    }
+    store4(dY + ((size_t)ti * 64 + lane) * 4, acc);
+  }
+  // Kb as A-operand fragments over the keys, -W^T as fragments over the tokens
+  E* dKB = reinterpret_cast<E*>(dst + DB::KB);
+  for (int i = tid; i < NT * 4 * 64; i += 256) {
+    const int f = i / 64, ln = i % 64, rt = f / 4, ks = f % 4, r = ln & 15, gg = ln >> 4;
+    E vals[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = 32 * ks + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4);
+      vals[e] = from_f32<E>(fv.kb(16 * rt + r, key));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dKB[((size_t)f * 64 + ln) * 8 + e] = vals[e];
+  }
+  E* dWT = reinterpret_cast<E*>(dst + DB::WT);
+  for (int i = tid; i < 8 * KT * 64; i += 256) {
+    const int f = i / 64, ln = i % 64, rt8 = f / KT, kt = f % KT, r = ln & 15, gg = ln >> 4;
+    E vals[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tok = 32 * kt + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4);
+      vals[e] = from_f32<E>(fv.neg_w(tok, 16 * rt8 + r));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dWT[((size_t)f * 64 + ln) * 8 + e] = vals[e];
+  }
+  if (tid < D) reinterpret_cast<float*>(dst + DB::G)[tid] = fv.gamma(tid);
+}
+
+// ---------------------------------------------------------------------------
+// bwd_carry_kernel: four compute waves of 16 value columns plus one loader
+// wave per (sequence, head, 64-column block), chunks in reverse order.  The
+// loader copies each chunk's Kb, -W^T and gamma into a three-slot LDS ring
+// two chunks ahead; one barrier per chunk hands the slots over (as in the
+// forward carry).
+// ---------------------------------------------------------------------------
+template <typename E, int C>
+struct CarryBwdLayout {
+  using DB = DCarryBlock<(int)sizeof(E), C>;
+  static constexpr uint32_t SLOT = DB::LDS_PART;
+  static constexpr int PIECES = (int)(SLOT / 1024);
+  static constexpr int NBUF = 3;
+  static constexpr size_t BYTES = (size_t)NBUF * SLOT;
+  static_assert(SLOT % 1024 == 0, "1 KiB pieces");
+};
+
+template <typename E, int C>
+__global__ __launch_bounds__(320) void bwd_carry_kernel(const BwdArgs p) {
+  constexpr int NWC = 4;
+  constexpr int ES = (int)sizeof(E);
+  using DB = DCarryBlock<ES, C>;
+  using L = CarryBwdLayout<E, C>;
+  constexpr int NT = C / 16, KT = C / 32;
+  static_assert(L::BYTES <= 160 * 1024, "LDS budget exceeded");
+  static_assert(L::PIECES <= 63, "copy exceeds the outstanding-load counter");
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // XCD-aware decode: blocks b and b + 8 (the two column blocks of one
+  // (sequence, head)) run on the same XCD
+  const int xcd = blockIdx.x & 7, sl = blockIdx.x >> 3;
+  const int cb = sl % 2;
+  const int u = (sl / 2) * 8 + xcd;
+  const int H = p.num_heads;
+  if (u >= p.num_seqs * H) return;
+  const int rnk = u / H, h = u % H;
+  const int n = p.order ? p.order[rnk] : rnk;
+  const int slot0 = p.seq_first[n];
+  const int nch = max(0, p.seq_first[n + 1] - slot0);
+  const char* dbase = static_cast<const char*>(p.dblocks);
+  auto block_of = [&](int ci) { return dbase + ((size_t)(slot0 + ci) * H + h) * DB::BYTES; };
+
+  if (wv == NWC) {
+    auto copy_block = [&](int k) {
+      const char* blk = block_of(nch - 1 - k);
+      unsigned char* dstl = smem + (k % L::NBUF) * L::SLOT;
+#pragma unroll
+      for (int j = 0; j < L::PIECES; ++j)
+        __builtin_amdgcn_global_load_lds(blk + j * 1024u + lane * 16,
+                                         (__attribute__((address_space(3))) void*)(dstl + j * 1024), 16, 0, 0);
+    };
+    if (nch > 0) copy_block(0);
+    if (nch > 1) copy_block(1);
+    for (int k = 0; k < nch; ++k) {
+      if (k + 1 < nch)
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(L::PIECES));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+      __syncthreads();
+      if (k + 2 < nch) copy_block(k + 2);
+    }
+    return;
+  }
+
+  const int l16 = lane & 15, g = lane >> 4;
+  const int col0 = cb * 64 + 16 * wv, ct = col0 / 16;
+  const size_t sbase = ((size_t)n * H + h) * (size_t)(D * D);
+  // dS at the end of the sequence: d_final_state, or zero
+  f32x4 accD[8];
+#pragma unroll
+  for (int rt8 = 0; rt8 < 8; ++rt8)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      accD[rt8][i] = p.d_final_state ? p.d_final_state[sbase + (size_t)(16 * rt8 + 4 * g + i) * D + col0 + l16] : 0.f;
+
+  using Raw = std::conditional_t<ES == 2, u32x2, f32x4>;
+  auto raw_f32 = [](Raw x) -> f32x4 {
+    if constexpr (ES == 2) {
+      const bf16x4 b = __builtin_bit_cast(bf16x4, x);
+      return (f32x4){(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+    } else {
+      return x;
+    }
+  };
+  auto buf_ld_raw = [](Rsrc rb, uint32_t voff, uint32_t soff) -> Raw {
+    if constexpr (ES == 2)
+      return __builtin_amdgcn_raw_buffer_load_b64(rb, (int)voff, (int)soff, 0);
+    else
+      return __builtin_bit_cast(f32x4, buf_ld16(rb, voff, soff));
+  };
+  constexpr int FRE = 512;  // elements per fragment
+
+  for (int k = 0; k < nch; ++k) {
+    const int ci = nch - 1 - k;
+    const size_t blkid = (size_t)(slot0 + ci) * H + h;
+    const Rsrc rb = make_rsrc(block_of(ci), DB::BYTES);
+    Raw rX[NT], rY[8];
+#pragma unroll
+    for (int a = 0; a < NT; ++a) rX[a] = buf_ld_raw(rb, (uint32_t)(lane * 4 * ES), DB::X + (a * 8 + ct) * DB::TILE);
+#pragma unroll
+    for (int rt8 = 0; rt8 < 8; ++rt8)
+      rY[rt8] = buf_ld_raw(rb, (uint32_t)(lane * 4 * ES), DB::Y + (rt8 * 8 + ct) * DB::TILE);
+    // the gradient reaching this chunk's end
+    float* ds_dst = p.chunk_ds + blkid * (size_t)(D * D);
+#pragma unroll
+    for (int rt8 = 0; rt8 < 8; ++rt8)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ds_dst[(size_t)(16 * rt8 + 4 * g + i) * D + col0 + l16] = accD[rt8][i];
+    __syncthreads();  // slot k % 3 holds chunk ci
+    const unsigned char* buf = smem + (k % L::NBUF) * L::SLOT;
+    const E* sKB = reinterpret_cast<const E*>(buf + DB::KB + lane * 8 * ES);
+    const E* sWT = reinterpret_cast<const E*>(buf + DB::WT + lane * 8 * ES);
+    const float* sG = reinterpret_cast<const float*>(buf + DB::G);
+
+    // dU = P^T dO + Kb dS'
+    Frag<E> sf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) frag_from_acc(sf[ks], accD[2 * ks], accD[2 * ks + 1]);
+    f32x4 accU[NT];
+#pragma unroll
+    for (int a = 0; a < NT; ++a) accU[a] = raw_f32(rX[a]);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int a = 0; a < NT; ++a) {
+        Frag<E> fa;
+        ld_frag(fa, sKB + (a * 4 + ks) * FRE);
+        accU[a] = mma(accU[a], fa, sf[ks]);
+      }
+    float* du_dst = p.chunk_du + blkid * (size_t)(C * D);
+#pragma unroll
+    for (int a = 0; a < NT; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) du_dst[(size_t)(16 * a + 4 * g + i) * D + col0 + l16] = accU[a][i];
+    // dS = Diag(gamma) dS' + Qt^T dO - W^T dU
+    Frag<E> uf[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) frag_from_acc(uf[kt], accU[2 * kt], accU[2 * kt + 1]);
+#pragma unroll
+    for (int rt8 = 0; rt8 < 8; ++rt8) {
+      const f32x4 gam = *reinterpret_cast<const f32x4*>(sG + 16 * rt8 + 4 * g);
+      accD[rt8] = accD[rt8] * gam + raw_f32(rY[rt8]);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        Frag<E> fw;
+        ld_frag(fw, sWT + (rt8 * KT + kt) * FRE);
+        accD[rt8] = mma(accD[rt8], fw, uf[kt]);
+      }
+    }
+  }
+  if (p.d_initial_state) {
+#pragma unroll
+    for (int rt8 = 0; rt8 < 8; ++rt8)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p.d_initial_state[sbase + (size_t)(16 * rt8 + 4 * g + i) * D + col0 + l16] = accD[rt8][i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_grad_kernel: one workgroup of four waves per (slot, head).  Wave w owns
+// key tiles 2w and 2w + 1 (32 key channels) of every per-token gradient;
+// C x C quantities live in LDS.  All products run in fp32 on the matrix cores
+// (four v_mfma_f32_16x16x4_f32 per 16-deep step).
+// ---------------------------------------------------------------------------
+template <typename E, int C>
+struct GradLayout {
+  static constexpr int PK = D + 4;   // pitch of [C][128] arrays (elements)
+  static constexpr int PC = C + 4;   // pitch of [C][C] arrays
+  static constexpr int JB = 32;      // value columns per staging block
+  static constexpr int PJ = JB + 4;
+  static constexpr size_t K = 0;                                     // E   [C][PK] k
+  static constexpr size_t Q = K + (size_t)C * PK * sizeof(E);        // E   [C][PK] q
+  static constexpr size_t G = Q + (size_t)C * PK * sizeof(E);        // f32 [C][PK] g
+  static constexpr size_t M = G + (size_t)C * PK * 4;                // f32 [C][PC] (I + A)^{-1}
+  static constexpr size_t DP = M + (size_t)C * PC * 4;               // f32 [C][PC] dP
+  static constexpr size_t UN = DP + (size_t)C * PC * 4;              // union area
+  static constexpr size_t UN_STAGE = 4 * (size_t)C * PJ * 4;         //   dO, U, dU, V column blocks
+  static constexpr size_t UN_DW = (size_t)C * PK * 4;                //   dW [C][PK]
+  static constexpr size_t UN_CC = 2 * (size_t)C * PC * 4;            //   A, or dM / dB and X = dM M^T
+  static constexpr size_t UN_BYTES = UN_STAGE > UN_DW ? (UN_STAGE > UN_CC ? UN_STAGE : UN_CC)
+                                                     : (UN_DW > UN_CC ? UN_DW : UN_CC);
+  static constexpr size_t BETA = UN + UN_BYTES;                      // f32 [C]
+  static constexpr size_t DBETA = BETA + (size_t)C * 4;              // f32 [C]
+  static constexpr size_t DG = DBETA + (size_t)C * 4;                // f32 [128] dG per key
+  static constexpr size_t BYTES = DG + (size_t)D * 4;
+};
+
+template <typename E, int C>
+__global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
+  using L = GradLayout<E, C>;
+  constexpr int NT = C / 16, PK = L::PK, PC = L::PC, JB = L::JB, PJ = L::PJ;
+  static_assert(L::BYTES <= 160 * 1024, "LDS budget exceeded");
+  extern __shared__ __align__(16) unsigned char smem[];
+  E* sK = reinterpret_cast<E*>(smem + L::K);
+  E* sQ = reinterpret_cast<E*>(smem + L::Q);
+  float* sG = reinterpret_cast<float*>(smem + L::G);
+  float* sM = reinterpret_cast<float*>(smem + L::M);
+  float* sDP = reinterpret_cast<float*>(smem + L::DP);
+  float* sUN = reinterpret_cast<float*>(smem + L::UN);
+  float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
+  float* sDbeta = reinterpret_cast<float*>(smem + L::DBETA);
+  float* sDG = reinterpret_cast<float*>(smem + L::DG);
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  const int H = p.num_heads, h = blockIdx.x % H, slot = blockIdx.x / H;
+  if (slot >= p.seq_first[p.num_seqs]) return;
+  const int n = slot_seq(p.seq_first, p.num_seqs, slot);
+  int64_t bos, eos;
+  seq_range(p.cu, n, p.total_tokens, bos, eos);
+  const int64_t t0 = bos + (int64_t)(slot - p.seq_first[n]) * C;
+  const int nv = (int)max((int64_t)0, min((int64_t)C, eos - t0));
+  const size_t blk = (size_t)slot * H + h;
+  const int64_t rs = (int64_t)H * D;
+  const int64_t hoff = (int64_t)h * D;
+
+  // ---- inputs: k, q rows, the cumulative log-decay g (zeros past the end) ----
+  {
+    const E* gk = static_cast<const E*>(p.k);
+    const E* gq = static_cast<const E*>(p.q);
+    for (int i = tid; i < C * D; i += 256) {
+      const int t = i / D, c = i % D;
+      const bool ok = t < nv;
+      sK[t * PK + c] = ok ? gk[(t0 + t) * rs + hoff + c] : from_f32<E>(0.f);
+      sQ[t * PK + c] = ok ? gq[(t0 + t) * rs + hoff + c] : from_f32<E>(0.f);
+    }
+    if (tid < D) {
+      float run = 0.f;
+      for (int t = 0; t < C; ++t) {
+        if (t < nv) run += p.log_alpha[(t0 + t) * rs + hoff + tid];
+        sG[t * PK + tid] = run;
+      }
+    }
+    if (tid < C) {
+      sBeta[tid] = tid < nv ? p.beta[(t0 + tid) * H + h] : 0.f;
+      sDbeta[tid] = 0.f;
+    }
+    for (int i = tid; i < C * PC; i += 256) {
+      sM[i] = 0.f;
+      sDP[i] = 0.f;
+      sUN[i] = 0.f;  // A (strictly lower part written below)
+    }
+  }
+  __syncthreads();
+  auto kf = [&](int t, int i) { return to_f32(sK[t * PK + i]); };
+  auto qf = [&](int t, int i) { return to_f32(sQ[t * PK + i]); };
+  auto gf = [&](int t, int i) { return sG[t * PK + i]; };
+  // decay before token tile a (its reference), per key channel
+  auto rho = [&](int a, int i) { return a == 0 ? 0.f : sG[(16 * a - 1) * PK + i]; };
+  auto Gc = [&](int i) { return sG[(C - 1) * PK + i]; };
+
+  // Gram tile B[t][s] = sum_i K_t e^{g_t - rho_a} K_s e^{rho_a - g_s} (a = t's tile)
+  auto gram_tile = [&](int a, int b) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < 8; ++kb) {
+      Frag16<float> A, B;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * kb + 4 * g + e;
+        const float r = rho(a, i);
+        const int t = 16 * a + l16, s = 16 * b + l16;
+        A.v[e] = kf(t, i) * __expf(gf(t, i) - r);
+        B.v[e] = kf(s, i) * __expf(r - gf(s, i));
+      }
+      acc = mma16(acc, A, B);
+    }
+    return acc;  // rows t = 16a + 4g + e, column s = 16b + l16
+  };
+  // lower tiles (a, b), b <= a, enumerated row by row
+  constexpr int NLT = NT * (NT + 1) / 2;
+  auto lower_tile = [](int idx, int& a, int& b) {
+    a = 0;
+    while ((a + 1) * (a + 2) / 2 <= idx) ++a;
+    b = idx - a * (a + 1) / 2;
+  };
+
+  // ---- A = strictly-lower(Diag(beta) B) into the union area ----
+  float* sA = sUN;
+  for (int idx = wv; idx < NLT; idx += 4) {
+    int a, b;
+    lower_tile(idx, a, b);
+    const f32x4 acc = gram_tile(a, b);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * a + 4 * g + e, s = 16 * b + l16;
+      if (s < t) sA[t * PC + s] = sBeta[t] * acc[e];
+    }
+  }
+  __syncthreads();
+  // ---- M = (I + A)^{-1}: diagonal 16 x 16 blocks by forward substitution ----
+  if (wv < NT && g == 0) {
+    const int a = wv, j = l16;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = (r == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int c = 0; c < r; ++c) v -= sA[(16 * a + r) * PC + 16 * a + c] * x[c];
+      x[r] = v;
+      sM[(16 * a + r) * PC + 16 * a + j] = v;
+    }
+  }
+  __syncthreads();
+  // ... then the blocks below the diagonal, one block row at a time:
+  // M_ab = -M_aa sum_{c=b}^{a-1} A_ac M_cb
+  for (int a = 1; a < NT; ++a) {
+    if (wv < a) {
+      const int b = wv;
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      for (int c = b; c < a; ++c) {
+        Frag16<float> A, B;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          A.v[e] = sA[(16 * a + l16) * PC + 16 * c + 4 * g + e];
+          B.v[e] = sM[(16 * c + 4 * g + e) * PC + 16 * b + l16];
+        }
+        z = mma16(z, A, B);
+      }
+      Frag16<float> A, B;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) A.v[e] = sM[(16 * a + l16) * PC + 16 * a + 4 * g + e];
+      B.v = z;
+      const f32x4 m = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, A, B);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sM[(16 * a + 4 * g + e) * PC + 16 * b + l16] = -m[e];
+    }
+    __syncthreads();
+  }
+
+  // ---- products with S and dS' over the value columns, 32 at a time ----
+  const float* gS = p.chunk_states + blk * (size_t)(D * D);
+  const float* gDS = p.chunk_ds + blk * (size_t)(D * D);
+  const float* gU = p.chunk_u + blk * (size_t)(C * D);
+  const float* gDU = p.chunk_du + blk * (size_t)(C * D);
+  float* sDO = sUN;
+  float* sU = sUN + C * PJ;
+  float* sDU = sUN + 2 * C * PJ;
+  float* sV = sUN + 3 * C * PJ;
+  f32x4 rQs[NT][2], rW[NT][2], rKb[NT][2];
+  float gpart[2] = {0.f, 0.f};
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) rQs[rt][c] = rW[rt][c] = rKb[rt][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  constexpr int MAXLT = (NLT + 3) / 4;  // lower tiles per wave
+  f32x4 rdP[MAXLT], rdT[MAXLT];
+#pragma unroll
+  for (int x = 0; x < MAXLT; ++x) rdP[x] = rdT[x] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const E* gdo = static_cast<const E*>(p.d_o);
+  const E* gv = static_cast<const E*>(p.v);
+  E* gdv = static_cast<E*>(p.dv);
+  __syncthreads();  // A (in the union area) is no longer read
+  for (int j0 = 0; j0 < D; j0 += JB) {
+    for (int i = tid; i < C * JB; i += 256) {
+      const int t = i / JB, c = i % JB;
+      const bool ok = t < nv;
+      sDO[t * PJ + c] = ok ? to_f32(gdo[(t0 + t) * rs + hoff + j0 + c]) : 0.f;
+      sV[t * PJ + c] = ok ? to_f32(gv[(t0 + t) * rs + hoff + j0 + c]) : 0.f;
+      sU[t * PJ + c] = ok ? gU[(size_t)t * D + j0 + c] : 0.f;
+      sDU[t * PJ + c] = ok ? gDU[(size_t)t * D + j0 + c] : 0.f;
+    }
+    __syncthreads();
+    // dQt += dO S^T, (dU S^T), dKb += U dS'^T, dgamma partials: own key tiles
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int i = 16 * (2 * wv + c) + l16;
+#pragma unroll
+      for (int js = 0; js < JB / 16; ++js) {
+        Frag16<float> BS, BD;
+        BS.v = *reinterpret_cast<const f32x4*>(gS + (size_t)i * D + j0 + 16 * js + 4 * g);
+        BD.v = *reinterpret_cast<const f32x4*>(gDS + (size_t)i * D + j0 + 16 * js + 4 * g);
+        gpart[c] += BS.v[0] * BD.v[0] + BS.v[1] * BD.v[1] + BS.v[2] * BD.v[2] + BS.v[3] * BD.v[3];
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+          const int off = (16 * rt + l16) * PJ + 16 * js + 4 * g;
+          Frag16<float> A;
+          A.v = *reinterpret_cast<const f32x4*>(sDO + off);
+          rQs[rt][c] = mma16(rQs[rt][c], A, BS);
+          A.v = *reinterpret_cast<const f32x4*>(sDU + off);
+          rW[rt][c] = mma16(rW[rt][c], A, BS);
+          A.v = *reinterpret_cast<const f32x4*>(sU + off);
+          rKb[rt][c] = mma16(rKb[rt][c], A, BD);
+        }
+      }
+    }
+    // dP += dO U^T and dT += dU V^T on this wave's lower tiles
+#pragma unroll
+    for (int x = 0; x < MAXLT; ++x) {
+      const int idx = wv + 4 * x;
+      if (idx < NLT) {
+        int a, b;
+        lower_tile(idx, a, b);
+#pragma unroll
+        for (int js = 0; js < JB / 16; ++js) {
+          const int offa = (16 * a + l16) * PJ + 16 * js + 4 * g;
+          const int offb = (16 * b + l16) * PJ + 16 * js + 4 * g;
+          Frag16<float> A, B;
+          A.v = *reinterpret_cast<const f32x4*>(sDO + offa);
+          B.v = *reinterpret_cast<const f32x4*>(sU + offb);
+          rdP[x] = mma16(rdP[x], A, B);
+          A.v = *reinterpret_cast<const f32x4*>(sDU + offa);
+          B.v = *reinterpret_cast<const f32x4*>(sV + offb);
+          rdT[x] = mma16(rdT[x], A, B);
+        }
+      }
+    }
+    // dV = T^T dU for these columns: tile (token tile st, column tile jt);
+    // T[t][s] = M[t][s] beta_s is zero for t < s
+    for (int ti = wv; ti < NT * (JB / 16); ti += 4) {
+      const int st = ti / (JB / 16), jt = ti % (JB / 16);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = st; kb < NT; ++kb) {
+        Frag16<float> A, B;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * kb + 4 * g + e;
+          A.v[e] = sM[t * PC + 16 * st + l16];
+          B.v[e] = sDU[t * PJ + 16 * jt + l16];
+        }
+        acc = mma16(acc, A, B);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = 16 * st + 4 * g + e;
+        if (s < nv) gdv[(t0 + s) * rs + hoff + j0 + 16 * jt + l16] = from_f32<E>(sBeta[s] * acc[e]);
+      }
+    }
+    __syncthreads();
+  }
+  // dgamma for this wave's keys (lane l16 of each key tile)
+  float dgam[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    float v = gpart[c];
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    dgam[c] = v;
+  }
+
+  // ---- dW = -dU S^T to LDS, dP (lower) to LDS ----
+  float* sDW = sUN;
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sDW[(16 * rt + 4 * g + e) * PK + 16 * (2 * wv + c) + l16] = -rW[rt][c][e];
+#pragma unroll
+  for (int x = 0; x < MAXLT; ++x) {
+    const int idx = wv + 4 * x;
+    if (idx < NLT) {
+      int a, b;
+      lower_tile(idx, a, b);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * a + 4 * g + e, s = 16 * b + l16;
+        sDP[t * PC + s] = s <= t ? rdP[x][e] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  // dT += dW Kt^T (Kt = K e^{g}); dbeta_j += sum_r M_rj dT_rj
+#pragma unroll
+  for (int x = 0; x < MAXLT; ++x) {
+    const int idx = wv + 4 * x;
+    if (idx < NLT) {
+      int a, b;
+      lower_tile(idx, a, b);
+      for (int kb = 0; kb < 8; ++kb) {
+        Frag16<float> A, B;
+        A.v = *reinterpret_cast<const f32x4*>(sDW + (16 * a + l16) * PK + 16 * kb + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s = 16 * b + l16, i = 16 * kb + 4 * g + e;
+          B.v[e] = kf(s, i) * __expf(gf(s, i));
+        }
+        rdT[x] = mma16(rdT[x], A, B);
+      }
+      float col = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) col += sM[(16 * a + 4 * g + e) * PC + 16 * b + l16] * rdT[x][e];
+      col += __shfl_xor(col, 16);
+      col += __shfl_xor(col, 32);
+      if (g == 0) atomicAdd(&sDbeta[16 * b + l16], col);
+    }
+  }
+  // dKt = T^T dW on this wave's keys: rows s, dW from registers (rows t)
+  f32x4 rKt[NT][2];
+#pragma unroll
+  for (int st = 0; st < NT; ++st)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NT; ++kb) {
+        if (kb < st) continue;
+        Frag16<float> A, B;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) A.v[e] = sM[(16 * kb + 4 * g + e) * PC + 16 * st + l16];
+        B.v = -rW[kb][c];
+        acc = mma16(acc, A, B);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] *= sBeta[16 * st + 4 * g + e];
+      rKt[st][c] = acc;
+    }
+  __syncthreads();  // dW is no longer read
+  // ---- dA = strictly-lower(-M^T dM M^T), dM = dT Diag(beta) ----
+  float* sDM = sUN;            // dM, later dB
+  float* sX = sUN + C * PC;    // X = dM M^T
+  for (int i = tid; i < C * PC; i += 256) sDM[i] = 0.f;
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < MAXLT; ++x) {
+    const int idx = wv + 4 * x;
+    if (idx < NLT) {
+      int a, b;
+      lower_tile(idx, a, b);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * a + 4 * g + e, s = 16 * b + l16;
+        sDM[t * PC + s] = s < t ? rdT[x][e] * sBeta[s] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  // X[m][c] = sum_j dM[m][j] M[c][j], j <= c (lower tiles suffice)
+  for (int idx = wv; idx < NLT; idx += 4) {
+    int a, b;
+    lower_tile(idx, a, b);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int jb = 0; jb <= b; ++jb) {
+      Frag16<float> A, B;
+      A.v = *reinterpret_cast<const f32x4*>(sDM + (16 * a + l16) * PC + 16 * jb + 4 * g);
+      B.v = *reinterpret_cast<const f32x4*>(sM + (16 * b + l16) * PC + 16 * jb + 4 * g);
+      acc = mma16(acc, A, B);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sX[(16 * a + 4 * g + e) * PC + 16 * b + l16] = acc[e];
+  }
+  __syncthreads();
+  // dA[r][c] = -sum_{m >= r} M[m][r] X[m][c]; dB = Diag(beta) dA into sDM;
+  // dbeta_r += sum_c dA[r][c] B[r][c]
+  f32x4 rdB[MAXLT];
+#pragma unroll
+  for (int x = 0; x < MAXLT; ++x) {
+    const int idx = wv + 4 * x;
+    rdB[x] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if (idx < NLT) {
+      int a, b;
+      lower_tile(idx, a, b);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int mb = a; mb < NT; ++mb) {
+        Frag16<float> A, B;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = 16 * mb + 4 * g + e;
+          A.v[e] = sM[m * PC + 16 * a + l16];
+          B.v[e] = sX[m * PC + 16 * b + l16];
+        }
+        acc = mma16(acc, A, B);
+      }
+      const f32x4 bt = gram_tile(a, b);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * a + 4 * g + e, c = 16 * b + l16;
+        const float da = c < r ? -acc[e] : 0.f;
+        rdB[x][e] = sBeta[r] * da;
+        float v = da * bt[e];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 8);
+        if (l16 == 0) atomicAdd(&sDbeta[r], v);
+      }
+    }
+  }
+  __syncthreads();  // every wave is past reading dM and X
+#pragma unroll
+  for (int x = 0; x < MAXLT; ++x) {
+    const int idx = wv + 4 * x;
+    if (idx < NLT) {
+      int a, b;
+      lower_tile(idx, a, b);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sDM[(16 * a + 4 * g + e) * PC + 16 * b + l16] = rdB[x][e];
+    }
+  }
+  __syncthreads();
+  const float* sDB = sDM;
+
+  // ---- tile products of dB and dP with the referenced K and Q, own keys ----
+  // row side: YB = dB Kh_a, YP = dP Kh_a over tokens s <= tile a
+  f32x4 rYB[NT][2], rYP[NT][2], rZ[NT][2];
+#pragma unroll
+  for (int a = 0; a < NT; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int i = 16 * (2 * wv + c) + l16;
+      f32x4 yb = {0.f, 0.f, 0.f, 0.f}, yp = {0.f, 0.f, 0.f, 0.f};
+      const float r = rho(a, i);
+#pragma unroll
+      for (int sb = 0; sb < NT; ++sb) {
+        if (sb > a) continue;
+        Frag16<float> AB, AP, B;
+        AB.v = *reinterpret_cast<const f32x4*>(sDB + (16 * a + l16) * PC + 16 * sb + 4 * g);
+        AP.v = *reinterpret_cast<const f32x4*>(sDP + (16 * a + l16) * PC + 16 * sb + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s = 16 * sb + 4 * g + e;
+          B.v[e] = kf(s, i) * __expf(r - gf(s, i));
+        }
+        yb = mma16(yb, AB, B);
+        yp = mma16(yp, AP, B);
+      }
+      rYB[a][c] = yb;
+      rYP[a][c] = yp;
+    }
+  // column side: Z = dB^T K_b + dP^T Q_b over tokens t >= tile b
+#pragma unroll
+  for (int b = 0; b < NT; ++b)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int i = 16 * (2 * wv + c) + l16;
+      const float r = rho(b, i);
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int tb = 0; tb < NT; ++tb) {
+        if (tb < b) continue;
+        Frag16<float> AB, AP, BK, BQ;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * tb + 4 * g + e;
+          AB.v[e] = sDB[t * PC + 16 * b + l16];
+          AP.v[e] = sDP[t * PC + 16 * b + l16];
+          const float f = __expf(gf(t, i) - r);
+          BK.v[e] = kf(t, i) * f;
+          BQ.v[e] = qf(t, i) * f;
+        }
+        z = mma16(z, AB, BK);
+        z = mma16(z, AP, BQ);
+      }
+      rZ[b][c] = z;
+    }
+
+  // ---- per-token gradients of this wave's keys ----
+  f32x4 odq[NT][2], odk[NT][2], odg[NT][2];
+  float dGp[2] = {0.f, 0.f};
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int i = 16 * (2 * wv + c) + l16;
+      const float Gi = Gc(i), r = rho(rt, i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * rt + 4 * g + e;
+        const float gi = gf(t, i), kv = kf(t, i), qv = qf(t, i);
+        const float eg = __expf(gi), eb = __expf(Gi - gi), ra = __expf(gi - r), rb = __expf(r - gi);
+        const float dQs = rQs[rt][c][e], dKt = rKt[rt][c][e], dKb = rKb[rt][c][e];
+        const float yb = rYB[rt][c][e], yp = rYP[rt][c][e], z = rZ[rt][c][e];
+        odq[rt][c][e] = dQs * eg + yp * ra;
+        odk[rt][c][e] = dKt * eg + dKb * eb + yb * ra + z * rb;
+        odg[rt][c][e] = dQs * (qv * eg) + dKt * (kv * eg) - dKb * (kv * eb) + (kv * ra) * yb + (qv * ra) * yp -
+                        (kv * rb) * z;
+        dGp[c] += dKb * (kv * eb);
+      }
+    }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    float v = dGp[c];
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    const int i = 16 * (2 * wv + c) + l16;
+    if (g == 0) sDG[i] = v + dgam[c] * __expf(Gc(i));
+  }
+  __syncthreads();  // k, q and g are no longer read: their LDS takes the outputs
+  E* oQ = sK;
+  E* oK = sQ;
+  float* oG = sG;
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * rt + 4 * g + e, i = 16 * (2 * wv + c) + l16;
+        oQ[t * PK + i] = from_f32<E>(odq[rt][c][e]);
+        oK[t * PK + i] = from_f32<E>(odk[rt][c][e]);
+        oG[t * PK + i] = odg[rt][c][e];
+      }
+  __syncthreads();
+  // dlog_alpha_t = sum_{t' >= t} dg_t' + dG
+  if (tid < D) {
+    float run = sDG[tid];
+    for (int t = C - 1; t >= 0; --t) {
+      run += oG[t * PK + tid];
+      oG[t * PK + tid] = run;
+    }
+  }
+  __syncthreads();
+  E* gdq = static_cast<E*>(p.dq);
+  E* gdk = static_cast<E*>(p.dk);
+  for (int i = tid; i < nv * D; i += 256) {
+    const int t = i / D, c = i % D;
+    gdq[(t0 + t) * rs + hoff + c] = oQ[t * PK + c];
+    gdk[(t0 + t) * rs + hoff + c] = oK[t * PK + c];
+    p.dlog_alpha[(t0 + t) * rs + hoff + c] = oG[t * PK + c];
+  }
+  if (tid < nv) p.dbeta[(t0 + tid) * H + h] = sDbeta[tid];
+}
+
+template <typename Kern>
+hipError_t launch_lds(Kern fn, unsigned grid, unsigned block, size_t lds, const BwdArgs& a, hipStream_t stream) {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(block), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream) {
+  const unsigned grid = (unsigned)((size_t)a.slots * a.num_heads);
+  if (a.bf16)
+    return launch_lds(bwd_prep_kernel<__bf16, 64>, grid, 256, PrepBwdLayout<__bf16, 64>::BYTES, a, stream);
+  return launch_lds(bwd_prep_kernel<float, 32>, grid, 256, PrepBwdLayout<float, 32>::BYTES, a, stream);
+}
+
+hipError_t launch_bwd_carry(const BwdArgs& a, hipStream_t stream) {
+  const int units = a.num_seqs * a.num_heads;
+  const unsigned grid = (unsigned)(8 * 2 * ((units + 7) / 8));
+  if (a.bf16)
+    return launch_lds(bwd_carry_kernel<__bf16, 64>, grid, 320, CarryBwdLayout<__bf16, 64>::BYTES, a, stream);
+  return launch_lds(bwd_carry_kernel<float, 32>, grid, 320, CarryBwdLayout<float, 32>::BYTES, a, stream);
+}
+
+hipError_t launch_bwd_grad(const BwdArgs& a, hipStream_t stream) {
+  const unsigned grid = (unsigned)((size_t)a.slots * a.num_heads);
+  if (a.bf16) return launch_lds(bwd_grad_kernel<__bf16, 64>, grid, 256, GradLayout<__bf16, 64>::BYTES, a, stream);
+  return launch_lds(bwd_grad_kernel<float, 32>, grid, 256, GradLayout<float, 32>::BYTES, a, stream);
+}
+
+}  // namespace kda

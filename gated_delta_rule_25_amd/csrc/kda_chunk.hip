@@ -229,8 +229,9 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
   const int H = p.num_heads;
   const int rnk = u / H, h = u % H;
   // work item: sequence n, chunks [c0, c0 + nch) of it, factor slots from slot0
+  constexpr bool SEQ = PASS == 0 || PASS == 3;  // one work item per (sequence, head)
   int n, c0, nch, slot0;
-  if constexpr (PASS == 0) {
+  if constexpr (SEQ) {
     n = p.order ? p.order[rnk] : rnk;
     c0 = p.seq_c0[n];
     nch = p.seq_c1[n] - c0;
@@ -246,11 +247,11 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
   // pass 1: the second half of the blocks traces M (identity start, U' = 0)
   const bool mpart = PASS == 1 && cb_all >= p.col_split / 2;
   const int cb = PASS == 1 ? cb_all % (p.col_split / 2) : cb_all;
-  constexpr bool write_o = PASS != 1;
+  constexpr bool write_o = PASS == 0 || PASS == 2;
   const size_t pair_base = ((size_t)rnk * H + h) * 2 * (size_t)(D * D);
-  const float* s_in = PASS == 0 ? (p.state_in ? p.state_in + ((size_t)n * H + h) * (size_t)(D * D) : nullptr)
+  const float* s_in = SEQ ? (p.state_in ? p.state_in + ((size_t)n * H + h) * (size_t)(D * D) : nullptr)
                     : PASS == 2 ? p.pairs + pair_base : nullptr;
-  float* s_out = PASS == 0 ? (p.state_out ? p.state_out + ((size_t)n * H + h) * (size_t)(D * D) : nullptr)
+  float* s_out = SEQ ? (p.state_out ? p.state_out + ((size_t)n * H + h) * (size_t)(D * D) : nullptr)
                : PASS == 1 ? p.pairs + pair_base + (mpart ? (size_t)(D * D) : 0) : nullptr;
   int64_t seq_bos, seq_eos;
   seq_range(p.cu, n, p.total_tokens, seq_bos, seq_eos);
@@ -260,15 +261,15 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
   auto block_of = [&](int ci) { return fbase + ((size_t)(slot0 + ci) * H + h) * F::BYTES; };
 
   if (wv == NWC) {
-    // ---- loader wave (the pairs pass forms no outputs and skips Qt) ----
+    // ---- loader wave (the passes that form no outputs skip Qt) ----
     constexpr uint32_t kSlotQ = L::Q, kSlotK = L::K, kBlockK = F::K;
-    constexpr int NPC = PASS == 1 ? L::PIECES - (int)((kSlotK - kSlotQ) / 1024) : L::PIECES;  // pieces per chunk
+    constexpr int NPC = !write_o ? L::PIECES - (int)((kSlotK - kSlotQ) / 1024) : L::PIECES;  // pieces per chunk
     auto copy_block = [&](int ci) {
       const char* blk = block_of(ci);
       unsigned char* dst = smem + (ci % L::NBUF) * L::SLOT;
 #pragma unroll
       for (int j = 0; j < L::PIECES; ++j) {
-        if (PASS == 1 && j * 1024u >= kSlotQ && j * 1024u < kSlotK) continue;
+        if (!write_o && j * 1024u >= kSlotQ && j * 1024u < kSlotK) continue;
         __builtin_amdgcn_global_load_lds(blk + (j * 1024u < kSlotK ? j * 1024u : kBlockK + (j * 1024u - kSlotK)) + lane * 16,
                                          (__attribute__((address_space(3))) void*)(dst + j * 1024), 16, 0, 0);
       }
@@ -403,6 +404,20 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
     for (int c = 0; c < CT; ++c)
 #pragma unroll
       for (int a = 0; a < NT; ++a) accU[c][a] = raw_f32(rU[c][a]);
+    // states pass: the state entering this chunk, row-major fp32 (rows are
+    // key channels), for the backward pass
+    float* cs_dst = nullptr;
+    if constexpr (PASS == 3) {
+      const size_t blk = (size_t)(slot0 + ci) * H + h;
+      cs_dst = p.chunk_states + blk * (size_t)(D * D);
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int rt8 = 0; rt8 < 8; ++rt8)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            cs_dst[(size_t)(16 * rt8 + 4 * g + i) * D + col0 + 16 * c + l16] = accS[c][rt8][i];
+    }
     __syncthreads();
     if (EPI) load_gate(t0, nv);
     if (ci + 1 < nch) load_u(ci + 1);
@@ -464,6 +479,17 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
 #pragma unroll
             for (int c = 0; c < CT; ++c) accO[c][rt] = mma(accO[c][rt], fa, sf[c][ks]);
           }
+    }
+    if constexpr (PASS == 3) {
+      // U = U' - W S of this chunk, row-major fp32 [C][128] (rows past the
+      // sequence end are zero)
+      float* u_dst = p.chunk_u + ((size_t)(slot0 + ci) * H + h) * (size_t)(C * D);
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int a = 0; a < NT; ++a)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) u_dst[(size_t)(16 * a + 4 * g + i) * D + col0 + 16 * c + l16] = accU[c][a][i];
     }
     Frag<E> uf[CT][KT];
 #pragma unroll
@@ -621,6 +647,8 @@ static hipError_t launch_carry_dtype(const CarryArgs& a, hipStream_t stream) {
     return hipErrorInvalidValue;
   }
   if (a.pass == 0 && a.col_split == 2) return launch_carry_t<E, C, 64, false, 1, 0>(a, stream);
+  if (a.pass == 3 && a.col_split == 2 && a.chunk_states && a.chunk_u)
+    return launch_carry_t<E, C, 64, false, 1, 3>(a, stream);
   if (a.pass == 1 && a.col_split == 4) return launch_carry_t<E, C, 64, false, 1, 1>(a, stream);
   if (a.pass == 2 && a.col_split == 2) return launch_carry_t<E, C, 64, false, 1, 2>(a, stream);
   return hipErrorInvalidValue;

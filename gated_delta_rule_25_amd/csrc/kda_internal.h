@@ -188,12 +188,86 @@ struct CarryArgs {
   //   the end states go to pairs[seg][h][0 or 1], no outputs are written.
   // pass 2: one per (segment, head): from pairs[seg][h][0] (which the scan
   //   has overwritten with the segment's incoming state), outputs only.
+  // pass 3 (states pass of the backward): as pass 0 without outputs; every
+  //   chunk's incoming state goes to chunk_states [slot][H][128][128] and its
+  //   U = U' - W S to chunk_u [slot][H][C][128], both row-major fp32.
   int pass;
+  float* chunk_states;
+  float* chunk_u;
   const int32_t* seg_list;   // [2 * segments]: sequence, segment index within the window's range
   const int32_t* seg_count;  // device: number of segments
   int seg_chunks;            // chunks per segment
   float* pairs;              // [segments][H][2][128][128] fp32
 };
+
+// ---------------------------------------------------------------------------
+// Backward pass (kda_bwd.hip).  One factor-store window covers every chunk, so
+// a slot index is a global chunk index (sequence n owns slots
+// [seq_first[n], seq_first[n + 1])).  Per slot and head the workspace holds
+// the forward factor block, the chunk's incoming state S and U = U' - W S
+// (the carry's states pass), the reverse carry's block below, and the
+// gradient dS reaching the chunk's end plus dU = P^T dO + Kb dS (the reverse
+// carry), all row-major fp32 except the blocks.
+//
+// Reverse-carry block of one (chunk, head), in the fragment order of the
+// reverse carry's matrix-core steps (fragments as in FactorBlock):
+//   KB [NT][4]    Kb = K (.) e^{g_n - g}: row tile = 16 tokens, step over keys
+//   WT [8][KT]    -W^T: row tile = 16 key channels, step over tokens
+//   G  [128]      e^{g_n} (fp32, in a 1 KiB piece)
+//   X  [NT][8][64][4]  P^T dO in accumulator order (token tile, column tile)
+//   Y  [8][8][64][4]   Qt^T dO in accumulator order (key tile, column tile)
+// X and Y in the I/O dtype.  KB, WT and G are contiguous, so one copy moves
+// them into LDS.
+template <int ES, int C>
+struct DCarryBlock {
+  static constexpr int NT = C / 16;
+  static constexpr int KT = C / 32;
+  static constexpr uint32_t FR = 512u * ES;
+  static constexpr uint32_t TILE = 256u * ES;  // one accumulator-order tile
+  static constexpr uint32_t KB = 0;
+  static constexpr uint32_t WT = KB + NT * 4 * FR;
+  static constexpr uint32_t G = WT + 8 * KT * FR;
+  static constexpr uint32_t X = G + 1024;
+  static constexpr uint32_t Y = X + NT * 8 * TILE;
+  static constexpr uint32_t BYTES = (Y + 64 * TILE + 255) & ~255u;
+  static constexpr uint32_t LDS_PART = X;  // the part the loader copies
+};
+constexpr size_t dcarry_block_bytes(bool bf16) {
+  return bf16 ? DCarryBlock<2, 64>::BYTES : DCarryBlock<4, 32>::BYTES;
+}
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_alpha;
+  const float* beta;
+  const void* d_o;               // [T,H,128] dtype
+  const float* d_final_state;    // [N,H,128,128] or null (zero)
+  const int32_t* cu;
+  const int32_t* order;          // longest-first sequences or null
+  const int32_t* seq_first;      // [N+1] first slot of each sequence
+  int num_seqs;
+  int num_heads;
+  int64_t total_tokens;
+  int slots;                     // slot capacity (grid bound of the per-chunk kernels)
+  bool bf16;
+  const void* factors;           // forward factor blocks [slot][H]
+  void* dblocks;                 // reverse-carry blocks [slot][H]
+  const float* chunk_states;     // [slot][H][128][128]
+  const float* chunk_u;          // [slot][H][C][128]
+  float* chunk_ds;               // [slot][H][128][128]: dS at the chunk's end
+  float* chunk_du;               // [slot][H][C][128]
+  void* dq;                      // [T,H,128] dtype
+  void* dk;
+  void* dv;
+  float* dlog_alpha;             // [T,H,128]
+  float* dbeta;                  // [T,H]
+  float* d_initial_state;        // [N,H,128,128] or null (not written)
+};
+hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_carry(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_grad(const BwdArgs& a, hipStream_t stream);
 
 // Window w of nw: sequence n of G_n chunks gets chunks
 // [min(w Q_n, G_n), min((w + 1) Q_n, G_n)) with Q_n = ceil(G_n / nw).

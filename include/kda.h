@@ -223,6 +223,54 @@ kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, co
                                  hipStream_t stream);
 
 /*
+ * Bytes of device workspace kda_chunk_bwd needs for these sizes (host-side
+ * computation; 0 for invalid sizes).  Every chunk of the input is held at
+ * once: per (64-token chunk, head) for bf16 I/O about 70.5 KiB of forward
+ * factors, 81 KiB for the reverse carry, and 2 x 64 KiB + 2 x 32 KiB of fp32
+ * states, gradients and intermediates (about 343 KiB, i.e. 5.4 KiB per
+ * token and head); fp32 I/O uses 32-token chunks (about 342 KiB per chunk,
+ * 10.7 KiB per token and head).
+ */
+size_t kda_chunk_bwd_workspace_bytes(int num_seqs, int64_t total_tokens, int num_heads, int d_k, int d_v,
+                                     kda_dtype dtype);
+
+/*
+ * Backward pass of kda_chunk_fwd without the fused prologue and epilogue
+ * (training; "Kimi K3 架构…" section 7.1: the FlashKDA kernel serves training
+ * as well as prefill).  For the loss
+ *
+ *     L = sum_t <d_o_t, o_t> + <d_final_state, S_T>       (per sequence and head)
+ *
+ * it writes the gradients of L with respect to q, k, v, log_alpha, beta and
+ * initial_state.  The forward states are recomputed internally (the call
+ * needs only the forward's inputs), so it does not depend on a prior
+ * kda_chunk_fwd call.
+ *
+ *   q, k, v, log_alpha, beta, initial_state, cu_seqlens
+ *                  as for kda_chunk_fwd (log_alpha in [-5, 0]: the unbounded
+ *                  decay is not supported here)
+ *   d_o            [T_total, H, 128] dtype: gradient of L with respect to o
+ *   d_final_state  [N, H, 128, 128] fp32 or NULL (zero)
+ *   dq, dk, dv     [T_total, H, 128] dtype outputs
+ *   dlog_alpha     [T_total, H, 128] fp32 output
+ *   dbeta          [T_total, H] fp32 output
+ *   d_initial_state [N, H, 128, 128] fp32 output, or NULL (not written); for
+ *                  a zero-length sequence it equals d_final_state
+ *   workspace      at least kda_chunk_bwd_workspace_bytes() bytes (contents
+ *                  on entry ignored)
+ * No output may overlap an input, another output or the workspace
+ * (KDA_ERR_INVALID_ARG).  Alignment as for kda_chunk_fwd; d_o, the gradients
+ * and the state gradients need 16 bytes, dbeta 4.  Asynchronous on `stream`
+ * like every other call; the recomputed forward uses the same kernels as
+ * kda_chunk_fwd, so its rounding is that of the forward.
+ */
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                         const float* initial_state, const int32_t* cu_seqlens, const void* d_o,
+                         const float* d_final_state, int num_seqs, int64_t total_tokens, int num_heads, int d_k,
+                         int d_v, kda_dtype dtype, void* dq, void* dk, void* dv, float* dlog_alpha, float* dbeta,
+                         float* d_initial_state, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * One decode step for N independent sequences: each (n, h) state advances by
  * one token in place ("Kimi K3 架构…" section 4.2.7: decoding keeps one
  * fixed-size d_k x d_v state per head and advances it in place).

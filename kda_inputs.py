@@ -38,6 +38,9 @@ is deterministic for a given device type):
            before the drafts); S0 std * N(0,1).  Tokens run per sequence on
            commit: uniform on {1, ..., L} from numpy's Philox generator (the
            pages give no acceptance rate).
+  backward seeds (the loss gradients a training step feeds the backward
+           pass): d_o N(0,1) in the I/O dtype [T, H, 128]; d_final_state
+           std * N(0,1) fp32 [N, H, 128, 128], or None when std = 0.
 """
 from __future__ import annotations
 
@@ -159,6 +162,15 @@ def make_prefill(H, lengths, dtype="bf16", s0_std=0.0, fused=False, device="cpu"
         out["gate"] = gate
         out["norm_w"] = None
     return out
+
+
+def make_grad_seeds(H, N, T, dtype="bf16", ds_std=1.0, device="cpu", seed=SEED_BASE + 0x6B):
+    """Gradients of the loss with respect to o and to the final state."""
+    g = _gen(device, seed)
+    d_o = torch.empty((T, H, D), dtype=torch_dtype(dtype), device=device)
+    _fill_unit(d_o, g, device, False, 16384)
+    dsT = ds_std * _randn((N, H, D, D), g, device) if ds_std > 0 else None
+    return d_o, dsT
 
 
 def make_decode(N, H, steps, dtype="bf16", s0_std=0.02, device="cpu", seed=SEED_BASE):

@@ -39,6 +39,10 @@ def lib():
     L.kda_chunk_fwd.argtypes = [vp] * 7 + [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.kda_chunk_fwd_noalloc.restype = i32
     L.kda_chunk_fwd_noalloc.argtypes = [vp] * 7 + [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp]
+    L.kda_chunk_bwd_workspace_bytes.restype = sz
+    L.kda_chunk_bwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32]
+    L.kda_chunk_bwd.restype = i32
+    L.kda_chunk_bwd.argtypes = [vp] * 9 + [i32, i64, i32, i32, i32, i32] + [vp] * 7 + [sz, vp]
     L.kda_decode_step.restype = i32
     L.kda_decode_step.argtypes = [vp] * 6 + [i32, i32, i32, i32, i32, vp, vp]
     L.kda_decode_replay.restype = i32
@@ -54,7 +58,8 @@ def declared_functions():
 
 def test_header_symbols_exported(lib):
     names = declared_functions()
-    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_workspace_bytes", "kda_decode_step",
+    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_workspace_bytes", "kda_chunk_bwd",
+                          "kda_chunk_bwd_workspace_bytes", "kda_decode_step",
                           "kda_decode_replay", "kda_last_precondition_flags", "kda_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s+(kda_\w+)", out))
@@ -244,6 +249,55 @@ def test_noalloc_limits(lib):
     assert na(T=-1) == INVALID
     assert na(opts=opts_p(Opts(factor_budget_mib=-5))) == INVALID
     assert na(N=1, cu=None, H=2, opts=opts_p(Opts(segment_tokens=100))) == INVALID
+
+
+def bwd_ws(N, T, H, C=64, fb=FB_BF16, db=82944):
+    """Workspace of kda_chunk_bwd (the layout kda_api.hip documents): order
+    (N > 1), chunk table, then per (slot, head) the forward factor block, the
+    reverse-carry block, two 128 x 128 fp32 states and two C x 128 fp32 blocks."""
+    slots = T // C + N + 1
+    b = (a256(4 * N) if N > 1 else 0) + a256(4 * (N + 1)) + 2 * a256(4 * N)
+    return b + slots * H * (fb + db + 2 * 65536 + 2 * C * 512)
+
+
+def test_bwd_workspace_bytes(lib):
+    # reverse-carry block (bf16, 64-token chunks): Kb 16 KiB + -W^T 16 KiB + gamma
+    # 1 KiB + P^T dO 16 KiB + Qt^T dO 32 KiB = 82944 bytes
+    assert lib.kda_chunk_bwd_workspace_bytes(1, 8192, 96, 128, 128, BF16) == bwd_ws(1, 8192, 96)
+    assert lib.kda_chunk_bwd_workspace_bytes(3, 1000, 2, 128, 128, BF16) == bwd_ws(3, 1000, 2)
+    assert lib.kda_chunk_bwd_workspace_bytes(1, 0, 2, 128, 128, BF16) == bwd_ws(1, 0, 2)
+    assert lib.kda_chunk_bwd_workspace_bytes(1, 100, 2, 64, 128, BF16) == 0
+    assert lib.kda_chunk_bwd_workspace_bytes(0, 100, 2, 128, 128, BF16) == 0
+    assert lib.kda_chunk_bwd_workspace_bytes(1, 100, 2, 128, 128, 9) == 0
+
+
+def bwd(lib, **kw):
+    a = dict(q=p(0), k=p(1), v=p(2), la=p(3), b=p(4), s0=None, cu=None, do=p(5), dsT=None, N=1, T=10, H=2,
+             dk_=128, dv_=128, dt=BF16, gq=p(6), gk=p(7), gv=p(8), gla=p(9), gb=p(10), gs0=None, ws=p(11),
+             wsb=64 * MB)
+    a.update(kw)
+    return lib.kda_chunk_bwd(a["q"], a["k"], a["v"], a["la"], a["b"], a["s0"], a["cu"], a["do"], a["dsT"], a["N"],
+                             a["T"], a["H"], a["dk_"], a["dv_"], a["dt"], a["gq"], a["gk"], a["gv"], a["gla"], a["gb"],
+                             a["gs0"], a["ws"], a["wsb"], None)
+
+
+def test_bwd_validation(lib):
+    assert bwd(lib, dk_=64) == UNSUPPORTED
+    assert bwd(lib, dt=3) == UNSUPPORTED
+    assert bwd(lib, N=0) == INVALID
+    assert bwd(lib, N=2) == INVALID                            # several sequences need cu_seqlens
+    assert bwd(lib, do=None) == INVALID
+    assert bwd(lib, gla=None) == INVALID
+    assert bwd(lib, ws=None, wsb=0) == WORKSPACE
+    need = lib.kda_chunk_bwd_workspace_bytes(1, 10, 2, 128, 128, BF16)
+    assert bwd(lib, wsb=need - 1) == WORKSPACE
+    assert bwd(lib, gq=p(0)) == INVALID                        # dq aliases q
+    assert bwd(lib, gk=p(6)) == INVALID                        # two gradients share memory
+    assert bwd(lib, gb=p(5)) == INVALID                        # dbeta aliases d_o
+    assert bwd(lib, ws=p(9)) == INVALID                        # workspace aliases dlog_alpha
+    assert bwd(lib, gs0=p(12), s0=p(12)) == INVALID            # d_initial_state aliases initial_state
+    assert bwd(lib, gv=ctypes.c_void_p(BASE + 8 * 64 * MB + 8)) == INVALID  # not 16-byte aligned
+    assert bwd(lib, gb=ctypes.c_void_p(BASE + 10 * 64 * MB + 2)) == INVALID  # dbeta not 4-byte aligned
 
 
 def decode(lib, **kw):

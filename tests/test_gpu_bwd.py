@@ -1,0 +1,139 @@
+"""GPU parity of the backward pass (kda_chunk_bwd) against the fp64 oracle's
+backward (oracle.chunk_bwd), through the C ABI (Python binding).
+
+Every gradient is compared per (sequence, head) slice with the normwise
+metric of tests/kda_testlib.py (bars 2e-2 for bf16 I/O, 1e-4 for fp32): dq,
+dk, dv, dlog_alpha ([tokens, 128] slices), dbeta ([tokens] slices) and
+d_initial_state ([128, 128]).  The loss seeds d_o and d_final_state are
+drawn by kda_inputs.make_grad_seeds.
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+import gated_delta_rule_25_amd as kda
+import oracle
+from kda_testlib import TOL, elem_err, slice_err, sync, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+NAMES = ["dq", "dk", "dv", "dlog_alpha", "dbeta", "d_initial_state"]
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_bwd(inp, d_o, dsT):
+    out = kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], d_o,
+                        initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"], d_final_state=dsT)
+    sync()
+    return out
+
+
+def compare_bwd(inp, d_o, dsT, got, heads=None):
+    """Worst normwise (and secondary elementwise) slice error per gradient,
+    the oracle run per sequence on the selected heads."""
+    cu = inp["cu_host"].numpy().astype(np.int64)
+    H = inp["H"]
+    hs = list(range(H)) if heads is None else list(heads)
+    worst = {k: 0.0 for k in NAMES}
+    welem = {k: 0.0 for k in NAMES}
+    for n in range(len(cu) - 1):
+        a, e = int(cu[n]), int(cu[n + 1])
+        sl = slice(a, e)
+        s0 = None if inp["initial_state"] is None else to64(inp["initial_state"][n:n + 1, hs])
+        dst = None if dsT is None else to64(dsT[n:n + 1, hs])
+        ref = oracle.chunk_bwd(to64(inp["q"][sl][:, hs]), to64(inp["k"][sl][:, hs]), to64(inp["v"][sl][:, hs]),
+                               to64(inp["log_alpha"][sl][:, hs]), to64(inp["beta"][sl][:, hs]),
+                               to64(d_o[sl][:, hs]), initial_state=s0, d_final_state=dst)
+        for idx, name in enumerate(NAMES):
+            y = to64(got[idx][n:n + 1, hs])[0] if name == "d_initial_state" else to64(got[idx][sl][:, hs])
+            r = ref[idx][0] if name == "d_initial_state" else ref[idx]
+            for j in range(len(hs)):
+                yy = y[j] if name == "d_initial_state" else y[:, j]
+                rr = r[j] if name == "d_initial_state" else r[:, j]
+                if yy.size == 0:
+                    continue
+                worst[name] = max(worst[name], slice_err(yy, rr))
+                welem[name] = max(welem[name], elem_err(yy, rr))
+    return worst, welem
+
+
+CASES = [
+    # (name, H, lengths, dtype, s0_std, ds_std, log_alpha scale)
+    ("f32_T256_config0_shape", 2, [256], "f32", 0.0, 1.0, 1.0),
+    ("f32_T1", 2, [1], "f32", 0.5, 1.0, 1.0),
+    ("f32_T33_ragged", 2, [33], "f32", 0.5, 0.0, 1.0),
+    ("f32_varlen_empty", 2, [70, 0, 1, 45], "f32", 0.3, 1.0, 1.0),
+    ("f32_slow_decay", 2, [300], "f32", 0.3, 1.0, 0.002),
+    ("bf16_T64_one_chunk", 2, [64], "bf16", 0.02, 1.0, 1.0),
+    ("bf16_T200_ragged", 3, [200], "bf16", 0.02, 1.0, 1.0),
+    ("bf16_varlen_empty", 2, [100, 0, 37, 1], "bf16", 0.3, 1.0, 1.0),
+    ("bf16_slow_decay", 2, [700], "bf16", 0.3, 1.0, 0.002),
+    ("bf16_no_final_grad", 2, [150], "bf16", 0.3, 0.0, 1.0),
+]
+
+
+@pytest.mark.parametrize("name,H,lengths,dtype,s0,ds,scale", CASES, ids=[c[0] for c in CASES])
+def test_bwd_parity(name, H, lengths, dtype, s0, ds, scale):
+    say("case %s H=%d lengths=%s dtype=%s S0 std %g dS_T std %g decay x%g" % (name, H, lengths, dtype, s0, ds, scale))
+    seed = zlib.crc32(name.encode()) & 0xFFFF
+    inp = kda_inputs.make_prefill(H, lengths, dtype, s0, False, DEV, seed=seed)
+    inp["log_alpha"].mul_(scale)
+    d_o, dsT = kda_inputs.make_grad_seeds(H, len(lengths), sum(lengths), dtype, ds, DEV, seed=seed + 1)
+    got = run_bwd(inp, d_o, dsT)
+    for t in got:
+        assert torch.isfinite(t.float()).all()
+    worst, welem = compare_bwd(inp, d_o, dsT, got)
+    say("  " + " ".join("%s %.2e" % (k, worst[k]) for k in NAMES))
+    say("  elementwise " + " ".join("%s %.2e" % (k, welem[k]) for k in NAMES))
+    for k in NAMES:
+        assert worst[k] <= TOL[dtype], (k, worst[k])
+
+
+def test_bwd_worst_case_decay():
+    """log_alpha = -5 everywhere: the diagonal tiles' factors reach exactly
+    e^80, the decay bound's limit."""
+    say("case worst-case decay: bf16 H=2 T=128, log_alpha = -5")
+    inp = kda_inputs.make_prefill(2, [128], "bf16", 0.3, False, DEV, seed=77)
+    inp["log_alpha"].fill_(-5.0)
+    d_o, dsT = kda_inputs.make_grad_seeds(2, 1, 128, "bf16", 1.0, DEV, seed=78)
+    got = run_bwd(inp, d_o, dsT)
+    for t in got:
+        assert torch.isfinite(t.float()).all()
+    worst, _ = compare_bwd(inp, d_o, dsT, got)
+    say("  " + " ".join("%s %.2e" % (k, worst[k]) for k in NAMES))
+    for k in NAMES:
+        assert worst[k] <= TOL["bf16"], (k, worst[k])
+
+
+@pytest.mark.timeout(900)
+def test_bwd_one_layer_T8192_all_heads():
+    """The K3 layer's shape (H=96, T=8192, bf16), every head against the oracle."""
+    say("workload 1 backward: bf16 H=96 T=8192, every head")
+    inp = kda_inputs.make_workload(1, device=DEV)
+    d_o, dsT = kda_inputs.make_grad_seeds(96, 1, 8192, "bf16", 1.0, DEV)
+    got = run_bwd(inp, d_o, dsT)
+    for t in got:
+        assert torch.isfinite(t.float()).all()
+    total = {k: 0.0 for k in NAMES}
+    for h0 in range(0, 96, 16):
+        worst, welem = compare_bwd(inp, d_o, dsT, got, heads=range(h0, h0 + 16))
+        say("  heads %d..%d: " % (h0, h0 + 15) + " ".join("%s %.2e" % (k, worst[k]) for k in NAMES))
+        for k in NAMES:
+            total[k] = max(total[k], worst[k])
+    for k in NAMES:
+        assert total[k] <= TOL["bf16"], (k, total[k])
+
+
+def test_bwd_errors():
+    inp = kda_inputs.make_prefill(2, [10], "bf16", 0.0, False, DEV, seed=5)
+    d_o, _ = kda_inputs.make_grad_seeds(2, 1, 10, "bf16", 0.0, DEV)
+    with pytest.raises(ValueError):
+        kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], d_o[:5])
