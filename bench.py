@@ -14,6 +14,9 @@ the varlen fused prologue/epilogue, the few-head (H=8, T=131072, segmented
 schedule) and the unbounded-decay (the one-layer shape with Kimi Linear's
 negative-softplus decay, per-position diagonal tiles) workloads are timed with
 fewer steps and reported under "workloads".
+The backward pass (kda_chunk_bwd: gradients of q, k, v, log_alpha, beta and
+the initial state for the one-layer workload and seeded d_o, d_final_state)
+is reported under "backward".
 The speculative-decoding replay (the same 256 x 96 batch with 8 cached tokens
 per sequence: a verification pass over all of them, then the in-place commit
 of the drawn accepted counts, both kda_decode_replay with the fused
@@ -58,6 +61,25 @@ def prefill_algorithmic_flops(T: int, H: int, C: int) -> float:
     P U) + C^2 / 3 (the solve) + d^2 / C (the state decay)."""
     d = 128
     return T * H * (6 * d * d + 5 * C * d + C * C / 3 + d * d / C)
+
+
+def backward_algorithmic_bytes(T: int, H: int, N: int, es: int) -> int:
+    """Compulsory HBM bytes of one kda_chunk_bwd: read q, k, v, d_o (I/O
+    dtype), log_alpha, beta; write dq, dk, dv (I/O dtype), dlog_alpha, dbeta;
+    read the initial state and d_final_state, write d_initial_state."""
+    d = 128
+    per_tok_head = 4 * d * es + d * 4 + 4 + 3 * d * es + d * 4 + 4
+    return T * H * per_tok_head + 3 * N * H * d * d * 4
+
+
+def backward_algorithmic_flops(T: int, H: int, C: int) -> float:
+    """Flops of the chunked backward per layer, per token-head: the forward
+    states recomputed (4 d^2 + 5 C d + C^2 / 3), the reverse carry (6 d^2 + C d:
+    Kb dS, W^T dU, Qt^T dO, P^T dO) and the gradient products (6 d^2 + 10 C d + C^2:
+    dO S^T, dU S^T, U dS^T, dO U^T, dU V^T, dW Kt^T, T^T dW, T^T dU, the Gram
+    tiles and their tile-referenced gradients, M^T dM M^T)."""
+    d = 128
+    return T * H * (16 * d * d + 16 * C * d + 4 * C * C / 3)
 
 
 def decode_algorithmic_bytes(N: int, H: int, es: int) -> int:
@@ -245,6 +267,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-decode", action="store_true", help="time only the decode workload (profiling)")
     ap.add_argument("--only-prefill", action="store_true", help="time only the prefill workload (profiling)")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=5)
+    ap.add_argument("--only-backward", action="store_true", help="time only the backward pass (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -262,17 +287,19 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     result = {}
-    if args.only_prefill:
-        args.no_decode = True
-        args.no_cpu_baseline = True
-    if args.only_prefill or args.only_decode or args.only_replay:
+    only = args.only_prefill or args.only_decode or args.only_replay or args.only_backward
+    if only:
         args.extra_workloads = ""
-    if args.only_decode or args.only_replay:
+    if only and not args.only_prefill:
         args.no_cpu_baseline = True
-    if args.only_prefill or args.only_replay:
+    if args.only_prefill:
+        args.no_cpu_baseline = True
+    if only and not args.only_decode:
         args.no_decode = True
-    if args.only_prefill or args.only_decode:
+    if only and not args.only_replay:
         args.no_replay = True
+    if only and not args.only_backward:
+        args.no_backward = True
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -281,7 +308,7 @@ def main():
         result["copy_calibration_bytes"] = src.numel() * 4
         del src, dst
 
-    if not (args.only_decode or args.only_replay):
+    if not (args.only_decode or args.only_replay or args.only_backward):
         inp, tm = time_prefill(kda, kda_inputs, args.workload, args.steps, args.warmup, dev, stream)
         result.update({
             "metric": "KDA prefill tokens/s (H=96,d=128,T=8K) + decode steps/s; % of roofline",
@@ -366,6 +393,13 @@ def main():
         del d, state, outs
         torch.cuda.empty_cache()
 
+    if not args.no_backward:
+        result["backward"] = time_backward(kda, kda_inputs, args.backward_steps, dev, stream)
+        if args.only_backward:
+            result.update({"metric": "KDA backward tokens/s", "unit": "tokens/s",
+                           "value": result["backward"]["tokens_per_s"]})
+        torch.cuda.empty_cache()
+
     if not args.no_replay:
         result["replay"] = time_replay(kda, kda_inputs, args.replay_rounds, dev, stream,
                                        result.get("decode", {}).get("ms_per_step"))
@@ -373,6 +407,47 @@ def main():
             result.update({"metric": "KDA replay committed tokens/s", "unit": "tokens/s",
                            "value": result["replay"]["committed_tokens_per_s"]})
     print(json.dumps(result), flush=True)
+
+
+def time_backward(kda, kda_inputs, steps, dev, stream):
+    """kda_chunk_bwd over the one-layer workload (H=96, T=8192, bf16, S0 and
+    d_final_state given): one warm-up call, then `steps` calls, each bracketed
+    by HIP events on the stream the kernels run on."""
+    import torch
+    w = kda_inputs.WORKLOADS[1]
+    inp = kda_inputs.make_workload(1, device=dev)
+    T, H, N = inp["T"], inp["H"], inp["N"]
+    d_o, dsT = kda_inputs.make_grad_seeds(H, N, T, w["dtype"], 1.0, dev)
+    ws = torch.empty(kda.chunk_bwd_workspace_bytes(N, T, H, inp["q"].dtype), dtype=torch.uint8, device=dev)
+
+    def call():
+        return kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], d_o,
+                             initial_state=inp["initial_state"], d_final_state=dsT, workspace=ws)
+
+    out = call()
+    torch.cuda.synchronize()
+    finite = all(bool(torch.isfinite(t.float()).all().item()) for t in out)
+    del out
+    per = time_events(call, steps, stream)
+    ms = sum(per) / len(per)
+    es = 2
+    C = 64
+    b = backward_algorithmic_bytes(T, H, N, es)
+    flops = backward_algorithmic_flops(T, H, C)
+    ach = b / (ms * 1e-3) / 1e9
+    tfl = flops / (ms * 1e-3) / 1e12
+    res = {"workload": w["name"], "dtype": w["dtype"], "steps": steps, "ms_per_call": ms, "ms_min": min(per),
+           "tokens_per_s": T * 1e3 / ms, "finite": finite,
+           "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": ach / HBM_PEAK_GBPS, "algorithmic_bytes": b, "traffic": None,
+                        "kernel": "kda_chunk_bwd = worklist/window table + prep_kernel + carry_kernel (states "
+                                  "pass) + bwd_prep_kernel + bwd_carry_kernel + bwd_grad_kernel",
+                        "kernel_ms_avg": ms},
+           "mfma": {"algorithmic_flops": flops, "chunk": C, "achieved_tflops": tfl,
+                    "bf16_peak_tflops": MFMA_BF16_PEAK_TFLOPS, "fp32_peak_tflops": MFMA_FP32_PEAK_TFLOPS,
+                    "attainable_tflops_bf16": min(MFMA_BF16_PEAK_TFLOPS, flops / b * HBM_PEAK_GBPS / 1e3)}}
+    del inp, d_o, dsT, ws
+    return res
 
 
 def time_replay(kda, kda_inputs, rounds, dev, stream, decode_ms=None):
