@@ -103,15 +103,28 @@ __device__ __forceinline__ void store4(E* dst, f32x4 x) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_prep_kernel: one workgroup of four waves per (slot, head).
+// bwd_prep_kernel: one workgroup of four waves per (slot, head).  The factor
+// block's Qt and P and the chunk's dO are first transposed once into
+// row-major LDS arrays (contraction index contiguous), so every 16-deep
+// matrix-core step reads its four operand values per lane in one access.
+// The products run in the I/O dtype: Qt, P and dO are values of that dtype
+// already, so with fp32 accumulation nothing is rounded.
 // ---------------------------------------------------------------------------
 template <typename E, int C>
 struct PrepBwdLayout {
   using F = FactorBlock<(int)sizeof(E), C>;
-  static constexpr int PD = D + 4;                       // dO row pitch (floats)
-  static constexpr size_t DO = F::BYTES;                 // f32 [C][PD]
-  static constexpr size_t BYTES = DO + (size_t)C * PD * 4;
+  static constexpr int PT = C + 8;                          // row pitch (elements) of the transposed arrays
+  static constexpr size_t FB = F::U;                        // the factor block up to U' (not needed)
+  static constexpr size_t QT = FB;                          // E [128][PT]  Qt^T
+  static constexpr size_t PTR = QT + (size_t)D * PT * sizeof(E);   // E [C][PT]  P^T
+  static constexpr size_t DOT = PTR + (size_t)C * PT * sizeof(E);  // E [128][PT] dO^T
+  static constexpr size_t BYTES = DOT + (size_t)D * PT * sizeof(E);
+  static_assert(FB % 16 == 0 && QT % 16 == 0 && PTR % 16 == 0 && DOT % 16 == 0, "16-byte pieces");
 };
+
+// 4 consecutive elements (16-deep operand of one lane) as Frag16
+__device__ __forceinline__ void ld4(Frag16<__bf16>& f, const __bf16* p) { f.v = *reinterpret_cast<const bf16x4*>(p); }
+__device__ __forceinline__ void ld4(Frag16<float>& f, const float* p) { f.v = *reinterpret_cast<const f32x4*>(p); }
 
 template <typename E, int C>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
@@ -119,10 +132,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
   using F = FactorBlock<ES, C>;
   using DB = DCarryBlock<ES, C>;
   using L = PrepBwdLayout<E, C>;
-  constexpr int NT = C / 16, KT = C / 32, PD = L::PD;
+  constexpr int NT = C / 16, KT = C / 32, PT = L::PT;
   static_assert(L::BYTES <= 160 * 1024, "LDS budget exceeded");
   extern __shared__ __align__(16) unsigned char smem[];
-  float* sDO = reinterpret_cast<float*>(smem + L::DO);
+  E* sQT = reinterpret_cast<E*>(smem + L::QT);
+  E* sPT = reinterpret_cast<E*>(smem + L::PTR);
+  E* sDOT = reinterpret_cast<E*>(smem + L::DOT);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int H = p.num_heads, h = blockIdx.x % H, slot = blockIdx.x / H;
   if (slot >= p.seq_first[p.num_seqs]) return;
@@ -135,16 +150,32 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
 
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(p.factors) + blk * F::BYTES);
-    for (int i = tid; i < (int)(F::BYTES / 16); i += 256) reinterpret_cast<u32x4*>(smem)[i] = src[i];
+    for (int i = tid; i < (int)(L::FB / 16); i += 256) reinterpret_cast<u32x4*>(smem)[i] = src[i];
+    // dO rows (16-byte pieces), transposed into dO^T[j][t]; zero past the end
+    constexpr int PER = 16 / ES;  // elements per piece
     const E* gdo = static_cast<const E*>(p.d_o);
     const int64_t rs = (int64_t)H * D;
-    for (int i = tid; i < C * D; i += 256) {
-      const int t = i / D, c = i % D;
-      sDO[t * PD + c] = t < nv ? to_f32(gdo[(t0 + t) * rs + (int64_t)h * D + c]) : 0.f;
+    for (int i = tid; i < C * (D / PER); i += 256) {
+      const int t = i / (D / PER), j0 = (i % (D / PER)) * PER;
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (t < nv) raw = *reinterpret_cast<const u32x4*>(gdo + (t0 + t) * rs + (int64_t)h * D + j0);
+      const E* x = reinterpret_cast<const E*>(&raw);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) sDOT[(j0 + e) * PT + t] = x[e];
     }
   }
   __syncthreads();
   const FactorView<E, C> fv{smem};
+  // Qt^T and P^T, one gather per element
+  for (int i = tid; i < C * D; i += 256) {
+    const int key = i % D, t = i / D;
+    sQT[key * PT + t] = from_f32<E>(fv.qt(t, key));
+  }
+  for (int i = tid; i < C * C; i += 256) {
+    const int s = i % C, t = i / C;
+    sPT[s * PT + t] = from_f32<E>(fv.p(t, s));
+  }
+  __syncthreads();
   char* dst = static_cast<char*>(p.dblocks) + blk * DB::BYTES;
 
   // X = P^T dO: tile (token tile sa, column tile jt); P[t][s] is zero for t < s
@@ -153,13 +184,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
     const int sa = ti / 8, jt = ti % 8;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int kb = sa; kb < NT; ++kb) {
-      Frag16<float> A, B;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * kb + 4 * g + e;
-        A.v[e] = fv.p(t, 16 * sa + l16);
-        B.v[e] = sDO[t * PD + 16 * jt + l16];
-      }
+      Frag16<E> A, B;
+      ld4(A, sPT + (16 * sa + l16) * PT + 16 * kb + 4 * g);
+      ld4(B, sDOT + (16 * jt + l16) * PT + 16 * kb + 4 * g);
       acc = mma16(acc, A, B);
     }
     store4(dX + ((size_t)ti * 64 + lane) * 4, acc);
@@ -169,14 +196,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
   for (int ti = wv; ti < 64; ti += 4) {
     const int it = ti / 8, jt = ti % 8;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int kb = 0; kb < NT; ++kb) {
-      Frag16<float> A, B;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * kb + 4 * g + e;
-        A.v[e] = fv.qt(t, 16 * it + l16);
-        B.v[e] = sDO[t * PD + 16 * jt + l16];
-      }
+    for (int kb = 0; kb < NT; ++kb) {
+      Frag16<E> A, B;
+      ld4(A, sQT + (16 * it + l16) * PT + 16 * kb + 4 * g);
+      ld4(B, sDOT + (16 * jt + l16) * PT + 16 * kb + 4 * g);
       acc = mma16(acc, A, B);
     }
     store4(dY + ((size_t)ti * 64 + lane) * 4, acc);
@@ -376,17 +400,17 @@ __global__ __launch_bounds__(320) void bwd_carry_kernel(const BwdArgs p) {
 // ---------------------------------------------------------------------------
 template <typename E, int C>
 struct GradLayout {
-  static constexpr int PK = D + 4;   // pitch of [C][128] arrays (elements)
+  static constexpr int PK = D + 8;   // pitch of [C][128] arrays (elements; 16-byte rows)
   static constexpr int PC = C + 4;   // pitch of [C][C] arrays
   static constexpr int JB = 32;      // value columns per staging block
-  static constexpr int PJ = JB + 4;
+  static constexpr int PJ = JB + 8;  // staging pitch (elements of E)
   static constexpr size_t K = 0;                                     // E   [C][PK] k
   static constexpr size_t Q = K + (size_t)C * PK * sizeof(E);        // E   [C][PK] q
   static constexpr size_t G = Q + (size_t)C * PK * sizeof(E);        // f32 [C][PK] g
   static constexpr size_t M = G + (size_t)C * PK * 4;                // f32 [C][PC] (I + A)^{-1}
   static constexpr size_t DP = M + (size_t)C * PC * 4;               // f32 [C][PC] dP
   static constexpr size_t UN = DP + (size_t)C * PC * 4;              // union area
-  static constexpr size_t UN_STAGE = 4 * (size_t)C * PJ * 4;         //   dO, U, dU, V column blocks
+  static constexpr size_t UN_STAGE = 4 * (size_t)C * PJ * sizeof(E); //   dO, U, dU, V column blocks (E)
   static constexpr size_t UN_DW = (size_t)C * PK * 4;                //   dW [C][PK]
   static constexpr size_t UN_CC = 2 * (size_t)C * PC * 4;            //   A, or dM / dB and X = dM M^T
   static constexpr size_t UN_BYTES = UN_STAGE > UN_DW ? (UN_STAGE > UN_CC ? UN_STAGE : UN_CC)
@@ -426,20 +450,47 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
   const int64_t hoff = (int64_t)h * D;
 
   // ---- inputs: k, q rows, the cumulative log-decay g (zeros past the end) ----
+  constexpr int PER = 16 / (int)sizeof(E);  // elements per 16-byte piece
   {
     const E* gk = static_cast<const E*>(p.k);
     const E* gq = static_cast<const E*>(p.q);
-    for (int i = tid; i < C * D; i += 256) {
-      const int t = i / D, c = i % D;
-      const bool ok = t < nv;
-      sK[t * PK + c] = ok ? gk[(t0 + t) * rs + hoff + c] : from_f32<E>(0.f);
-      sQ[t * PK + c] = ok ? gq[(t0 + t) * rs + hoff + c] : from_f32<E>(0.f);
+    for (int i = tid; i < C * (D / PER); i += 256) {
+      const int t = i / (D / PER), c = (i % (D / PER)) * PER;
+      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+      if (t < nv) {
+        a = *reinterpret_cast<const u32x4*>(gk + (t0 + t) * rs + hoff + c);
+        b = *reinterpret_cast<const u32x4*>(gq + (t0 + t) * rs + hoff + c);
+      }
+      *reinterpret_cast<u32x4*>(sK + t * PK + c) = a;
+      *reinterpret_cast<u32x4*>(sQ + t * PK + c) = b;
     }
-    if (tid < D) {
+    // cumulative log-decay: each half of the threads sums half of the tokens
+    // of one key channel (loads issued together), then the second half adds
+    // the first half's total
+    {
+      constexpr int HC = C / 2;
+      const int c = tid & (D - 1), half = tid >> 7;
+      float x[HC];
+#pragma unroll
+      for (int u = 0; u < HC; ++u) {
+        const int t = half * HC + u;
+        x[u] = t < nv ? p.log_alpha[(t0 + t) * rs + hoff + c] : 0.f;
+      }
       float run = 0.f;
-      for (int t = 0; t < C; ++t) {
-        if (t < nv) run += p.log_alpha[(t0 + t) * rs + hoff + tid];
-        sG[t * PK + tid] = run;
+#pragma unroll
+      for (int u = 0; u < HC; ++u) {
+        run += x[u];
+        x[u] = run;
+      }
+      if (half == 0) {
+#pragma unroll
+        for (int u = 0; u < HC; ++u) sG[u * PK + c] = x[u];
+      }
+      __syncthreads();
+      if (half == 1) {
+        const float base = sG[(HC - 1) * PK + c];
+#pragma unroll
+        for (int u = 0; u < HC; ++u) sG[(HC + u) * PK + c] = base + x[u];
       }
     }
     if (tid < C) {
@@ -543,10 +594,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
   const float* gDS = p.chunk_ds + blk * (size_t)(D * D);
   const float* gU = p.chunk_u + blk * (size_t)(C * D);
   const float* gDU = p.chunk_du + blk * (size_t)(C * D);
-  float* sDO = sUN;
-  float* sU = sUN + C * PJ;
-  float* sDU = sUN + 2 * C * PJ;
-  float* sV = sUN + 3 * C * PJ;
+  E* sDO = reinterpret_cast<E*>(sUN);
+  E* sU = sDO + C * PJ;
+  E* sDU = sDO + 2 * C * PJ;
+  E* sV = sDO + 3 * C * PJ;
   f32x4 rQs[NT][2], rW[NT][2], rKb[NT][2];
   float gpart[2] = {0.f, 0.f};
 #pragma unroll
@@ -562,13 +613,29 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
   E* gdv = static_cast<E*>(p.dv);
   __syncthreads();  // A (in the union area) is no longer read
   for (int j0 = 0; j0 < D; j0 += JB) {
-    for (int i = tid; i < C * JB; i += 256) {
-      const int t = i / JB, c = i % JB;
-      const bool ok = t < nv;
-      sDO[t * PJ + c] = ok ? to_f32(gdo[(t0 + t) * rs + hoff + j0 + c]) : 0.f;
-      sV[t * PJ + c] = ok ? to_f32(gv[(t0 + t) * rs + hoff + j0 + c]) : 0.f;
-      sU[t * PJ + c] = ok ? gU[(size_t)t * D + j0 + c] : 0.f;
-      sDU[t * PJ + c] = ok ? gDU[(size_t)t * D + j0 + c] : 0.f;
+    // dO and V (16-byte pieces of E), U and dU (fp32, four at a time, rounded to E)
+    for (int i = tid; i < C * (JB / PER); i += 256) {
+      const int t = i / (JB / PER), c = (i % (JB / PER)) * PER;
+      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+      if (t < nv) {
+        a = *reinterpret_cast<const u32x4*>(gdo + (t0 + t) * rs + hoff + j0 + c);
+        b = *reinterpret_cast<const u32x4*>(gv + (t0 + t) * rs + hoff + j0 + c);
+      }
+      *reinterpret_cast<u32x4*>(sDO + t * PJ + c) = a;
+      *reinterpret_cast<u32x4*>(sV + t * PJ + c) = b;
+    }
+    for (int i = tid; i < C * (JB / 4); i += 256) {
+      const int t = i / (JB / 4), c = (i % (JB / 4)) * 4;
+      f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+      if (t < nv) {
+        a = *reinterpret_cast<const f32x4*>(gU + (size_t)t * D + j0 + c);
+        b = *reinterpret_cast<const f32x4*>(gDU + (size_t)t * D + j0 + c);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sU[t * PJ + c + e] = from_f32<E>(a[e]);
+        sDU[t * PJ + c + e] = from_f32<E>(b[e]);
+      }
     }
     __syncthreads();
     // dQt += dO S^T, (dU S^T), dKb += U dS'^T, dgamma partials: own key tiles
@@ -577,19 +644,21 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
       const int i = 16 * (2 * wv + c) + l16;
 #pragma unroll
       for (int js = 0; js < JB / 16; ++js) {
-        Frag16<float> BS, BD;
-        BS.v = *reinterpret_cast<const f32x4*>(gS + (size_t)i * D + j0 + 16 * js + 4 * g);
-        BD.v = *reinterpret_cast<const f32x4*>(gDS + (size_t)i * D + j0 + 16 * js + 4 * g);
-        gpart[c] += BS.v[0] * BD.v[0] + BS.v[1] * BD.v[1] + BS.v[2] * BD.v[2] + BS.v[3] * BD.v[3];
+        const f32x4 xs = *reinterpret_cast<const f32x4*>(gS + (size_t)i * D + j0 + 16 * js + 4 * g);
+        const f32x4 xd = *reinterpret_cast<const f32x4*>(gDS + (size_t)i * D + j0 + 16 * js + 4 * g);
+        gpart[c] += xs[0] * xd[0] + xs[1] * xd[1] + xs[2] * xd[2] + xs[3] * xd[3];
+        Frag16<E> BS, BD;
+        frag16_from_acc(BS, xs);
+        frag16_from_acc(BD, xd);
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
           const int off = (16 * rt + l16) * PJ + 16 * js + 4 * g;
-          Frag16<float> A;
-          A.v = *reinterpret_cast<const f32x4*>(sDO + off);
+          Frag16<E> A;
+          ld4(A, sDO + off);
           rQs[rt][c] = mma16(rQs[rt][c], A, BS);
-          A.v = *reinterpret_cast<const f32x4*>(sDU + off);
+          ld4(A, sDU + off);
           rW[rt][c] = mma16(rW[rt][c], A, BS);
-          A.v = *reinterpret_cast<const f32x4*>(sU + off);
+          ld4(A, sU + off);
           rKb[rt][c] = mma16(rKb[rt][c], A, BD);
         }
       }
@@ -605,12 +674,12 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
         for (int js = 0; js < JB / 16; ++js) {
           const int offa = (16 * a + l16) * PJ + 16 * js + 4 * g;
           const int offb = (16 * b + l16) * PJ + 16 * js + 4 * g;
-          Frag16<float> A, B;
-          A.v = *reinterpret_cast<const f32x4*>(sDO + offa);
-          B.v = *reinterpret_cast<const f32x4*>(sU + offb);
+          Frag16<E> A, B;
+          ld4(A, sDO + offa);
+          ld4(B, sU + offb);
           rdP[x] = mma16(rdP[x], A, B);
-          A.v = *reinterpret_cast<const f32x4*>(sDU + offa);
-          B.v = *reinterpret_cast<const f32x4*>(sV + offb);
+          ld4(A, sDU + offa);
+          ld4(B, sV + offb);
           rdT[x] = mma16(rdT[x], A, B);
         }
       }
@@ -626,7 +695,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
         for (int e = 0; e < 4; ++e) {
           const int t = 16 * kb + 4 * g + e;
           A.v[e] = sM[t * PC + 16 * st + l16];
-          B.v[e] = sDU[t * PJ + 16 * jt + l16];
+          B.v[e] = to_f32(sDU[t * PJ + 16 * jt + l16]);
         }
         acc = mma16(acc, A, B);
       }
@@ -912,11 +981,14 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
   __syncthreads();
   E* gdq = static_cast<E*>(p.dq);
   E* gdk = static_cast<E*>(p.dk);
-  for (int i = tid; i < nv * D; i += 256) {
-    const int t = i / D, c = i % D;
-    gdq[(t0 + t) * rs + hoff + c] = oQ[t * PK + c];
-    gdk[(t0 + t) * rs + hoff + c] = oK[t * PK + c];
-    p.dlog_alpha[(t0 + t) * rs + hoff + c] = oG[t * PK + c];
+  for (int i = tid; i < nv * (D / PER); i += 256) {
+    const int t = i / (D / PER), c = (i % (D / PER)) * PER;
+    *reinterpret_cast<u32x4*>(gdq + (t0 + t) * rs + hoff + c) = *reinterpret_cast<const u32x4*>(oQ + t * PK + c);
+    *reinterpret_cast<u32x4*>(gdk + (t0 + t) * rs + hoff + c) = *reinterpret_cast<const u32x4*>(oK + t * PK + c);
+  }
+  for (int i = tid; i < nv * (D / 4); i += 256) {
+    const int t = i / (D / 4), c = (i % (D / 4)) * 4;
+    *reinterpret_cast<f32x4*>(p.dlog_alpha + (t0 + t) * rs + hoff + c) = *reinterpret_cast<const f32x4*>(oG + t * PK + c);
   }
   if (tid < nv) p.dbeta[(t0 + tid) * H + h] = sDbeta[tid];
 }
