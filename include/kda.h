@@ -52,7 +52,15 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enums have int as their underlying type in C++ as well, so that any
+ * int a C caller passes is a valid value for the library to check. */
+#ifdef __cplusplus
+#define KDA_ENUM_BASE : int
+#else
+#define KDA_ENUM_BASE
+#endif
+
+typedef enum KDA_ENUM_BASE {
   KDA_OK = 0,
   KDA_ERR_INVALID_ARG = 1, /* NULL where required, bad sizes, illegal overlap */
   KDA_ERR_UNSUPPORTED = 2, /* d_k or d_v other than 128, unknown dtype       */
@@ -80,7 +88,7 @@ enum {
   KDA_CHECK_CU_SEQLENS = 16 /* cu_seqlens not non-decreasing from 0 to total_tokens    */
 };
 
-typedef enum {
+typedef enum KDA_ENUM_BASE {
   KDA_DTYPE_F32 = 0,  /* q, k, v, gate and o are float                      */
   KDA_DTYPE_BF16 = 1  /* q, k, v, gate and o are bfloat16 (round-to-nearest-even on output) */
 } kda_dtype;
