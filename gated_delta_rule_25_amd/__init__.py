@@ -352,7 +352,7 @@ def decode_replay(state_in: Optional[torch.Tensor], q: torch.Tensor, k: torch.Te
                   conv_k_w: Optional[torch.Tensor] = None, conv_q_state: Optional[torch.Tensor] = None,
                   conv_k_state: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
                   norm_w: Optional[torch.Tensor] = None, l2_eps: float = 1e-6, rms_eps: float = 1e-6,
-                  out=None) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+                  out=None, unbounded_decay: bool = False) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
     """Multi-token decode from cached token inputs (kda_decode_replay).
 
     q, k, v: [N, L, H, 128] float32 or bfloat16 (L <= 16), log_alpha
@@ -363,7 +363,9 @@ def decode_replay(state_in: Optional[torch.Tensor], q: torch.Tensor, k: torch.Te
     itself) or the string "new" to allocate one.  conv_*_state [N, 3, H, 128]
     in the I/O dtype hold the raw rows before token 0 and are advanced in
     place when state_out is given.  out: None allocates the outputs, False
-    skips them.  Returns (o or None, state_out or None).
+    skips them.  unbounded_decay: accept any log_alpha <= 0 (the
+    negative-softplus decay) instead of the bound [-5, 0].  Returns (o or
+    None, state_out or None).
     """
     lib = _load()
     if q.dim() != 4 or q.shape[3] != D:
@@ -405,9 +407,9 @@ def decode_replay(state_in: Optional[torch.Tensor], q: torch.Tensor, k: torch.Te
     else:
         _check(out, "out", (N, L, H, D), dt, dev)
     opts = None
-    if any(x is not None for x in (conv_q_w, conv_k_w, gate, norm_w)):
+    if any(x is not None for x in (conv_q_w, conv_k_w, gate, norm_w)) or unbounded_decay:
         opts = ctypes.byref(_FusedOpts(_ptr(conv_q_w), _ptr(conv_k_w), _ptr(gate), _ptr(norm_w), float(l2_eps),
-                                       float(rms_eps), 0))
+                                       float(rms_eps), 0, int(bool(unbounded_decay)), 0))
     rc = lib.kda_decode_replay(_ptr(state_in), _ptr(state_out), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                                _ptr(beta), _ptr(num_tokens), N, L, H, D, D, _DTYPES[dt], opts,
                                _ptr(conv_q_state), _ptr(conv_k_state), _ptr(out), _stream(dev))

@@ -738,7 +738,6 @@ kda_status kda_decode_replay(const float* state_in, float* state_out, const void
   if (d_k != kD || d_v != kD || !dtype_ok(dtype) || max_tokens > kda::kReplayMaxTokens) return KDA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !log_alpha || !beta) return KDA_ERR_INVALID_ARG;
   const kda_fused_opts& f = opts ? *opts : kNoOpts;
-  if (f.unbounded_decay) return KDA_ERR_UNSUPPORTED;  // the block form needs the decay bound
   if (!(f.l2_eps >= 0.f) || !(f.rms_eps >= 0.f)) return KDA_ERR_INVALID_ARG;
   if ((f.conv_q_w && !conv_q_state) || (f.conv_k_w && !conv_k_state)) return KDA_ERR_INVALID_ARG;
   // a history without its convolution is neither read nor written
@@ -795,7 +794,7 @@ kda_status kda_decode_replay(const float* state_in, float* state_out, const void
     chk.q = f.conv_q_w ? nullptr : q;
     chk.k = f.conv_k_w ? nullptr : k;
     chk.bf16 = dtype == KDA_DTYPE_BF16;
-    chk.la_min = kBoundedLaMin;
+    chk.la_min = f.unbounded_decay ? -INFINITY : kBoundedLaMin;
     const kda_status cs = checked(chk, stream);
     if (cs != KDA_OK) return cs;
   }
@@ -823,6 +822,7 @@ kda_status kda_decode_replay(const float* state_in, float* state_out, const void
   a.num_heads = num_heads;
   a.max_tokens = max_tokens;
   a.bf16 = (dtype == KDA_DTYPE_BF16);
+  a.unbounded = f.unbounded_decay != 0;
   if (kda::launch_replay(a, stream) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
 }

@@ -41,6 +41,7 @@ struct ReplayArgs {
   int num_heads;
   int max_tokens;            // L
   bool bf16;
+  bool unbounded;            // log_alpha not bounded below: pairwise decay products, no 1 / D
 };
 
 // Inputs of the optional precondition checks (kda_debug.hip).

@@ -20,7 +20,12 @@
 // which is the token-by-token recurrence regrouped.  The decay lower bound
 // (log alpha >= -5, section 4.2.5: over 16 tokens the reciprocal stays
 // below e^80, inside the fp32 range) keeps every factor finite; that bound is
-// why a block holds at most 16 tokens.
+// why a block holds at most 16 tokens.  With the unbounded decay (Kimi
+// Linear's negative softplus, section 4.2.5) 1 / D can overflow, so that
+// mode never forms it: G[t][s] = sum_i x_t[i] k_s[i] prod_{s<r<=t} alpha_r[i]
+// is built pair by pair from running sums of log alpha over the tokens
+// between the two (same-sign sums, factors <= 1) and reduced over the
+// channels with wave sums, and Kb_t = k_t prod_{r>t} alpha_r from suffix sums.
 //
 // One 256-thread workgroup per (n, h).  Wave w owns value columns 32w..32w+31
 // as two 16-column MFMA tiles (tile C holds columns 32w + 2c + C, c = lane %
@@ -71,7 +76,7 @@ struct ReplayLayout {
     PX = RLA + (uint32_t)L * 512u;                // f32 [LP][128] q before L2, then X
     PY = PX + (uint32_t)LP * 512u;                // f32 [LP][128] k before L2, then Y
     SP = PY + (uint32_t)LP * 512u;                // f32 [2LP][PS] K~ then Q~; later U [LP][128]
-    SKH = SP + (uint32_t)(2 * LP) * PS * 4u;      // f32 [LP][PS] K^ (rows >= nt zero)
+    SKH = SP + (uint32_t)(2 * LP) * PS * 4u;      // f32 [LP][PS] K^, or Kb with unbounded decay (rows >= nt zero)
     SGAM = SKH + (uint32_t)LP * PS * 4u;          // f32 [128] D_last
     SSC = SGAM + 512u;                            // f32 [LP][4] 1/|q|, 1/|k|, -, beta
     SSS = SSC + (uint32_t)LP * 16u;               // f32 [2][LP] sums of squares of o
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
         }
         sP[(LP + t) * PS + j] = qt;
       }
-    } else {
+    } else if (!p.unbounded) {
 #pragma unroll
       for (int t = 0; t < LP; ++t) {
         float kt = 0.f, kh = 0.f;
@@ -285,6 +290,47 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
         sKh[t * PS + j] = kh;
       }
       sGam[j] = Dt;  // D_last: the decay over all tokens run
+    } else {
+      // unbounded decay: K~ = D k, and Kb (not K^) from suffix sums of log alpha
+#pragma unroll
+      for (int t = 0; t < LP; ++t) {
+        float kt = 0.f;
+        if (t < nt) {
+          Dt *= exp2_fast(sLA[t * D + j] * LOG2E);
+          kt = sY[t * D + j] * ((cq || ck) ? sSC[4 * t + 1] : 1.f) * Dt;
+        }
+        sP[t * PS + j] = kt;
+      }
+      sGam[j] = Dt;
+      float suf = 0.f;  // sum of log alpha over the tokens after t
+#pragma unroll
+      for (int t = LP - 1; t >= 0; --t) {
+        float kb = 0.f;
+        if (t < nt) {
+          kb = sY[t * D + j] * ((cq || ck) ? sSC[4 * t + 1] : 1.f) * exp2_fast(suf * LOG2E);
+          suf += sLA[t * D + j];
+        }
+        sKh[t * PS + j] = kb;
+      }
+    }
+  }
+  if (p.unbounded) {
+    // pairwise Gram entries: waves 0-1 (q channels) form the Q~ rows, waves
+    // 2-3 (k channels) the K~ rows; each wave's 64-channel partial sums go to
+    // its own block of the partial-Gram array, the other rows zero
+    float* mine = sGP + wv * 2 * LP * 16;
+    for (int i = lane; i < 2 * LP * 16; i += 64) mine[i] = 0.f;
+    for (int s = 0; s < nt; ++s) {
+      const float ks = sY[s * D + j] * ((cq || ck) ? sSC[4 * s + 1] : 1.f);
+      float cum = 0.f;  // sum of log alpha over tokens s+1 .. t
+      for (int t = s; t < nt; ++t) {
+        if (t > s) cum += sLA[t * D + j];
+        const float xt = isk ? sY[t * D + j] * ((cq || ck) ? sSC[4 * t + 1] : 1.f)
+                             : sX[t * D + j] * ((cq || ck) ? sSC[4 * t] : 1.f);
+        const float v = xt * ks * exp2_fast(cum * LOG2E);
+        const float sum = wave_sum(v);
+        if (lane == 0) mine[((isk ? 0 : LP) + t) * 16 + s] = sum;
+      }
     }
   }
   __syncthreads();
@@ -307,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
 #pragma unroll
         for (int R = 0; R < NR; ++R) acc[R][C] = mma16(acc[R][C], a[R], b);
       }
-      if ((T >> 1) == wv) {  // this wave's quarter of the Gram contraction
+      if (!p.unbounded && (T >> 1) == wv) {  // this wave's quarter of the Gram contraction
         Frag16<float> b;
         b.v = (f32x4){0.f, 0.f, 0.f, 0.f};
         if (c16 < LP) b.v = *reinterpret_cast<const f32x4*>(sKh + c16 * PS + 16 * T + 4 * g4);
@@ -323,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
         const int row = 16 * R + 4 * g4 + e;
         float* dst = row < LP ? sX + row * D : sY + (row - LP) * D;
         *reinterpret_cast<f32x2*>(dst + col0) = (f32x2){acc[R][0][e], acc[R][1][e]};
-        sGP[(wv * 2 * LP + row) * 16 + c16] = gacc[R][e];
+        if (!p.unbounded) sGP[(wv * 2 * LP + row) * 16 + c16] = gacc[R][e];
       }
   }
   __syncthreads();
@@ -391,7 +437,8 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
 
   // ---- 4. commit: S = Diag(D_last) S0 + Kb^T U ----
   // The contraction runs over the LP block rows, four per instruction: lane
-  // group g4 carries rows g4 + 4 jj.  Kb^T[i][t] = K^[t][i] D_last[i].
+  // group g4 carries rows g4 + 4 jj.  Kb^T[i][t] = K^[t][i] D_last[i] (with
+  // unbounded decay the array already holds Kb).
   if (commit) {
     constexpr int NJ = LP / 4;
     float bu[2][NJ];
@@ -408,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
       const float gi = sGam[16 * T + c16];
       float a[NJ];
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) a[jj] = sKh[(g4 + 4 * jj) * PS + 16 * T + c16] * gi;
+      for (int jj = 0; jj < NJ; ++jj) a[jj] = sKh[(g4 + 4 * jj) * PS + 16 * T + c16] * (p.unbounded ? 1.f : gi);
 #pragma unroll
       for (int C = 0; C < 2; ++C) {
         f32x4 acc = gam * st[T][C];

@@ -33,9 +33,10 @@
  *   - Preconditions that the fast path does not check (KDA_DEBUG_CHECKS
  *     below checks them on request): log_alpha in
  *     [-5, 0] (the lower-bounded decay of "Kimi K3 架构…" section 4.2.5,
- *     gate_lower_bound = -5 of section 2.1) for kda_chunk_fwd and
- *     kda_decode_replay, or any value <= 0 (-inf included, NaN not) for
- *     kda_decode_step and for kda_chunk_fwd with unbounded_decay set;
+ *     gate_lower_bound = -5 of section 2.1) for kda_chunk_fwd,
+ *     kda_chunk_bwd and kda_decode_replay, or any value <= 0 (-inf included,
+ *     NaN not) for kda_decode_step and for kda_chunk_fwd and
+ *     kda_decode_replay with unbounded_decay set;
  *     beta in [0, 1]; ||q||, ||k||
  *     about 1 per head when no prologue runs; cu_seqlens non-decreasing from
  *     0 to total_tokens.  Outside them the results are undefined (they may
@@ -114,8 +115,11 @@ typedef enum KDA_ENUM_BASE {
  *       section 4.2.5); the diagonal 16-token tiles are then formed position
  *       pair by position pair (e^{g_i - g_j} as a running product of the
  *       alphas between the two tokens, never above 1), which is slower.
- *       kda_decode_replay returns KDA_ERR_UNSUPPORTED when it is set;
- *       kda_decode_step needs no flag (it accepts any log_alpha <= 0).
+ *       kda_decode_replay takes the same flag: its block of cached tokens then
+ *       forms every pair's decay product from the log_alpha sums between the
+ *       two tokens instead of dividing by the cumulative decay.
+ *       kda_decode_step needs no flag (it accepts any log_alpha <= 0);
+ *       kda_chunk_bwd does not take it.
  *   segment_tokens  scheduling of long sequences when there are too few
  *       (sequence, head) pairs to occupy the GPU: 0 lets the library decide
  *       (it segments only when the sequential schedule would leave more than
@@ -322,7 +326,9 @@ kda_status kda_decode_step(float* state, const void* q, const void* k, const voi
  *   max_tokens    1 .. 16 (larger values are KDA_ERR_UNSUPPORTED).
  *   opts          NULL or the fused options of kda_chunk_fwd: conv_q_w /
  *                 conv_k_w, gate ([N, max_tokens, H, 128] dtype logits),
- *                 norm_w, l2_eps, rms_eps; segment_tokens is ignored.
+ *                 norm_w, l2_eps, rms_eps, unbounded_decay (any log_alpha <= 0,
+ *                 -inf included); segment_tokens and factor_budget_mib are
+ *                 ignored.
  *   conv_q_state, conv_k_state
  *                 [N, 3, H, 128] dtype: the raw q (k) rows of the three
  *                 positions before token 0, oldest first (zeros at a

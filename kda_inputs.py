@@ -201,9 +201,12 @@ def accepted_counts(seed: int, n: int, L: int) -> list:
     return [int(x) for x in rng.integers(1, L + 1, size=n)]
 
 
-def make_replay(N, H, L, dtype="bf16", s0_std=0.02, fused=True, device="cpu", seed=SEED_BASE):
+def make_replay(N, H, L, dtype="bf16", s0_std=0.02, fused=True, device="cpu", seed=SEED_BASE, decay="bounded"):
     """Cached draft-token inputs [N, L, H, 128] plus the verified state, the
-    convolution histories and the per-sequence counts of tokens to commit."""
+    convolution histories and the per-sequence counts of tokens to commit.
+    decay: "bounded" (-5 sigmoid) or "softplus" (unbounded, as make_prefill)."""
+    if decay not in ("bounded", "softplus"):
+        raise ValueError("decay must be 'bounded' or 'softplus'")
     dt = torch_dtype(dtype)
     g = _gen(device, seed)
     out = {"N": N, "H": H, "L": L, "dtype": dtype, "fused": fused}
@@ -215,9 +218,15 @@ def make_replay(N, H, L, dtype="bf16", s0_std=0.02, fused=True, device="cpu", se
     _fill_unit(q, g, device, not fused, 16384)
     _fill_unit(k, g, device, not fused, 16384)
     _fill_unit(v, g, device, False, 16384)
-    la = -5.0 * torch.sigmoid(_randn((N, L, H, D), g, device))
+    z = _randn((N, L, H, D), g, device)
+    if decay == "softplus":
+        rate = torch.pow(16.0, torch.rand((H, 1), generator=_gen(device, seed + 0x5F0), device=device))
+        la = -rate * torch.nn.functional.softplus(z)
+    else:
+        la = -5.0 * torch.sigmoid(z)
     beta = torch.sigmoid(_randn((N, L, H), g, device))
-    out.update(q=q.view(N, L, H, D), k=k.view(N, L, H, D), v=v.view(N, L, H, D), log_alpha=la, beta=beta)
+    out.update(q=q.view(N, L, H, D), k=k.view(N, L, H, D), v=v.view(N, L, H, D), log_alpha=la, beta=beta,
+               decay=decay)
     if fused:
         out["conv_q_w"] = 0.5 * _randn((H * D, 4), g, device)
         out["conv_k_w"] = 0.5 * _randn((H * D, 4), g, device)

@@ -350,7 +350,8 @@ def test_replay_validation(lib):
     neg = Opts(None, None, None, None, 1e-6, -1.0, 0)
     assert replay(lib, opts=opts_p(neg)) == INVALID          # negative epsilon
     unb = Opts(None, None, None, None, 1e-6, 1e-6, 0, 1)
-    assert replay(lib, opts=opts_p(unb)) == UNSUPPORTED      # the block form needs the decay bound
+    assert replay(lib, opts=opts_p(unb), L=17) == UNSUPPORTED  # the flag is accepted; sizes still checked
+    assert replay(lib, opts=opts_p(unb), o=p(3)) == INVALID
     # nothing to produce: accepted without launching anything
     assert replay(lib, s1=None, o=None) == OK
 

@@ -48,7 +48,8 @@ def run_lib(inp, num_tokens, commit, in_place=False):
     o, s_out = kda.decode_replay(s_in, inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], num_tokens,
                                  state_out=state_out, conv_q_w=inp.get("conv_q_w"),
                                  conv_k_w=inp.get("conv_k_w"), conv_q_state=hq, conv_k_state=hk,
-                                 gate=inp.get("gate"), norm_w=inp.get("norm_w"), out=o)
+                                 gate=inp.get("gate"), norm_w=inp.get("norm_w"), out=o,
+                                 unbounded_decay=inp.get("decay") == "softplus")
     sync()
     return o, s_out, s_in, hq, hk
 
@@ -272,4 +273,52 @@ def test_replay_no_decay_and_beta_extremes(dtype):
     counts = [8, 5, 1]
     nt = torch.tensor(counts, dtype=torch.int32, device=DEV)
     res = run_lib(r, nt, True)
+    compare(r, counts, res, run_oracle(r, counts), True, dtype)
+
+
+UNB_CASES = [
+    # (name, dtype, fused, L, N, H, counts, s0_std)
+    ("f32_L8_fused_ragged", "f32", True, 8, 4, 3, [8, 3, 0, 5], 0.5),
+    ("bf16_L8_fused_ragged", "bf16", True, 8, 5, 4, [8, 1, 2, 0, 6], 0.02),
+    ("bf16_L16_plain", "bf16", False, 16, 3, 2, [16, 7, 13], 0.3),
+    ("f32_L16_plain_all", "f32", False, 16, 2, 2, None, 0.5),
+]
+
+
+@pytest.mark.parametrize("case", UNB_CASES, ids=[c[0] for c in UNB_CASES])
+@pytest.mark.parametrize("mode", ["verify", "commit_in_place"])
+def test_replay_unbounded_decay(case, mode):
+    """Kimi Linear's unbounded negative-softplus decay ("Kimi K3 架构…"
+    section 4.2.5): log_alpha = -a_h softplus(z) with per-head rates up to 16,
+    far past the bounded block's range; the pairwise decay products keep every
+    factor <= 1."""
+    name, dtype, fused, L, N, H, counts, s0 = case
+    say("case replay unbounded %s %s" % (name, mode))
+    inp = kda_inputs.make_replay(N, H, L, dtype, s0, fused, DEV, seed=131 + len(name), decay="softplus")
+    say("  log_alpha min %.1f, 16-token sum min %.1f" % (float(inp["log_alpha"].min()),
+                                                        float(inp["log_alpha"].sum(dim=1).min())))
+    nt = None if counts is None else torch.tensor(counts, dtype=torch.int32, device=DEV)
+    commit = mode != "verify"
+    res = run_lib(inp, nt, commit, in_place=(mode == "commit_in_place"))
+    assert torch.isfinite(res[0].float()[~torch.isnan(res[0].float())]).all()
+    ref = run_oracle(inp, counts)
+    compare(inp, counts, res, ref, commit, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_replay_unbounded_extremes(dtype):
+    """Unbounded decay with log_alpha = -20 on every channel (the bounded
+    block's 1/D would be e^320), then single channels at -1e4 and -inf (the
+    channel forgets everything) beside tokens with no decay at all."""
+    say("case replay unbounded extremes %s" % dtype)
+    r = kda_inputs.make_replay(3, 2, 16, dtype, 0.5, True, DEV, seed=141, decay="softplus")
+    r["log_alpha"].fill_(-20.0)
+    r["log_alpha"][1, 3:6] = 0.0
+    r["log_alpha"][1, 4, :, 7] = -1e4
+    r["log_alpha"][2, 2, :, 0:5] = float("-inf")
+    r["log_alpha"][2, 9:12] = 0.0
+    counts = [16, 12, 16]
+    nt = torch.tensor(counts, dtype=torch.int32, device=DEV)
+    res = run_lib(r, nt, True)
+    assert torch.isfinite(res[1]).all()
     compare(r, counts, res, run_oracle(r, counts), True, dtype)
