@@ -101,28 +101,39 @@ def replay_algorithmic_bytes(N: int, H: int, L: int, counts, es: int, commit: bo
     return N * H * (2 * d * d * 4 + 2 * hist) + H * int(sum(counts)) * tok_in
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch recorded in profiles/hbm_traffic.json (rocprofv3
-    FETCH_SIZE / WRITE_SIZE, copy-calibrated; for kda_chunk_fwd the sum over
-    its kernels), or None when the kernel's sources have changed since the
-    counters were taken."""
+TRAFFIC_SOURCES = {
+    "kda_chunk_fwd": ["kda_chunk.hip", "kda_prep.hip", "kda_scan.hip", "kda_chunk_util.h", "kda_device.h",
+                      "kda_internal.h", "kda_api.hip"],
+    "kda_chunk_bwd": ["kda_bwd.hip", "kda_chunk.hip", "kda_prep.hip", "kda_chunk_util.h", "kda_device.h",
+                      "kda_internal.h", "kda_api.hip"],
+    "decode_kernel": ["kda_decode.hip", "kda_device.h", "kda_internal.h"],
+    "replay_verify": ["kda_replay.hip", "kda_chunk_util.h", "kda_device.h", "kda_internal.h"],
+    "replay_commit": ["kda_replay.hip", "kda_chunk_util.h", "kda_device.h", "kda_internal.h"],
+}
+
+
+def source_hash(kernel: str) -> str:
+    """First 16 hex digits of the sha256 over the sources a measured call runs."""
     import hashlib
+    m = hashlib.sha256()
+    for f in TRAFFIC_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "gated_delta_rule_25_amd", "csrc", f), "rb") as fh:
+            m.update(fh.read())
+    return m.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per call recorded in profiles/hbm_traffic.json (rocprofv3
+    FETCH_SIZE / WRITE_SIZE, copy-calibrated, summed over the call's
+    kernels) for this call and workload, or None when there is no record or
+    the sources have changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get(kernel)
-    if rec is None or rec.get("workload") != workload:
+    rec = json.load(open(path)).get("records", {}).get(kernel + "@" + workload)
+    if rec is None:
         return None
-    chunk_src = ["kda_chunk.hip", "kda_prep.hip", "kda_chunk_util.h", "kda_device.h", "kda_internal.h", "kda_api.hip"]
-    src = {"kda_chunk_fwd": chunk_src, "kda_chunk_fwd_unbounded": chunk_src,
-           "decode_kernel": ["kda_decode.hip", "kda_device.h", "kda_internal.h"],
-           "replay_verify": ["kda_replay.hip", "kda_chunk_util.h", "kda_device.h", "kda_internal.h"],
-           "replay_commit": ["kda_replay.hip", "kda_chunk_util.h", "kda_device.h", "kda_internal.h"]}[kernel]
-    m = hashlib.sha256()
-    for f in src:
-        with open(os.path.join(ROOT, "gated_delta_rule_25_amd", "csrc", f), "rb") as fh:
-            m.update(fh.read())
-    return rec["bytes"] if m.hexdigest()[:16] == rec["source_sha256_16"] else None
+    return rec["bytes"] if rec.get("source_sha256_16") == source_hash(kernel) else None
 
 
 def time_events(fn, steps, stream):
@@ -240,8 +251,7 @@ def time_prefill(kda, kda_inputs, wid, steps, warmup, dev, stream, inp=None, **c
                    "decay": ("unbounded negative softplus: per-position diagonal tiles" if unbounded
                              else "bounded [-5, 0]: dense tiles")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic("kda_chunk_fwd_unbounded" if unbounded else "kda_chunk_fwd",
-                                                                w["name"]),
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic("kda_chunk_fwd", w["name"]),
                      "kernel": "kda_chunk_fwd = window_table_kernel + prep_kernel + carry_kernel",
                      "kernel_ms_avg": ms_avg, "algorithmic_bytes": algo},
         "mfma": {"algorithmic_flops": flops, "chunk": C, "achieved_tflops": tflops, "peak_tflops": mfma_peak,
@@ -439,7 +449,8 @@ def time_backward(kda, kda_inputs, steps, dev, stream):
     res = {"workload": w["name"], "dtype": w["dtype"], "steps": steps, "ms_per_call": ms, "ms_min": min(per),
            "tokens_per_s": T * 1e3 / ms, "finite": finite,
            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                        "frac": ach / HBM_PEAK_GBPS, "algorithmic_bytes": b, "traffic": None,
+                        "frac": ach / HBM_PEAK_GBPS, "algorithmic_bytes": b,
+                        "traffic": measured_traffic("kda_chunk_bwd", w["name"]),
                         "kernel": "kda_chunk_bwd = worklist/window table + prep_kernel + carry_kernel (states "
                                   "pass) + bwd_prep_kernel + bwd_carry_kernel + bwd_grad_kernel",
                         "kernel_ms_avg": ms},
