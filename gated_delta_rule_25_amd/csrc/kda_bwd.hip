@@ -393,8 +393,8 @@ __global__ __launch_bounds__(320) void bwd_carry_kernel(const BwdArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_grad_kernel: one workgroup of four waves per (slot, head).  Wave w owns
-// key tiles 2w and 2w + 1 (32 key channels) of every per-token gradient;
+// bwd_grad_kernel: one workgroup of NW waves per (slot, head).  Wave w owns
+// key tiles (8 / NW) w .. (8 / NW)(w + 1) - 1 of every per-token gradient;
 // C x C quantities live in LDS.  All products run in fp32 on the matrix cores
 // (four v_mfma_f32_16x16x4_f32 per 16-deep step).
 // ---------------------------------------------------------------------------
@@ -421,9 +421,12 @@ struct GradLayout {
   static constexpr size_t BYTES = DG + (size_t)D * 4;
 };
 
-template <typename E, int C>
-__global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
+template <typename E, int C, int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
   using L = GradLayout<E, C>;
+  constexpr int NTH = 64 * NW;      // threads
+  constexpr int KPW = 8 / NW;       // 16-key tiles per wave
+  static_assert(KPW * NW == 8, "the waves cover the 8 key tiles");
   constexpr int NT = C / 16, PK = L::PK, PC = L::PC, JB = L::JB, PJ = L::PJ;
   static_assert(L::BYTES <= 160 * 1024, "LDS budget exceeded");
   extern __shared__ __align__(16) unsigned char smem[];
@@ -454,7 +457,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
   {
     const E* gk = static_cast<const E*>(p.k);
     const E* gq = static_cast<const E*>(p.q);
-    for (int i = tid; i < C * (D / PER); i += 256) {
+    for (int i = tid; i < C * (D / PER); i += NTH) {
       const int t = i / (D / PER), c = (i % (D / PER)) * PER;
       u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
       if (t < nv) {
@@ -469,12 +472,13 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
     // the first half's total
     {
       constexpr int HC = C / 2;
-      const int c = tid & (D - 1), half = tid >> 7;
+      const bool act = tid < 2 * D;
+      const int c = tid & (D - 1), half = (tid >> 7) & 1;
       float x[HC];
 #pragma unroll
       for (int u = 0; u < HC; ++u) {
         const int t = half * HC + u;
-        x[u] = t < nv ? p.log_alpha[(t0 + t) * rs + hoff + c] : 0.f;
+        x[u] = (act && t < nv) ? p.log_alpha[(t0 + t) * rs + hoff + c] : 0.f;
       }
       float run = 0.f;
 #pragma unroll
@@ -482,12 +486,12 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
         run += x[u];
         x[u] = run;
       }
-      if (half == 0) {
+      if (act && half == 0) {
 #pragma unroll
         for (int u = 0; u < HC; ++u) sG[u * PK + c] = x[u];
       }
       __syncthreads();
-      if (half == 1) {
+      if (act && half == 1) {
         const float base = sG[(HC - 1) * PK + c];
 #pragma unroll
         for (int u = 0; u < HC; ++u) sG[(HC + u) * PK + c] = base + x[u];
@@ -497,7 +501,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
       sBeta[tid] = tid < nv ? p.beta[(t0 + tid) * H + h] : 0.f;
       sDbeta[tid] = 0.f;
     }
-    for (int i = tid; i < C * PC; i += 256) {
+    for (int i = tid; i < C * PC; i += NTH) {
       sM[i] = 0.f;
       sDP[i] = 0.f;
       sUN[i] = 0.f;  // A (strictly lower part written below)
@@ -538,7 +542,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
 
   // ---- A = strictly-lower(Diag(beta) B) into the union area ----
   float* sA = sUN;
-  for (int idx = wv; idx < NLT; idx += 4) {
+  for (int idx = wv; idx < NLT; idx += NW) {
     int a, b;
     lower_tile(idx, a, b);
     const f32x4 acc = gram_tile(a, b);
@@ -598,13 +602,15 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
   E* sU = sDO + C * PJ;
   E* sDU = sDO + 2 * C * PJ;
   E* sV = sDO + 3 * C * PJ;
-  f32x4 rQs[NT][2], rW[NT][2], rKb[NT][2];
-  float gpart[2] = {0.f, 0.f};
+  f32x4 rQs[NT][KPW], rW[NT][KPW], rKb[NT][KPW];
+  float gpart[KPW];
+#pragma unroll
+  for (int c = 0; c < KPW; ++c) gpart[c] = 0.f;
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) rQs[rt][c] = rW[rt][c] = rKb[rt][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  constexpr int MAXLT = (NLT + 3) / 4;  // lower tiles per wave
+    for (int c = 0; c < KPW; ++c) rQs[rt][c] = rW[rt][c] = rKb[rt][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  constexpr int MAXLT = (NLT + NW - 1) / NW;  // lower tiles per wave
   f32x4 rdP[MAXLT], rdT[MAXLT];
 #pragma unroll
   for (int x = 0; x < MAXLT; ++x) rdP[x] = rdT[x] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -614,7 +620,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
   __syncthreads();  // A (in the union area) is no longer read
   for (int j0 = 0; j0 < D; j0 += JB) {
     // dO and V (16-byte pieces of E), U and dU (fp32, four at a time, rounded to E)
-    for (int i = tid; i < C * (JB / PER); i += 256) {
+    for (int i = tid; i < C * (JB / PER); i += NTH) {
       const int t = i / (JB / PER), c = (i % (JB / PER)) * PER;
       u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
       if (t < nv) {
@@ -624,7 +630,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
       *reinterpret_cast<u32x4*>(sDO + t * PJ + c) = a;
       *reinterpret_cast<u32x4*>(sV + t * PJ + c) = b;
     }
-    for (int i = tid; i < C * (JB / 4); i += 256) {
+    for (int i = tid; i < C * (JB / 4); i += NTH) {
       const int t = i / (JB / 4), c = (i % (JB / 4)) * 4;
       f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
       if (t < nv) {
@@ -640,8 +646,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
     __syncthreads();
     // dQt += dO S^T, (dU S^T), dKb += U dS'^T, dgamma partials: own key tiles
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int i = 16 * (2 * wv + c) + l16;
+    for (int c = 0; c < KPW; ++c) {
+      const int i = 16 * (KPW * wv + c) + l16;
 #pragma unroll
       for (int js = 0; js < JB / 16; ++js) {
         const f32x4 xs = *reinterpret_cast<const f32x4*>(gS + (size_t)i * D + j0 + 16 * js + 4 * g);
@@ -666,7 +672,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
     // dP += dO U^T and dT += dU V^T on this wave's lower tiles
 #pragma unroll
     for (int x = 0; x < MAXLT; ++x) {
-      const int idx = wv + 4 * x;
+      const int idx = wv + NW * x;
       if (idx < NLT) {
         int a, b;
         lower_tile(idx, a, b);
@@ -686,7 +692,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
     }
     // dV = T^T dU for these columns: tile (token tile st, column tile jt);
     // T[t][s] = M[t][s] beta_s is zero for t < s
-    for (int ti = wv; ti < NT * (JB / 16); ti += 4) {
+    for (int ti = wv; ti < NT * (JB / 16); ti += NW) {
       const int st = ti / (JB / 16), jt = ti % (JB / 16);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int kb = st; kb < NT; ++kb) {
@@ -708,9 +714,9 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
     __syncthreads();
   }
   // dgamma for this wave's keys (lane l16 of each key tile)
-  float dgam[2];
+  float dgam[KPW];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < KPW; ++c) {
     float v = gpart[c];
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
@@ -722,12 +728,12 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < KPW; ++c)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sDW[(16 * rt + 4 * g + e) * PK + 16 * (2 * wv + c) + l16] = -rW[rt][c][e];
+      for (int e = 0; e < 4; ++e) sDW[(16 * rt + 4 * g + e) * PK + 16 * (KPW * wv + c) + l16] = -rW[rt][c][e];
 #pragma unroll
   for (int x = 0; x < MAXLT; ++x) {
-    const int idx = wv + 4 * x;
+    const int idx = wv + NW * x;
     if (idx < NLT) {
       int a, b;
       lower_tile(idx, a, b);
@@ -742,7 +748,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
   // dT += dW Kt^T (Kt = K e^{g}); dbeta_j += sum_r M_rj dT_rj
 #pragma unroll
   for (int x = 0; x < MAXLT; ++x) {
-    const int idx = wv + 4 * x;
+    const int idx = wv + NW * x;
     if (idx < NLT) {
       int a, b;
       lower_tile(idx, a, b);
@@ -765,11 +771,11 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
     }
   }
   // dKt = T^T dW on this wave's keys: rows s, dW from registers (rows t)
-  f32x4 rKt[NT][2];
+  f32x4 rKt[NT][KPW];
 #pragma unroll
   for (int st = 0; st < NT; ++st)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < KPW; ++c) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NT; ++kb) {
@@ -788,11 +794,11 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
   // ---- dA = strictly-lower(-M^T dM M^T), dM = dT Diag(beta) ----
   float* sDM = sUN;            // dM, later dB
   float* sX = sUN + C * PC;    // X = dM M^T
-  for (int i = tid; i < C * PC; i += 256) sDM[i] = 0.f;
+  for (int i = tid; i < C * PC; i += NTH) sDM[i] = 0.f;
   __syncthreads();
 #pragma unroll
   for (int x = 0; x < MAXLT; ++x) {
-    const int idx = wv + 4 * x;
+    const int idx = wv + NW * x;
     if (idx < NLT) {
       int a, b;
       lower_tile(idx, a, b);
@@ -805,7 +811,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
   }
   __syncthreads();
   // X[m][c] = sum_j dM[m][j] M[c][j], j <= c (lower tiles suffice)
-  for (int idx = wv; idx < NLT; idx += 4) {
+  for (int idx = wv; idx < NLT; idx += NW) {
     int a, b;
     lower_tile(idx, a, b);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -824,7 +830,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
   f32x4 rdB[MAXLT];
 #pragma unroll
   for (int x = 0; x < MAXLT; ++x) {
-    const int idx = wv + 4 * x;
+    const int idx = wv + NW * x;
     rdB[x] = (f32x4){0.f, 0.f, 0.f, 0.f};
     if (idx < NLT) {
       int a, b;
@@ -858,7 +864,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
   __syncthreads();  // every wave is past reading dM and X
 #pragma unroll
   for (int x = 0; x < MAXLT; ++x) {
-    const int idx = wv + 4 * x;
+    const int idx = wv + NW * x;
     if (idx < NLT) {
       int a, b;
       lower_tile(idx, a, b);
@@ -869,22 +875,26 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
   __syncthreads();
   const float* sDB = sDM;
 
-  // ---- tile products of dB and dP with the referenced K and Q, own keys ----
-  // row side: YB = dB Kh_a, YP = dP Kh_a over tokens s <= tile a
-  f32x4 rYB[NT][2], rYP[NT][2], rZ[NT][2];
+  // ---- per-token gradients of this wave's keys, one token tile rt at a time:
+  // row side YB = dB Kh_rt, YP = dP Kh_rt over tokens s <= tile rt; column side
+  // Z = dB^T K_rt + dP^T Q_rt over tokens t >= tile rt (both referenced to rho_rt)
+  f32x4 odq[NT][KPW], odk[NT][KPW], odg[NT][KPW];
+  float dGp[KPW];
 #pragma unroll
-  for (int a = 0; a < NT; ++a)
+  for (int c = 0; c < KPW; ++c) dGp[c] = 0.f;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int i = 16 * (2 * wv + c) + l16;
-      f32x4 yb = {0.f, 0.f, 0.f, 0.f}, yp = {0.f, 0.f, 0.f, 0.f};
-      const float r = rho(a, i);
+  for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+    for (int c = 0; c < KPW; ++c) {
+      const int i = 16 * (KPW * wv + c) + l16;
+      const float Gi = Gc(i), r = rho(rt, i);
+      f32x4 yb = {0.f, 0.f, 0.f, 0.f}, yp = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int sb = 0; sb < NT; ++sb) {
-        if (sb > a) continue;
+        if (sb > rt) continue;
         Frag16<float> AB, AP, B;
-        AB.v = *reinterpret_cast<const f32x4*>(sDB + (16 * a + l16) * PC + 16 * sb + 4 * g);
-        AP.v = *reinterpret_cast<const f32x4*>(sDP + (16 * a + l16) * PC + 16 * sb + 4 * g);
+        AB.v = *reinterpret_cast<const f32x4*>(sDB + (16 * rt + l16) * PC + 16 * sb + 4 * g);
+        AP.v = *reinterpret_cast<const f32x4*>(sDP + (16 * rt + l16) * PC + 16 * sb + 4 * g);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int s = 16 * sb + 4 * g + e;
@@ -893,26 +903,15 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
         yb = mma16(yb, AB, B);
         yp = mma16(yp, AP, B);
       }
-      rYB[a][c] = yb;
-      rYP[a][c] = yp;
-    }
-  // column side: Z = dB^T K_b + dP^T Q_b over tokens t >= tile b
-#pragma unroll
-  for (int b = 0; b < NT; ++b)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int i = 16 * (2 * wv + c) + l16;
-      const float r = rho(b, i);
-      f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int tb = 0; tb < NT; ++tb) {
-        if (tb < b) continue;
+        if (tb < rt) continue;
         Frag16<float> AB, AP, BK, BQ;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 16 * tb + 4 * g + e;
-          AB.v[e] = sDB[t * PC + 16 * b + l16];
-          AP.v[e] = sDP[t * PC + 16 * b + l16];
+          AB.v[e] = sDB[t * PC + 16 * rt + l16];
+          AP.v[e] = sDP[t * PC + 16 * rt + l16];
           const float f = __expf(gf(t, i) - r);
           BK.v[e] = kf(t, i) * f;
           BQ.v[e] = qf(t, i) * f;
@@ -920,38 +919,25 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
         z = mma16(z, AB, BK);
         z = mma16(z, AP, BQ);
       }
-      rZ[b][c] = z;
-    }
-
-  // ---- per-token gradients of this wave's keys ----
-  f32x4 odq[NT][2], odk[NT][2], odg[NT][2];
-  float dGp[2] = {0.f, 0.f};
-#pragma unroll
-  for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int i = 16 * (2 * wv + c) + l16;
-      const float Gi = Gc(i), r = rho(rt, i);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * rt + 4 * g + e;
         const float gi = gf(t, i), kv = kf(t, i), qv = qf(t, i);
         const float eg = __expf(gi), eb = __expf(Gi - gi), ra = __expf(gi - r), rb = __expf(r - gi);
         const float dQs = rQs[rt][c][e], dKt = rKt[rt][c][e], dKb = rKb[rt][c][e];
-        const float yb = rYB[rt][c][e], yp = rYP[rt][c][e], z = rZ[rt][c][e];
-        odq[rt][c][e] = dQs * eg + yp * ra;
-        odk[rt][c][e] = dKt * eg + dKb * eb + yb * ra + z * rb;
-        odg[rt][c][e] = dQs * (qv * eg) + dKt * (kv * eg) - dKb * (kv * eb) + (kv * ra) * yb + (qv * ra) * yp -
-                        (kv * rb) * z;
+        odq[rt][c][e] = dQs * eg + yp[e] * ra;
+        odk[rt][c][e] = dKt * eg + dKb * eb + yb[e] * ra + z[e] * rb;
+        odg[rt][c][e] = dQs * (qv * eg) + dKt * (kv * eg) - dKb * (kv * eb) + (kv * ra) * yb[e] +
+                        (qv * ra) * yp[e] - (kv * rb) * z[e];
         dGp[c] += dKb * (kv * eb);
       }
     }
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < KPW; ++c) {
     float v = dGp[c];
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
-    const int i = 16 * (2 * wv + c) + l16;
+    const int i = 16 * (KPW * wv + c) + l16;
     if (g == 0) sDG[i] = v + dgam[c] * __expf(Gc(i));
   }
   __syncthreads();  // k, q and g are no longer read: their LDS takes the outputs
@@ -961,10 +947,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < KPW; ++c)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = 16 * rt + 4 * g + e, i = 16 * (2 * wv + c) + l16;
+        const int t = 16 * rt + 4 * g + e, i = 16 * (KPW * wv + c) + l16;
         oQ[t * PK + i] = from_f32<E>(odq[rt][c][e]);
         oK[t * PK + i] = from_f32<E>(odk[rt][c][e]);
         oG[t * PK + i] = odg[rt][c][e];
@@ -981,12 +967,12 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(const BwdArgs p) {
   __syncthreads();
   E* gdq = static_cast<E*>(p.dq);
   E* gdk = static_cast<E*>(p.dk);
-  for (int i = tid; i < nv * (D / PER); i += 256) {
+  for (int i = tid; i < nv * (D / PER); i += NTH) {
     const int t = i / (D / PER), c = (i % (D / PER)) * PER;
     *reinterpret_cast<u32x4*>(gdq + (t0 + t) * rs + hoff + c) = *reinterpret_cast<const u32x4*>(oQ + t * PK + c);
     *reinterpret_cast<u32x4*>(gdk + (t0 + t) * rs + hoff + c) = *reinterpret_cast<const u32x4*>(oK + t * PK + c);
   }
-  for (int i = tid; i < nv * (D / 4); i += 256) {
+  for (int i = tid; i < nv * (D / 4); i += NTH) {
     const int t = i / (D / 4), c = (i % (D / 4)) * 4;
     *reinterpret_cast<f32x4*>(p.dlog_alpha + (t0 + t) * rs + hoff + c) = *reinterpret_cast<const f32x4*>(oG + t * PK + c);
   }
@@ -1022,8 +1008,10 @@ hipError_t launch_bwd_carry(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_bwd_grad(const BwdArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)((size_t)a.slots * a.num_heads);
-  if (a.bf16) return launch_lds(bwd_grad_kernel<__bf16, 64>, grid, 256, GradLayout<__bf16, 64>::BYTES, a, stream);
-  return launch_lds(bwd_grad_kernel<float, 32>, grid, 256, GradLayout<float, 32>::BYTES, a, stream);
+  constexpr int NW = 8;  // one 16-key tile per wave
+  if (a.bf16)
+    return launch_lds(bwd_grad_kernel<__bf16, 64, NW>, grid, 64 * NW, GradLayout<__bf16, 64>::BYTES, a, stream);
+  return launch_lds(bwd_grad_kernel<float, 32, NW>, grid, 64 * NW, GradLayout<float, 32>::BYTES, a, stream);
 }
 
 }  // namespace kda
