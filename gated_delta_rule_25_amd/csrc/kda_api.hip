@@ -199,7 +199,8 @@ bool segments_ok(const Plan& pl, int num_heads, const kda_fused_opts& f) {
 // (N > 1), the chunk table (seq_first [N+1], seq_c0 [N], seq_c1 [N]), the
 // forward factor blocks and the reverse-carry blocks [slots][H], then per
 // (slot, head) the chunk's incoming state and the gradient at its end
-// ([128][128] fp32 each) and U and dU ([C][128] fp32 each).
+// ([128 x 128] each) and U and dU ([C x 128] each), in the I/O dtype as
+// 16 x 16 tiles.
 struct BwdPlan {
   int64_t slots = 0;
   size_t off_first = 0, off_c0 = 0, off_c1 = 0, off_factors = 0, off_dblocks = 0;
@@ -224,14 +225,15 @@ BwdPlan make_bwd_plan(int num_seqs, int64_t total_tokens, int num_heads, kda_dty
   off += units * kda::factor_block_bytes(bf);
   pl.off_dblocks = off;
   off += units * kda::dcarry_block_bytes(bf);
+  const size_t es = bf ? 2 : 4;
   pl.off_states = off;
-  off += units * kD * kD * sizeof(float);
+  off += units * kD * kD * es;
   pl.off_ds = off;
-  off += units * kD * kD * sizeof(float);
+  off += units * kD * kD * es;
   pl.off_u = off;
-  off += units * (size_t)C * kD * sizeof(float);
+  off += units * (size_t)C * kD * es;
   pl.off_du = off;
-  off += units * (size_t)C * kD * sizeof(float);
+  off += units * (size_t)C * kD * es;
   pl.bytes = off;
   return pl;
 }
@@ -592,8 +594,8 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const floa
   int32_t* seq_c0 = reinterpret_cast<int32_t*>(ws + pl.off_c0);
   int32_t* seq_c1 = reinterpret_cast<int32_t*>(ws + pl.off_c1);
   void* factors = ws + pl.off_factors;
-  float* chunk_states = reinterpret_cast<float*>(ws + pl.off_states);
-  float* chunk_u = reinterpret_cast<float*>(ws + pl.off_u);
+  void* chunk_states = ws + pl.off_states;
+  void* chunk_u = ws + pl.off_u;
   if (num_seqs > 1 && kda::launch_worklist(cu_seqlens, num_seqs, order, stream) != hipSuccess) return KDA_ERR_HIP;
   if (kda::launch_window_table(cu_seqlens, num_seqs, total_tokens, kda::chunk_len(bf16), 1, 0, (int)pl.slots,
                                seq_first, seq_c0, seq_c1, stream) != hipSuccess)
@@ -659,8 +661,8 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const floa
   ba.dblocks = ws + pl.off_dblocks;
   ba.chunk_states = chunk_states;
   ba.chunk_u = chunk_u;
-  ba.chunk_ds = reinterpret_cast<float*>(ws + pl.off_ds);
-  ba.chunk_du = reinterpret_cast<float*>(ws + pl.off_du);
+  ba.chunk_ds = ws + pl.off_ds;
+  ba.chunk_du = ws + pl.off_du;
   ba.dq = dq;
   ba.dk = dk;
   ba.dv = dv;

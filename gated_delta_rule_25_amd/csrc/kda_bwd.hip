@@ -61,38 +61,22 @@ __device__ __forceinline__ int frag_elem(int c, int& grp) {
   return (c & 3) + ((c >> 4) << 2);
 }
 
-// Elements of a forward factor block held in LDS (layout in kda_internal.h).
+// Elements of forward factor-block fragments (layout in kda_internal.h).
+// 16-token-row fragments (-W and Qt): fragment (t / 16) * 4 + i / 32, lane
+// (group, t % 16), element frag_elem(i % 32).
+template <typename E>
+__device__ __forceinline__ float rowfrag_at(const E* f, int t, int i) {
+  int grp;
+  const int e = frag_elem(i & 31, grp);
+  return to_f32(f[(((t >> 4) * 4 + (i >> 5)) * 64 + grp * 16 + (t & 15)) * 8 + e]);
+}
+// Kb[t][i] from the Kb^T fragments split in halves
 template <typename E, int C>
-struct FactorView {
-  using F = FactorBlock<(int)sizeof(E), C>;
-  static constexpr int KT = C / 32;
-  const unsigned char* b;
-  // -W[t][i] (W and Qt: row tile of 16 tokens, 32-deep steps over the keys)
-  __device__ float neg_w(int t, int i) const { return at(F::W, t, i); }
-  __device__ float qt(int t, int i) const { return at(F::Q, t, i); }
-  __device__ float at(uint32_t base, int t, int i) const {
-    int grp;
-    const int e = frag_elem(i & 31, grp);
-    const int idx = (((t >> 4) * 4 + (i >> 5)) * 64 + grp * 16 + (t & 15)) * 8 + e;
-    return to_f32(reinterpret_cast<const E*>(b + base)[idx]);
-  }
-  // P[t][s] (zero above the diagonal; fragments only for 32-token steps that reach t)
-  __device__ float p(int t, int s) const {
-    const int rt = t >> 4, kt = s >> 5;
-    if (kt > rt / 2) return 0.f;
-    int grp;
-    const int e = frag_elem(s & 31, grp);
-    const int idx = (F::p_frag(rt, kt) * 64 + grp * 16 + (t & 15)) * 8 + e;
-    return to_f32(reinterpret_cast<const E*>(b + F::P)[idx]);
-  }
-  // Kb[t][i], stored as Kb^T fragments split in halves
-  __device__ float kb(int t, int i) const {
-    const int c = t & 31;
-    const int idx = (((i >> 4) * KT + (t >> 5)) * 2 + (c >> 4)) * 256 + (((c & 15) >> 2) * 16 + (i & 15)) * 4 + (c & 3);
-    return to_f32(reinterpret_cast<const E*>(b + F::K)[idx]);
-  }
-  __device__ float gamma(int i) const { return reinterpret_cast<const float*>(b + F::G)[i]; }
-};
+__device__ __forceinline__ float kbt_at(const E* f, int t, int i) {
+  constexpr int KT = C / 32;
+  const int c = t & 31;
+  return to_f32(f[(((i >> 4) * KT + (t >> 5)) * 2 + (c >> 4)) * 256 + (((c & 15) >> 2) * 16 + (i & 15)) * 4 + (c & 3)]);
+}
 
 template <typename E>
 __device__ __forceinline__ void store4(E* dst, f32x4 x) {
@@ -102,29 +86,36 @@ __device__ __forceinline__ void store4(E* dst, f32x4 x) {
     *reinterpret_cast<f32x4*>(dst) = x;
 }
 
+// 4 consecutive elements (16-deep operand of one lane) as Frag16
+__device__ __forceinline__ void ld4(Frag16<__bf16>& f, const __bf16* p) { f.v = *reinterpret_cast<const bf16x4*>(p); }
+__device__ __forceinline__ void ld4(Frag16<float>& f, const float* p) { f.v = *reinterpret_cast<const f32x4*>(p); }
+
 // ---------------------------------------------------------------------------
 // bwd_prep_kernel: one workgroup of four waves per (slot, head).  The factor
-// block's Qt and P and the chunk's dO are first transposed once into
-// row-major LDS arrays (contraction index contiguous), so every 16-deep
-// matrix-core step reads its four operand values per lane in one access.
-// The products run in the I/O dtype: Qt, P and dO are values of that dtype
-// already, so with fp32 accumulation nothing is rounded.
+// block's Qt and P fragments and the chunk's dO rows are loaded into registers
+// and scattered straight into row-major transposed LDS arrays (contraction
+// index contiguous), so every 16-deep matrix-core step reads its four operand
+// values per lane in one access.  The -W and Kb^T fragments are loaded at the
+// start as well and staged raw in the same LDS bytes once the products are
+// done, for the gathers into the reverse carry's operand order.  46 KiB of LDS
+// lets three workgroups share a compute unit.  The products run in the I/O
+// dtype: Qt, P and dO are values of that dtype already, so with fp32
+// accumulation nothing is rounded.
 // ---------------------------------------------------------------------------
 template <typename E, int C>
 struct PrepBwdLayout {
   using F = FactorBlock<(int)sizeof(E), C>;
-  static constexpr int PT = C + 8;                          // row pitch (elements) of the transposed arrays
-  static constexpr size_t FB = F::U;                        // the factor block up to U' (not needed)
-  static constexpr size_t QT = FB;                          // E [128][PT]  Qt^T
-  static constexpr size_t PTR = QT + (size_t)D * PT * sizeof(E);   // E [C][PT]  P^T
-  static constexpr size_t DOT = PTR + (size_t)C * PT * sizeof(E);  // E [128][PT] dO^T
+  static constexpr int PT = C + 8;                                  // row pitch (elements) of the transposed arrays
+  static constexpr size_t QT = 0;                                   // E [128][PT]  Qt^T
+  static constexpr size_t PTR = QT + (size_t)D * PT * sizeof(E);    // E [C][PT]  P^T
+  static constexpr size_t DOT = PTR + (size_t)C * PT * sizeof(E);   // E [128][PT] dO^T
   static constexpr size_t BYTES = DOT + (size_t)D * PT * sizeof(E);
-  static_assert(FB % 16 == 0 && QT % 16 == 0 && PTR % 16 == 0 && DOT % 16 == 0, "16-byte pieces");
+  // second phase, over the same bytes: raw -W and Kb^T fragments
+  static constexpr size_t RW = 0;
+  static constexpr size_t RK = RW + (size_t)(C / 16) * 4 * F::FR;
+  static_assert(RK + (size_t)8 * (C / 32) * F::FR <= BYTES, "raw fragments fit the transposed arrays");
+  static_assert(PTR % 16 == 0 && DOT % 16 == 0 && RK % 16 == 0, "16-byte pieces");
 };
-
-// 4 consecutive elements (16-deep operand of one lane) as Frag16
-__device__ __forceinline__ void ld4(Frag16<__bf16>& f, const __bf16* p) { f.v = *reinterpret_cast<const bf16x4*>(p); }
-__device__ __forceinline__ void ld4(Frag16<float>& f, const float* p) { f.v = *reinterpret_cast<const f32x4*>(p); }
 
 template <typename E, int C>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
@@ -133,6 +124,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
   using DB = DCarryBlock<ES, C>;
   using L = PrepBwdLayout<E, C>;
   constexpr int NT = C / 16, KT = C / 32, PT = L::PT;
+  constexpr int PER = 16 / ES;    // elements per 16-byte piece
+  constexpr int LPC = 8 / PER;    // pieces per lane chunk (8 elements of one fragment lane)
+  constexpr int NW = (int)(NT * 4 * F::FR / 16) / 256;  // -W pieces per thread
+  constexpr int NK = (int)(8 * KT * F::FR / 16) / 256;  // Kb^T pieces per thread
+  static_assert(NW * 256 * 16 == (int)(NT * 4 * F::FR) && NK * 256 * 16 == (int)(8 * KT * F::FR), "whole pieces");
   static_assert(L::BYTES <= 160 * 1024, "LDS budget exceeded");
   extern __shared__ __align__(16) unsigned char smem[];
   E* sQT = reinterpret_cast<E*>(smem + L::QT);
@@ -147,12 +143,47 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
   const int64_t t0 = bos + (int64_t)(slot - p.seq_first[n]) * C;
   const int nv = (int)max((int64_t)0, min((int64_t)C, eos - t0));
   const size_t blk = (size_t)slot * H + h;
+  const char* fb = static_cast<const char*>(p.factors) + blk * F::BYTES;
 
+  // -W and Kb^T pieces, held in registers until the second phase
+  u32x4 rw[NW], rk[NK];
+#pragma unroll
+  for (int m = 0; m < NW; ++m) rw[m] = reinterpret_cast<const u32x4*>(fb + F::W)[tid + 256 * m];
+#pragma unroll
+  for (int m = 0; m < NK; ++m) rk[m] = reinterpret_cast<const u32x4*>(fb + F::K)[tid + 256 * m];
+  // one lane chunk: fragment f, lane ln -> 8 elements (row t = 16 (f / 4) + ln % 16,
+  // contraction index 32 (f % 4) + the fragment order)
+  auto load_chunk = [&](uint32_t base, int f, int ln, E (&v)[8]) {
+    u32x4 raw[LPC];
+#pragma unroll
+    for (int q = 0; q < LPC; ++q) raw[q] = reinterpret_cast<const u32x4*>(fb + base)[(f * 64 + ln) * LPC + q];
+    __builtin_memcpy(v, raw, sizeof(raw));
+  };
+  auto frag_col = [](int ks, int grp, int e) { return 32 * ks + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4); };
+  // Qt^T: chunk (f, ln) of the Qt fragments to sQT[key][t]
+  for (int c = tid; c < NT * 4 * 64; c += 256) {
+    const int f = c >> 6, ln = c & 63, rt = f >> 2, ks = f & 3, grp = ln >> 4, t = 16 * rt + (ln & 15);
+    E v[8];
+    load_chunk(F::Q, f, ln, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sQT[frag_col(ks, grp, e) * PT + t] = v[e];
+  }
+  // P^T: fragments (rt, kt) with kt <= rt / 2 are stored (P is zero above the
+  // diagonal); the rest of sPT is zero
+  for (int c = tid; c < NT * KT * 64; c += 256) {
+    const int pr = c >> 6, ln = c & 63, rt = pr / KT, kt = pr % KT, grp = ln >> 4, t = 16 * rt + (ln & 15);
+    E v[8];
+    if (kt <= rt / 2) {
+      load_chunk(F::P, F::p_frag(rt, kt), ln, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = from_f32<E>(0.f);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sPT[frag_col(kt, grp, e) * PT + t] = v[e];
+  }
+  // dO rows (16-byte pieces), transposed into dO^T[j][t]; zero past the end
   {
-    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(p.factors) + blk * F::BYTES);
-    for (int i = tid; i < (int)(L::FB / 16); i += 256) reinterpret_cast<u32x4*>(smem)[i] = src[i];
-    // dO rows (16-byte pieces), transposed into dO^T[j][t]; zero past the end
-    constexpr int PER = 16 / ES;  // elements per piece
     const E* gdo = static_cast<const E*>(p.d_o);
     const int64_t rs = (int64_t)H * D;
     for (int i = tid; i < C * (D / PER); i += 256) {
@@ -163,17 +194,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
 #pragma unroll
       for (int e = 0; e < PER; ++e) sDOT[(j0 + e) * PT + t] = x[e];
     }
-  }
-  __syncthreads();
-  const FactorView<E, C> fv{smem};
-  // Qt^T and P^T, one gather per element
-  for (int i = tid; i < C * D; i += 256) {
-    const int key = i % D, t = i / D;
-    sQT[key * PT + t] = from_f32<E>(fv.qt(t, key));
-  }
-  for (int i = tid; i < C * C; i += 256) {
-    const int s = i % C, t = i / C;
-    sPT[s * PT + t] = from_f32<E>(fv.p(t, s));
   }
   __syncthreads();
   char* dst = static_cast<char*>(p.dblocks) + blk * DB::BYTES;
@@ -205,16 +225,21 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
     }
     store4(dY + ((size_t)ti * 64 + lane) * 4, acc);
   }
+  __syncthreads();  // the transposed arrays are no longer read
+#pragma unroll
+  for (int m = 0; m < NW; ++m) reinterpret_cast<u32x4*>(smem + L::RW)[tid + 256 * m] = rw[m];
+#pragma unroll
+  for (int m = 0; m < NK; ++m) reinterpret_cast<u32x4*>(smem + L::RK)[tid + 256 * m] = rk[m];
+  __syncthreads();
+  const E* sW = reinterpret_cast<const E*>(smem + L::RW);
+  const E* sKbt = reinterpret_cast<const E*>(smem + L::RK);
   // Kb as A-operand fragments over the keys, -W^T as fragments over the tokens
   E* dKB = reinterpret_cast<E*>(dst + DB::KB);
   for (int i = tid; i < NT * 4 * 64; i += 256) {
     const int f = i / 64, ln = i % 64, rt = f / 4, ks = f % 4, r = ln & 15, gg = ln >> 4;
     E vals[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int key = 32 * ks + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4);
-      vals[e] = from_f32<E>(fv.kb(16 * rt + r, key));
-    }
+    for (int e = 0; e < 8; ++e) vals[e] = from_f32<E>(kbt_at<E, C>(sKbt, 16 * rt + r, frag_col(ks, gg, e)));
 #pragma unroll
     for (int e = 0; e < 8; ++e) dKB[((size_t)f * 64 + ln) * 8 + e] = vals[e];
   }
@@ -223,14 +248,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
     const int f = i / 64, ln = i % 64, rt8 = f / KT, kt = f % KT, r = ln & 15, gg = ln >> 4;
     E vals[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int tok = 32 * kt + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4);
-      vals[e] = from_f32<E>(fv.neg_w(tok, 16 * rt8 + r));
-    }
+    for (int e = 0; e < 8; ++e) vals[e] = from_f32<E>(rowfrag_at(sW, frag_col(kt, gg, e), 16 * rt8 + r));
 #pragma unroll
     for (int e = 0; e < 8; ++e) dWT[((size_t)f * 64 + ln) * 8 + e] = vals[e];
   }
-  if (tid < D) reinterpret_cast<float*>(dst + DB::G)[tid] = fv.gamma(tid);
+  if (tid < D) reinterpret_cast<float*>(dst + DB::G)[tid] = reinterpret_cast<const float*>(fb + F::G)[tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -335,12 +357,12 @@ __global__ __launch_bounds__(320) void bwd_carry_kernel(const BwdArgs p) {
 #pragma unroll
     for (int rt8 = 0; rt8 < 8; ++rt8)
       rY[rt8] = buf_ld_raw(rb, (uint32_t)(lane * 4 * ES), DB::Y + (rt8 * 8 + ct) * DB::TILE);
-    // the gradient reaching this chunk's end
-    float* ds_dst = p.chunk_ds + blkid * (size_t)(D * D);
+    // the gradient reaching this chunk's end (16 x 16 tiles, I/O dtype)
+    E* ds_dst = static_cast<E*>(p.chunk_ds) + blkid * (size_t)(D * D);
 #pragma unroll
     for (int rt8 = 0; rt8 < 8; ++rt8)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ds_dst[(size_t)(16 * rt8 + 4 * g + i) * D + col0 + l16] = accD[rt8][i];
+      for (int i = 0; i < 4; ++i) ds_dst[tile16_index(16 * rt8 + 4 * g + i, col0 + l16)] = from_f32<E>(accD[rt8][i]);
     __syncthreads();  // slot k % 3 holds chunk ci
     const unsigned char* buf = smem + (k % L::NBUF) * L::SLOT;
     const E* sKB = reinterpret_cast<const E*>(buf + DB::KB + lane * 8 * ES);
@@ -362,11 +384,11 @@ __global__ __launch_bounds__(320) void bwd_carry_kernel(const BwdArgs p) {
         ld_frag(fa, sKB + (a * 4 + ks) * FRE);
         accU[a] = mma(accU[a], fa, sf[ks]);
       }
-    float* du_dst = p.chunk_du + blkid * (size_t)(C * D);
+    E* du_dst = static_cast<E*>(p.chunk_du) + blkid * (size_t)(C * D);
 #pragma unroll
     for (int a = 0; a < NT; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) du_dst[(size_t)(16 * a + 4 * g + i) * D + col0 + l16] = accU[a][i];
+      for (int i = 0; i < 4; ++i) du_dst[tile16_index(16 * a + 4 * g + i, col0 + l16)] = from_f32<E>(accU[a][i]);
     // dS = Diag(gamma) dS' + Qt^T dO - W^T dU
     Frag<E> uf[KT];
 #pragma unroll
@@ -418,7 +440,8 @@ struct GradLayout {
   static constexpr size_t BETA = UN + UN_BYTES;                      // f32 [C]
   static constexpr size_t DBETA = BETA + (size_t)C * 4;              // f32 [C]
   static constexpr size_t DG = DBETA + (size_t)C * 4;                // f32 [128] dG per key
-  static constexpr size_t BYTES = DG + (size_t)D * 4;
+  static constexpr size_t GRAM = DG + (size_t)D * 4;                 // f32 [C][PC] Gram B (lower tiles)
+  static constexpr size_t BYTES = GRAM + (size_t)C * PC * 4;
 };
 
 template <typename E, int C, int NW>
@@ -439,6 +462,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
   float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
   float* sDbeta = reinterpret_cast<float*>(smem + L::DBETA);
   float* sDG = reinterpret_cast<float*>(smem + L::DG);
+  float* sB = reinterpret_cast<float*>(smem + L::GRAM);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int H = p.num_heads, h = blockIdx.x % H, slot = blockIdx.x / H;
@@ -540,7 +564,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
     b = idx - a * (a + 1) / 2;
   };
 
-  // ---- A = strictly-lower(Diag(beta) B) into the union area ----
+  // ---- A = strictly-lower(Diag(beta) B) into the union area; B kept for dbeta ----
   float* sA = sUN;
   for (int idx = wv; idx < NLT; idx += NW) {
     int a, b;
@@ -549,6 +573,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 16 * a + 4 * g + e, s = 16 * b + l16;
+      sB[t * PC + s] = acc[e];
       if (s < t) sA[t * PC + s] = sBeta[t] * acc[e];
     }
   }
@@ -594,10 +619,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
   }
 
   // ---- products with S and dS' over the value columns, 32 at a time ----
-  const float* gS = p.chunk_states + blk * (size_t)(D * D);
-  const float* gDS = p.chunk_ds + blk * (size_t)(D * D);
-  const float* gU = p.chunk_u + blk * (size_t)(C * D);
-  const float* gDU = p.chunk_du + blk * (size_t)(C * D);
+  const E* gS = static_cast<const E*>(p.chunk_states) + blk * (size_t)(D * D);
+  const E* gDS = static_cast<const E*>(p.chunk_ds) + blk * (size_t)(D * D);
+  const E* gU = static_cast<const E*>(p.chunk_u) + blk * (size_t)(C * D);
+  const E* gDU = static_cast<const E*>(p.chunk_du) + blk * (size_t)(C * D);
   E* sDO = reinterpret_cast<E*>(sUN);
   E* sU = sDO + C * PJ;
   E* sDU = sDO + 2 * C * PJ;
@@ -619,29 +644,21 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
   E* gdv = static_cast<E*>(p.dv);
   __syncthreads();  // A (in the union area) is no longer read
   for (int j0 = 0; j0 < D; j0 += JB) {
-    // dO and V (16-byte pieces of E), U and dU (fp32, four at a time, rounded to E)
+    // dO, V, U and dU in 16-byte pieces of E (U and dU from their 16 x 16
+    // tiles: a piece never crosses a tile row)
     for (int i = tid; i < C * (JB / PER); i += NTH) {
       const int t = i / (JB / PER), c = (i % (JB / PER)) * PER;
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u}, u = {0u, 0u, 0u, 0u}, du = {0u, 0u, 0u, 0u};
       if (t < nv) {
         a = *reinterpret_cast<const u32x4*>(gdo + (t0 + t) * rs + hoff + j0 + c);
         b = *reinterpret_cast<const u32x4*>(gv + (t0 + t) * rs + hoff + j0 + c);
+        u = *reinterpret_cast<const u32x4*>(gU + tile16_index(t, j0 + c));
+        du = *reinterpret_cast<const u32x4*>(gDU + tile16_index(t, j0 + c));
       }
       *reinterpret_cast<u32x4*>(sDO + t * PJ + c) = a;
       *reinterpret_cast<u32x4*>(sV + t * PJ + c) = b;
-    }
-    for (int i = tid; i < C * (JB / 4); i += NTH) {
-      const int t = i / (JB / 4), c = (i % (JB / 4)) * 4;
-      f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-      if (t < nv) {
-        a = *reinterpret_cast<const f32x4*>(gU + (size_t)t * D + j0 + c);
-        b = *reinterpret_cast<const f32x4*>(gDU + (size_t)t * D + j0 + c);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sU[t * PJ + c + e] = from_f32<E>(a[e]);
-        sDU[t * PJ + c + e] = from_f32<E>(b[e]);
-      }
+      *reinterpret_cast<u32x4*>(sU + t * PJ + c) = u;
+      *reinterpret_cast<u32x4*>(sDU + t * PJ + c) = du;
     }
     __syncthreads();
     // dQt += dO S^T, (dU S^T), dKb += U dS'^T, dgamma partials: own key tiles
@@ -650,12 +667,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
       const int i = 16 * (KPW * wv + c) + l16;
 #pragma unroll
       for (int js = 0; js < JB / 16; ++js) {
-        const f32x4 xs = *reinterpret_cast<const f32x4*>(gS + (size_t)i * D + j0 + 16 * js + 4 * g);
-        const f32x4 xd = *reinterpret_cast<const f32x4*>(gDS + (size_t)i * D + j0 + 16 * js + 4 * g);
-        gpart[c] += xs[0] * xd[0] + xs[1] * xd[1] + xs[2] * xd[2] + xs[3] * xd[3];
         Frag16<E> BS, BD;
-        frag16_from_acc(BS, xs);
-        frag16_from_acc(BD, xd);
+        ld4(BS, gS + tile16_index(i, j0 + 16 * js + 4 * g));
+        ld4(BD, gDS + tile16_index(i, j0 + 16 * js + 4 * g));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gpart[c] += (float)BS.v[e] * (float)BD.v[e];
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
           const int off = (16 * rt + l16) * PJ + 16 * js + 4 * g;
@@ -846,13 +862,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
         }
         acc = mma16(acc, A, B);
       }
-      const f32x4 bt = gram_tile(a, b);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * a + 4 * g + e, c = 16 * b + l16;
         const float da = c < r ? -acc[e] : 0.f;
         rdB[x][e] = sBeta[r] * da;
-        float v = da * bt[e];
+        float v = da * sB[r * PC + c];
         v += __shfl_xor(v, 1);
         v += __shfl_xor(v, 2);
         v += __shfl_xor(v, 4);

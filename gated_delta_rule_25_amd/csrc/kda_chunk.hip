@@ -404,19 +404,18 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
     for (int c = 0; c < CT; ++c)
 #pragma unroll
       for (int a = 0; a < NT; ++a) accU[c][a] = raw_f32(rU[c][a]);
-    // states pass: the state entering this chunk, row-major fp32 (rows are
-    // key channels), for the backward pass
-    float* cs_dst = nullptr;
+    // states pass: the state entering this chunk (rows are key channels), in
+    // the I/O dtype as 16 x 16 tiles, for the backward pass
     if constexpr (PASS == 3) {
       const size_t blk = (size_t)(slot0 + ci) * H + h;
-      cs_dst = p.chunk_states + blk * (size_t)(D * D);
+      E* cs_dst = static_cast<E*>(p.chunk_states) + blk * (size_t)(D * D);
 #pragma unroll
       for (int c = 0; c < CT; ++c)
 #pragma unroll
         for (int rt8 = 0; rt8 < 8; ++rt8)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            cs_dst[(size_t)(16 * rt8 + 4 * g + i) * D + col0 + 16 * c + l16] = accS[c][rt8][i];
+            cs_dst[tile16_index(16 * rt8 + 4 * g + i, col0 + 16 * c + l16)] = from_f32<E>(accS[c][rt8][i]);
     }
     __syncthreads();
     if (EPI) load_gate(t0, nv);
@@ -481,15 +480,16 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
           }
     }
     if constexpr (PASS == 3) {
-      // U = U' - W S of this chunk, row-major fp32 [C][128] (rows past the
-      // sequence end are zero)
-      float* u_dst = p.chunk_u + ((size_t)(slot0 + ci) * H + h) * (size_t)(C * D);
+      // U = U' - W S of this chunk, [C x 128] 16 x 16 tiles in the I/O dtype
+      // (rows past the sequence end are zero)
+      E* u_dst = static_cast<E*>(p.chunk_u) + ((size_t)(slot0 + ci) * H + h) * (size_t)(C * D);
 #pragma unroll
       for (int c = 0; c < CT; ++c)
 #pragma unroll
         for (int a = 0; a < NT; ++a)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) u_dst[(size_t)(16 * a + 4 * g + i) * D + col0 + 16 * c + l16] = accU[c][a][i];
+          for (int i = 0; i < 4; ++i)
+            u_dst[tile16_index(16 * a + 4 * g + i, col0 + 16 * c + l16)] = from_f32<E>(accU[c][a][i]);
     }
     Frag<E> uf[CT][KT];
 #pragma unroll

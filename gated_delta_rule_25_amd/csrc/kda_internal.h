@@ -190,11 +190,12 @@ struct CarryArgs {
   // pass 2: one per (segment, head): from pairs[seg][h][0] (which the scan
   //   has overwritten with the segment's incoming state), outputs only.
   // pass 3 (states pass of the backward): as pass 0 without outputs; every
-  //   chunk's incoming state goes to chunk_states [slot][H][128][128] and its
-  //   U = U' - W S to chunk_u [slot][H][C][128], both row-major fp32.
+  //   chunk's incoming state goes to chunk_states [slot][H][128 x 128] and its
+  //   U = U' - W S to chunk_u [slot][H][C x 128], both in the I/O dtype as
+  //   16 x 16 tiles (tile16_index).
   int pass;
-  float* chunk_states;
-  float* chunk_u;
+  void* chunk_states;
+  void* chunk_u;
   const int32_t* seg_list;   // [2 * segments]: sequence, segment index within the window's range
   const int32_t* seg_count;  // device: number of segments
   int seg_chunks;            // chunks per segment
@@ -237,6 +238,13 @@ constexpr size_t dcarry_block_bytes(bool bf16) {
   return bf16 ? DCarryBlock<2, 64>::BYTES : DCarryBlock<4, 32>::BYTES;
 }
 
+// Storage of an [R][128] matrix as row-major 16 x 16 tiles, tiles in row-major
+// order: element (r, j) sits at ((r / 16) * 8 + j / 16) * 256 + (r % 16) * 16 + j % 16,
+// so the 16 values of a tile row are contiguous and a tile is 256 elements.
+__host__ __device__ constexpr size_t tile16_index(int r, int j) {
+  return ((size_t)((r >> 4) * 8 + (j >> 4)) << 8) + (size_t)((r & 15) * 16 + (j & 15));
+}
+
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -255,10 +263,11 @@ struct BwdArgs {
   bool bf16;
   const void* factors;           // forward factor blocks [slot][H]
   void* dblocks;                 // reverse-carry blocks [slot][H]
-  const float* chunk_states;     // [slot][H][128][128]
-  const float* chunk_u;          // [slot][H][C][128]
-  float* chunk_ds;               // [slot][H][128][128]: dS at the chunk's end
-  float* chunk_du;               // [slot][H][C][128]
+  // per-chunk matrices in the I/O dtype, 16 x 16 tiles (tile16_index)
+  const void* chunk_states;      // [slot][H][128 x 128]: S entering the chunk
+  const void* chunk_u;           // [slot][H][C x 128]: U = U' - W S
+  void* chunk_ds;                // [slot][H][128 x 128]: dS at the chunk's end
+  void* chunk_du;                // [slot][H][C x 128]
   void* dq;                      // [T,H,128] dtype
   void* dk;
   void* dv;

@@ -238,10 +238,10 @@ kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, co
  * Bytes of device workspace kda_chunk_bwd needs for these sizes (host-side
  * computation; 0 for invalid sizes).  Every chunk of the input is held at
  * once: per (64-token chunk, head) for bf16 I/O about 70.5 KiB of forward
- * factors, 81 KiB for the reverse carry, and 2 x 64 KiB + 2 x 32 KiB of fp32
- * states, gradients and intermediates (about 343 KiB, i.e. 5.4 KiB per
- * token and head); fp32 I/O uses 32-token chunks (about 342 KiB per chunk,
- * 10.7 KiB per token and head).
+ * factors, 81 KiB for the reverse carry, and 2 x 32 KiB + 2 x 16 KiB of
+ * states, gradients and intermediates held in the I/O dtype (about 247.5 KiB,
+ * i.e. 3.9 KiB per token and head); fp32 I/O uses 32-token chunks (about
+ * 342 KiB per chunk, 10.7 KiB per token and head).
  */
 size_t kda_chunk_bwd_workspace_bytes(int num_seqs, int64_t total_tokens, int num_heads, int d_k, int d_v,
                                      kda_dtype dtype);

@@ -251,13 +251,14 @@ def test_noalloc_limits(lib):
     assert na(N=1, cu=None, H=2, opts=opts_p(Opts(segment_tokens=100))) == INVALID
 
 
-def bwd_ws(N, T, H, C=64, fb=FB_BF16, db=82944):
+def bwd_ws(N, T, H, C=64, fb=FB_BF16, db=82944, es=2):
     """Workspace of kda_chunk_bwd (the layout kda_api.hip documents): order
     (N > 1), chunk table, then per (slot, head) the forward factor block, the
-    reverse-carry block, two 128 x 128 fp32 states and two C x 128 fp32 blocks."""
+    reverse-carry block, two 128 x 128 states and two C x 128 blocks in the
+    I/O dtype (es bytes per element)."""
     slots = T // C + N + 1
     b = (a256(4 * N) if N > 1 else 0) + a256(4 * (N + 1)) + 2 * a256(4 * N)
-    return b + slots * H * (fb + db + 2 * 65536 + 2 * C * 512)
+    return b + slots * H * (fb + db + 2 * 128 * 128 * es + 2 * C * 128 * es)
 
 
 def test_bwd_workspace_bytes(lib):
