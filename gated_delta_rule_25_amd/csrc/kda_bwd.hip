@@ -642,34 +642,58 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
   const E* gdo = static_cast<const E*>(p.d_o);
   const E* gv = static_cast<const E*>(p.v);
   E* gdv = static_cast<E*>(p.dv);
+  // Each 32-column block's dO, V, U and dU (16-byte pieces of E; U and dU
+  // from their 16 x 16 tiles, where a piece never crosses a tile row) and the
+  // wave's S and dS' operands are loaded into registers one block ahead, so
+  // their latency overlaps the previous block's products.
+  constexpr int NSTG = C * (JB / PER);  // staging pieces per array and block
+  static_assert(NSTG <= NTH, "one staging piece per thread");
+  const int st_t = tid / (JB / PER), st_c = (tid % (JB / PER)) * PER;
+  const bool st_ld = tid < NSTG && st_t < nv;
+  u32x4 nA, nB, nU, nDU;
+  Frag16<E> nS[KPW][JB / 16], nD[KPW][JB / 16];
+  auto fetch = [&](int j0) {
+    nA = nB = nU = nDU = (u32x4){0u, 0u, 0u, 0u};
+    if (st_ld) {
+      nA = *reinterpret_cast<const u32x4*>(gdo + (t0 + st_t) * rs + hoff + j0 + st_c);
+      nB = *reinterpret_cast<const u32x4*>(gv + (t0 + st_t) * rs + hoff + j0 + st_c);
+      nU = *reinterpret_cast<const u32x4*>(gU + tile16_index(st_t, j0 + st_c));
+      nDU = *reinterpret_cast<const u32x4*>(gDU + tile16_index(st_t, j0 + st_c));
+    }
+#pragma unroll
+    for (int c = 0; c < KPW; ++c)
+#pragma unroll
+      for (int js = 0; js < JB / 16; ++js) {
+        const int i = 16 * (KPW * wv + c) + l16;
+        ld4(nS[c][js], gS + tile16_index(i, j0 + 16 * js + 4 * g));
+        ld4(nD[c][js], gDS + tile16_index(i, j0 + 16 * js + 4 * g));
+      }
+  };
+  fetch(0);
   __syncthreads();  // A (in the union area) is no longer read
   for (int j0 = 0; j0 < D; j0 += JB) {
-    // dO, V, U and dU in 16-byte pieces of E (U and dU from their 16 x 16
-    // tiles: a piece never crosses a tile row)
-    for (int i = tid; i < C * (JB / PER); i += NTH) {
-      const int t = i / (JB / PER), c = (i % (JB / PER)) * PER;
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u}, u = {0u, 0u, 0u, 0u}, du = {0u, 0u, 0u, 0u};
-      if (t < nv) {
-        a = *reinterpret_cast<const u32x4*>(gdo + (t0 + t) * rs + hoff + j0 + c);
-        b = *reinterpret_cast<const u32x4*>(gv + (t0 + t) * rs + hoff + j0 + c);
-        u = *reinterpret_cast<const u32x4*>(gU + tile16_index(t, j0 + c));
-        du = *reinterpret_cast<const u32x4*>(gDU + tile16_index(t, j0 + c));
-      }
-      *reinterpret_cast<u32x4*>(sDO + t * PJ + c) = a;
-      *reinterpret_cast<u32x4*>(sV + t * PJ + c) = b;
-      *reinterpret_cast<u32x4*>(sU + t * PJ + c) = u;
-      *reinterpret_cast<u32x4*>(sDU + t * PJ + c) = du;
+    if (tid < NSTG) {
+      *reinterpret_cast<u32x4*>(sDO + st_t * PJ + st_c) = nA;
+      *reinterpret_cast<u32x4*>(sV + st_t * PJ + st_c) = nB;
+      *reinterpret_cast<u32x4*>(sU + st_t * PJ + st_c) = nU;
+      *reinterpret_cast<u32x4*>(sDU + st_t * PJ + st_c) = nDU;
     }
+    Frag16<E> cS[KPW][JB / 16], cD[KPW][JB / 16];
+#pragma unroll
+    for (int c = 0; c < KPW; ++c)
+#pragma unroll
+      for (int js = 0; js < JB / 16; ++js) {
+        cS[c][js] = nS[c][js];
+        cD[c][js] = nD[c][js];
+      }
     __syncthreads();
+    if (j0 + JB < D) fetch(j0 + JB);
     // dQt += dO S^T, (dU S^T), dKb += U dS'^T, dgamma partials: own key tiles
 #pragma unroll
     for (int c = 0; c < KPW; ++c) {
-      const int i = 16 * (KPW * wv + c) + l16;
 #pragma unroll
       for (int js = 0; js < JB / 16; ++js) {
-        Frag16<E> BS, BD;
-        ld4(BS, gS + tile16_index(i, j0 + 16 * js + 4 * g));
-        ld4(BD, gDS + tile16_index(i, j0 + 16 * js + 4 * g));
+        const Frag16<E> BS = cS[c][js], BD = cD[c][js];
 #pragma unroll
         for (int e = 0; e < 4; ++e) gpart[c] += (float)BS.v[e] * (float)BD.v[e];
 #pragma unroll
