@@ -477,52 +477,87 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
   const int64_t hoff = (int64_t)h * D;
 
   // ---- inputs: k, q rows, the cumulative log-decay g (zeros past the end) ----
+  // Every load is issued before the first one is used (rows past the end are
+  // read from the last valid row and replaced by zeros), so the phase waits
+  // for one memory round trip.
+  if (nv <= 0) return;
   constexpr int PER = 16 / (int)sizeof(E);  // elements per 16-byte piece
+  constexpr int KQ = C * (D / PER) / NTH;   // pieces of k (and of q) per thread
+  static_assert(KQ * NTH == C * (D / PER), "whole pieces per thread");
+  constexpr int QG = NTH / D;               // token groups of the cumulative sum
+  constexpr int TG = C / QG;                // tokens per group
+  static_assert(QG * D == NTH && TG * QG == C, "cumulative-sum groups");
+  const E* gS = static_cast<const E*>(p.chunk_states) + blk * (size_t)(D * D);
+  const E* gDS = static_cast<const E*>(p.chunk_ds) + blk * (size_t)(D * D);
+  const E* gU = static_cast<const E*>(p.chunk_u) + blk * (size_t)(C * D);
+  const E* gDU = static_cast<const E*>(p.chunk_du) + blk * (size_t)(C * D);
+  const E* gdo = static_cast<const E*>(p.d_o);
+  const E* gv = static_cast<const E*>(p.v);
+  // Each 32-column block's dO, V, U and dU (16-byte pieces of E; U and dU
+  // from their 16 x 16 tiles, where a piece never crosses a tile row) and the
+  // wave's S and dS' operands are loaded into registers one block ahead, so
+  // their latency overlaps the previous block's products.
+  constexpr int NSTG = C * (JB / PER);  // staging pieces per array and block
+  static_assert(NSTG <= NTH, "one staging piece per thread");
+  const int st_t = tid / (JB / PER), st_c = (tid % (JB / PER)) * PER;
+  const bool st_ld = tid < NSTG && st_t < nv;
+  u32x4 nA, nB, nU, nDU;
+  Frag16<E> nS[KPW][JB / 16], nD[KPW][JB / 16];
+  auto fetch = [&](int j0) {
+    nA = nB = nU = nDU = (u32x4){0u, 0u, 0u, 0u};
+    if (st_ld) {
+      nA = *reinterpret_cast<const u32x4*>(gdo + (t0 + st_t) * rs + hoff + j0 + st_c);
+      nB = *reinterpret_cast<const u32x4*>(gv + (t0 + st_t) * rs + hoff + j0 + st_c);
+      nU = *reinterpret_cast<const u32x4*>(gU + tile16_index(st_t, j0 + st_c));
+      nDU = *reinterpret_cast<const u32x4*>(gDU + tile16_index(st_t, j0 + st_c));
+    }
+#pragma unroll
+    for (int c = 0; c < KPW; ++c)
+#pragma unroll
+      for (int js = 0; js < JB / 16; ++js) {
+        const int i = 16 * (KPW * wv + c) + l16;
+        ld4(nS[c][js], gS + tile16_index(i, j0 + 16 * js + 4 * g));
+        ld4(nD[c][js], gDS + tile16_index(i, j0 + 16 * js + 4 * g));
+      }
+  };
   {
     const E* gk = static_cast<const E*>(p.k);
     const E* gq = static_cast<const E*>(p.q);
-    for (int i = tid; i < C * (D / PER); i += NTH) {
-      const int t = i / (D / PER), c = (i % (D / PER)) * PER;
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-      if (t < nv) {
-        a = *reinterpret_cast<const u32x4*>(gk + (t0 + t) * rs + hoff + c);
-        b = *reinterpret_cast<const u32x4*>(gq + (t0 + t) * rs + hoff + c);
-      }
-      *reinterpret_cast<u32x4*>(sK + t * PK + c) = a;
-      *reinterpret_cast<u32x4*>(sQ + t * PK + c) = b;
+    u32x4 ka[KQ], qa[KQ];
+#pragma unroll
+    for (int m = 0; m < KQ; ++m) {
+      const int i = tid + NTH * m, t = i / (D / PER), c = (i % (D / PER)) * PER;
+      const int64_t row = (t0 + min(t, nv - 1)) * rs + hoff + c;
+      ka[m] = *reinterpret_cast<const u32x4*>(gk + row);
+      qa[m] = *reinterpret_cast<const u32x4*>(gq + row);
     }
-    // cumulative log-decay: each half of the threads sums half of the tokens
-    // of one key channel (loads issued together), then the second half adds
-    // the first half's total
-    {
-      constexpr int HC = C / 2;
-      const bool act = tid < 2 * D;
-      const int c = tid & (D - 1), half = (tid >> 7) & 1;
-      float x[HC];
+    const int gc = tid & (D - 1), grp = tid / D;
+    float x[TG];
 #pragma unroll
-      for (int u = 0; u < HC; ++u) {
-        const int t = half * HC + u;
-        x[u] = (act && t < nv) ? p.log_alpha[(t0 + t) * rs + hoff + c] : 0.f;
-      }
-      float run = 0.f;
-#pragma unroll
-      for (int u = 0; u < HC; ++u) {
-        run += x[u];
-        x[u] = run;
-      }
-      if (act && half == 0) {
-#pragma unroll
-        for (int u = 0; u < HC; ++u) sG[u * PK + c] = x[u];
-      }
-      __syncthreads();
-      if (act && half == 1) {
-        const float base = sG[(HC - 1) * PK + c];
-#pragma unroll
-        for (int u = 0; u < HC; ++u) sG[(HC + u) * PK + c] = base + x[u];
-      }
+    for (int u = 0; u < TG; ++u) {
+      const int t = grp * TG + u;
+      x[u] = p.log_alpha[(t0 + min(t, nv - 1)) * rs + hoff + gc];
     }
+    const float bt = p.beta[(t0 + min(tid, nv - 1)) * H + h];
+    fetch(0);  // the first column block of the products with S and dS'
+#pragma unroll
+    for (int m = 0; m < KQ; ++m) {
+      const int i = tid + NTH * m, t = i / (D / PER), c = (i % (D / PER)) * PER;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sK + t * PK + c) = t < nv ? ka[m] : z;
+      *reinterpret_cast<u32x4*>(sQ + t * PK + c) = t < nv ? qa[m] : z;
+    }
+    // cumulative log-decay: each group sums its tokens, then adds the totals
+    // of the groups before it (exchanged through the Gram array, unused yet)
+    float run = 0.f;
+#pragma unroll
+    for (int u = 0; u < TG; ++u) {
+      run += grp * TG + u < nv ? x[u] : 0.f;
+      x[u] = run;
+    }
+    sB[grp * D + gc] = run;
     if (tid < C) {
-      sBeta[tid] = tid < nv ? p.beta[(t0 + tid) * H + h] : 0.f;
+      sBeta[tid] = tid < nv ? bt : 0.f;
       sDbeta[tid] = 0.f;
     }
     for (int i = tid; i < C * PC; i += NTH) {
@@ -530,6 +565,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
       sDP[i] = 0.f;
       sUN[i] = 0.f;  // A (strictly lower part written below)
     }
+    __syncthreads();
+    float off = 0.f;
+    for (int q = 0; q < grp; ++q) off += sB[q * D + gc];
+#pragma unroll
+    for (int u = 0; u < TG; ++u) sG[(grp * TG + u) * PK + gc] = off + x[u];
   }
   __syncthreads();
   auto kf = [&](int t, int i) { return to_f32(sK[t * PK + i]); };
@@ -619,10 +659,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
   }
 
   // ---- products with S and dS' over the value columns, 32 at a time ----
-  const E* gS = static_cast<const E*>(p.chunk_states) + blk * (size_t)(D * D);
-  const E* gDS = static_cast<const E*>(p.chunk_ds) + blk * (size_t)(D * D);
-  const E* gU = static_cast<const E*>(p.chunk_u) + blk * (size_t)(C * D);
-  const E* gDU = static_cast<const E*>(p.chunk_du) + blk * (size_t)(C * D);
   E* sDO = reinterpret_cast<E*>(sUN);
   E* sU = sDO + C * PJ;
   E* sDU = sDO + 2 * C * PJ;
@@ -639,37 +675,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
   f32x4 rdP[MAXLT], rdT[MAXLT];
 #pragma unroll
   for (int x = 0; x < MAXLT; ++x) rdP[x] = rdT[x] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  const E* gdo = static_cast<const E*>(p.d_o);
-  const E* gv = static_cast<const E*>(p.v);
   E* gdv = static_cast<E*>(p.dv);
-  // Each 32-column block's dO, V, U and dU (16-byte pieces of E; U and dU
-  // from their 16 x 16 tiles, where a piece never crosses a tile row) and the
-  // wave's S and dS' operands are loaded into registers one block ahead, so
-  // their latency overlaps the previous block's products.
-  constexpr int NSTG = C * (JB / PER);  // staging pieces per array and block
-  static_assert(NSTG <= NTH, "one staging piece per thread");
-  const int st_t = tid / (JB / PER), st_c = (tid % (JB / PER)) * PER;
-  const bool st_ld = tid < NSTG && st_t < nv;
-  u32x4 nA, nB, nU, nDU;
-  Frag16<E> nS[KPW][JB / 16], nD[KPW][JB / 16];
-  auto fetch = [&](int j0) {
-    nA = nB = nU = nDU = (u32x4){0u, 0u, 0u, 0u};
-    if (st_ld) {
-      nA = *reinterpret_cast<const u32x4*>(gdo + (t0 + st_t) * rs + hoff + j0 + st_c);
-      nB = *reinterpret_cast<const u32x4*>(gv + (t0 + st_t) * rs + hoff + j0 + st_c);
-      nU = *reinterpret_cast<const u32x4*>(gU + tile16_index(st_t, j0 + st_c));
-      nDU = *reinterpret_cast<const u32x4*>(gDU + tile16_index(st_t, j0 + st_c));
-    }
-#pragma unroll
-    for (int c = 0; c < KPW; ++c)
-#pragma unroll
-      for (int js = 0; js < JB / 16; ++js) {
-        const int i = 16 * (KPW * wv + c) + l16;
-        ld4(nS[c][js], gS + tile16_index(i, j0 + 16 * js + 4 * g));
-        ld4(nD[c][js], gDS + tile16_index(i, j0 + 16 * js + 4 * g));
-      }
-  };
-  fetch(0);
   __syncthreads();  // A (in the union area) is no longer read
   for (int j0 = 0; j0 < D; j0 += JB) {
     if (tid < NSTG) {
