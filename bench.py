@@ -136,6 +136,90 @@ def measured_traffic(kernel: str, workload: str):
     return rec["bytes"] if rec.get("source_sha256_16") == source_hash(kernel) else None
 
 
+# Counter passes behind profiles/hbm_traffic.json: one rocprofv3 --pmc run per
+# counter (FETCH_SIZE, WRITE_SIZE) and call, written to <dir>/<name>_<counter>/
+# with `-o run --output-format csv`, each a bench.py run with --copy-calibration
+# and the arguments below.  `calls` is the number of library calls that run
+# makes (warm-up + timed + wall-clock steps for the prefill; warm-up + timed
+# calls or rounds otherwise).
+TRAFFIC_PASSES = {
+    "prefill1": (["--only-prefill", "--workload", "1", "--steps", "2", "--warmup", "1"], 5),
+    "prefill2": (["--only-prefill", "--workload", "2", "--steps", "2", "--warmup", "1"], 5),
+    "prefill4": (["--only-prefill", "--workload", "4", "--steps", "2", "--warmup", "1"], 5),
+    "prefill5": (["--only-prefill", "--workload", "5", "--steps", "2", "--warmup", "1"], 5),
+    "prefill7": (["--only-prefill", "--workload", "7", "--steps", "2", "--warmup", "1"], 5),
+    "decode": (["--only-decode", "--decode-steps", "4"], 8),
+    "replay": (["--only-replay", "--replay-rounds", "2"], 4),
+    "backward": (["--only-backward", "--backward-steps", "1"], 2),
+}
+
+
+def record_traffic(directory: str) -> None:
+    """Write profiles/hbm_traffic.json from the counter passes in `directory`
+    (see TRAFFIC_PASSES): per call, the library kernels' FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) summed and divided by the calls, each scaled
+    by what the same counter reads for the run's 1 GiB device-to-device copy."""
+    import csv
+    one_gib = 1 << 30
+
+    def load(name, ctr):
+        path = os.path.join(directory, "%s_%s" % (name, ctr), "run_counter_collection.csv")
+        rows = [(int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]))
+                for r in csv.DictReader(open(path)) if r["Counter_Name"] == ctr]
+        return sorted(rows)
+
+    def calib(rows):
+        return [v for _, k, v in rows if "copyBuffer" in k][0]
+
+    def lib_rows(rows):
+        return [x for x in rows if "kda" in x[1] and "copyBuffer" not in x[1]]
+
+    out = {"_about": ("HBM bytes per call from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each "
+                      "scaled by the factor a plain 1 GiB device-to-device copy reads on the same counter in the "
+                      "same run, summed over the library kernels of a call and divided by the number of calls. "
+                      "Valid only for the sources whose hash is recorded (bench.source_hash). Written by "
+                      "`python3 bench.py --record-traffic DIR` from the passes bench.TRAFFIC_PASSES lists."),
+           "records": {}}
+
+    def record(key, kernel, workload, name, select=None):
+        calls = TRAFFIC_PASSES[name][1]
+        f, w = load(name, "FETCH_SIZE"), load(name, "WRITE_SIZE")
+        fs, wsc = one_gib / 1024 / calib(f), one_gib / 1024 / calib(w)
+        fl, wl = lib_rows(f), lib_rows(w)
+        if select:
+            fl, wl = select(fl), select(wl)
+        per_kernel = {}
+        for rows, field in ((fl, "fetch_kib"), (wl, "write_kib")):
+            for _, k, v in rows:
+                nm = k.split("(")[0].replace("void ", "")
+                e = per_kernel.setdefault(nm, {"fetch_kib": 0.0, "write_kib": 0.0, "dispatches": 0})
+                e[field] += v / calls
+                if field == "fetch_kib":
+                    e["dispatches"] += 1
+        fk = sum(v for _, _, v in fl) / calls
+        wk = sum(v for _, _, v in wl) / calls
+        b = fk * 1024 * fs + wk * 1024 * wsc
+        out["records"][key] = {"workload": workload, "source_sha256_16": source_hash(kernel), "calls": calls,
+                               "fetch_kib": fk, "write_kib": wk, "fetch_scale": fs, "write_scale": wsc,
+                               "bytes": b, "per_kernel_per_call": per_kernel}
+        print("%-45s %.3f GB per call" % (key, b / 1e9))
+
+    sys.path.insert(0, ROOT)
+    import kda_inputs
+    for wid in (1, 2, 4, 5, 7):
+        wl = kda_inputs.WORKLOADS[wid]["name"]
+        record("kda_chunk_fwd@" + wl, "kda_chunk_fwd", wl, "prefill%d" % wid)
+    record("decode_kernel@kda_decode_N256_H96_64steps", "decode_kernel", "kda_decode_N256_H96_64steps", "decode")
+    # replay launches alternate: verification pass, then commit
+    record("replay_verify@kda_replay_N256_H96_L8", "replay_verify", "kda_replay_N256_H96_L8", "replay",
+           select=lambda rows: rows[0::2])
+    record("replay_commit@kda_replay_N256_H96_L8", "replay_commit", "kda_replay_N256_H96_L8", "replay",
+           select=lambda rows: rows[1::2])
+    record("kda_chunk_bwd@kda_prefill_H96_T8192", "kda_chunk_bwd", "kda_prefill_H96_T8192", "backward")
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+
+
 def time_events(fn, steps, stream):
     import torch
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -282,7 +366,12 @@ def main():
     ap.add_argument("--only-backward", action="store_true", help="time only the backward pass (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--record-traffic", metavar="DIR",
+                    help="write profiles/hbm_traffic.json from the counter passes in DIR (no GPU work)")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.record_traffic)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the KDA path here is built and timed on a single MI355X; "
