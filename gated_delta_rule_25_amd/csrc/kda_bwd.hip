@@ -78,13 +78,6 @@ __device__ __forceinline__ float kbt_at(const E* f, int t, int i) {
   return to_f32(f[(((i >> 4) * KT + (t >> 5)) * 2 + (c >> 4)) * 256 + (((c & 15) >> 2) * 16 + (i & 15)) * 4 + (c & 3)]);
 }
 
-template <typename E>
-__device__ __forceinline__ void store4(E* dst, f32x4 x) {
-  if constexpr (sizeof(E) == 2)
-    *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
-  else
-    *reinterpret_cast<f32x4*>(dst) = x;
-}
 
 // 4 consecutive elements (16-deep operand of one lane) as Frag16
 __device__ __forceinline__ void ld4(Frag16<__bf16>& f, const __bf16* p) { f.v = *reinterpret_cast<const bf16x4*>(p); }
@@ -209,7 +202,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
       ld4(B, sDOT + (16 * jt + l16) * PT + 16 * kb + 4 * g);
       acc = mma16(acc, A, B);
     }
-    store4(dX + ((size_t)ti * 64 + lane) * 4, acc);
+    store_row4(dX + ((size_t)ti * 64 + lane) * 4, acc);
   }
   // Y = Qt^T dO: tile (key tile it, column tile jt)
   E* dY = reinterpret_cast<E*>(dst + DB::Y);
@@ -223,7 +216,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
       ld4(B, sDOT + (16 * jt + l16) * PT + 16 * kb + 4 * g);
       acc = mma16(acc, A, B);
     }
-    store4(dY + ((size_t)ti * 64 + lane) * 4, acc);
+    store_row4(dY + ((size_t)ti * 64 + lane) * 4, acc);
   }
   __syncthreads();  // the transposed arrays are no longer read
 #pragma unroll
@@ -346,6 +339,13 @@ __global__ __launch_bounds__(320) void bwd_carry_kernel(const BwdArgs p) {
       return __builtin_bit_cast(f32x4, buf_ld16(rb, voff, soff));
   };
   constexpr int FRE = 512;  // elements per fragment
+  Frag16<E> id16;  // the 16 x 16 identity as a B operand
+  {
+    f32x4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = (4 * g + e == l16) ? 1.f : 0.f;
+    frag16_from_acc(id16, x);
+  }
 
   for (int k = 0; k < nch; ++k) {
     const int ci = nch - 1 - k;
@@ -357,12 +357,17 @@ __global__ __launch_bounds__(320) void bwd_carry_kernel(const BwdArgs p) {
 #pragma unroll
     for (int rt8 = 0; rt8 < 8; ++rt8)
       rY[rt8] = buf_ld_raw(rb, (uint32_t)(lane * 4 * ES), DB::Y + (rt8 * 8 + ct) * DB::TILE);
-    // the gradient reaching this chunk's end (16 x 16 tiles, I/O dtype)
+    // the gradient reaching this chunk's end (16 x 16 tiles, I/O dtype); each
+    // tile is transposed on the matrix cores (a product with the identity,
+    // exact) so that a lane stores four consecutive columns of one row and a
+    // store instruction writes the whole 512-byte tile
     E* ds_dst = static_cast<E*>(p.chunk_ds) + blkid * (size_t)(D * D);
 #pragma unroll
-    for (int rt8 = 0; rt8 < 8; ++rt8)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ds_dst[tile16_index(16 * rt8 + 4 * g + i, col0 + l16)] = from_f32<E>(accD[rt8][i]);
+    for (int rt8 = 0; rt8 < 8; ++rt8) {
+      Frag16<E> a;
+      frag16_from_acc(a, accD[rt8]);
+      store_row4(ds_dst + tile16_index(16 * rt8 + l16, col0 + 4 * g), mma16((f32x4){0.f, 0.f, 0.f, 0.f}, a, id16));
+    }
     __syncthreads();  // slot k % 3 holds chunk ci
     const unsigned char* buf = smem + (k % L::NBUF) * L::SLOT;
     const E* sKB = reinterpret_cast<const E*>(buf + DB::KB + lane * 8 * ES);
@@ -386,9 +391,11 @@ __global__ __launch_bounds__(320) void bwd_carry_kernel(const BwdArgs p) {
       }
     E* du_dst = static_cast<E*>(p.chunk_du) + blkid * (size_t)(C * D);
 #pragma unroll
-    for (int a = 0; a < NT; ++a)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) du_dst[tile16_index(16 * a + 4 * g + i, col0 + l16)] = from_f32<E>(accU[a][i]);
+    for (int a = 0; a < NT; ++a) {
+      Frag16<E> fr;
+      frag16_from_acc(fr, accU[a]);
+      store_row4(du_dst + tile16_index(16 * a + l16, col0 + 4 * g), mma16((f32x4){0.f, 0.f, 0.f, 0.f}, fr, id16));
+    }
     // dS = Diag(gamma) dS' + Qt^T dO - W^T dU
     Frag<E> uf[KT];
 #pragma unroll
@@ -475,6 +482,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
   const size_t blk = (size_t)slot * H + h;
   const int64_t rs = (int64_t)H * D;
   const int64_t hoff = (int64_t)h * D;
+  Frag16<E> id16;  // the 16 x 16 identity as a B operand
+  {
+    f32x4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = (4 * g + e == l16) ? 1.f : 0.f;
+    frag16_from_acc(id16, x);
+  }
 
   // ---- inputs: k, q rows, the cumulative log-decay g (zeros past the end) ----
   // Every load is issued before the first one is used (rows past the end are
@@ -751,11 +765,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
         }
         acc = mma16(acc, A, B);
       }
+      // scaled by beta per token, then transposed on the matrix cores (exact)
+      // so that a lane stores four consecutive columns of one token
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int s = 16 * st + 4 * g + e;
-        if (s < nv) gdv[(t0 + s) * rs + hoff + j0 + 16 * jt + l16] = from_f32<E>(sBeta[s] * acc[e]);
-      }
+      for (int e = 0; e < 4; ++e) acc[e] *= sBeta[16 * st + 4 * g + e];
+      Frag16<E> fr;
+      frag16_from_acc(fr, acc);
+      const f32x4 tr = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, fr, id16);
+      const int s = 16 * st + l16;
+      if (s < nv) store_row4(gdv + (t0 + s) * rs + hoff + j0 + 16 * jt + 4 * g, tr);
     }
     __syncthreads();
   }

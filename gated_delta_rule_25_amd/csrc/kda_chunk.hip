@@ -405,17 +405,29 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
 #pragma unroll
       for (int a = 0; a < NT; ++a) accU[c][a] = raw_f32(rU[c][a]);
     // states pass: the state entering this chunk (rows are key channels), in
-    // the I/O dtype as 16 x 16 tiles, for the backward pass
+    // the I/O dtype as 16 x 16 tiles, for the backward pass.  Each tile is
+    // transposed on the matrix cores (a product with the identity, exact) so
+    // that a lane holds four consecutive columns of one row and a store
+    // instruction writes the whole 512-byte tile.
+    Frag16<E> id16;
     if constexpr (PASS == 3) {
+      {
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (4 * g + e == l16) ? 1.f : 0.f;
+        frag16_from_acc(id16, x);
+      }
       const size_t blk = (size_t)(slot0 + ci) * H + h;
       E* cs_dst = static_cast<E*>(p.chunk_states) + blk * (size_t)(D * D);
 #pragma unroll
       for (int c = 0; c < CT; ++c)
 #pragma unroll
-        for (int rt8 = 0; rt8 < 8; ++rt8)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            cs_dst[tile16_index(16 * rt8 + 4 * g + i, col0 + 16 * c + l16)] = from_f32<E>(accS[c][rt8][i]);
+        for (int rt8 = 0; rt8 < 8; ++rt8) {
+          Frag16<E> a;
+          frag16_from_acc(a, accS[c][rt8]);
+          store_row4(cs_dst + tile16_index(16 * rt8 + l16, col0 + 16 * c + 4 * g),
+                     mma16((f32x4){0.f, 0.f, 0.f, 0.f}, a, id16));
+        }
     }
     __syncthreads();
     if (EPI) load_gate(t0, nv);
@@ -481,15 +493,17 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
     }
     if constexpr (PASS == 3) {
       // U = U' - W S of this chunk, [C x 128] 16 x 16 tiles in the I/O dtype
-      // (rows past the sequence end are zero)
+      // (rows past the sequence end are zero), transposed as the state
       E* u_dst = static_cast<E*>(p.chunk_u) + ((size_t)(slot0 + ci) * H + h) * (size_t)(C * D);
 #pragma unroll
       for (int c = 0; c < CT; ++c)
 #pragma unroll
-        for (int a = 0; a < NT; ++a)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            u_dst[tile16_index(16 * a + 4 * g + i, col0 + 16 * c + l16)] = from_f32<E>(accU[c][a][i]);
+        for (int a = 0; a < NT; ++a) {
+          Frag16<E> fr;
+          frag16_from_acc(fr, accU[c][a]);
+          store_row4(u_dst + tile16_index(16 * a + l16, col0 + 16 * c + 4 * g),
+                     mma16((f32x4){0.f, 0.f, 0.f, 0.f}, fr, id16));
+        }
     }
     Frag<E> uf[CT][KT];
 #pragma unroll

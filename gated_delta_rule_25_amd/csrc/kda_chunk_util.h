@@ -32,4 +32,13 @@ __device__ __forceinline__ void buf_st4(float v, Rsrc r, uint32_t voff, uint32_t
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)voff, (int)soff, kStreamStore);
 }
 
+// Four consecutive values of E at dst (one 8- or 16-byte store), from fp32.
+template <typename E>
+__device__ __forceinline__ void store_row4(E* dst, f32x4 x) {
+  if constexpr (sizeof(E) == 2)
+    *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+  else
+    *reinterpret_cast<f32x4*>(dst) = x;
+}
+
 }  // namespace kda
