@@ -127,6 +127,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
   E* sQT = reinterpret_cast<E*>(smem + L::QT);
   E* sPT = reinterpret_cast<E*>(smem + L::PTR);
   E* sDOT = reinterpret_cast<E*>(smem + L::DOT);
+  // dO^T[j][t] sits at column t ^ 4 ((j / 8) mod (C / 4)) of row j: the scatter
+  // below writes rows 8 apart from neighbouring lanes, which this spreads over
+  // the banks; groups of four tokens stay contiguous for the operand reads
+  auto dot_at = [](int j, int t) { return j * PT + (t ^ (4 * ((j >> 3) & (C / 4 - 1)))); };
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int H = p.num_heads, h = blockIdx.x % H, slot = blockIdx.x / H;
   if (slot >= p.seq_first[p.num_seqs]) return;
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
       if (t < nv) raw = *reinterpret_cast<const u32x4*>(gdo + (t0 + t) * rs + (int64_t)h * D + j0);
       const E* x = reinterpret_cast<const E*>(&raw);
 #pragma unroll
-      for (int e = 0; e < PER; ++e) sDOT[(j0 + e) * PT + t] = x[e];
+      for (int e = 0; e < PER; ++e) sDOT[dot_at(j0 + e, t)] = x[e];
     }
   }
   __syncthreads();
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
     for (int kb = sa; kb < NT; ++kb) {
       Frag16<E> A, B;
       ld4(A, sPT + (16 * sa + l16) * PT + 16 * kb + 4 * g);
-      ld4(B, sDOT + (16 * jt + l16) * PT + 16 * kb + 4 * g);
+      ld4(B, sDOT + dot_at(16 * jt + l16, 16 * kb + 4 * g));
       acc = mma16(acc, A, B);
     }
     store_row4(dX + ((size_t)ti * 64 + lane) * 4, acc);
@@ -213,7 +217,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs p) {
     for (int kb = 0; kb < NT; ++kb) {
       Frag16<E> A, B;
       ld4(A, sQT + (16 * it + l16) * PT + 16 * kb + 4 * g);
-      ld4(B, sDOT + (16 * jt + l16) * PT + 16 * kb + 4 * g);
+      ld4(B, sDOT + dot_at(16 * jt + l16, 16 * kb + 4 * g));
       acc = mma16(acc, A, B);
     }
     store_row4(dY + ((size_t)ti * 64 + lane) * 4, acc);
