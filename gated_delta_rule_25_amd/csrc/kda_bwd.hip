@@ -448,9 +448,11 @@ struct GradLayout {
   static constexpr size_t UN_CC = 2 * (size_t)C * PC * 4;            //   A, or dM / dB and X = dM M^T
   static constexpr size_t UN_BYTES = UN_STAGE > UN_DW ? (UN_STAGE > UN_CC ? UN_STAGE : UN_CC)
                                                      : (UN_DW > UN_CC ? UN_DW : UN_CC);
+  static constexpr int NLT = (C / 16) * (C / 16 + 1) / 2;           // lower 16 x 16 tiles of a C x C matrix
   static constexpr size_t BETA = UN + UN_BYTES;                      // f32 [C]
-  static constexpr size_t DBETA = BETA + (size_t)C * 4;              // f32 [C]
-  static constexpr size_t DG = DBETA + (size_t)C * 4;                // f32 [128] dG per key
+  static constexpr size_t DBT = BETA + (size_t)C * 4;                // f32 [NLT][16] dbeta parts, T term (columns)
+  static constexpr size_t DBB = DBT + (size_t)NLT * 16 * 4;          // f32 [NLT][16] dbeta parts, B term (rows)
+  static constexpr size_t DG = DBB + (size_t)NLT * 16 * 4;           // f32 [128] dG per key
   static constexpr size_t GRAM = DG + (size_t)D * 4;                 // f32 [C][PC] Gram B (lower tiles)
   static constexpr size_t BYTES = GRAM + (size_t)C * PC * 4;
 };
@@ -471,7 +473,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
   float* sDP = reinterpret_cast<float*>(smem + L::DP);
   float* sUN = reinterpret_cast<float*>(smem + L::UN);
   float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
-  float* sDbeta = reinterpret_cast<float*>(smem + L::DBETA);
+  // dbeta from per-tile parts summed in a fixed order at the end, so the
+  // result does not depend on which wave finishes first
+  float* sDbT = reinterpret_cast<float*>(smem + L::DBT);
+  float* sDbB = reinterpret_cast<float*>(smem + L::DBB);
   float* sDG = reinterpret_cast<float*>(smem + L::DG);
   float* sB = reinterpret_cast<float*>(smem + L::GRAM);
 
@@ -574,10 +579,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
       x[u] = run;
     }
     sB[grp * D + gc] = run;
-    if (tid < C) {
-      sBeta[tid] = tid < nv ? bt : 0.f;
-      sDbeta[tid] = 0.f;
-    }
+    if (tid < C) sBeta[tid] = tid < nv ? bt : 0.f;
     for (int i = tid; i < C * PC; i += NTH) {
       sM[i] = 0.f;
       sDP[i] = 0.f;
@@ -835,7 +837,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
       for (int e = 0; e < 4; ++e) col += sM[(16 * a + 4 * g + e) * PC + 16 * b + l16] * rdT[x][e];
       col += __shfl_xor(col, 16);
       col += __shfl_xor(col, 32);
-      if (g == 0) atomicAdd(&sDbeta[16 * b + l16], col);
+      if (g == 0) sDbT[idx * 16 + l16] = col;
     }
   }
   // dKt = T^T dW on this wave's keys: rows s, dW from registers (rows t)
@@ -924,7 +926,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
         v += __shfl_xor(v, 2);
         v += __shfl_xor(v, 4);
         v += __shfl_xor(v, 8);
-        if (l16 == 0) atomicAdd(&sDbeta[r], v);
+        if (l16 == 0) sDbB[idx * 16 + 4 * g + e] = v;
       }
     }
   }
@@ -1043,7 +1045,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
     const int t = i / (D / 4), c = (i % (D / 4)) * 4;
     *reinterpret_cast<f32x4*>(p.dlog_alpha + (t0 + t) * rs + hoff + c) = *reinterpret_cast<const f32x4*>(oG + t * PK + c);
   }
-  if (tid < nv) p.dbeta[(t0 + tid) * H + h] = sDbeta[tid];
+  // dbeta_s: the T-term parts of the tiles in column tile s / 16 (row tiles
+  // s / 16 .. NT - 1), then the B-term parts of the tiles in row tile s / 16
+  if (tid < nv) {
+    const int st = tid >> 4, sl = tid & 15;
+    float db = 0.f;
+    for (int a = st; a < NT; ++a) db += sDbT[(a * (a + 1) / 2 + st) * 16 + sl];
+    for (int b = 0; b <= st; ++b) db += sDbB[(st * (st + 1) / 2 + b) * 16 + sl];
+    p.dbeta[(t0 + tid) * H + h] = db;
+  }
 }
 
 template <typename Kern>

@@ -137,3 +137,24 @@ def test_bwd_errors():
     d_o, _ = kda_inputs.make_grad_seeds(2, 1, 10, "bf16", 0.0, DEV)
     with pytest.raises(ValueError):
         kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], d_o[:5])
+
+
+def test_bwd_bitwise_repeatable_and_optional_state_gradient():
+    """Every gradient is a fixed-order sum: two calls give the same bits (the
+    per-token dbeta is assembled from per-tile parts in a fixed order, not by
+    atomics). need_d_initial_state=False skips only that output."""
+    say("case repeatability: bf16 H=4 lengths [300, 77, 0, 129], S0 and d_final_state given")
+    inp = kda_inputs.make_prefill(4, [300, 77, 0, 129], "bf16", 0.3, False, DEV, seed=91)
+    d_o, dsT = kda_inputs.make_grad_seeds(4, 4, 506, "bf16", 1.0, DEV, seed=92)
+    first = run_bwd(inp, d_o, dsT)
+    for rep in range(3):
+        again = run_bwd(inp, d_o, dsT)
+        for name, a, b in zip(NAMES, first, again):
+            assert torch.equal(a, b), (rep, name)
+    no_ds0 = kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], d_o,
+                           initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"], d_final_state=dsT,
+                           need_d_initial_state=False)
+    sync()
+    assert no_ds0[5] is None
+    for name, a, b in zip(NAMES[:5], first[:5], no_ds0[:5]):
+        assert torch.equal(a, b), name
