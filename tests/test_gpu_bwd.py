@@ -158,3 +158,41 @@ def test_bwd_bitwise_repeatable_and_optional_state_gradient():
     assert no_ds0[5] is None
     for name, a, b in zip(NAMES[:5], first[:5], no_ds0[:5]):
         assert torch.equal(a, b), name
+
+
+VARLEN_LENGTHS = [1, 31, 32, 33, 63, 64, 65, 128, 0, 1000, 2, 97]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_varlen_chunk_boundaries(dtype):
+    """Twelve sequences whose lengths sit on both sides of the 32- and
+    64-token chunk edges (and an empty one), every head against the oracle."""
+    say("case varlen chunk edges: %s H=3 lengths=%s" % (dtype, VARLEN_LENGTHS))
+    inp = kda_inputs.make_prefill(3, VARLEN_LENGTHS, dtype, 0.3, False, DEV, seed=93)
+    d_o, dsT = kda_inputs.make_grad_seeds(3, len(VARLEN_LENGTHS), sum(VARLEN_LENGTHS), dtype, 1.0, DEV, seed=94)
+    got = run_bwd(inp, d_o, dsT)
+    for t in got:
+        assert torch.isfinite(t.float()).all()
+    worst, welem = compare_bwd(inp, d_o, dsT, got)
+    say("  " + " ".join("%s %.2e" % (k, worst[k]) for k in NAMES))
+    for k in NAMES:
+        assert worst[k] <= TOL[dtype], (k, worst[k])
+
+
+@pytest.mark.timeout(900)
+def test_bwd_one_layer_T8192_all_heads_fp32():
+    """The K3 layer's shape in fp32 I/O (32-token chunks), every head."""
+    say("workload 1 shape in fp32: H=96 T=8192, every head")
+    inp = kda_inputs.make_prefill(96, [8192], "f32", 0.02, False, DEV, seed=95)
+    d_o, dsT = kda_inputs.make_grad_seeds(96, 1, 8192, "f32", 1.0, DEV, seed=96)
+    got = run_bwd(inp, d_o, dsT)
+    for t in got:
+        assert torch.isfinite(t.float()).all()
+    total = {k: 0.0 for k in NAMES}
+    for h0 in range(0, 96, 16):
+        worst, _ = compare_bwd(inp, d_o, dsT, got, heads=range(h0, h0 + 16))
+        for k in NAMES:
+            total[k] = max(total[k], worst[k])
+    say("  " + " ".join("%s %.2e" % (k, total[k]) for k in NAMES))
+    for k in NAMES:
+        assert total[k] <= TOL["f32"], (k, total[k])
