@@ -428,8 +428,10 @@ __global__ __launch_bounds__(320) void bwd_carry_kernel(const BwdArgs p) {
 // ---------------------------------------------------------------------------
 // bwd_grad_kernel: one workgroup of NW waves per (slot, head).  Wave w owns
 // key tiles (8 / NW) w .. (8 / NW)(w + 1) - 1 of every per-token gradient;
-// C x C quantities live in LDS.  All products run in fp32 on the matrix cores
-// (four v_mfma_f32_16x16x4_f32 per 16-deep step).
+// C x C quantities live in LDS.  The Gram tiles, the C x C chain and the
+// tile-referenced products run in fp32 on the matrix cores (four
+// v_mfma_f32_16x16x4_f32 per 16-deep step); the products with S, dS', U, dU,
+// dO and V run in the I/O dtype, the precision those values are stored in.
 // ---------------------------------------------------------------------------
 template <typename E, int C>
 struct GradLayout {

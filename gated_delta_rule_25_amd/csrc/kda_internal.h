@@ -209,7 +209,7 @@ struct CarryArgs {
 // the forward factor block, the chunk's incoming state S and U = U' - W S
 // (the carry's states pass), the reverse carry's block below, and the
 // gradient dS reaching the chunk's end plus dU = P^T dO + Kb dS (the reverse
-// carry), all row-major fp32 except the blocks.
+// carry); S, U, dS and dU in the I/O dtype as 16 x 16 tiles (tile16_index).
 //
 // Reverse-carry block of one (chunk, head), in the fragment order of the
 // reverse carry's matrix-core steps (fragments as in FactorBlock):
