@@ -9,6 +9,7 @@ library is not built this module raises on first use.
 
     o, final_state = chunk_fwd(q, k, v, log_alpha, beta, initial_state, cu_seqlens)
     dq, dk, dv, dlog_alpha, dbeta, d_initial_state = chunk_bwd(q, k, v, log_alpha, beta, d_o, ...)
+    o, final_state = chunk_kda(q, k, v, log_alpha, beta, initial_state)   # torch.autograd: forward + backward
     o = decode_step(state, q, k, v, log_alpha, beta)      # state updated in place
     o, state_out = decode_replay(state, q, k, v, log_alpha, beta, num_tokens, state_out=state)
 """
@@ -20,8 +21,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_bwd", "chunk_bwd_workspace_bytes", "decode_step", "decode_replay", "chunk_fwd_workspace_bytes", "status_string", "KDAError",
-           "last_precondition_flags",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_bwd", "chunk_bwd_workspace_bytes", "chunk_kda", "decode_step",
+           "decode_replay", "chunk_fwd_workspace_bytes", "status_string", "KDAError", "last_precondition_flags",
            "library_path", "D", "REPLAY_MAX_TOKENS"]
 
 D = 128
@@ -261,6 +262,42 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
     if rc != KDA_OK:
         raise KDAError(rc, "kda_chunk_bwd")
     return dq, dk, dv, dla, db, ds0
+
+
+class _ChunkKDA(torch.autograd.Function):
+    """chunk_fwd forward, chunk_bwd backward (the plain recurrence with the
+    bounded decay).  The forward saves only its inputs; the backward
+    recomputes the chunk states."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, log_alpha, beta, initial_state, cu_seqlens):
+        o, final_state = chunk_fwd(q, k, v, log_alpha, beta, initial_state, cu_seqlens, output_final_state=True)
+        ctx.save_for_backward(q, k, v, log_alpha, beta, initial_state, cu_seqlens)
+        ctx.mark_non_differentiable(*(t for t in (cu_seqlens,) if t is not None))
+        return o, final_state
+
+    @staticmethod
+    def backward(ctx, d_o, d_final_state):
+        q, k, v, log_alpha, beta, initial_state, cu_seqlens = ctx.saved_tensors
+        if d_o is None:
+            d_o = torch.zeros_like(q)
+        d_o = d_o.to(q.dtype).contiguous()
+        if d_final_state is not None:
+            d_final_state = d_final_state.to(torch.float32).contiguous()
+        need_ds0 = initial_state is not None and ctx.needs_input_grad[5]
+        dq, dk, dv, dla, db, ds0 = chunk_bwd(q, k, v, log_alpha, beta, d_o, initial_state, cu_seqlens, d_final_state,
+                                             need_d_initial_state=need_ds0)
+        return dq, dk, dv, dla, db, ds0, None
+
+
+def chunk_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor, beta: torch.Tensor,
+              initial_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Differentiable KDA prefill (torch.autograd): (o, final_state) as
+    chunk_fwd, with gradients for q, k, v, log_alpha, beta and the initial
+    state from chunk_bwd.  Plain recurrence only (no fused prologue or
+    epilogue), log_alpha in [-5, 0]."""
+    return _ChunkKDA.apply(q, k, v, log_alpha, beta, initial_state, cu_seqlens)
 
 
 def _prefill_args(q, k, v, log_alpha, beta, initial_state, cu_seqlens, conv_q_w, conv_k_w, gate, norm_w, l2_eps,

@@ -196,3 +196,30 @@ def test_bwd_one_layer_T8192_all_heads_fp32():
     say("  " + " ".join("%s %.2e" % (k, total[k]) for k in NAMES))
     for k in NAMES:
         assert total[k] <= TOL["f32"], (k, total[k])
+
+
+def test_chunk_kda_autograd_matches_the_two_calls():
+    """chunk_kda (torch.autograd) gives chunk_fwd's outputs and, for the loss
+    <d_o, o> + <d_final_state, S_T>, chunk_bwd's gradients bit for bit; with
+    an initial state that needs no gradient its gradient is not formed."""
+    say("case autograd: bf16 H=2 lengths [90, 40], S0 given")
+    inp = kda_inputs.make_prefill(2, [90, 40], "bf16", 0.3, False, DEV, seed=97)
+    d_o, dsT = kda_inputs.make_grad_seeds(2, 2, 130, "bf16", 1.0, DEV, seed=98)
+    leaves = [inp[n].clone().requires_grad_(True) for n in ("q", "k", "v", "log_alpha", "beta", "initial_state")]
+    o, fs = kda.chunk_kda(*leaves, inp["cu_seqlens"])
+    o_ref, fs_ref = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                                  inp["initial_state"], inp["cu_seqlens"])
+    sync()
+    assert torch.equal(o.detach(), o_ref) and torch.equal(fs.detach(), fs_ref)
+    ((o.float() * d_o.float()).sum() + (fs * dsT).sum()).backward()
+    sync()
+    ref = run_bwd(inp, d_o, dsT)
+    for name, leaf, r in zip(NAMES, leaves, ref):
+        assert leaf.grad is not None and torch.equal(leaf.grad, r), name
+    # no gradient wanted for the initial state
+    leaves2 = [inp[n].clone().requires_grad_(n != "initial_state")
+               for n in ("q", "k", "v", "log_alpha", "beta", "initial_state")]
+    o2, _ = kda.chunk_kda(*leaves2, inp["cu_seqlens"])
+    (o2.float() * d_o.float()).sum().backward()
+    sync()
+    assert leaves2[5].grad is None and leaves2[0].grad is not None
