@@ -454,8 +454,7 @@ struct GradLayout {
   static constexpr size_t BETA = UN + UN_BYTES;                      // f32 [C]
   static constexpr size_t DBT = BETA + (size_t)C * 4;                // f32 [NLT][16] dbeta parts, T term (columns)
   static constexpr size_t DBB = DBT + (size_t)NLT * 16 * 4;          // f32 [NLT][16] dbeta parts, B term (rows)
-  static constexpr size_t DG = DBB + (size_t)NLT * 16 * 4;           // f32 [128] dG per key
-  static constexpr size_t GRAM = DG + (size_t)D * 4;                 // f32 [C][PC] Gram B (lower tiles)
+  static constexpr size_t GRAM = DBB + (size_t)NLT * 16 * 4;         // f32 [C][PC] Gram B (lower tiles)
   static constexpr size_t BYTES = GRAM + (size_t)C * PC * 4;
 };
 
@@ -479,7 +478,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
   // result does not depend on which wave finishes first
   float* sDbT = reinterpret_cast<float*>(smem + L::DBT);
   float* sDbB = reinterpret_cast<float*>(smem + L::DBB);
-  float* sDG = reinterpret_cast<float*>(smem + L::DG);
   float* sB = reinterpret_cast<float*>(smem + L::GRAM);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
@@ -1003,18 +1001,48 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
         dGp[c] += dKb * (kv * eb);
       }
     }
+  // dlog_alpha_t = sum_{t' >= t} dg_t' + dG, in registers: a lane holds the
+  // tokens 16 rt + 4 g + e of its channel; the sums of its four-token groups
+  // are exchanged across the lane groups g, then each token adds the groups
+  // after it and its own group's tail.  Tokens past the end carry dg = 0
+  // (their k and q are zero).  Stored straight from registers: 16 lanes
+  // write one token's 16 channels (64 bytes).
 #pragma unroll
   for (int c = 0; c < KPW; ++c) {
     float v = dGp[c];
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
     const int i = 16 * (KPW * wv + c) + l16;
-    if (g == 0) sDG[i] = v + dgam[c] * __expf(Gc(i));
+    const float dGi = v + dgam[c] * __expf(Gc(i));
+    float after[NT], tot[NT];  // groups g' > g of tile rt; all four groups of tile rt
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      const float bs = (odg[rt][c][0] + odg[rt][c][1]) + (odg[rt][c][2] + odg[rt][c][3]);
+      after[rt] = 0.f;
+      tot[rt] = 0.f;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const float bg = __shfl(bs, l16 + 16 * gg);
+        tot[rt] += bg;
+        if (gg > g) after[rt] += bg;
+      }
+    }
+    float later = dGi;  // dG plus every tile after rt
+#pragma unroll
+    for (int rt = NT - 1; rt >= 0; --rt) {
+      float run = later + after[rt];
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        run += odg[rt][c][e];
+        const int t = 16 * rt + 4 * g + e;
+        if (t < nv) p.dlog_alpha[(t0 + t) * rs + hoff + i] = run;
+      }
+      later += tot[rt];
+    }
   }
-  __syncthreads();  // k, q and g are no longer read: their LDS takes the outputs
+  __syncthreads();  // k and q are no longer read: their LDS takes dq and dk
   E* oQ = sK;
   E* oK = sQ;
-  float* oG = sG;
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
@@ -1024,17 +1052,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
         const int t = 16 * rt + 4 * g + e, i = 16 * (KPW * wv + c) + l16;
         oQ[t * PK + i] = from_f32<E>(odq[rt][c][e]);
         oK[t * PK + i] = from_f32<E>(odk[rt][c][e]);
-        oG[t * PK + i] = odg[rt][c][e];
       }
-  __syncthreads();
-  // dlog_alpha_t = sum_{t' >= t} dg_t' + dG
-  if (tid < D) {
-    float run = sDG[tid];
-    for (int t = C - 1; t >= 0; --t) {
-      run += oG[t * PK + tid];
-      oG[t * PK + tid] = run;
-    }
-  }
   __syncthreads();
   E* gdq = static_cast<E*>(p.dq);
   E* gdk = static_cast<E*>(p.dk);
@@ -1042,10 +1060,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
     const int t = i / (D / PER), c = (i % (D / PER)) * PER;
     *reinterpret_cast<u32x4*>(gdq + (t0 + t) * rs + hoff + c) = *reinterpret_cast<const u32x4*>(oQ + t * PK + c);
     *reinterpret_cast<u32x4*>(gdk + (t0 + t) * rs + hoff + c) = *reinterpret_cast<const u32x4*>(oK + t * PK + c);
-  }
-  for (int i = tid; i < nv * (D / 4); i += NTH) {
-    const int t = i / (D / 4), c = (i % (D / 4)) * 4;
-    *reinterpret_cast<f32x4*>(p.dlog_alpha + (t0 + t) * rs + hoff + c) = *reinterpret_cast<const f32x4*>(oG + t * PK + c);
   }
   // dbeta_s: the T-term parts of the tiles in column tile s / 16 (row tiles
   // s / 16 .. NT - 1), then the B-term parts of the tiles in row tile s / 16
