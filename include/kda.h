@@ -274,7 +274,8 @@ size_t kda_chunk_bwd_workspace_bytes(int num_seqs, int64_t total_tokens, int num
  * (KDA_ERR_INVALID_ARG).  Alignment as for kda_chunk_fwd; d_o, the gradients
  * and the state gradients need 16 bytes, dbeta 4.  Asynchronous on `stream`
  * like every other call; the recomputed forward uses the same kernels as
- * kda_chunk_fwd, so its rounding is that of the forward.
+ * kda_chunk_fwd, so its rounding is that of the forward.  Every sum runs in a
+ * fixed order (no atomics), so repeated calls give the same bits.
  */
 kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
                          const float* initial_state, const int32_t* cu_seqlens, const void* d_o,
