@@ -223,3 +223,19 @@ def test_chunk_kda_autograd_matches_the_two_calls():
     (o2.float() * d_o.float()).sum().backward()
     sync()
     assert leaves2[5].grad is None and leaves2[0].grad is not None
+
+
+def test_bwd_all_sequences_empty():
+    """T = 0 with two empty sequences: no token gradients, and the state
+    gradient passes through unchanged (d_initial_state = d_final_state)."""
+    say("case empty batch: bf16 H=2 lengths [0, 0]")
+    inp = kda_inputs.make_prefill(2, [0, 0], "bf16", 0.3, False, DEV, seed=99)
+    d_o, dsT = kda_inputs.make_grad_seeds(2, 2, 0, "bf16", 1.0, DEV, seed=100)
+    got = run_bwd(inp, d_o, dsT)
+    for t in got[:5]:
+        assert t.shape[0] == 0
+    assert torch.equal(got[5], dsT)
+    got0 = kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], d_o,
+                         initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"], d_final_state=None)
+    sync()
+    assert torch.count_nonzero(got0[5]).item() == 0
