@@ -431,7 +431,16 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
     }
     __syncthreads();
     if (EPI) load_gate(t0, nv);
-    if (ci + 1 < nch) load_u(ci + 1);
+    // In the passes that write outputs, the next chunk's loads (on the last
+    // chunk a repeat of this one's) and the output stores below are issued on
+    // every path: with a load or store behind a branch the compiler cannot
+    // count what is in flight after the P loads, and their wait drains every
+    // outstanding access, the U' loads just issued included (measured: 269 ->
+    // 257 us for the one-layer carry).  The passes without outputs keep the
+    // conditional load, which measured faster there (242 against 276 us for
+    // the states pass).
+    if constexpr (write_o) load_u(ci + 1 < nch ? ci + 1 : ci);
+    else if (ci + 1 < nch) load_u(ci + 1);
 
     // Four-wave single-tile blocks: each stage first issues all of its LDS
     // fragment reads (the scheduling barrier keeps them ahead of the
@@ -518,7 +527,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
           if (kt <= rt / 2)
 #pragma unroll
             for (int c = 0; c < CT; ++c) accO[c][rt] = mma(accO[c][rt], rP[F::p_frag(rt, kt)], uf[c][kt]);
-    if (write_o && ci + 1 < nch) load_p(ci + 1);
+    if (write_o) load_p(ci + 1 < nch ? ci + 1 : ci);
 
     // outputs: each 16 x 16 tile transposed on the matrix cores to lane =
     // token, four consecutive columns, then (with the epilogue) the head-wise
@@ -532,14 +541,15 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
         for (int e = 0; e < 4; ++e) x[e] = (4 * g + e == l16) ? 1.f : 0.f;
         frag16_from_acc(id, x);
       }
+      // rows past the sequence end fall outside the buffer view and are dropped
+      const Rsrc orb = make_rsrc(go + t0 * rs, (uint32_t)((int64_t)nv * rs * ES));
       auto store = [&](const f32x4& t, int c, int rt) {
-        const int tok = 16 * rt + l16;
-        if (tok < nv) {
-          E* dst = go + (t0 + tok) * rs + hoff + col0 + 16 * c + 4 * g;
-          if constexpr (ES == 2)
-            *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
-          else
-            *reinterpret_cast<f32x4*>(dst) = t;
+        const uint32_t off = (uint32_t)(((16 * rt + l16) * rs + hoff + col0 + 16 * c + 4 * g) * ES);
+        if constexpr (ES == 2) {
+          const bf16x4 b = (bf16x4){(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), orb, (int)off, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t), orb, (int)off, 0, 0);
         }
       };
       if constexpr (EPI) {
