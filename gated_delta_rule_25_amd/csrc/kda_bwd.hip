@@ -82,6 +82,13 @@ __device__ __forceinline__ float kbt_at(const E* f, int t, int i) {
 // 4 consecutive elements (16-deep operand of one lane) as Frag16
 __device__ __forceinline__ void ld4(Frag16<__bf16>& f, const __bf16* p) { f.v = *reinterpret_cast<const bf16x4*>(p); }
 __device__ __forceinline__ void ld4(Frag16<float>& f, const float* p) { f.v = *reinterpret_cast<const f32x4*>(p); }
+// the same four values through a buffer view (byte offset; out of range reads zero)
+__device__ __forceinline__ void buf_ld4(Frag16<__bf16>& f, Rsrc r, uint32_t off) {
+  f.v = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void buf_ld4(Frag16<float>& f, Rsrc r, uint32_t off) {
+  f.v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
 
 // ---------------------------------------------------------------------------
 // bwd_prep_kernel: one workgroup of four waves per (slot, head).  The factor
@@ -519,28 +526,42 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
   // Each 32-column block's dO, V, U and dU (16-byte pieces of E; U and dU
   // from their 16 x 16 tiles, where a piece never crosses a tile row) and the
   // wave's S and dS' operands are loaded into registers one block ahead, so
-  // their latency overlaps the previous block's products.
+  // their latency overlaps the previous block's products.  The loads go
+  // through buffer views and are issued for every block and lane: threads
+  // without a piece, rows past the sequence end and the block after the last
+  // read zero from outside the view.  With no load or store behind a branch,
+  // the wait for a block's data counts only the accesses issued after it
+  // instead of draining the dV stores too.
   constexpr int NSTG = C * (JB / PER);  // staging pieces per array and block
   static_assert(NSTG <= NTH, "one staging piece per thread");
   const int st_t = tid / (JB / PER), st_c = (tid % (JB / PER)) * PER;
   const bool st_ld = tid < NSTG && st_t < nv;
+  constexpr uint32_t kOutside = 0x80000000u;  // past every view below
+  constexpr int ES = (int)sizeof(E);
+  const uint32_t rows_bytes = (uint32_t)((int64_t)nv * rs * ES);
   u32x4 nA, nB, nU, nDU;
   Frag16<E> nS[KPW][JB / 16], nD[KPW][JB / 16];
-  auto fetch = [&](int j0) {
-    nA = nB = nU = nDU = (u32x4){0u, 0u, 0u, 0u};
-    if (st_ld) {
-      nA = *reinterpret_cast<const u32x4*>(gdo + (t0 + st_t) * rs + hoff + j0 + st_c);
-      nB = *reinterpret_cast<const u32x4*>(gv + (t0 + st_t) * rs + hoff + j0 + st_c);
-      nU = *reinterpret_cast<const u32x4*>(gU + tile16_index(st_t, j0 + st_c));
-      nDU = *reinterpret_cast<const u32x4*>(gDU + tile16_index(st_t, j0 + st_c));
-    }
+  auto fetch = [&](int j0, bool any) {
+    const Rsrc rDO = make_rsrc(gdo + t0 * rs, any ? rows_bytes : 0u);
+    const Rsrc rV = make_rsrc(gv + t0 * rs, any ? rows_bytes : 0u);
+    const Rsrc rU = make_rsrc(gU, any ? (uint32_t)(C * D * ES) : 0u);
+    const Rsrc rDU = make_rsrc(gDU, any ? (uint32_t)(C * D * ES) : 0u);
+    const Rsrc rS = make_rsrc(gS, any ? (uint32_t)(D * D * ES) : 0u);
+    const Rsrc rDS = make_rsrc(gDS, any ? (uint32_t)(D * D * ES) : 0u);
+    const uint32_t orow = st_ld ? (uint32_t)((st_t * rs + hoff + j0 + st_c) * ES) : kOutside;
+    const uint32_t otile = st_ld ? (uint32_t)(tile16_index(st_t, j0 + st_c) * ES) : kOutside;
+    nA = buf_ld16(rDO, orow, 0);
+    nB = buf_ld16(rV, orow, 0);
+    nU = buf_ld16(rU, otile, 0);
+    nDU = buf_ld16(rDU, otile, 0);
 #pragma unroll
     for (int c = 0; c < KPW; ++c)
 #pragma unroll
       for (int js = 0; js < JB / 16; ++js) {
         const int i = 16 * (KPW * wv + c) + l16;
-        ld4(nS[c][js], gS + tile16_index(i, j0 + 16 * js + 4 * g));
-        ld4(nD[c][js], gDS + tile16_index(i, j0 + 16 * js + 4 * g));
+        const uint32_t o = (uint32_t)(tile16_index(i, j0 + 16 * js + 4 * g) * ES);
+        buf_ld4(nS[c][js], rS, o);
+        buf_ld4(nD[c][js], rDS, o);
       }
   };
   {
@@ -562,7 +583,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
       x[u] = p.log_alpha[(t0 + min(t, nv - 1)) * rs + hoff + gc];
     }
     const float bt = p.beta[(t0 + min(tid, nv - 1)) * H + h];
-    fetch(0);  // the first column block of the products with S and dS'
+    fetch(0, true);  // the first column block of the products with S and dS'
 #pragma unroll
     for (int m = 0; m < KQ; ++m) {
       const int i = tid + NTH * m, t = i / (D / PER), c = (i % (D / PER)) * PER;
@@ -713,7 +734,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
         cD[c][js] = nD[c][js];
       }
     __syncthreads();
-    if (j0 + JB < D) fetch(j0 + JB);
+    fetch(j0 + JB < D ? j0 + JB : j0, j0 + JB < D);
     // dQt += dO S^T, (dU S^T), dKb += U dS'^T, dgamma partials: own key tiles
 #pragma unroll
     for (int c = 0; c < KPW; ++c) {
@@ -757,8 +778,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
       }
     }
     // dV = T^T dU for these columns: tile (token tile st, column tile jt);
-    // T[t][s] = M[t][s] beta_s is zero for t < s
-    for (int ti = wv; ti < NT * (JB / 16); ti += NW) {
+    // T[t][s] = M[t][s] beta_s is zero for t < s.  One tile per wave, stored
+    // through a view of the chunk's rows (rows past the end are dropped).
+    constexpr int NDV = NT * (JB / 16);
+    static_assert(NDV <= NW, "at most one dV tile per wave");
+    if (NDV == NW || wv < NDV) {
+      const int ti = wv;
       const int st = ti / (JB / 16), jt = ti % (JB / 16);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int kb = st; kb < NT; ++kb) {
@@ -778,8 +803,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_grad_kernel(const BwdArgs p) {
       Frag16<E> fr;
       frag16_from_acc(fr, acc);
       const f32x4 tr = mma16((f32x4){0.f, 0.f, 0.f, 0.f}, fr, id16);
-      const int s = 16 * st + l16;
-      if (s < nv) store_row4(gdv + (t0 + s) * rs + hoff + j0 + 16 * jt + 4 * g, tr);
+      const Rsrc rdv = make_rsrc(gdv + t0 * rs, rows_bytes);
+      const uint32_t off = (uint32_t)(((16 * st + l16) * rs + hoff + j0 + 16 * jt + 4 * g) * ES);
+      if constexpr (ES == 2) {
+        const bf16x4 b = (bf16x4){(__bf16)tr[0], (__bf16)tr[1], (__bf16)tr[2], (__bf16)tr[3]};
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), rdv, (int)off, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, tr), rdv, (int)off, 0, 0);
+      }
     }
     __syncthreads();
   }
