@@ -156,7 +156,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
     one.  unbounded_decay: accept any log_alpha <= 0 (the negative-softplus
     decay) instead of the bound [-5, 0]; the diagonal tiles then run position
     pair by position pair.  factor_budget_mib: cap on one window's factor
-    store in MiB (0: 4096); longer inputs run in several windows.  Returns
+    store in MiB (0: 16384); longer inputs run in several windows.  Returns
     (o, final_state); final_state may be the same tensor as initial_state
     (in-place continuation).
     """

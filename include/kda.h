@@ -136,8 +136,8 @@ typedef enum KDA_ENUM_BASE {
  *       writes the outputs.  Results agree with the sequential form up to
  *       rounding.
  *   factor_budget_mib  cap, in MiB, on the factor store of one window of
- *       kda_chunk_fwd (the bulk of its workspace): 0 means the largest, 4096;
- *       values above 4096 are taken as 4096; negative values are
+ *       kda_chunk_fwd (the bulk of its workspace): 0 means the largest, 16384;
+ *       values above 16384 are taken as 16384; negative values are
  *       KDA_ERR_INVALID_ARG.  Inputs whose factor blocks exceed the cap run in
  *       several windows, one after another on the stream, with the same
  *       results up to rounding.  The workspace query and the call must be
@@ -161,7 +161,7 @@ typedef struct {
  * which the segmented form depends on).  Returns 0 for invalid sizes.
  * Most of it is the factor store: a 70.5 KiB block per (64-token chunk, head)
  * for bf16 I/O, 68.5 KiB per (32-token chunk, head) for fp32.  It is capped at
- * 4 GiB, or at opts->factor_budget_mib; longer inputs run in several windows.
+ * 16 GiB, or at opts->factor_budget_mib; longer inputs run in several windows.
  * The query depends on no environment variable: the same sizes and options
  * give the same value on the same device.
  */

@@ -77,14 +77,14 @@ def test_status_strings(lib):
 
 def test_workspace_bytes(lib):
     # the two-kernel schedule keeps a factor store in the workspace: it grows
-    # with the number of (chunk, head) blocks and is capped (long inputs run in
-    # windows), so a one-layer 1M-token input still needs only a few GiB
+    # with the number of (chunk, head) blocks and is capped at 16 GiB (long
+    # inputs run in windows), so a one-layer 1M-token input needs about that
     w8k = lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, None)
     w16k = lib.kda_chunk_fwd_workspace_bytes(1, 16384, 96, 128, 128, BF16, None)
     assert w8k > 0 and w16k > w8k
     assert w8k % 256 == 0
-    assert lib.kda_chunk_fwd_workspace_bytes(1, 1 << 20, 96, 128, 128, BF16, None) < 6 << 30
-    assert lib.kda_chunk_fwd_workspace_bytes(64, 10 ** 6, 96, 128, 128, BF16, None) < 6 << 30
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 1 << 20, 96, 128, 128, BF16, None) < 17 << 30
+    assert lib.kda_chunk_fwd_workspace_bytes(64, 10 ** 6, 96, 128, 128, BF16, None) < 17 << 30
     # fp32 chunks are half as long, so more blocks
     assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, 0, None) > w8k
     assert lib.kda_chunk_fwd_workspace_bytes(2, 10, 2, 64, 128, BF16, None) == 0  # invalid sizes
@@ -93,14 +93,14 @@ def test_workspace_bytes(lib):
 
 def test_workspace_factor_budget_field(lib, monkeypatch):
     # kda_fused_opts.factor_budget_mib caps one window's factor store:
-    # 129 chunk slots x 96 heads x 70.5 KiB fit 4 GiB; a 64 MiB cap needs 14
-    # windows of 129 // 14 + 2 = 11 slots; 0 and anything above 4096 keep the
-    # default; a negative cap is refused.  No environment variable changes it.
+    # 129 chunk slots x 96 heads x 70.5 KiB fit one window; a 64 MiB cap needs
+    # 14 windows of 129 // 14 + 2 = 11 slots; 0 and anything above 16384 keep
+    # the default; a negative cap is refused.  No environment variable changes it.
     one = lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, None)
     assert one == two_kernel_ws(1, 8192, 96)
     capped = lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, opts_p(Opts(factor_budget_mib=64)))
     assert capped == 768 + 96 * 128 * 128 * 4 + 11 * 96 * FB_BF16  # + the state carried between windows
-    for mib in (0, 4096, 1 << 20):
+    for mib in (0, 4096, 16384, 1 << 20):
         assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16,
                                                  opts_p(Opts(factor_budget_mib=mib))) == one
     assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, BF16, opts_p(Opts(factor_budget_mib=-1))) == 0
