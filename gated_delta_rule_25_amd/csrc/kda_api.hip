@@ -184,8 +184,13 @@ kda_status checked(const kda::CheckArgs& a, hipStream_t stream) {
   return flags ? KDA_ERR_PRECONDITION : KDA_OK;
 }
 
+// The kernels address one chunk's rows of a [T, H, 128] tensor through
+// buffer views with 32-bit byte offsets: 64 tokens x H x 128 x 4 bytes must
+// stay below 2^31, so H is at most kMaxHeads.
+constexpr int kMaxHeads = 65535;
+
 bool sizes_ok(int num_seqs, int64_t total_tokens, int num_heads) {
-  return num_seqs >= 1 && num_heads >= 1 && total_tokens >= 0 &&
+  return num_seqs >= 1 && num_heads >= 1 && num_heads <= kMaxHeads && total_tokens >= 0 &&
          (int64_t)num_seqs * num_heads <= (int64_t)INT32_MAX / 2 && total_tokens <= (int64_t)INT32_MAX;
 }
 

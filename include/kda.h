@@ -184,6 +184,10 @@ size_t kda_chunk_fwd_workspace_bytes(int num_seqs, int64_t total_tokens, int num
  *                  sequence spans all T_total tokens).  Zero-length sequences
  *                  are allowed; their final state equals the initial state.
  *   opts           NULL or the fused prologue/epilogue options above.
+ *   num_heads      H, 1 .. 65535 (one chunk's rows of a [T_total, H, 128]
+ *                  tensor are addressed with 32-bit offsets); else
+ *                  KDA_ERR_INVALID_ARG.  The same bound holds for
+ *                  kda_chunk_fwd_noalloc and kda_chunk_bwd.
  *   o              [T_total, H, 128] dtype output; must not overlap any input.
  *   final_state    [N, H, 128, 128] fp32 output or NULL (not written).
  *   workspace      device scratch of at least kda_chunk_fwd_workspace_bytes()

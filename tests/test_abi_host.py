@@ -87,6 +87,12 @@ def test_workspace_bytes(lib):
     assert lib.kda_chunk_fwd_workspace_bytes(64, 10 ** 6, 96, 128, 128, BF16, None) < 17 << 30
     # fp32 chunks are half as long, so more blocks
     assert lib.kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, 0, None) > w8k
+    # at most 65535 heads: a chunk's rows of a [T, H, 128] tensor are
+    # addressed with 32-bit byte offsets
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 64, 65535, 128, 128, 0, None) > 0
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 64, 65536, 128, 128, BF16, None) == 0
+    assert lib.kda_chunk_bwd_workspace_bytes(1, 64, 65536, 128, 128, BF16) == 0
+    assert chunk(lib, T=0, H=65536) == INVALID
     assert lib.kda_chunk_fwd_workspace_bytes(2, 10, 2, 64, 128, BF16, None) == 0  # invalid sizes
     assert lib.kda_chunk_fwd_workspace_bytes(0, 10, 2, 128, 128, BF16, None) == 0
 
