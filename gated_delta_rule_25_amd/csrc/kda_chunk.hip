@@ -660,10 +660,10 @@ static hipError_t launch_carry_t(const CarryArgs& a, hipStream_t stream) {
 
 template <typename E, int C>
 static hipError_t launch_carry_dtype(const CarryArgs& a, hipStream_t stream) {
-  // whole heads (the epilogue normalises over all 128 value columns) on four
-  // two-tile waves, else 64-column blocks on four one-tile waves (two per
-  // work item, four in the pass that traces B and M), the blocks sharing the
-  // factor reads through L2
+  // whole heads on four two-tile waves (the epilogue normalises over all 128
+  // value columns; the pass that traces B and M runs one block of each),
+  // else 64-column blocks on four one-tile waves (two per work item), the
+  // blocks sharing the factor reads through L2
   if (a.gate) {
     if (a.col_split != 1) return hipErrorInvalidValue;
     if (a.pass == 0) return launch_carry_t<E, C, 128, true, 2, 0>(a, stream);
@@ -673,7 +673,7 @@ static hipError_t launch_carry_dtype(const CarryArgs& a, hipStream_t stream) {
   if (a.pass == 0 && a.col_split == 2) return launch_carry_t<E, C, 64, false, 1, 0>(a, stream);
   if (a.pass == 3 && a.col_split == 2 && a.chunk_states && a.chunk_u)
     return launch_carry_t<E, C, 64, false, 1, 3>(a, stream);
-  if (a.pass == 1 && a.col_split == 4) return launch_carry_t<E, C, 64, false, 1, 1>(a, stream);
+  if (a.pass == 1 && a.col_split == 2) return launch_carry_t<E, C, 128, false, 2, 1>(a, stream);
   if (a.pass == 2 && a.col_split == 2) return launch_carry_t<E, C, 64, false, 1, 2>(a, stream);
   return hipErrorInvalidValue;
 }
