@@ -60,7 +60,6 @@ template <>
 struct Raw4<float> {
   f32x4 v;
 };
-__device__ __forceinline__ void ld_raw4(Raw4<__bf16>& x, const __bf16* p) { x.v = *reinterpret_cast<const bf16x4*>(p); }
 __device__ __forceinline__ void ld_raw4(Raw4<float>& x, const float* p) { x.v = *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void cvt_raw4(float* y, const Raw4<__bf16>& x) {
 #pragma unroll
@@ -181,11 +180,7 @@ __device__ __forceinline__ void tap_bcast(float (&wt)[4], const float (&wl)[8], 
   });
 }
 
-// Fragment of step s from the lane's per-piece values x[8][4].
-__device__ __forceinline__ void frag_step(Frag<__bf16>& f, const float (&x)[8][4], int s) {
-  f.v = (bf16x8){(__bf16)x[2 * s][0], (__bf16)x[2 * s][1], (__bf16)x[2 * s][2], (__bf16)x[2 * s][3],
-                 (__bf16)x[2 * s + 1][0], (__bf16)x[2 * s + 1][1], (__bf16)x[2 * s + 1][2], (__bf16)x[2 * s + 1][3]};
-}
+// Fragment of step s from the lane's per-piece values x[8][4] (fp32 operands).
 __device__ __forceinline__ void frag_step(Frag<float>& f, const float (&x)[8][4], int s) {
   f.lo = (f32x4){x[2 * s][0], x[2 * s][1], x[2 * s][2], x[2 * s][3]};
   f.hi = (f32x4){x[2 * s + 1][0], x[2 * s + 1][1], x[2 * s + 1][2], x[2 * s + 1][3]};
@@ -323,7 +318,6 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
   const E* gk = static_cast<const E*>(p.k);
   const E* gv = static_cast<const E*>(p.v);
   const int tok = 16 * w + r;  // this lane's token within the chunk
-  const uint32_t lane_fr = (uint32_t)lane * 8 * ES;  // lane's entry in a fragment
 
   // Token range of every slot of this workgroup, found once up front and
   // kept in LDS: global loads in the chunk loop would make its waits drain
