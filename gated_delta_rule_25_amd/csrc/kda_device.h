@@ -105,7 +105,9 @@ __device__ __forceinline__ f32x4 mma(f32x4 acc, const Frag<float>& a, const Frag
   return acc;
 }
 
-__device__ __forceinline__ float sigmoidf_fast(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// 1 / (1 + e^-x) with the hardware reciprocal (1 ulp) instead of the IEEE
+// division's scale / refine / fix-up sequence, about ten instructions
+__device__ __forceinline__ float sigmoidf_fast(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // s_waitcnt operand that lets n vector-memory operations stay outstanding.
 __host__ __device__ constexpr int vmcnt_wait(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }

@@ -128,14 +128,15 @@ __device__ __forceinline__ void static_for(Fn&& f) {
 }
 
 // 32-bit DPP moves within 16-lane rows: shift right by N (zero fill), rotate
-// right by N, broadcast of lane N.
+// right by N, broadcast of lane N.  A rotate or broadcast reads a valid lane
+// everywhere, so it needs no fallback value (no zeroed register to start from).
 template <int N>
 __device__ __forceinline__ uint32_t dpp_shr(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x110 + N, 0xf, 0xf, true);
 }
 template <int N>
 __device__ __forceinline__ uint32_t dpp_ror(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x120 + N, 0xf, 0xf, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x120 + N, 0xf, 0xf, true);
 }
 // Shift right by N; lanes with no source (the first N of a row) keep `old`.
 template <int N>
@@ -144,7 +145,7 @@ __device__ __forceinline__ uint32_t dpp_shr_or(uint32_t old, uint32_t x) {
 }
 template <int N>
 __device__ __forceinline__ float dpp_bcast(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, true));
 }
 
 // Rows tok - 1 .. tok - 3 of a piece, for the lane at row position r: from
@@ -478,7 +479,8 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
           load_rows(ok, hk, gk);
         }
         auto prologue = [&](QK (&y)[8], const Raw4<E> (&own)[8], const Raw4<E> (&halo)[8], const float (&wl)[8],
-                            bool conv) {
+                            auto conv_c) {
+          constexpr bool conv = decltype(conv_c)::value;
           float ss = 0.f;
 #pragma unroll
           for (int pc = 0; pc < 8; ++pc) {
@@ -488,7 +490,7 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               float c = x[0][i];
-              if (conv) {
+              if constexpr (conv) {
                 float wt[4];
                 tap_bcast(wt, wl, pc, i);
                 c = wt[0] * x[3][i] + wt[1] * x[2][i] + wt[2] * x[1][i] + wt[3] * x[0][i];
@@ -498,7 +500,7 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
               y[pc].v[i] = c;
             }
           }
-          if (conv) {
+          if constexpr (conv) {
             ss += __shfl_xor(ss, 16);
             ss += __shfl_xor(ss, 32);
             const float inv = rsqrtf(ss + p.l2_eps);
@@ -506,8 +508,13 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
             for (int pc = 0; pc < 8; ++pc) y[pc].v *= inv;
           }
         };
-        prologue(rq, oq, hq, wlq, p.conv_q_w != nullptr);
-        prologue(rk, ok, hk, wlk, p.conv_k_w != nullptr);
+        // the convolution switch is taken once per tensor: inside the unrolled
+        // element loop each element ended its own basic block, and the
+        // exponentials and reciprocals of neighbouring elements could not overlap
+        if (p.conv_q_w) prologue(rq, oq, hq, wlq, std::true_type{});
+        else prologue(rq, oq, hq, wlq, std::false_type{});
+        if (p.conv_k_w) prologue(rk, ok, hk, wlk, std::true_type{});
+        else prologue(rk, ok, hk, wlk, std::false_type{});
       }
 #pragma unroll
       for (int pc = 0; pc < 8; ++pc) cvt_raw4(dl[pc], rla[pc]);

@@ -98,9 +98,6 @@ __device__ __forceinline__ float wave_sum(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
-// 1 / (1 + e^-x) with the hardware reciprocal
-__device__ __forceinline__ float sigmoid_rcp(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
-
 template <typename E>
 __device__ __forceinline__ float lds_elem(const unsigned char* base, int row, int j) {
   return to_f32(reinterpret_cast<const E*>(base)[row * D + j]);
@@ -239,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
       float s = x3;
       if (conv) {
         const float c = w4[0] * x0 + w4[1] * x1 + w4[2] * x2 + w4[3] * x3;
-        s = c * sigmoid_rcp(c);
+        s = c * sigmoidf_fast(c);
         x0 = x1;
         x1 = x2;
         x2 = x3;
@@ -428,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
         float o = ov[t];
         if (EPI) {
           const float inv = rsqrtf((sSS[t] + sSS[LP + t]) * (1.f / D) + p.rms_eps);
-          o = o * inv * nw * sigmoid_rcp(to_f32(sGt[t * D + c]));
+          o = o * inv * nw * sigmoidf_fast(to_f32(sGt[t * D + c]));
         }
         go[((size_t)(n * L + t) * H + h) * D + c] = from_f32<E>(o);
       }
