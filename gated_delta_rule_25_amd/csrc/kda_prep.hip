@@ -97,6 +97,24 @@ __device__ __forceinline__ float row_suffix_excl(float x) {
   x += row_shl<8>(x);
   return x;
 }
+// The same two sums within one 8-lane half of a row, for inputs that are zero
+// in the other half: the prefix over lanes 8 .. r (for r >= 8) and the
+// exclusive suffix over lanes r + 1 .. 7 (for r < 8).  Eight lanes need one
+// doubling step less; the lanes the shorter span reaches beyond the half hold
+// zeros.
+__device__ __forceinline__ float row_scan_upper(float x) {
+  x += row_shr<1>(x);
+  x += row_shr<2>(x);
+  x += row_shr<4>(x);
+  return x;
+}
+__device__ __forceinline__ float row_suffix_excl_lower(float x) {
+  x = row_shl<1>(x);
+  x += row_shl<1>(x);
+  x += row_shl<2>(x);
+  x += row_shl<4>(x);
+  return x;
+}
 
 // Piece pc = 2 s + h of a lane's channels: channels 32 s + 16 h + 4 g + {0..3}.
 __device__ __forceinline__ int piece_ch(int pc, int g) { return 32 * (pc >> 1) + 16 * (pc & 1) + 4 * g; }
@@ -577,22 +595,24 @@ __global__ __launch_bounds__(4 * C, 2) void prep_kernel(const PrepArgs p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float l2 = dl[2 * st + (e >> 2)][e & 3] * LOG2E;
-          const float pre = row_scan(r >= 8 ? l2 : 0.f);         // g_i - g_7, rows 8..15
-          const float suf = row_suffix_excl(r < 8 ? l2 : 0.f);  // g_7 - g_j, columns 0..7
-          const float fr = r >= 8 ? exp2_fast(pre) : 0.f;
-          const float fc = r < 8 ? exp2_fast(suf) : 0.f;
+          const float pre = row_scan_upper(r >= 8 ? l2 : 0.f);         // g_i - g_7, rows 8..15
+          const float suf = row_suffix_excl_lower(r < 8 ? l2 : 0.f);  // g_7 - g_j, columns 0..7
+          const float f = exp2_fast(r >= 8 ? pre : suf);               // a lane needs one of the two
+          const float fr = r >= 8 ? f : 0.f;
+          const float fc = r < 8 ? f : 0.f;
           xr[e] = k8[e] * fr;
           xs_q[2 * st + (e >> 2)][e & 3] = q8[e] * fr;
           xs_c[2 * st + (e >> 2)][e & 3] = k8[e] * fc;
           const float al = exp2_fast(l2);  // alpha_i
-          float ed = al;                   // e^{g_i - g_{i-1}}
           gp_d[0] += q8[e] * k8[e];
+          // u = k_{i-d} e^{g_i - g_{i-d}}, one distance further per step: the
+          // lane below's value times alpha_i (zero where i - d < 0)
+          float u = k8[e];
           static_for<1, 8>([&](auto D) {
             constexpr int d = decltype(D)::value;
-            if constexpr (d >= 2) ed *= row_shr<d - 1>(al);  // e^{g_i - g_{i-d}}
-            const float t = row_shr<d>(k8[e]) * ed;          // k_{i-d} e^{g_i - g_{i-d}}
-            ga_d[d] += k8[e] * t;
-            gp_d[d] += q8[e] * t;
+            u = al * row_shr<1>(u);
+            ga_d[d] += k8[e] * u;
+            gp_d[d] += q8[e] * u;
           });
         }
         Frag<E> mk, mqh, mql, mch, mcl;
