@@ -61,7 +61,7 @@ constexpr int PS = D + 4;   // padded row stride (floats) of the MFMA A / B oper
 // Dynamic LDS of one workgroup for L cached tokens, LP = 8 or 16 block rows
 // (byte offsets, all multiples of 16).
 struct ReplayLayout {
-  uint32_t RQ, RK, SGP, SG, RV, RG, RLA, PX, PY, SP, SKH, SGAM, SSC, SSS, BYTES;
+  uint32_t RQ, RK, SGP, SG, RV, RG, RLA, PX, PY, SP, SKH, SGAM, SSC, BYTES;
   __host__ __device__ ReplayLayout(int L, int es, bool gate, int LP) {
     const uint32_t rb = 128u * (uint32_t)es;
     RQ = 0;                                       // E [3 + L][128]: raw q, history rows then tokens
@@ -79,8 +79,7 @@ struct ReplayLayout {
     SKH = SP + (uint32_t)(2 * LP) * PS * 4u;      // f32 [LP][PS] K^, or Kb with unbounded decay (rows >= nt zero)
     SGAM = SKH + (uint32_t)LP * PS * 4u;          // f32 [128] D_last
     SSC = SGAM + 512u;                            // f32 [LP][4] 1/|q|, 1/|k|, -, beta
-    SSS = SSC + (uint32_t)LP * 16u;               // f32 [2][LP] sums of squares of o
-    BYTES = SSS + (uint32_t)LP * 8u;
+    BYTES = SSC + (uint32_t)LP * 16u;
   }
 };
 
@@ -104,7 +103,7 @@ __device__ __forceinline__ float lds_elem(const unsigned char* base, int row, in
 }
 
 template <typename E, int LP, bool PRO, bool EPI>
-__global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LP == 8 ? 3 : 1))) void replay_kernel(const ReplayArgs p) {
   constexpr int ES = (int)sizeof(E);
   constexpr int RP = D * ES / 16;  // 16-byte pieces of one row in the I/O dtype
   constexpr int LP4 = D * 4 / 16;  // pieces of one log_alpha row
@@ -170,10 +169,13 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
   }
   float bt = 0.f;
   if (tid < nt) bt = p.beta[((size_t)n * L + tid) * H + h];
-  // RMSNorm weight of column tid (read here so that the output stores at
-  // the end never wait behind a late load)
-  float nw = 1.f;
-  if (EPI && p.norm_w && tid < D) nw = p.norm_w[tid];
+  // RMSNorm weights of the four value columns this thread outputs (read
+  // here so that the output stores at the end never wait behind a late load)
+  const int cc = 4 * (tid & 31);
+  float nw[4] = {1.f, 1.f, 1.f, 1.f};
+  if (EPI && p.norm_w)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) nw[e] = p.norm_w[cc + e];
   // convolution taps of channel j of the branch this thread forms (q: threads 0..127, k: 128..255)
   const int j = tid & 127;
   const bool isk = tid >= 128;
@@ -214,7 +216,6 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
   float* sSC = reinterpret_cast<float*>(smem + lay.SSC);
   float* sGP = reinterpret_cast<float*>(smem + lay.SGP);
   float* sG = reinterpret_cast<float*>(smem + lay.SG);
-  float* sSS = reinterpret_cast<float*>(smem + lay.SSS);
   const float* sLA = reinterpret_cast<const float*>(smem + lay.RLA);
   if (tid < nt) sSC[4 * tid + 3] = bt;
   __syncthreads();
@@ -374,63 +375,87 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(const ReplayArgs p) {
     sG[i] = sGP[i] + sGP[2 * LP * 16 + i] + sGP[4 * LP * 16 + i] + sGP[6 * LP * 16 + i];
   __syncthreads();
 
-  // per column: u by forward substitution, then the outputs
+  // ---- the block's triangular system, for every value column at once ----
+  // u_t = beta_t (v_t - X_t - sum_{r<t} G_K[t][r] u_r) reads U = T (V - X)
+  // with T = (I + Diag(beta) G_K)^{-1} Diag(beta), and o_t = Y_t +
+  // sum_{r<=t} G_Q[t][r] u_r reads O = Y + M (V - X) with M = G_Q T.  Lane j
+  // of wave 0 solves column j of T by forward substitution and forms column
+  // j of M; rows past nt are zero, their beta being zero.  Then every thread
+  // takes value columns cc .. cc + 3 of token rows tr, tr + 8, ...: independent
+  // dot products over the LP block rows (T and M are lower triangular, so the
+  // terms above the diagonal are exact zeros), a token's RMS sum over the 32
+  // lanes that hold its row, and one 8- or 16-byte store per output row.
   E* go = static_cast<E*>(p.o);
   const E* sV = reinterpret_cast<const E*>(smem + lay.RV);
   const E* sGt = reinterpret_cast<const E*>(smem + lay.RG);
-  float* sU = sP;  // [LP][128]: the [K~; Q~] block is no longer read
-  float ov[LP];
-  if (tid < D) {
-    const int c = tid;
-    float uu[LP];
+  float* sU = sP;           // [LP][128]: the [K~; Q~] block is no longer read
+  float* sT = sGP;          // [LP][16]: the partial Gram products are summed
+  float* sM = sGP + LP * 16;  // [LP][16]
+  float* sW = sX;           // [LP][128] V - X over X, zero past nt
+  if (wv == 0) {
+    const int jc = lane;
+    float x[LP];
 #pragma unroll
     for (int t = 0; t < LP; ++t) {
-      float s = 0.f;
-      if (t < nt) {
-        s = to_f32(sV[t * D + c]) - sX[t * D + c];
+      float s = (t == jc) ? 1.f : 0.f;
 #pragma unroll
-        for (int r = 0; r < t; ++r) s -= sG[t * 16 + r] * uu[r];
-        s *= sSC[4 * t + 3];
-      }
-      uu[t] = s;
+      for (int r = 0; r < t; ++r) s -= sG[t * 16 + r] * x[r];
+      x[t] = t < nt ? s * sSC[4 * t + 3] : 0.f;
     }
-#pragma unroll
-    for (int t = 0; t < LP; ++t) sU[t * D + c] = uu[t];
-    if (go) {
+    if (jc < LP)
 #pragma unroll
       for (int t = 0; t < LP; ++t) {
-        float o = 0.f;
-        if (t < nt) {
-          o = sY[t * D + c];
+        float m = 0.f;
 #pragma unroll
-          for (int r = 0; r <= t; ++r) o += sG[(LP + t) * 16 + r] * uu[r];
-        }
-        ov[t] = o;
+        for (int r = 0; r <= t; ++r) m += sG[(LP + t) * 16 + r] * x[r];
+        sT[t * 16 + jc] = x[t];
+        sM[t * 16 + jc] = m;
       }
-      if (EPI) {
+  }
+  constexpr int TPT = LP / 8;  // token rows per thread
+  const int tr = tid >> 5;
 #pragma unroll
-        for (int t = 0; t < LP; ++t) {
-          const float ss = wave_sum(ov[t] * ov[t]);
-          if (lane == 0) sSS[wv * LP + t] = ss;
-        }
-      }
+  for (int q = 0; q < TPT; ++q) {
+    const int t = tr + 8 * q;
+    f32x4 w = {0.f, 0.f, 0.f, 0.f};
+    if (t < nt) {  // V's rows past nt were never loaded
+      Frag16<E> vf;
+      ld_frag16(vf, sV + t * D + cc);
+      w = frag16_to_f32(vf) - *reinterpret_cast<const f32x4*>(sX + t * D + cc);
     }
+    *reinterpret_cast<f32x4*>(sW + t * D + cc) = w;
   }
   __syncthreads();
-  if (tid < D && go) {
-    const int c = tid;
 #pragma unroll
-    for (int t = 0; t < LP; ++t) {
-      if (t < nt) {
-        float o = ov[t];
-        if (EPI) {
-          const float inv = rsqrtf((sSS[t] + sSS[LP + t]) * (1.f / D) + p.rms_eps);
-          o = o * inv * nw * sigmoidf_fast(to_f32(sGt[t * D + c]));
+  for (int q = 0; q < TPT; ++q) {
+    const int t = tr + 8 * q;
+    f32x4 o = *reinterpret_cast<const f32x4*>(sY + t * D + cc);
+    f32x4 uu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < LP; ++r) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(sW + r * D + cc);
+      o += sM[t * 16 + r] * w;
+      if (commit) uu += sT[t * 16 + r] * w;
+    }
+    if (commit) *reinterpret_cast<f32x4*>(sU + t * D + cc) = uu;
+    if (go) {
+      if constexpr (EPI) {
+        float ss = (o[0] * o[0] + o[1] * o[1]) + (o[2] * o[2] + o[3] * o[3]);
+#pragma unroll
+        for (int m = 1; m < 32; m <<= 1) ss += __shfl_xor(ss, m);
+        const float inv = rsqrtf(ss * (1.f / D) + p.rms_eps);
+        if (t < nt) {
+          Frag16<E> gf;
+          ld_frag16(gf, sGt + t * D + cc);
+          const f32x4 gl = frag16_to_f32(gf);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] *= inv * nw[e] * sigmoidf_fast(gl[e]);
         }
-        go[((size_t)(n * L + t) * H + h) * D + c] = from_f32<E>(o);
       }
+      if (t < nt) store_row4(go + ((size_t)(n * L + t) * H + h) * D + cc, o);
     }
   }
+  if (commit) __syncthreads();  // U is read across the threads below
 
   // ---- 4. commit: S = Diag(D_last) S0 + Kb^T U ----
   // The contraction runs over the LP block rows, four per instruction: lane
