@@ -41,8 +41,8 @@
 //      channels; section 4.2.3) and the decay products D_t, giving K~, Q~,
 //      K^ (and Kb, D_last when committing);
 //   3. [X; Y] = [K~; Q~] S0 and G on fp32 MFMA (v_mfma_f32_16x16x4_f32);
-//      per column the substitution for u and the outputs, then RMSNorm x
-//      sigmoid(gate) (section 4.2.6);
+//      the substitution solved once for all columns (T and M below), the
+//      outputs O = Y + M (V - X), then RMSNorm x sigmoid(gate) (section 4.2.6);
 //   4. when a state output is given: S = Diag(D_last) S0 + Kb^T U on MFMA,
 //      the state store, and the three raw rows before the next token.
 // All arithmetic is fp32.  The state is read once and written at most once
