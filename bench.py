@@ -150,7 +150,7 @@ TRAFFIC_PASSES = {
     "prefill7": (["--only-prefill", "--workload", "7", "--steps", "2", "--warmup", "1"], 5),
     "decode": (["--only-decode", "--decode-steps", "4"], 8),
     "replay": (["--only-replay", "--replay-rounds", "2"], 4),
-    "backward": (["--only-backward", "--backward-steps", "1"], 2),
+    "backward": (["--only-backward", "--backward-steps", "1", "--no-training-step"], 2),
 }
 
 
@@ -364,6 +364,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--only-backward", action="store_true", help="time only the backward pass (profiling)")
+    ap.add_argument("--no-training-step", action="store_true",
+                    help="skip the forward + backward comparison in the backward leg (counter passes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--record-traffic", metavar="DIR",
@@ -493,7 +495,8 @@ def main():
         torch.cuda.empty_cache()
 
     if not args.no_backward:
-        result["backward"] = time_backward(kda, kda_inputs, args.backward_steps, dev, stream)
+        result["backward"] = time_backward(kda, kda_inputs, args.backward_steps, dev, stream,
+                                           training_step=not args.no_training_step)
         if args.only_backward:
             result.update({"metric": "KDA backward tokens/s", "unit": "tokens/s",
                            "value": result["backward"]["tokens_per_s"]})
@@ -508,7 +511,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def time_backward(kda, kda_inputs, steps, dev, stream):
+def time_backward(kda, kda_inputs, steps, dev, stream, training_step=True):
     """kda_chunk_bwd over the one-layer workload (H=96, T=8192, bf16, S0 and
     d_final_state given): one warm-up call, then `steps` calls, each bracketed
     by HIP events on the stream the kernels run on."""
@@ -546,7 +549,43 @@ def time_backward(kda, kda_inputs, steps, dev, stream):
            "mfma": {"algorithmic_flops": flops, "chunk": C, "achieved_tflops": tfl,
                     "bf16_peak_tflops": MFMA_BF16_PEAK_TFLOPS, "fp32_peak_tflops": MFMA_FP32_PEAK_TFLOPS,
                     "attainable_tflops_bf16": min(MFMA_BF16_PEAK_TFLOPS, flops / b * HBM_PEAK_GBPS / 1e3)}}
-    del inp, d_o, dsT, ws
+
+    if not training_step:
+        del inp, d_o, dsT, ws
+        return res
+    # A training step both ways on the same inputs: kda_chunk_fwd + kda_chunk_bwd
+    # (the backward recomputes the chunk states), and kda_chunk_fwd_save +
+    # kda_chunk_bwd_saved (the forward leaves them in the backward's workspace).
+    o = torch.empty_like(inp["q"])
+    fs = torch.empty_like(inp["initial_state"])
+
+    def fwd():
+        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["initial_state"], out=o,
+                      final_state=fs)
+
+    def fwd_save():
+        kda.chunk_fwd_save(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["initial_state"], out=o,
+                           final_state=fs, workspace=ws)
+
+    def bwd_saved():
+        return kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], d_o,
+                             initial_state=inp["initial_state"], d_final_state=dsT, saved=ws)
+
+    fwd_save()
+    bwd_saved()
+    torch.cuda.synchronize()
+    f_ms = sum(time_events(fwd, steps, stream)) / steps
+    fs_ms = sum(time_events(fwd_save, steps, stream)) / steps
+    fwd_save()
+    torch.cuda.synchronize()
+    bs_ms = sum(time_events(bwd_saved, steps, stream)) / steps
+    res["training_step"] = {"forward_ms": f_ms, "recompute_ms_per_step": f_ms + ms,
+                            "forward_save_ms": fs_ms, "backward_saved_ms": bs_ms, "saved_ms_per_step": fs_ms + bs_ms,
+                            "tokens_per_s_saved": T * 1e3 / (fs_ms + bs_ms),
+                            "note": "forward + backward of one layer: kda_chunk_fwd + kda_chunk_bwd against "
+                                    "kda_chunk_fwd_save + kda_chunk_bwd_saved (residuals kept in the backward's "
+                                    "workspace between them)"}
+    del inp, d_o, dsT, ws, o, fs
     return res
 
 

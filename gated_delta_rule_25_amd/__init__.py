@@ -21,7 +21,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_bwd", "chunk_bwd_workspace_bytes", "chunk_kda", "decode_step",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_fwd_save", "chunk_bwd", "chunk_bwd_workspace_bytes", "chunk_kda",
+           "decode_step",
            "decode_replay", "chunk_fwd_workspace_bytes", "status_string", "KDAError", "last_precondition_flags",
            "library_path", "D", "REPLAY_MAX_TOKENS"]
 
@@ -79,6 +80,10 @@ def _load():
     lib.kda_chunk_bwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32]
     lib.kda_chunk_bwd.restype = i32
     lib.kda_chunk_bwd.argtypes = [vp] * 9 + [i32, i64, i32, i32, i32, i32] + [vp] * 7 + [sz, vp]
+    lib.kda_chunk_bwd_saved.restype = i32
+    lib.kda_chunk_bwd_saved.argtypes = [vp] * 9 + [i32, i64, i32, i32, i32, i32] + [vp] * 7 + [sz, vp]
+    lib.kda_chunk_fwd_save.restype = i32
+    lib.kda_chunk_fwd_save.argtypes = [vp] * 7 + [i32, i64, i32, i32, i32, i32] + [vp] * 3 + [sz, vp]
     lib.kda_decode_step.restype = i32
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.kda_last_precondition_flags.restype = ctypes.c_uint32
@@ -210,10 +215,63 @@ def chunk_bwd_workspace_bytes(num_seqs: int, total_tokens: int, num_heads: int,
     return int(_load().kda_chunk_bwd_workspace_bytes(num_seqs, total_tokens, num_heads, D, D, _DTYPES[dtype]))
 
 
+def chunk_fwd_save(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor, beta: torch.Tensor,
+                   initial_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None, *,
+                   out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                   output_final_state: bool = True, workspace: Optional[torch.Tensor] = None):
+    """Forward pass for training (kda_chunk_fwd_save): (o, final_state,
+    workspace), o and final_state as chunk_fwd gives them without fused
+    options, and workspace the backward's residuals, to be passed unchanged
+    as chunk_bwd(..., saved=workspace) for the same inputs.  final_state may
+    be initial_state (in place)."""
+    lib = _load()
+    if q.dim() != 3 or q.shape[2] != D:
+        raise ValueError("q must be [T, H, 128]")
+    T, H, _ = q.shape
+    dev, dt = q.device, q.dtype
+    if dt not in _DTYPES:
+        raise TypeError("q/k/v must be float32 or bfloat16")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, (T, H, D), dt, dev)
+    _check(log_alpha, "log_alpha", (T, H, D), torch.float32, dev)
+    _check(beta, "beta", (T, H), torch.float32, dev)
+    if cu_seqlens is None:
+        N = 1
+    else:
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be [N+1]")
+        N = cu_seqlens.numel() - 1
+        _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (N, H, D, D), torch.float32, dev)
+    if out is None:
+        out = torch.empty((T, H, D), dtype=dt, device=dev)
+    _check(out, "out", (T, H, D), dt, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", (N, H, D, D), torch.float32, dev)
+    dtc = _DTYPES[dt]
+    need = int(lib.kda_chunk_bwd_workspace_bytes(N, T, H, D, D, dtc))
+    if need == 0:
+        raise ValueError("chunk_fwd_save: unsupported sizes")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    rc = lib.kda_chunk_fwd_save(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
+                                _ptr(cu_seqlens), N, T, H, D, D, dtc, _ptr(out), _ptr(final_state), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(dev))
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_chunk_fwd_save")
+    return out, final_state, workspace
+
+
 def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor, beta: torch.Tensor,
               d_o: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
               cu_seqlens: Optional[torch.Tensor] = None, d_final_state: Optional[torch.Tensor] = None, *,
-              need_d_initial_state: bool = True, workspace: Optional[torch.Tensor] = None):
+              need_d_initial_state: bool = True, workspace: Optional[torch.Tensor] = None,
+              saved: Optional[torch.Tensor] = None):
     """Gradients of sum <d_o, o> + <d_final_state, S_T> through chunk_fwd
     (kda_chunk_bwd; no fused prologue or epilogue, log_alpha in [-5, 0]).
 
@@ -221,7 +279,8 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
     [N, H, 128, 128] float32 or None (zero).  Returns (dq, dk, dv, dlog_alpha,
     dbeta, d_initial_state) with the shapes and dtypes of q, k, v, log_alpha,
     beta and the initial state (float32; None when need_d_initial_state is
-    False)."""
+    False).  saved: the workspace chunk_fwd_save returned for these inputs
+    (kda_chunk_bwd_saved: the forward is not recomputed; the same bits)."""
     lib = _load()
     if q.dim() != 3 or q.shape[2] != D:
         raise ValueError("q must be [T, H, 128]")
@@ -253,25 +312,35 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
     need = int(lib.kda_chunk_bwd_workspace_bytes(N, T, H, D, D, dtc))
     if need == 0:
         raise ValueError("chunk_bwd: unsupported sizes")
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    rc = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
-                           _ptr(cu_seqlens), _ptr(d_o), _ptr(d_final_state), N, T, H, D, D, dtc, _ptr(dq), _ptr(dk),
-                           _ptr(dv), _ptr(dla), _ptr(db), _ptr(ds0), _ptr(workspace),
-                           workspace.numel() * workspace.element_size(), _stream(dev))
+    if saved is not None:
+        if saved.device != dev or saved.numel() * saved.element_size() < need:
+            raise ValueError("chunk_bwd: saved must be the workspace chunk_fwd_save returned for these inputs")
+        workspace, fn, name = saved, lib.kda_chunk_bwd_saved, "kda_chunk_bwd_saved"
+    else:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        fn, name = lib.kda_chunk_bwd, "kda_chunk_bwd"
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens), _ptr(d_o),
+            _ptr(d_final_state), N, T, H, D, D, dtc, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dla), _ptr(db), _ptr(ds0),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
     if rc != KDA_OK:
-        raise KDAError(rc, "kda_chunk_bwd")
+        raise KDAError(rc, name)
     return dq, dk, dv, dla, db, ds0
 
 
 class _ChunkKDA(torch.autograd.Function):
     """chunk_fwd forward, chunk_bwd backward (the plain recurrence with the
-    bounded decay).  The forward saves only its inputs; the backward
-    recomputes the chunk states."""
+    bounded decay).  By default the forward saves only its inputs and the
+    backward recomputes the chunk states; with save_residuals the forward is
+    chunk_fwd_save and the backward starts from its workspace."""
 
     @staticmethod
-    def forward(ctx, q, k, v, log_alpha, beta, initial_state, cu_seqlens):
-        o, final_state = chunk_fwd(q, k, v, log_alpha, beta, initial_state, cu_seqlens, output_final_state=True)
+    def forward(ctx, q, k, v, log_alpha, beta, initial_state, cu_seqlens, save_residuals):
+        ctx.residuals = None
+        if save_residuals:
+            o, final_state, ctx.residuals = chunk_fwd_save(q, k, v, log_alpha, beta, initial_state, cu_seqlens)
+        else:
+            o, final_state = chunk_fwd(q, k, v, log_alpha, beta, initial_state, cu_seqlens, output_final_state=True)
         ctx.save_for_backward(q, k, v, log_alpha, beta, initial_state, cu_seqlens)
         ctx.mark_non_differentiable(*(t for t in (cu_seqlens,) if t is not None))
         return o, final_state
@@ -286,18 +355,22 @@ class _ChunkKDA(torch.autograd.Function):
             d_final_state = d_final_state.to(torch.float32).contiguous()
         need_ds0 = initial_state is not None and ctx.needs_input_grad[5]
         dq, dk, dv, dla, db, ds0 = chunk_bwd(q, k, v, log_alpha, beta, d_o, initial_state, cu_seqlens, d_final_state,
-                                             need_d_initial_state=need_ds0)
-        return dq, dk, dv, dla, db, ds0, None
+                                             need_d_initial_state=need_ds0, saved=ctx.residuals)
+        ctx.residuals = None
+        return dq, dk, dv, dla, db, ds0, None, None
 
 
 def chunk_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor, beta: torch.Tensor,
-              initial_state: Optional[torch.Tensor] = None,
-              cu_seqlens: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+              initial_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None, *,
+              save_residuals: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """Differentiable KDA prefill (torch.autograd): (o, final_state) as
     chunk_fwd, with gradients for q, k, v, log_alpha, beta and the initial
     state from chunk_bwd.  Plain recurrence only (no fused prologue or
-    epilogue), log_alpha in [-5, 0]."""
-    return _ChunkKDA.apply(q, k, v, log_alpha, beta, initial_state, cu_seqlens)
+    epilogue), log_alpha in [-5, 0].  save_residuals keeps the backward's
+    workspace (chunk_bwd_workspace_bytes) from the forward to the backward
+    instead of recomputing the chunk states: faster, and that much memory
+    held in between."""
+    return _ChunkKDA.apply(q, k, v, log_alpha, beta, initial_state, cu_seqlens, save_residuals)
 
 
 def _prefill_args(q, k, v, log_alpha, beta, initial_state, cu_seqlens, conv_q_w, conv_k_w, gate, norm_w, l2_eps,

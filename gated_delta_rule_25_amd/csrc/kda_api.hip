@@ -537,11 +537,151 @@ size_t kda_chunk_bwd_workspace_bytes(int num_seqs, int64_t total_tokens, int num
   return make_bwd_plan(num_seqs, total_tokens, num_heads, dtype).bytes;
 }
 
-kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
-                         const float* initial_state, const int32_t* cu_seqlens, const void* d_o,
-                         const float* d_final_state, int num_seqs, int64_t total_tokens, int num_heads, int d_k,
-                         int d_v, kda_dtype dtype, void* dq, void* dk, void* dv, float* dlog_alpha, float* dbeta,
-                         float* d_initial_state, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// Debug check of the backward's and the training forward's inputs (the
+// decay bound of the plain prefill).
+kda_status bwd_input_checks(const void* q, const void* k, const float* log_alpha, const float* beta,
+                            const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens, int num_heads, bool bf16,
+                            hipStream_t stream) {
+  kda::CheckArgs chk;
+  std::memset(&chk, 0, sizeof(chk));
+  chk.rows = total_tokens * num_heads;
+  chk.heads = num_heads;
+  chk.tokens_per_seq = 1;
+  chk.log_alpha = log_alpha;
+  chk.beta = beta;
+  chk.q = q;
+  chk.k = k;
+  chk.cu = cu_seqlens;
+  chk.num_seqs = num_seqs;
+  chk.total_tokens = total_tokens;
+  chk.bf16 = bf16;
+  chk.la_min = kBoundedLaMin;
+  return checked(chk, stream);
+}
+
+// The longest-first order and the window table (one window over every
+// chunk) in the backward's workspace, from cu_seqlens.
+kda_status bwd_tables(const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens, bool bf16, const BwdPlan& pl,
+                      char* ws, hipStream_t stream) {
+  int32_t* order = num_seqs > 1 ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  if (num_seqs > 1 && kda::launch_worklist(cu_seqlens, num_seqs, order, stream) != hipSuccess) return KDA_ERR_HIP;
+  if (kda::launch_window_table(cu_seqlens, num_seqs, total_tokens, kda::chunk_len(bf16), 1, 0, (int)pl.slots,
+                               reinterpret_cast<int32_t*>(ws + pl.off_first), reinterpret_cast<int32_t*>(ws + pl.off_c0),
+                               reinterpret_cast<int32_t*>(ws + pl.off_c1), stream) != hipSuccess)
+    return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+// The backward's residuals in its workspace: the tables above, the forward
+// factor blocks and, per chunk, the incoming state and U (carry pass 3).
+// With o given (the training forward) the same walk also writes the outputs
+// and the final state (carry pass 4).
+kda_status bwd_residuals(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                         const float* initial_state, const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens,
+                         int num_heads, bool bf16, const BwdPlan& pl, char* ws, void* o, float* final_state,
+                         hipStream_t stream) {
+  const kda_status ts = bwd_tables(cu_seqlens, num_seqs, total_tokens, bf16, pl, ws, stream);
+  if (ts != KDA_OK) return ts;
+  int32_t* order = num_seqs > 1 ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  int32_t* seq_first = reinterpret_cast<int32_t*>(ws + pl.off_first);
+  int32_t* seq_c0 = reinterpret_cast<int32_t*>(ws + pl.off_c0);
+  int32_t* seq_c1 = reinterpret_cast<int32_t*>(ws + pl.off_c1);
+  void* factors = ws + pl.off_factors;
+  kda::PrepArgs pa;
+  std::memset(&pa, 0, sizeof(pa));
+  pa.q = q;
+  pa.k = k;
+  pa.v = v;
+  pa.log_alpha = log_alpha;
+  pa.beta = beta;
+  pa.cu = cu_seqlens;
+  pa.l2_eps = 1e-6f;
+  pa.num_seqs = num_seqs;
+  pa.num_heads = num_heads;
+  pa.total_tokens = total_tokens;
+  pa.bf16 = bf16;
+  pa.seq_first = seq_first;
+  pa.seq_c0 = seq_c0;
+  pa.cap = (int)pl.slots;
+  pa.chunks_per_block = kPrepChunksPerBlock;
+  pa.factors = factors;
+  if (kda::launch_prep(pa, stream) != hipSuccess) return KDA_ERR_HIP;
+  kda::CarryArgs ca;
+  std::memset(&ca, 0, sizeof(ca));
+  ca.factors = factors;
+  ca.cu = cu_seqlens;
+  ca.order = order;
+  ca.seq_first = seq_first;
+  ca.seq_c0 = seq_c0;
+  ca.seq_c1 = seq_c1;
+  ca.state_in = initial_state;
+  ca.state_out = o ? final_state : nullptr;
+  ca.o = o;
+  ca.rms_eps = 1e-6f;
+  ca.num_seqs = num_seqs;
+  ca.num_heads = num_heads;
+  ca.total_tokens = total_tokens;
+  ca.units = num_seqs * num_heads;
+  ca.col_split = 2;
+  ca.bf16 = bf16;
+  ca.pass = o ? 4 : 3;
+  ca.chunk_states = ws + pl.off_states;
+  ca.chunk_u = ws + pl.off_u;
+  if (kda::launch_carry(ca, stream) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+// The gradients from the residuals: reverse-carry blocks, the reverse carry,
+// the per-chunk gradients.
+kda_status bwd_gradients(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                         const int32_t* cu_seqlens, const void* d_o, const float* d_final_state, int num_seqs,
+                         int64_t total_tokens, int num_heads, bool bf16, const BwdPlan& pl, char* ws, void* dq,
+                         void* dk, void* dv, float* dlog_alpha, float* dbeta, float* d_initial_state,
+                         hipStream_t stream) {
+  kda::BwdArgs ba;
+  std::memset(&ba, 0, sizeof(ba));
+  ba.q = q;
+  ba.k = k;
+  ba.v = v;
+  ba.log_alpha = log_alpha;
+  ba.beta = beta;
+  ba.d_o = d_o;
+  ba.d_final_state = d_final_state;
+  ba.cu = cu_seqlens;
+  ba.order = num_seqs > 1 ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  ba.seq_first = reinterpret_cast<int32_t*>(ws + pl.off_first);
+  ba.num_seqs = num_seqs;
+  ba.num_heads = num_heads;
+  ba.total_tokens = total_tokens;
+  ba.slots = (int)pl.slots;
+  ba.bf16 = bf16;
+  ba.factors = ws + pl.off_factors;
+  ba.dblocks = ws + pl.off_dblocks;
+  ba.chunk_states = ws + pl.off_states;
+  ba.chunk_u = ws + pl.off_u;
+  ba.chunk_ds = ws + pl.off_ds;
+  ba.chunk_du = ws + pl.off_du;
+  ba.dq = dq;
+  ba.dk = dk;
+  ba.dv = dv;
+  ba.dlog_alpha = dlog_alpha;
+  ba.dbeta = dbeta;
+  ba.d_initial_state = d_initial_state;
+  if (kda::launch_bwd_prep(ba, stream) != hipSuccess) return KDA_ERR_HIP;
+  if (kda::launch_bwd_carry(ba, stream) != hipSuccess) return KDA_ERR_HIP;
+  if (kda::launch_bwd_grad(ba, stream) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+// Argument checks of kda_chunk_bwd and kda_chunk_bwd_saved.
+kda_status bwd_args_ok(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                       const float* initial_state, const int32_t* cu_seqlens, const void* d_o,
+                       const float* d_final_state, int num_seqs, int64_t total_tokens, int num_heads, int d_k,
+                       int d_v, kda_dtype dtype, const void* dq, const void* dk, const void* dv,
+                       const float* dlog_alpha, const float* dbeta, const float* d_initial_state,
+                       const void* workspace, size_t workspace_bytes) {
   if (num_seqs < 1 || num_heads < 1 || total_tokens < 0) return KDA_ERR_INVALID_ARG;
   if (d_k != kD || d_v != kD || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
   if (!cu_seqlens && num_seqs != 1) return KDA_ERR_INVALID_ARG;
@@ -581,111 +721,100 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const floa
     for (int j = i + 1; j < kOuts; ++j)
       if (overlap(outs[i], outs[j])) return KDA_ERR_INVALID_ARG;
   }
-  const bool bf16 = dtype == KDA_DTYPE_BF16;
-  {
-    kda::CheckArgs chk;
-    std::memset(&chk, 0, sizeof(chk));
-    chk.rows = total_tokens * num_heads;
-    chk.heads = num_heads;
-    chk.tokens_per_seq = 1;
-    chk.log_alpha = log_alpha;
-    chk.beta = beta;
-    chk.q = q;
-    chk.k = k;
-    chk.cu = cu_seqlens;
-    chk.num_seqs = num_seqs;
-    chk.total_tokens = total_tokens;
-    chk.bf16 = bf16;
-    chk.la_min = kBoundedLaMin;
-    const kda_status cs = checked(chk, stream);
-    if (cs != KDA_OK) return cs;
-  }
-
-  char* ws = static_cast<char*>(workspace);
-  int32_t* order = num_seqs > 1 ? reinterpret_cast<int32_t*>(ws) : nullptr;
-  int32_t* seq_first = reinterpret_cast<int32_t*>(ws + pl.off_first);
-  int32_t* seq_c0 = reinterpret_cast<int32_t*>(ws + pl.off_c0);
-  int32_t* seq_c1 = reinterpret_cast<int32_t*>(ws + pl.off_c1);
-  void* factors = ws + pl.off_factors;
-  void* chunk_states = ws + pl.off_states;
-  void* chunk_u = ws + pl.off_u;
-  if (num_seqs > 1 && kda::launch_worklist(cu_seqlens, num_seqs, order, stream) != hipSuccess) return KDA_ERR_HIP;
-  if (kda::launch_window_table(cu_seqlens, num_seqs, total_tokens, kda::chunk_len(bf16), 1, 0, (int)pl.slots,
-                               seq_first, seq_c0, seq_c1, stream) != hipSuccess)
-    return KDA_ERR_HIP;
-  // forward factors and, per chunk, the incoming state and U (states pass)
-  kda::PrepArgs pa;
-  std::memset(&pa, 0, sizeof(pa));
-  pa.q = q;
-  pa.k = k;
-  pa.v = v;
-  pa.log_alpha = log_alpha;
-  pa.beta = beta;
-  pa.cu = cu_seqlens;
-  pa.l2_eps = 1e-6f;
-  pa.num_seqs = num_seqs;
-  pa.num_heads = num_heads;
-  pa.total_tokens = total_tokens;
-  pa.bf16 = bf16;
-  pa.seq_first = seq_first;
-  pa.seq_c0 = seq_c0;
-  pa.cap = (int)pl.slots;
-  pa.chunks_per_block = kPrepChunksPerBlock;
-  pa.factors = factors;
-  if (kda::launch_prep(pa, stream) != hipSuccess) return KDA_ERR_HIP;
-  kda::CarryArgs ca;
-  std::memset(&ca, 0, sizeof(ca));
-  ca.factors = factors;
-  ca.cu = cu_seqlens;
-  ca.order = order;
-  ca.seq_first = seq_first;
-  ca.seq_c0 = seq_c0;
-  ca.seq_c1 = seq_c1;
-  ca.state_in = initial_state;
-  ca.num_seqs = num_seqs;
-  ca.num_heads = num_heads;
-  ca.total_tokens = total_tokens;
-  ca.units = num_seqs * num_heads;
-  ca.col_split = 2;
-  ca.bf16 = bf16;
-  ca.pass = 3;
-  ca.chunk_states = chunk_states;
-  ca.chunk_u = chunk_u;
-  if (kda::launch_carry(ca, stream) != hipSuccess) return KDA_ERR_HIP;
-  // reverse-carry blocks, the reverse carry, the gradients
-  kda::BwdArgs ba;
-  std::memset(&ba, 0, sizeof(ba));
-  ba.q = q;
-  ba.k = k;
-  ba.v = v;
-  ba.log_alpha = log_alpha;
-  ba.beta = beta;
-  ba.d_o = d_o;
-  ba.d_final_state = d_final_state;
-  ba.cu = cu_seqlens;
-  ba.order = order;
-  ba.seq_first = seq_first;
-  ba.num_seqs = num_seqs;
-  ba.num_heads = num_heads;
-  ba.total_tokens = total_tokens;
-  ba.slots = (int)pl.slots;
-  ba.bf16 = bf16;
-  ba.factors = factors;
-  ba.dblocks = ws + pl.off_dblocks;
-  ba.chunk_states = chunk_states;
-  ba.chunk_u = chunk_u;
-  ba.chunk_ds = ws + pl.off_ds;
-  ba.chunk_du = ws + pl.off_du;
-  ba.dq = dq;
-  ba.dk = dk;
-  ba.dv = dv;
-  ba.dlog_alpha = dlog_alpha;
-  ba.dbeta = dbeta;
-  ba.d_initial_state = d_initial_state;
-  if (kda::launch_bwd_prep(ba, stream) != hipSuccess) return KDA_ERR_HIP;
-  if (kda::launch_bwd_carry(ba, stream) != hipSuccess) return KDA_ERR_HIP;
-  if (kda::launch_bwd_grad(ba, stream) != hipSuccess) return KDA_ERR_HIP;
   return KDA_OK;
+}
+
+}  // namespace
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                         const float* initial_state, const int32_t* cu_seqlens, const void* d_o,
+                         const float* d_final_state, int num_seqs, int64_t total_tokens, int num_heads, int d_k,
+                         int d_v, kda_dtype dtype, void* dq, void* dk, void* dv, float* dlog_alpha, float* dbeta,
+                         float* d_initial_state, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const kda_status st = bwd_args_ok(q, k, v, log_alpha, beta, initial_state, cu_seqlens, d_o, d_final_state,
+                                    num_seqs, total_tokens, num_heads, d_k, d_v, dtype, dq, dk, dv, dlog_alpha, dbeta,
+                                    d_initial_state, workspace, workspace_bytes);
+  if (st != KDA_OK) return st;
+  const bool bf16 = dtype == KDA_DTYPE_BF16;
+  const kda_status cs = bwd_input_checks(q, k, log_alpha, beta, cu_seqlens, num_seqs, total_tokens, num_heads, bf16,
+                                         stream);
+  if (cs != KDA_OK) return cs;
+  const BwdPlan pl = make_bwd_plan(num_seqs, total_tokens, num_heads, dtype);
+  char* ws = static_cast<char*>(workspace);
+  const kda_status rs = bwd_residuals(q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs, total_tokens,
+                                      num_heads, bf16, pl, ws, nullptr, nullptr, stream);
+  if (rs != KDA_OK) return rs;
+  return bwd_gradients(q, k, v, log_alpha, beta, cu_seqlens, d_o, d_final_state, num_seqs, total_tokens, num_heads,
+                       bf16, pl, ws, dq, dk, dv, dlog_alpha, dbeta, d_initial_state, stream);
+}
+
+kda_status kda_chunk_fwd_save(const void* q, const void* k, const void* v, const float* log_alpha,
+                              const float* beta, const float* initial_state, const int32_t* cu_seqlens, int num_seqs,
+                              int64_t total_tokens, int num_heads, int d_k, int d_v, kda_dtype dtype, void* o,
+                              float* final_state, void* bwd_workspace, size_t bwd_workspace_bytes,
+                              hipStream_t stream) {
+  if (num_seqs < 1 || num_heads < 1 || total_tokens < 0) return KDA_ERR_INVALID_ARG;
+  if (d_k != kD || d_v != kD || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+  if (!cu_seqlens && num_seqs != 1) return KDA_ERR_INVALID_ARG;
+  if (!bwd_sizes_ok(num_seqs, total_tokens, num_heads, dtype)) return KDA_ERR_INVALID_ARG;
+  if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_INVALID_ARG;
+  {
+    const void* vec[] = {q, k, v, log_alpha, initial_state, o, final_state, bwd_workspace};
+    for (const void* ptr : vec)
+      if (!aligned(ptr, 16)) return KDA_ERR_INVALID_ARG;
+    const void* sca[] = {beta, cu_seqlens};
+    for (const void* ptr : sca)
+      if (!aligned(ptr, 4)) return KDA_ERR_INVALID_ARG;
+  }
+  const BwdPlan pl = make_bwd_plan(num_seqs, total_tokens, num_heads, dtype);
+  if (!bwd_workspace || bwd_workspace_bytes < pl.bytes) return KDA_ERR_WORKSPACE;
+  const size_t es = elem_size(dtype);
+  const size_t tok_elems = (size_t)total_tokens * num_heads * kD;
+  const size_t state_bytes = (size_t)num_seqs * num_heads * kD * kD * sizeof(float);
+  const Range r_s0 = range_of(initial_state, state_bytes);
+  const Range ins[] = {range_of(q, tok_elems * es), range_of(k, tok_elems * es), range_of(v, tok_elems * es),
+                       range_of(log_alpha, tok_elems * sizeof(float)),
+                       range_of(beta, (size_t)total_tokens * num_heads * sizeof(float)), r_s0,
+                       range_of(cu_seqlens, cu_seqlens ? (size_t)(num_seqs + 1) * sizeof(int32_t) : 0)};
+  const Range r_o = range_of(o, tok_elems * es), r_fs = range_of(final_state, final_state ? state_bytes : 0),
+              r_ws = range_of(bwd_workspace, pl.bytes);
+  for (const Range& in : ins) {
+    if (overlap(r_o, in) || overlap(r_ws, in)) return KDA_ERR_INVALID_ARG;
+    if (&in != &ins[5] && overlap(r_fs, in)) return KDA_ERR_INVALID_ARG;
+  }
+  // final_state may be exactly initial_state (in-place continuation)
+  if (overlap(r_fs, r_s0) && !(r_fs.lo == r_s0.lo && r_fs.hi == r_s0.hi)) return KDA_ERR_INVALID_ARG;
+  if (overlap(r_o, r_fs) || overlap(r_o, r_ws) || overlap(r_fs, r_ws)) return KDA_ERR_INVALID_ARG;
+  const bool bf16 = dtype == KDA_DTYPE_BF16;
+  const kda_status cs = bwd_input_checks(q, k, log_alpha, beta, cu_seqlens, num_seqs, total_tokens, num_heads, bf16,
+                                         stream);
+  if (cs != KDA_OK) return cs;
+  return bwd_residuals(q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, bf16,
+                       pl, static_cast<char*>(bwd_workspace), o, final_state, stream);
+}
+
+kda_status kda_chunk_bwd_saved(const void* q, const void* k, const void* v, const float* log_alpha,
+                               const float* beta, const float* initial_state, const int32_t* cu_seqlens,
+                               const void* d_o, const float* d_final_state, int num_seqs, int64_t total_tokens,
+                               int num_heads, int d_k, int d_v, kda_dtype dtype, void* dq, void* dk, void* dv,
+                               float* dlog_alpha, float* dbeta, float* d_initial_state, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  const kda_status st = bwd_args_ok(q, k, v, log_alpha, beta, initial_state, cu_seqlens, d_o, d_final_state,
+                                    num_seqs, total_tokens, num_heads, d_k, d_v, dtype, dq, dk, dv, dlog_alpha, dbeta,
+                                    d_initial_state, workspace, workspace_bytes);
+  if (st != KDA_OK) return st;
+  const bool bf16 = dtype == KDA_DTYPE_BF16;
+  const kda_status cs = bwd_input_checks(q, k, log_alpha, beta, cu_seqlens, num_seqs, total_tokens, num_heads, bf16,
+                                         stream);
+  if (cs != KDA_OK) return cs;
+  // the tables again, from this call's cu_seqlens: the same values for the
+  // forward's inputs, and every slot index within this plan whatever it holds
+  const BwdPlan pl = make_bwd_plan(num_seqs, total_tokens, num_heads, dtype);
+  char* ws = static_cast<char*>(workspace);
+  const kda_status ts = bwd_tables(cu_seqlens, num_seqs, total_tokens, bf16, pl, ws, stream);
+  if (ts != KDA_OK) return ts;
+  return bwd_gradients(q, k, v, log_alpha, beta, cu_seqlens, d_o, d_final_state, num_seqs, total_tokens, num_heads,
+                       bf16, pl, ws, dq, dk, dv, dlog_alpha, dbeta, d_initial_state, stream);
 }
 
 kda_status kda_decode_step(float* state, const void* q, const void* k, const void* v, const float* log_alpha,

@@ -229,7 +229,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
   const int H = p.num_heads;
   const int rnk = u / H, h = u % H;
   // work item: sequence n, chunks [c0, c0 + nch) of it, factor slots from slot0
-  constexpr bool SEQ = PASS == 0 || PASS == 3;  // one work item per (sequence, head)
+  constexpr bool SEQ = PASS == 0 || PASS == 3 || PASS == 4;  // one work item per (sequence, head)
   int n, c0, nch, slot0;
   if constexpr (SEQ) {
     n = p.order ? p.order[rnk] : rnk;
@@ -247,7 +247,8 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
   // pass 1: the second half of the blocks traces M (identity start, U' = 0)
   const bool mpart = PASS == 1 && cb_all >= p.col_split / 2;
   const int cb = PASS == 1 ? cb_all % (p.col_split / 2) : cb_all;
-  constexpr bool write_o = PASS == 0 || PASS == 2;
+  constexpr bool write_o = PASS == 0 || PASS == 2 || PASS == 4;
+  constexpr bool keep_su = PASS == 3 || PASS == 4;  // per-chunk S and U for the backward pass
   const size_t pair_base = ((size_t)rnk * H + h) * 2 * (size_t)(D * D);
   const float* s_in = SEQ ? (p.state_in ? p.state_in + ((size_t)n * H + h) * (size_t)(D * D) : nullptr)
                     : PASS == 2 ? p.pairs + pair_base : nullptr;
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
     // that a lane holds four consecutive columns of one row and a store
     // instruction writes the whole 512-byte tile.
     Frag16<E> id16;
-    if constexpr (PASS == 3) {
+    if constexpr (keep_su) {
       {
         f32x4 x;
 #pragma unroll
@@ -500,7 +501,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * CT) + 1)) void carry_kernel(const 
             for (int c = 0; c < CT; ++c) accO[c][rt] = mma(accO[c][rt], fa, sf[c][ks]);
           }
     }
-    if constexpr (PASS == 3) {
+    if constexpr (keep_su) {
       // U = U' - W S of this chunk, [C x 128] 16 x 16 tiles in the I/O dtype
       // (rows past the sequence end are zero), transposed as the state
       E* u_dst = static_cast<E*>(p.chunk_u) + ((size_t)(slot0 + ci) * H + h) * (size_t)(C * D);
@@ -673,6 +674,8 @@ static hipError_t launch_carry_dtype(const CarryArgs& a, hipStream_t stream) {
   if (a.pass == 0 && a.col_split == 2) return launch_carry_t<E, C, 64, false, 1, 0>(a, stream);
   if (a.pass == 3 && a.col_split == 2 && a.chunk_states && a.chunk_u)
     return launch_carry_t<E, C, 64, false, 1, 3>(a, stream);
+  if (a.pass == 4 && a.col_split == 2 && a.chunk_states && a.chunk_u)
+    return launch_carry_t<E, C, 64, false, 1, 4>(a, stream);
   if (a.pass == 1 && a.col_split == 2) return launch_carry_t<E, C, 128, false, 2, 1>(a, stream);
   if (a.pass == 2 && a.col_split == 2) return launch_carry_t<E, C, 64, false, 1, 2>(a, stream);
   return hipErrorInvalidValue;

@@ -193,6 +193,8 @@ struct CarryArgs {
   //   chunk's incoming state goes to chunk_states [slot][H][128 x 128] and its
   //   U = U' - W S to chunk_u [slot][H][C x 128], both in the I/O dtype as
   //   16 x 16 tiles (tile16_index).
+  // pass 4 (forward for training): pass 0 and pass 3 in one walk, the outputs
+  //   and the final state as pass 0, the per-chunk S and U as pass 3.
   int pass;
   void* chunk_states;
   void* chunk_u;

@@ -288,6 +288,53 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const floa
                          float* d_initial_state, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Forward pass for training: kda_chunk_fwd without the fused options and with
+ * the bounded decay (its o and final_state, from the same kernels), which
+ * also leaves in bwd_workspace everything kda_chunk_bwd would recompute from
+ * the inputs: the factor blocks of every chunk and each chunk's incoming
+ * state and U = U' - W S ("Kimi K3 架构…" section 7.1: the FlashKDA kernel
+ * serves training as well as prefill).  kda_chunk_bwd_saved then starts from
+ * them.  One walk over the chunks writes the outputs and those states
+ * together.
+ *
+ *   q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs,
+ *   total_tokens, num_heads, d_k, d_v, dtype
+ *                  as for kda_chunk_bwd
+ *   o              [T_total, H, 128] dtype output
+ *   final_state    [N, H, 128, 128] fp32 output or NULL; may be exactly
+ *                  initial_state (in-place continuation)
+ *   bwd_workspace  at least kda_chunk_bwd_workspace_bytes() bytes; owned by
+ *                  the caller, who keeps it unchanged until the matching
+ *                  kda_chunk_bwd_saved call
+ * Any other overlap of o, final_state and bwd_workspace with an input or with
+ * each other is KDA_ERR_INVALID_ARG; alignment as for kda_chunk_bwd.  With
+ * KDA_DEBUG_CHECKS the inputs are checked as for kda_chunk_bwd.
+ */
+kda_status kda_chunk_fwd_save(const void* q, const void* k, const void* v, const float* log_alpha,
+                              const float* beta, const float* initial_state, const int32_t* cu_seqlens, int num_seqs,
+                              int64_t total_tokens, int num_heads, int d_k, int d_v, kda_dtype dtype, void* o,
+                              float* final_state, void* bwd_workspace, size_t bwd_workspace_bytes,
+                              hipStream_t stream);
+
+/*
+ * kda_chunk_bwd from the residuals kda_chunk_fwd_save left in `workspace`:
+ * the same gradients, bit for bit, without recomputing the forward's factor
+ * blocks and chunk states.  The arguments are those of kda_chunk_bwd, with
+ * the same checks; q, k, v, log_alpha, beta, cu_seqlens and the sizes must be
+ * the ones the forward ran on, unchanged since.  The call cannot tell: other
+ * inputs give meaningless gradients, but the chunk tables are rebuilt from
+ * this call's cu_seqlens, so every access stays inside the buffers.
+ * initial_state is not read (the saved chunk states hold it), so an in-place
+ * forward that has overwritten it is fine.
+ */
+kda_status kda_chunk_bwd_saved(const void* q, const void* k, const void* v, const float* log_alpha,
+                               const float* beta, const float* initial_state, const int32_t* cu_seqlens,
+                               const void* d_o, const float* d_final_state, int num_seqs, int64_t total_tokens,
+                               int num_heads, int d_k, int d_v, kda_dtype dtype, void* dq, void* dk, void* dv,
+                               float* dlog_alpha, float* dbeta, float* d_initial_state, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
  * One decode step for N independent sequences: each (n, h) state advances by
  * one token in place ("Kimi K3 架构…" section 4.2.7: decoding keeps one
  * fixed-size d_k x d_v state per head and advances it in place).

@@ -83,6 +83,17 @@ int main(void) {
                        P(7), P(8), P(9), P(10), NULL, NULL, 0, 0), KDA_ERR_WORKSPACE);
   EXPECT(kda_chunk_bwd(P(0), P(1), P(2), P(3), P(4), NULL, NULL, NULL, NULL, 1, 10, 2, D, D, KDA_DTYPE_BF16, P(6),
                        P(7), P(8), P(9), P(10), NULL, P(11), 64u << 20, 0), KDA_ERR_INVALID_ARG);
+  EXPECT(kda_chunk_bwd_saved(P(0), P(1), P(2), P(3), P(4), NULL, NULL, P(5), NULL, 1, 10, 2, D, D, KDA_DTYPE_BF16,
+                             P(0), P(7), P(8), P(9), P(10), NULL, P(11), 64u << 20, 0), KDA_ERR_INVALID_ARG);
+  EXPECT(kda_chunk_bwd_saved(P(0), P(1), P(2), P(3), P(4), NULL, NULL, P(5), NULL, 1, 10, 2, D, D, KDA_DTYPE_BF16,
+                             P(6), P(7), P(8), P(9), P(10), NULL, NULL, 0, 0), KDA_ERR_WORKSPACE);
+  /* the training forward */
+  EXPECT(kda_chunk_fwd_save(P(0), P(1), P(2), P(3), P(4), NULL, NULL, 1, 10, 2, D, D, KDA_DTYPE_BF16, P(1), NULL,
+                            P(11), 64u << 20, 0), KDA_ERR_INVALID_ARG);
+  EXPECT(kda_chunk_fwd_save(P(0), P(1), P(2), P(3), P(4), NULL, NULL, 1, 10, 2, D, D, KDA_DTYPE_BF16, P(6), NULL,
+                            NULL, 0, 0), KDA_ERR_WORKSPACE);
+  EXPECT(kda_chunk_fwd_save(P(0), P(1), P(2), P(3), P(4), NULL, NULL, 1, 10, 2, D, 64, KDA_DTYPE_BF16, P(6), NULL,
+                            P(11), 64u << 20, 0), KDA_ERR_UNSUPPORTED);
   /* decode and replay */
   EXPECT(kda_decode_step(P(0), P(1), P(2), P(3), P(4), P(5), 2, 2, D, D, KDA_DTYPE_BF16, P(1), 0),
          KDA_ERR_INVALID_ARG);

@@ -8,6 +8,7 @@
 - the input generator's recipe (ranges, determinism, varlen lengths).
 """
 import ctypes
+import functools
 import os
 import re
 import subprocess
@@ -43,6 +44,10 @@ def lib():
     L.kda_chunk_bwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32]
     L.kda_chunk_bwd.restype = i32
     L.kda_chunk_bwd.argtypes = [vp] * 9 + [i32, i64, i32, i32, i32, i32] + [vp] * 7 + [sz, vp]
+    L.kda_chunk_bwd_saved.restype = i32
+    L.kda_chunk_bwd_saved.argtypes = [vp] * 9 + [i32, i64, i32, i32, i32, i32] + [vp] * 7 + [sz, vp]
+    L.kda_chunk_fwd_save.restype = i32
+    L.kda_chunk_fwd_save.argtypes = [vp] * 7 + [i32, i64, i32, i32, i32, i32] + [vp] * 3 + [sz, vp]
     L.kda_decode_step.restype = i32
     L.kda_decode_step.argtypes = [vp] * 6 + [i32, i32, i32, i32, i32, vp, vp]
     L.kda_decode_replay.restype = i32
@@ -59,7 +64,8 @@ def declared_functions():
 def test_header_symbols_exported(lib):
     names = declared_functions()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_workspace_bytes", "kda_chunk_bwd",
-                          "kda_chunk_bwd_workspace_bytes", "kda_decode_step",
+                          "kda_chunk_bwd_workspace_bytes", "kda_chunk_fwd_save", "kda_chunk_bwd_saved",
+                          "kda_decode_step",
                           "kda_decode_replay", "kda_last_precondition_flags", "kda_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s+(kda_\w+)", out))
@@ -278,17 +284,19 @@ def test_bwd_workspace_bytes(lib):
     assert lib.kda_chunk_bwd_workspace_bytes(1, 100, 2, 128, 128, 9) == 0
 
 
-def bwd(lib, **kw):
+def bwd(lib, fn="kda_chunk_bwd", **kw):
     a = dict(q=p(0), k=p(1), v=p(2), la=p(3), b=p(4), s0=None, cu=None, do=p(5), dsT=None, N=1, T=10, H=2,
              dk_=128, dv_=128, dt=BF16, gq=p(6), gk=p(7), gv=p(8), gla=p(9), gb=p(10), gs0=None, ws=p(11),
              wsb=64 * MB)
     a.update(kw)
-    return lib.kda_chunk_bwd(a["q"], a["k"], a["v"], a["la"], a["b"], a["s0"], a["cu"], a["do"], a["dsT"], a["N"],
-                             a["T"], a["H"], a["dk_"], a["dv_"], a["dt"], a["gq"], a["gk"], a["gv"], a["gla"], a["gb"],
-                             a["gs0"], a["ws"], a["wsb"], None)
+    return getattr(lib, fn)(a["q"], a["k"], a["v"], a["la"], a["b"], a["s0"], a["cu"], a["do"], a["dsT"], a["N"],
+                            a["T"], a["H"], a["dk_"], a["dv_"], a["dt"], a["gq"], a["gk"], a["gv"], a["gla"], a["gb"],
+                            a["gs0"], a["ws"], a["wsb"], None)
 
 
-def test_bwd_validation(lib):
+@pytest.mark.parametrize("fn", ["kda_chunk_bwd", "kda_chunk_bwd_saved"])
+def test_bwd_validation(lib, fn):
+    bwd = functools.partial(globals()["bwd"], fn=fn)
     assert bwd(lib, dk_=64) == UNSUPPORTED
     assert bwd(lib, dt=3) == UNSUPPORTED
     assert bwd(lib, N=0) == INVALID
@@ -305,6 +313,31 @@ def test_bwd_validation(lib):
     assert bwd(lib, gs0=p(12), s0=p(12)) == INVALID            # d_initial_state aliases initial_state
     assert bwd(lib, gv=ctypes.c_void_p(BASE + 8 * 64 * MB + 8)) == INVALID  # not 16-byte aligned
     assert bwd(lib, gb=ctypes.c_void_p(BASE + 10 * 64 * MB + 2)) == INVALID  # dbeta not 4-byte aligned
+
+
+def fwd_save(lib, **kw):
+    a = dict(q=p(0), k=p(1), v=p(2), la=p(3), b=p(4), s0=None, cu=None, N=1, T=10, H=2, dk_=128, dv_=128, dt=BF16,
+             o=p(6), fs=None, ws=p(11), wsb=64 * MB)
+    a.update(kw)
+    return lib.kda_chunk_fwd_save(a["q"], a["k"], a["v"], a["la"], a["b"], a["s0"], a["cu"], a["N"], a["T"], a["H"],
+                                  a["dk_"], a["dv_"], a["dt"], a["o"], a["fs"], a["ws"], a["wsb"], None)
+
+
+def test_fwd_save_validation(lib):
+    assert fwd_save(lib, dk_=64) == UNSUPPORTED
+    assert fwd_save(lib, dt=3) == UNSUPPORTED
+    assert fwd_save(lib, N=0) == INVALID
+    assert fwd_save(lib, N=2) == INVALID                       # several sequences need cu_seqlens
+    assert fwd_save(lib, o=None) == INVALID
+    assert fwd_save(lib, ws=None, wsb=0) == WORKSPACE
+    need = lib.kda_chunk_bwd_workspace_bytes(1, 10, 2, 128, 128, BF16)
+    assert fwd_save(lib, wsb=need - 1) == WORKSPACE
+    assert fwd_save(lib, o=p(1)) == INVALID                    # o aliases k
+    assert fwd_save(lib, ws=p(3)) == INVALID                   # workspace aliases log_alpha
+    assert fwd_save(lib, fs=p(6)) == INVALID                   # final state aliases o
+    assert fwd_save(lib, s0=p(12), fs=ctypes.c_void_p(BASE + 12 * 64 * MB + 4096)) == INVALID  # partial overlap
+    assert fwd_save(lib, o=ctypes.c_void_p(BASE + 6 * 64 * MB + 8)) == INVALID  # not 16-byte aligned
+    assert fwd_save(lib, H=65536) == INVALID
 
 
 def decode(lib, **kw):

@@ -239,3 +239,65 @@ def test_bwd_all_sequences_empty():
                          initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"], d_final_state=None)
     sync()
     assert torch.count_nonzero(got0[5]).item() == 0
+
+
+SAVE_CASES = [
+    # (name, H, lengths, dtype, s0_std, ds_std, in_place)
+    ("bf16_varlen_empty", 3, [200, 0, 65, 1], "bf16", 0.3, 1.0, False),
+    ("bf16_in_place", 2, [150, 77], "bf16", 0.02, 1.0, True),
+    ("f32_T100_no_final_grad", 2, [100], "f32", 0.5, 0.0, False),
+    ("f32_varlen_no_state", 2, [64, 33], "f32", 0.0, 1.0, False),
+]
+
+
+@pytest.mark.parametrize("name,H,lengths,dtype,s0,ds,in_place", SAVE_CASES, ids=[c[0] for c in SAVE_CASES])
+def test_fwd_save_then_bwd_saved(name, H, lengths, dtype, s0, ds, in_place):
+    """kda_chunk_fwd_save gives kda_chunk_fwd's outputs and final state bit for
+    bit (the sequential schedule in one window runs the same kernels), and
+    kda_chunk_bwd_saved from its residuals gives kda_chunk_bwd's gradients bit
+    for bit; an in-place forward overwrites the initial state, which the saved
+    backward does not read."""
+    say("case fwd_save + bwd_saved %s H=%d lengths=%s dtype=%s in_place=%s" % (name, H, lengths, dtype, in_place))
+    seed = zlib.crc32(name.encode()) & 0xFFFF
+    inp = kda_inputs.make_prefill(H, lengths, dtype, s0, False, DEV, seed=seed)
+    args = (inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"])
+    s0_orig = None if inp["initial_state"] is None else inp["initial_state"].clone()
+    o_ref, fs_ref = kda.chunk_fwd(*args, s0_orig, inp["cu_seqlens"], segment_tokens=-1)
+    if in_place:
+        st = s0_orig.clone()
+        o, fs, ws = kda.chunk_fwd_save(*args, st, inp["cu_seqlens"], final_state=st)
+        assert fs is st
+    else:
+        o, fs, ws = kda.chunk_fwd_save(*args, inp["initial_state"], inp["cu_seqlens"])
+    sync()
+    assert torch.equal(o, o_ref) and torch.equal(fs, fs_ref)
+    d_o, dsT = kda_inputs.make_grad_seeds(H, len(lengths), sum(lengths), dtype, ds, DEV, seed=seed + 1)
+    ref = kda.chunk_bwd(*args, d_o, s0_orig, inp["cu_seqlens"], dsT)
+    got = kda.chunk_bwd(*args, d_o, fs if in_place else inp["initial_state"], inp["cu_seqlens"], dsT, saved=ws)
+    sync()
+    for n, g, r in zip(NAMES, got, ref):
+        assert (g is None and r is None) or torch.equal(g, r), n
+    # and against the oracle
+    inp["initial_state"] = s0_orig
+    worst, _ = compare_bwd(inp, d_o, dsT, got)
+    say("  " + " ".join("%s %.2e" % (k, worst[k]) for k in NAMES))
+    for k in NAMES:
+        assert worst[k] <= TOL[dtype], (k, worst[k])
+
+
+def test_chunk_kda_save_residuals():
+    """chunk_kda with save_residuals (the training forward and the backward
+    from its workspace) gives the default path's outputs and gradients bit
+    for bit."""
+    say("case autograd with saved residuals: bf16 H=2 lengths [90, 40]")
+    inp = kda_inputs.make_prefill(2, [90, 40], "bf16", 0.3, False, DEV, seed=97)
+    d_o, dsT = kda_inputs.make_grad_seeds(2, 2, 130, "bf16", 1.0, DEV, seed=98)
+    grads = []
+    for save in (False, True):
+        leaves = [inp[n].clone().requires_grad_(True) for n in ("q", "k", "v", "log_alpha", "beta", "initial_state")]
+        o, fs = kda.chunk_kda(*leaves, inp["cu_seqlens"], save_residuals=save)
+        ((o.float() * d_o.float()).sum() + (fs * dsT).sum()).backward()
+        sync()
+        grads.append([o.detach(), fs.detach()] + [leaf.grad for leaf in leaves])
+    for a, b in zip(*grads):
+        assert torch.equal(a, b)
