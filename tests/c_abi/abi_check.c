@@ -12,6 +12,9 @@
  *      commit;
  *   4. kda_chunk_fwd again with kda_fused_opts.unbounded_decay = 1 and
  *      log_alpha = -20 softplus(z) (far below the -5 bound), one sequence;
+ *   5. kda_chunk_fwd_save on step 1's inputs (its o and final state must equal
+ *      step 1's bit for bit), then kda_chunk_bwd_saved from its workspace for
+ *      random d_o and d_final_state, against the oracle's backward;
  * and compares each output slice (per sequence and head) with the oracle by
  * max|y - r| / max|r| against 1e-4.  Exit status 0 when everything passes.
  * Inputs come from a fixed linear congruential generator (q, k normalised
@@ -30,6 +33,9 @@
 int kda_oracle_chunk_fwd(const double*, const double*, const double*, const double*, const double*, const double*,
                          const int64_t*, int, int64_t, int, int, int, const double*, const double*, const double*,
                          const double*, double, double, double*, double*, int);
+int kda_oracle_chunk_bwd(const double*, const double*, const double*, const double*, const double*, const double*,
+                         const int64_t*, int, int64_t, int, int, int, const double*, const double*, double*, double*,
+                         double*, double*, double*, double*, int);
 int kda_oracle_decode_step(double*, const double*, const double*, const double*, const double*, const double*, int,
                            int, int, int, double*, int);
 int kda_oracle_decode_multi(const double*, const double*, const double*, const double*, const double*, const double*,
@@ -279,6 +285,49 @@ int main(void) {
       free(r);
     }
     free(wq); free(wk); free(wv); free(wla); free(wb); free(ro); free(rfs);
+  }
+
+  /* ---- 5. the training forward and the backward from its residuals, on step 1's inputs ---- */
+  {
+    const size_t bwb = kda_chunk_bwd_workspace_bytes(N, T, H, D, D, KDA_DTYPE_F32);
+    void *dwb = bwb ? dev_copy(NULL, bwb) : NULL, *so = dev_copy(NULL, tok * D * 4), *sfs = dev_copy(NULL, st * 4);
+    if (!dwb || !so || !sfs) return 2;
+    KDA_OK_(kda_chunk_fwd_save(dq, dk, dv, dla, db, ds0, dcu, N, T, H, D, D, KDA_DTYPE_F32, so, sfs, dwb, bwb, 0));
+    float *o2 = malloc(tok * D * 4), *fs2 = malloc(st * 4);
+    HIP_OK(hipMemcpy(o2, so, tok * D * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(fs2, sfs, st * 4, hipMemcpyDeviceToHost));
+    const int same = memcmp(o2, o, tok * D * 4) == 0 && memcmp(fs2, fs, st * 4) == 0;
+    if (!same) ++failures;
+    printf("%-44s %s\n", "chunk_fwd_save o, S_T = chunk_fwd bit for bit", same ? "ok" : "FAIL");
+    float *gdo = malloc(tok * D * 4), *gds = malloc(st * 4);
+    fill_rows(gdo, tok, 0);
+    for (size_t i = 0; i < st; ++i) gds[i] = (float)normal();
+    void *ddo = dev_copy(gdo, tok * D * 4), *dds = dev_copy(gds, st * 4), *xq = dev_copy(NULL, tok * D * 4);
+    void *xk = dev_copy(NULL, tok * D * 4), *xv = dev_copy(NULL, tok * D * 4), *xla = dev_copy(NULL, tok * D * 4);
+    void *xb = dev_copy(NULL, tok * 4), *xs0 = dev_copy(NULL, st * 4);
+    if (!ddo || !dds || !xq || !xk || !xv || !xla || !xb || !xs0) return 2;
+    KDA_OK_(kda_chunk_bwd_saved(dq, dk, dv, dla, db, ds0, dcu, ddo, dds, N, T, H, D, D, KDA_DTYPE_F32, xq, xk, xv, xla,
+                                xb, xs0, dwb, bwb, 0));
+    const size_t sizes[6] = {tok * D, tok * D, tok * D, tok * D, tok, st};
+    void* devs[6] = {xq, xk, xv, xla, xb, xs0};
+    const char* names[6] = {"chunk_bwd_saved dq", "chunk_bwd_saved dk", "chunk_bwd_saved dv",
+                            "chunk_bwd_saved dlog_alpha", "chunk_bwd_saved dbeta", "chunk_bwd_saved d_initial_state"};
+    double *wq = widen(q, tok * D), *wk = widen(k, tok * D), *wv = widen(v, tok * D), *wla = widen(la, tok * D);
+    double *wb = widen(b, tok), *ws0 = widen(s0, st), *wdo = widen(gdo, tok * D), *wds = widen(gds, st);
+    double* ref[6];
+    for (int i = 0; i < 6; ++i) ref[i] = malloc(sizes[i] * 8);
+    if (kda_oracle_chunk_bwd(wq, wk, wv, wla, wb, ws0, cu64, N, T, H, D, D, wdo, wds, ref[0], ref[1], ref[2], ref[3],
+                             ref[4], ref[5], 0) != 0)
+      return 4;
+    for (int i = 0; i < 6; ++i) {
+      float* y = malloc(sizes[i] * 4);
+      HIP_OK(hipMemcpy(y, devs[i], sizes[i] * 4, hipMemcpyDeviceToHost));
+      check(names[i], y, ref[i], sizes[i]);
+      free(y);
+      free(ref[i]);
+    }
+    free(wq); free(wk); free(wv); free(wla); free(wb); free(ws0); free(wdo); free(wds);
+    free(o2); free(fs2); free(gdo); free(gds);
   }
 
   /* an argument error comes back before anything is launched */
