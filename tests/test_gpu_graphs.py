@@ -2,7 +2,7 @@
 
 Every compute path of the library only launches kernels on the caller's
 stream (no memsets, copies or host waits), so a serving loop can capture it
-once and replay it (the unbounded-decay prefill included).  Each graph case captures one call, then replays the
+once and replay it (the unbounded-decay prefill and the training pair included).  Each graph case captures one call, then replays the
 graph several times with eager work and synchronisations in between, and
 checks every replay bit for bit against the same call run eagerly (the
 kernels are deterministic).  The last case runs calls on three streams at
@@ -88,6 +88,39 @@ def test_chunk_fwd_graph(segment_tokens, unbounded):
         torch.cuda.synchronize()
         assert torch.equal(o_g, o_e), i
         assert torch.equal(fs_g, fs_e), i
+
+
+def test_training_step_graph():
+    """kda_chunk_fwd_save and kda_chunk_bwd_saved captured together: every
+    replay gives the eager kda_chunk_fwd outputs and kda_chunk_bwd gradients."""
+    say("case graph: chunk_fwd_save + chunk_bwd(saved)")
+    inp = kda_inputs.make_prefill(2, [150, 77], "bf16", 0.02, False, DEV, seed=94)
+    N, T, H = inp["N"], inp["T"], inp["H"]
+    d_o, dsT = kda_inputs.make_grad_seeds(H, N, T, "bf16", 1.0, DEV, seed=95)
+    args = (inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"])
+    ws = torch.empty(kda.chunk_bwd_workspace_bytes(N, T, H, torch.bfloat16), dtype=torch.uint8, device=DEV)
+    o_g = torch.empty_like(inp["v"])
+    fs_g = torch.empty((N, H, 128, 128), dtype=torch.float32, device=DEV)
+    res = {}
+
+    def call(warm):
+        kda.chunk_fwd_save(*args, inp["initial_state"], inp["cu_seqlens"], out=o_g, final_state=fs_g, workspace=ws)
+        res["grads"] = kda.chunk_bwd(*args, d_o, inp["initial_state"], inp["cu_seqlens"], dsT, saved=ws)
+
+    g = capture(call)
+    grads_g = res["grads"]
+    for i in range(REPLAYS):
+        o_g.zero_()
+        fs_g.zero_()
+        for t in grads_g:
+            t.zero_()
+        g.replay()
+        o_e, fs_e = kda.chunk_fwd(*args, inp["initial_state"], inp["cu_seqlens"], segment_tokens=-1)
+        grads_e = kda.chunk_bwd(*args, d_o, inp["initial_state"], inp["cu_seqlens"], dsT)
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e) and torch.equal(fs_g, fs_e), i
+        for x, y in zip(grads_g, grads_e):
+            assert torch.equal(x, y), i
 
 
 def test_decode_replay_graph():
