@@ -576,12 +576,12 @@ kda_status bwd_tables(const int32_t* cu_seqlens, int num_seqs, int64_t total_tok
 
 // The backward's residuals in its workspace: the tables above, the forward
 // factor blocks and, per chunk, the incoming state and U (carry pass 3).
-// With o given (the training forward) the same walk also writes the outputs
-// and the final state (carry pass 4).
+// For the training forward the same walk also writes the outputs and the
+// final state (carry pass 4); o may be NULL there when there are no tokens.
 kda_status bwd_residuals(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
                          const float* initial_state, const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens,
-                         int num_heads, bool bf16, const BwdPlan& pl, char* ws, void* o, float* final_state,
-                         hipStream_t stream) {
+                         int num_heads, bool bf16, const BwdPlan& pl, char* ws, bool forward, void* o,
+                         float* final_state, hipStream_t stream) {
   const kda_status ts = bwd_tables(cu_seqlens, num_seqs, total_tokens, bf16, pl, ws, stream);
   if (ts != KDA_OK) return ts;
   int32_t* order = num_seqs > 1 ? reinterpret_cast<int32_t*>(ws) : nullptr;
@@ -617,7 +617,7 @@ kda_status bwd_residuals(const void* q, const void* k, const void* v, const floa
   ca.seq_c0 = seq_c0;
   ca.seq_c1 = seq_c1;
   ca.state_in = initial_state;
-  ca.state_out = o ? final_state : nullptr;
+  ca.state_out = forward ? final_state : nullptr;
   ca.o = o;
   ca.rms_eps = 1e-6f;
   ca.num_seqs = num_seqs;
@@ -626,7 +626,7 @@ kda_status bwd_residuals(const void* q, const void* k, const void* v, const floa
   ca.units = num_seqs * num_heads;
   ca.col_split = 2;
   ca.bf16 = bf16;
-  ca.pass = o ? 4 : 3;
+  ca.pass = forward ? 4 : 3;
   ca.chunk_states = ws + pl.off_states;
   ca.chunk_u = ws + pl.off_u;
   if (kda::launch_carry(ca, stream) != hipSuccess) return KDA_ERR_HIP;
@@ -742,7 +742,7 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const floa
   const BwdPlan pl = make_bwd_plan(num_seqs, total_tokens, num_heads, dtype);
   char* ws = static_cast<char*>(workspace);
   const kda_status rs = bwd_residuals(q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs, total_tokens,
-                                      num_heads, bf16, pl, ws, nullptr, nullptr, stream);
+                                      num_heads, bf16, pl, ws, false, nullptr, nullptr, stream);
   if (rs != KDA_OK) return rs;
   return bwd_gradients(q, k, v, log_alpha, beta, cu_seqlens, d_o, d_final_state, num_seqs, total_tokens, num_heads,
                        bf16, pl, ws, dq, dk, dv, dlog_alpha, dbeta, d_initial_state, stream);
@@ -790,7 +790,7 @@ kda_status kda_chunk_fwd_save(const void* q, const void* k, const void* v, const
                                          stream);
   if (cs != KDA_OK) return cs;
   return bwd_residuals(q, k, v, log_alpha, beta, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, bf16,
-                       pl, static_cast<char*>(bwd_workspace), o, final_state, stream);
+                       pl, static_cast<char*>(bwd_workspace), true, o, final_state, stream);
 }
 
 kda_status kda_chunk_bwd_saved(const void* q, const void* k, const void* v, const float* log_alpha,

@@ -301,3 +301,21 @@ def test_chunk_kda_save_residuals():
         grads.append([o.detach(), fs.detach()] + [leaf.grad for leaf in leaves])
     for a, b in zip(*grads):
         assert torch.equal(a, b)
+
+
+def test_fwd_save_and_bwd_saved_all_sequences_empty():
+    """T = 0 with two empty sequences: the training forward passes the initial
+    state through as the plain forward does, and the saved backward gives
+    d_initial_state = d_final_state."""
+    say("case empty batch, training pair: bf16 H=2 lengths [0, 0]")
+    inp = kda_inputs.make_prefill(2, [0, 0], "bf16", 0.3, False, DEV, seed=101)
+    args = (inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"])
+    o_ref, fs_ref = kda.chunk_fwd(*args, inp["initial_state"], inp["cu_seqlens"], segment_tokens=-1)
+    o, fs, ws = kda.chunk_fwd_save(*args, inp["initial_state"], inp["cu_seqlens"])
+    d_o, dsT = kda_inputs.make_grad_seeds(2, 2, 0, "bf16", 1.0, DEV, seed=102)
+    got = kda.chunk_bwd(*args, d_o, inp["initial_state"], inp["cu_seqlens"], dsT, saved=ws)
+    sync()
+    assert o.shape[0] == 0 and torch.equal(fs, fs_ref) and torch.equal(fs, inp["initial_state"])
+    for t in got[:5]:
+        assert t.shape[0] == 0
+    assert torch.equal(got[5], dsT)
