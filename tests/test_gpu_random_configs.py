@@ -150,3 +150,42 @@ def test_random_replay(case):
     res = run_lib(inp, nt, commit, in_place=(mode == "commit_in_place"))
     ref = run_oracle(inp, counts)
     compare(inp, counts, res, ref, commit, dtype)
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_training_pair(case):
+    """kda_chunk_fwd_save + kda_chunk_bwd_saved against kda_chunk_fwd (sequential
+    schedule) + kda_chunk_bwd, bit for bit, over random sizes, empty
+    sequences, a single sequence without cu_seqlens, with and without an
+    initial state, a final state or an in-place continuation."""
+    rng = np.random.Generator(np.random.Philox(0x7A400000 + case))
+    n = int(rng.integers(1, 5))
+    lengths = [int(x) for x in rng.integers(0, 181, size=n)]
+    if rng.random() < 0.15:
+        lengths = [0] * n
+    dtype = "f32" if rng.random() < 0.35 else "bf16"
+    H = int(rng.integers(1, 4))
+    s0 = float(rng.choice([0.0, 0.3]))
+    keep_fs = bool(rng.random() < 0.8)
+    in_place = keep_fs and s0 > 0 and bool(rng.random() < 0.4)
+    say("case random training pair %d: %s H=%d lengths=%s S0 %g final state %s in place %s"
+        % (case, dtype, H, lengths, s0, keep_fs, in_place))
+    inp = kda_inputs.make_prefill(H, lengths, dtype, s0, False, DEV, seed=8000 + case)
+    args = (inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"])
+    s0_orig = None if inp["initial_state"] is None else inp["initial_state"].clone()
+    o_ref, fs_ref = kda.chunk_fwd(*args, s0_orig, inp["cu_seqlens"], segment_tokens=-1)
+    if in_place:
+        st = s0_orig.clone()
+        o, fs, ws = kda.chunk_fwd_save(*args, st, inp["cu_seqlens"], final_state=st)
+    else:
+        o, fs, ws = kda.chunk_fwd_save(*args, inp["initial_state"], inp["cu_seqlens"], output_final_state=keep_fs)
+    d_o, dsT = kda_inputs.make_grad_seeds(H, n, sum(lengths), dtype, 1.0, DEV, seed=8500 + case)
+    ref = kda.chunk_bwd(*args, d_o, s0_orig, inp["cu_seqlens"], dsT)
+    got = kda.chunk_bwd(*args, d_o, fs if in_place else inp["initial_state"], inp["cu_seqlens"], dsT, saved=ws)
+    sync()
+    assert torch.equal(o, o_ref)
+    assert (fs is None) == (not keep_fs)
+    if keep_fs:
+        assert torch.equal(fs, fs_ref)
+    for g, r in zip(got, ref):
+        assert (g is None and r is None) or torch.equal(g, r)
